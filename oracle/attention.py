@@ -1,0 +1,143 @@
+"""Single-query decode attention over a packed cache: the plain definition.
+
+During decoding every new token attends over the keys and values of all cached
+tokens, and the whole cache is streamed from HBM for each of them (page
+"TurboQuant vs OSCAR vs EpiCache", section on the KV-cache memory bottleneck).
+A fused streaming kernel reaches exactly this result, so the oracle is the
+definition, materialised in fp64:
+
+  for each sequence b and query head hq, with KV head g = hq // (Hq / H)
+  (reading: contiguous query-head groups share a KV head):
+      l_t = scale * logit(q[b, hq], cache[b, g, t])      for t < L_b
+      p   = softmax(l)      (max subtracted, fp64)
+      o   = sum_t p_t * value(cache[b, g, t])
+
+Reading: a single query sees all L_b cached tokens with no mask (its own key
+and value were appended before the call); the softmax scale is an argument.
+
+Per format, logit() and value() are:
+  fp4, kivi2   <q, k_hat>,  v_hat                 (dequantised in fp64)
+  latent       <q_c, c_hat> + <q_r, k_rope>,  c_hat (value = the latent)
+  turbo        n_k * ( <R q, u_tilde> + kappa * gamma * <S R q, sigma> ),
+               value n_v * R^T u_tilde_v
+  qjl1         kappa * n_k * <S q, sigma>,  v_hat (FP4)
+with sigma = +-1 from the sketch bits and kappa = sqrt(pi/2) / m.  kappa follows
+from E[ sign(<g, r>) <g, q> ] = sqrt(2/pi) <q, r> / ||r|| for g ~ N(0, I): the
+QJL estimate of <q, r> is kappa * ||r|| * <S q, sign(S r)>, unbiased over S
+(page "TurboQuant vs OSCAR vs EpiCache", section "quantization frontiers",
+stage two).  The turbo logit rests on <q, k> = n <R q, u> for orthogonal R
+and u = R k / n = u_tilde + r.
+
+Logits and dequantised values are computed in token chunks only to bound
+memory; the softmax is taken over the full logit vector.
+"""
+
+import math
+
+import numpy as np
+
+from . import formats as F
+from .numerics import bf16_from_bits, fp16_from_bits
+
+CHUNK = 65536
+
+
+def qjl_kappa(m: int) -> float:
+    return math.sqrt(math.pi / 2.0) / m
+
+
+def _key_logits(fmt, cache, b, h, t0, t1, qg, consts, latent_dim):
+    """Unscaled logits [G, t1-t0] of query rows qg [G, key_width] against tokens t0..t1."""
+    if fmt == "fp4":
+        kh = F.fp4_decode(cache["k_codes"][b, h, t0:t1], cache["k_scale"][b, h, t0:t1])
+        return qg @ kh.T
+    if fmt == "kivi2":
+        g0, g1 = t0 // F.KIVI_GROUP, -(-t1 // F.KIVI_GROUP)
+        kh = F.kivi2_decode_keys(cache["k_codes"][b, h, g0 * F.KIVI_GROUP:g1 * F.KIVI_GROUP],
+                                 cache["k_scale"][b, h, g0:g1], cache["k_zero"][b, h, g0:g1])
+        kh = kh[t0 - g0 * F.KIVI_GROUP:t1 - g0 * F.KIVI_GROUP]
+        return qg @ kh.T
+    if fmt == "latent":
+        ch = F.fp4_decode(cache["k_codes"][b, t0:t1], cache["k_scale"][b, t0:t1])
+        kr = bf16_from_bits(cache["rope"][b, t0:t1])
+        return qg[:, :latent_dim] @ ch.T + qg[:, latent_dim:] @ kr.T
+    if fmt == "turbo":
+        rot = np.asarray(consts["rot"], np.float64)
+        proj = np.asarray(consts["proj"], np.float64)
+        lv = np.asarray(consts["levels"], np.float64)
+        q_rot = qg @ rot.T
+        q_s = q_rot @ proj.T
+        ut = lv[F.unpack_2bit(cache["k_codes"][b, h, t0:t1])]
+        sig = 2.0 * F.unpack_bits(cache["k_sketch"][b, h, t0:t1]).astype(np.float64) - 1.0
+        n = fp16_from_bits(cache["k_norm"][b, h, t0:t1])
+        gam = fp16_from_bits(cache["k_rnorm"][b, h, t0:t1])
+        kap = qjl_kappa(proj.shape[0])
+        return n[None, :] * (q_rot @ ut.T + kap * gam[None, :] * (q_s @ sig.T))
+    if fmt == "qjl1":
+        proj = np.asarray(consts["proj"], np.float64)
+        q_s = qg @ proj.T
+        sig = 2.0 * F.unpack_bits(cache["k_sketch"][b, h, t0:t1]).astype(np.float64) - 1.0
+        n = fp16_from_bits(cache["k_norm"][b, h, t0:t1])
+        return qjl_kappa(proj.shape[0]) * n[None, :] * (q_s @ sig.T)
+    raise ValueError(fmt)
+
+
+def _values(fmt, cache, b, h, t0, t1, consts, latent_dim):
+    """Dequantised values [t1-t0, dv] (turbo: in the rotated space, times n_v)."""
+    if fmt in ("fp4", "qjl1"):
+        return F.fp4_decode(cache["v_codes"][b, h, t0:t1], cache["v_scale"][b, h, t0:t1])
+    if fmt == "kivi2":
+        return F.kivi2_decode_values(cache["v_codes"][b, h, t0:t1], cache["v_scale"][b, h, t0:t1],
+                                     cache["v_zero"][b, h, t0:t1])
+    if fmt == "latent":
+        return F.fp4_decode(cache["k_codes"][b, t0:t1], cache["k_scale"][b, t0:t1])
+    if fmt == "turbo":
+        lv = np.asarray(consts["levels"], np.float64)
+        ut = lv[F.unpack_2bit(cache["v_codes"][b, h, t0:t1])]
+        n = fp16_from_bits(cache["v_norm"][b, h, t0:t1])
+        return n[:, None] * ut
+    raise ValueError(fmt)
+
+
+def decode_attention_row_group(fmt, cache, b, h, qg, L, scale, consts=None, latent_dim=512,
+                               chunk=CHUNK):
+    """Outputs [G, dv] for the query rows qg of sequence b, KV head h, over L tokens."""
+    qg = np.asarray(qg, dtype=np.float64)
+    if L <= 0:
+        raise ValueError("decode over an empty context is undefined")
+    logits = np.concatenate([
+        _key_logits(fmt, cache, b, h, t0, min(L, t0 + chunk), qg, consts, latent_dim)
+        for t0 in range(0, L, chunk)], axis=1) * scale
+    m = logits.max(axis=1, keepdims=True)
+    p = np.exp(logits - m)
+    p /= p.sum(axis=1, keepdims=True)
+    out = None
+    for t0 in range(0, L, chunk):
+        t1 = min(L, t0 + chunk)
+        part = p[:, t0:t1] @ _values(fmt, cache, b, h, t0, t1, consts, latent_dim)
+        out = part if out is None else out + part
+    if fmt == "turbo":
+        out = out @ np.asarray(consts["rot"], np.float64)   # R^T applied to each row
+    return out
+
+
+def decode_attention(fmt, cache, q, seq_lens, scale, hkv, consts=None, latent_dim=512,
+                     rows=None):
+    """fp64 outputs [B, Hq, dv] (or only the (b, hq) pairs in `rows`, as a dict)."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq = q.shape[:2]
+    G = Hq // hkv
+    if rows is None:
+        outs = []
+        for b in range(B):
+            per_b = [decode_attention_row_group(fmt, cache, b, h, q[b, h * G:(h + 1) * G],
+                                                int(seq_lens[b]), scale, consts, latent_dim)
+                     for h in range(hkv)]
+            outs.append(np.concatenate(per_b, 0))
+        return np.stack(outs, 0)
+    res = {}
+    for (b, hq) in rows:
+        h = hq // G
+        res[(b, hq)] = decode_attention_row_group(fmt, cache, b, h, q[b, hq:hq + 1],
+                                                  int(seq_lens[b]), scale, consts, latent_dim)[0]
+    return res
