@@ -39,6 +39,10 @@ def gaussian_lloyd_max(bits: int, sigma: float = 1.0, iters: int = 100000, tol: 
         pb = np.where(np.isinf(b), 0.0, _phi(np.where(np.isinf(b), 0.0, b)))
         mass = ndtr(b) - ndtr(a)
         new = (pa - pb) / mass
+        # the source is symmetric about 0, so is the optimum: keep the iterate
+        # exactly antisymmetric (rounding would otherwise leave the middle
+        # threshold a few 1e-18 off zero)
+        new = 0.5 * (new - new[::-1])
         done = np.max(np.abs(new - lv)) <= tol
         lv = new
         if done:

@@ -106,7 +106,8 @@ def test_lloyd_max_optimality_by_quadrature(bits):
         mean = integrate.quad(lambda z: z * norm.pdf(z), edges[j], edges[j + 1], epsabs=1e-14)[0] / mass
         assert abs(mean - c) < 1e-9
     assert np.all(np.diff(lv) > 0)
-    np.testing.assert_allclose(lv, -lv[::-1], atol=1e-14)
+    np.testing.assert_array_equal(lv, -lv[::-1])          # symmetric source, symmetric optimum
+    assert th[len(th) // 2] == 0.0
 
 
 def test_lloyd_max_sigma_scaling_and_canonical():
