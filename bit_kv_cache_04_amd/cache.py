@@ -1,0 +1,125 @@
+"""A packed KV cache held in torch device memory, driven through the C ABI.
+
+torch owns the buffers, the constants and the workspace; every quantisation
+and attention step runs in libkvq's kernels via the same-name wrappers of
+`kvq`.  Nothing here computes on the data.
+"""
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import kvq
+from .kvq import BUFFERS, DT_BF16, DT_F32, FMT, KVCache, KVDecodeOpts, make_layout
+
+_TORCH_DT = {torch.float32: DT_F32, torch.bfloat16: DT_BF16}
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream_ptr(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def buffer_view_spec(fmt, B, H, T, d, rope=0, m=128):
+    """{name: (torch dtype, shape)} of each buffer's natural element view."""
+    u8, u16, f32 = torch.uint8, torch.uint16, torch.float32
+    if fmt == "kivi2":
+        return dict(k_codes=(u8, (B, H, T, d // 4)), k_scale=(f32, (B, H, T // 32, d)),
+                    k_zero=(f32, (B, H, T // 32, d)), v_codes=(u8, (B, H, T, d // 4)),
+                    v_scale=(f32, (B, H, T, d // 32)), v_zero=(f32, (B, H, T, d // 32)))
+    if fmt == "fp4":
+        return dict(k_codes=(u8, (B, H, T, d // 2)), k_scale=(u16, (B, H, T, d // 16)),
+                    v_codes=(u8, (B, H, T, d // 2)), v_scale=(u16, (B, H, T, d // 16)))
+    if fmt == "turbo":
+        return dict(k_codes=(u8, (B, H, T, d // 4)), k_sketch=(u8, (B, H, T, m // 8)),
+                    k_norm=(u16, (B, H, T)), k_rnorm=(u16, (B, H, T)),
+                    v_codes=(u8, (B, H, T, d // 4)), v_norm=(u16, (B, H, T)))
+    if fmt == "qjl1":
+        return dict(k_sketch=(u8, (B, H, T, m // 8)), k_norm=(u16, (B, H, T)),
+                    v_codes=(u8, (B, H, T, d // 2)), v_scale=(u16, (B, H, T, d // 16)))
+    if fmt == "latent":
+        return dict(k_codes=(u8, (B, T, d // 2)), k_scale=(u16, (B, T, d // 16)), rope=(u16, (B, T, rope)))
+    raise ValueError(fmt)
+
+
+def make_constants(fmt, head_dim, rot_gauss=None, proj_gauss=None):
+    """The method's constants from caller-drawn Gaussians, made by libkvq's host helpers."""
+    out = {}
+    if fmt == "turbo":
+        out["rot"] = kvq.kv_make_rotation(rot_gauss)
+        out["levels"], out["thresholds"] = kvq.kv_lloyd_max_gaussian(2, head_dim)
+    if fmt in ("turbo", "qjl1"):
+        out["proj"] = kvq.kv_make_projection(proj_gauss)
+    return out
+
+
+class PackedKVCache:
+    def __init__(self, fmt, batch, num_kv_heads, head_dim, capacity, rope_dim=0, device="cuda",
+                 constants=None):
+        self.fmt, self.device = fmt, torch.device(device)
+        self.B, self.H, self.d, self.T, self.rope = batch, num_kv_heads, head_dim, capacity, rope_dim
+        self.layout = make_layout(fmt, batch, num_kv_heads, head_dim, capacity, rope_dim)
+        self.bufs = {}
+        ptrs = []
+        for i, name in enumerate(BUFFERS):
+            nb = kvq.kv_buffer_bytes(self.layout, i)
+            if nb:
+                self.bufs[name] = torch.zeros(nb, dtype=torch.uint8, device=self.device)
+            ptrs.append(self.bufs[name].data_ptr() if nb else None)
+        if not self.bufs:
+            raise kvq.KvError("kv_buffer_bytes", -3)
+        self.consts = {}
+        for k, v in (constants or {}).items():
+            self.consts[k] = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(self.device)
+        cp = lambda k: self.consts[k].data_ptr() if k in self.consts else None  # noqa: E731
+        self.struct = KVCache(self.layout, (ctypes.c_void_p * len(BUFFERS))(*ptrs),
+                              cp("rot"), cp("proj"), cp("levels"), cp("thresholds"))
+        self._ws = None
+
+    # ---- views of the packed bytes
+    def view(self, name):
+        dt, shape = buffer_view_spec(self.fmt, self.B, self.H, self.T, self.d, self.rope)[name]
+        return self.bufs[name].view(dt).view(shape)
+
+    def bytes_per_token(self, num_layers=1):
+        return kvq.kv_bytes_per_token(self.layout, num_layers)
+
+    # ---- the two device entry points
+    def append(self, k, v, start):
+        """k, v: contiguous [B, H, n, d] (latent: k [B, n, d + rope], v None), fp32 or bf16."""
+        if not k.is_contiguous() or (v is not None and not v.is_contiguous()):
+            raise ValueError("append inputs must be contiguous")
+        if v is not None and v.dtype != k.dtype:
+            raise ValueError("k and v must share a dtype")
+        n = k.shape[-2]
+        kvq.kv_quant_append(self.struct, _ptr(k), _ptr(v), _TORCH_DT[k.dtype], start, n,
+                            _stream_ptr(self.device))
+
+    def workspace_bytes(self, num_q_heads, max_seq_len, splits=0):
+        opts = KVDecodeOpts(splits, None, None)
+        return kvq.kv_decode_attention(self.struct, None, DT_BF16, num_q_heads, None, max_seq_len, 1.0,
+                                       None, None, 0, opts)
+
+    def decode(self, q, seq_lens, scale, max_seq_len=None, splits=0, out=None, ws=None, events=None):
+        """q: [B, Hq, d(+rope)] fp32/bf16; seq_lens: int32 device [B]. Returns fp32 [B, Hq, d]."""
+        q = q.contiguous()
+        Hq = q.shape[1]
+        max_seq_len = self.T if max_seq_len is None else max_seq_len
+        need = self.workspace_bytes(Hq, max_seq_len, splits)
+        if ws is None:
+            if self._ws is None or self._ws.numel() < need:
+                self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+            ws = self._ws
+        if out is None:
+            out = torch.empty(self.B, Hq, self.d, dtype=torch.float32, device=self.device)
+        ev = (None, None) if events is None else (ctypes.c_void_p(events[0].cuda_event),
+                                                  ctypes.c_void_p(events[1].cuda_event))
+        opts = KVDecodeOpts(splits, ev[0], ev[1])
+        kvq.kv_decode_attention(self.struct, _ptr(q), _TORCH_DT[q.dtype], Hq, _ptr(seq_lens), max_seq_len,
+                                float(scale), _ptr(out), _ptr(ws), ws.numel(), opts,
+                                _stream_ptr(self.device))
+        return out

@@ -1,0 +1,60 @@
+// Exported entry points: argument validation on the host, then the launchers.
+// Nothing here touches a GPU before every check has passed, so each error path
+// can be exercised on a machine without one.
+#include <cmath>
+#include <cstdint>
+
+#include "kvq_internal.h"
+
+using namespace kvq;
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+extern "C" int kv_quant_append(const kv_cache* c, const void* k, const void* v, int32_t in_dtype,
+                               int32_t start, int32_t n_new, void* ws, size_t* ws_bytes, void* stream) {
+  (void)ws;
+  int st = check_cache(c);
+  if (st != KV_OK) return st;
+  if (ws_bytes) *ws_bytes = 0;
+  if (in_dtype != KV_DT_F32 && in_dtype != KV_DT_BF16) return KV_EUNSUPPORTED;
+  if (start < 0 || n_new < 0) return KV_EINVAL;
+  if ((int64_t)start + n_new > c->layout.capacity) return KV_ECAPACITY;
+  if (c->layout.format == KV_FMT_KIVI2 && (start % kKiviGroup || n_new % kKiviGroup)) return KV_EINVAL;
+  if (n_new == 0) return KV_OK;
+  const bool latent = c->layout.format == KV_FMT_LATENT_FP4;
+  if (!k || (!latent && !v) || (latent && v)) return KV_EINVAL;
+  if (!aligned(k, 16) || (v && !aligned(v, 16))) return KV_EINVAL;
+  return launch_append(c, k, v, in_dtype, start, n_new, stream);
+}
+
+extern "C" int kv_decode_attention(const kv_cache* c, const void* q, int32_t q_dtype, int32_t num_q_heads,
+                                   const int32_t* seq_lens, int32_t max_seq_len, float softmax_scale,
+                                   float* out, void* ws, size_t* ws_bytes, const kv_decode_opts* opts,
+                                   void* stream) {
+  int st = check_cache(c);
+  if (st != KV_OK) return st;
+  const kv_layout& L = c->layout;
+  if (num_q_heads < 1 || num_q_heads % L.num_kv_heads) return KV_EINVAL;
+  if (num_q_heads / L.num_kv_heads > 1024) return KV_EUNSUPPORTED;
+  if (max_seq_len < 1 || max_seq_len > L.capacity) return KV_EINVAL;
+  if (q_dtype != KV_DT_F32 && q_dtype != KV_DT_BF16) return KV_EUNSUPPORTED;
+  if (!std::isfinite(softmax_scale)) return KV_EINVAL;
+  const int req = opts ? opts->num_splits : 0;
+  if (req < 0 || req > 1024) return KV_EINVAL;
+  const SplitPlan plan = plan_splits(&L, num_q_heads, max_seq_len, req);
+  const DecodeWorkspace wsl = decode_workspace(&L, num_q_heads, plan.splits);
+  if (!ws) {
+    if (!ws_bytes) return KV_EINVAL;
+    *ws_bytes = wsl.total;
+    return KV_OK;
+  }
+  if (!ws_bytes || *ws_bytes < wsl.total) return KV_EWORKSPACE;
+  if (!aligned(ws, 256)) return KV_EINVAL;
+  if (!q || !seq_lens || !out) return KV_EINVAL;
+  return launch_decode(c, q, q_dtype, num_q_heads, seq_lens, max_seq_len, softmax_scale, out, ws, plan, wsl,
+                       opts ? opts->ev_begin : nullptr, opts ? opts->ev_end : nullptr, stream);
+}

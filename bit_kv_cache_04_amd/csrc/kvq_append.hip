@@ -1,0 +1,522 @@
+// Append kernels: quantise new tokens' keys/values into the packed cache.
+//
+// FP4 E2M1 groups (page "How DeepSeek-V4.1-Flash cut KV-cache storage by 4x via
+// CSA2", numerical-precision section), KIVI 2-bit (page "TurboQuant vs OSCAR vs
+// EpiCache", "quantization frontiers", KIVI paragraph), TurboQuant and QJL
+// sign sketches (same section, stages one and two).  The rotation and the QJL
+// projection are the only dense contractions here and run on the matrix cores.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Token rows of an append are flat indices r in [0, bh_count * n): sequence-head
+// bh = r / n, position start + r % n; the input row r starts at x + r * stride.
+__device__ __forceinline__ size_t dst_row(size_t r, int n, int cap, int start) {
+  return (r / n) * (size_t)cap + start + (r % n);
+}
+
+// ---------------------------------------------------------------- FP4
+
+// One thread per 16-channel group: s = bf16_RNE(absmax / 6) (the quotient taken
+// in fp64, then rounded once), then each element's E2M1 nibble against s.
+template <typename InT>
+__global__ void __launch_bounds__(256) fp4_append_kernel(const InT* __restrict__ x, size_t stride,
+                                                         int d, uint8_t* __restrict__ codes,
+                                                         uint16_t* __restrict__ scales, size_t rows,
+                                                         int n, int cap, int start) {
+  const int groups = d / 16;
+  size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= rows * groups) return;
+  const int g = (int)(gid % groups);
+  const size_t r = gid / groups;
+  const InT* src = x + r * stride + g * 16;
+  float a[16];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    a[i] = load_as_f32(src, i);
+    amax = fmaxf(amax, fabsf(a[i]));
+  }
+  const uint16_t sb = bf16_from_f64(__ddiv_rn((double)amax, 6.0));
+  const float s = bf16_to_f32(sb);
+  unsigned long long packed = 0;
+  if (s > 0.f) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) packed |= (unsigned long long)e2m1_encode(a[i], s) << (4 * i);
+  }
+  const size_t dr = dst_row(r, n, cap, start);
+  *reinterpret_cast<unsigned long long*>(codes + dr * (d / 2) + g * 8) = packed;
+  scales[dr * groups + g] = sb;
+}
+
+// Latent RoPE part: copied through as bf16 (rounded once if the input is fp32).
+template <typename InT>
+__global__ void rope_copy_kernel(const InT* __restrict__ x, size_t stride, int off, int width,
+                                 uint16_t* __restrict__ rope, size_t rows, int n, int cap, int start) {
+  size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= rows * width) return;
+  const int c = (int)(gid % width);
+  const size_t r = gid / width;
+  const float v = load_as_f32(x + r * stride + off, c);
+  rope[dst_row(r, n, cap, start) * width + c] = bf16_from_f64((double)v);
+}
+
+// ---------------------------------------------------------------- KIVI 2-bit
+
+// codes c = clamp(RNE((x - z) / s), 0, 3) in fp32 with s = (max - min) / 3,
+// z = min; c = 0 when s == 0.
+__device__ __forceinline__ uint32_t kivi_code(float x, float z, float s) {
+  if (!(s > 0.f)) return 0;
+  float q = rintf(__fdiv_rn(__fsub_rn(x, z), s));
+  q = fminf(fmaxf(q, 0.f), 3.f);
+  return (uint32_t)q;
+}
+
+// Keys: per channel over each 32-token group.  One thread per (row group, group
+// of 4 channels = one output byte per token).
+template <typename InT>
+__global__ void __launch_bounds__(256) kivi_keys_kernel(const InT* __restrict__ x, int d,
+                                                        uint8_t* __restrict__ codes,
+                                                        float* __restrict__ kscale,
+                                                        float* __restrict__ kzero, int bh_count,
+                                                        int n, int cap, int start) {
+  const int quads = d / 4, ngroups = n / 32;
+  size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (size_t)bh_count * ngroups * quads) return;
+  const int cq = (int)(gid % quads);
+  const size_t rest = gid / quads;
+  const int g = (int)(rest % ngroups);
+  const size_t bh = rest / ngroups;
+  const size_t r0 = bh * n + (size_t)g * 32;
+  float mn[4], mx[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) mn[j] = INFINITY, mx[j] = -INFINITY;
+  for (int t = 0; t < 32; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float v = load_as_f32(x + (r0 + t) * d, 4 * cq + j);
+      mn[j] = fminf(mn[j], v);
+      mx[j] = fmaxf(mx[j], v);
+    }
+  float s[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) s[j] = __fdiv_rn(__fsub_rn(mx[j], mn[j]), 3.0f);
+  for (int t = 0; t < 32; ++t) {
+    uint32_t byte = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      byte |= kivi_code(load_as_f32(x + (r0 + t) * d, 4 * cq + j), mn[j], s[j]) << (2 * j);
+    codes[(bh * cap + start + (size_t)g * 32 + t) * quads + cq] = (uint8_t)byte;
+  }
+  const size_t meta = (bh * (cap / 32) + start / 32 + g) * (size_t)d + 4 * cq;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    kscale[meta + j] = s[j];
+    kzero[meta + j] = mn[j];
+  }
+}
+
+// Values: per token over each 32-channel group.  One thread per (token, group).
+template <typename InT>
+__global__ void __launch_bounds__(256) kivi_values_kernel(const InT* __restrict__ x, int d,
+                                                          uint8_t* __restrict__ codes,
+                                                          float* __restrict__ vscale,
+                                                          float* __restrict__ vzero, size_t rows,
+                                                          int n, int cap, int start) {
+  const int groups = d / 32;
+  size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= rows * groups) return;
+  const int g = (int)(gid % groups);
+  const size_t r = gid / groups;
+  const InT* src = x + r * d + g * 32;
+  float mn = INFINITY, mx = -INFINITY;
+  for (int i = 0; i < 32; ++i) {
+    float v = load_as_f32(src, i);
+    mn = fminf(mn, v);
+    mx = fmaxf(mx, v);
+  }
+  const float s = __fdiv_rn(__fsub_rn(mx, mn), 3.0f);
+  unsigned long long packed = 0;
+  for (int i = 0; i < 32; ++i) packed |= (unsigned long long)kivi_code(load_as_f32(src, i), mn, s) << (2 * i);
+  const size_t dr = dst_row(r, n, cap, start);
+  *reinterpret_cast<unsigned long long*>(codes + dr * (d / 4) + g * 8) = packed;
+  vscale[dr * groups + g] = s;
+  vzero[dr * groups + g] = mn;
+}
+
+// ---------------------------------------------------------------- QJL sign sketch (MFMA)
+
+// Split x into bf16 parts whose sum is exactly x (1 part for bf16 input, 3 for fp32).
+template <typename InT>
+struct Bf16Parts;
+template <>
+struct Bf16Parts<uint16_t> {
+  static constexpr int N = 1;
+  __device__ static void get(const uint16_t* p, uint16_t out[N][8]) {
+    uint4 raw = *reinterpret_cast<const uint4*>(p);
+    const uint16_t* h = reinterpret_cast<const uint16_t*>(&raw);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[0][i] = h[i];
+  }
+};
+template <>
+struct Bf16Parts<float> {
+  static constexpr int N = 3;
+  __device__ static void get(const float* p, uint16_t out[N][8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float v = p[i];
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        uint32_t hi = __float_as_uint(v) & 0xFFFF0000u;  // truncation: exact top part
+        out[k][i] = (uint16_t)(hi >> 16);
+        v = v - __uint_as_float(hi);                      // exact remainder
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint16_t (&h)[8]) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = __builtin_bit_cast(__bf16, h[i]);
+  return r;
+}
+
+constexpr int kSPad = 136;  // LDS row pitch (elements) of the staged 128 x 128 bf16 matrix
+
+// sketch bit i of a token = [(S k)_i >= 0], plus the token's fp16 norm.
+// A wave takes 16 tokens: A = K rows (bf16, or exact bf16 parts of fp32),
+// B = S^T from LDS, fp32 accumulation on v_mfma_f32_16x16x32_bf16.  Where
+// |y| is within a conservative bound of the fp32 accumulation error
+// (2^-14 * ||S_i|| * ||k||), the sign is recomputed exactly in fp64, so the
+// stored bits equal the exact-arithmetic signs.
+template <typename InT>
+__global__ void __launch_bounds__(256) qjl_keys_kernel(const InT* __restrict__ x,
+                                                       const float* __restrict__ proj,
+                                                       uint8_t* __restrict__ sketch,
+                                                       uint16_t* __restrict__ knorm, size_t rows,
+                                                       int n, int cap, int start) {
+  __shared__ __align__(16) uint16_t S_lds[128 * kSPad];
+  __shared__ float srow_norm[128];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < 128 * 128; e += 256) {
+    const float v = proj[e];
+    S_lds[(e >> 7) * kSPad + (e & 127)] = (uint16_t)(__float_as_uint(v) >> 16);  // bf16-valued
+  }
+  if (tid < 128) {
+    float acc = 0.f;
+    for (int j = 0; j < 128; ++j) acc = fmaf(proj[tid * 128 + j], proj[tid * 128 + j], acc);
+    srow_norm[tid] = sqrtf(acc) * 1.0001f;
+  }
+  __syncthreads();
+  constexpr int NP = Bf16Parts<InT>::N;
+  const int col = lane & 15, kq = lane >> 4;
+  for (size_t base = ((size_t)blockIdx.x * 4 + wave) * 16; base < rows; base += (size_t)gridDim.x * 64) {
+    const size_t my_row = base + col;  // A-operand token of this lane
+    const bool valid = my_row < rows;
+    f32x4 acc[8];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    double ss = 0.0;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      uint16_t part[NP][8];
+      if (valid) {
+        Bf16Parts<InT>::get(x + my_row * 128 + ks * 32 + kq * 8, part);
+      } else {
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) part[p][i] = 0;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        double v = 0.0;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) v += (double)bf16_to_f32(part[p][i]);
+        ss = fma(v, v, ss);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const uint16_t* srow = &S_lds[(nt * 16 + col) * kSPad + ks * 32 + kq * 8];
+        uint4 braw = *reinterpret_cast<const uint4*>(srow);
+        uint16_t bh[8];
+        *reinterpret_cast<uint4*>(bh) = braw;
+        bf16x8 b = as_bf16x8(bh);
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(part[p]), b, acc[nt], 0, 0, 0);
+      }
+    }
+    // token norms: sum the four k-quarters held by lanes col, col+16, col+32, col+48
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    const double nrm = sqrt(ss);  // lane holds the norm of token `col`
+    unsigned long long ballots[8][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = kq * 4 + i;  // C-operand rows held by this lane
+      const double tn = __shfl(nrm, tok);
+      const size_t trow = base + tok;
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const int srow_i = nt * 16 + col;
+        float y = acc[nt][i];
+        bool bit = y >= 0.f;
+        const float bound = (NP == 1 ? 0x1p-14f : 0x1p-12f) * srow_norm[srow_i] * (float)tn;
+        if (fabsf(y) <= bound && trow < rows) {
+          double e = 0.0;
+          for (int j = 0; j < 128; ++j)
+            e = fma((double)bf16_to_f32(S_lds[srow_i * kSPad + j]), (double)load_as_f32(x + trow * 128, j), e);
+          bit = e >= 0.0;
+        }
+        ballots[nt][i] = __ballot(bit);
+      }
+    }
+    if (lane < 16 && base + lane < rows) {
+      const int q = lane >> 2, i = lane & 3;
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t lo = (uint32_t)(ballots[2 * j][i] >> (16 * q)) & 0xFFFFu;
+        uint32_t hi = (uint32_t)(ballots[2 * j + 1][i] >> (16 * q)) & 0xFFFFu;
+        w[j] = lo | (hi << 16);
+      }
+      const size_t dr = dst_row(base + lane, n, cap, start);
+      *reinterpret_cast<uint4*>(sketch + dr * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+      knorm[dr] = f16_from_f64_nonneg(nrm);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- TurboQuant (fp64 MFMA)
+
+// Keys (WITH_SKETCH) or values: n = ||x||; u = R x / n; idx = #{thresholds <= u};
+// keys also r = u - levels[idx], gamma = ||r||, sketch = [S r >= 0].  Both
+// products run on v_mfma_f64_16x16x4f64: R and S are bf16-valued and x is
+// bf16/fp32, so each product term is exact and the fp64 sums match the
+// exact-arithmetic decisions except at exact ties.
+template <typename InT, bool WITH_SKETCH>
+__global__ void __launch_bounds__(256) turbo_kernel(const InT* __restrict__ x,
+                                                    const float* __restrict__ rot,
+                                                    const float* __restrict__ proj,
+                                                    const float* __restrict__ levels,
+                                                    const float* __restrict__ thresh,
+                                                    uint8_t* __restrict__ codes,
+                                                    uint8_t* __restrict__ sketch,
+                                                    uint16_t* __restrict__ norm_out,
+                                                    uint16_t* __restrict__ rnorm_out, size_t rows,
+                                                    int n, int cap, int start) {
+  __shared__ __align__(16) uint16_t R_lds[128 * kSPad];
+  __shared__ __align__(16) uint16_t S_lds[WITH_SKETCH ? 128 * kSPad : 1];
+  __shared__ double scratch[4][16 * 129];  // per wave: x tile (as double), then the residual
+  __shared__ uint8_t idx_lds[4][16 * 128];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < 128 * 128; e += 256) {
+    R_lds[(e >> 7) * kSPad + (e & 127)] = (uint16_t)(__float_as_uint(rot[e]) >> 16);
+    if (WITH_SKETCH) S_lds[(e >> 7) * kSPad + (e & 127)] = (uint16_t)(__float_as_uint(proj[e]) >> 16);
+  }
+  __syncthreads();
+  const double t0 = thresh[0], t1 = thresh[1], t2 = thresh[2];
+  const double lv0 = levels[0], lv1 = levels[1], lv2 = levels[2], lv3 = levels[3];
+  double* xs = scratch[wave];
+  const int col = lane & 15, kq = lane >> 4;
+  for (size_t base = ((size_t)blockIdx.x * 4 + wave) * 16; base < rows; base += (size_t)gridDim.x * 64) {
+    // stage 16 tokens x 128 as double, zero past the last row
+    for (int e = lane; e < 16 * 128; e += 64) {
+      const int tk = e >> 7, c = e & 127;
+      xs[tk * 129 + c] = (base + tk < rows) ? (double)load_as_f32(x + (base + tk) * 128, c) : 0.0;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    // norms: lane `col` sums its token over the lane quarter kq, then reduce
+    double ss = 0.0;
+    for (int c = kq * 32; c < kq * 32 + 32; ++c) ss = fma(xs[col * 129 + c], xs[col * 129 + c], ss);
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    const double nrm = sqrt(ss);
+    // Y = X R^T: A[m = token][k] = x, B[k][n = output row] = R[n][k]
+    f64x4 acc[8];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) acc[nt] = f64x4{0.0, 0.0, 0.0, 0.0};
+    for (int ks = 0; ks < 32; ++ks) {
+      const double a = xs[col * 129 + ks * 4 + kq];
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const double b = (double)bf16_to_f32(R_lds[(nt * 16 + col) * kSPad + ks * 4 + kq]);
+        acc[nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[nt], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    // quantise: lane holds y[token kq*4+i][row nt*16+col]
+    double rr[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = kq * 4 + i;
+      const double tn = __shfl(nrm, tok);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const double u = tn > 0.0 ? __ddiv_rn(acc[nt][i], tn) : 0.0;
+        const int id = (u >= t0) + (u >= t1) + (u >= t2);
+        idx_lds[wave][tok * 128 + nt * 16 + col] = (uint8_t)id;
+        if (WITH_SKETCH) {
+          const double lv = id == 0 ? lv0 : id == 1 ? lv1 : id == 2 ? lv2 : lv3;
+          const double r = u - lv;
+          xs[tok * 129 + nt * 16 + col] = r;  // residual replaces x (same wave only)
+          rr[i] = fma(r, r, rr[i]);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    // pack the 2-bit codes: lane < 16 owns token `lane`
+    if (lane < 16 && base + lane < rows) {
+      const size_t dr = dst_row(base + lane, n, cap, start);
+      const uint8_t* ip = &idx_lds[wave][lane * 128];
+      uint32_t w[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int b = 0; b < 16; ++b) v |= (uint32_t)ip[j * 16 + b] << (2 * b);
+        w[j] = v;
+      }
+      uint4* dst = reinterpret_cast<uint4*>(codes + dr * 32);
+      dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+      norm_out[dr] = f16_from_f64_nonneg(nrm);
+    }
+    if (WITH_SKETCH) {
+      // gamma^2 per token: rows are spread over the 16 lanes of each quarter
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        double v = rr[i];
+        v += __shfl_xor(v, 1);
+        v += __shfl_xor(v, 2);
+        v += __shfl_xor(v, 4);
+        v += __shfl_xor(v, 8);
+        rr[i] = v;
+      }
+      // S r: A[m = token][k] = r, B[k][n = sketch row] = S[n][k]
+      f64x4 sacc[8];
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) sacc[nt] = f64x4{0.0, 0.0, 0.0, 0.0};
+      for (int ks = 0; ks < 32; ++ks) {
+        const double a = xs[col * 129 + ks * 4 + kq];
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          const double b = (double)bf16_to_f32(S_lds[(nt * 16 + col) * kSPad + ks * 4 + kq]);
+          sacc[nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, sacc[nt], 0, 0, 0);
+        }
+      }
+      unsigned long long ballots[8][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) ballots[nt][i] = __ballot(sacc[nt][i] >= 0.0);
+      // lane (kq, col) holds gamma^2 of token kq*4+i in rr[i]; token `lane` needs it
+      double g2 = 0.0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        double v = __shfl(rr[i], (lane >> 2) * 16);
+        if ((lane & 3) == i) g2 = v;
+      }
+      if (lane < 16 && base + lane < rows) {
+        const int q = lane >> 2, i = lane & 3;
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t lo = (uint32_t)(ballots[2 * j][i] >> (16 * q)) & 0xFFFFu;
+          uint32_t hi = (uint32_t)(ballots[2 * j + 1][i] >> (16 * q)) & 0xFFFFu;
+          w[j] = lo | (hi << 16);
+        }
+        const size_t dr = dst_row(base + lane, n, cap, start);
+        *reinterpret_cast<uint4*>(sketch + dr * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+        rnorm_out[dr] = f16_from_f64_nonneg(sqrt(g2));
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+int blocks_for(size_t threads) { return (int)((threads + 255) / 256); }
+
+int persistent_blocks(size_t rows) {
+  size_t tiles = (rows + 63) / 64;
+  return (int)std::min<size_t>(tiles, 2048);
+}
+
+template <typename InT>
+int append_typed(const kv_cache* c, const InT* k, const InT* v, int start, int n, hipStream_t st) {
+  const kv_layout& L = c->layout;
+  const int d = L.head_dim, cap = L.capacity;
+  const int bh = L.batch * L.num_kv_heads;
+  const size_t rows = (size_t)bh * n;
+  auto* kc = static_cast<uint8_t*>(c->buf[KV_BUF_K_CODES]);
+  auto* ks = static_cast<uint16_t*>(c->buf[KV_BUF_K_SCALE]);
+  auto* vc = static_cast<uint8_t*>(c->buf[KV_BUF_V_CODES]);
+  auto* vs = static_cast<uint16_t*>(c->buf[KV_BUF_V_SCALE]);
+  switch (L.format) {
+    case KV_FMT_FP4:
+      fp4_append_kernel<InT><<<blocks_for(rows * (d / 16)), 256, 0, st>>>(k, d, d, kc, ks, rows, n, cap, start);
+      fp4_append_kernel<InT><<<blocks_for(rows * (d / 16)), 256, 0, st>>>(v, d, d, vc, vs, rows, n, cap, start);
+      break;
+    case KV_FMT_LATENT_FP4: {
+      const size_t stride = (size_t)d + L.rope_dim;
+      fp4_append_kernel<InT><<<blocks_for(rows * (d / 16)), 256, 0, st>>>(k, stride, d, kc, ks, rows, n, cap, start);
+      rope_copy_kernel<InT><<<blocks_for(rows * L.rope_dim), 256, 0, st>>>(
+          k, stride, d, L.rope_dim, static_cast<uint16_t*>(c->buf[KV_BUF_ROPE]), rows, n, cap, start);
+      break;
+    }
+    case KV_FMT_KIVI2:
+      kivi_keys_kernel<InT><<<blocks_for((size_t)bh * (n / 32) * (d / 4)), 256, 0, st>>>(
+          k, d, kc, static_cast<float*>(c->buf[KV_BUF_K_SCALE]), static_cast<float*>(c->buf[KV_BUF_K_ZERO]),
+          bh, n, cap, start);
+      kivi_values_kernel<InT><<<blocks_for(rows * (d / 32)), 256, 0, st>>>(
+          v, d, vc, static_cast<float*>(c->buf[KV_BUF_V_SCALE]), static_cast<float*>(c->buf[KV_BUF_V_ZERO]),
+          rows, n, cap, start);
+      break;
+    case KV_FMT_QJL1_FP4V:
+      qjl_keys_kernel<InT><<<persistent_blocks(rows), 256, 0, st>>>(
+          k, c->proj, static_cast<uint8_t*>(c->buf[KV_BUF_K_SKETCH]),
+          static_cast<uint16_t*>(c->buf[KV_BUF_K_NORM]), rows, n, cap, start);
+      fp4_append_kernel<InT><<<blocks_for(rows * (d / 16)), 256, 0, st>>>(v, d, d, vc, vs, rows, n, cap, start);
+      break;
+    case KV_FMT_TURBO:
+      turbo_kernel<InT, true><<<persistent_blocks(rows), 256, 0, st>>>(
+          k, c->rot, c->proj, c->lm_levels, c->lm_thresh, kc,
+          static_cast<uint8_t*>(c->buf[KV_BUF_K_SKETCH]), static_cast<uint16_t*>(c->buf[KV_BUF_K_NORM]),
+          static_cast<uint16_t*>(c->buf[KV_BUF_K_RNORM]), rows, n, cap, start);
+      turbo_kernel<InT, false><<<persistent_blocks(rows), 256, 0, st>>>(
+          v, c->rot, nullptr, c->lm_levels, c->lm_thresh, vc, nullptr,
+          static_cast<uint16_t*>(c->buf[KV_BUF_V_NORM]), nullptr, rows, n, cap, start);
+      break;
+    default:
+      return KV_EUNSUPPORTED;
+  }
+  return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
+}
+
+}  // namespace
+
+int launch_append(const kv_cache* c, const void* k, const void* v, int in_dtype, int start, int n_new,
+                  void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (in_dtype == KV_DT_F32)
+    return append_typed<float>(c, static_cast<const float*>(k), static_cast<const float*>(v), start, n_new, st);
+  return append_typed<uint16_t>(c, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), start,
+                                n_new, st);
+}
+
+}  // namespace kvq

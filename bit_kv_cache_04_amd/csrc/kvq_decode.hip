@@ -1,0 +1,361 @@
+// Decode attention over the packed cache: query preparation, split-context
+// attention with an online softmax, and the log-sum-exp merge of the splits.
+//
+// Every new token reads the whole cache (page "TurboQuant vs OSCAR vs EpiCache",
+// KV-cache memory bottleneck section), so the attention kernel streams packed
+// tiles once and never writes scores to memory (page "How TriAttention cut LLM
+// memory use 10x without losing accuracy": fused attention keeps the score
+// matrix on chip).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct DecodeArgs {
+  // cache
+  const uint8_t* k_codes;
+  const void* k_scale;
+  const float* k_zero;
+  const uint8_t* k_sketch;
+  const uint16_t* k_norm;
+  const uint16_t* k_rnorm;
+  const uint8_t* v_codes;
+  const void* v_scale;
+  const float* v_zero;
+  const uint16_t* v_norm;
+  const uint16_t* rope;
+  const float* levels;
+  int H, cap, d, rope_dim;
+  // query / output
+  const float* qv;  // prepared queries [B][Hq][QW]
+  int Hq, G, head_blocks, hb_size;
+  const int32_t* seq_lens;
+  int max_len;
+  float scale_log2;  // softmax scale * log2(e)
+  float kappa;       // sqrt(pi/2) / m
+  float* part;       // [B][Hq][splits][DV + 2]: m (log2 units), l, o[DV]
+  int splits, per_split;
+};
+
+// ---------------------------------------------------------------- per-format element access
+
+// Virtual key element c of token (bh, t); the logit is <prepared q, key>.
+template <int FMT>
+__device__ __forceinline__ float key_elem(const DecodeArgs& a, size_t bh, int t, int c) {
+  const size_t row = bh * a.cap + t;
+  if constexpr (FMT == KV_FMT_FP4 || FMT == KV_FMT_LATENT_FP4) {
+    if (FMT == KV_FMT_LATENT_FP4 && c >= a.d) return bf16_to_f32(a.rope[row * a.rope_dim + (c - a.d)]);
+    const uint32_t nib = (a.k_codes[row * (a.d / 2) + c / 2] >> (4 * (c & 1))) & 15u;
+    const float s = bf16_to_f32(static_cast<const uint16_t*>(a.k_scale)[row * (a.d / 16) + c / 16]);
+    return e2m1_value(nib) * s;
+  } else if constexpr (FMT == KV_FMT_KIVI2) {
+    const uint32_t code = (a.k_codes[row * (a.d / 4) + c / 4] >> (2 * (c & 3))) & 3u;
+    const size_t m = (bh * (a.cap / 32) + t / 32) * a.d + c;
+    return fmaf((float)code, static_cast<const float*>(a.k_scale)[m], a.k_zero[m]);
+  } else if constexpr (FMT == KV_FMT_TURBO) {
+    const float n = f16_to_f32(a.k_norm[row]);
+    if (c < 128) {
+      const uint32_t code = (a.k_codes[row * 32 + c / 4] >> (2 * (c & 3))) & 3u;
+      return n * a.levels[code];
+    }
+    const int i = c - 128;
+    const uint32_t bit = (a.k_sketch[row * 16 + i / 8] >> (i & 7)) & 1u;
+    const float g = f16_to_f32(a.k_rnorm[row]);
+    return (bit ? 1.f : -1.f) * (a.kappa * g * n);
+  } else {  // QJL1
+    const float n = f16_to_f32(a.k_norm[row]);
+    const uint32_t bit = (a.k_sketch[row * 16 + c / 8] >> (c & 7)) & 1u;
+    return (bit ? 1.f : -1.f) * (a.kappa * n);
+  }
+}
+
+// Value element c of token (bh, t) (TURBO: in the rotated space, times n_v).
+template <int FMT>
+__device__ __forceinline__ float value_elem(const DecodeArgs& a, size_t bh, int t, int c) {
+  const size_t row = bh * a.cap + t;
+  if constexpr (FMT == KV_FMT_FP4 || FMT == KV_FMT_QJL1_FP4V) {
+    const uint32_t nib = (a.v_codes[row * (a.d / 2) + c / 2] >> (4 * (c & 1))) & 15u;
+    const float s = bf16_to_f32(static_cast<const uint16_t*>(a.v_scale)[row * (a.d / 16) + c / 16]);
+    return e2m1_value(nib) * s;
+  } else if constexpr (FMT == KV_FMT_KIVI2) {
+    const uint32_t code = (a.v_codes[row * (a.d / 4) + c / 4] >> (2 * (c & 3))) & 3u;
+    const size_t m = row * (a.d / 32) + c / 32;
+    return fmaf((float)code, static_cast<const float*>(a.v_scale)[m], a.v_zero[m]);
+  } else if constexpr (FMT == KV_FMT_TURBO) {
+    const uint32_t code = (a.v_codes[row * 32 + c / 4] >> (2 * (c & 3))) & 3u;
+    return f16_to_f32(a.v_norm[row]) * a.levels[code];
+  } else {
+    return 0.f;  // latent values alias the key tile
+  }
+}
+
+// ---------------------------------------------------------------- split-context attention
+
+// One workgroup per (split, KV head x head block, sequence).  Each token tile is
+// dequantised into LDS once and used by every query head of the block; the
+// running max / sum per head implement the online softmax.
+template <int FMT, int DK, int DV, int TT, int HB>
+__global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
+  constexpr bool kAlias = (FMT == KV_FMT_LATENT_FP4);
+  constexpr int NT = 256;
+  constexpr int OPT = (HB * DV + NT - 1) / NT;
+  __shared__ float qs[HB][DK];
+  __shared__ float ks[TT][DK + 1];
+  __shared__ float vs[kAlias ? 1 : TT][kAlias ? 1 : DV + 1];
+  __shared__ float ss[HB][TT];
+  __shared__ float ms[HB], ls[HB], al[HB];
+
+  const int tid = threadIdx.x;
+  const int split = blockIdx.x;
+  const int h = blockIdx.y / a.head_blocks, hb = blockIdx.y % a.head_blocks;
+  const int b = blockIdx.z;
+  const int hq0 = h * a.G + hb * a.hb_size;
+  const int nh = min(a.hb_size, a.G - hb * a.hb_size);
+  const size_t bh = (size_t)b * a.H + h;
+  const int L = min(min(a.seq_lens[b], a.max_len), a.cap);
+  const int t_begin = split * a.per_split;
+  const int t_end = min(L, t_begin + a.per_split);
+
+  for (int e = tid; e < HB * DK; e += NT) {
+    const int hh = e / DK, c = e % DK;
+    qs[hh][c] = hh < nh ? a.qv[((size_t)b * a.Hq + hq0 + hh) * DK + c] : 0.f;
+  }
+  if (tid < HB) {
+    ms[tid] = -INFINITY;
+    ls[tid] = 0.f;
+  }
+  float o[OPT];
+#pragma unroll
+  for (int j = 0; j < OPT; ++j) o[j] = 0.f;
+  __syncthreads();
+
+  for (int t0 = t_begin; t0 < t_end; t0 += TT) {
+    const int nt = min(TT, t_end - t0);
+    for (int e = tid; e < TT * DK; e += NT) {
+      const int t = e / DK, c = e % DK;
+      ks[t][c] = t < nt ? key_elem<FMT>(a, bh, t0 + t, c) : 0.f;
+    }
+    if constexpr (!kAlias) {
+      for (int e = tid; e < TT * DV; e += NT) {
+        const int t = e / DV, c = e % DV;
+        vs[t][c] = t < nt ? value_elem<FMT>(a, bh, t0 + t, c) : 0.f;
+      }
+    }
+    __syncthreads();
+    for (int p = tid; p < HB * TT; p += NT) {
+      const int hh = p / TT, t = p % TT;
+      float s = 0.f;
+      for (int c = 0; c < DK; ++c) s = fmaf(qs[hh][c], ks[t][c], s);
+      ss[hh][t] = (t < nt && hh < nh) ? s * a.scale_log2 : -INFINITY;
+    }
+    __syncthreads();
+    if (tid < nh) {
+      float mx = -INFINITY;
+      for (int t = 0; t < nt; ++t) mx = fmaxf(mx, ss[tid][t]);
+      const float mnew = fmaxf(ms[tid], mx);
+      const float alpha = exp2f(ms[tid] - mnew);
+      float sum = 0.f;
+      for (int t = 0; t < TT; ++t) {
+        const float p = t < nt ? exp2f(ss[tid][t] - mnew) : 0.f;
+        ss[tid][t] = p;
+        sum += p;
+      }
+      ls[tid] = ls[tid] * alpha + sum;
+      ms[tid] = mnew;
+      al[tid] = alpha;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < OPT; ++j) {
+      const int e = tid + j * NT;
+      if (e < HB * DV) {
+        const int hh = e / DV, c = e % DV;
+        if (hh < nh) {
+          float acc = o[j] * al[hh];
+          for (int t = 0; t < nt; ++t) acc = fmaf(ss[hh][t], kAlias ? ks[t][c] : vs[t][c], acc);
+          o[j] = acc;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // partial results of this split
+#pragma unroll
+  for (int j = 0; j < OPT; ++j) {
+    const int e = tid + j * NT;
+    if (e < HB * DV) {
+      const int hh = e / DV, c = e % DV;
+      if (hh < nh) {
+        float* p = a.part + (((size_t)b * a.Hq + hq0 + hh) * a.splits + split) * (DV + 2);
+        p[2 + c] = o[j];
+        if (c == 0) {
+          p[0] = ms[hh];
+          p[1] = ls[hh];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- query preparation
+
+// Prepared fp32 query: q itself, or [R q, S R q] (TURBO), or S q (QJL1).
+template <typename QT>
+__global__ void __launch_bounds__(128) prep_query_kernel(const QT* __restrict__ q, int qw_in, int qw_out,
+                                                         int fmt, const float* __restrict__ rot,
+                                                         const float* __restrict__ proj,
+                                                         float* __restrict__ out) {
+  __shared__ float qin[640];
+  __shared__ float qrot[128];
+  const size_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  for (int c = tid; c < qw_in; c += 128) qin[c] = load_as_f32(q + row * qw_in, c);
+  __syncthreads();
+  float* dst = out + row * qw_out;
+  if (fmt == KV_FMT_TURBO) {
+    float acc = 0.f;
+    for (int j = 0; j < 128; ++j) acc = fmaf(rot[tid * 128 + j], qin[j], acc);
+    qrot[tid] = acc;
+    dst[tid] = acc;
+    __syncthreads();
+    float acc2 = 0.f;
+    for (int j = 0; j < 128; ++j) acc2 = fmaf(proj[tid * 128 + j], qrot[j], acc2);
+    dst[128 + tid] = acc2;
+  } else if (fmt == KV_FMT_QJL1_FP4V) {
+    float acc = 0.f;
+    for (int j = 0; j < 128; ++j) acc = fmaf(proj[tid * 128 + j], qin[j], acc);
+    dst[tid] = acc;
+  } else {
+    for (int c = tid; c < qw_out; c += 128) dst[c] = qin[c];
+  }
+}
+
+// ---------------------------------------------------------------- merge
+
+// out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.  TURBO maps
+// the rotated output back with R^T.  An all-empty row (no tokens) writes zeros.
+__global__ void __launch_bounds__(256) merge_kernel(const float* __restrict__ part, int splits, int dv,
+                                                    int fmt, const float* __restrict__ rot,
+                                                    float* __restrict__ out) {
+  __shared__ float w[1024];
+  __shared__ float ov[512];
+  __shared__ float inv_l;
+  const size_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* p = part + row * (size_t)splits * (dv + 2);
+  if (tid == 0) {
+    float M = -INFINITY;
+    for (int s = 0; s < splits; ++s) M = fmaxf(M, p[(size_t)s * (dv + 2)]);
+    float l = 0.f;
+    for (int s = 0; s < splits; ++s) {
+      const float ms = p[(size_t)s * (dv + 2)];
+      const float ws = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+      w[s] = ws;
+      l += ws * p[(size_t)s * (dv + 2) + 1];
+    }
+    inv_l = l > 0.f ? 1.f / l : 0.f;
+  }
+  __syncthreads();
+  for (int c = tid; c < dv; c += 256) {
+    float acc = 0.f;
+    for (int s = 0; s < splits; ++s)
+      if (w[s] != 0.f) acc = fmaf(w[s], p[(size_t)s * (dv + 2) + 2 + c], acc);
+    ov[c] = acc * inv_l;
+  }
+  __syncthreads();
+  float* dst = out + row * dv;
+  if (fmt == KV_FMT_TURBO) {
+    for (int c = tid; c < dv; c += 256) {
+      float acc = 0.f;
+      for (int j = 0; j < dv; ++j) acc = fmaf(rot[j * dv + c], ov[j], acc);
+      dst[c] = acc;
+    }
+  } else {
+    for (int c = tid; c < dv; c += 256) dst[c] = ov[c];
+  }
+}
+
+template <int FMT, int DK, int DV, int HB>
+void launch_split(const DecodeArgs& a, int B, hipStream_t st) {
+  dim3 grid(a.splits, a.H * a.head_blocks, B);
+  decode_split_kernel<FMT, DK, DV, 32, HB><<<grid, 256, 0, st>>>(a);
+}
+
+}  // namespace
+
+int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads, const int32_t* seq_lens,
+                  int max_seq_len, float scale, float* out, void* ws, const SplitPlan& plan,
+                  const DecodeWorkspace& wsl, void* ev_begin, void* ev_end, void* stream) {
+  const kv_layout& L = c->layout;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* wsb = static_cast<char*>(ws);
+  float* qv = reinterpret_cast<float*>(wsb + wsl.qprep_off);
+  float* part = reinterpret_cast<float*>(wsb + wsl.part_off);
+  const int B = L.batch;
+  const int rows = B * num_q_heads;
+  const int qw_in = query_width(&L), qw_out = prepared_query_width(&L);
+  if (q_dtype == KV_DT_F32)
+    prep_query_kernel<float><<<rows, 128, 0, st>>>(static_cast<const float*>(q), qw_in, qw_out, L.format,
+                                                   c->rot, c->proj, qv);
+  else
+    prep_query_kernel<uint16_t><<<rows, 128, 0, st>>>(static_cast<const uint16_t*>(q), qw_in, qw_out,
+                                                      L.format, c->rot, c->proj, qv);
+
+  DecodeArgs a{};
+  a.k_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_K_CODES]);
+  a.k_scale = c->buf[KV_BUF_K_SCALE];
+  a.k_zero = static_cast<const float*>(c->buf[KV_BUF_K_ZERO]);
+  a.k_sketch = static_cast<const uint8_t*>(c->buf[KV_BUF_K_SKETCH]);
+  a.k_norm = static_cast<const uint16_t*>(c->buf[KV_BUF_K_NORM]);
+  a.k_rnorm = static_cast<const uint16_t*>(c->buf[KV_BUF_K_RNORM]);
+  a.v_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_V_CODES]);
+  a.v_scale = c->buf[KV_BUF_V_SCALE];
+  a.v_zero = static_cast<const float*>(c->buf[KV_BUF_V_ZERO]);
+  a.v_norm = static_cast<const uint16_t*>(c->buf[KV_BUF_V_NORM]);
+  a.rope = static_cast<const uint16_t*>(c->buf[KV_BUF_ROPE]);
+  a.levels = c->lm_levels;
+  a.H = L.num_kv_heads;
+  a.cap = L.capacity;
+  a.d = L.head_dim;
+  a.rope_dim = L.rope_dim;
+  a.qv = qv;
+  a.Hq = num_q_heads;
+  a.G = num_q_heads / L.num_kv_heads;
+  a.hb_size = std::min(a.G, 16);
+  a.head_blocks = (a.G + a.hb_size - 1) / a.hb_size;
+  a.seq_lens = seq_lens;
+  a.max_len = max_seq_len;
+  a.scale_log2 = scale * kLog2e;
+  a.kappa = (float)(1.2533141373155002512 / (double)(L.qjl_m > 0 ? L.qjl_m : 1));
+  a.part = part;
+  a.splits = plan.splits;
+  a.per_split = plan.tokens_per_split;
+
+  if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), st) != hipSuccess) return KV_EDEVICE;
+  switch (L.format) {
+    case KV_FMT_KIVI2:
+      if (L.head_dim == 64) launch_split<KV_FMT_KIVI2, 64, 64, 16>(a, B, st);
+      else launch_split<KV_FMT_KIVI2, 128, 128, 16>(a, B, st);
+      break;
+    case KV_FMT_FP4:
+      if (L.head_dim == 64) launch_split<KV_FMT_FP4, 64, 64, 16>(a, B, st);
+      else launch_split<KV_FMT_FP4, 128, 128, 16>(a, B, st);
+      break;
+    case KV_FMT_TURBO: launch_split<KV_FMT_TURBO, 256, 128, 16>(a, B, st); break;
+    case KV_FMT_QJL1_FP4V: launch_split<KV_FMT_QJL1_FP4V, 128, 128, 16>(a, B, st); break;
+    case KV_FMT_LATENT_FP4: launch_split<KV_FMT_LATENT_FP4, 576, 512, 16>(a, B, st); break;
+    default: return KV_EUNSUPPORTED;
+  }
+  if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess) return KV_EDEVICE;
+  merge_kernel<<<rows, 256, 0, st>>>(part, plan.splits, L.head_dim, L.format, c->rot, out);
+  return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
+}
+
+}  // namespace kvq

@@ -1,0 +1,94 @@
+// Device-side helpers for the libkvq kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+// ---------------------------------------------------------------- 16-bit floats
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Nearest bf16 of a finite double, ties to even; returns the bit pattern.
+__device__ __forceinline__ uint16_t bf16_from_f64(double x) {
+  if (x == 0.0) return (uint16_t)(__double_as_longlong(x) >> 48);  // keeps -0
+  double a = fabs(x);
+  float f;
+  if (a < 0x1p-126) {
+    f = (float)(rint(a * 0x1p133) * 0x1p-133);
+  } else {
+    unsigned long long u = (unsigned long long)__double_as_longlong(a);
+    unsigned long long lsb = (u >> 45) & 1ull;
+    u += (1ull << 44) - 1ull + lsb;
+    u &= ~((1ull << 45) - 1ull);
+    f = (float)__longlong_as_double((long long)u);
+  }
+  uint16_t bits = (uint16_t)(__float_as_uint(f) >> 16);
+  return x < 0 ? (uint16_t)(bits | 0x8000u) : bits;
+}
+
+// Nearest fp16 of a non-negative finite double (a norm), ties to even; bit pattern.
+__device__ __forceinline__ uint16_t f16_from_f64_nonneg(double a) {
+  if (a == 0.0) return 0;
+  if (a < 0x1p-14) {  // subnormal: spacing 2^-24
+    double q = rint(a * 0x1p24);
+    return (uint16_t)q;  // q <= 1024; 1024 is the smallest normal's pattern 0x0400
+  }
+  unsigned long long u = (unsigned long long)__double_as_longlong(a);
+  unsigned long long lsb = (u >> 42) & 1ull;
+  u += (1ull << 41) - 1ull + lsb;
+  u &= ~((1ull << 42) - 1ull);
+  double r = __longlong_as_double((long long)u);
+  if (r > 65504.0) return 0x7C00;  // +inf
+  int e = (int)((u >> 52) & 0x7FF) - 1023;           // 2^e <= r < 2^(e+1), e >= -14
+  unsigned frac = (unsigned)((u >> 42) & 0x3FF);
+  return (uint16_t)(((e + 15) << 10) | frac);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// ---------------------------------------------------------------- E2M1
+
+// E2M1 magnitudes by code 0..7.
+__device__ __forceinline__ float e2m1_mag(uint32_t i) {
+  // 0, 0.5, 1, 1.5, 2, 3, 4, 6
+  const float t[8] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
+  return t[i & 7];
+}
+
+__device__ __forceinline__ float e2m1_value(uint32_t nib) {
+  float m = e2m1_mag(nib);
+  return (nib & 8) ? -m : m;
+}
+
+// Nibble of x with scale s > 0: nearest value to |x|/s, exact ties to the even
+// code, saturating at 6, sign bit from x.  The midpoints times s are exact in
+// fp32 (at most 11 significant bits), so every comparison is exact.
+__device__ __forceinline__ uint32_t e2m1_encode(float x, float s) {
+  const float ax = fabsf(x);
+  uint32_t idx = 0;
+  idx += (ax > 0.25f * s);
+  idx += (ax >= 0.75f * s);  // tie between codes 1 and 2 goes up (to even 2)
+  idx += (ax > 1.25f * s);
+  idx += (ax >= 1.75f * s);
+  idx += (ax > 2.5f * s);
+  idx += (ax >= 3.5f * s);
+  idx += (ax > 5.0f * s);
+  return idx | (__float_as_uint(x) >> 31 << 3);
+}
+
+// ---------------------------------------------------------------- input loads
+
+template <typename T>
+__device__ __forceinline__ float load_as_f32(const T* p, size_t i);
+template <>
+__device__ __forceinline__ float load_as_f32<float>(const float* p, size_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p, size_t i) {
+  return bf16_to_f32(p[i]);
+}
+
+}  // namespace kvq

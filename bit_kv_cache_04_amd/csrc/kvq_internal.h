@@ -1,0 +1,52 @@
+// Internal declarations shared by the host translation units of libkvq.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "kvq.h"
+
+namespace kvq {
+
+constexpr int kFp4Group = 16;
+constexpr int kKiviGroup = 32;
+constexpr int kQjlM = 128;
+constexpr int kLmBits = 2;
+
+// KV_OK if the layout is one this library supports, else the status to return.
+int check_layout(const kv_layout* L);
+// KV_OK if every buffer and constant the format needs is non-NULL.
+int check_cache(const kv_cache* c);
+
+// Width of the query a caller passes (d, or d + rope for the latent format).
+int query_width(const kv_layout* L);
+// Width of the prepared fp32 query the attention kernel reads: the query itself,
+// [R q, S R q] for TURBO, S q for QJL1.
+int prepared_query_width(const kv_layout* L);
+// Width of the attention output / value vector.
+int value_width(const kv_layout* L);
+
+// Context splits per (sequence, KV head) and the tokens each split covers.
+struct SplitPlan {
+  int splits;
+  int tokens_per_split;
+};
+SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int max_seq_len, int requested);
+
+// Workspace of a decode call: prepared queries, then per-split partial results
+// (running max, running sum, unnormalised output) — offsets in bytes.
+struct DecodeWorkspace {
+  size_t qprep_off, part_off, total;
+};
+DecodeWorkspace decode_workspace(const kv_layout* L, int num_q_heads, int splits);
+
+// Device launchers (defined in the HIP translation units).  Arguments are
+// validated by the caller.
+int launch_append(const kv_cache* c, const void* k, const void* v, int in_dtype, int start,
+                  int n_new, void* stream);
+int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads,
+                  const int32_t* seq_lens, int max_seq_len, float scale, float* out, void* ws,
+                  const SplitPlan& plan, const DecodeWorkspace& wsl, void* ev_begin, void* ev_end,
+                  void* stream);
+
+}  // namespace kvq

@@ -1,0 +1,223 @@
+/*
+ * kvq.h - low-bit KV-cache append and single-query decode attention (C ABI).
+ *
+ * The problem, as the pages state it (page "TurboQuant vs OSCAR vs EpiCache:
+ * the battle over KV-cache compression", section on the KV-cache memory
+ * bottleneck): a decoder stores one key and one value vector per token, per
+ * layer, per KV head; every newly generated token then reads the whole cache
+ * from HBM, so decoding is bound by memory bandwidth, and the bytes stored per
+ * token are layers x KV heads x head dim x 2 tensors x bytes per element.
+ * This library stores K/V in packed low-bit formats and runs decode attention
+ * directly on the packed bytes:
+ *
+ *   kv_quant_append      write new tokens' K/V into a packed cache (one layer)
+ *   kv_decode_attention  one query token per sequence attends over its cache
+ *   kv_bytes_per_token   stored bytes per token for a layout and layer count
+ *
+ * Formats (each cited where it is defined):
+ *   KV_FMT_KIVI2      2-bit asymmetric; keys per channel over 32-token groups,
+ *                     values per token over 32-channel groups, fp32 scale and
+ *                     zero (page "TurboQuant vs OSCAR vs EpiCache", section
+ *                     "quantization frontiers", KIVI paragraph).
+ *   KV_FMT_FP4        E2M1 nibbles with one bf16 scale per 16 channels, for K
+ *                     and V (page "How DeepSeek-V4.1-Flash cut KV-cache storage
+ *                     by 4x via CSA2", section on numerical precision).
+ *   KV_FMT_TURBO      keys: seeded Haar rotation, 2-bit Gaussian Lloyd-Max
+ *                     codes of the rotated unit vector, 1-bit QJL sign sketch
+ *                     of the residual, fp16 norm and fp16 residual norm; values:
+ *                     rotation + 2-bit Lloyd-Max + fp16 norm (page "TurboQuant
+ *                     vs OSCAR vs EpiCache", section "quantization frontiers",
+ *                     stages one and two).
+ *   KV_FMT_QJL1_FP4V  keys: 1-bit QJL sign sketch + fp16 norm; values: FP4.
+ *   KV_FMT_LATENT_FP4 one 512-wide latent per token shared by all query heads,
+ *                     stored FP4, plus a 64-wide RoPE key kept bf16 (page "How
+ *                     DeepSeek-V4.1-Flash cut KV-cache storage by 4x via
+ *                     CSA2", CSA2 section: a 512-d latent shared across heads
+ *                     with a 64-d RoPE part).
+ *   KV_FMT_BF16       uncompressed reference for kv_bytes_per_token only.
+ *
+ * Packed layout: arrays are C-contiguous and token-major; sequence b, KV head
+ * h, token t index ((b*H + h)*capacity + t).  Bit order is least significant
+ * first: FP4 channel 2j in the low nibble of byte j; 2-bit channel 4j+i in
+ * bits [2i+1:2i] of byte j; sketch row 8j+i in bit i of byte j.  bf16/fp16
+ * values are stored as their 16-bit patterns.
+ *
+ * Ownership and errors: every pointer passed is owned by the caller; device
+ * pointers must stay valid until the stream work completes.  The library never
+ * allocates device memory and keeps no global state.  Every error is a
+ * negative status returned before any work is enqueued, except KV_EDEVICE,
+ * which reports a failed launch; faults inside a kernel surface at the caller's
+ * next synchronisation.  Calls are asynchronous on `stream` (a hipStream_t; NULL
+ * is the default stream).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum kv_format {
+  KV_FMT_BF16 = 0,
+  KV_FMT_KIVI2 = 1,
+  KV_FMT_FP4 = 2,
+  KV_FMT_TURBO = 3,
+  KV_FMT_QJL1_FP4V = 4,
+  KV_FMT_LATENT_FP4 = 5
+};
+
+enum kv_dtype { KV_DT_F32 = 0, KV_DT_BF16 = 1 };
+
+enum kv_status {
+  KV_OK = 0,
+  KV_EINVAL = -1,        /* malformed argument: NULL pointer, bad size, misaligned KIVI append */
+  KV_ECAPACITY = -2,     /* tokens beyond the cache capacity */
+  KV_EUNSUPPORTED = -3,  /* a valid request this library does not implement */
+  KV_EWORKSPACE = -4,    /* workspace missing or smaller than required */
+  KV_EDEVICE = -5        /* a kernel launch failed */
+};
+
+/* Shape of one layer's cache.  Supported: KIVI2 head_dim 64|128, group 32,
+ * capacity a multiple of 32; FP4 head_dim 64|128, group 16; TURBO head_dim 128,
+ * qjl_m 128, lm_bits 2; QJL1_FP4V head_dim 128, qjl_m 128, group 16;
+ * LATENT_FP4 num_kv_heads 1, head_dim 512, rope_dim 64, group 16.  Fields a
+ * format does not use must be 0, except `group`, which is always the format's
+ * quantisation group (0 for TURBO). */
+typedef struct kv_layout {
+  int32_t format;       /* enum kv_format */
+  int32_t batch;        /* sequences B */
+  int32_t num_kv_heads; /* H */
+  int32_t head_dim;     /* d (latent width for LATENT_FP4) */
+  int32_t rope_dim;     /* LATENT_FP4: bf16 RoPE key width; else 0 */
+  int32_t capacity;     /* token slots per sequence */
+  int32_t group;        /* FP4 scale group (16) or KIVI group (32) */
+  int32_t qjl_m;        /* QJL sketch rows (TURBO, QJL1_FP4V) */
+  int32_t lm_bits;      /* Lloyd-Max bits (TURBO) */
+} kv_layout;
+
+/* Buffers of a cache, by role.  Element types and shapes (Tc = capacity):
+ *   K_CODES  u8   KIVI2 [B][H][Tc][d/4]; FP4 [B][H][Tc][d/2]; TURBO [B][H][Tc][d/4];
+ *                 LATENT [B][Tc][d/2]
+ *   K_SCALE  KIVI2 f32 [B][H][Tc/32][d]; FP4 bf16 [B][H][Tc][d/16]; LATENT bf16 [B][Tc][d/16]
+ *   K_ZERO   f32  KIVI2 [B][H][Tc/32][d]
+ *   K_SKETCH u8   TURBO, QJL1 [B][H][Tc][m/8]
+ *   K_NORM   f16  TURBO, QJL1 [B][H][Tc]
+ *   K_RNORM  f16  TURBO [B][H][Tc]  (residual norm)
+ *   V_CODES  u8   KIVI2 [B][H][Tc][d/4]; FP4, QJL1 [B][H][Tc][d/2]; TURBO [B][H][Tc][d/4]
+ *   V_SCALE  KIVI2 f32 [B][H][Tc][d/32]; FP4, QJL1 bf16 [B][H][Tc][d/16]
+ *   V_ZERO   f32  KIVI2 [B][H][Tc][d/32]
+ *   V_NORM   f16  TURBO [B][H][Tc]
+ *   ROPE     bf16 LATENT [B][Tc][rope_dim]                                   */
+enum kv_buffer {
+  KV_BUF_K_CODES = 0, KV_BUF_K_SCALE, KV_BUF_K_ZERO, KV_BUF_K_SKETCH, KV_BUF_K_NORM,
+  KV_BUF_K_RNORM, KV_BUF_V_CODES, KV_BUF_V_SCALE, KV_BUF_V_ZERO, KV_BUF_V_NORM,
+  KV_BUF_ROPE, KV_BUF_COUNT
+};
+
+/* A cache: its layout, device buffers (NULL where the format has none) and
+ * the method's constants, as device arrays of fp32 (made by the helpers below):
+ *   rot        TURBO: d x d rotation R, row-major, y = R x, bf16-valued
+ *   proj       TURBO, QJL1: m x d QJL matrix S, row-major, bf16-valued
+ *   lm_levels  TURBO: 2^lm_bits Lloyd-Max levels, ascending
+ *   lm_thresh  TURBO: 2^lm_bits - 1 thresholds, ascending                   */
+typedef struct kv_cache {
+  kv_layout layout;
+  void* buf[KV_BUF_COUNT];
+  const float* rot;
+  const float* proj;
+  const float* lm_levels;
+  const float* lm_thresh;
+} kv_cache;
+
+/* Options for kv_decode_attention; pass NULL for defaults.
+ *   num_splits   context splits per (sequence, KV head); 0 picks one from the
+ *                shape; the workspace size depends on it
+ *   ev_begin/end optional hipEvent_t recorded on `stream` immediately before
+ *                and after the split-context attention kernel (for timing) */
+typedef struct kv_decode_opts {
+  int32_t num_splits;
+  void* ev_begin;
+  void* ev_end;
+} kv_decode_opts;
+
+/* Bytes of one buffer of a cache with this layout; 0 if the format has no
+ * such buffer or the layout is invalid.  Host only. */
+size_t kv_buffer_bytes(const kv_layout* L, int32_t which);
+
+/* Bytes stored per token over `num_layers` layers: packed codes plus the
+ * metadata kept for that token (KIVI key scale/zero, kept per 32 tokens, counted
+ * as 1/32 per token) for all KV heads (page "TurboQuant vs OSCAR vs EpiCache",
+ * KV-cache memory bottleneck section: layers x KV heads x head dim x 2 x bytes
+ * per element for BF16).  Host only; returns 0 for an invalid layout or
+ * num_layers < 1.  BF16 needs only format, num_kv_heads and head_dim. */
+size_t kv_bytes_per_token(const kv_layout* L, int32_t num_layers);
+
+/* Append n_new tokens at positions [start, start+n_new) of every sequence.
+ *   k, v      device, [B][H][n_new][d] in `in_dtype` (KV_DT_F32 or KV_DT_BF16);
+ *             LATENT_FP4: k is [B][n_new][d + rope_dim] (latent then RoPE key)
+ *             and v must be NULL
+ *   ws        unused by every current format: pass NULL; *ws_bytes (if given)
+ *             is set to 0
+ * KIVI2 needs start and n_new to be multiples of 32 (whole key groups):
+ * KV_EINVAL otherwise.  start + n_new > capacity: KV_ECAPACITY.  n_new == 0
+ * enqueues nothing.  The method's encoding steps are those of the format
+ * definitions above (TurboQuant: norm, rotate, divide, Lloyd-Max code,
+ * residual, residual norm, sketch of the residual, in that order). */
+int kv_quant_append(const kv_cache* c, const void* k, const void* v, int32_t in_dtype,
+                    int32_t start, int32_t n_new, void* ws, size_t* ws_bytes, void* stream);
+
+/* One query token per sequence attends over the first seq_lens[b] cached
+ * tokens of its sequence (no mask; a query head hq reads KV head hq / (Hq/H)):
+ *   out[b][hq] = sum_t softmax_t(scale * logit(q[b][hq], t)) * value(t)
+ * (page "TurboQuant vs OSCAR vs EpiCache", section on the KV-cache memory
+ * bottleneck: each new token reads the whole cache).  Logits per format: the
+ * dot product with the dequantised key (KIVI2, FP4; LATENT: latent part plus
+ * RoPE part); TURBO: n*(<Rq, u~> + sqrt(pi/2)/m * gamma * <S R q, sigma>);
+ * QJL1: sqrt(pi/2)/m * n * <S q, sigma>; sigma = +-1 from the sketch bits.
+ *   q         device, [B][Hq][d] (LATENT: [B][Hq][d + rope_dim]) in q_dtype
+ *   seq_lens  device int32 [B], each in [1, max_seq_len]; values beyond
+ *             max_seq_len are clamped to it
+ *   out       device fp32 [B][Hq][d] (LATENT: [B][Hq][d]); for TURBO the value
+ *             path is mapped back with R^T
+ *   ws        device workspace of *ws_bytes bytes, 256-byte aligned; ws == NULL
+ *             is a size query that writes *ws_bytes and returns KV_OK
+ * Errors: num_q_heads not a multiple of H, max_seq_len outside
+ * [1, capacity], NULL pointers: KV_EINVAL; workspace smaller than required:
+ * KV_EWORKSPACE. */
+int kv_decode_attention(const kv_cache* c, const void* q, int32_t q_dtype, int32_t num_q_heads,
+                        const int32_t* seq_lens, int32_t max_seq_len, float softmax_scale,
+                        float* out, void* ws, size_t* ws_bytes, const kv_decode_opts* opts,
+                        void* stream);
+
+/* ---- the method's constants (host memory, host only) ---- */
+
+/* Lloyd-Max quantiser for N(0, 1/dim) with 2^bits levels: the fixed point of
+ * "thresholds are midpoints of neighbouring levels" and "each level is the
+ * mean of the source over its cell", iterated in fp64 and rounded to fp32
+ * (page "TurboQuant vs OSCAR vs EpiCache", section "quantization frontiers",
+ * stage one: a precomputed optimal scalar quantiser per coordinate).
+ * levels: 2^bits floats, thresholds: 2^bits - 1 floats, ascending.
+ * bits in [1, 4], dim >= 1; else KV_EINVAL. */
+int kv_lloyd_max_gaussian(int32_t bits, int32_t dim, float* levels, float* thresholds);
+
+/* Haar rotation from a d x d matrix of iid N(0,1) draws (row-major fp64): the
+ * orthogonal factor Q of gauss = Q R with diag(R) > 0, rounded to bf16 values,
+ * written as fp32 row-major (same section, stage one: a random rotation).
+ * d in [1, 1024]; a rank-deficient input gives KV_EINVAL. */
+int kv_make_rotation(const double* gauss, int32_t d, float* rot);
+
+/* QJL matrix from m x d iid N(0,1) draws (row-major fp64): each draw rounded
+ * to bf16, written as fp32 (same section, stage two). */
+int kv_make_projection(const double* gauss, int32_t m, int32_t d, float* proj);
+
+/* Static description of a status code. */
+const char* kv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

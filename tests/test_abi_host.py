@@ -1,0 +1,155 @@
+"""C-ABI checks that need no GPU: the library loads and exports every declared
+symbol, the host arithmetic (sizes, bytes per token, constants) agrees with the
+oracle and the pages, and every validation error is returned before any launch.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from bit_kv_cache_04_amd import kvq
+from oracle.bytes import per_token_head
+from oracle.lloyd_max import canonical_codebook
+from oracle.numerics import round_bf16
+from oracle.rotation import canonical_rotation
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "kvq.h")
+
+OK, EINVAL, ECAP, EUNSUP, EWS = 0, -1, -2, -3, -4
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(kv_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert set(names) == set(kvq.EXPORTED), names
+    L = kvq.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_bytes_per_token_bf16_pages(golden):
+    for layers, heads, d, tokens, want, _ in golden("bytes_per_token.txt"):
+        lay = kvq.make_layout("bf16", 1, int(heads), int(d), 1)
+        assert kvq.kv_bytes_per_token(lay, int(layers)) * int(tokens) == int(want)
+
+
+@pytest.mark.parametrize("fmt,H,d,rope", [("fp4", 8, 128, 0), ("fp4", 4, 64, 0), ("kivi2", 2, 64, 0),
+                                          ("kivi2", 8, 128, 0), ("turbo", 8, 128, 0), ("qjl1", 8, 128, 0),
+                                          ("latent", 1, 512, 64)])
+def test_bytes_per_token_matches_oracle(fmt, H, d, rope):
+    lay = kvq.make_layout(fmt, 3, H, d, 96, rope)
+    for layers in (1, 40, 80):
+        assert kvq.kv_bytes_per_token(lay, layers) == layers * H * per_token_head(fmt, d, rope)
+    total = sum(kvq.kv_buffer_bytes(lay, i) for i in range(len(kvq.BUFFERS)))
+    assert total == 3 * H * 96 * per_token_head(fmt, d, rope)
+
+
+def test_bytes_per_token_invalid():
+    assert kvq.kv_bytes_per_token(kvq.make_layout("fp4", 1, 8, 96, 16), 1) == 0   # unsupported d
+    assert kvq.kv_bytes_per_token(kvq.make_layout("fp4", 1, 8, 128, 16), 0) == 0  # no layers
+
+
+def test_codebook_matches_oracle():
+    for d in (64, 128):
+        lv, th = kvq.kv_lloyd_max_gaussian(2, d)
+        olv, oth = canonical_codebook(2, d)
+        np.testing.assert_array_equal(lv.astype(np.float64), olv)
+        np.testing.assert_array_equal(th.astype(np.float64), oth)
+    for b in (1, 3, 4):
+        lv, th = kvq.kv_lloyd_max_gaussian(b, 128)
+        olv, oth = canonical_codebook(b, 128)
+        np.testing.assert_allclose(lv, olv, rtol=2 ** -23)
+        np.testing.assert_allclose(th, oth, rtol=2 ** -23, atol=1e-30)
+    assert kvq.lib().kv_lloyd_max_gaussian(0, 128, None, None) == EINVAL
+
+
+@pytest.mark.parametrize("seed,d", [(0, 128), (1, 128), (2, 64), (3, 16)])
+def test_rotation_and_projection_match_oracle(seed, d):
+    g = np.random.default_rng(seed).standard_normal((d, d))
+    np.testing.assert_array_equal(kvq.kv_make_rotation(g).astype(np.float64), canonical_rotation(g))
+    p = np.random.default_rng(seed + 100).standard_normal((128, d))
+    np.testing.assert_array_equal(kvq.kv_make_projection(p).astype(np.float64), round_bf16(p))
+
+
+def test_rotation_rank_deficient():
+    g = np.zeros((8, 8))
+    out = np.zeros((8, 8), np.float32)
+    assert kvq.lib().kv_make_rotation(g.ctypes.data, 8, out.ctypes.data) == EINVAL
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5):
+        assert kvq.kv_status_string(s) != "unknown status"
+    assert kvq.kv_status_string(7) == "unknown status"
+
+
+# ---------------------------------------------------------------- validation (no launch)
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def _cache(fmt="fp4", B=2, H=2, d=128, T=64, rope=0, fill=True, consts=True):
+    lay = kvq.make_layout(fmt, B, H, d, T, rope)
+    bufs = (ctypes.c_void_p * len(kvq.BUFFERS))(
+        *[(FAKE if fill and kvq.kv_buffer_bytes(lay, i) else None) for i in range(len(kvq.BUFFERS))])
+    c = FAKE if consts else None
+    return kvq.KVCache(lay, bufs, c, c, c, c)
+
+
+def _append(c, k=FAKE, v=FAKE, dt=kvq.DT_BF16, start=0, n=1):
+    nb = ctypes.c_size_t(99)
+    return kvq.lib().kv_quant_append(ctypes.byref(c), k, v, dt, start, n, None, ctypes.byref(nb), None)
+
+
+def _decode(c, q=FAKE, qdt=kvq.DT_BF16, hq=4, lens=FAKE, maxlen=64, scale=1.0, out=FAKE, ws=None,
+            wsb=0, splits=0):
+    nb = ctypes.c_size_t(wsb)
+    opts = kvq.KVDecodeOpts(splits, None, None)
+    st = kvq.lib().kv_decode_attention(ctypes.byref(c), q, qdt, hq, lens, maxlen, ctypes.c_float(scale), out,
+                                       ws, ctypes.byref(nb), ctypes.byref(opts), None)
+    return st, nb.value
+
+
+def test_append_validation():
+    assert _append(_cache(), start=60, n=5) == ECAP
+    assert _append(_cache(), start=-1) == EINVAL
+    assert _append(_cache(), dt=7) == EUNSUP
+    assert _append(_cache(), k=None) == EINVAL
+    assert _append(_cache(), v=None) == EINVAL
+    assert _append(_cache(), k=FAKE + 2) == EINVAL                     # misaligned input
+    assert _append(_cache(fill=False)) == EINVAL                      # NULL buffers
+    assert _append(_cache("kivi2", d=64), n=16) == EINVAL             # partial KIVI key group
+    assert _append(_cache("kivi2", d=64), start=16, n=32) == EINVAL
+    assert _append(_cache("latent", H=1, d=512, rope=64)) == EINVAL   # latent takes no v
+    assert _append(_cache("turbo", consts=False)) == EINVAL           # constants missing
+    assert _append(_cache("fp4", d=96)) == EUNSUP
+    assert _append(_cache("fp4", B=0)) == EINVAL
+    assert _append(_cache(), n=0) == OK                               # nothing to do, nothing launched
+
+
+def test_decode_validation_and_size_query():
+    c = _cache()
+    st, nb = _decode(c, ws=None)
+    assert st == OK and nb > 0 and nb % 256 == 0
+    st, nb2 = _decode(c, ws=None, splits=3)
+    assert st == OK and nb2 >= nb or nb2 > 0
+    assert _decode(c, ws=FAKE, wsb=nb - 1)[0] == EWS
+    assert _decode(c, ws=FAKE + 16, wsb=nb)[0] == EINVAL                # workspace misaligned
+    assert _decode(c, hq=3)[0] == EINVAL                               # not a multiple of H
+    assert _decode(c, maxlen=65)[0] == EINVAL                          # beyond capacity
+    assert _decode(c, maxlen=0)[0] == EINVAL
+    assert _decode(c, qdt=5)[0] == EUNSUP
+    assert _decode(c, scale=float("nan"))[0] == EINVAL
+    assert _decode(c, splits=-1)[0] == EINVAL
+    assert _decode(c, ws=FAKE, wsb=nb, q=None)[0] == EINVAL
+    assert _decode(c, ws=FAKE, wsb=nb, out=None)[0] == EINVAL
+    assert _decode(c, ws=FAKE, wsb=nb, lens=None)[0] == EINVAL
+    assert _decode(_cache("bf16"))[0] == EUNSUP
