@@ -80,6 +80,21 @@ class PackedKVCache:
                               cp("rot"), cp("proj"), cp("levels"), cp("thresholds"))
         self._ws = None
 
+    def sequence(self, b):
+        """A one-sequence cache sharing sequence b's slice of every buffer (appends at
+        a position of its own, e.g. for ragged prefill)."""
+        sub = PackedKVCache.__new__(PackedKVCache)
+        sub.__dict__.update(self.__dict__)
+        sub.B = 1
+        sub.layout = make_layout(self.fmt, 1, self.H, self.d, self.T, self.rope)
+        sub.bufs = {n: t.view(self.B, -1)[b] for n, t in self.bufs.items()}
+        ptrs = [sub.bufs[n].data_ptr() if n in sub.bufs else None for n in BUFFERS]
+        c = self.struct
+        sub.struct = KVCache(sub.layout, (ctypes.c_void_p * len(BUFFERS))(*ptrs), c.rot, c.proj,
+                             c.lm_levels, c.lm_thresh)
+        sub._ws = None
+        return sub
+
     # ---- views of the packed bytes
     def view(self, name):
         dt, shape = buffer_view_spec(self.fmt, self.B, self.H, self.T, self.d, self.rope)[name]

@@ -359,11 +359,12 @@ __global__ void __launch_bounds__(256) turbo_kernel(const InT* __restrict__ x,
       }
     }
     __builtin_amdgcn_wave_barrier();
-    // quantise: lane holds y[token kq*4+i][row nt*16+col]
+    // quantise: the fp64 16x16x4 product leaves y[token kq + 4i][row nt*16 + col]
+    // in element i of this lane's accumulators
     double rr[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int tok = kq * 4 + i;
+      const int tok = kq + 4 * i;
       const double tn = __shfl(nrm, tok);
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
@@ -425,15 +426,15 @@ __global__ void __launch_bounds__(256) turbo_kernel(const InT* __restrict__ x,
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) ballots[nt][i] = __ballot(sacc[nt][i] >= 0.0);
-      // lane (kq, col) holds gamma^2 of token kq*4+i in rr[i]; token `lane` needs it
+      // lane (kq, col) holds gamma^2 of token kq + 4i in rr[i]; token `lane` needs it
       double g2 = 0.0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        double v = __shfl(rr[i], (lane >> 2) * 16);
-        if ((lane & 3) == i) g2 = v;
+        double v = __shfl(rr[i], (lane & 3) * 16);
+        if ((lane >> 2) == i) g2 = v;
       }
       if (lane < 16 && base + lane < rows) {
-        const int q = lane >> 2, i = lane & 3;
+        const int q = lane & 3, i = lane >> 2;
         uint32_t w[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {

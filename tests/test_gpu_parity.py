@@ -1,0 +1,110 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Packed bytes must be bit-exact (KIVI-2 and FP4 by definition; TurboQuant and
+QJL sketches are computed so that they match the exact-arithmetic signs and
+codes, and any difference is counted against the 1e-5 tie budget); attention
+outputs must be within 2e-3 max relative error per (sequence, query head) row.
+Small shapes span several 32-token tiles, several splits and a ragged tail.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_helpers import (RTOL, assert_bytes_equal, gpu_buffers, host64, inputs, new_cache, oracle_constants,
+                         oracle_encode, row_rel_err, softmax_scale)
+from oracle import attention as OA
+
+pytestmark = pytest.mark.gpu
+
+C = synth.CONFIGS
+SMALL = {
+    "kivi2": C["kivi2_tiny"],
+    "fp4": C["fp4_b16_t32k"].scaled(batch=2, hq=8, hkv=2, context=1000),
+    "turbo": C["turbo_b8_t128k"].scaled(batch=2, hq=16, hkv=2, context=777),
+    "qjl1": C["qjl1_b1_t1m"].scaled(batch=2, hq=8, hkv=2, context=1500),
+    "latent": C["latent_b64_t64k"].scaled(batch=2, hq=128, context=300),
+}
+
+
+def _build(cfg, chunks=2):
+    torch.manual_seed(0)
+    cache = new_cache(cfg)
+    K, V = inputs(cfg)
+    T = cfg.context
+    step = -(-T // chunks)
+    if cfg.fmt == "kivi2":
+        step = -(-step // 32) * 32
+    for t0 in range(0, T, step):
+        t1 = min(T, t0 + step)
+        if cfg.fmt == "latent":
+            cache.append(K[:, t0:t1].contiguous(), None, t0)
+        else:
+            cache.append(K[:, :, t0:t1].contiguous(), V[:, :, t0:t1].contiguous(), t0)
+    torch.cuda.synchronize()
+    return cache, K, V
+
+
+@pytest.mark.parametrize("fmt", list(SMALL))
+def test_append_bytes_match_oracle(fmt):
+    cfg = SMALL[fmt]
+    print(f"[append] {fmt} {cfg}", flush=True)
+    cache, K, V = _build(cfg)
+    want = oracle_encode(cfg, host64(K), host64(V), oracle_constants(cfg))
+    assert_bytes_equal(gpu_buffers(cache), want, fmt)
+
+
+@pytest.mark.parametrize("fmt", list(SMALL))
+def test_decode_matches_oracle(fmt):
+    cfg = SMALL[fmt]
+    print(f"[decode] {fmt} {cfg}", flush=True)
+    cache, K, V = _build(cfg)
+    consts = oracle_constants(cfg)
+    enc = oracle_encode(cfg, host64(K), host64(V), consts)
+    q = synth.make_queries(cfg, device="cuda")
+    lens = synth.seq_lens_for(cfg, ragged=True)
+    lens[-1] = 1                                        # a single-token context
+    lens_d = torch.from_numpy(lens).cuda()
+    out = cache.decode(q, lens_d, softmax_scale(cfg)).cpu().numpy()
+    ref = OA.decode_attention(cfg.fmt, enc, host64(q), lens, softmax_scale(cfg), cfg.hkv, consts,
+                              latent_dim=cfg.head_dim)
+    err = row_rel_err(out, ref)
+    print(f"  max row rel err {err.max():.3e}", flush=True)
+    assert err.max() <= RTOL
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "turbo", "qjl1", "latent"])
+def test_token_by_token_append_equals_bulk(fmt):
+    """A decode loop appends one token per step; the bytes must equal a bulk append."""
+    cfg = SMALL[fmt].scaled(context=70)
+    bulk, K, V = _build(cfg, chunks=1)
+    step = new_cache(cfg)
+    for t in range(cfg.context):
+        if fmt == "latent":
+            step.append(K[:, t:t + 1].contiguous(), None, t)
+        else:
+            step.append(K[:, :, t:t + 1].contiguous(), V[:, :, t:t + 1].contiguous(), t)
+    torch.cuda.synchronize()
+    assert_bytes_equal(gpu_buffers(step), gpu_buffers(bulk), fmt)
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "turbo", "latent"])
+def test_split_count_invariance_and_determinism(fmt):
+    cfg = SMALL[fmt]
+    cache, _, _ = _build(cfg)
+    q = synth.make_queries(cfg, device="cuda")
+    lens = torch.from_numpy(synth.seq_lens_for(cfg)).cuda()
+    outs = [cache.decode(q, lens, softmax_scale(cfg), splits=s).cpu().numpy() for s in (1, 0, 5, 0)]
+    np.testing.assert_array_equal(outs[1], outs[3])
+    for o in outs[:3]:
+        assert row_rel_err(o, outs[0]).max() < 1e-5
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "qjl1", "turbo"])
+def test_fp32_inputs(fmt):
+    """fp32 K/V (values not representable in bf16) go through the same formats."""
+    cfg = SMALL[fmt].scaled(in_dtype="f32", context=200)
+    cache, K, V = _build(cfg, chunks=1)
+    want = oracle_encode(cfg, host64(K), host64(V), oracle_constants(cfg))
+    assert_bytes_equal(gpu_buffers(cache), want, fmt + "/f32")
