@@ -113,7 +113,7 @@ def main():
     lens = torch.full((cfg.batch,), T, dtype=torch.int32, device=dev)
     scale = 1.0 / math.sqrt(cfg.key_width)
     out = torch.empty(cfg.batch, cfg.hq, cfg.head_dim, dtype=torch.float32, device=dev)
-    ws = torch.empty(cache.workspace_bytes(cfg.hq, T, args.splits), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(cache.workspace_bytes(cfg.hq, T, args.splits, q.dtype), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))

@@ -114,20 +114,20 @@ class PackedKVCache:
         kvq.kv_quant_append(self.struct, _ptr(k), _ptr(v), _TORCH_DT[k.dtype], start, n,
                             _stream_ptr(self.device))
 
-    def workspace_bytes(self, num_q_heads, max_seq_len, splits=0):
+    def workspace_bytes(self, num_q_heads, max_seq_len, splits=0, q_dtype=torch.bfloat16):
         opts = KVDecodeOpts(splits, None, None)
-        return kvq.kv_decode_attention(self.struct, None, DT_BF16, num_q_heads, None, max_seq_len, 1.0,
-                                       None, None, 0, opts)
+        return kvq.kv_decode_attention(self.struct, None, _TORCH_DT[q_dtype], num_q_heads, None, max_seq_len,
+                                       1.0, None, None, 0, opts)
 
     def decode(self, q, seq_lens, scale, max_seq_len=None, splits=0, out=None, ws=None, events=None):
         """q: [B, Hq, d(+rope)] fp32/bf16; seq_lens: int32 device [B]. Returns fp32 [B, Hq, d]."""
         q = q.contiguous()
         Hq = q.shape[1]
         max_seq_len = self.T if max_seq_len is None else max_seq_len
-        need = self.workspace_bytes(Hq, max_seq_len, splits)
+        need = self.workspace_bytes(Hq, max_seq_len, splits, q.dtype)
         if ws is None:
             if self._ws is None or self._ws.numel() < need:
-                self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+                self._ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
             ws = self._ws
         if out is None:
             out = torch.empty(self.B, Hq, self.d, dtype=torch.float32, device=self.device)

@@ -45,7 +45,7 @@ extern "C" int kv_decode_attention(const kv_cache* c, const void* q, int32_t q_d
   if (!std::isfinite(softmax_scale)) return KV_EINVAL;
   const int req = opts ? opts->num_splits : 0;
   if (req < 0 || req > 1024) return KV_EINVAL;
-  const SplitPlan plan = plan_splits(&L, num_q_heads, max_seq_len, req);
+  const SplitPlan plan = plan_splits(&L, num_q_heads, q_dtype, max_seq_len, req);
   const DecodeWorkspace wsl = decode_workspace(&L, num_q_heads, plan.splits);
   if (!ws) {
     if (!ws_bytes) return KV_EINVAL;

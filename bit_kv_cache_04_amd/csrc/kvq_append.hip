@@ -30,12 +30,10 @@ __device__ __forceinline__ size_t dst_row(size_t r, int n, int cap, int start) {
 // One thread per 16-channel group: s = bf16_RNE(absmax / 6) (the quotient taken
 // in fp64, then rounded once), then each element's E2M1 nibble against s.
 template <typename InT>
-__global__ void __launch_bounds__(256) fp4_append_kernel(const InT* __restrict__ x, size_t stride,
-                                                         int d, uint8_t* __restrict__ codes,
-                                                         uint16_t* __restrict__ scales, size_t rows,
-                                                         int n, int cap, int start) {
+__device__ __forceinline__ void fp4_group(const InT* __restrict__ x, size_t stride, int d,
+                                          uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
+                                          size_t rows, int n, int cap, int start, size_t gid) {
   const int groups = d / 16;
-  size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= rows * groups) return;
   const int g = (int)(gid % groups);
   const size_t r = gid / groups;
@@ -59,16 +57,34 @@ __global__ void __launch_bounds__(256) fp4_append_kernel(const InT* __restrict__
   scales[dr * groups + g] = sb;
 }
 
-// Latent RoPE part: copied through as bf16 (rounded once if the input is fp32).
+// K (blockIdx.y = 0) and V (blockIdx.y = 1) of an FP4 cache in one launch.
 template <typename InT>
-__global__ void rope_copy_kernel(const InT* __restrict__ x, size_t stride, int off, int width,
-                                 uint16_t* __restrict__ rope, size_t rows, int n, int cap, int start) {
-  size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= rows * width) return;
-  const int c = (int)(gid % width);
-  const size_t r = gid / width;
-  const float v = load_as_f32(x + r * stride + off, c);
-  rope[dst_row(r, n, cap, start) * width + c] = bf16_from_f64((double)v);
+__global__ void __launch_bounds__(256) fp4_append_kernel(const InT* __restrict__ k, const InT* __restrict__ v,
+                                                         int d, uint8_t* __restrict__ kc, uint16_t* __restrict__ ks,
+                                                         uint8_t* __restrict__ vc, uint16_t* __restrict__ vs,
+                                                         size_t rows, int n, int cap, int start) {
+  const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (blockIdx.y == 0) fp4_group(k, d, d, kc, ks, rows, n, cap, start, gid);
+  else fp4_group(v, d, d, vc, vs, rows, n, cap, start, gid);
+}
+
+// Latent: the 512-wide latent as FP4 groups (blockIdx.y = 0) and the RoPE key
+// copied through as bf16, rounded once if the input is fp32 (blockIdx.y = 1).
+template <typename InT>
+__global__ void __launch_bounds__(256) latent_append_kernel(const InT* __restrict__ x, int d, int rope_dim,
+                                                            uint8_t* __restrict__ cc, uint16_t* __restrict__ cs,
+                                                            uint16_t* __restrict__ rope, size_t rows, int n,
+                                                            int cap, int start) {
+  const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)d + rope_dim;
+  if (blockIdx.y == 0) {
+    fp4_group(x, stride, d, cc, cs, rows, n, cap, start, gid);
+  } else if (gid < rows * rope_dim) {
+    const int c = (int)(gid % rope_dim);
+    const size_t r = gid / rope_dim;
+    const float val = load_as_f32(x + r * stride + d, c);
+    rope[dst_row(r, n, cap, start) * rope_dim + c] = bf16_from_f64((double)val);
+  }
 }
 
 // ---------------------------------------------------------------- KIVI 2-bit
@@ -85,13 +101,10 @@ __device__ __forceinline__ uint32_t kivi_code(float x, float z, float s) {
 // Keys: per channel over each 32-token group.  One thread per (row group, group
 // of 4 channels = one output byte per token).
 template <typename InT>
-__global__ void __launch_bounds__(256) kivi_keys_kernel(const InT* __restrict__ x, int d,
-                                                        uint8_t* __restrict__ codes,
-                                                        float* __restrict__ kscale,
-                                                        float* __restrict__ kzero, int bh_count,
-                                                        int n, int cap, int start) {
+__device__ __forceinline__ void kivi_keys(const InT* __restrict__ x, int d, uint8_t* __restrict__ codes,
+                                          float* __restrict__ kscale, float* __restrict__ kzero,
+                                          int bh_count, int n, int cap, int start, size_t gid) {
   const int quads = d / 4, ngroups = n / 32;
-  size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (size_t)bh_count * ngroups * quads) return;
   const int cq = (int)(gid % quads);
   const size_t rest = gid / quads;
@@ -128,13 +141,10 @@ __global__ void __launch_bounds__(256) kivi_keys_kernel(const InT* __restrict__ 
 
 // Values: per token over each 32-channel group.  One thread per (token, group).
 template <typename InT>
-__global__ void __launch_bounds__(256) kivi_values_kernel(const InT* __restrict__ x, int d,
-                                                          uint8_t* __restrict__ codes,
-                                                          float* __restrict__ vscale,
-                                                          float* __restrict__ vzero, size_t rows,
-                                                          int n, int cap, int start) {
+__device__ __forceinline__ void kivi_values(const InT* __restrict__ x, int d, uint8_t* __restrict__ codes,
+                                            float* __restrict__ vscale, float* __restrict__ vzero, size_t rows,
+                                            int n, int cap, int start, size_t gid) {
   const int groups = d / 32;
-  size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= rows * groups) return;
   const int g = (int)(gid % groups);
   const size_t r = gid / groups;
@@ -152,6 +162,17 @@ __global__ void __launch_bounds__(256) kivi_values_kernel(const InT* __restrict_
   *reinterpret_cast<unsigned long long*>(codes + dr * (d / 4) + g * 8) = packed;
   vscale[dr * groups + g] = s;
   vzero[dr * groups + g] = mn;
+}
+
+// Keys (blockIdx.y = 0) and values (blockIdx.y = 1) of a KIVI cache in one launch.
+template <typename InT>
+__global__ void __launch_bounds__(256) kivi_append_kernel(const InT* __restrict__ k, const InT* __restrict__ v,
+                                                          int d, uint8_t* kc, float* ks, float* kz, uint8_t* vc,
+                                                          float* vs, float* vz, int bh_count, int n, int cap,
+                                                          int start) {
+  const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (blockIdx.y == 0) kivi_keys(k, d, kc, ks, kz, bh_count, n, cap, start, gid);
+  else kivi_values(v, d, vc, vs, vz, (size_t)bh_count * n, n, cap, start, gid);
 }
 
 // ---------------------------------------------------------------- QJL sign sketch (MFMA)
@@ -202,13 +223,10 @@ constexpr int kSPad = 136;  // LDS row pitch (elements) of the staged 128 x 128 
 // (2^-14 * ||S_i|| * ||k||), the sign is recomputed exactly in fp64, so the
 // stored bits equal the exact-arithmetic signs.
 template <typename InT>
-__global__ void __launch_bounds__(256) qjl_keys_kernel(const InT* __restrict__ x,
-                                                       const float* __restrict__ proj,
-                                                       uint8_t* __restrict__ sketch,
-                                                       uint16_t* __restrict__ knorm, size_t rows,
-                                                       int n, int cap, int start) {
-  __shared__ __align__(16) uint16_t S_lds[128 * kSPad];
-  __shared__ float srow_norm[128];
+__device__ __forceinline__ void qjl_keys(const InT* __restrict__ x, const float* __restrict__ proj,
+                                         uint8_t* __restrict__ sketch, uint16_t* __restrict__ knorm,
+                                         size_t rows, int n, int cap, int start, uint16_t* S_lds,
+                                         float* srow_norm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < 128 * 128; e += 256) {
     const float v = proj[e];
@@ -300,6 +318,25 @@ __global__ void __launch_bounds__(256) qjl_keys_kernel(const InT* __restrict__ x
   }
 }
 
+// QJL keys (blockIdx.y = 0, persistent over 16-token tiles) and FP4 values
+// (blockIdx.y = 1) in one launch.
+template <typename InT>
+__global__ void __launch_bounds__(256) qjl_append_kernel(const InT* __restrict__ k, const InT* __restrict__ v,
+                                                         const float* __restrict__ proj, uint8_t* sketch,
+                                                         uint16_t* knorm, uint8_t* vc, uint16_t* vs, size_t rows,
+                                                         int n, int cap, int start) {
+  __shared__ __align__(16) uint16_t S_lds[128 * kSPad];
+  __shared__ float srow_norm[128];
+  if (blockIdx.y == 0) {
+    qjl_keys(k, proj, sketch, knorm, rows, n, cap, start, S_lds, srow_norm);
+  } else {
+    const size_t groups = rows * 8;
+    for (size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x; gid < groups;
+         gid += (size_t)gridDim.x * blockDim.x)
+      fp4_group(v, 128, 128, vc, vs, rows, n, cap, start, gid);
+  }
+}
+
 // ---------------------------------------------------------------- TurboQuant (fp64 MFMA)
 
 // Keys (WITH_SKETCH) or values: n = ||x||; u = R x / n; idx = #{thresholds <= u};
@@ -308,20 +345,13 @@ __global__ void __launch_bounds__(256) qjl_keys_kernel(const InT* __restrict__ x
 // bf16/fp32, so each product term is exact and the fp64 sums match the
 // exact-arithmetic decisions except at exact ties.
 template <typename InT, bool WITH_SKETCH>
-__global__ void __launch_bounds__(256) turbo_kernel(const InT* __restrict__ x,
-                                                    const float* __restrict__ rot,
-                                                    const float* __restrict__ proj,
-                                                    const float* __restrict__ levels,
-                                                    const float* __restrict__ thresh,
-                                                    uint8_t* __restrict__ codes,
-                                                    uint8_t* __restrict__ sketch,
-                                                    uint16_t* __restrict__ norm_out,
-                                                    uint16_t* __restrict__ rnorm_out, size_t rows,
-                                                    int n, int cap, int start) {
-  __shared__ __align__(16) uint16_t R_lds[128 * kSPad];
-  __shared__ __align__(16) uint16_t S_lds[WITH_SKETCH ? 128 * kSPad : 1];
-  __shared__ double scratch[4][16 * 129];  // per wave: x tile (as double), then the residual
-  __shared__ uint8_t idx_lds[4][16 * 128];
+__device__ __forceinline__ void turbo_body(const InT* __restrict__ x, const float* __restrict__ rot,
+                                           const float* __restrict__ proj, const float* __restrict__ levels,
+                                           const float* __restrict__ thresh, uint8_t* __restrict__ codes,
+                                           uint8_t* __restrict__ sketch, uint16_t* __restrict__ norm_out,
+                                           uint16_t* __restrict__ rnorm_out, size_t rows, int n, int cap,
+                                           int start, uint16_t* R_lds, uint16_t* S_lds,
+                                           double (*scratch)[16 * 129], uint8_t (*idx_lds)[16 * 128]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < 128 * 128; e += 256) {
     R_lds[(e >> 7) * kSPad + (e & 127)] = (uint16_t)(__float_as_uint(rot[e]) >> 16);
@@ -451,6 +481,29 @@ __global__ void __launch_bounds__(256) turbo_kernel(const InT* __restrict__ x,
   }
 }
 
+// TurboQuant keys (blockIdx.y = 0, with the residual sketch) and values
+// (blockIdx.y = 1) in one launch; each wave takes 16-token tiles.
+template <typename InT>
+__global__ void __launch_bounds__(256) turbo_append_kernel(const InT* __restrict__ k, const InT* __restrict__ v,
+                                                           const float* __restrict__ rot,
+                                                           const float* __restrict__ proj,
+                                                           const float* __restrict__ levels,
+                                                           const float* __restrict__ thresh, uint8_t* kc,
+                                                           uint8_t* sketch, uint16_t* knorm, uint16_t* krnorm,
+                                                           uint8_t* vc, uint16_t* vnorm, size_t rows, int n,
+                                                           int cap, int start) {
+  __shared__ __align__(16) uint16_t R_lds[128 * kSPad];
+  __shared__ __align__(16) uint16_t S_lds[128 * kSPad];
+  __shared__ double scratch[4][16 * 129];  // per wave: x tile (as double), then the residual
+  __shared__ uint8_t idx_lds[4][16 * 128];
+  if (blockIdx.y == 0)
+    turbo_body<InT, true>(k, rot, proj, levels, thresh, kc, sketch, knorm, krnorm, rows, n, cap, start, R_lds,
+                          S_lds, scratch, idx_lds);
+  else
+    turbo_body<InT, false>(v, rot, nullptr, levels, thresh, vc, nullptr, vnorm, nullptr, rows, n, cap, start,
+                           R_lds, S_lds, scratch, idx_lds);
+}
+
 int blocks_for(size_t threads) { return (int)((threads + 255) / 256); }
 
 int persistent_blocks(size_t rows) {
@@ -470,38 +523,35 @@ int append_typed(const kv_cache* c, const InT* k, const InT* v, int start, int n
   auto* vs = static_cast<uint16_t*>(c->buf[KV_BUF_V_SCALE]);
   switch (L.format) {
     case KV_FMT_FP4:
-      fp4_append_kernel<InT><<<blocks_for(rows * (d / 16)), 256, 0, st>>>(k, d, d, kc, ks, rows, n, cap, start);
-      fp4_append_kernel<InT><<<blocks_for(rows * (d / 16)), 256, 0, st>>>(v, d, d, vc, vs, rows, n, cap, start);
+      fp4_append_kernel<InT><<<dim3(blocks_for(rows * (d / 16)), 2), 256, 0, st>>>(k, v, d, kc, ks, vc, vs, rows,
+                                                                                  n, cap, start);
       break;
     case KV_FMT_LATENT_FP4: {
-      const size_t stride = (size_t)d + L.rope_dim;
-      fp4_append_kernel<InT><<<blocks_for(rows * (d / 16)), 256, 0, st>>>(k, stride, d, kc, ks, rows, n, cap, start);
-      rope_copy_kernel<InT><<<blocks_for(rows * L.rope_dim), 256, 0, st>>>(
-          k, stride, d, L.rope_dim, static_cast<uint16_t*>(c->buf[KV_BUF_ROPE]), rows, n, cap, start);
+      const size_t work = std::max(rows * (d / 16), rows * (size_t)L.rope_dim);
+      latent_append_kernel<InT><<<dim3(blocks_for(work), 2), 256, 0, st>>>(
+          k, d, L.rope_dim, kc, ks, static_cast<uint16_t*>(c->buf[KV_BUF_ROPE]), rows, n, cap, start);
       break;
     }
-    case KV_FMT_KIVI2:
-      kivi_keys_kernel<InT><<<blocks_for((size_t)bh * (n / 32) * (d / 4)), 256, 0, st>>>(
-          k, d, kc, static_cast<float*>(c->buf[KV_BUF_K_SCALE]), static_cast<float*>(c->buf[KV_BUF_K_ZERO]),
-          bh, n, cap, start);
-      kivi_values_kernel<InT><<<blocks_for(rows * (d / 32)), 256, 0, st>>>(
-          v, d, vc, static_cast<float*>(c->buf[KV_BUF_V_SCALE]), static_cast<float*>(c->buf[KV_BUF_V_ZERO]),
-          rows, n, cap, start);
+    case KV_FMT_KIVI2: {
+      const size_t work = std::max((size_t)bh * (n / 32) * (d / 4), rows * (d / 32));
+      kivi_append_kernel<InT><<<dim3(blocks_for(work), 2), 256, 0, st>>>(
+          k, v, d, kc, static_cast<float*>(c->buf[KV_BUF_K_SCALE]), static_cast<float*>(c->buf[KV_BUF_K_ZERO]),
+          vc, static_cast<float*>(c->buf[KV_BUF_V_SCALE]), static_cast<float*>(c->buf[KV_BUF_V_ZERO]), bh, n,
+          cap, start);
       break;
-    case KV_FMT_QJL1_FP4V:
-      qjl_keys_kernel<InT><<<persistent_blocks(rows), 256, 0, st>>>(
-          k, c->proj, static_cast<uint8_t*>(c->buf[KV_BUF_K_SKETCH]),
-          static_cast<uint16_t*>(c->buf[KV_BUF_K_NORM]), rows, n, cap, start);
-      fp4_append_kernel<InT><<<blocks_for(rows * (d / 16)), 256, 0, st>>>(v, d, d, vc, vs, rows, n, cap, start);
+    }
+    case KV_FMT_QJL1_FP4V: {
+      const int blocks = std::max(persistent_blocks(rows), std::min(blocks_for(rows * (d / 16)), 2048));
+      qjl_append_kernel<InT><<<dim3(blocks, 2), 256, 0, st>>>(
+          k, v, c->proj, static_cast<uint8_t*>(c->buf[KV_BUF_K_SKETCH]), static_cast<uint16_t*>(c->buf[KV_BUF_K_NORM]),
+          vc, vs, rows, n, cap, start);
       break;
+    }
     case KV_FMT_TURBO:
-      turbo_kernel<InT, true><<<persistent_blocks(rows), 256, 0, st>>>(
-          k, c->rot, c->proj, c->lm_levels, c->lm_thresh, kc,
-          static_cast<uint8_t*>(c->buf[KV_BUF_K_SKETCH]), static_cast<uint16_t*>(c->buf[KV_BUF_K_NORM]),
-          static_cast<uint16_t*>(c->buf[KV_BUF_K_RNORM]), rows, n, cap, start);
-      turbo_kernel<InT, false><<<persistent_blocks(rows), 256, 0, st>>>(
-          v, c->rot, nullptr, c->lm_levels, c->lm_thresh, vc, nullptr,
-          static_cast<uint16_t*>(c->buf[KV_BUF_V_NORM]), nullptr, rows, n, cap, start);
+      turbo_append_kernel<InT><<<dim3(persistent_blocks(rows), 2), 256, 0, st>>>(
+          k, v, c->rot, c->proj, c->lm_levels, c->lm_thresh, kc, static_cast<uint8_t*>(c->buf[KV_BUF_K_SKETCH]),
+          static_cast<uint16_t*>(c->buf[KV_BUF_K_NORM]), static_cast<uint16_t*>(c->buf[KV_BUF_K_RNORM]), vc,
+          static_cast<uint16_t*>(c->buf[KV_BUF_V_NORM]), rows, n, cap, start);
       break;
     default:
       return KV_EUNSUPPORTED;

@@ -12,6 +12,7 @@
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "kvq_kernels.h"
 
 namespace kvq {
 namespace {
@@ -239,47 +240,65 @@ __global__ void __launch_bounds__(128) prep_query_kernel(const QT* __restrict__ 
 
 // ---------------------------------------------------------------- merge
 
-// out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.  TURBO maps
-// the rotated output back with R^T.  An all-empty row (no tokens) writes zeros.
-__global__ void __launch_bounds__(256) merge_kernel(const float* __restrict__ part, int splits, int dv,
-                                                    int fmt, const float* __restrict__ rot,
-                                                    float* __restrict__ out) {
-  __shared__ float w[1024];
+// out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, M = max_s m_s, for one
+// (sequence, query head) row per workgroup of 128 threads.  The split weights
+// are formed once in LDS; each thread then sums its channels over the splits
+// with independent loads.  TURBO maps the rotated output back with R^T.  A row
+// with no tokens at all writes zeros.
+constexpr int kMergeThreads = 128;
+constexpr int kMaxSplits = 1024;
+
+__global__ void __launch_bounds__(kMergeThreads) merge_kernel(const float* __restrict__ part, int splits, int dv,
+                                                              int fmt, const float* __restrict__ rot,
+                                                              float* __restrict__ out) {
+  __shared__ float w[kMaxSplits];
+  __shared__ float red[kMergeThreads / 64];
   __shared__ float ov[512];
-  __shared__ float inv_l;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t row = blockIdx.x;
-  const int tid = threadIdx.x;
   const float* p = part + row * (size_t)splits * (dv + 2);
-  if (tid == 0) {
-    float M = -INFINITY;
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, p[(size_t)s * (dv + 2)]);
-    float l = 0.f;
-    for (int s = 0; s < splits; ++s) {
-      const float ms = p[(size_t)s * (dv + 2)];
-      const float ws = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-      w[s] = ws;
-      l += ws * p[(size_t)s * (dv + 2) + 1];
-    }
-    inv_l = l > 0.f ? 1.f / l : 0.f;
-  }
+  float M = -INFINITY;
+  for (int s = tid; s < splits; s += kMergeThreads) M = fmaxf(M, p[(size_t)s * (dv + 2)]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if (lane == 0) red[wave] = M;
   __syncthreads();
-  for (int c = tid; c < dv; c += 256) {
-    float acc = 0.f;
-    for (int s = 0; s < splits; ++s)
-      if (w[s] != 0.f) acc = fmaf(w[s], p[(size_t)s * (dv + 2) + 2 + c], acc);
-    ov[c] = acc * inv_l;
-  }
+  M = fmaxf(red[0], red[1]);
   __syncthreads();
+  float l = 0.f;
+  for (int s = tid; s < splits; s += kMergeThreads) {
+    const float ms = p[(size_t)s * (dv + 2)];
+    const float ws = ms == -INFINITY ? 0.f : exp2f(ms - M);
+    w[s] = ws;
+    l += ws * p[(size_t)s * (dv + 2) + 1];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
+  if (lane == 0) red[wave] = l;
+  __syncthreads();
+  l = red[0] + red[1];
+  const float inv_l = l > 0.f ? 1.f / l : 0.f;
   float* dst = out + row * dv;
+  for (int c = tid; c < dv; c += kMergeThreads) {
+    float acc = 0.f;
+#pragma unroll 8
+    for (int s = 0; s < splits; ++s) acc = fmaf(w[s], p[(size_t)s * (dv + 2) + 2 + c], acc);
+    if (fmt == KV_FMT_TURBO) ov[c] = acc * inv_l;
+    else dst[c] = acc * inv_l;
+  }
   if (fmt == KV_FMT_TURBO) {
-    for (int c = tid; c < dv; c += 256) {
+    __syncthreads();
+    for (int c = tid; c < dv; c += kMergeThreads) {
       float acc = 0.f;
       for (int j = 0; j < dv; ++j) acc = fmaf(rot[j * dv + c], ov[j], acc);
       dst[c] = acc;
     }
-  } else {
-    for (int c = tid; c < dv; c += 256) dst[c] = ov[c];
   }
+}
+
+void launch_merge(const float* part, int rows, int splits, int dv, int fmt, const float* rot, float* out,
+                  hipStream_t st) {
+  merge_kernel<<<rows, kMergeThreads, 0, st>>>(part, splits, dv, fmt, rot, out);
 }
 
 template <int FMT, int DK, int DV, int HB>
@@ -301,6 +320,29 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
   const int B = L.batch;
   const int rows = B * num_q_heads;
   const int qw_in = query_width(&L), qw_out = prepared_query_width(&L);
+  if (fp4_fast_path_ok(L, num_q_heads, q_dtype)) {
+    Fp4DecodeArgs f{};
+    f.k_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_K_CODES]);
+    f.k_scale = static_cast<const uint16_t*>(c->buf[KV_BUF_K_SCALE]);
+    f.v_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_V_CODES]);
+    f.v_scale = static_cast<const uint16_t*>(c->buf[KV_BUF_V_SCALE]);
+    f.q = static_cast<const uint16_t*>(q);
+    f.seq_lens = seq_lens;
+    f.max_len = max_seq_len;
+    f.H = L.num_kv_heads;
+    f.cap = L.capacity;
+    f.Hq = num_q_heads;
+    f.scale_log2 = scale * kLog2e;
+    f.part = part;
+    f.splits = plan.splits;
+    f.per_split = plan.tokens_per_split;
+    if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), st) != hipSuccess) return KV_EDEVICE;
+    int rc = launch_decode_fp4_fast(f, B, num_q_heads / L.num_kv_heads, st);
+    if (rc != KV_OK) return rc;
+    if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess) return KV_EDEVICE;
+    launch_merge(part, rows, plan.splits, L.head_dim, L.format, c->rot, out, st);
+    return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
+  }
   if (q_dtype == KV_DT_F32)
     prep_query_kernel<float><<<rows, 128, 0, st>>>(static_cast<const float*>(q), qw_in, qw_out, L.format,
                                                    c->rot, c->proj, qv);
@@ -354,7 +396,7 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     default: return KV_EUNSUPPORTED;
   }
   if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess) return KV_EDEVICE;
-  merge_kernel<<<rows, 256, 0, st>>>(part, plan.splits, L.head_dim, L.format, c->rot, out);
+  launch_merge(part, rows, plan.splits, L.head_dim, L.format, c->rot, out, st);
   return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
 }
 

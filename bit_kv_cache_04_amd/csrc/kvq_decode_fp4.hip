@@ -1,0 +1,334 @@
+// FP4 E2M1 decode attention on the matrix cores (gfx950).
+//
+// One workgroup = 4 waves over one (sequence, KV head, context split); each
+// wave streams its own 32-token tiles of packed codes from HBM into a private
+// two-stage LDS ring with direct-to-LDS buffer loads (the next tile is in
+// flight while the current one is computed, without holding registers), and
+// keeps an online-softmax state for all query heads of the group.  Per tile
+// and wave:
+//   S^T = K_tile . Q^T   4 x 2 v_mfma_f32_16x16x32_f16 (rows = tokens, cols = heads)
+//   online softmax       per head = per lane column; row max over the 4 lane quarters
+//   O  += P . V_tile     8 v_mfma_f32_16x16x32_f16 (rows = heads, cols = channels)
+// The group's query heads share every packed byte read (page "TurboQuant vs
+// OSCAR vs EpiCache", KV-cache memory bottleneck section: decode is bound by
+// streaming the cache), and scores never leave registers.
+//
+// Element values: an E2M1 code times its bf16 group scale has at most 10
+// significant bits, so it is exact in fp16 while |x| stays within the fp16
+// range; products with the bf16 query (exact in fp16 in range) accumulate in
+// fp32.  Softmax weights enter the PV product as fp16 (relative error 2^-11).
+#include <hip/hip_runtime.h>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+#include "kvq_kernels.h"
+
+namespace kvq {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+namespace {
+
+template <int SEL>
+__device__ __forceinline__ h2_t fp4x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+}
+
+__device__ __forceinline__ h2_t bf16x2_to_h2(uint32_t lo_hi) {
+  return __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(lo_hi << 16),
+                                                            __uint_as_float(lo_hi & 0xFFFF0000u)));
+}
+
+__device__ __forceinline__ h2_t splat_bf16(uint32_t s) {
+  const float f = __uint_as_float(s << 16);
+  return __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(f, f));
+}
+
+__device__ __forceinline__ h8_t h8_from(h2_t a, h2_t b, h2_t c, h2_t d) {
+  h8_t r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+// 8 E2M1 codes (one dword) times one scale -> 8 fp16 (A-operand k-slots in order).
+__device__ __forceinline__ h8_t dequant8(uint32_t w, h2_t s) {
+  return h8_from(fp4x2<0>(w) * s, fp4x2<1>(w) * s, fp4x2<2>(w) * s, fp4x2<3>(w) * s);
+}
+
+// Bytes of one 32-token tile in a wave's LDS stage: K codes, K scales, V codes, V scales.
+constexpr int kStKc = 0, kStKs = 2048, kStVc = 2560, kStVs = 4608, kStage = 5120;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Direct-to-LDS loads of one tile (8 instructions per wave): lane i moves bytes
+// [size*i, size*i + size) of each chunk.  The token offset travels in the
+// bounds-checked VGPR offset, so a tile past the end of the resource (including
+// the no-tile sentinel, t0 = capacity) reads zeros and touches no memory.
+__device__ __forceinline__ void issue_tile(uint8_t* st, int lane, int t0, __amdgpu_buffer_rsrc_t kc,
+                                           __amdgpu_buffer_rsrc_t ks, __amdgpu_buffer_rsrc_t vc,
+                                           __amdgpu_buffer_rsrc_t vs) {
+  const int co = t0 * 64 + lane * 16, so = t0 * 16 + lane * 4;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(kc, (lds_ptr_t)(st + kStKc), 16, co, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(kc, (lds_ptr_t)(st + kStKc + 1024), 16, co + 1024, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(ks, (lds_ptr_t)(st + kStKs), 4, so, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(ks, (lds_ptr_t)(st + kStKs + 256), 4, so + 256, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(vc, (lds_ptr_t)(st + kStVc), 16, co, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(vc, (lds_ptr_t)(st + kStVc + 1024), 16, co + 1024, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(vs, (lds_ptr_t)(st + kStVs), 4, so, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(vs, (lds_ptr_t)(st + kStVs + 256), 4, so + 256, 0, 0, 0);
+}
+
+// Everything one wave carries across tiles.
+template <int G>
+struct WaveState {
+  h8_t qf[4];
+  float m_run, l_run;
+  f4_t o[8];
+};
+
+// One tile: read this lane's fragments from the stage, then (once the reads
+// have returned) refill the stage with tile `t_next` (the sentinel `capacity`
+// when there is none, so that the refill is unconditional and the compiler's
+// wait counts stay exact), then compute.
+template <int G>
+__device__ __forceinline__ void tile_step(WaveState<G>& w, uint8_t* st, int lane, int t0, int t_end, int t_next,
+                                          float scale_log2, __amdgpu_buffer_rsrc_t kc_r, __amdgpu_buffer_rsrc_t ks_r,
+                                          __amdgpu_buffer_rsrc_t vc_r, __amdgpu_buffer_rsrc_t vs_r) {
+  const int q4 = lane >> 4, c = lane & 15;
+  // A-operand row c of a 16-token block holds token 4*(c%4) + c/4, so that the
+  // C rows 4*q4 + v of a lane quarter are the tokens 4*v + q4.
+  const int row_tok = 4 * (c & 3) + (c >> 2);
+  // Lane byte offsets into the stage; opaque to the optimiser so that every read
+  // below is one base register plus an immediate offset, instead of a hoisted
+  // register per read.
+  int ko = row_tok * 64 + 16 * q4, kso = row_tok * 16 + 4 * q4, vo = q4 * 64 + 4 * c,
+      vso = q4 * 16 + 2 * (c >> 1);
+  asm volatile("" : "+v"(ko), "+v"(kso), "+v"(vo), "+v"(vso));
+  uint4 kw[2];
+  uint32_t s2[2], dv[8], sc[8];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    kw[blk] = *reinterpret_cast<const uint4*>(st + ko + kStKc + 1024 * blk);
+    s2[blk] = *reinterpret_cast<const uint32_t*>(st + kso + kStKs + 256 * blk);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {  // the lane's token j is tile row 4j + q4
+    dv[j] = *reinterpret_cast<const uint32_t*>(st + vo + kStVc + 256 * j);
+    sc[j] = *reinterpret_cast<const uint16_t*>(st + vso + kStVs + 64 * j);
+  }
+  // the reads above must have returned before the stage is overwritten
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  issue_tile(st, lane, t_next, kc_r, ks_r, vc_r, vs_r);
+
+  // ---------------- logits: S^T = K Q^T for the two 16-token blocks
+  f4_t sacc[2];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const h2_t s_lo = splat_bf16(s2[blk] & 0xFFFFu), s_hi = splat_bf16(s2[blk] >> 16);
+    f4_t acc = f4_t{0.f, 0.f, 0.f, 0.f};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8(kw[blk].x, s_lo), w.qf[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8(kw[blk].y, s_lo), w.qf[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8(kw[blk].z, s_hi), w.qf[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8(kw[blk].w, s_hi), w.qf[3], acc, 0, 0, 0);
+    sacc[blk] = acc;
+  }
+  // ---------------- online softmax (this lane: head c, tokens t0 + 16*blk + 4*v + q4)
+  float sv[8];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int tok = t0 + 16 * blk + 4 * v + q4;
+      const float s = tok < t_end ? sacc[blk][v] * scale_log2 : -INFINITY;
+      sv[4 * blk + v] = s;
+      tmax = fmaxf(tmax, s);
+    }
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  // The reference max moves only when the tile max exceeds it by more than 2^8
+  // (weights up to 256 are exact enough in fp16 and cannot overflow), so the
+  // accumulator rescale below is rare.
+  const bool bump = tmax > w.m_run + 8.f;
+  const float m_new = bump ? tmax : w.m_run;
+  const float alpha = bump ? __builtin_amdgcn_exp2f(w.m_run - m_new) : 1.f;
+  h8_t pf;
+  float psum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float p = __builtin_amdgcn_exp2f(sv[j] - m_new);
+    psum += p;
+    pf[j] = (_Float16)p;
+  }
+  w.l_run = w.l_run * alpha + psum;
+  w.m_run = m_new;
+  // O rows are heads 4*q4 + v; head hh's alpha lives in lane hh (quarter 0)
+  if (__ballot(bump && c < G)) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float av = __shfl(alpha, (4 * q4 + v) & 15);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) w.o[nt][v] *= av;
+    }
+  }
+  // ---------------- values: lane (q4, c) takes channels 8c..8c+7 of its 8 tokens.
+  // Byte i of X[p] holds the codes of (token 2p, token 2p+1) for channel 8c + 2i,
+  // of Y[p] for channel 8c + 2i + 1; one converted byte is one k-slot pair of the
+  // PV B operand, so N-tile 2i (2i+1) is built from byte i of X (Y).
+  uint32_t X[4], Y[4];
+  h2_t sp[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    X[p] = (dv[2 * p] & 0x0F0F0F0Fu) | ((dv[2 * p + 1] & 0x0F0F0F0Fu) << 4);
+    Y[p] = ((dv[2 * p] >> 4) & 0x0F0F0F0Fu) | (dv[2 * p + 1] & 0xF0F0F0F0u);
+    sp[p] = bf16x2_to_h2((sc[2 * p] & 0xFFFFu) | (sc[2 * p + 1] << 16));
+  }
+#define KVQ_PV_BYTE(I)                                                                                   \
+  {                                                                                                      \
+    const h8_t bx = h8_from(fp4x2<I>(X[0]) * sp[0], fp4x2<I>(X[1]) * sp[1], fp4x2<I>(X[2]) * sp[2],     \
+                            fp4x2<I>(X[3]) * sp[3]);                                                     \
+    w.o[2 * I] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, bx, w.o[2 * I], 0, 0, 0);                    \
+    const h8_t by = h8_from(fp4x2<I>(Y[0]) * sp[0], fp4x2<I>(Y[1]) * sp[1], fp4x2<I>(Y[2]) * sp[2],     \
+                            fp4x2<I>(Y[3]) * sp[3]);                                                     \
+    w.o[2 * I + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, by, w.o[2 * I + 1], 0, 0, 0);            \
+  }
+  KVQ_PV_BYTE(0)
+  KVQ_PV_BYTE(1)
+  KVQ_PV_BYTE(2)
+  KVQ_PV_BYTE(3)
+#undef KVQ_PV_BYTE
+  // keep the scheduler from interleaving two tiles (register pressure)
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int G>
+__global__ void __launch_bounds__(256, 3) decode_fp4_mfma_kernel(Fp4DecodeArgs a) {
+  // two LDS stages per wave, as separate arrays so that the compiler can tell
+  // which stage a direct-to-LDS load writes and wait only for that one
+  __shared__ __attribute__((aligned(16))) uint8_t stA[4][kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t stB[4][kStage];
+  __shared__ float sm_m[4][16], sm_l[4][16];
+  __shared__ float sm_o[4][G][129];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q4 = lane >> 4, c = lane & 15;
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const size_t bh = (size_t)b * a.H + h;
+  const int L = min(min(a.seq_lens[b], a.max_len), a.cap);
+  const int t_begin = split * a.per_split;
+  const int t_end = min(L, t_begin + a.per_split);
+
+  WaveState<G> w;
+  // B operand of S^T = K Q^T: lane (q4, c) holds head c, channels 32*q4 + 8*i + j for MFMA i
+  {
+    const int head = c < G ? c : 0;
+    const uint16_t* qp = a.q + ((size_t)b * a.Hq + (size_t)h * G + head) * 128 + 32 * q4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(qp + 8 * i);
+      const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        h2_t v = bf16x2_to_h2(wd[j]);
+        w.qf[i][2 * j] = c < G ? v[0] : (_Float16)0.f;
+        w.qf[i][2 * j + 1] = c < G ? v[1] : (_Float16)0.f;
+      }
+    }
+  }
+  w.m_run = -INFINITY;
+  w.l_run = 0.f;
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) w.o[nt] = f4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Buffer resources over this (sequence, KV head)'s rows: 32-bit offsets, and a
+  // read past the end of a resource returns zeros instead of faulting.
+  constexpr int kFlags = 0x00020000;
+  const __amdgpu_buffer_rsrc_t kc_r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.k_codes + bh * a.cap * 64), 0, a.cap * 64, kFlags);
+  const __amdgpu_buffer_rsrc_t ks_r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.k_scale + bh * a.cap * 8), 0, a.cap * 16, kFlags);
+  const __amdgpu_buffer_rsrc_t vc_r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.v_codes + bh * a.cap * 64), 0, a.cap * 64, kFlags);
+  const __amdgpu_buffer_rsrc_t vs_r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.v_scale + bh * a.cap * 8), 0, a.cap * 16, kFlags);
+
+  uint8_t* sa = stA[wave];
+  uint8_t* sb = stB[wave];
+  const int none = a.cap;  // an offset past every resource: reads zeros, no memory traffic
+  auto tile_or_none = [&](int t) { return t < t_end ? t : none; };
+  int t0 = t_begin + wave * 32;
+  issue_tile(sa, lane, tile_or_none(t0), kc_r, ks_r, vc_r, vs_r);
+  issue_tile(sb, lane, tile_or_none(t0 + 128), kc_r, ks_r, vc_r, vs_r);
+  for (; t0 < t_end; t0 += 256) {
+    // the second tile of a pair may lie past t_end: all its tokens are masked
+    tile_step<G>(w, sa, lane, t0, t_end, tile_or_none(t0 + 256), a.scale_log2, kc_r, ks_r, vc_r, vs_r);
+    tile_step<G>(w, sb, lane, t0 + 128, t_end, tile_or_none(t0 + 384), a.scale_log2, kc_r, ks_r, vc_r, vs_r);
+  }
+  // drain the refills still in flight before the waves' LDS is reused or the wave exits
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+
+  // ---------------- combine the four waves, write this split's partial result
+  float l_run = w.l_run;
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (q4 == 0) {
+    sm_m[wave][c] = w.m_run;
+    sm_l[wave][c] = l_run;
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int hh = 4 * q4 + v;
+    if (hh < G) {
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) sm_o[wave][hh][8 * c + nt] = w.o[nt][v];
+    }
+  }
+  __syncthreads();
+  const size_t row0 = (size_t)b * a.Hq + (size_t)h * G;  // first query-head row of this group
+  for (int e = threadIdx.x; e < G * 128; e += 256) {
+    const int hh = e >> 7, ch = e & 127;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sm_m[ww][hh]);
+    float Ls = 0.f, O = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const float mw = sm_m[ww][hh];
+      const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
+      Ls += f * sm_l[ww][hh];
+      O += f * sm_o[ww][hh][ch];
+    }
+    float* p = a.part + ((row0 + hh) * a.splits + split) * 130;
+    p[2 + ch] = O;
+    if (ch == 0) {
+      p[0] = M;
+      p[1] = Ls;
+    }
+  }
+}
+
+}  // namespace
+
+bool fp4_fast_path_ok(const kv_layout& L, int num_q_heads, int q_dtype) {
+  const int G = num_q_heads / L.num_kv_heads;
+  return L.format == KV_FMT_FP4 && L.head_dim == 128 && q_dtype == KV_DT_BF16 &&
+         (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
+}
+
+int launch_decode_fp4_fast(const Fp4DecodeArgs& a, int B, int G, hipStream_t st) {
+  dim3 grid(a.splits, a.H, B);
+  switch (G) {
+    case 1: decode_fp4_mfma_kernel<1><<<grid, 256, 0, st>>>(a); break;
+    case 2: decode_fp4_mfma_kernel<2><<<grid, 256, 0, st>>>(a); break;
+    case 4: decode_fp4_mfma_kernel<4><<<grid, 256, 0, st>>>(a); break;
+    case 8: decode_fp4_mfma_kernel<8><<<grid, 256, 0, st>>>(a); break;
+    case 16: decode_fp4_mfma_kernel<16><<<grid, 256, 0, st>>>(a); break;
+    default: return KV_EUNSUPPORTED;
+  }
+  return KV_OK;
+}
+
+}  // namespace kvq

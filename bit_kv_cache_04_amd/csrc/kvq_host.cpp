@@ -67,19 +67,20 @@ int prepared_query_width(const kv_layout* L) {
 
 int value_width(const kv_layout* L) { return L->head_dim; }
 
-SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int max_seq_len, int requested) {
-  // Enough workgroups to keep every CU of a 256-CU part busy several times
-  // over, but no split shorter than 256 tokens.
-  const int tile = 64;
+SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int q_dtype, int max_seq_len, int requested) {
+  // Workgroups cover their split in steps of `tile` tokens; aim for enough
+  // workgroups to keep a 256-CU part busy several times over, but no split
+  // shorter than a few steps.
+  const int G = num_q_heads / L->num_kv_heads;
+  const bool fast = L->format == KV_FMT_FP4 && L->head_dim == 128 && q_dtype == KV_DT_BF16 &&
+                    (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
+  const int tile = fast ? 128 : 64;
   long units = (long)L->batch * L->num_kv_heads;
-  int head_blocks = 1;
-  int G = num_q_heads / L->num_kv_heads;
-  if (G > 16) head_blocks = (G + 15) / 16;
-  units *= head_blocks;
+  if (!fast && G > 16) units *= (G + 15) / 16;
   int splits = requested;
   if (splits <= 0) {
     long want = (2048 + units - 1) / units;
-    long maxs = (max_seq_len + 255) / 256;
+    long maxs = (max_seq_len + 4 * tile - 1) / (4 * tile);
     splits = (int)std::max(1L, std::min(want, maxs));
   }
   if (splits > 1024) splits = 1024;
@@ -92,11 +93,14 @@ SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int max_seq_len, int 
 }
 
 DecodeWorkspace decode_workspace(const kv_layout* L, int num_q_heads, int splits) {
+  // Counters first, at a fixed offset: they must stay zero between calls, and a
+  // later call with another split count must find them where it left them.
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
   DecodeWorkspace w;
   size_t rows = (size_t)L->batch * num_q_heads;
-  w.qprep_off = 0;
-  w.part_off = align(rows * prepared_query_width(L) * sizeof(float));
+  w.cnt_off = 0;
+  w.qprep_off = align((size_t)L->batch * L->num_kv_heads * sizeof(unsigned));
+  w.part_off = w.qprep_off + align(rows * prepared_query_width(L) * sizeof(float));
   w.total = w.part_off + align(rows * (size_t)splits * (value_width(L) + 2) * sizeof(float));
   return w;
 }

@@ -31,12 +31,12 @@ struct SplitPlan {
   int splits;
   int tokens_per_split;
 };
-SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int max_seq_len, int requested);
+SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int q_dtype, int max_seq_len, int requested);
 
 // Workspace of a decode call: prepared queries, then per-split partial results
 // (running max, running sum, unnormalised output) — offsets in bytes.
 struct DecodeWorkspace {
-  size_t qprep_off, part_off, total;
+  size_t qprep_off, part_off, cnt_off, total;
 };
 DecodeWorkspace decode_workspace(const kv_layout* L, int num_q_heads, int splits);
 

@@ -182,8 +182,10 @@ int kv_quant_append(const kv_cache* c, const void* k, const void* v, int32_t in_
  *             max_seq_len are clamped to it
  *   out       device fp32 [B][Hq][d] (LATENT: [B][Hq][d]); for TURBO the value
  *             path is mapped back with R^T
- *   ws        device workspace of *ws_bytes bytes, 256-byte aligned; ws == NULL
- *             is a size query that writes *ws_bytes and returns KV_OK
+ *   ws        device workspace of *ws_bytes bytes, 256-byte aligned, filled with
+ *             zeros before its first use (every call leaves it zeroed again);
+ *             ws == NULL is a size query that writes *ws_bytes and returns KV_OK.
+ *             Calls that overlap on one workspace race.
  * Errors: num_q_heads not a multiple of H, max_seq_len outside
  * [1, capacity], NULL pointers: KV_EINVAL; workspace smaller than required:
  * KV_EWORKSPACE. */
