@@ -39,28 +39,63 @@ def cpu_baseline(cfg, budget_s=12.0):
     from oracle import attention as OA
     from oracle import formats as OF
     from oracle.bytes import per_token_head
+    from oracle.lloyd_max import canonical_codebook
+    from oracle.rotation import canonical_projection, canonical_rotation
 
-    if cfg.fmt != "fp4":
-        return None
     T = cfg.context
     unit = cfg.scaled(batch=1, hkv=1, hq=cfg.group)
-    K, V = synth.make_kv(unit, device="cpu")
-    enc = OF.encode_cache("fp4", K.float().numpy().astype(np.float64), V.float().numpy().astype(np.float64))
+    consts = {}
+    if cfg.fmt == "turbo":
+        consts["rot"] = canonical_rotation(synth.gaussian_matrix(cfg.seed, cfg.head_dim, cfg.head_dim, stream=1))
+        consts["levels"], consts["thresholds"] = canonical_codebook(2, cfg.head_dim)
+    if cfg.fmt in ("turbo", "qjl1"):
+        consts["proj"] = canonical_projection(synth.gaussian_matrix(cfg.seed, 128, cfg.head_dim, stream=2))
+    enc_parts = []
+    for t0 in range(0, T, 65536):
+        t1 = min(T, t0 + 65536)
+        if cfg.fmt == "latent":
+            lat = synth.make_latent(unit, 0, 1, t0, t1, device="cpu").float().numpy().astype(np.float64)
+            enc_parts.append(OF.encode_cache("latent", latent=lat, latent_dim=cfg.head_dim))
+        else:
+            K, V = synth.make_kv(unit, 0, 1, t0, t1, device="cpu")
+            enc_parts.append(OF.encode_cache(cfg.fmt, K.float().numpy().astype(np.float64),
+                                             V.float().numpy().astype(np.float64), consts=consts))
+    axis = 1 if cfg.fmt == "latent" else 2
+    enc = {k: np.concatenate([e[k] for e in enc_parts], axis=axis) for k in enc_parts[0]}
     q = synth.make_queries(unit, device="cpu").float().numpy().astype(np.float64)
-    scale = 1.0 / math.sqrt(cfg.head_dim)
+    scale = 1.0 / math.sqrt(cfg.key_width)
     units = 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         while True:
-            OA.decode_attention("fp4", enc, q, [T], scale, 1)
+            OA.decode_attention(cfg.fmt, enc, q, [T], scale, 1, consts, latent_dim=cfg.head_dim)
             units += 1
             el = time.perf_counter() - t0
             if el >= budget_s:
                 break
-    nbytes = units * T * per_token_head("fp4", cfg.head_dim)
+    nbytes = units * T * per_token_head(cfg.fmt, cfg.head_dim, cfg.rope_dim)
     return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{units} x decode of 1 sequence x 1 KV head ({cfg.group} q heads) over {T} tokens, "
-                      f"fp64 numpy, {el:.1f} s"}
+            "sample": f"{units} x decode of 1 sequence x 1 KV head ({unit.hq} q heads) over {T} tokens, "
+                      f"fp64 numpy on 1 thread, {el:.1f} s"}
+
+
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def roofline(cfg, nbytes, dec_ms):
+    """Roofline of the split-context attention kernel, timed by events around its launch."""
+    if cfg.fmt == "latent":
+        # 128 heads x (576 + 512) x 2 flop per token: a dense contraction on fp16 matrix cores
+        flops = 2.0 * cfg.batch * cfg.context * cfg.hq * (cfg.key_width + cfg.head_dim)
+        ach = flops / (dec_ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "split-context attention", "kernel_us": round(dec_ms * 1e3, 2),
+                "hbm_gbs": round(nbytes / (dec_ms * 1e-3) / 1e9, 2)}
+    ach = nbytes / (dec_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "split-context attention", "kernel_us": round(dec_ms * 1e3, 2)}
 
 
 def main():
@@ -94,21 +129,26 @@ def main():
     cache = PackedKVCache(cfg.fmt, cfg.batch, cfg.hkv, cfg.head_dim, cfg.context, cfg.rope_dim, device=dev,
                           constants=consts)
     T = cfg.context
-    # prefill T-1 tokens (untimed), one sequence and 16K tokens at a time to bound input memory
+    # prefill the first T - n tokens (untimed), one sequence and 16K tokens at a
+    # time to bound input memory
+    # KIVI keys are quantised per whole 32-token group, so its step appends one group
+    n_new = 32 if cfg.fmt == "kivi2" else max(1, cfg.append_new)
+    n_pre = T - n_new
     for b in range(cfg.batch):
         seq = cache.sequence(b)
-        for t0 in range(0, T - 1, 16384):
-            t1 = min(T - 1, t0 + 16384)
+        for t0 in range(0, n_pre, 16384):
+            t1 = min(n_pre, t0 + 16384)
             if cfg.fmt == "latent":
                 seq.append(synth.make_latent(cfg, b, b + 1, t0, t1, device=dev), None, t0)
             else:
                 K, V = synth.make_kv(cfg, b, b + 1, t0, t1, device=dev)
                 seq.append(K, V, t0)
-    # the decode token's K/V (appended at T-1 inside every step)
+    # the tokens appended inside every step: the decode token at T-1, or for a
+    # bulk-append workload the last `append_new` tokens of the context
     if cfg.fmt == "latent":
-        k_new, v_new = synth.make_latent(cfg, 0, cfg.batch, T - 1, T, device=dev), None
+        k_new, v_new = synth.make_latent(cfg, 0, cfg.batch, T - n_new, T, device=dev), None
     else:
-        k_new, v_new = synth.make_kv(cfg, 0, cfg.batch, T - 1, T, device=dev)
+        k_new, v_new = synth.make_kv(cfg, 0, cfg.batch, T - n_new, T, device=dev)
     q = synth.make_queries(cfg, device=dev)
     lens = torch.full((cfg.batch,), T, dtype=torch.int32, device=dev)
     scale = 1.0 / math.sqrt(cfg.key_width)
@@ -123,7 +163,7 @@ def main():
         b.record()
 
     def step(i=None):
-        cache.append(k_new, v_new, T - 1)
+        cache.append(k_new, v_new, T - n_new)
         cache.decode(q, lens, scale, splits=args.splits, out=out, ws=ws,
                      events=None if i is None else ev[i])
 
@@ -163,9 +203,7 @@ def main():
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "query_tokens_per_s": round(cfg.batch / (ms_step * 1e-3), 1),
         "wall_s": round(wall, 3),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode_split_kernel", "kernel_us": round(dec_ms * 1e3, 2)},
+        "roofline": roofline(cfg, nbytes, dec_ms),
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg)

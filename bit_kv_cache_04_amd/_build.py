@@ -22,22 +22,22 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into libkvq.so next to this file; returns its path."""
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile every source into libkvq.so next to this file (or `out`); returns its path."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC] + FLAGS + ["-o", tmp] + srcs + ["-lamdhip64"]
+    tmp = out + ".tmp"
+    cmd = [HIPCC] + FLAGS + [f"-D{d}" for d in defines] + ["-o", tmp] + srcs + ["-lamdhip64"]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    out = "\n".join(l for l in res.stdout.splitlines() if "packed-fp32-ops" not in l)
+    log = "\n".join(l for l in res.stdout.splitlines() if "packed-fp32-ops" not in l)
     if res.returncode != 0:
-        sys.stderr.write(out + "\n")
+        sys.stderr.write(log + "\n")
         raise RuntimeError("hipcc failed building libkvq.so")
-    if verbose and out.strip():
-        print(out)
-    os.replace(tmp, LIB)
-    return LIB
+    if verbose and log.strip():
+        print(log)
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

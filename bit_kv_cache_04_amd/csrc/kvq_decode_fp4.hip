@@ -205,13 +205,23 @@ __device__ __forceinline__ void tile_step(WaveState<G>& w, uint8_t* st, int lane
 }
 
 template <int G>
-__global__ void __launch_bounds__(256, 3) decode_fp4_mfma_kernel(Fp4DecodeArgs a) {
+#ifndef KVQ_FP4_WAVES_PER_EU
+#define KVQ_FP4_WAVES_PER_EU 3  // waves per SIMD the register budget is cut for
+#endif
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(KVQ_FP4_WAVES_PER_EU, KVQ_FP4_WAVES_PER_EU))) decode_fp4_mfma_kernel(Fp4DecodeArgs a) {
   // two LDS stages per wave, as separate arrays so that the compiler can tell
   // which stage a direct-to-LDS load writes and wait only for that one
   __shared__ __attribute__((aligned(16))) uint8_t stA[4][kStage];
   __shared__ __attribute__((aligned(16))) uint8_t stB[4][kStage];
-  __shared__ float sm_m[4][16], sm_l[4][16];
-  __shared__ float sm_o[4][G][129];
+  // the waves' running max / sum are combined through stage-B memory, their
+  // outputs through stage-A memory when they fit there (G <= 8), else through a
+  // buffer of their own; both stages are idle by then
+  float (*sm_m)[16] = reinterpret_cast<float (*)[16]>(&stB[0][0]);
+  float (*sm_l)[16] = reinterpret_cast<float (*)[16]>(&stB[0][0] + 4 * 16 * sizeof(float));
+  constexpr bool kAliasA = sizeof(float) * 4 * G * 129 <= sizeof(stA);
+  __shared__ float sm_own[kAliasA ? 1 : 4 * G * 129];
+  float (*sm_o)[G][129] = reinterpret_cast<float (*)[G][129]>(kAliasA ? (void*)&stA[0][0] : (void*)sm_own);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q4 = lane >> 4, c = lane & 15;
@@ -271,24 +281,29 @@ __global__ void __launch_bounds__(256, 3) decode_fp4_mfma_kernel(Fp4DecodeArgs a
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
   // ---------------- combine the four waves, write this split's partial result
+  // (lane indices are recomputed here rather than kept live across the loop)
+  __syncthreads();  // every wave is done with its stages before they hold outputs
+  const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int q4e = lane_e >> 4, ce = lane_e & 15;
+  const int tid_e = wave * 64 + lane_e;
   float l_run = w.l_run;
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  if (q4 == 0) {
-    sm_m[wave][c] = w.m_run;
-    sm_l[wave][c] = l_run;
+  if (q4e == 0) {
+    sm_m[wave][ce] = w.m_run;
+    sm_l[wave][ce] = l_run;
   }
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const int hh = 4 * q4 + v;
+    const int hh = 4 * q4e + v;
     if (hh < G) {
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) sm_o[wave][hh][8 * c + nt] = w.o[nt][v];
+      for (int nt = 0; nt < 8; ++nt) sm_o[wave][hh][8 * ce + nt] = w.o[nt][v];
     }
   }
   __syncthreads();
   const size_t row0 = (size_t)b * a.Hq + (size_t)h * G;  // first query-head row of this group
-  for (int e = threadIdx.x; e < G * 128; e += 256) {
+  for (int e = tid_e; e < G * 128; e += 256) {
     const int hh = e >> 7, ch = e & 127;
     float M = -INFINITY;
 #pragma unroll

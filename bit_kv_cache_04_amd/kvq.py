@@ -10,7 +10,8 @@ import os
 
 import numpy as np
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
+# KVQ_LIBRARY names another build of the same library (e.g. a debug build).
+_LIB_PATH = os.environ.get("KVQ_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
 
 # enum kv_format
 FMT = {"bf16": 0, "kivi2": 1, "fp4": 2, "turbo": 3, "qjl1": 4, "latent": 5}
