@@ -320,35 +320,43 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
   const int B = L.batch;
   const int rows = B * num_q_heads;
   const int qw_in = query_width(&L), qw_out = prepared_query_width(&L);
-  if (fp4_fast_path_ok(L, num_q_heads, q_dtype)) {
-    Fp4DecodeArgs f{};
+  const bool mfma = mfma_fast_path_ok(L, num_q_heads, q_dtype);
+  // FP4 keys read the caller's bf16 queries as they are; every other format
+  // first prepares its fp32 query (projection / rotation)
+  if (!(mfma && L.format == KV_FMT_FP4)) {
+    if (q_dtype == KV_DT_F32)
+      prep_query_kernel<float><<<rows, 128, 0, st>>>(static_cast<const float*>(q), qw_in, qw_out, L.format,
+                                                     c->rot, c->proj, qv);
+    else
+      prep_query_kernel<uint16_t><<<rows, 128, 0, st>>>(static_cast<const uint16_t*>(q), qw_in, qw_out,
+                                                        L.format, c->rot, c->proj, qv);
+  }
+  if (mfma) {
+    MfmaDecodeArgs f{};
     f.k_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_K_CODES]);
     f.k_scale = static_cast<const uint16_t*>(c->buf[KV_BUF_K_SCALE]);
+    f.k_sketch = static_cast<const uint8_t*>(c->buf[KV_BUF_K_SKETCH]);
+    f.k_norm = static_cast<const uint16_t*>(c->buf[KV_BUF_K_NORM]);
     f.v_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_V_CODES]);
     f.v_scale = static_cast<const uint16_t*>(c->buf[KV_BUF_V_SCALE]);
-    f.q = static_cast<const uint16_t*>(q);
+    f.q = L.format == KV_FMT_FP4 ? q : static_cast<const void*>(qv);
     f.seq_lens = seq_lens;
     f.max_len = max_seq_len;
     f.H = L.num_kv_heads;
     f.cap = L.capacity;
     f.Hq = num_q_heads;
     f.scale_log2 = scale * kLog2e;
+    f.kappa = (float)(1.2533141373155002512 / (double)(L.qjl_m > 0 ? L.qjl_m : 1));
     f.part = part;
     f.splits = plan.splits;
     f.per_split = plan.tokens_per_split;
     if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), st) != hipSuccess) return KV_EDEVICE;
-    int rc = launch_decode_fp4_fast(f, B, num_q_heads / L.num_kv_heads, st);
+    int rc = launch_decode_mfma(f, L.format, B, num_q_heads / L.num_kv_heads, st);
     if (rc != KV_OK) return rc;
     if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess) return KV_EDEVICE;
     launch_merge(part, rows, plan.splits, L.head_dim, L.format, c->rot, out, st);
     return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
   }
-  if (q_dtype == KV_DT_F32)
-    prep_query_kernel<float><<<rows, 128, 0, st>>>(static_cast<const float*>(q), qw_in, qw_out, L.format,
-                                                   c->rot, c->proj, qv);
-  else
-    prep_query_kernel<uint16_t><<<rows, 128, 0, st>>>(static_cast<const uint16_t*>(q), qw_in, qw_out,
-                                                      L.format, c->rot, c->proj, qv);
 
   DecodeArgs a{};
   a.k_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_K_CODES]);

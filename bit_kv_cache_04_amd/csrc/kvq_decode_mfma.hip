@@ -1,0 +1,509 @@
+// Decode attention on the matrix cores (gfx950) for caches whose values are FP4
+// E2M1 with one bf16 scale per 16 channels: FP4 keys, or 1-bit QJL keys.
+//
+// One workgroup = 4 waves over one (sequence, KV head, context split); each
+// wave streams its own 32-token tiles of packed codes from HBM into a private
+// two-stage LDS ring with direct-to-LDS buffer loads (the next tile is in
+// flight while the current one is computed, without holding registers), and
+// keeps an online-softmax state for all query heads of the group.  Per tile
+// and wave:
+//   S^T = K_tile . Q^T   v_mfma_f32_16x16x32_f16 (rows = tokens, cols = heads)
+//   online softmax       per head = per lane column; row max over the 4 lane quarters
+//   O  += P . V_tile     8 v_mfma_f32_16x16x32_f16 (rows = heads, cols = channels)
+// The group's query heads share every packed byte read (page "TurboQuant vs
+// OSCAR vs EpiCache", KV-cache memory bottleneck section: decode is bound by
+// streaming the cache), and scores never leave registers.
+//
+// FP4 element values: an E2M1 code times its bf16 group scale has at most 10
+// significant bits, so it is exact in fp16 while |x| stays within the fp16
+// range; products with the bf16 query (exact in fp16 in range) accumulate in
+// fp32.  Softmax weights enter the PV product as fp16 (relative error 2^-11).
+//
+// QJL keys: the logit is sqrt(pi/2)/m * n * <S q, sigma> with sigma = +-1 from
+// the sketch bits (page "TurboQuant vs OSCAR vs EpiCache", section
+// "quantization frontiers", stage two).  <S q, sigma> = 2 <S q, b> - sum(S q)
+// for the bits b; each bit enters the product as the fp16 value 2^-14 or 0 and
+// S q as an exact fp16 hi + lo pair, so the sum is exact up to fp32 rounding.
+#include <hip/hip_runtime.h>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+#include "kvq_kernels.h"
+
+namespace kvq {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+namespace {
+
+constexpr int kRsrcFlags = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcFlags);
+}
+
+template <int SEL>
+__device__ __forceinline__ h2_t fp4x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+}
+
+__device__ __forceinline__ h2_t bf16x2_to_h2(uint32_t lo_hi) {
+  return __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(lo_hi << 16),
+                                                            __uint_as_float(lo_hi & 0xFFFF0000u)));
+}
+
+__device__ __forceinline__ h2_t splat_bf16(uint32_t s) {
+  const float f = __uint_as_float(s << 16);
+  return __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(f, f));
+}
+
+__device__ __forceinline__ h8_t h8_from(h2_t a, h2_t b, h2_t c, h2_t d) {
+  h8_t r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+// 8 E2M1 codes (one dword) times one scale -> 8 fp16 (A-operand k-slots in order).
+__device__ __forceinline__ h8_t dequant8(uint32_t w, h2_t s) {
+  return h8_from(fp4x2<0>(w) * s, fp4x2<1>(w) * s, fp4x2<2>(w) * s, fp4x2<3>(w) * s);
+}
+
+// Two sketch bits m and m + 16 of w as the fp16 pair (2^-14 * bit_m, 2^-14 * bit_{m+16}):
+// each bit moved onto bit 10 of its half (the lowest exponent bit).
+template <int M>
+__device__ __forceinline__ h2_t bits2(uint32_t w) {
+  const uint32_t x = w & (0x00010001u << M);
+  return __builtin_bit_cast(h2_t, M <= 10 ? (x << (10 - M)) : (x >> (M - 10)));
+}
+
+// A-operand row c of a 16-token block holds token 4*(c%4) + c/4, so that the
+// C rows 4*q4 + v of a lane quarter are the tokens 4*v + q4.
+__device__ __forceinline__ int row_token(int c) { return 4 * (c & 3) + (c >> 2); }
+
+// ---------------------------------------------------------------- key policies
+
+// FP4 keys: codes (64 B per token) and scales (16 B per token).
+struct KeysFp4 {
+  static constexpr int kBytes = 2560;  // codes 2048 | scales 512
+  struct Q {
+    h8_t f[4];  // lane (q4, c): head c, channels 32*q4 + 8*i + j for MFMA i
+  };
+  struct R {
+    __amdgpu_buffer_rsrc_t kc, ks;
+  };
+  struct Frag {
+    uint4 kw[2];
+    uint32_t s2[2];
+  };
+  __device__ static void load_q(Q& q, const MfmaDecodeArgs& a, int b, int h, int G, int q4, int c) {
+    const int head = c < G ? c : 0;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G + head) * 128 + 32 * q4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(qp + 8 * i);
+      const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const h2_t v = bf16x2_to_h2(wd[j]);
+        q.f[i][2 * j] = c < G ? v[0] : (_Float16)0.f;
+        q.f[i][2 * j + 1] = c < G ? v[1] : (_Float16)0.f;
+      }
+    }
+  }
+  __device__ static R resources(const MfmaDecodeArgs& a, size_t bh) {
+    return R{rsrc(a.k_codes + bh * a.cap * 64, (size_t)a.cap * 64),
+             rsrc(a.k_scale + bh * a.cap * 8, (size_t)a.cap * 16)};
+  }
+  __device__ static void issue(uint8_t* st, int lane, int t0, const R& r) {
+    const int co = t0 * 64 + lane * 16, so = t0 * 16 + lane * 4;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.kc, (lds_ptr_t)(st), 16, co, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.kc, (lds_ptr_t)(st + 1024), 16, co + 1024, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.ks, (lds_ptr_t)(st + 2048), 4, so, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.ks, (lds_ptr_t)(st + 2304), 4, so + 256, 0, 0, 0);
+  }
+  __device__ static void read(Frag& f, const uint8_t* st, int q4, int c) {
+    int ko = row_token(c) * 64 + 16 * q4, kso = row_token(c) * 16 + 4 * q4;
+    asm volatile("" : "+v"(ko), "+v"(kso));
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      f.kw[blk] = *reinterpret_cast<const uint4*>(st + ko + 1024 * blk);
+      f.s2[blk] = *reinterpret_cast<const uint32_t*>(st + kso + 2048 + 256 * blk);
+    }
+  }
+  // raw logits of the lane's 8 (token, head) pairs: [blk][v] for token 16 blk + 4 v + q4
+  __device__ static void logits(const Frag& f, const Q& q, f4_t sacc[2]) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const h2_t s_lo = splat_bf16(f.s2[blk] & 0xFFFFu), s_hi = splat_bf16(f.s2[blk] >> 16);
+      f4_t acc = f4_t{0.f, 0.f, 0.f, 0.f};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8(f.kw[blk].x, s_lo), q.f[0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8(f.kw[blk].y, s_lo), q.f[1], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8(f.kw[blk].z, s_hi), q.f[2], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8(f.kw[blk].w, s_hi), q.f[3], acc, 0, 0, 0);
+      sacc[blk] = acc;
+    }
+  }
+};
+
+// 1-bit QJL keys: 128 sketch bits (16 B per token) and the fp16 key norm.
+struct KeysQjl {
+  static constexpr int kBytes = 768;  // sketch 512 | norms, one per dword: 128 (+ 128 zeros)
+  struct Q {
+    // lane (q4, c): head c; MFMA i, k-slot pair p, element e <-> sketch row 32*q4 + 4*i + p + 16*e
+    h8_t hi[4], lo[4];
+    float sumq;  // sum of the head's 128 projected-query values
+  };
+  struct R {
+    __amdgpu_buffer_rsrc_t sk, nm;
+    int nm_end;  // byte size of the norm resource: an offset that reads zeros
+  };
+  struct Frag {
+    uint32_t w[2];   // sketch rows 32*q4 .. 32*q4 + 31 of token row_token(c)
+    uint32_t n[8];   // fp16 norm bits of tokens 16 blk + 4 v + q4
+  };
+  __device__ static void load_q(Q& q, const MfmaDecodeArgs& a, int b, int h, int G, int q4, int c) {
+    const int head = c < G ? c : 0;
+    const float* qp = static_cast<const float*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G + head) * 128 + 32 * q4;
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float v = c < G ? qp[4 * i + p + 16 * e] : 0.f;
+          const _Float16 hi = (_Float16)v;
+          q.hi[i][2 * p + e] = hi;
+          q.lo[i][2 * p + e] = (_Float16)(v - (float)hi);
+          s += v;
+        }
+    s += __shfl_xor(s, 16);
+    s += __shfl_xor(s, 32);
+    q.sumq = s;
+  }
+  __device__ static R resources(const MfmaDecodeArgs& a, size_t bh) {
+    return R{rsrc(a.k_sketch + bh * a.cap * 16, (size_t)a.cap * 16),
+             rsrc(a.k_norm + bh * a.cap, (size_t)a.cap * 2), a.cap * 2};
+  }
+  __device__ static void issue(uint8_t* st, int lane, int t0, const R& r) {
+    const int so = t0 * 16 + lane * 4;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.sk, (lds_ptr_t)(st), 4, so, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.sk, (lds_ptr_t)(st + 256), 4, so + 256, 0, 0, 0);
+    // one 2-byte norm per lane for lanes 0..31 (a 2-byte load lands in its lane's
+    // dword of LDS, zero-extended); lanes 32..63 read past the resource and write
+    // zeros.  2-byte granules keep the range check exact: a dword holding the
+    // last token of an odd capacity would straddle the end and read as zero.
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.nm, (lds_ptr_t)(st + 512), 2, lane < 32 ? t0 * 2 + lane * 2 : r.nm_end,
+                                             0, 0, 0);
+  }
+  __device__ static void read(Frag& f, const uint8_t* st, int q4, int c) {
+    int so = row_token(c) * 16 + 4 * q4, no = 512 + 4 * q4;
+    asm volatile("" : "+v"(so), "+v"(no));
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) f.w[blk] = *reinterpret_cast<const uint32_t*>(st + so + 256 * blk);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f.n[j] = *reinterpret_cast<const uint16_t*>(st + no + 16 * j);
+  }
+  __device__ static void logits(const Frag& f, const Q& q, float kappa, f4_t sacc[2]) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const uint32_t w = f.w[blk];
+      f4_t acc = f4_t{0.f, 0.f, 0.f, 0.f};
+#define KVQ_QJL_STEP(I)                                                                                  \
+  {                                                                                                      \
+    const h8_t A = h8_from(bits2<4 * I + 0>(w), bits2<4 * I + 1>(w), bits2<4 * I + 2>(w), bits2<4 * I + 3>(w)); \
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, q.hi[I], acc, 0, 0, 0);                               \
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, q.lo[I], acc, 0, 0, 0);                               \
+  }
+      KVQ_QJL_STEP(0)
+      KVQ_QJL_STEP(1)
+      KVQ_QJL_STEP(2)
+      KVQ_QJL_STEP(3)
+#undef KVQ_QJL_STEP
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float n = f16_to_f32((uint16_t)f.n[4 * blk + v]);
+        // acc = 2^-14 <S q, b>: <S q, sigma> = 2^15 acc - sum(S q)
+        acc[v] = kappa * n * fmaf(32768.f, acc[v], -q.sumq);
+      }
+      sacc[blk] = acc;
+    }
+  }
+};
+
+// ---------------------------------------------------------------- the kernel
+
+template <class KP>
+__device__ __forceinline__ void logits_of(const typename KP::Frag& f, const typename KP::Q& q,
+                                          const MfmaDecodeArgs& a, f4_t sacc[2]);
+template <>
+__device__ __forceinline__ void logits_of<KeysFp4>(const KeysFp4::Frag& f, const KeysFp4::Q& q,
+                                                   const MfmaDecodeArgs&, f4_t sacc[2]) {
+  KeysFp4::logits(f, q, sacc);
+}
+template <>
+__device__ __forceinline__ void logits_of<KeysQjl>(const KeysQjl::Frag& f, const KeysQjl::Q& q,
+                                                   const MfmaDecodeArgs& a, f4_t sacc[2]) {
+  KeysQjl::logits(f, q, a.kappa, sacc);
+}
+
+// V region of a stage (after the keys): codes 2048 | scales 512.
+template <class KP>
+struct Stage {
+  static constexpr int kVc = KP::kBytes, kVs = KP::kBytes + 2048, kBytes = KP::kBytes + 2560;
+};
+
+struct VRsrc {
+  __amdgpu_buffer_rsrc_t vc, vs;
+};
+
+// Direct-to-LDS loads of one tile: lane i moves bytes [size*i, size*i + size) of
+// each chunk.  The token offset travels in the bounds-checked VGPR offset, so a
+// tile past the end of the resource (including the no-tile sentinel, t0 =
+// capacity) reads zeros and touches no memory.
+template <class KP>
+__device__ __forceinline__ void issue_tile(uint8_t* st, int lane, int t0, const typename KP::R& kr,
+                                           const VRsrc& vr) {
+  KP::issue(st, lane, t0, kr);
+  const int co = t0 * 64 + lane * 16, so = t0 * 16 + lane * 4;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(vr.vc, (lds_ptr_t)(st + Stage<KP>::kVc), 16, co, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(vr.vc, (lds_ptr_t)(st + Stage<KP>::kVc + 1024), 16, co + 1024, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(vr.vs, (lds_ptr_t)(st + Stage<KP>::kVs), 4, so, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(vr.vs, (lds_ptr_t)(st + Stage<KP>::kVs + 256), 4, so + 256, 0, 0, 0);
+}
+
+// Everything one wave carries across tiles.
+template <class KP>
+struct WaveState {
+  typename KP::Q q;
+  float m_run, l_run;
+  f4_t o[8];
+};
+
+// One tile: read this lane's fragments from the stage, then (once the reads
+// have returned) refill the stage with tile `t_next` (the sentinel `capacity`
+// when there is none, so that the refill is unconditional and the compiler's
+// wait counts stay exact), then compute.
+template <int G, class KP>
+__device__ __forceinline__ void tile_step(WaveState<KP>& w, uint8_t* st, int lane, int t0, int t_end, int t_next,
+                                          const MfmaDecodeArgs& a, const typename KP::R& kr, const VRsrc& vr) {
+  const int q4 = lane >> 4, c = lane & 15;
+  typename KP::Frag kf;
+  KP::read(kf, st, q4, c);
+  // Lane byte offsets into the stage; opaque to the optimiser so that every read
+  // below is one base register plus an immediate offset, instead of a hoisted
+  // register per read.
+  int vo = q4 * 64 + 4 * c, vso = q4 * 16 + 2 * (c >> 1);
+  asm volatile("" : "+v"(vo), "+v"(vso));
+  uint32_t dv[8], sc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {  // the lane's token j is tile row 4j + q4
+    dv[j] = *reinterpret_cast<const uint32_t*>(st + vo + Stage<KP>::kVc + 256 * j);
+    sc[j] = *reinterpret_cast<const uint16_t*>(st + vso + Stage<KP>::kVs + 64 * j);
+  }
+  // the reads above must have returned before the stage is overwritten
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  issue_tile<KP>(st, lane, t_next, kr, vr);
+
+  // ---------------- logits: S^T = K Q^T for the two 16-token blocks
+  f4_t sacc[2];
+  logits_of<KP>(kf, w.q, a, sacc);
+  // ---------------- online softmax (this lane: head c, tokens t0 + 16*blk + 4*v + q4)
+  float sv[8];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int tok = t0 + 16 * blk + 4 * v + q4;
+      const float s = tok < t_end ? sacc[blk][v] * a.scale_log2 : -INFINITY;
+      sv[4 * blk + v] = s;
+      tmax = fmaxf(tmax, s);
+    }
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  // The reference max moves only when the tile max exceeds it by more than 2^8
+  // (weights up to 256 are exact enough in fp16 and cannot overflow), so the
+  // accumulator rescale below is rare.
+  const bool bump = tmax > w.m_run + 8.f;
+  const float m_new = bump ? tmax : w.m_run;
+  const float alpha = bump ? __builtin_amdgcn_exp2f(w.m_run - m_new) : 1.f;
+  h8_t pf;
+  float psum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float p = __builtin_amdgcn_exp2f(sv[j] - m_new);
+    psum += p;
+    pf[j] = (_Float16)p;
+  }
+  w.l_run = w.l_run * alpha + psum;
+  w.m_run = m_new;
+  // O rows are heads 4*q4 + v; head hh's alpha lives in lane hh (quarter 0)
+  if (__ballot(bump && c < G)) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float av = __shfl(alpha, (4 * q4 + v) & 15);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) w.o[nt][v] *= av;
+    }
+  }
+  // ---------------- values: lane (q4, c) takes channels 8c..8c+7 of its 8 tokens.
+  // Byte i of X[p] holds the codes of (token 2p, token 2p+1) for channel 8c + 2i,
+  // of Y[p] for channel 8c + 2i + 1; one converted byte is one k-slot pair of the
+  // PV B operand, so N-tile 2i (2i+1) is built from byte i of X (Y).
+  uint32_t X[4], Y[4];
+  h2_t sp[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    X[p] = (dv[2 * p] & 0x0F0F0F0Fu) | ((dv[2 * p + 1] & 0x0F0F0F0Fu) << 4);
+    Y[p] = ((dv[2 * p] >> 4) & 0x0F0F0F0Fu) | (dv[2 * p + 1] & 0xF0F0F0F0u);
+    sp[p] = bf16x2_to_h2((sc[2 * p] & 0xFFFFu) | (sc[2 * p + 1] << 16));
+  }
+#define KVQ_PV_BYTE(I)                                                                                   \
+  {                                                                                                      \
+    const h8_t bx = h8_from(fp4x2<I>(X[0]) * sp[0], fp4x2<I>(X[1]) * sp[1], fp4x2<I>(X[2]) * sp[2],     \
+                            fp4x2<I>(X[3]) * sp[3]);                                                     \
+    w.o[2 * I] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, bx, w.o[2 * I], 0, 0, 0);                    \
+    const h8_t by = h8_from(fp4x2<I>(Y[0]) * sp[0], fp4x2<I>(Y[1]) * sp[1], fp4x2<I>(Y[2]) * sp[2],     \
+                            fp4x2<I>(Y[3]) * sp[3]);                                                     \
+    w.o[2 * I + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, by, w.o[2 * I + 1], 0, 0, 0);            \
+  }
+  KVQ_PV_BYTE(0)
+  KVQ_PV_BYTE(1)
+  KVQ_PV_BYTE(2)
+  KVQ_PV_BYTE(3)
+#undef KVQ_PV_BYTE
+  // keep the scheduler from interleaving two tiles (register pressure)
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+#ifndef KVQ_MFMA_WAVES_PER_EU
+#define KVQ_MFMA_WAVES_PER_EU 3  // waves per SIMD the register budget is cut for
+#endif
+
+template <int G, class KP>
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(KVQ_MFMA_WAVES_PER_EU, KVQ_MFMA_WAVES_PER_EU))) decode_mfma_kernel(MfmaDecodeArgs a) {
+  constexpr int kStage = Stage<KP>::kBytes;
+  // two LDS stages per wave, as separate arrays so that the compiler can tell
+  // which stage a direct-to-LDS load writes and wait only for that one
+  __shared__ __attribute__((aligned(16))) uint8_t stA[4][kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t stB[4][kStage];
+  // the waves' running max / sum are combined through stage-B memory, their
+  // outputs through stage-A memory when they fit there, else through a buffer
+  // of their own; both stages are idle by then
+  constexpr bool kAliasA = sizeof(float) * 4 * G * 129 <= sizeof(stA);
+  __shared__ float sm_own[kAliasA ? 1 : 4 * G * 129];
+  float (*sm_o)[G][129] = reinterpret_cast<float (*)[G][129]>(kAliasA ? (void*)&stA[0][0] : (void*)sm_own);
+  float (*sm_m)[16] = reinterpret_cast<float (*)[16]>(&stB[0][0]);
+  float (*sm_l)[16] = reinterpret_cast<float (*)[16]>(&stB[0][0] + 4 * 16 * sizeof(float));
+  static_assert(2 * 4 * 16 * sizeof(float) <= sizeof(stB), "stage B too small");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const size_t bh = (size_t)b * a.H + h;
+  const int L = min(min(a.seq_lens[b], a.max_len), a.cap);
+  const int t_begin = split * a.per_split;
+  const int t_end = min(L, t_begin + a.per_split);
+
+  WaveState<KP> w;
+  KP::load_q(w.q, a, b, h, G, lane >> 4, lane & 15);
+  w.m_run = -INFINITY;
+  w.l_run = 0.f;
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) w.o[nt] = f4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Buffer resources over this (sequence, KV head)'s rows: 32-bit offsets, and a
+  // read past the end of a resource returns zeros instead of faulting.
+  const typename KP::R kr = KP::resources(a, bh);
+  const VRsrc vr{rsrc(a.v_codes + bh * a.cap * 64, (size_t)a.cap * 64),
+                 rsrc(a.v_scale + bh * a.cap * 8, (size_t)a.cap * 16)};
+
+  uint8_t* sa = stA[wave];
+  uint8_t* sb = stB[wave];
+  const int none = a.cap;  // an offset past every resource: reads zeros, no memory traffic
+  auto tile_or_none = [&](int t) { return t < t_end ? t : none; };
+  int t0 = t_begin + wave * 32;
+  issue_tile<KP>(sa, lane, tile_or_none(t0), kr, vr);
+  issue_tile<KP>(sb, lane, tile_or_none(t0 + 128), kr, vr);
+  for (; t0 < t_end; t0 += 256) {
+    // the second tile of a pair may lie past t_end: all its tokens are masked
+    tile_step<G, KP>(w, sa, lane, t0, t_end, tile_or_none(t0 + 256), a, kr, vr);
+    tile_step<G, KP>(w, sb, lane, t0 + 128, t_end, tile_or_none(t0 + 384), a, kr, vr);
+  }
+  // drain the refills still in flight before the waves' LDS is reused or the wave exits
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+
+  // ---------------- combine the four waves, write this split's partial result
+  // (lane indices are recomputed here rather than kept live across the loop)
+  __syncthreads();  // every wave is done with its stages before they hold outputs
+  const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int q4e = lane_e >> 4, ce = lane_e & 15;
+  const int tid_e = wave * 64 + lane_e;
+  float l_run = w.l_run;
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (q4e == 0) {
+    sm_m[wave][ce] = w.m_run;
+    sm_l[wave][ce] = l_run;
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int hh = 4 * q4e + v;
+    if (hh < G) {
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) sm_o[wave][hh][8 * ce + nt] = w.o[nt][v];
+    }
+  }
+  __syncthreads();
+  const size_t row0 = (size_t)b * a.Hq + (size_t)h * G;  // first query-head row of this group
+  for (int e = tid_e; e < G * 128; e += 256) {
+    const int hh = e >> 7, ch = e & 127;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sm_m[ww][hh]);
+    float Ls = 0.f, O = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const float mw = sm_m[ww][hh];
+      const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
+      Ls += f * sm_l[ww][hh];
+      O += f * sm_o[ww][hh][ch];
+    }
+    float* p = a.part + ((row0 + hh) * a.splits + split) * 130;
+    p[2 + ch] = O;
+    if (ch == 0) {
+      p[0] = M;
+      p[1] = Ls;
+    }
+  }
+}
+
+template <class KP>
+int launch_g(const MfmaDecodeArgs& a, int B, int G, hipStream_t st) {
+  dim3 grid(a.splits, a.H, B);
+  switch (G) {
+    case 1: decode_mfma_kernel<1, KP><<<grid, 256, 0, st>>>(a); break;
+    case 2: decode_mfma_kernel<2, KP><<<grid, 256, 0, st>>>(a); break;
+    case 4: decode_mfma_kernel<4, KP><<<grid, 256, 0, st>>>(a); break;
+    case 8: decode_mfma_kernel<8, KP><<<grid, 256, 0, st>>>(a); break;
+    case 16: decode_mfma_kernel<16, KP><<<grid, 256, 0, st>>>(a); break;
+    default: return KV_EUNSUPPORTED;
+  }
+  return KV_OK;
+}
+
+}  // namespace
+
+int launch_decode_mfma(const MfmaDecodeArgs& a, int format, int B, int G, hipStream_t st) {
+  if (format == KV_FMT_FP4) return launch_g<KeysFp4>(a, B, G, st);
+  if (format == KV_FMT_QJL1_FP4V) return launch_g<KeysQjl>(a, B, G, st);
+  return KV_EUNSUPPORTED;
+}
+
+}  // namespace kvq

@@ -67,13 +67,21 @@ int prepared_query_width(const kv_layout* L) {
 
 int value_width(const kv_layout* L) { return L->head_dim; }
 
+bool mfma_fast_path_ok(const kv_layout& L, int num_q_heads, int q_dtype) {
+  const int G = num_q_heads / L.num_kv_heads;
+  const bool g_ok = G == 1 || G == 2 || G == 4 || G == 8 || G == 16;
+  if (!g_ok || L.head_dim != 128) return false;
+  if (L.format == KV_FMT_FP4) return q_dtype == KV_DT_BF16;
+  if (L.format == KV_FMT_QJL1_FP4V) return L.qjl_m == 128;
+  return false;
+}
+
 SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int q_dtype, int max_seq_len, int requested) {
   // Workgroups cover their split in steps of `tile` tokens; aim for enough
   // workgroups to keep a 256-CU part busy several times over, but no split
   // shorter than a few steps.
   const int G = num_q_heads / L->num_kv_heads;
-  const bool fast = L->format == KV_FMT_FP4 && L->head_dim == 128 && q_dtype == KV_DT_BF16 &&
-                    (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
+  const bool fast = mfma_fast_path_ok(*L, num_q_heads, q_dtype);
   const int tile = fast ? 128 : 64;
   long units = (long)L->batch * L->num_kv_heads;
   if (!fast && G > 16) units *= (G + 15) / 16;

@@ -8,21 +8,24 @@
 
 namespace kvq {
 
-// FP4 cache, head_dim 128, bf16 queries, G = Hq / H in {1, 2, 4, 8, 16}.
-struct Fp4DecodeArgs {
-  const uint8_t* k_codes;
-  const uint16_t* k_scale;
-  const uint8_t* v_codes;
-  const uint16_t* v_scale;
-  const uint16_t* q;  // bf16 [B][Hq][128]
+// Matrix-core decode: head_dim 128, FP4 values, G = Hq / H in {1, 2, 4, 8, 16};
+// keys FP4 (bf16 queries) or 1-bit QJL with m = 128 (projected fp32 queries).
+struct MfmaDecodeArgs {
+  const uint8_t* k_codes;   // FP4 keys: [B][H][cap][64]
+  const uint16_t* k_scale;  //           [B][H][cap][8] bf16
+  const uint8_t* k_sketch;  // QJL keys: [B][H][cap][16]
+  const uint16_t* k_norm;   //           [B][H][cap] fp16
+  const uint8_t* v_codes;   // [B][H][cap][64]
+  const uint16_t* v_scale;  // [B][H][cap][8] bf16
+  const void* q;            // FP4: bf16 [B][Hq][128]; QJL: fp32 S q [B][Hq][128]
   const int32_t* seq_lens;
   int max_len, H, cap, Hq;
-  float scale_log2;
-  float* part;  // [B][Hq][splits][130]: running max (log2 units), sum, output
+  float scale_log2;  // softmax scale * log2(e)
+  float kappa;       // QJL: sqrt(pi/2) / m
+  float* part;       // [B][Hq][splits][130]: running max (log2 units), sum, output
   int splits, per_split;
 };
 
-bool fp4_fast_path_ok(const kv_layout& L, int num_q_heads, int q_dtype);
-int launch_decode_fp4_fast(const Fp4DecodeArgs& a, int B, int G, hipStream_t st);
+int launch_decode_mfma(const MfmaDecodeArgs& a, int format, int B, int G, hipStream_t st);
 
 }  // namespace kvq

@@ -89,7 +89,7 @@ def test_token_by_token_append_equals_bulk(fmt):
     assert_bytes_equal(gpu_buffers(step), gpu_buffers(bulk), fmt)
 
 
-@pytest.mark.parametrize("fmt", ["fp4", "turbo", "latent"])
+@pytest.mark.parametrize("fmt", ["fp4", "qjl1", "turbo", "latent"])
 def test_split_count_invariance_and_determinism(fmt):
     cfg = SMALL[fmt]
     cache, _, _ = _build(cfg)
@@ -97,10 +97,10 @@ def test_split_count_invariance_and_determinism(fmt):
     lens = torch.from_numpy(synth.seq_lens_for(cfg)).cuda()
     outs = [cache.decode(q, lens, softmax_scale(cfg), splits=s).cpu().numpy() for s in (1, 0, 5, 0)]
     np.testing.assert_array_equal(outs[1], outs[3])
-    # the FP4 matrix-core kernel feeds softmax weights to the PV product in fp16
-    # (relative rounding 2^-12 per weight), so different split points may move a
-    # row by a few 1e-4; the fp32 kernels agree to fp32 rounding
-    tol = 6e-4 if fmt == "fp4" else 1e-5
+    # the matrix-core kernel (FP4 values) feeds softmax weights to the PV product
+    # in fp16 (relative rounding 2^-12 per weight), so different split points may
+    # move a row by a few 1e-4; the fp32 kernels agree to fp32 rounding
+    tol = 6e-4 if fmt in ("fp4", "qjl1") else 1e-5
     for o in outs[:3]:
         assert row_rel_err(o, outs[0]).max() < tol
 
@@ -114,17 +114,21 @@ def test_fp32_inputs(fmt):
     assert_bytes_equal(gpu_buffers(cache), want, fmt + "/f32")
 
 
-@pytest.mark.parametrize("G", [1, 2, 8, 16])
-def test_fp4_group_sizes(G):
-    """Every query-group size the FP4 matrix-core kernel is built for, with a ragged tail."""
-    cfg = SMALL["fp4"].scaled(hq=2 * G, hkv=2, context=611)
+@pytest.mark.parametrize("fmt", ["fp4", "qjl1"])
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+def test_mfma_group_sizes(fmt, G):
+    """Every query-group size the matrix-core kernel is built for, with a ragged tail."""
+    cfg = SMALL[fmt].scaled(hq=2 * G, hkv=2, context=611)
     cache, K, V = _build(cfg, chunks=1)
-    enc = oracle_encode(cfg, host64(K), host64(V), {})
+    consts = oracle_constants(cfg)
+    enc = oracle_encode(cfg, host64(K), host64(V), consts)
     q = synth.make_queries(cfg, device="cuda")
     lens = np.array([611, 97], dtype=np.int32)
     out = cache.decode(q, torch.from_numpy(lens).cuda(), softmax_scale(cfg)).cpu().numpy()
-    ref = OA.decode_attention("fp4", enc, host64(q), lens, softmax_scale(cfg), cfg.hkv)
-    assert row_rel_err(out, ref).max() <= RTOL
+    ref = OA.decode_attention(fmt, enc, host64(q), lens, softmax_scale(cfg), cfg.hkv, consts)
+    err = row_rel_err(out, ref)
+    print(f"  {fmt} G={G} max row rel err {err.max():.3e}", flush=True)
+    assert err.max() <= RTOL
 
 
 def test_fp4_fp32_queries():
