@@ -320,6 +320,28 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
   const int B = L.batch;
   const int rows = B * num_q_heads;
   const int qw_in = query_width(&L), qw_out = prepared_query_width(&L);
+  if (latent_fast_path_ok(L, num_q_heads, q_dtype)) {
+    MfmaDecodeArgs f{};
+    f.k_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_K_CODES]);
+    f.k_scale = static_cast<const uint16_t*>(c->buf[KV_BUF_K_SCALE]);
+    f.rope = static_cast<const uint16_t*>(c->buf[KV_BUF_ROPE]);
+    f.q = q;
+    f.seq_lens = seq_lens;
+    f.max_len = max_seq_len;
+    f.H = L.num_kv_heads;
+    f.cap = L.capacity;
+    f.Hq = num_q_heads;
+    f.scale_log2 = scale * kLog2e;
+    f.part = part;
+    f.splits = plan.splits;
+    f.per_split = plan.tokens_per_split;
+    if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), st) != hipSuccess) return KV_EDEVICE;
+    int rc = launch_decode_latent(f, B, st);
+    if (rc != KV_OK) return rc;
+    if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess) return KV_EDEVICE;
+    launch_merge(part, rows, plan.splits, L.head_dim, L.format, c->rot, out, st);
+    return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
+  }
   const bool mfma = mfma_fast_path_ok(L, num_q_heads, q_dtype);
   // FP4 keys read the caller's bf16 queries as they are; every other format
   // first prepares its fp32 query (projection / rotation)

@@ -1,0 +1,351 @@
+// Decode attention on the matrix cores over a shared latent cache: every query
+// head attends to one 512-channel latent per token (FP4 E2M1, one bf16 scale per
+// 16 channels) plus a 64-channel bf16 RoPE key; the value is the latent itself
+// (page "How DeepSeek-V4 ...": the latent-compressed attention whose keys and
+// values are one shared low-rank vector per token, with a separate rotary part).
+//
+// With 128 query heads on one latent the per-token work is a dense contraction
+// (2 x 128 x (576 + 512) flop per 448 packed bytes), far past the HBM ridge, so
+// the whole tile math runs on v_mfma_f32_32x32x16_{f16,bf16}.
+//
+// One workgroup = one (sequence, context split), all Hq = 32 * NW query heads,
+// NW waves, one per SIMD.  Wave w owns heads [32 w, 32 w + 32) end to end: its
+// query operand (144 registers) and its 32 x 512 fp32 output accumulators (256
+// registers) stay in registers for the whole split.  Per 32-token tile:
+//   1. the packed tile (codes, scales, RoPE) arrives by direct-to-LDS loads,
+//      issued two tiles ahead;
+//   2. all threads dequantise it once into a token-major tile Kt (fp16 latent,
+//      bf16 RoPE) and a channel-major tile Vt (fp16 latent);
+//   3. each wave computes S^T = K Q^T for its heads (36 MFMAs);
+//   4. online softmax per head (each lane pair holds one head), P to fp16;
+//   5. O += P V (32 MFMAs).
+// FP4 element values times their bf16 scale are exact in fp16 (within its range);
+// the bf16 query's latent part is exact in fp16 within the fp16 normal range.
+#include <hip/hip_runtime.h>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+#include "kvq_kernels.h"
+
+namespace kvq {
+
+namespace {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
+typedef float f16v_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+constexpr int kTile = 32;
+constexpr int kLat = 512, kRope = 64;
+// packed stage: codes 32 x 256 | scales 32 x 64 | RoPE 32 x 128
+constexpr int kStCodes = 0, kStScale = 8192, kStRope = 10240, kStBytes = 14336;
+// Kt: 32 token rows of 576 halves; row stride 73 x 16 bytes (odd in 16-byte
+// units), and token t kept in row kt_row(t), the row the QK operand lane reading
+// it has, so that any 16 consecutive lanes read 16 different 16-byte bank groups.
+constexpr int kKtStride = kLat + kRope + 8;
+// Vt: 512 channel rows of 32 tokens; row stride 5 x 16 bytes, and the four
+// 16-byte chunks of row r permuted by (r / 8) % 4, so that neither the PV operand
+// reads (consecutive rows, one chunk) nor the dequantiser's writes (rows 4 apart)
+// pile onto one bank group.
+constexpr int kVtStride = kTile + 8;
+constexpr int kRsrcFlags = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcFlags);
+}
+
+template <int SEL>
+__device__ __forceinline__ h2_t fp4x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+}
+
+__device__ __forceinline__ h2_t splat_bf16(uint32_t s) {
+  const float f = __uint_as_float(s << 16);
+  return __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(f, f));
+}
+
+__device__ __forceinline__ h2_t bf16x2_to_h2(uint32_t lo_hi) {
+  return __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(lo_hi << 16),
+                                                            __uint_as_float(lo_hi & 0xFFFF0000u)));
+}
+
+// Row rho of the QK A operand holds token kt_row(rho) (bits 2 and 3 of rho
+// swapped): then the result rows a lane holds (i % 4 + 8 (i / 4) + 4 (lane / 32),
+// i = 0..15) are the tokens 16 (i / 8) + 8 (lane / 32) + i % 8, exactly the
+// k-slots that lane supplies as the A operand of the two 16-token PV products.
+// Kt keeps token t in row kt_row(t) (an involution), so lane rho reads row rho.
+__device__ __forceinline__ int kt_row(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
+
+// Vt element offset (halves) of channel ch, 16-byte chunk c (tokens 8c..8c+7)
+__device__ __forceinline__ int vt_off(int ch, int c) { return ch * kVtStride + 8 * (c ^ ((ch >> 3) & 3)); }
+
+// s_waitcnt immediate that waits for vmcnt <= n and nothing else
+constexpr int vmcnt_wait(int n) { return 0x0F70 | (n & 0xF) | ((n >> 4) << 14); }
+
+struct Res {
+  __amdgpu_buffer_rsrc_t codes, scale, rope;
+};
+
+// Direct-to-LDS loads of one packed tile, spread evenly over the NW waves
+// (32 / NW loads each).  The token offset rides in the range-checked VGPR
+// offset: a tile at or past the end of the resources reads zeros.
+template <int NW>
+__device__ __forceinline__ void issue_tile(uint8_t* st, int wave, int lane, int t0, const Res& r) {
+#pragma unroll
+  for (int k = 0; k < 8 / NW; ++k) {
+    const int c = wave + k * NW;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.codes, (lds_ptr_t)(st + kStCodes + c * 1024), 16,
+                                             t0 * 256 + c * 1024 + lane * 16, 0, 0, 0);
+  }
+#pragma unroll
+  for (int k = 0; k < 8 / NW; ++k) {
+    const int c = wave + k * NW;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.scale, (lds_ptr_t)(st + kStScale + c * 256), 4,
+                                             t0 * 64 + c * 256 + lane * 4, 0, 0, 0);
+  }
+#pragma unroll
+  for (int k = 0; k < 16 / NW; ++k) {
+    const int c = wave + k * NW;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.rope, (lds_ptr_t)(st + kStRope + c * 256), 4,
+                                             t0 * 128 + c * 256 + lane * 4, 0, 0, 0);
+  }
+}
+
+// o *= f for one accumulator held in an AGPR, without the compiler staging the
+// whole accumulator array through arch VGPRs.
+__device__ __forceinline__ void scale_acc(float& x, float f) {
+  float t;
+  asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+               : "+a"(x), "=&v"(t)
+               : "v"(f));
+}
+
+template <int NW>
+__global__ void __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(1, 1))) decode_latent_kernel(MfmaDecodeArgs a) {
+  constexpr int NT = 64 * NW;
+  __shared__ __attribute__((aligned(16))) uint8_t stA[kStBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t stB[kStBytes];
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[kTile * kKtStride];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[kLat * kVtStride];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int split = blockIdx.x, b = blockIdx.y;
+  const int L = min(min(a.seq_lens[b], a.max_len), a.cap);
+  const int t_begin = split * a.per_split;
+  const int t_end = min(L, t_begin + a.per_split);
+  const int col = lane & 31, half = lane >> 5;
+
+  // ---------------- the query operand: 32 fp16 latent steps, 4 bf16 RoPE steps
+  h8_t ql[32];
+  b8_t qr[4];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + 32 * wave + col) * (kLat + kRope);
+#pragma unroll
+    for (int s = 0; s < 32; ++s) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(qp + 16 * s + 8 * half);
+      const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const h2_t v = bf16x2_to_h2(wd[j]);
+        ql[s][2 * j] = v[0];
+        ql[s][2 * j + 1] = v[1];
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(qp + kLat + 16 * s + 8 * half);
+      qr[s] = __builtin_bit_cast(b8_t, raw);
+    }
+  }
+
+  f16v_t o[16];
+#pragma unroll
+  for (int n = 0; n < 16; ++n) o[n] = f16v_t{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const Res res{rsrc(a.k_codes + (size_t)b * a.cap * 256, (size_t)a.cap * 256),
+                rsrc(a.k_scale + (size_t)b * a.cap * 32, (size_t)a.cap * 64),
+                rsrc(a.rope + (size_t)b * a.cap * 64, (size_t)a.cap * 128)};
+  const int none = a.cap;
+  auto tile_or_none = [&](int t) { return t < t_end ? t : none; };
+
+  issue_tile<NW>(stA, wave, lane, tile_or_none(t_begin), res);
+  issue_tile<NW>(stB, wave, lane, tile_or_none(t_begin + kTile), res);
+
+  // lane constants of the fragment reads (kept opaque so that the compiler does
+  // not hoist one address register per read out of the loop)
+  // this lane's QK A operand is token kt_row(col), kept in Kt row col
+  int ka = col * kKtStride + 8 * half;
+  // this lane's PV B operand: channel 32 n + col, chunk 2 c + half; the chunk
+  // permutation (ch / 8) % 4 is the same for every n
+  int va0 = vt_off(col, half), va1 = vt_off(col, 2 + half);
+  asm volatile("" : "+v"(ka), "+v"(va0), "+v"(va1));
+
+  for (int t0 = t_begin; t0 < t_end; t0 += 2 * kTile) {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int tt = t0 + sub * kTile;
+      uint8_t* st = sub == 0 ? stA : stB;
+      // -------- 1. this wave's loads into this stage have landed (the other
+      // stage's are still in flight); the barrier then covers every wave's, and
+      // every wave is done with the previous tile's Kt / Vt
+      __builtin_amdgcn_s_waitcnt(vmcnt_wait(32 / NW));
+      __syncthreads();
+      // -------- 2. dequantise: item = (token octet, channel quad); a wave's lanes
+      // take consecutive channel quads
+      for (int it = tid; it < 4 * 128; it += NT) {
+        const int to = it >> 7, cq = it & 127;
+        h2_t v[8][2];  // [token][channel pair]
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int tok = 8 * to + k;
+          const uint32_t cw = *reinterpret_cast<const uint16_t*>(st + kStCodes + tok * 256 + 2 * cq);
+          const h2_t sc = splat_bf16(*reinterpret_cast<const uint16_t*>(st + kStScale + tok * 64 + 2 * (cq >> 2)));
+          v[k][0] = fp4x2<0>(cw) * sc;
+          v[k][1] = fp4x2<1>(cw) * sc;
+          *reinterpret_cast<uint2*>(&Kt[kt_row(tok) * kKtStride + 4 * cq]) =
+              uint2{__builtin_bit_cast(uint32_t, v[k][0]), __builtin_bit_cast(uint32_t, v[k][1])};
+        }
+        // channel-major: channel 4 cq + 2 p + e gets the 8 tokens' values
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            uint32_t w[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              h2_t pr;
+              pr[0] = v[2 * k][p][e];
+              pr[1] = v[2 * k + 1][p][e];
+              w[k] = __builtin_bit_cast(uint32_t, pr);
+            }
+            *reinterpret_cast<uint4*>(&Vt[vt_off(4 * cq + 2 * p + e, to)]) = uint4{w[0], w[1], w[2], w[3]};
+          }
+      }
+      for (int it = tid; it < kTile * 8; it += NT) {  // RoPE: 32 tokens x 8 x 16 bytes
+        const int tok = it >> 3, part = it & 7;
+        *reinterpret_cast<uint4*>(&Kt[kt_row(tok) * kKtStride + kLat + 8 * part]) =
+            *reinterpret_cast<const uint4*>(st + kStRope + tok * 128 + 16 * part);
+      }
+      __syncthreads();
+      // -------- the stage is free: refill it two tiles ahead
+      issue_tile<NW>(st, wave, lane, tile_or_none(tt + 2 * kTile), res);
+      // -------- 3. S^T = K Q^T for this wave's 32 heads
+      f16v_t s = f16v_t{};
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        const h8_t kf = *reinterpret_cast<const h8_t*>(&Kt[ka + 16 * k]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, ql[k], s, 0, 0, 0);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const b8_t kf = *reinterpret_cast<const b8_t*>(&Kt[ka + kLat + 16 * k]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qr[k], s, 0, 0, 0);
+      }
+      // at most three fragments in flight: 2 reads ahead, then one read per MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int k = 0; k < 34; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      // -------- 4. online softmax for head 32 wave + col over this lane's 16 tokens
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int tok = tt + 16 * (i >> 3) + 8 * half + (i & 7);
+        s[i] = tok < t_end ? s[i] * a.scale_log2 : -INFINITY;
+        tmax = fmaxf(tmax, s[i]);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      // the reference max moves only when the tile max passes it by more than 2^8
+      const bool bump = tmax > m_run + 8.f;
+      const float m_new = bump ? tmax : m_run;
+      const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+      h8_t pf[2];
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(s[i] - m_new);
+        psum += p;
+        pf[i >> 3][i & 7] = (_Float16)p;
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      if (__ballot(bump)) {
+        // output rows are heads i % 4 + 8 (i / 4) + 4 half; head r's alpha is in
+        // lane r.  The products are issued well after the last MFMA wrote the
+        // accumulators (the whole QK product and softmax lie between).
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float ar = __shfl(alpha, (i & 3) + 8 * (i >> 2) + 4 * half);
+#pragma unroll
+          for (int n = 0; n < 16; ++n) {
+            float x = o[n][i];
+            scale_acc(x, ar);
+            o[n][i] = x;
+          }
+        }
+        asm volatile("s_nop 7");  // VALU writes of the accumulators, then MFMA reads of them
+      }
+      // -------- 5. O += P V
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const h8_t vf = *reinterpret_cast<const h8_t*>(&Vt[(c ? va1 : va0) + 32 * n * kVtStride]);
+          o[n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pf[c], vf, o[n], 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+#pragma unroll
+      for (int k = 0; k < 30; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load into LDS outlives the workgroup
+
+  // ---------------- partial result of this split
+  l_run += __shfl_xor(l_run, 32);
+  const size_t row0 = (size_t)b * a.Hq + 32 * wave;
+  const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int col_e = lane_e & 31, half_e = lane_e >> 5;
+  if (half_e == 0) {
+    float* p = a.part + ((row0 + col_e) * a.splits + split) * (kLat + 2);
+    p[0] = m_run;
+    p[1] = l_run;
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int head = (i & 3) + 8 * (i >> 2) + 4 * half_e;
+    float* p = a.part + ((row0 + head) * a.splits + split) * (kLat + 2) + 2 + col_e;
+#pragma unroll
+    for (int n = 0; n < 16; ++n) p[32 * n] = o[n][i];
+  }
+}
+
+}  // namespace
+
+int launch_decode_latent(const MfmaDecodeArgs& a, int B, hipStream_t st) {
+  dim3 grid(a.splits, B);
+  switch (a.Hq) {
+    case 32: decode_latent_kernel<1><<<grid, 64, 0, st>>>(a); break;
+    case 64: decode_latent_kernel<2><<<grid, 128, 0, st>>>(a); break;
+    case 128: decode_latent_kernel<4><<<grid, 256, 0, st>>>(a); break;
+    default: return KV_EUNSUPPORTED;
+  }
+  return KV_OK;
+}
+
+}  // namespace kvq

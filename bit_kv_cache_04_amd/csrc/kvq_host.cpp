@@ -67,6 +67,12 @@ int prepared_query_width(const kv_layout* L) {
 
 int value_width(const kv_layout* L) { return L->head_dim; }
 
+bool latent_fast_path_ok(const kv_layout& L, int num_q_heads, int q_dtype) {
+  return L.format == KV_FMT_LATENT_FP4 && L.head_dim == 512 && L.rope_dim == 64 && q_dtype == KV_DT_BF16 &&
+         (num_q_heads == 32 || num_q_heads == 64 || num_q_heads == 128) &&
+         (size_t)L.capacity * 256 < (size_t(1) << 31);
+}
+
 bool mfma_fast_path_ok(const kv_layout& L, int num_q_heads, int q_dtype) {
   const int G = num_q_heads / L.num_kv_heads;
   const bool g_ok = G == 1 || G == 2 || G == 4 || G == 8 || G == 16;
@@ -82,12 +88,16 @@ SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int q_dtype, int max_
   // shorter than a few steps.
   const int G = num_q_heads / L->num_kv_heads;
   const bool fast = mfma_fast_path_ok(*L, num_q_heads, q_dtype);
+  const bool latent = latent_fast_path_ok(*L, num_q_heads, q_dtype);
   const int tile = fast ? 128 : 64;
+  // the latent kernel keeps one workgroup per compute unit resident and every
+  // split writes Hq x 514 partial floats: a few long splits per sequence
+  const long target = latent ? 512 : 2048;
   long units = (long)L->batch * L->num_kv_heads;
-  if (!fast && G > 16) units *= (G + 15) / 16;
+  if (!fast && !latent && G > 16) units *= (G + 15) / 16;  // the generic kernel's head blocks
   int splits = requested;
   if (splits <= 0) {
-    long want = (2048 + units - 1) / units;
+    long want = (target + units - 1) / units;
     long maxs = (max_seq_len + 4 * tile - 1) / (4 * tile);
     splits = (int)std::max(1L, std::min(want, maxs));
   }

@@ -17,6 +17,7 @@ struct MfmaDecodeArgs {
   const uint16_t* k_norm;   //           [B][H][cap] fp16
   const uint8_t* v_codes;   // [B][H][cap][64]
   const uint16_t* v_scale;  // [B][H][cap][8] bf16
+  const uint16_t* rope;     // latent: [B][cap][64] bf16 (k_codes [B][cap][256], k_scale [B][cap][32])
   const void* q;            // FP4: bf16 [B][Hq][128]; QJL: fp32 S q [B][Hq][128]
   const int32_t* seq_lens;
   int max_len, H, cap, Hq;
@@ -27,5 +28,9 @@ struct MfmaDecodeArgs {
 };
 
 int launch_decode_mfma(const MfmaDecodeArgs& a, int format, int B, int G, hipStream_t st);
+
+// Shared-latent cache (512 FP4 + 64 bf16 RoPE), bf16 queries, Hq in {32, 64, 128}.
+bool latent_fast_path_ok(const kv_layout& L, int num_q_heads, int q_dtype);
+int launch_decode_latent(const MfmaDecodeArgs& a, int B, hipStream_t st);
 
 }  // namespace kvq

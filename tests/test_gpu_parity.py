@@ -28,11 +28,16 @@ SMALL = {
 }
 
 
-def _build(cfg, chunks=2):
+def _build(cfg, chunks=2, ramp=None):
+    """Cache of cfg's seeded inputs; ramp multiplies token t's key (latent) by 1 + ramp * t / T."""
     torch.manual_seed(0)
     cache = new_cache(cfg)
     K, V = inputs(cfg)
     T = cfg.context
+    if ramp is not None:
+        r = 1.0 + ramp * torch.arange(T, device=K.device, dtype=torch.float32) / T
+        r = r.view(1, T, 1) if cfg.fmt == "latent" else r.view(1, 1, T, 1)
+        K = (K.float() * r).to(K.dtype)
     step = -(-T // chunks)
     if cfg.fmt == "kivi2":
         step = -(-step // 32) * 32
@@ -97,10 +102,10 @@ def test_split_count_invariance_and_determinism(fmt):
     lens = torch.from_numpy(synth.seq_lens_for(cfg)).cuda()
     outs = [cache.decode(q, lens, softmax_scale(cfg), splits=s).cpu().numpy() for s in (1, 0, 5, 0)]
     np.testing.assert_array_equal(outs[1], outs[3])
-    # the matrix-core kernel (FP4 values) feeds softmax weights to the PV product
+    # the matrix-core kernels feed softmax weights to the PV product
     # in fp16 (relative rounding 2^-12 per weight), so different split points may
     # move a row by a few 1e-4; the fp32 kernels agree to fp32 rounding
-    tol = 6e-4 if fmt in ("fp4", "qjl1") else 1e-5
+    tol = 6e-4 if fmt in ("fp4", "qjl1", "latent") else 1e-5
     for o in outs[:3]:
         assert row_rel_err(o, outs[0]).max() < tol
 
@@ -141,3 +146,40 @@ def test_fp4_fp32_queries():
     out = cache.decode(q, torch.from_numpy(lens).cuda(), softmax_scale(cfg)).cpu().numpy()
     ref = OA.decode_attention("fp4", enc, host64(q), lens, softmax_scale(cfg), cfg.hkv)
     assert row_rel_err(out, ref).max() <= RTOL
+
+
+@pytest.mark.parametrize("hq", [32, 64])
+def test_latent_head_counts(hq):
+    """The latent matrix-core kernel at 1 and 2 waves per workgroup, ragged lengths."""
+    cfg = SMALL["latent"].scaled(hq=hq, context=433)
+    cache, K, _ = _build(cfg, chunks=1)
+    enc = oracle_encode(cfg, host64(K), None, {})
+    q = synth.make_queries(cfg, device="cuda")
+    lens = np.array([433, 40], dtype=np.int32)
+    out = cache.decode(q, torch.from_numpy(lens).cuda(), softmax_scale(cfg)).cpu().numpy()
+    ref = OA.decode_attention("latent", enc, host64(q), lens, softmax_scale(cfg), cfg.hkv, {},
+                              latent_dim=cfg.head_dim)
+    err = row_rel_err(out, ref)
+    print(f"  latent hq={hq} max row rel err {err.max():.3e}", flush=True)
+    assert err.max() <= RTOL
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "qjl1", "latent", "kivi2", "turbo"])
+def test_growing_logits_rescale(fmt):
+    """Keys that grow along the context push every later tile's maximum logit past
+    the running one, so the online-softmax rescale runs many times per split."""
+    cfg = SMALL[fmt].scaled(context=640 if fmt == "kivi2" else 700)
+    cache, K, V = _build(cfg, chunks=1, ramp=12.0)
+    consts = oracle_constants(cfg)
+    if fmt == "latent":
+        enc = oracle_encode(cfg, host64(K), None, consts)
+    else:
+        enc = oracle_encode(cfg, host64(K), host64(V), consts)
+    q = synth.make_queries(cfg, device="cuda")
+    lens = synth.seq_lens_for(cfg, ragged=True)
+    out = cache.decode(q, torch.from_numpy(lens).cuda(), softmax_scale(cfg)).cpu().numpy()
+    ref = OA.decode_attention(fmt, enc, host64(q), lens, softmax_scale(cfg), cfg.hkv, consts,
+                              latent_dim=cfg.head_dim)
+    err = row_rel_err(out, ref)
+    print(f"  {fmt} ramped keys: max row rel err {err.max():.3e}", flush=True)
+    assert err.max() <= RTOL
