@@ -15,7 +15,7 @@
 //   1. the packed tile (codes, scales, RoPE) arrives by direct-to-LDS loads,
 //      issued two tiles ahead;
 //   2. all threads dequantise it once into a token-major tile Kt (fp16 latent,
-//      bf16 RoPE) and a channel-major tile Vt (fp16 latent);
+//      bf16 RoPE); the PV operand reads it back transposed (ds_read_b64_tr_b16);
 //   3. each wave computes S^T = K Q^T for its heads (36 MFMAs);
 //   4. online softmax per head (each lane pair holds one head), P to fp16;
 //   5. O += P V (32 MFMAs).
@@ -41,15 +41,12 @@ constexpr int kTile = 32;
 constexpr int kLat = 512, kRope = 64;
 // packed stage: codes 32 x 256 | scales 32 x 64 | RoPE 32 x 128
 constexpr int kStCodes = 0, kStScale = 8192, kStRope = 10240, kStBytes = 14336;
-// Kt: 32 token rows of 576 halves; row stride 73 x 16 bytes (odd in 16-byte
-// units), and token t kept in row kt_row(t), the row the QK operand lane reading
-// it has, so that any 16 consecutive lanes read 16 different 16-byte bank groups.
+// Kt: 32 token rows of 576 halves (fp16 latent, then bf16 RoPE), row stride
+// 73 x 16 bytes.  Token t = 16 c + 8 h + 4 h2 + e (e < 4) lives in row
+// kt_phys(t) = 16 c + 8 h2 + 2 e + h, chosen so that both readers see distinct
+// bank groups: the QK operand (lanes of 8 read 8 rows differing in e and h) and
+// the transposing PV reads (4 rows differing in e, 32 bytes each).
 constexpr int kKtStride = kLat + kRope + 8;
-// Vt: 512 channel rows of 32 tokens; row stride 5 x 16 bytes, and the four
-// 16-byte chunks of row r permuted by (r / 8) % 4, so that neither the PV operand
-// reads (consecutive rows, one chunk) nor the dequantiser's writes (rows 4 apart)
-// pile onto one bank group.
-constexpr int kVtStride = kTile + 8;
 constexpr int kRsrcFlags = 0x00020000;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, size_t bytes) {
@@ -71,15 +68,24 @@ __device__ __forceinline__ h2_t bf16x2_to_h2(uint32_t lo_hi) {
                                                             __uint_as_float(lo_hi & 0xFFFF0000u)));
 }
 
-// Row rho of the QK A operand holds token kt_row(rho) (bits 2 and 3 of rho
+// Row rho of the QK A operand holds token qk_token(rho) (bits 2 and 3 of rho
 // swapped): then the result rows a lane holds (i % 4 + 8 (i / 4) + 4 (lane / 32),
 // i = 0..15) are the tokens 16 (i / 8) + 8 (lane / 32) + i % 8, exactly the
 // k-slots that lane supplies as the A operand of the two 16-token PV products.
-// Kt keeps token t in row kt_row(t) (an involution), so lane rho reads row rho.
-__device__ __forceinline__ int kt_row(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
+__device__ __forceinline__ int qk_token(int rho) { return (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1); }
 
-// Vt element offset (halves) of channel ch, 16-byte chunk c (tokens 8c..8c+7)
-__device__ __forceinline__ int vt_off(int ch, int c) { return ch * kVtStride + 8 * (c ^ ((ch >> 3) & 3)); }
+__device__ __forceinline__ int kt_phys(int t) {
+  return (t & 16) | ((t & 4) << 1) | ((t & 3) << 1) | ((t >> 3) & 1);
+}
+
+typedef short s4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s4_t* lds_s4_ptr;
+
+// Transposing LDS read: within each 16-lane group, lane i gets element i % 4 of
+// the 8-byte chunks addressed by lanes 4 e + i / 4, e = 0..3.
+__device__ __forceinline__ s4_t read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(p));
+}
 
 // s_waitcnt immediate that waits for vmcnt <= n and nothing else
 constexpr int vmcnt_wait(int n) { return 0x0F70 | (n & 0xF) | ((n >> 4) << 14); }
@@ -129,7 +135,6 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) decode_latent_kernel(MfmaDecodeArgs a
   __shared__ __attribute__((aligned(16))) uint8_t stA[kStBytes];
   __shared__ __attribute__((aligned(16))) uint8_t stB[kStBytes];
   __shared__ __attribute__((aligned(16))) uint16_t Kt[kTile * kKtStride];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[kLat * kVtStride];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -179,12 +184,17 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) decode_latent_kernel(MfmaDecodeArgs a
 
   // lane constants of the fragment reads (kept opaque so that the compiler does
   // not hoist one address register per read out of the loop)
-  // this lane's QK A operand is token kt_row(col), kept in Kt row col
-  int ka = col * kKtStride + 8 * half;
-  // this lane's PV B operand: channel 32 n + col, chunk 2 c + half; the chunk
-  // permutation (ch / 8) % 4 is the same for every n
-  int va0 = vt_off(col, half), va1 = vt_off(col, 2 + half);
-  asm volatile("" : "+v"(ka), "+v"(va0), "+v"(va1));
+  // this lane's QK A operand: token qk_token(col), channels 16 k + 8 half + [0, 8)
+  int ka = kt_phys(qk_token(col)) * kKtStride + 8 * half;
+  // this lane's transposing PV reads: lane (group G = lane / 16, j = lane % 16)
+  // addresses channels 32 n + 16 (G % 2) + 4 (j % 4) + [0, 4) of token
+  // 16 c + 8 half + 4 h2 + j / 4, so that it receives channel 32 n + col of
+  // tokens 16 c + 8 half + 4 h2 + [0, 4): its PV B operand k-slots
+  const int jj = lane & 15, gg = lane >> 4;
+  int vb = kt_phys(8 * half + (jj >> 2)) * kKtStride + 16 * (gg & 1) + 4 * (jj & 3);
+  asm volatile("" : "+v"(ka), "+v"(vb));
+  constexpr int kH2 = 8 * kKtStride;   // h2 = 1: token + 4 -> row + 8
+  constexpr int kC = 16 * kKtStride;   // c = 1: token + 16 -> row + 16
 
   for (int t0 = t_begin; t0 < t_end; t0 += 2 * kTile) {
 #pragma unroll
@@ -193,69 +203,57 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) decode_latent_kernel(MfmaDecodeArgs a
       uint8_t* st = sub == 0 ? stA : stB;
       // -------- 1. this wave's loads into this stage have landed (the other
       // stage's are still in flight); the barrier then covers every wave's, and
-      // every wave is done with the previous tile's Kt / Vt
+      // every wave is done with the previous tile's Kt
       __builtin_amdgcn_s_waitcnt(vmcnt_wait(32 / NW));
       __syncthreads();
-      // -------- 2. dequantise: item = (token octet, channel quad); a wave's lanes
-      // take consecutive channel quads
-      for (int it = tid; it < 4 * 128; it += NT) {
-        const int to = it >> 7, cq = it & 127;
-        h2_t v[8][2];  // [token][channel pair]
+      // -------- 2. dequantise: item = (token quad, channel octet); a wave's lanes
+      // take consecutive channel octets of one token quad
+      for (int it = tid; it < 8 * 64; it += NT) {
+        const int tq = it >> 6, co = it & 63;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int tok = 8 * to + k;
-          const uint32_t cw = *reinterpret_cast<const uint16_t*>(st + kStCodes + tok * 256 + 2 * cq);
-          const h2_t sc = splat_bf16(*reinterpret_cast<const uint16_t*>(st + kStScale + tok * 64 + 2 * (cq >> 2)));
-          v[k][0] = fp4x2<0>(cw) * sc;
-          v[k][1] = fp4x2<1>(cw) * sc;
-          *reinterpret_cast<uint2*>(&Kt[kt_row(tok) * kKtStride + 4 * cq]) =
-              uint2{__builtin_bit_cast(uint32_t, v[k][0]), __builtin_bit_cast(uint32_t, v[k][1])};
+        for (int k = 0; k < 4; ++k) {
+          const int tok = 4 * tq + k;
+          const uint32_t cw = *reinterpret_cast<const uint32_t*>(st + kStCodes + tok * 256 + 4 * co);
+          const h2_t sc = splat_bf16(*reinterpret_cast<const uint16_t*>(st + kStScale + tok * 64 + 2 * (co >> 1)));
+          *reinterpret_cast<uint4*>(&Kt[kt_phys(tok) * kKtStride + 8 * co]) =
+              uint4{__builtin_bit_cast(uint32_t, fp4x2<0>(cw) * sc), __builtin_bit_cast(uint32_t, fp4x2<1>(cw) * sc),
+                    __builtin_bit_cast(uint32_t, fp4x2<2>(cw) * sc), __builtin_bit_cast(uint32_t, fp4x2<3>(cw) * sc)};
         }
-        // channel-major: channel 4 cq + 2 p + e gets the 8 tokens' values
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            uint32_t w[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              h2_t pr;
-              pr[0] = v[2 * k][p][e];
-              pr[1] = v[2 * k + 1][p][e];
-              w[k] = __builtin_bit_cast(uint32_t, pr);
-            }
-            *reinterpret_cast<uint4*>(&Vt[vt_off(4 * cq + 2 * p + e, to)]) = uint4{w[0], w[1], w[2], w[3]};
-          }
       }
       for (int it = tid; it < kTile * 8; it += NT) {  // RoPE: 32 tokens x 8 x 16 bytes
         const int tok = it >> 3, part = it & 7;
-        *reinterpret_cast<uint4*>(&Kt[kt_row(tok) * kKtStride + kLat + 8 * part]) =
+        *reinterpret_cast<uint4*>(&Kt[kt_phys(tok) * kKtStride + kLat + 8 * part]) =
             *reinterpret_cast<const uint4*>(st + kStRope + tok * 128 + 16 * part);
       }
       __syncthreads();
       // -------- the stage is free: refill it two tiles ahead
       issue_tile<NW>(st, wave, lane, tile_or_none(tt + 2 * kTile), res);
-      // -------- 3. S^T = K Q^T for this wave's 32 heads
-      f16v_t s = f16v_t{};
+      // -------- 3. S^T = K Q^T for this wave's 32 heads (two accumulation chains)
+      f16v_t s = f16v_t{}, s2 = f16v_t{};
 #pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        const h8_t kf = *reinterpret_cast<const h8_t*>(&Kt[ka + 16 * k]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, ql[k], s, 0, 0, 0);
+      for (int k = 0; k < 32; k += 2) {
+        const h8_t kf0 = *reinterpret_cast<const h8_t*>(&Kt[ka + 16 * k]);
+        const h8_t kf1 = *reinterpret_cast<const h8_t*>(&Kt[ka + 16 * k + 16]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf0, ql[k], s, 0, 0, 0);
+        s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf1, ql[k + 1], s2, 0, 0, 0);
       }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const b8_t kf = *reinterpret_cast<const b8_t*>(&Kt[ka + kLat + 16 * k]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qr[k], s, 0, 0, 0);
+      for (int k = 0; k < 4; k += 2) {
+        const b8_t kf0 = *reinterpret_cast<const b8_t*>(&Kt[ka + kLat + 16 * k]);
+        const b8_t kf1 = *reinterpret_cast<const b8_t*>(&Kt[ka + kLat + 16 * k + 16]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qr[k], s, 0, 0, 0);
+        s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1, qr[k + 1], s2, 0, 0, 0);
       }
-      // at most three fragments in flight: 2 reads ahead, then one read per MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      // a few fragments in flight: 3 reads ahead, then one read per MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
-      for (int k = 0; k < 34; ++k) {
+      for (int k = 0; k < 33; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
       __builtin_amdgcn_sched_barrier(0);
+      s += s2;
       // -------- 4. online softmax for head 32 wave + col over this lane's 16 tokens
       float tmax = -INFINITY;
 #pragma unroll
@@ -300,15 +298,17 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) decode_latent_kernel(MfmaDecodeArgs a
       for (int n = 0; n < 16; ++n) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          const h8_t vf = *reinterpret_cast<const h8_t*>(&Vt[(c ? va1 : va0) + 32 * n * kVtStride]);
+          const s4_t lo = read_tr16(&Kt[vb + c * kC + 32 * n]);
+          const s4_t hi = read_tr16(&Kt[vb + c * kC + kH2 + 32 * n]);
+          const h8_t vf = __builtin_bit_cast(h8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           o[n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pf[c], vf, o[n], 0, 0, 0);
         }
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
 #pragma unroll
       for (int k = 0; k < 30; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
       __builtin_amdgcn_sched_barrier(0);
