@@ -353,6 +353,33 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
       prep_query_kernel<uint16_t><<<rows, 128, 0, st>>>(static_cast<const uint16_t*>(q), qw_in, qw_out,
                                                         L.format, c->rot, c->proj, qv);
   }
+  if (turbo_fast_path_ok(L, num_q_heads)) {
+    TurboDecodeArgs f{};
+    f.k_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_K_CODES]);
+    f.k_sketch = static_cast<const uint8_t*>(c->buf[KV_BUF_K_SKETCH]);
+    f.k_norm = static_cast<const uint16_t*>(c->buf[KV_BUF_K_NORM]);
+    f.k_rnorm = static_cast<const uint16_t*>(c->buf[KV_BUF_K_RNORM]);
+    f.v_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_V_CODES]);
+    f.v_norm = static_cast<const uint16_t*>(c->buf[KV_BUF_V_NORM]);
+    f.levels = c->lm_levels;
+    f.q = qv;
+    f.seq_lens = seq_lens;
+    f.max_len = max_seq_len;
+    f.H = L.num_kv_heads;
+    f.cap = L.capacity;
+    f.Hq = num_q_heads;
+    f.scale_log2 = scale * kLog2e;
+    f.kappa = (float)(1.2533141373155002512 / (double)L.qjl_m);
+    f.part = part;
+    f.splits = plan.splits;
+    f.per_split = plan.tokens_per_split;
+    if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), st) != hipSuccess) return KV_EDEVICE;
+    int rc = launch_decode_turbo(f, B, num_q_heads / L.num_kv_heads, st);
+    if (rc != KV_OK) return rc;
+    if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess) return KV_EDEVICE;
+    launch_merge(part, rows, plan.splits, L.head_dim, L.format, c->rot, out, st);
+    return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
+  }
   if (mfma) {
     MfmaDecodeArgs f{};
     f.k_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_K_CODES]);

@@ -1,0 +1,368 @@
+// TurboQuant decode attention on the matrix cores (gfx950).
+//
+// Keys: 2-bit Lloyd-Max codes of the rotated unit key u~, a 128-bit QJL sign
+// sketch of the residual, and fp16 norms n (key) and gamma (residual); values:
+// 2-bit codes of the rotated unit value and its fp16 norm (page "TurboQuant vs
+// OSCAR vs EpiCache", section "quantization frontiers": rotation, a scalar
+// Lloyd-Max stage, then the 1-bit QJL stage on the residual).  The logit is
+//   n * ( <R q, u~> + sqrt(pi/2)/m * gamma * <S R q, sigma> ).
+//
+// A symmetric 4-level codebook (levels -l2, -l1, l1, l2 by code 0..3) makes a
+// code's level linear in its two bits b1 (high) and b0 (low):
+//   level = a0 + a1 b1 + a2 b0,  a0 = lv0, a1 = lv2 - lv0, a2 = lv1 - lv0,
+// because the b1 b0 term, lv3 - lv2 - lv1 + lv0, vanishes.  So both products
+// become exact 0/1 bit-plane products on the matrix cores:
+//   <q, u~>      = a0 sum(q) + <a1 q, b1> + <a2 q, b0>
+//   <qS, sigma>  = 2 <qS, b> - sum(qS)
+//   O            = a0 sum(P') + (a1 P') B1 + (a2 P') B0,   P' = p n_v
+// Bits enter v_mfma_f32_16x16x32_f16 as the fp16 value 1.0 or 0 (the FP4
+// converter turns a nibble holding one set low bit into 0.5, scaled by 2);
+// the fp32 query side is split into fp16 hi + lo parts carried in MFMA columns
+// G..G+7 (G <= 8 query heads share a KV head), so the key products are exact up
+// to fp32 accumulation.  Value codes are transposed to token-major bit planes by
+// ds_read_b64_tr_b4 (a 16 x 16 nibble transpose within each 16-lane group).
+//
+// Layout per workgroup, as in the FP4 kernel: 4 waves, each streaming its own
+// 32-token tiles through a two-stage LDS ring filled by direct-to-LDS loads,
+// one (sequence, KV head, split) per workgroup; the output stays in the rotated
+// basis (the split merge applies R^T).
+#include <hip/hip_runtime.h>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+#include "kvq_kernels.h"
+
+namespace kvq {
+
+namespace {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef int i2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+constexpr int kRsrcFlags = 0x00020000;
+// stage layout (bytes) for 32 tokens
+constexpr int kSK = 0;      // key codes, 32 B per token
+constexpr int kSS = 1024;   // sketch, 16 B per token (lanes 32..63 of its load write zeros up to 2048)
+constexpr int kSN = 2048;   // key norm: token t in the low half of dword t (then zeros)
+constexpr int kSR = 2304;   // residual norm, same form
+constexpr int kSV = 2560;   // value codes, 32 B per token
+constexpr int kSVN = 3584;  // value norm, same form as the key norm
+constexpr int kStage = 3840;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcFlags);
+}
+
+// 8 bits at positions 0, 4, ..., 28 of m as fp16 1.0 / 0 (element n <- bit 4n)
+__device__ __forceinline__ h8_t bits8(uint32_t m) {
+  h8_t r;
+  const h2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 2.0f, 0);
+  const h2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 2.0f, 1);
+  const h2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 2.0f, 2);
+  const h2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 2.0f, 3);
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// QK A-operand row rho of block b (16 rows) holds token 8 (rho / 4) + 4 b + rho % 4:
+// then the result rows a lane holds (4 (lane / 16) + v) in blocks 0 and 1 are the
+// tokens 8 (lane / 16) + j, j = 4 b + v = 0..7: the PV k-slots of that lane.
+__device__ __forceinline__ int qk_token(int rho, int b) { return 8 * (rho >> 2) + 4 * b + (rho & 3); }
+
+struct Res {
+  __amdgpu_buffer_rsrc_t kc, sk, kn, kr, vc, vn;
+  int n_end;  // a byte offset past every norm resource
+};
+
+__device__ __forceinline__ void issue_tile(uint8_t* st, int lane, int t0, const Res& r) {
+  const int c16 = t0 * 32 + lane * 16;
+  const int nb = lane < 32 ? t0 * 2 + lane * 2 : r.n_end;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.kc, (lds_ptr_t)(st + kSK), 16, c16, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.sk, (lds_ptr_t)(st + kSS), 16, lane < 32 ? t0 * 16 + lane * 16 : r.n_end,
+                                           0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.kn, (lds_ptr_t)(st + kSN), 2, nb, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.kr, (lds_ptr_t)(st + kSR), 2, nb, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vc, (lds_ptr_t)(st + kSV), 16, c16, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vn, (lds_ptr_t)(st + kSVN), 2, nb, 0, 0, 0);
+}
+
+struct Consts {
+  float a0, a1, a2;  // level = a0 + a1 b1 + a2 b0
+};
+
+template <int G>
+struct WaveState {
+  h8_t blm[8];   // B operand of the 8 code-bit steps: (a1 or a2) * R q, hi or lo
+  h8_t bqs[4];   // B operand of the 4 sketch steps: S R q, hi or lo
+  float cst;     // a0 * sum(R q) for this lane's head
+  float sqs;     // sum(S R q)
+  float m_run, l_run, sp;  // running max, sum of p, sum of p * n_v
+  f4_t o[8];
+};
+
+// One 32-token tile (see tile_step of the FP4 kernel for the ring protocol).
+template <int G>
+__device__ __forceinline__ void tile_step(WaveState<G>& w, uint8_t* st, int lane, int t0, int t_end, int t_next,
+                                          const TurboDecodeArgs& a, const Consts& k, const Res& res) {
+  const int q4 = lane >> 4, c = lane & 15;
+  // ---- fragments of this lane
+  int ko = qk_token(c, 0) * 32, so = qk_token(c, 0) * 16, no = 4 * 8 * q4;
+  int vo = (8 * q4 + (c & 7)) * 32 + 8 * (c >> 3);
+  asm volatile("" : "+v"(ko), "+v"(so), "+v"(no), "+v"(vo));
+  uint4 kw[2][2], sw[2];
+  // block 1's token is 4 after block 0's: 128 bytes of codes, 64 of sketch
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    kw[b][0] = *reinterpret_cast<const uint4*>(st + kSK + ko + 128 * b);
+    kw[b][1] = *reinterpret_cast<const uint4*>(st + kSK + ko + 128 * b + 16);
+    sw[b] = *reinterpret_cast<const uint4*>(st + kSS + so + 64 * b);
+  }
+  uint4 nk[2], nr[2], nv[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    nk[h] = *reinterpret_cast<const uint4*>(st + kSN + no + 16 * h);
+    nr[h] = *reinterpret_cast<const uint4*>(st + kSR + no + 16 * h);
+    nv[h] = *reinterpret_cast<const uint4*>(st + kSVN + no + 16 * h);
+  }
+  const i2_t vx0 = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+      (__attribute__((address_space(3))) i2_t*)(st + kSV + vo));
+  const i2_t vx1 = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+      (__attribute__((address_space(3))) i2_t*)(st + kSV + vo + 16));
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the stage may be refilled
+  issue_tile(st, lane, t_next, res);
+
+  // ---- logits: S^T = K Q^T, code-bit steps then sketch steps, per 16-token block
+  float sv[8];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const uint32_t words[8] = {kw[b][0].x, kw[b][0].y, kw[b][0].z, kw[b][0].w,
+                               kw[b][1].x, kw[b][1].y, kw[b][1].z, kw[b][1].w};
+    f4_t lm = f4_t{0.f, 0.f, 0.f, 0.f}, qj = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      lm = __builtin_amdgcn_mfma_f32_16x16x32_f16(bits8((words[i] >> q4) & 0x11111111u), w.blm[i], lm, 0, 0, 0);
+    const uint32_t sks[4] = {sw[b].x, sw[b].y, sw[b].z, sw[b].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      qj = __builtin_amdgcn_mfma_f32_16x16x32_f16(bits8((sks[i] >> q4) & 0x11111111u), w.bqs[i], qj, 0, 0, 0);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      // hi part (columns < 8) plus lo part (columns 8..15) of the same head
+      const float l_ = lm[v] + __shfl_xor(lm[v], 8);
+      const float q_ = qj[v] + __shfl_xor(qj[v], 8);
+      const int j = 4 * b + v;  // token 8 q4 + j
+      const uint32_t nkw = j < 4 ? (&nk[0].x)[j] : (&nk[1].x)[j - 4];
+      const uint32_t nrw = j < 4 ? (&nr[0].x)[j] : (&nr[1].x)[j - 4];
+      const float n = f16_to_f32((uint16_t)nkw), gm = f16_to_f32((uint16_t)nrw);
+      const float logit = n * ((l_ + w.cst) + a.kappa * gm * fmaf(2.f, q_, -w.sqs));
+      const int tok = t0 + 8 * q4 + j;
+      float s = tok < t_end ? logit * a.scale_log2 : -INFINITY;
+      if (c >= G) s = 0.f;  // columns past the group hold no head: keep them finite
+      sv[j] = s;
+      tmax = fmaxf(tmax, s);
+    }
+  }
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  const bool bump = tmax > w.m_run + 8.f;
+  const float m_new = bump ? tmax : w.m_run;
+  const float alpha = bump ? __builtin_amdgcn_exp2f(w.m_run - m_new) : 1.f;
+  h8_t p1, p0;
+  float psum = 0.f, spsum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float p = __builtin_amdgcn_exp2f(sv[j] - m_new);
+    const uint32_t nvw = j < 4 ? (&nv[0].x)[j] : (&nv[1].x)[j - 4];
+    const float pv = p * f16_to_f32((uint16_t)nvw);
+    psum += p;
+    spsum += pv;
+    p1[j] = (_Float16)(pv * k.a1);
+    p0[j] = (_Float16)(pv * k.a2);
+  }
+  w.l_run = w.l_run * alpha + psum;
+  w.sp = w.sp * alpha + spsum;
+  w.m_run = m_new;
+  if (__ballot(bump && c < G)) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float av = __shfl(alpha, (4 * q4 + v) & 15);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) w.o[nt][v] *= av;
+    }
+  }
+  // ---- values: N-tile nt = 2 chunk + parity; column c <-> channel 32 chunk + 2 c + parity
+  const uint32_t vx[4] = {(uint32_t)vx0[0], (uint32_t)vx0[1], (uint32_t)vx1[0], (uint32_t)vx1[1]};
+#pragma unroll
+  for (int ch = 0; ch < 4; ++ch) {
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int nt = 2 * ch + par;
+      w.o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p1, bits8((vx[ch] >> (2 * par + 1)) & 0x11111111u), w.o[nt], 0,
+                                                      0, 0);
+      w.o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p0, bits8((vx[ch] >> (2 * par)) & 0x11111111u), w.o[nt], 0, 0,
+                                                      0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int G>
+__global__ void __launch_bounds__(256) decode_turbo_kernel(TurboDecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t stA[4][kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t stB[4][kStage];
+  __shared__ float sm_o[4][G][129];
+  float (*sm_m)[16] = reinterpret_cast<float (*)[16]>(&stB[0][0]);
+  float (*sm_l)[16] = reinterpret_cast<float (*)[16]>(&stB[0][0] + 4 * 16 * sizeof(float));
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const size_t bh = (size_t)b * a.H + h;
+  const int L = min(min(a.seq_lens[b], a.max_len), a.cap);
+  const int t_begin = split * a.per_split;
+  const int t_end = min(L, t_begin + a.per_split);
+  const int q4 = lane >> 4, c = lane & 15;
+
+  Consts k;
+  {
+    const float lv0 = a.levels[0], lv1 = a.levels[1], lv2 = a.levels[2];
+    k.a0 = lv0;
+    k.a1 = lv2 - lv0;
+    k.a2 = lv1 - lv0;
+  }
+  WaveState<G> w;
+  {
+    // prepared query: [R q (128) | S R q (128)] fp32 per query head
+    const int head = c % 8;
+    const bool live = head < G;
+    const bool lo = c >= 8;
+    const float* qp = a.q + ((size_t)b * a.Hq + (size_t)h * G + (live ? head : 0)) * 256;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float coef = (q4 & 1) ? k.a1 : k.a2;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const float v = live ? coef * qp[16 * i + 2 * n + (q4 >> 1)] : 0.f;
+        const _Float16 hi = (_Float16)v;
+        w.blm[i][n] = lo ? (_Float16)(v - (float)hi) : hi;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const float v = live ? qp[128 + 32 * i + 4 * n + q4] : 0.f;
+        const _Float16 hi = (_Float16)v;
+        w.bqs[i][n] = lo ? (_Float16)(v - (float)hi) : hi;
+      }
+    // per-head sums over all 128 entries: this lane's 32 + the other quarters'
+    float sr = 0.f, ss = 0.f;
+#pragma unroll
+    for (int x = 0; x < 32; ++x) {
+      sr += live ? qp[32 * q4 + x] : 0.f;
+      ss += live ? qp[128 + 32 * q4 + x] : 0.f;
+    }
+    sr += __shfl_xor(sr, 16);
+    sr += __shfl_xor(sr, 32);
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    w.cst = k.a0 * sr;
+    w.sqs = ss;
+  }
+  w.m_run = -INFINITY;
+  w.l_run = 0.f;
+  w.sp = 0.f;
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) w.o[nt] = f4_t{0.f, 0.f, 0.f, 0.f};
+
+  const Res res{rsrc(a.k_codes + bh * a.cap * 32, (size_t)a.cap * 32),
+                rsrc(a.k_sketch + bh * a.cap * 16, (size_t)a.cap * 16),
+                rsrc(a.k_norm + bh * a.cap, (size_t)a.cap * 2),
+                rsrc(a.k_rnorm + bh * a.cap, (size_t)a.cap * 2),
+                rsrc(a.v_codes + bh * a.cap * 32, (size_t)a.cap * 32),
+                rsrc(a.v_norm + bh * a.cap, (size_t)a.cap * 2),
+                a.cap * 32};
+  uint8_t* sa = stA[wave];
+  uint8_t* sb = stB[wave];
+  const int none = a.cap;
+  auto tile_or_none = [&](int t) { return t < t_end ? t : none; };
+  int t0 = t_begin + wave * 32;
+  issue_tile(sa, lane, tile_or_none(t0), res);
+  issue_tile(sb, lane, tile_or_none(t0 + 128), res);
+  for (; t0 < t_end; t0 += 256) {
+    tile_step<G>(w, sa, lane, t0, t_end, tile_or_none(t0 + 256), a, k, res);
+    tile_step<G>(w, sb, lane, t0 + 128, t_end, tile_or_none(t0 + 384), a, k, res);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+
+  // ---------------- combine the four waves, write this split's partial result
+  __syncthreads();
+  const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int q4e = lane_e >> 4, ce = lane_e & 15;
+  const int tid_e = wave * 64 + lane_e;
+  float l_run = w.l_run, sp = w.sp;
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  sp += __shfl_xor(sp, 16);
+  sp += __shfl_xor(sp, 32);
+  if (q4e == 0) {
+    sm_m[wave][ce] = w.m_run;
+    sm_l[wave][ce] = l_run;
+  }
+  // the a0 sum(P') term of every output channel, for the head of each O row
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int hh = 4 * q4e + v;
+    const float base = k.a0 * __shfl(sp, hh & 15);
+    if (hh < G) {
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const int ch = 32 * (nt >> 1) + 2 * ce + (nt & 1);
+        sm_o[wave][hh][ch] = w.o[nt][v] + base;
+      }
+    }
+  }
+  __syncthreads();
+  const size_t row0 = (size_t)b * a.Hq + (size_t)h * G;
+  for (int e = tid_e; e < G * 128; e += 256) {
+    const int hh = e >> 7, ch = e & 127;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sm_m[ww][hh]);
+    float Ls = 0.f, O = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const float mw = sm_m[ww][hh];
+      const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
+      Ls += f * sm_l[ww][hh];
+      O += f * sm_o[ww][hh][ch];
+    }
+    float* p = a.part + ((row0 + hh) * a.splits + split) * 130;
+    p[2 + ch] = O;
+    if (ch == 0) {
+      p[0] = M;
+      p[1] = Ls;
+    }
+  }
+}
+
+}  // namespace
+
+int launch_decode_turbo(const TurboDecodeArgs& a, int B, int G, hipStream_t st) {
+  dim3 grid(a.splits, a.H, B);
+  switch (G) {
+    case 1: decode_turbo_kernel<1><<<grid, 256, 0, st>>>(a); break;
+    case 2: decode_turbo_kernel<2><<<grid, 256, 0, st>>>(a); break;
+    case 4: decode_turbo_kernel<4><<<grid, 256, 0, st>>>(a); break;
+    case 8: decode_turbo_kernel<8><<<grid, 256, 0, st>>>(a); break;
+    default: return KV_EUNSUPPORTED;
+  }
+  return KV_OK;
+}
+
+}  // namespace kvq

@@ -67,6 +67,12 @@ int prepared_query_width(const kv_layout* L) {
 
 int value_width(const kv_layout* L) { return L->head_dim; }
 
+bool turbo_fast_path_ok(const kv_layout& L, int num_q_heads) {
+  const int G = num_q_heads / L.num_kv_heads;
+  return L.format == KV_FMT_TURBO && L.head_dim == 128 && L.qjl_m == 128 && L.lm_bits == 2 &&
+         (G == 1 || G == 2 || G == 4 || G == 8) && (size_t)L.capacity * 32 < (size_t(1) << 31);
+}
+
 bool latent_fast_path_ok(const kv_layout& L, int num_q_heads, int q_dtype) {
   return L.format == KV_FMT_LATENT_FP4 && L.head_dim == 512 && L.rope_dim == 64 && q_dtype == KV_DT_BF16 &&
          (num_q_heads == 32 || num_q_heads == 64 || num_q_heads == 128) &&
@@ -87,7 +93,7 @@ SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int q_dtype, int max_
   // workgroups to keep a 256-CU part busy several times over, but no split
   // shorter than a few steps.
   const int G = num_q_heads / L->num_kv_heads;
-  const bool fast = mfma_fast_path_ok(*L, num_q_heads, q_dtype);
+  const bool fast = mfma_fast_path_ok(*L, num_q_heads, q_dtype) || turbo_fast_path_ok(*L, num_q_heads);
   const bool latent = latent_fast_path_ok(*L, num_q_heads, q_dtype);
   const int tile = fast ? 128 : 64;
   // the latent kernel keeps one workgroup per compute unit resident and every

@@ -33,6 +33,8 @@ struct SplitPlan {
 };
 // The matrix-core decode kernel covers this cache / query combination.
 bool mfma_fast_path_ok(const kv_layout& L, int num_q_heads, int q_dtype);
+// The TurboQuant matrix-core kernel covers this cache / query combination.
+bool turbo_fast_path_ok(const kv_layout& L, int num_q_heads);
 // The shared-latent matrix-core kernel covers this cache / query combination.
 bool latent_fast_path_ok(const kv_layout& L, int num_q_heads, int q_dtype);
 SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int q_dtype, int max_seq_len, int requested);

@@ -29,6 +29,26 @@ struct MfmaDecodeArgs {
 
 int launch_decode_mfma(const MfmaDecodeArgs& a, int format, int B, int G, hipStream_t st);
 
+// TurboQuant cache (d = 128, m = 128, 2-bit symmetric codebook), G = Hq / H in
+// {1, 2, 4, 8}; queries prepared as [R q | S R q] fp32.
+struct TurboDecodeArgs {
+  const uint8_t* k_codes;   // [B][H][cap][32]
+  const uint8_t* k_sketch;  // [B][H][cap][16]
+  const uint16_t* k_norm;   // [B][H][cap] fp16
+  const uint16_t* k_rnorm;  // [B][H][cap] fp16
+  const uint8_t* v_codes;   // [B][H][cap][32]
+  const uint16_t* v_norm;   // [B][H][cap] fp16
+  const float* levels;      // 4 codebook levels, ascending, symmetric
+  const float* q;           // [B][Hq][256]
+  const int32_t* seq_lens;
+  int max_len, H, cap, Hq;
+  float scale_log2, kappa;
+  float* part;  // [B][Hq][splits][130]
+  int splits, per_split;
+};
+
+int launch_decode_turbo(const TurboDecodeArgs& a, int B, int G, hipStream_t st);
+
 // Shared-latent cache (512 FP4 + 64 bf16 RoPE), bf16 queries, Hq in {32, 64, 128}.
 bool latent_fast_path_ok(const kv_layout& L, int num_q_heads, int q_dtype);
 int launch_decode_latent(const MfmaDecodeArgs& a, int B, hipStream_t st);

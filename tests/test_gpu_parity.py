@@ -102,10 +102,13 @@ def test_split_count_invariance_and_determinism(fmt):
     lens = torch.from_numpy(synth.seq_lens_for(cfg)).cuda()
     outs = [cache.decode(q, lens, softmax_scale(cfg), splits=s).cpu().numpy() for s in (1, 0, 5, 0)]
     np.testing.assert_array_equal(outs[1], outs[3])
-    # the matrix-core kernels feed softmax weights to the PV product
-    # in fp16 (relative rounding 2^-12 per weight), so different split points may
-    # move a row by a few 1e-4; the fp32 kernels agree to fp32 rounding
-    tol = 6e-4 if fmt in ("fp4", "qjl1", "latent") else 1e-5
+    # The matrix-core kernels feed softmax weights to the PV product in fp16, so
+    # each split configuration moves an output channel by up to 2^-11 of the
+    # largest value it averages; two configurations differ by up to twice that,
+    # and TurboQuant's R^T mixes the rotated channels' rounding into every output.
+    # A split-boundary bug (a token lost or counted twice) shows as ~1e-1.  The
+    # fp32 general kernel agrees with itself to fp32 rounding.
+    tol = 1.5e-3 if fmt in ("fp4", "qjl1", "latent", "turbo") else 1e-5
     for o in outs[:3]:
         assert row_rel_err(o, outs[0]).max() < tol
 
@@ -119,10 +122,11 @@ def test_fp32_inputs(fmt):
     assert_bytes_equal(gpu_buffers(cache), want, fmt + "/f32")
 
 
-@pytest.mark.parametrize("fmt", ["fp4", "qjl1"])
+@pytest.mark.parametrize("fmt", ["fp4", "qjl1", "turbo"])
 @pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
 def test_mfma_group_sizes(fmt, G):
-    """Every query-group size the matrix-core kernel is built for, with a ragged tail."""
+    """Every query-group size the matrix-core kernels are built for (TurboQuant with 16
+    heads per KV head takes the general kernel), with a ragged tail."""
     cfg = SMALL[fmt].scaled(hq=2 * G, hkv=2, context=611)
     cache, K, V = _build(cfg, chunks=1)
     consts = oracle_constants(cfg)
