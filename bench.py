@@ -5,6 +5,11 @@ that token's K/V into the packed cache (the format's pack kernel) and run
 single-query attention over the full context (query prep, split-context
 attention, merge), at a fixed context length.
 
+The timed region replays the step as a HIP graph (captured once after the
+warm-up and checked bit for bit against the eager step); the attention kernel's
+own duration, for the roofline, comes from HIP events around its launches in
+an eager pass over the same number of steps.
+
 Prints one JSON line.  `value` is decode KV GB/s: the packed bytes the
 attention reads per step (codes + scales/norms of every cached token) over the
 measured step time.  The default workload is FP4 E2M1 with one bf16 scale per
@@ -106,6 +111,7 @@ def main():
     ap.add_argument("--config", default="fp4_b16_t32k")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph replay")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -170,6 +176,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # eager timed pass: events around the split-context attention kernel
     s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     w0 = time.perf_counter()
     s0.record()
@@ -178,8 +185,42 @@ def main():
     s1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    ms_step = s0.elapsed_time(s1) / args.steps
+    ms_eager = s0.elapsed_time(s1) / args.steps
     dec_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    ms_step = ms_eager
+    if not args.no_graph:
+        # The same step captured once as a HIP graph and replayed: the launch
+        # overhead of the four kernels leaves the timed region.  Every replay must
+        # reproduce the eager output bit for bit, with eager steps in between.
+        ref = out.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(3):
+            out.zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(out, ref):
+                raise RuntimeError("graph replay differs from the eager step")
+            step()
+            torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        s0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        s1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        ms_step = s0.elapsed_time(s1) / args.steps
     nbytes = counted_bytes(cfg, cache.layout, kvq)
     gbs = nbytes / (ms_step * 1e-3) / 1e9
     achieved = nbytes / (dec_ms * 1e-3) / 1e9
@@ -203,6 +244,8 @@ def main():
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "query_tokens_per_s": round(cfg.batch / (ms_step * 1e-3), 1),
         "wall_s": round(wall, 3),
+        "timing": "hip-graph replay of the step" if not args.no_graph else "eager launches",
+        "ms_per_step_eager": round(ms_eager, 5),
         "roofline": roofline(cfg, nbytes, dec_ms),
     }
     if not args.no_cpu_baseline:

@@ -98,81 +98,100 @@ __device__ __forceinline__ uint32_t kivi_code(float x, float z, float s) {
   return (uint32_t)q;
 }
 
-// Keys: per channel over each 32-token group.  One thread per (row group, group
-// of 4 channels = one output byte per token).
-template <typename InT>
-__device__ __forceinline__ void kivi_keys(const InT* __restrict__ x, int d, uint8_t* __restrict__ codes,
-                                          float* __restrict__ kscale, float* __restrict__ kzero,
-                                          int bh_count, int n, int cap, int start, size_t gid) {
-  const int quads = d / 4, ngroups = n / 32;
-  if (gid >= (size_t)bh_count * ngroups * quads) return;
-  const int cq = (int)(gid % quads);
-  const size_t rest = gid / quads;
-  const int g = (int)(rest % ngroups);
-  const size_t bh = rest / ngroups;
-  const size_t r0 = bh * n + (size_t)g * 32;
-  float mn[4], mx[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) mn[j] = INFINITY, mx[j] = -INFINITY;
-  for (int t = 0; t < 32; ++t)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float v = load_as_f32(x + (r0 + t) * d, 4 * cq + j);
-      mn[j] = fminf(mn[j], v);
-      mx[j] = fmaxf(mx[j], v);
-    }
-  float s[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) s[j] = __fdiv_rn(__fsub_rn(mx[j], mn[j]), 3.0f);
-  for (int t = 0; t < 32; ++t) {
-    uint32_t byte = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      byte |= kivi_code(load_as_f32(x + (r0 + t) * d, 4 * cq + j), mn[j], s[j]) << (2 * j);
-    codes[(bh * cap + start + (size_t)g * 32 + t) * quads + cq] = (uint8_t)byte;
-  }
-  const size_t meta = (bh * (cap / 32) + start / 32 + g) * (size_t)d + 4 * cq;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    kscale[meta + j] = s[j];
-    kzero[meta + j] = mn[j];
-  }
+// One workgroup per (sequence x KV head, 32-token group): the group's keys and
+// values are staged in LDS with coalesced loads, then
+//   keys:   one thread per channel quad, min / max over the 32 tokens;
+//   values: one thread per (token, 32-channel group).
+constexpr int kKiviMaxD = 128;
+
+__device__ __forceinline__ float4 load4_as_f32(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load4_as_f32(const uint16_t* p) {
+  const uint2 r = *reinterpret_cast<const uint2*>(p);
+  return float4{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xFFFF0000u), __uint_as_float(r.y << 16),
+                __uint_as_float(r.y & 0xFFFF0000u)};
 }
 
-// Values: per token over each 32-channel group.  One thread per (token, group).
-template <typename InT>
-__device__ __forceinline__ void kivi_values(const InT* __restrict__ x, int d, uint8_t* __restrict__ codes,
-                                            float* __restrict__ vscale, float* __restrict__ vzero, size_t rows,
-                                            int n, int cap, int start, size_t gid) {
-  const int groups = d / 32;
-  if (gid >= rows * groups) return;
-  const int g = (int)(gid % groups);
-  const size_t r = gid / groups;
-  const InT* src = x + r * d + g * 32;
-  float mn = INFINITY, mx = -INFINITY;
-  for (int i = 0; i < 32; ++i) {
-    float v = load_as_f32(src, i);
-    mn = fminf(mn, v);
-    mx = fmaxf(mx, v);
-  }
-  const float s = __fdiv_rn(__fsub_rn(mx, mn), 3.0f);
-  unsigned long long packed = 0;
-  for (int i = 0; i < 32; ++i) packed |= (unsigned long long)kivi_code(load_as_f32(src, i), mn, s) << (2 * i);
-  const size_t dr = dst_row(r, n, cap, start);
-  *reinterpret_cast<unsigned long long*>(codes + dr * (d / 4) + g * 8) = packed;
-  vscale[dr * groups + g] = s;
-  vzero[dr * groups + g] = mn;
-}
-
-// Keys (blockIdx.y = 0) and values (blockIdx.y = 1) of a KIVI cache in one launch.
 template <typename InT>
 __global__ void __launch_bounds__(256) kivi_append_kernel(const InT* __restrict__ k, const InT* __restrict__ v,
                                                           int d, uint8_t* kc, float* ks, float* kz, uint8_t* vc,
                                                           float* vs, float* vz, int bh_count, int n, int cap,
                                                           int start) {
-  const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (blockIdx.y == 0) kivi_keys(k, d, kc, ks, kz, bh_count, n, cap, start, gid);
-  else kivi_values(v, d, vc, vs, vz, (size_t)bh_count * n, n, cap, start, gid);
+  __shared__ float xk[32][kKiviMaxD + 1];
+  __shared__ float xv[32][kKiviMaxD + 1];
+  const int tid = threadIdx.x;
+  const int ngroups = n / 32;
+  const int g = blockIdx.x % ngroups;
+  const size_t bh = blockIdx.x / ngroups;
+  const size_t r0 = bh * n + (size_t)g * 32;  // first input row of the group
+  {
+    // 32 x d elements as groups of 4 (rows are 16-byte aligned: d is 64 or 128),
+    // every load of this thread in flight before the first store
+    constexpr int kMaxIt = 32 * kKiviMaxD / 4 / 256;
+    float4 a[kMaxIt], bq[kMaxIt];
+#pragma unroll
+    for (int i = 0; i < kMaxIt; ++i) {
+      const int e = 4 * (tid + 256 * i);
+      if (e < 32 * d) {
+        a[i] = load4_as_f32(k + r0 * d + e);
+        bq[i] = load4_as_f32(v + r0 * d + e);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxIt; ++i) {
+      const int e = 4 * (tid + 256 * i);
+      if (e < 32 * d) {
+        const int t = e / d, c = e % d;
+        xk[t][c] = a[i].x, xk[t][c + 1] = a[i].y, xk[t][c + 2] = a[i].z, xk[t][c + 3] = a[i].w;
+        xv[t][c] = bq[i].x, xv[t][c + 1] = bq[i].y, xv[t][c + 2] = bq[i].z, xv[t][c + 3] = bq[i].w;
+      }
+    }
+  }
+  __syncthreads();
+  const int quads = d / 4;
+  const size_t slot0 = bh * cap + start + (size_t)g * 32;  // cache row of the group's first token
+  if (tid < quads) {
+    const int cq = tid;
+    float mn[4], mx[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mn[j] = INFINITY, mx[j] = -INFINITY;
+    for (int t = 0; t < 32; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        mn[j] = fminf(mn[j], xk[t][4 * cq + j]);
+        mx[j] = fmaxf(mx[j], xk[t][4 * cq + j]);
+      }
+    float sc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sc[j] = __fdiv_rn(__fsub_rn(mx[j], mn[j]), 3.0f);
+    for (int t = 0; t < 32; ++t) {
+      uint32_t byte = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) byte |= kivi_code(xk[t][4 * cq + j], mn[j], sc[j]) << (2 * j);
+      kc[(slot0 + t) * quads + cq] = (uint8_t)byte;
+    }
+    const size_t meta = (bh * (cap / 32) + start / 32 + g) * (size_t)d + 4 * cq;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ks[meta + j] = sc[j];
+      kz[meta + j] = mn[j];
+    }
+  }
+  const int vgroups = d / 32;
+  for (int it = tid; it < 32 * vgroups; it += 256) {
+    const int t = it / vgroups, vg = it % vgroups;
+    float mn = INFINITY, mx = -INFINITY;
+    for (int i = 0; i < 32; ++i) {
+      mn = fminf(mn, xv[t][32 * vg + i]);
+      mx = fmaxf(mx, xv[t][32 * vg + i]);
+    }
+    const float sc = __fdiv_rn(__fsub_rn(mx, mn), 3.0f);
+    unsigned long long packed = 0;
+    for (int i = 0; i < 32; ++i) packed |= (unsigned long long)kivi_code(xv[t][32 * vg + i], mn, sc) << (2 * i);
+    const size_t dr = slot0 + t;
+    *reinterpret_cast<unsigned long long*>(vc + dr * (d / 4) + vg * 8) = packed;
+    vs[dr * vgroups + vg] = sc;
+    vz[dr * vgroups + vg] = mn;
+  }
 }
 
 // ---------------------------------------------------------------- QJL sign sketch (MFMA)
@@ -216,6 +235,52 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint16_t (&h)[8]) {
 
 constexpr int kSPad = 136;  // LDS row pitch (elements) of the staged 128 x 128 bf16 matrix
 
+// 32 consecutive elements (bf16 or fp32, 16-byte aligned) as fp32, with the
+// loads issued together.
+__device__ __forceinline__ void load32_as_f32(const uint16_t* p, float (&out)[32]) {
+  uint4 r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = reinterpret_cast<const uint4*>(p)[i];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      out[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+      out[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+  }
+}
+__device__ __forceinline__ void load32_as_f32(const float* p, float (&out)[32]) {
+  float4 r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = reinterpret_cast<const float4*>(p)[i];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    out[4 * i] = r[i].x;
+    out[4 * i + 1] = r[i].y;
+    out[4 * i + 2] = r[i].z;
+    out[4 * i + 3] = r[i].w;
+  }
+}
+
+// Stage a bf16-valued 128 x 128 fp32 matrix into LDS as bf16 (row pitch kSPad):
+// 16 four-float loads per thread, all in flight before the first store.
+__device__ __forceinline__ void stage_bf16_matrix(const float* __restrict__ m, uint16_t* dst) {
+  const int tid = threadIdx.x;
+  float4 v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = reinterpret_cast<const float4*>(m)[tid + 256 * i];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = 4 * (tid + 256 * i);
+    uint2 h;
+    h.x = (__float_as_uint(v[i].x) >> 16) | (__float_as_uint(v[i].y) & 0xFFFF0000u);
+    h.y = (__float_as_uint(v[i].z) >> 16) | (__float_as_uint(v[i].w) & 0xFFFF0000u);
+    *reinterpret_cast<uint2*>(&dst[(e >> 7) * kSPad + (e & 127)]) = h;
+  }
+}
+
 // sketch bit i of a token = [(S k)_i >= 0], plus the token's fp16 norm.
 // A wave takes 16 tokens: A = K rows (bf16, or exact bf16 parts of fp32),
 // B = S^T from LDS, fp32 accumulation on v_mfma_f32_16x16x32_bf16.  Where
@@ -226,21 +291,25 @@ template <typename InT>
 __device__ __forceinline__ void qjl_keys(const InT* __restrict__ x, const float* __restrict__ proj,
                                          uint8_t* __restrict__ sketch, uint16_t* __restrict__ knorm,
                                          size_t rows, int n, int cap, int start, uint16_t* S_lds,
-                                         float* srow_norm) {
+                                         float* srow_norm, int key_blocks) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < 128 * 128; e += 256) {
-    const float v = proj[e];
-    S_lds[(e >> 7) * kSPad + (e & 127)] = (uint16_t)(__float_as_uint(v) >> 16);  // bf16-valued
-  }
-  if (tid < 128) {
+  stage_bf16_matrix(proj, S_lds);  // bf16-valued
+  __syncthreads();
+  {
+    // row norms of S from the staged copy: two threads per row, 64 entries each
+    const int r = tid >> 1, h = tid & 1;
     float acc = 0.f;
-    for (int j = 0; j < 128; ++j) acc = fmaf(proj[tid * 128 + j], proj[tid * 128 + j], acc);
-    srow_norm[tid] = sqrtf(acc) * 1.0001f;
+    for (int j = 0; j < 64; ++j) {
+      const float sv = bf16_to_f32(S_lds[r * kSPad + 64 * h + j]);
+      acc = fmaf(sv, sv, acc);
+    }
+    acc += __shfl_xor(acc, 1);
+    if (h == 0) srow_norm[r] = sqrtf(acc) * 1.0001f;
   }
   __syncthreads();
   constexpr int NP = Bf16Parts<InT>::N;
   const int col = lane & 15, kq = lane >> 4;
-  for (size_t base = ((size_t)blockIdx.x * 4 + wave) * 16; base < rows; base += (size_t)gridDim.x * 64) {
+  for (size_t base = ((size_t)blockIdx.x * 4 + wave) * 16; base < rows; base += (size_t)key_blocks * 64) {
     const size_t my_row = base + col;  // A-operand token of this lane
     const bool valid = my_row < rows;
     f32x4 acc[8];
@@ -290,14 +359,27 @@ __device__ __forceinline__ void qjl_keys(const InT* __restrict__ x, const float*
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
         const int srow_i = nt * 16 + col;
-        float y = acc[nt][i];
+        const float y = acc[nt][i];
         bool bit = y >= 0.f;
         const float bound = (NP == 1 ? 0x1p-14f : 0x1p-12f) * srow_norm[srow_i] * (float)tn;
-        if (fabsf(y) <= bound && trow < rows) {
+        // Signs too close to call in fp32 (about one element in 2^11) are
+        // recomputed in fp64 by the whole wave: every lane takes two of the 128
+        // terms and a butterfly sums them.
+        unsigned long long close = __ballot(fabsf(y) <= bound && trow < rows);
+        while (close) {
+          const int src = __builtin_ctzll(close);
+          close &= close - 1;
+          const int s_row = nt * 16 + (src & 15);
+          const size_t x_row = base + (src >> 4) * 4 + i;
           double e = 0.0;
-          for (int j = 0; j < 128; ++j)
-            e = fma((double)bf16_to_f32(S_lds[srow_i * kSPad + j]), (double)load_as_f32(x + trow * 128, j), e);
-          bit = e >= 0.0;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int j = 2 * lane + h;
+            e = fma((double)bf16_to_f32(S_lds[s_row * kSPad + j]), (double)load_as_f32(x + x_row * 128, j), e);
+          }
+#pragma unroll
+          for (int off = 32; off > 0; off >>= 1) e += __shfl_xor(e, off);
+          if (lane == src) bit = e >= 0.0;
         }
         ballots[nt][i] = __ballot(bit);
       }
@@ -318,17 +400,19 @@ __device__ __forceinline__ void qjl_keys(const InT* __restrict__ x, const float*
   }
 }
 
-// QJL keys (blockIdx.y = 0, persistent over 16-token tiles) and FP4 values
-// (blockIdx.y = 1) in one launch.
+// QJL keys (blockIdx.y = 0: the first key_blocks workgroups, persistent over
+// 64-token tiles, so that staging S is paid once per many tiles) and FP4
+// values (blockIdx.y = 1) in one launch.
 template <typename InT>
 __global__ void __launch_bounds__(256) qjl_append_kernel(const InT* __restrict__ k, const InT* __restrict__ v,
                                                          const float* __restrict__ proj, uint8_t* sketch,
                                                          uint16_t* knorm, uint8_t* vc, uint16_t* vs, size_t rows,
-                                                         int n, int cap, int start) {
+                                                         int n, int cap, int start, int key_blocks) {
   __shared__ __align__(16) uint16_t S_lds[128 * kSPad];
   __shared__ float srow_norm[128];
   if (blockIdx.y == 0) {
-    qjl_keys(k, proj, sketch, knorm, rows, n, cap, start, S_lds, srow_norm);
+    if ((int)blockIdx.x >= key_blocks) return;
+    qjl_keys(k, proj, sketch, knorm, rows, n, cap, start, S_lds, srow_norm, key_blocks);
   } else {
     const size_t groups = rows * 8;
     for (size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x; gid < groups;
@@ -353,20 +437,23 @@ __device__ __forceinline__ void turbo_body(const InT* __restrict__ x, const floa
                                            int start, uint16_t* R_lds, uint16_t* S_lds,
                                            double (*scratch)[16 * 129], uint8_t (*idx_lds)[16 * 128]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < 128 * 128; e += 256) {
-    R_lds[(e >> 7) * kSPad + (e & 127)] = (uint16_t)(__float_as_uint(rot[e]) >> 16);
-    if (WITH_SKETCH) S_lds[(e >> 7) * kSPad + (e & 127)] = (uint16_t)(__float_as_uint(proj[e]) >> 16);
-  }
+  stage_bf16_matrix(rot, R_lds);  // bf16-valued
+  if (WITH_SKETCH) stage_bf16_matrix(proj, S_lds);
   __syncthreads();
   const double t0 = thresh[0], t1 = thresh[1], t2 = thresh[2];
   const double lv0 = levels[0], lv1 = levels[1], lv2 = levels[2], lv3 = levels[3];
   double* xs = scratch[wave];
   const int col = lane & 15, kq = lane >> 4;
   for (size_t base = ((size_t)blockIdx.x * 4 + wave) * 16; base < rows; base += (size_t)gridDim.x * 64) {
-    // stage 16 tokens x 128 as double, zero past the last row
-    for (int e = lane; e < 16 * 128; e += 64) {
-      const int tk = e >> 7, c = e & 127;
-      xs[tk * 129 + c] = (base + tk < rows) ? (double)load_as_f32(x + (base + tk) * 128, c) : 0.0;
+    // stage 16 tokens x 128 as double, zero past the last row: lane takes token
+    // lane / 4, channels 32 (lane % 4) + [0, 32), all loads in flight at once
+    {
+      const int tk = lane >> 2, c0 = 32 * (lane & 3);
+      const bool ok = base + tk < rows;
+      float xv[32];
+      load32_as_f32(x + (base + (ok ? tk : 0)) * 128 + c0, xv);
+#pragma unroll
+      for (int j = 0; j < 32; ++j) xs[tk * 129 + c0 + j] = ok ? (double)xv[j] : 0.0;
     }
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
@@ -533,18 +620,19 @@ int append_typed(const kv_cache* c, const InT* k, const InT* v, int start, int n
       break;
     }
     case KV_FMT_KIVI2: {
-      const size_t work = std::max((size_t)bh * (n / 32) * (d / 4), rows * (d / 32));
-      kivi_append_kernel<InT><<<dim3(blocks_for(work), 2), 256, 0, st>>>(
+      kivi_append_kernel<InT><<<dim3(bh * (n / 32)), 256, 0, st>>>(
           k, v, d, kc, static_cast<float*>(c->buf[KV_BUF_K_SCALE]), static_cast<float*>(c->buf[KV_BUF_K_ZERO]),
           vc, static_cast<float*>(c->buf[KV_BUF_V_SCALE]), static_cast<float*>(c->buf[KV_BUF_V_ZERO]), bh, n,
           cap, start);
       break;
     }
     case KV_FMT_QJL1_FP4V: {
-      const int blocks = std::max(persistent_blocks(rows), std::min(blocks_for(rows * (d / 16)), 2048));
+      // keys: a few long-lived workgroups per CU; values: enough to fill the chip
+      const int key_blocks = (int)std::min<size_t>((rows + 63) / 64, 512);
+      const int blocks = std::max(key_blocks, std::min(blocks_for(rows * (d / 16)), 2048));
       qjl_append_kernel<InT><<<dim3(blocks, 2), 256, 0, st>>>(
           k, v, c->proj, static_cast<uint8_t*>(c->buf[KV_BUF_K_SKETCH]), static_cast<uint16_t*>(c->buf[KV_BUF_K_NORM]),
-          vc, vs, rows, n, cap, start);
+          vc, vs, rows, n, cap, start, key_blocks);
       break;
     }
     case KV_FMT_TURBO:

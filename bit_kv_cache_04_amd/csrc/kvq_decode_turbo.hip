@@ -211,8 +211,13 @@ __device__ __forceinline__ void tile_step(WaveState<G>& w, uint8_t* st, int lane
   __builtin_amdgcn_sched_barrier(0);
 }
 
+#ifndef KVQ_TURBO_WAVES_PER_EU
+#define KVQ_TURBO_WAVES_PER_EU 2  // waves per SIMD the register budget is cut for
+#endif
+
 template <int G>
-__global__ void __launch_bounds__(256) decode_turbo_kernel(TurboDecodeArgs a) {
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(KVQ_TURBO_WAVES_PER_EU, KVQ_TURBO_WAVES_PER_EU))) decode_turbo_kernel(TurboDecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t stA[4][kStage];
   __shared__ __attribute__((aligned(16))) uint8_t stB[4][kStage];
   __shared__ float sm_o[4][G][129];

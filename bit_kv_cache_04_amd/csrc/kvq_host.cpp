@@ -54,6 +54,8 @@ int check_cache(const kv_cache* c) {
   int f = c->layout.format;
   if (f == KV_FMT_TURBO && (!c->rot || !c->proj || !c->lm_levels || !c->lm_thresh)) return KV_EINVAL;
   if (f == KV_FMT_QJL1_FP4V && !c->proj) return KV_EINVAL;
+  // the append kernels stage R and S with 16-byte loads
+  if ((reinterpret_cast<uintptr_t>(c->rot) | reinterpret_cast<uintptr_t>(c->proj)) & 15) return KV_EINVAL;
   return KV_OK;
 }
 
@@ -104,7 +106,7 @@ SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int q_dtype, int max_
   int splits = requested;
   if (splits <= 0) {
     long want = (target + units - 1) / units;
-    long maxs = (max_seq_len + 4 * tile - 1) / (4 * tile);
+    long maxs = (max_seq_len + tile - 1) / tile;  // at least one tile per split
     splits = (int)std::max(1L, std::min(want, maxs));
   }
   if (splits > 1024) splits = 1024;

@@ -119,10 +119,15 @@ enum kv_buffer {
 
 /* A cache: its layout, device buffers (NULL where the format has none) and
  * the method's constants, as device arrays of fp32 (made by the helpers below):
- *   rot        TURBO: d x d rotation R, row-major, y = R x, bf16-valued
- *   proj       TURBO, QJL1: m x d QJL matrix S, row-major, bf16-valued
- *   lm_levels  TURBO: 2^lm_bits Lloyd-Max levels, ascending
- *   lm_thresh  TURBO: 2^lm_bits - 1 thresholds, ascending                   */
+ *   rot        TURBO: d x d rotation R, row-major, y = R x, bf16-valued,
+ *              16-byte aligned
+ *   proj       TURBO, QJL1: m x d QJL matrix S, row-major, bf16-valued,
+ *              16-byte aligned
+ *   lm_levels  TURBO: 2^lm_bits Lloyd-Max levels, ascending and symmetric
+ *              (levels[i] = -levels[last - i], as kv_lloyd_max_gaussian makes
+ *              them: the decode kernel relies on it)
+ *   lm_thresh  TURBO: 2^lm_bits - 1 thresholds, ascending
+ * A missing or misaligned constant is KV_EINVAL.                           */
 typedef struct kv_cache {
   kv_layout layout;
   void* buf[KV_BUF_COUNT];

@@ -130,6 +130,9 @@ def test_append_validation():
     assert _append(_cache("kivi2", d=64), start=16, n=32) == EINVAL
     assert _append(_cache("latent", H=1, d=512, rope=64)) == EINVAL   # latent takes no v
     assert _append(_cache("turbo", consts=False)) == EINVAL           # constants missing
+    c = _cache("qjl1")
+    c.proj = FAKE + 8
+    assert _append(c) == EINVAL                                       # misaligned projection
     assert _append(_cache("fp4", d=96)) == EUNSUP
     assert _append(_cache("fp4", B=0)) == EINVAL
     assert _append(_cache(), n=0) == OK                               # nothing to do, nothing launched

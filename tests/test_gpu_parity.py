@@ -187,3 +187,46 @@ def test_growing_logits_rescale(fmt):
     err = row_rel_err(out, ref)
     print(f"  {fmt} ramped keys: max row rel err {err.max():.3e}", flush=True)
     assert err.max() <= RTOL
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "qjl1", "turbo", "latent", "kivi2"])
+def test_graph_replay_matches_eager(fmt):
+    """Append + decode captured as a HIP graph: every replay, with eager work and
+    synchronisations in between, reproduces the eager result bit for bit."""
+    cfg = SMALL[fmt]
+    cache, K, V = _build(cfg)
+    q = synth.make_queries(cfg, device="cuda")
+    lens = torch.from_numpy(synth.seq_lens_for(cfg)).cuda()
+    n = 32 if fmt == "kivi2" else 1
+    t0 = cfg.context - n
+    if fmt == "latent":
+        kn, vn = K[:, t0:].contiguous(), None
+    else:
+        kn, vn = K[:, :, t0:].contiguous(), V[:, :, t0:].contiguous()
+    out = torch.empty(cfg.batch, cfg.hq, cfg.head_dim, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(cache.workspace_bytes(cfg.hq, cfg.context, 0, q.dtype), dtype=torch.uint8, device="cuda")
+
+    def step():
+        cache.append(kn, vn, t0)
+        cache.decode(q, lens, softmax_scale(cfg), out=out, ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
