@@ -1,8 +1,9 @@
 // Decode attention on the matrix cores over a shared latent cache: every query
 // head attends to one 512-channel latent per token (FP4 E2M1, one bf16 scale per
 // 16 channels) plus a 64-channel bf16 RoPE key; the value is the latent itself
-// (page "How DeepSeek-V4 ...": the latent-compressed attention whose keys and
-// values are one shared low-rank vector per token, with a separate rotary part).
+// (page "How DeepSeek-V4.1-Flash cut KV-cache storage by 4x via CSA2", CSA2
+// section: one 512-channel latent shared by the heads, with a 64-channel RoPE
+// part).
 //
 // With 128 query heads on one latent the per-token work is a dense contraction
 // (2 x 128 x (576 + 512) flop per 448 packed bytes), far past the HBM ridge, so
