@@ -89,6 +89,7 @@ __device__ __forceinline__ int row_token(int c) { return 4 * (c & 3) + (c >> 2);
 // FP4 keys: codes (64 B per token) and scales (16 B per token).
 struct KeysFp4 {
   static constexpr int kBytes = 2560;  // codes 2048 | scales 512
+  static constexpr int kDma = 4;       // direct-to-LDS loads issue() makes
   struct Q {
     h8_t f[4];  // lane (q4, c): head c, channels 32*q4 + 8*i + j for MFMA i
   };
@@ -152,6 +153,7 @@ struct KeysFp4 {
 // 1-bit QJL keys: 128 sketch bits (16 B per token) and the fp16 key norm.
 struct KeysQjl {
   static constexpr int kBytes = 768;  // sketch 512 | norms, one per dword: 128 (+ 128 zeros)
+  static constexpr int kDma = 3;      // direct-to-LDS loads issue() makes
   struct Q {
     // lane (q4, c): head c; MFMA i, k-slot pair p, element e <-> sketch row 32*q4 + 4*i + p + 16*e
     h8_t hi[4], lo[4];
@@ -292,6 +294,10 @@ template <int G, class KP>
 __device__ __forceinline__ void tile_step(WaveState<KP>& w, uint8_t* st, int lane, int t0, int t_end, int t_next,
                                           const MfmaDecodeArgs& a, const typename KP::R& kr, const VRsrc& vr) {
   const int q4 = lane >> 4, c = lane & 15;
+  // This stage's tile has landed once at most the other stage's refill is
+  // outstanding.  Waited for explicitly: the compiler's own wait for loads into
+  // LDS is not placed reliably across the loop back-edge.
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (KP::kDma + 4));  // vmcnt(key loads + 4 value loads)
   typename KP::Frag kf;
   KP::read(kf, st, q4, c);
   // Lane byte offsets into the stage; opaque to the optimiser so that every read

@@ -78,6 +78,8 @@ struct Res {
   int n_end;  // a byte offset past every norm resource
 };
 
+constexpr int kDmaPerTile = 6;  // direct-to-LDS loads issue_tile makes
+
 __device__ __forceinline__ void issue_tile(uint8_t* st, int lane, int t0, const Res& r) {
   const int c16 = t0 * 32 + lane * 16;
   const int nb = lane < 32 ? t0 * 2 + lane * 2 : r.n_end;
@@ -109,6 +111,11 @@ template <int G>
 __device__ __forceinline__ void tile_step(WaveState<G>& w, uint8_t* st, int lane, int t0, int t_end, int t_next,
                                           const TurboDecodeArgs& a, const Consts& k, const Res& res) {
   const int q4 = lane >> 4, c = lane & 15;
+  // This stage's tile has landed once at most the other stage's refill (the
+  // kDmaPerTile loads issued after it) is outstanding.  Waited for explicitly:
+  // the compiler's own wait for loads into LDS is not placed reliably across
+  // the loop back-edge.
+  __builtin_amdgcn_s_waitcnt(0x0F70 | kDmaPerTile);  // vmcnt(kDmaPerTile)
   // ---- fragments of this lane
   int ko = qk_token(c, 0) * 32, so = qk_token(c, 0) * 16, no = 4 * 8 * q4;
   int vo = (8 * q4 + (c & 7)) * 32 + 8 * (c >> 3);

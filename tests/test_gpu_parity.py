@@ -230,3 +230,20 @@ def test_graph_replay_matches_eager(fmt):
         step()
         torch.cuda.synchronize()
         assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "qjl1", "turbo", "latent"])
+def test_repeated_decode_bit_identical(fmt):
+    """Many tiles per wave on both halves of each LDS ring: repeated decodes of the
+    same cache must agree bit for bit (a read of a ring stage before its loads
+    land shows up here as run-to-run differences)."""
+    cfg = SMALL[fmt].scaled(batch=4, context=12288)
+    cache, _, _ = _build(cfg, chunks=3)
+    q = synth.make_queries(cfg, device="cuda")
+    lens = torch.full((cfg.batch,), cfg.context, dtype=torch.int32, device="cuda")
+    ref = cache.decode(q, lens, softmax_scale(cfg), splits=4)
+    torch.cuda.synchronize()
+    for _ in range(12):
+        out = cache.decode(q, lens, softmax_scale(cfg), splits=4)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
