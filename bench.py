@@ -87,6 +87,27 @@ def cpu_baseline(cfg, budget_s=12.0):
 MFMA_F16_PEAK_TFLOPS = 2500.0
 
 
+def measured_traffic(workload):
+    """HBM bytes per launch of the attention kernel from the committed counter
+    summary (profiles/*_<workload>_pmc.txt: FETCH_SIZE and WRITE_SIZE scaled by a
+    plain copy of known size), or None when there is none or the kernel's source
+    has changed since the counters were taken."""
+    import glob
+    import hashlib
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"*_{workload}_pmc.txt"))):
+        kv = {}
+        for line in open(path):
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        src = os.path.join(ROOT, kv.get("source", ""))
+        if not os.path.isfile(src) or "traffic_bytes_per_launch" not in kv:
+            continue
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() == kv.get("source_sha256"):
+            return int(kv["traffic_bytes_per_launch"])
+    return None
+
+
 def roofline(cfg, nbytes, dec_ms):
     """Roofline of the split-context attention kernel, timed by events around its launch."""
     if cfg.fmt == "latent":
@@ -94,12 +115,12 @@ def roofline(cfg, nbytes, dec_ms):
         flops = 2.0 * cfg.batch * cfg.context * cfg.hq * (cfg.key_width + cfg.head_dim)
         ach = flops / (dec_ms * 1e-3) / 1e12
         return {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4), "traffic": measured_traffic(cfg.name),
                 "kernel": "split-context attention", "kernel_us": round(dec_ms * 1e3, 2),
                 "hbm_gbs": round(nbytes / (dec_ms * 1e-3) / 1e9, 2)}
     ach = nbytes / (dec_ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(cfg.name),
             "kernel": "split-context attention", "kernel_us": round(dec_ms * 1e3, 2)}
 
 
