@@ -68,6 +68,15 @@ __device__ __forceinline__ h8_t bits8(uint32_t m) {
   return r;
 }
 
+// Value of lane (l & ~15) | ((l + 8) & 15): the other half of this lane's
+// 16-lane row (a DPP row rotation by 8).
+__device__ __forceinline__ float row_ror8(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t row_ror8(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, false);
+}
+
 // QK A-operand row rho of block b (16 rows) holds token 8 (rho / 4) + 4 b + rho % 4:
 // then the result rows a lane holds (4 (lane / 16) + v) in blocks 0 and 1 are the
 // tokens 8 (lane / 16) + j, j = 4 b + v = 0..7: the PV k-slots of that lane.
@@ -128,13 +137,12 @@ __device__ __forceinline__ void tile_step(WaveState<G>& w, uint8_t* st, int lane
     kw[b][1] = *reinterpret_cast<const uint4*>(st + kSK + ko + 128 * b + 16);
     sw[b] = *reinterpret_cast<const uint4*>(st + kSS + so + 64 * b);
   }
-  uint4 nk[2], nr[2], nv[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    nk[h] = *reinterpret_cast<const uint4*>(st + kSN + no + 16 * h);
-    nr[h] = *reinterpret_cast<const uint4*>(st + kSR + no + 16 * h);
-    nv[h] = *reinterpret_cast<const uint4*>(st + kSVN + no + 16 * h);
-  }
+  // Norms of the 4 tokens this lane scores after the hi + lo combine (below):
+  // columns 0..7 take tokens 8 q4 + [0, 4), columns 8..15 tokens 8 q4 + [4, 8).
+  const int nofs = no + (c >= 8 ? 16 : 0);
+  const uint4 nk = *reinterpret_cast<const uint4*>(st + kSN + nofs);
+  const uint4 nr = *reinterpret_cast<const uint4*>(st + kSR + nofs);
+  const uint4 nv = *reinterpret_cast<const uint4*>(st + kSVN + nofs);
   const i2_t vx0 = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
       (__attribute__((address_space(3))) i2_t*)(st + kSV + vo));
   const i2_t vx1 = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
@@ -143,57 +151,75 @@ __device__ __forceinline__ void tile_step(WaveState<G>& w, uint8_t* st, int lane
   issue_tile(st, lane, t_next, res);
 
   // ---- logits: S^T = K Q^T, code-bit steps then sketch steps, per 16-token block
-  float sv[8];
-  float tmax = -INFINITY;
+  f4_t lm[2], qj[2];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const uint32_t words[8] = {kw[b][0].x, kw[b][0].y, kw[b][0].z, kw[b][0].w,
                                kw[b][1].x, kw[b][1].y, kw[b][1].z, kw[b][1].w};
-    f4_t lm = f4_t{0.f, 0.f, 0.f, 0.f}, qj = f4_t{0.f, 0.f, 0.f, 0.f};
+    lm[b] = f4_t{0.f, 0.f, 0.f, 0.f};
+    qj[b] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      lm = __builtin_amdgcn_mfma_f32_16x16x32_f16(bits8((words[i] >> q4) & 0x11111111u), w.blm[i], lm, 0, 0, 0);
+      lm[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bits8((words[i] >> q4) & 0x11111111u), w.blm[i], lm[b], 0, 0, 0);
     const uint32_t sks[4] = {sw[b].x, sw[b].y, sw[b].z, sw[b].w};
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      qj = __builtin_amdgcn_mfma_f32_16x16x32_f16(bits8((sks[i] >> q4) & 0x11111111u), w.bqs[i], qj, 0, 0, 0);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      // hi part (columns < 8) plus lo part (columns 8..15) of the same head
-      const float l_ = lm[v] + __shfl_xor(lm[v], 8);
-      const float q_ = qj[v] + __shfl_xor(qj[v], 8);
-      const int j = 4 * b + v;  // token 8 q4 + j
-      const uint32_t nkw = j < 4 ? (&nk[0].x)[j] : (&nk[1].x)[j - 4];
-      const uint32_t nrw = j < 4 ? (&nr[0].x)[j] : (&nr[1].x)[j - 4];
-      const float n = f16_to_f32((uint16_t)nkw), gm = f16_to_f32((uint16_t)nrw);
-      const float logit = n * ((l_ + w.cst) + a.kappa * gm * fmaf(2.f, q_, -w.sqs));
-      const int tok = t0 + 8 * q4 + j;
-      float s = tok < t_end ? logit * a.scale_log2 : -INFINITY;
-      if (c >= G) s = 0.f;  // columns past the group hold no head: keep them finite
-      sv[j] = s;
-      tmax = fmaxf(tmax, s);
-    }
+      qj[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bits8((sks[i] >> q4) & 0x11111111u), w.bqs[i], qj[b], 0, 0, 0);
   }
+  // Column c < 8 holds the hi part of head c, column c + 8 its lo part.  Each
+  // lane keeps one block and adds the partner column's part of that block:
+  // columns 0..7 finish block 0, columns 8..15 block 1, both for head c % 8.
+  const bool upper = c >= 8;
+  float sv[4];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const float l_ = (upper ? lm[1][v] : lm[0][v]) + row_ror8(upper ? lm[0][v] : lm[1][v]);
+    const float q_ = (upper ? qj[1][v] : qj[0][v]) + row_ror8(upper ? qj[0][v] : qj[1][v]);
+    const float n = f16_to_f32((uint16_t)(&nk.x)[v]), gm = f16_to_f32((uint16_t)(&nr.x)[v]);
+    const float logit = n * ((l_ + w.cst) + a.kappa * gm * fmaf(2.f, q_, -w.sqs));
+    const int tok = t0 + 8 * q4 + (upper ? 4 : 0) + v;
+    float s = tok < t_end ? logit * a.scale_log2 : -INFINITY;
+    if ((c & 7) >= G) s = 0.f;  // columns past the group hold no head: keep them finite
+    sv[v] = s;
+    tmax = fmaxf(tmax, s);
+  }
+  tmax = fmaxf(tmax, row_ror8(tmax));
   tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
   const bool bump = tmax > w.m_run + 8.f;
   const float m_new = bump ? tmax : w.m_run;
   const float alpha = bump ? __builtin_amdgcn_exp2f(w.m_run - m_new) : 1.f;
-  h8_t p1, p0;
   float psum = 0.f, spsum = 0.f;
+  uint32_t own1[2], own0[2];  // this lane's 4 weights times a1 / a2, as fp16 pairs
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float p = __builtin_amdgcn_exp2f(sv[j] - m_new);
-    const uint32_t nvw = j < 4 ? (&nv[0].x)[j] : (&nv[1].x)[j - 4];
-    const float pv = p * f16_to_f32((uint16_t)nvw);
-    psum += p;
-    spsum += pv;
-    p1[j] = (_Float16)(pv * k.a1);
-    p0[j] = (_Float16)(pv * k.a2);
+  for (int v = 0; v < 4; v += 2) {
+    float pv[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float p = __builtin_amdgcn_exp2f(sv[v + e] - m_new);
+      pv[e] = p * f16_to_f32((uint16_t)(&nv.x)[v + e]);
+      psum += p;
+      spsum += pv[e];
+    }
+    // round to nearest (a truncating pack would bias every weight low)
+    own1[v / 2] = __builtin_bit_cast(uint32_t, h2_t{(_Float16)(pv[0] * k.a1), (_Float16)(pv[1] * k.a1)});
+    own0[v / 2] = __builtin_bit_cast(uint32_t, h2_t{(_Float16)(pv[0] * k.a2), (_Float16)(pv[1] * k.a2)});
   }
   w.l_run = w.l_run * alpha + psum;
   w.sp = w.sp * alpha + spsum;
   w.m_run = m_new;
+  // PV A operand of row c (head c for c < 8): tokens 8 q4 + [0, 8) = this lane's
+  // 4 and the partner column's 4 (rows 8..15 are not heads and are discarded)
+  h8_t p1, p0;
+  {
+    const uint32_t o1a = row_ror8(own1[0]), o1b = row_ror8(own1[1]);
+    const uint32_t o0a = row_ror8(own0[0]), o0b = row_ror8(own0[1]);
+    const uint4 w1 = upper ? uint4{o1a, o1b, own1[0], own1[1]} : uint4{own1[0], own1[1], o1a, o1b};
+    const uint4 w0 = upper ? uint4{o0a, o0b, own0[0], own0[1]} : uint4{own0[0], own0[1], o0a, o0b};
+    p1 = __builtin_bit_cast(h8_t, w1);
+    p0 = __builtin_bit_cast(h8_t, w0);
+  }
   if (__ballot(bump && c < G)) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -318,8 +344,10 @@ __attribute__((amdgpu_waves_per_eu(KVQ_TURBO_WAVES_PER_EU, KVQ_TURBO_WAVES_PER_E
   const int q4e = lane_e >> 4, ce = lane_e & 15;
   const int tid_e = wave * 64 + lane_e;
   float l_run = w.l_run, sp = w.sp;
+  l_run += row_ror8(l_run);  // the two column halves scored disjoint tokens
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
+  sp += row_ror8(sp);
   sp += __shfl_xor(sp, 16);
   sp += __shfl_xor(sp, 32);
   if (q4e == 0) {
