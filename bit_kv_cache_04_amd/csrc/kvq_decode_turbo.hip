@@ -245,7 +245,7 @@ __device__ __forceinline__ void tile_step(WaveState<G>& w, uint8_t* st, int lane
 }
 
 #ifndef KVQ_TURBO_WAVES_PER_EU
-#define KVQ_TURBO_WAVES_PER_EU 2  // waves per SIMD the register budget is cut for
+#define KVQ_TURBO_WAVES_PER_EU 3  // waves per SIMD the register budget is cut for
 #endif
 
 template <int G>
