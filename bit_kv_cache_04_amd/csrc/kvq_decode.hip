@@ -241,64 +241,101 @@ __global__ void __launch_bounds__(128) prep_query_kernel(const QT* __restrict__ 
 // ---------------------------------------------------------------- merge
 
 // out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, M = max_s m_s, for one
-// (sequence, query head) row per workgroup of 128 threads.  The split weights
-// are formed once in LDS; each thread then sums its channels over the splits
-// with independent loads.  TURBO maps the rotated output back with R^T.  A row
-// with no tokens at all writes zeros.
-constexpr int kMergeThreads = 128;
+// (sequence, query head) row per blockIdx.x and the columns
+// [64 * NJ * blockIdx.y, 64 * NJ * (blockIdx.y + 1)).  The split weights are
+// formed once in LDS; wave w then sums the splits w, w + W, ... (W waves) for
+// every column of the block, lane l owning columns NJ * l .. NJ * l + NJ - 1,
+// so that the loads of different splits are independent and spread over the
+// block; the W wave sums are added in wave order.  TURBO (the whole row in one
+// block) maps the rotated output back with R^T.  A row with no tokens at all
+// writes zeros.
+constexpr int kMergeMaxWaves = 16;
 constexpr int kMaxSplits = 1024;
 
-__global__ void __launch_bounds__(kMergeThreads) merge_kernel(const float* __restrict__ part, int splits, int dv,
-                                                              int fmt, const float* __restrict__ rot,
-                                                              float* __restrict__ out) {
+template <int NJ>
+__global__ void __launch_bounds__(64 * kMergeMaxWaves) merge_kernel(const float* __restrict__ part, int splits,
+                                                                    int dv, int fmt, const float* __restrict__ rot,
+                                                                    float* __restrict__ out) {
+  constexpr int CW = 64 * NJ;
   __shared__ float w[kMaxSplits];
-  __shared__ float red[kMergeThreads / 64];
-  __shared__ float ov[512];
+  __shared__ float red[kMergeMaxWaves];
+  __shared__ float sums[kMergeMaxWaves][CW];
+  __shared__ float ov[CW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nthr = blockDim.x, W = nthr >> 6;
   const size_t row = blockIdx.x;
-  const float* p = part + row * (size_t)splits * (dv + 2);
+  const size_t stride = (size_t)dv + 2;
+  const float* p = part + row * (size_t)splits * stride;
   float M = -INFINITY;
-  for (int s = tid; s < splits; s += kMergeThreads) M = fmaxf(M, p[(size_t)s * (dv + 2)]);
+  for (int s = tid; s < splits; s += nthr) M = fmaxf(M, p[s * stride]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   if (lane == 0) red[wave] = M;
   __syncthreads();
-  M = fmaxf(red[0], red[1]);
+  M = red[0];
+  for (int i = 1; i < W; ++i) M = fmaxf(M, red[i]);
   __syncthreads();
   float l = 0.f;
-  for (int s = tid; s < splits; s += kMergeThreads) {
-    const float ms = p[(size_t)s * (dv + 2)];
+  for (int s = tid; s < splits; s += nthr) {
+    const float ms = p[s * stride];
     const float ws = ms == -INFINITY ? 0.f : exp2f(ms - M);
     w[s] = ws;
-    l += ws * p[(size_t)s * (dv + 2) + 1];
+    l += ws * p[s * stride + 1];
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
   if (lane == 0) red[wave] = l;
   __syncthreads();
-  l = red[0] + red[1];
+  l = red[0];
+  for (int i = 1; i < W; ++i) l += red[i];
   const float inv_l = l > 0.f ? 1.f / l : 0.f;
-  float* dst = out + row * dv;
-  for (int c = tid; c < dv; c += kMergeThreads) {
-    float acc = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < splits; ++s) acc = fmaf(w[s], p[(size_t)s * (dv + 2) + 2 + c], acc);
-    if (fmt == KV_FMT_TURBO) ov[c] = acc * inv_l;
-    else dst[c] = acc * inv_l;
+  const int c0 = CW * blockIdx.y;
+  float acc[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) acc[j] = 0.f;
+  const float* pc = p + 2 + c0 + NJ * lane;
+#pragma unroll 4
+  for (int s = wave; s < splits; s += W) {
+    const float ws = w[s];
+    if constexpr (NJ == 2) {
+      const float2 v = *reinterpret_cast<const float2*>(pc + s * stride);
+      acc[0] = fmaf(ws, v.x, acc[0]);
+      acc[1] = fmaf(ws, v.y, acc[1]);
+    } else {
+      acc[0] = fmaf(ws, pc[s * stride], acc[0]);
+    }
   }
-  if (fmt == KV_FMT_TURBO) {
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) sums[wave][NJ * lane + j] = acc[j];
+  __syncthreads();
+  float* dst = out + row * dv;
+  for (int c = tid; c < CW; c += nthr) {
+    float t = sums[0][c];
+    for (int i = 1; i < W; ++i) t += sums[i][c];
+    if (fmt == KV_FMT_TURBO) ov[c] = t * inv_l;
+    else dst[c0 + c] = t * inv_l;
+  }
+  if (fmt == KV_FMT_TURBO) {  // CW == dv here
     __syncthreads();
-    for (int c = tid; c < dv; c += kMergeThreads) {
-      float acc = 0.f;
-      for (int j = 0; j < dv; ++j) acc = fmaf(rot[j * dv + c], ov[j], acc);
-      dst[c] = acc;
+    for (int c = tid; c < CW; c += nthr) {
+      float a = 0.f;
+      for (int j = 0; j < CW; ++j) a = fmaf(rot[j * CW + c], ov[j], a);
+      dst[c] = a;
     }
   }
 }
 
+// Column blocks of 128 (dv a multiple of 128) or 64; TURBO keeps the row in one
+// block.  Waves: about four splits each, at most 16.
 void launch_merge(const float* part, int rows, int splits, int dv, int fmt, const float* rot, float* out,
                   hipStream_t st) {
-  merge_kernel<<<rows, kMergeThreads, 0, st>>>(part, splits, dv, fmt, rot, out);
+  const int nj = dv % 128 == 0 ? 2 : 1;
+  const int cw = 64 * nj;
+  const int col_blocks = fmt == KV_FMT_TURBO ? 1 : dv / cw;
+  const int waves = std::min(kMergeMaxWaves, std::max(1, (splits + 3) / 4));
+  const dim3 grid(rows, col_blocks);
+  if (nj == 2) merge_kernel<2><<<grid, 64 * waves, 0, st>>>(part, splits, dv, fmt, rot, out);
+  else merge_kernel<1><<<grid, 64 * waves, 0, st>>>(part, splits, dv, fmt, rot, out);
 }
 
 template <int FMT, int DK, int DV, int HB>
