@@ -27,8 +27,138 @@ __device__ __forceinline__ size_t dst_row(size_t r, int n, int cap, int start) {
 
 // ---------------------------------------------------------------- FP4
 
-// One thread per 16-channel group: s = bf16_RNE(absmax / 6) (the quotient taken
-// in fp64, then rounded once), then each element's E2M1 nibble against s.
+// 16 consecutive input elements, read with 16-byte loads (input rows and group
+// offsets are multiples of 16 bytes) and unpacked to fp32 when needed.
+template <typename InT>
+struct Raw16;
+template <>
+struct Raw16<uint16_t> {
+  uint4 w[2];
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    w[0] = reinterpret_cast<const uint4*>(p)[0];
+    w[1] = reinterpret_cast<const uint4*>(p)[1];
+  }
+  __device__ __forceinline__ void zero() { w[0] = w[1] = make_uint4(0u, 0u, 0u, 0u); }
+  __device__ __forceinline__ void unpack(float (&f)[16]) const {
+    const uint32_t u[8] = {w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      f[2 * i] = __uint_as_float(u[i] << 16);
+      f[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+    }
+  }
+};
+template <>
+struct Raw16<float> {
+  float4 w[4];
+  __device__ __forceinline__ void load(const float* p) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = reinterpret_cast<const float4*>(p)[i];
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = float4{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ __forceinline__ void unpack(float (&f)[16]) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[4 * i] = w[i].x;
+      f[4 * i + 1] = w[i].y;
+      f[4 * i + 2] = w[i].z;
+      f[4 * i + 3] = w[i].w;
+    }
+  }
+};
+
+// One 16-value group: s = bf16_RNE(absmax / 6) (the quotient taken in fp64,
+// then rounded once), then each element's E2M1 nibble against s by comparing
+// |x| with the midpoints times s (exact in fp32: s has 8 significant bits).
+__device__ __forceinline__ void fp4_encode_compare(const float (&a)[16], float amax, unsigned long long& packed,
+                                                   uint16_t& sb) {
+  sb = bf16_from_f64(__ddiv_rn((double)amax, 6.0));
+  const float s = bf16_to_f32(sb);
+  packed = 0;
+  if (s > 0.f) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) packed |= (unsigned long long)e2m1_encode(a[i], s) << (4 * i);
+  }
+}
+
+// x rounded to 16 mantissa bits (halfway away from zero).
+__device__ __forceinline__ float snap16(float x) { return __uint_as_float((__float_as_uint(x) + 64u) & ~127u); }
+
+// The same group from bf16 inputs, without fp64 and without per-element
+// compares.  x and s both carry 8 significant bits, so x / s either equals an
+// E2M1 midpoint exactly or lies at least 2^-12.3 (relative) away from every
+// midpoint; likewise absmax / 6 lies at least 2^-10.6 away from every bf16
+// midpoint (it is never one).  Hence
+//   s = bf16_RNE(fl32(absmax * fl32(1/6)))        (error 2^-23)
+//   q = fl32(x * rcp(s)), rounded to 16 bits      (error 2^-22 before rounding;
+//                                                  an exact midpoint comes back
+//                                                  exactly, nothing else crosses one)
+// take the exact-arithmetic decisions, and the hardware E2M1 conversion (ties to
+// even, saturating at 6, sign of zero kept) forms each pair of nibbles.  A group
+// whose absmax lies outside [2^-100, 2^100], where rcp(s) could leave the normal
+// range, takes the compare path.
+__device__ __forceinline__ void fp4_encode_bf16(const float (&a)[16], unsigned long long& packed, uint16_t& sb) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(a[i]));
+  if (!(amax >= 0x1p-100f && amax <= 0x1p100f)) {
+    fp4_encode_compare(a, amax, packed, sb);
+    return;
+  }
+  const uint32_t u = __float_as_uint(amax * (1.0f / 6.0f));
+  const uint32_t sbits = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  sb = (uint16_t)sbits;
+  const float r = __builtin_amdgcn_rcpf(__uint_as_float(sbits << 16));
+  uint32_t w[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float* e = a + 8 * h;
+    uint32_t word = 0u;
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, snap16(e[0] * r), snap16(e[1] * r), 1.0f, 0);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, snap16(e[2] * r), snap16(e[3] * r), 1.0f, 1);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, snap16(e[4] * r), snap16(e[5] * r), 1.0f, 2);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, snap16(e[6] * r), snap16(e[7] * r), 1.0f, 3);
+    w[h] = word;
+  }
+  packed = (unsigned long long)w[0] | ((unsigned long long)w[1] << 32);
+}
+
+__device__ __forceinline__ void fp4_encode16(const float (&a)[16], unsigned long long& packed, uint16_t& sb,
+                                             const uint16_t*) {
+  fp4_encode_bf16(a, packed, sb);
+}
+__device__ __forceinline__ void fp4_encode16(const float (&a)[16], unsigned long long& packed, uint16_t& sb,
+                                             const float*) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(a[i]));
+  fp4_encode_compare(a, amax, packed, sb);
+}
+
+// Encode one group (values already loaded) and store its codes (element 2i in
+// the low nibble of byte i) and scale at cache row dr, group g.  `tag` only
+// selects the input type's encoder.
+template <typename InT>
+__device__ __forceinline__ void fp4_store_at(const float (&a)[16], const InT* tag, size_t dr, int g, int d,
+                                             uint8_t* __restrict__ codes, uint16_t* __restrict__ scales) {
+  unsigned long long packed;
+  uint16_t sb;
+  fp4_encode16(a, packed, sb, tag);
+  *reinterpret_cast<unsigned long long*>(codes + dr * (d / 2) + g * 8) = packed;
+  scales[dr * (d / 16) + g] = sb;
+}
+template <typename InT>
+__device__ __forceinline__ void fp4_store_group(const float (&a)[16], const InT* tag, size_t r, int g, int d,
+                                                uint8_t* __restrict__ codes, uint16_t* __restrict__ scales, int n,
+                                                int cap, int start) {
+  fp4_store_at(a, tag, dst_row(r, n, cap, start), g, d, codes, scales);
+}
+
+// Group gid (= row * (d / 16) + group) of a row-major input with row stride
+// `stride` elements.
 template <typename InT>
 __device__ __forceinline__ void fp4_group(const InT* __restrict__ x, size_t stride, int d,
                                           uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
@@ -37,24 +167,11 @@ __device__ __forceinline__ void fp4_group(const InT* __restrict__ x, size_t stri
   if (gid >= rows * groups) return;
   const int g = (int)(gid % groups);
   const size_t r = gid / groups;
-  const InT* src = x + r * stride + g * 16;
+  Raw16<InT> raw;
+  raw.load(x + r * stride + g * 16);
   float a[16];
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    a[i] = load_as_f32(src, i);
-    amax = fmaxf(amax, fabsf(a[i]));
-  }
-  const uint16_t sb = bf16_from_f64(__ddiv_rn((double)amax, 6.0));
-  const float s = bf16_to_f32(sb);
-  unsigned long long packed = 0;
-  if (s > 0.f) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) packed |= (unsigned long long)e2m1_encode(a[i], s) << (4 * i);
-  }
-  const size_t dr = dst_row(r, n, cap, start);
-  *reinterpret_cast<unsigned long long*>(codes + dr * (d / 2) + g * 8) = packed;
-  scales[dr * groups + g] = sb;
+  raw.unpack(a);
+  fp4_store_group(a, x, r, g, d, codes, scales, n, cap, start);
 }
 
 // K (blockIdx.y = 0) and V (blockIdx.y = 1) of an FP4 cache in one launch.
@@ -197,33 +314,51 @@ __global__ void __launch_bounds__(256) kivi_append_kernel(const InT* __restrict_
 // ---------------------------------------------------------------- QJL sign sketch (MFMA)
 
 // Split x into bf16 parts whose sum is exactly x (1 part for bf16 input, 3 for fp32).
+// A lane's share of a 16-token key tile as the A operand of
+// v_mfma_f32_16x16x32_bf16: token (lane & 15), channels ks * 32 + 8 * (lane >> 4)
+// + j (j < 8) of the four 32-wide k-steps ks.  A bf16 input is the operand as it
+// is; an fp32 input is the exact sum of three bf16 slices (truncations), each
+// its own product.  The fragment stays in registers for the fp64 recheck.
 template <typename InT>
-struct Bf16Parts;
+struct KeyFrag;
 template <>
-struct Bf16Parts<uint16_t> {
-  static constexpr int N = 1;
-  __device__ static void get(const uint16_t* p, uint16_t out[N][8]) {
-    uint4 raw = *reinterpret_cast<const uint4*>(p);
-    const uint16_t* h = reinterpret_cast<const uint16_t*>(&raw);
+struct KeyFrag<uint16_t> {
+  static constexpr int NP = 1;
+  uint4 r[4];
+  __device__ __forceinline__ void load(const uint16_t* row, int kq) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) out[0][i] = h[i];
+    for (int ks = 0; ks < 4; ++ks) r[ks] = *reinterpret_cast<const uint4*>(row + ks * 32 + kq * 8);
   }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) r[ks] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  __device__ __forceinline__ float value(int ks, int j) const {
+    const uint32_t w = j < 2 ? r[ks].x : j < 4 ? r[ks].y : j < 6 ? r[ks].z : r[ks].w;
+    return __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  }
+  __device__ __forceinline__ void parts(int ks, bf16x8 (&p)[NP]) const { p[0] = __builtin_bit_cast(bf16x8, r[ks]); }
 };
 template <>
-struct Bf16Parts<float> {
-  static constexpr int N = 3;
-  __device__ static void get(const float* p, uint16_t out[N][8]) {
+struct KeyFrag<float> {
+  static constexpr int NP = 3;
+  float4 r[4][2];
+  __device__ __forceinline__ void load(const float* row, int kq) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float v = p[i];
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        uint32_t hi = __float_as_uint(v) & 0xFFFF0000u;  // truncation: exact top part
-        out[k][i] = (uint16_t)(hi >> 16);
-        v = v - __uint_as_float(hi);                      // exact remainder
-      }
-    }
+      for (int h = 0; h < 2; ++h) r[ks][h] = *reinterpret_cast<const float4*>(row + ks * 32 + kq * 8 + 4 * h);
   }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) r[ks][0] = r[ks][1] = float4{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ __forceinline__ float value(int ks, int j) const {
+    const float4 q = r[ks][j >> 2];
+    const int c = j & 3;
+    return c == 0 ? q.x : c == 1 ? q.y : c == 2 ? q.z : q.w;
+  }
+  __device__ __forceinline__ void parts(int ks, bf16x8 (&p)[NP]) const;
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint16_t (&h)[8]) {
@@ -231,6 +366,22 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint16_t (&h)[8]) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) r[i] = __builtin_bit_cast(__bf16, h[i]);
   return r;
+}
+
+__device__ __forceinline__ void KeyFrag<float>::parts(int ks, bf16x8 (&p)[NP]) const {
+  uint16_t h[NP][8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float v = value(ks, j);
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      const uint32_t hi = __float_as_uint(v) & 0xFFFF0000u;  // truncation: exact top slice
+      h[k][j] = (uint16_t)(hi >> 16);
+      v = v - __uint_as_float(hi);                          // exact remainder
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NP; ++k) p[k] = as_bf16x8(h[k]);
 }
 
 constexpr int kSPad = 136;  // LDS row pitch (elements) of the staged 128 x 128 bf16 matrix
@@ -281,17 +432,120 @@ __device__ __forceinline__ void stage_bf16_matrix(const float* __restrict__ m, u
   }
 }
 
-// sketch bit i of a token = [(S k)_i >= 0], plus the token's fp16 norm.
-// A wave takes 16 tokens: A = K rows (bf16, or exact bf16 parts of fp32),
-// B = S^T from LDS, fp32 accumulation on v_mfma_f32_16x16x32_bf16.  Where
-// |y| is within a conservative bound of the fp32 accumulation error
-// (2^-14 * ||S_i|| * ||k||), the sign is recomputed exactly in fp64, so the
-// stored bits equal the exact-arithmetic signs.
+// Keys of one wave's 16 tokens [base, base + 16): sketch bit i = [(S k)_i >= 0]
+// and the token's fp16 norm.  C = K_tile S^T on v_mfma_f32_16x16x32_bf16 (S^T
+// read from LDS, fp32 accumulation of exact products).  Where |y| is within a
+// conservative bound of the fp32 accumulation error (2^-14 ||S_i|| ||k||; 2^-12
+// for three slices), about one element in 2^11, the sign is recomputed in fp64
+// from the registers: each of the token's four lanes sums its 32 products and
+// the four partial sums are added.
 template <typename InT>
-__device__ __forceinline__ void qjl_keys(const InT* __restrict__ x, const float* __restrict__ proj,
-                                         uint8_t* __restrict__ sketch, uint16_t* __restrict__ knorm,
-                                         size_t rows, int n, int cap, int start, uint16_t* S_lds,
-                                         float* srow_norm, int key_blocks) {
+__device__ __forceinline__ void qjl_key_tile(const KeyFrag<InT>& fr, size_t base, size_t rows,
+                                             const uint16_t* S_lds, const float (&sbound)[8], size_t my_dst,
+                                             uint8_t* __restrict__ sketch, uint16_t* __restrict__ knorm) {
+  constexpr int NP = KeyFrag<InT>::NP;
+  const int lane = threadIdx.x & 63, col = lane & 15, kq = lane >> 4;
+  // token norms: the lane's 32 squares, then the four k-quarters held by lanes
+  // col, col+16, col+32, col+48
+  double ss = 0.0;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const double v = (double)fr.value(ks, j);
+      ss = fma(v, v, ss);
+    }
+  ss += __shfl_xor(ss, 16);
+  ss += __shfl_xor(ss, 32);
+  const double nrm = sqrt(ss);  // lane holds the norm of token `col`
+  // Lane t < 16 assembles the sketch of token t: its bits sit in rows t & 3 of
+  // the C tiles, lanes 16 (t >> 2) .. 16 (t >> 2) + 15 of each ballot.
+  uint32_t words[4] = {0u, 0u, 0u, 0u};
+  const int my_q = (lane >> 2) & 3, my_i = lane & 3;
+  // S rows in two halves of 64 (n-tiles 4 hf .. 4 hf + 3), sketch words 2 hf, 2 hf + 1
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    f32x4 acc[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 pa[NP];
+      fr.parts(ks, pa);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int srow = (4 * hf + nt) * 16 + col;
+        const uint4 braw = *reinterpret_cast<const uint4*>(&S_lds[srow * kSPad + ks * 32 + kq * 8]);
+        const bf16x8 b = __builtin_bit_cast(bf16x8, braw);
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[p], b, acc[nt], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      unsigned long long bal[4];
+      const int tok = kq * 4 + i;  // C-operand rows held by this lane
+      const float tn = (float)__shfl(nrm, tok);
+      const bool tvalid = base + tok < rows;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const float y = acc[nt][i];
+        bool bit = y >= 0.f;
+        unsigned long long close = __ballot(fabsf(y) <= sbound[4 * hf + nt] * tn && tvalid);
+        while (close) {
+          const int src = __builtin_ctzll(close);
+          close &= close - 1;
+          const int ct = (src >> 4) * 4 + i;  // token of that element
+          const int sr = (4 * hf + nt) * 16 + (src & 15);  // its row of S
+          double e = 0.0;
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const uint4 sw = *reinterpret_cast<const uint4*>(&S_lds[sr * kSPad + ks * 32 + kq * 8]);
+            const uint32_t w[4] = {sw.x, sw.y, sw.z, sw.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float sv = __uint_as_float((j & 1) ? (w[j >> 1] & 0xFFFF0000u) : (w[j >> 1] << 16));
+              e = fma((double)sv, (double)fr.value(ks, j), e);
+            }
+          }
+          const double tot = (__shfl(e, ct) + __shfl(e, ct + 16)) + (__shfl(e, ct + 32) + __shfl(e, ct + 48));
+          if (lane == src) bit = tot >= 0.0;
+        }
+        bal[nt] = __ballot(bit);
+      }
+      if (my_i == i) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint32_t lo = (uint32_t)(bal[2 * j] >> (16 * my_q)) & 0xFFFFu;
+          const uint32_t hi = (uint32_t)(bal[2 * j + 1] >> (16 * my_q)) & 0xFFFFu;
+          words[2 * hf + j] = lo | (hi << 16);
+        }
+      }
+    }
+  }
+  if (lane < 16 && base + lane < rows) {
+    *reinterpret_cast<uint4*>(sketch + my_dst * 16) = make_uint4(words[0], words[1], words[2], words[3]);
+    knorm[my_dst] = f16_from_f64_nonneg(nrm);
+  }
+}
+
+// QJL keys and FP4 values in one persistent launch.  Each workgroup stages S
+// once (bf16 in LDS, with its row norms), then takes 64-token tiles: each wave
+// does the values and the keys of 16 tokens, both loaded at the start.
+#ifndef KVQ_QJL_APPEND_WAVES_PER_EU
+#define KVQ_QJL_APPEND_WAVES_PER_EU 3
+#endif
+
+template <typename InT>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVQ_QJL_APPEND_WAVES_PER_EU)))
+qjl_append_kernel(const InT* __restrict__ k, const InT* __restrict__ v,
+                                                         const float* __restrict__ proj,
+                                                         uint8_t* __restrict__ sketch, uint16_t* __restrict__ knorm,
+                                                         uint8_t* __restrict__ vc, uint16_t* __restrict__ vs,
+                                                         size_t rows, int n, int cap, int start) {
+  __shared__ __align__(16) uint16_t S_lds[128 * kSPad];
+  __shared__ float srow_norm[128];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   stage_bf16_matrix(proj, S_lds);  // bf16-valued
   __syncthreads();
@@ -299,125 +553,72 @@ __device__ __forceinline__ void qjl_keys(const InT* __restrict__ x, const float*
     // row norms of S from the staged copy: two threads per row, 64 entries each
     const int r = tid >> 1, h = tid & 1;
     float acc = 0.f;
-    for (int j = 0; j < 64; ++j) {
-      const float sv = bf16_to_f32(S_lds[r * kSPad + 64 * h + j]);
-      acc = fmaf(sv, sv, acc);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint4 w = *reinterpret_cast<const uint4*>(&S_lds[r * kSPad + 64 * h + 8 * c]);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float lo = __uint_as_float(ww[j] << 16), hi = __uint_as_float(ww[j] & 0xFFFF0000u);
+        acc = fmaf(lo, lo, acc);
+        acc = fmaf(hi, hi, acc);
+      }
     }
     acc += __shfl_xor(acc, 1);
     if (h == 0) srow_norm[r] = sqrtf(acc) * 1.0001f;
   }
   __syncthreads();
-  constexpr int NP = Bf16Parts<InT>::N;
-  const int col = lane & 15, kq = lane >> 4;
-  for (size_t base = ((size_t)blockIdx.x * 4 + wave) * 16; base < rows; base += (size_t)key_blocks * 64) {
-    const size_t my_row = base + col;  // A-operand token of this lane
-    const bool valid = my_row < rows;
-    f32x4 acc[8];
+  // this lane's sign bounds for S rows nt * 16 + (lane & 15), before the token norm
+  float sbound[8];
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    double ss = 0.0;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      uint16_t part[NP][8];
-      if (valid) {
-        Bf16Parts<InT>::get(x + my_row * 128 + ks * 32 + kq * 8, part);
-      } else {
-#pragma unroll
-        for (int p = 0; p < NP; ++p)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) part[p][i] = 0;
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        double v = 0.0;
-#pragma unroll
-        for (int p = 0; p < NP; ++p) v += (double)bf16_to_f32(part[p][i]);
-        ss = fma(v, v, ss);
-      }
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const uint16_t* srow = &S_lds[(nt * 16 + col) * kSPad + ks * 32 + kq * 8];
-        uint4 braw = *reinterpret_cast<const uint4*>(srow);
-        uint16_t bh[8];
-        *reinterpret_cast<uint4*>(bh) = braw;
-        bf16x8 b = as_bf16x8(bh);
-#pragma unroll
-        for (int p = 0; p < NP; ++p)
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(part[p]), b, acc[nt], 0, 0, 0);
-      }
-    }
-    // token norms: sum the four k-quarters held by lanes col, col+16, col+32, col+48
-    ss += __shfl_xor(ss, 16);
-    ss += __shfl_xor(ss, 32);
-    const double nrm = sqrt(ss);  // lane holds the norm of token `col`
-    unsigned long long ballots[8][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tok = kq * 4 + i;  // C-operand rows held by this lane
-      const double tn = __shfl(nrm, tok);
-      const size_t trow = base + tok;
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const int srow_i = nt * 16 + col;
-        const float y = acc[nt][i];
-        bool bit = y >= 0.f;
-        const float bound = (NP == 1 ? 0x1p-14f : 0x1p-12f) * srow_norm[srow_i] * (float)tn;
-        // Signs too close to call in fp32 (about one element in 2^11) are
-        // recomputed in fp64 by the whole wave: every lane takes two of the 128
-        // terms and a butterfly sums them.
-        unsigned long long close = __ballot(fabsf(y) <= bound && trow < rows);
-        while (close) {
-          const int src = __builtin_ctzll(close);
-          close &= close - 1;
-          const int s_row = nt * 16 + (src & 15);
-          const size_t x_row = base + (src >> 4) * 4 + i;
-          double e = 0.0;
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int j = 2 * lane + h;
-            e = fma((double)bf16_to_f32(S_lds[s_row * kSPad + j]), (double)load_as_f32(x + x_row * 128, j), e);
-          }
-#pragma unroll
-          for (int off = 32; off > 0; off >>= 1) e += __shfl_xor(e, off);
-          if (lane == src) bit = e >= 0.0;
+  for (int nt = 0; nt < 8; ++nt)
+    sbound[nt] = (KeyFrag<InT>::NP == 1 ? 0x1p-14f : 0x1p-12f) * srow_norm[nt * 16 + (lane & 15)];
+  const size_t tiles = (rows + 63) / 64;
+  const size_t vgroups = rows * 8;
+  for (size_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+    const size_t base = t * 64 + (size_t)wave * 16;
+    // cache row of tile row j < 16: one division per tile, then at most one wrap
+    // into the next sequence-head when n >= 16
+    const size_t bh0 = base / (size_t)n;
+    const uint32_t p0 = (uint32_t)(base - bh0 * (size_t)n);
+    auto tile_dst = [&](uint32_t j) -> size_t {
+      uint32_t p = p0 + j;
+      size_t bh = bh0;
+      if (n >= 16) {
+        if (p >= (uint32_t)n) {
+          p -= (uint32_t)n;
+          ++bh;
         }
-        ballots[nt][i] = __ballot(bit);
+      } else {
+        bh += p / (uint32_t)n;
+        p %= (uint32_t)n;
       }
-    }
-    if (lane < 16 && base + lane < rows) {
-      const int q = lane >> 2, i = lane & 3;
-      uint32_t w[4];
+      return bh * (size_t)cap + (size_t)start + p;
+    };
+    // values first: the 128 groups of rows [base, base + 16), two per lane
+    // (group g of the flat row-major input starts at v + 16 g), then the key
+    // fragment; the values are encoded and stored while the keys are in flight.
+    Raw16<InT> va[2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint32_t lo = (uint32_t)(ballots[2 * j][i] >> (16 * q)) & 0xFFFFu;
-        uint32_t hi = (uint32_t)(ballots[2 * j + 1][i] >> (16 * q)) & 0xFFFFu;
-        w[j] = lo | (hi << 16);
-      }
-      const size_t dr = dst_row(base + lane, n, cap, start);
-      *reinterpret_cast<uint4*>(sketch + dr * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-      knorm[dr] = f16_from_f64_nonneg(nrm);
+    for (int h = 0; h < 2; ++h) {
+      const size_t g = base * 8 + lane + 64 * h;
+      if (g < vgroups) va[h].load(v + g * 16);
+      else va[h].zero();
     }
-  }
-}
-
-// QJL keys (blockIdx.y = 0: the first key_blocks workgroups, persistent over
-// 64-token tiles, so that staging S is paid once per many tiles) and FP4
-// values (blockIdx.y = 1) in one launch.
-template <typename InT>
-__global__ void __launch_bounds__(256) qjl_append_kernel(const InT* __restrict__ k, const InT* __restrict__ v,
-                                                         const float* __restrict__ proj, uint8_t* sketch,
-                                                         uint16_t* knorm, uint8_t* vc, uint16_t* vs, size_t rows,
-                                                         int n, int cap, int start, int key_blocks) {
-  __shared__ __align__(16) uint16_t S_lds[128 * kSPad];
-  __shared__ float srow_norm[128];
-  if (blockIdx.y == 0) {
-    if ((int)blockIdx.x >= key_blocks) return;
-    qjl_keys(k, proj, sketch, knorm, rows, n, cap, start, S_lds, srow_norm, key_blocks);
-  } else {
-    const size_t groups = rows * 8;
-    for (size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x; gid < groups;
-         gid += (size_t)gridDim.x * blockDim.x)
-      fp4_group(v, 128, 128, vc, vs, rows, n, cap, start, gid);
+    const size_t my_row = base + (lane & 15);
+    KeyFrag<InT> fr;
+    if (my_row < rows) fr.load(k + my_row * 128, lane >> 4);
+    else fr.zero();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const size_t g = base * 8 + lane + 64 * h;
+      if (g < vgroups) {
+        float a[16];
+        va[h].unpack(a);
+        fp4_store_at(a, v, tile_dst((lane >> 3) + 8 * h), lane & 7, 128, vc, vs);
+      }
+    }
+    if (base < rows) qjl_key_tile(fr, base, rows, S_lds, sbound, tile_dst(lane & 15), sketch, knorm);
   }
 }
 
@@ -593,6 +794,11 @@ __global__ void __launch_bounds__(256) turbo_append_kernel(const InT* __restrict
 
 int blocks_for(size_t threads) { return (int)((threads + 255) / 256); }
 
+// Workgroups of the QJL append: one resident round (each stages S once).
+#ifndef KVQ_QJL_APPEND_BLOCKS
+#define KVQ_QJL_APPEND_BLOCKS (256 * KVQ_QJL_APPEND_WAVES_PER_EU)
+#endif
+
 int persistent_blocks(size_t rows) {
   size_t tiles = (rows + 63) / 64;
   return (int)std::min<size_t>(tiles, 2048);
@@ -627,12 +833,10 @@ int append_typed(const kv_cache* c, const InT* k, const InT* v, int start, int n
       break;
     }
     case KV_FMT_QJL1_FP4V: {
-      // keys: a few long-lived workgroups per CU; values: enough to fill the chip
-      const int key_blocks = (int)std::min<size_t>((rows + 63) / 64, 512);
-      const int blocks = std::max(key_blocks, std::min(blocks_for(rows * (d / 16)), 2048));
-      qjl_append_kernel<InT><<<dim3(blocks, 2), 256, 0, st>>>(
+      const int blocks = (int)std::min<size_t>((rows + 63) / 64, KVQ_QJL_APPEND_BLOCKS);
+      qjl_append_kernel<InT><<<blocks, 256, 0, st>>>(
           k, v, c->proj, static_cast<uint8_t*>(c->buf[KV_BUF_K_SKETCH]), static_cast<uint16_t*>(c->buf[KV_BUF_K_NORM]),
-          vc, vs, rows, n, cap, start, key_blocks);
+          vc, vs, rows, n, cap, start);
       break;
     }
     case KV_FMT_TURBO:

@@ -79,6 +79,74 @@ def test_decode_matches_oracle(fmt):
     assert err.max() <= RTOL
 
 
+E2M1_MIDPOINTS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+
+
+def _bf16_step(x, up):
+    """The bf16 neighbour of bf16 x (x != 0) one unit further from (up) or nearer to zero."""
+    u = np.array([x], np.float32).view(np.uint32)
+    u = u + np.uint32(0x10000) if up else u - np.uint32(0x10000)
+    return float(u.view(np.float32)[0])
+
+
+def _fp4_edge_groups(rng, n_groups):
+    """bf16-exact 16-value groups at the FP4 encoder's decision edges.
+
+    Each group's absmax A fixes s = bf16(A / 6); the other values are exact
+    midpoints t * s between E2M1 neighbours (where bf16 holds them), their bf16
+    neighbours, zeros and signed zeros.  Exponents span ordinary magnitudes,
+    both ends of [2^-100, 2^100] and beyond them on either side.
+    """
+    from oracle.numerics import round_bf16
+    exps = [(-6, 7)] * 6 + [(-112, -104), (104, 112)]
+    out = np.zeros((n_groups, 16))
+    for gi in range(n_groups):
+        kind = gi % 10
+        if kind == 9:
+            continue  # an all-zero group
+        if kind == 8:
+            a = float(2.0 ** rng.choice([-100, 100]))
+        else:
+            lo, hi = exps[kind]
+            a = float(round_bf16(rng.uniform(1.0, 2.0) * 2.0 ** int(rng.integers(lo, hi))))
+        s = float(round_bf16(a / 6.0))
+        cands = [0.0]
+        for t in E2M1_MIDPOINTS:
+            x = t * s
+            if float(round_bf16(x)) == x:
+                cands += [x, _bf16_step(x, True), _bf16_step(x, False)]
+        vals = rng.choice(np.array(cands), 15) * rng.choice([-1.0, 1.0], 15)
+        g = np.concatenate([[a * rng.choice([-1.0, 1.0])], vals])
+        out[gi] = g[rng.permutation(16)]
+    return out
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "qjl1", "latent"])
+def test_fp4_encoder_decision_edges(fmt):
+    """FP4 codes and scales at exact midpoints, their neighbours, saturation,
+    signed zeros and extreme exponents equal the oracle's, byte for byte."""
+    cfg = SMALL[fmt].scaled(batch=1, context=96)
+    print(f"[fp4 edges] {fmt}", flush=True)
+    rng = np.random.default_rng(11)
+    T = cfg.context
+    if fmt == "latent":
+        K = _fp4_edge_groups(rng, T * (cfg.head_dim + cfg.rope_dim) // 16).reshape(1, T, -1)
+        V = None
+    else:
+        V = _fp4_edge_groups(rng, cfg.hkv * T * cfg.head_dim // 16).reshape(1, cfg.hkv, T, cfg.head_dim)
+        if fmt == "fp4":
+            K = _fp4_edge_groups(rng, cfg.hkv * T * cfg.head_dim // 16).reshape(V.shape)
+        else:
+            K = rng.standard_normal(V.shape)
+    dev = lambda a: torch.from_numpy(a).to(torch.float32).to(torch.bfloat16).cuda() if a is not None else None
+    Kd, Vd = dev(K), dev(V)
+    cache = new_cache(cfg)
+    cache.append(Kd, Vd, 0)
+    torch.cuda.synchronize()
+    want = oracle_encode(cfg, host64(Kd), host64(Vd), oracle_constants(cfg))
+    assert_bytes_equal(gpu_buffers(cache), want, f"{fmt} decision edges")
+
+
 @pytest.mark.parametrize("fmt", ["fp4", "turbo", "qjl1", "latent"])
 def test_token_by_token_append_equals_bulk(fmt):
     """A decode loop appends one token per step; the bytes must equal a bulk append."""
