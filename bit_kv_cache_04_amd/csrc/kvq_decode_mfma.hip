@@ -290,14 +290,16 @@ struct WaveState {
 // have returned) refill the stage with tile `t_next` (the sentinel `capacity`
 // when there is none, so that the refill is unconditional and the compiler's
 // wait counts stay exact), then compute.
-template <int G, class KP>
+template <int G, int NS, class KP>
 __device__ __forceinline__ void tile_step(WaveState<KP>& w, uint8_t* st, int lane, int t0, int t_end, int t_next,
                                           const MfmaDecodeArgs& a, const typename KP::R& kr, const VRsrc& vr) {
   const int q4 = lane >> 4, c = lane & 15;
-  // This stage's tile has landed once at most the other stage's refill is
-  // outstanding.  Waited for explicitly: the compiler's own wait for loads into
-  // LDS is not placed reliably across the loop back-edge.
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (KP::kDma + 4));  // vmcnt(key loads + 4 value loads)
+  // This stage's tile has landed once at most the other NS - 1 stages' refills
+  // are outstanding.  Waited for explicitly: the compiler's own wait for loads
+  // into LDS is not placed reliably across the loop back-edge.
+  constexpr int kOther = (NS - 1) * (KP::kDma + 4);  // key loads + 4 value loads per stage
+  static_assert(kOther < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (kOther & 15) | ((kOther >> 4) << 14));
   typename KP::Frag kf;
   KP::read(kf, st, q4, c);
   // Lane byte offsets into the stage; opaque to the optimiser so that every read
@@ -387,23 +389,44 @@ __device__ __forceinline__ void tile_step(WaveState<KP>& w, uint8_t* st, int lan
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// LDS arrays that exist only in the kernels that use them (a function-scope
+// __shared__ array is allocated only where its function is instantiated), so
+// that the two-stage kernels use exactly two stages of LDS.
+template <int N>
+struct LdsBytes {
+  __device__ static uint8_t* get() {
+    __shared__ __attribute__((aligned(16))) uint8_t buf[N];
+    return buf;
+  }
+};
+template <>
+struct LdsBytes<0> {
+  __device__ static uint8_t* get() { return nullptr; }
+};
+
 #ifndef KVQ_MFMA_WAVES_PER_EU
 #define KVQ_MFMA_WAVES_PER_EU 3  // waves per SIMD the register budget is cut for
+#endif
+#ifndef KVQ_MFMA_STAGES
+#define KVQ_MFMA_STAGES 2  // LDS ring depth per wave (tiles in flight + 1)
 #endif
 
 template <int G, class KP>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(KVQ_MFMA_WAVES_PER_EU, KVQ_MFMA_WAVES_PER_EU))) decode_mfma_kernel(MfmaDecodeArgs a) {
   constexpr int kStage = Stage<KP>::kBytes;
-  // two LDS stages per wave, as separate arrays so that the compiler can tell
-  // which stage a direct-to-LDS load writes and wait only for that one
+  constexpr int NS = KVQ_MFMA_STAGES;
+  static_assert(NS == 2 || NS == 3, "ring depth");
+  // LDS stages per wave, as separate arrays so that the compiler can tell which
+  // stage a direct-to-LDS load writes and wait only for that one
   __shared__ __attribute__((aligned(16))) uint8_t stA[4][kStage];
   __shared__ __attribute__((aligned(16))) uint8_t stB[4][kStage];
+  uint8_t* stC = LdsBytes<NS == 3 ? 4 * kStage : 0>::get();  // third stage, NS == 3 only
   // the waves' running max / sum are combined through stage-B memory, their
   // outputs through stage-A memory when they fit there, else through a buffer
   // of their own; both stages are idle by then
   constexpr bool kAliasA = sizeof(float) * 4 * G * 129 <= sizeof(stA);
-  __shared__ float sm_own[kAliasA ? 1 : 4 * G * 129];
+  uint8_t* sm_own = LdsBytes<kAliasA ? 0 : sizeof(float) * 4 * G * 129>::get();
   float (*sm_o)[G][129] = reinterpret_cast<float (*)[G][129]>(kAliasA ? (void*)&stA[0][0] : (void*)sm_own);
   float (*sm_m)[16] = reinterpret_cast<float (*)[16]>(&stB[0][0]);
   float (*sm_l)[16] = reinterpret_cast<float (*)[16]>(&stB[0][0] + 4 * 16 * sizeof(float));
@@ -437,10 +460,23 @@ __attribute__((amdgpu_waves_per_eu(KVQ_MFMA_WAVES_PER_EU, KVQ_MFMA_WAVES_PER_EU)
   int t0 = t_begin + wave * 32;
   issue_tile<KP>(sa, lane, tile_or_none(t0), kr, vr);
   issue_tile<KP>(sb, lane, tile_or_none(t0 + 128), kr, vr);
-  for (; t0 < t_end; t0 += 256) {
-    // the second tile of a pair may lie past t_end: all its tokens are masked
-    tile_step<G, KP>(w, sa, lane, t0, t_end, tile_or_none(t0 + 256), a, kr, vr);
-    tile_step<G, KP>(w, sb, lane, t0 + 128, t_end, tile_or_none(t0 + 384), a, kr, vr);
+  if constexpr (NS == 2) {
+    for (; t0 < t_end; t0 += 256) {
+      // the second tile of a pair may lie past t_end: all its tokens are masked
+      tile_step<G, NS, KP>(w, sa, lane, t0, t_end, tile_or_none(t0 + 256), a, kr, vr);
+      tile_step<G, NS, KP>(w, sb, lane, t0 + 128, t_end, tile_or_none(t0 + 384), a, kr, vr);
+    }
+  } else {
+    uint8_t* sc = stC + wave * kStage;
+    issue_tile<KP>(sc, lane, tile_or_none(t0 + 256), kr, vr);
+    while (t0 < t_end) {
+      tile_step<G, NS, KP>(w, sa, lane, t0, t_end, tile_or_none(t0 + 384), a, kr, vr);
+      if (t0 + 128 >= t_end) break;
+      tile_step<G, NS, KP>(w, sb, lane, t0 + 128, t_end, tile_or_none(t0 + 512), a, kr, vr);
+      if (t0 + 256 >= t_end) break;
+      tile_step<G, NS, KP>(w, sc, lane, t0 + 256, t_end, tile_or_none(t0 + 640), a, kr, vr);
+      t0 += 384;
+    }
   }
   // drain the refills still in flight before the waves' LDS is reused or the wave exits
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
