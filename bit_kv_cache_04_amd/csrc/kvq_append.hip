@@ -792,12 +792,155 @@ __global__ void __launch_bounds__(256) turbo_append_kernel(const InT* __restrict
                            R_lds, S_lds, scratch, idx_lds);
 }
 
+// Small appends (a few tiles, e.g. one token per sequence): the same
+// arithmetic spread for latency rather than staged for throughput.  One
+// workgroup of 8 waves per 16-token tile (blockIdx.y = 0 keys, 1 values); wave
+// w computes output rows 16 w .. 16 w + 15 of R x (and of S r), reading just
+// those rows of R (S) from global memory.  Every product element is summed in
+// the same order as in turbo_body, so the codes and signs are the same.
+template <typename InT>
+__global__ void __launch_bounds__(512) turbo_append_small_kernel(
+    const InT* __restrict__ k, const InT* __restrict__ v, const float* __restrict__ rot,
+    const float* __restrict__ proj, const float* __restrict__ levels, const float* __restrict__ thresh,
+    uint8_t* __restrict__ kc, uint8_t* __restrict__ sketch, uint16_t* __restrict__ knorm,
+    uint16_t* __restrict__ krnorm, uint8_t* __restrict__ vc, uint16_t* __restrict__ vnorm, size_t rows, int n,
+    int cap, int start) {
+  __shared__ double xs[16 * 129];  // x tile as double
+  __shared__ double rs[16 * 129];  // keys: the residual
+  __shared__ __align__(16) uint16_t rows_lds[8][2][16 * kSPad];  // per wave: its rows of R, then of S (bf16)
+  __shared__ double g2part[8][16];  // keys: per-wave partial gamma^2 per token
+  const bool keys = blockIdx.y == 0;
+  const InT* x = keys ? k : v;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 15, kq = lane >> 4;
+  const size_t base = (size_t)blockIdx.x * 16;
+  // this wave's 16 rows of R (and S, keys only): 8 KB contiguous each, read
+  // with full-line loads (lane l, load j: float4 64 j + l of the rows) and kept
+  // in LDS as bf16 (both matrices are bf16-valued)
+  float4 mr[2][8];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const float4* src = reinterpret_cast<const float4*>((m == 0 ? rot : proj) + 16 * w * 128);
+    if (m == 0 || keys) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mr[m][j] = src[64 * j + lane];
+    }
+  }
+  // x tile: thread t takes token t / 32, channels 4 (t % 32) .. + 3, zero past the last row
+  {
+    const int tk = tid >> 5, c0 = 4 * (tid & 31);
+    const bool ok = base + tk < rows;
+    const float4 xv = load4_as_f32(x + (base + (ok ? tk : 0)) * 128 + c0);
+    xs[tk * 129 + c0] = ok ? (double)xv.x : 0.0;
+    xs[tk * 129 + c0 + 1] = ok ? (double)xv.y : 0.0;
+    xs[tk * 129 + c0 + 2] = ok ? (double)xv.z : 0.0;
+    xs[tk * 129 + c0 + 3] = ok ? (double)xv.w : 0.0;
+  }
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    if (m == 0 || keys) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int f = 64 * j + lane, r = f >> 5, c4 = 4 * (f & 31);
+        uint2 h;
+        h.x = (__float_as_uint(mr[m][j].x) >> 16) | (__float_as_uint(mr[m][j].y) & 0xFFFF0000u);
+        h.y = (__float_as_uint(mr[m][j].z) >> 16) | (__float_as_uint(mr[m][j].w) & 0xFFFF0000u);
+        *reinterpret_cast<uint2*>(&rows_lds[w][m][r * kSPad + c4]) = h;
+      }
+    }
+  }
+  __syncthreads();
+  // norms (every wave, same order as turbo_body): lane `col` sums its token over
+  // the quarter kq, then the quarters are added
+  double ss = 0.0;
+  for (int c = kq * 32; c < kq * 32 + 32; ++c) ss = fma(xs[col * 129 + c], xs[col * 129 + c], ss);
+  ss += __shfl_xor(ss, 16);
+  ss += __shfl_xor(ss, 32);
+  const double nrm = sqrt(ss);
+  f64x4 acc = f64x4{0.0, 0.0, 0.0, 0.0};
+  const uint16_t* Rw = &rows_lds[w][0][col * kSPad + kq];
+#pragma unroll
+  for (int ks = 0; ks < 32; ++ks)
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xs[col * 129 + ks * 4 + kq], (double)bf16_to_f32(Rw[4 * ks]), acc,
+                                               0, 0, 0);
+  const double t0 = thresh[0], t1 = thresh[1], t2 = thresh[2];
+  const double lv0 = levels[0], lv1 = levels[1], lv2 = levels[2], lv3 = levels[3];
+  // element i of acc is y[token kq + 4 i][row 16 w + col]; the 2-bit codes of
+  // rows 16 w .. 16 w + 15 form word w of each token's code row (row 16 w + b
+  // in bits 2 b), gathered across the 16 lanes of a quarter
+  uint8_t* codes = keys ? kc : vc;
+  double rr[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tok = kq + 4 * i;
+    const double tn = __shfl(nrm, tok);
+    const double u = tn > 0.0 ? __ddiv_rn(acc[i], tn) : 0.0;
+    const int id = (u >= t0) + (u >= t1) + (u >= t2);
+    uint32_t word = (uint32_t)id << (2 * col);
+    word |= __shfl_xor(word, 1);
+    word |= __shfl_xor(word, 2);
+    word |= __shfl_xor(word, 4);
+    word |= __shfl_xor(word, 8);
+    if (col == 0 && base + tok < rows)
+      *reinterpret_cast<uint32_t*>(codes + dst_row(base + tok, n, cap, start) * 32 + 4 * w) = word;
+    if (keys) {
+      const double lv = id == 0 ? lv0 : id == 1 ? lv1 : id == 2 ? lv2 : lv3;
+      const double r = u - lv;
+      rs[tok * 129 + 16 * w + col] = r;
+      rr[i] = r * r;
+    }
+  }
+  if (keys) {
+    // this wave's 16 columns of gamma^2 per token
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      double t = rr[i];
+      t += __shfl_xor(t, 1);
+      t += __shfl_xor(t, 2);
+      t += __shfl_xor(t, 4);
+      t += __shfl_xor(t, 8);
+      if (col == 0) g2part[w][kq + 4 * i] = t;
+    }
+  }
+  if (w == 0 && lane < 16 && base + lane < rows)
+    (keys ? knorm : vnorm)[dst_row(base + lane, n, cap, start)] = f16_from_f64_nonneg(nrm);
+  if (!keys) return;
+  __syncthreads();
+  // S r for sketch rows 16 w .. 16 w + 15
+  f64x4 sacc = f64x4{0.0, 0.0, 0.0, 0.0};
+  const uint16_t* Sw = &rows_lds[w][1][col * kSPad + kq];
+#pragma unroll
+  for (int ks = 0; ks < 32; ++ks)
+    sacc = __builtin_amdgcn_mfma_f64_16x16x4f64(rs[col * 129 + ks * 4 + kq], (double)bf16_to_f32(Sw[4 * ks]), sacc,
+                                                0, 0, 0);
+  // token t's bits for these rows: lanes 16 (t % 4) .. + 15 of ballot t / 4, bit
+  // col = row 16 w + col, i.e. bytes 2 w and 2 w + 1 of its sketch
+  uint32_t my_bits = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const unsigned long long bal = __ballot(sacc[i] >= 0.0);
+    if ((lane >> 2) == i) my_bits = (uint32_t)(bal >> (16 * (lane & 3))) & 0xFFFFu;
+  }
+  if (lane < 16 && base + lane < rows) {
+    const size_t dr = dst_row(base + lane, n, cap, start);
+    *reinterpret_cast<uint16_t*>(sketch + dr * 16 + 2 * w) = (uint16_t)my_bits;
+    if (w == 0) {
+      double g2 = 0.0;
+      for (int ww = 0; ww < 8; ++ww) g2 += g2part[ww][lane];
+      krnorm[dr] = f16_from_f64_nonneg(sqrt(g2));
+    }
+  }
+}
+
 int blocks_for(size_t threads) { return (int)((threads + 255) / 256); }
 
 // Workgroups of the QJL append: one resident round (each stages S once).
 #ifndef KVQ_QJL_APPEND_BLOCKS
 #define KVQ_QJL_APPEND_BLOCKS (256 * KVQ_QJL_APPEND_WAVES_PER_EU)
 #endif
+
+// Appends of at most this many rows take the latency-bound TurboQuant kernel.
+constexpr size_t kTurboSmallRows = 2048;
 
 int persistent_blocks(size_t rows) {
   size_t tiles = (rows + 63) / 64;
@@ -840,6 +983,13 @@ int append_typed(const kv_cache* c, const InT* k, const InT* v, int start, int n
       break;
     }
     case KV_FMT_TURBO:
+      if (rows <= kTurboSmallRows) {
+        turbo_append_small_kernel<InT><<<dim3((unsigned)((rows + 15) / 16), 2), 512, 0, st>>>(
+            k, v, c->rot, c->proj, c->lm_levels, c->lm_thresh, kc, static_cast<uint8_t*>(c->buf[KV_BUF_K_SKETCH]),
+            static_cast<uint16_t*>(c->buf[KV_BUF_K_NORM]), static_cast<uint16_t*>(c->buf[KV_BUF_K_RNORM]), vc,
+            static_cast<uint16_t*>(c->buf[KV_BUF_V_NORM]), rows, n, cap, start);
+        break;
+      }
       turbo_append_kernel<InT><<<dim3(persistent_blocks(rows), 2), 256, 0, st>>>(
           k, v, c->rot, c->proj, c->lm_levels, c->lm_thresh, kc, static_cast<uint8_t*>(c->buf[KV_BUF_K_SKETCH]),
           static_cast<uint16_t*>(c->buf[KV_BUF_K_NORM]), static_cast<uint16_t*>(c->buf[KV_BUF_K_RNORM]), vc,

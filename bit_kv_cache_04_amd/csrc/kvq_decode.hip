@@ -242,24 +242,31 @@ __global__ void __launch_bounds__(128) prep_query_kernel(const QT* __restrict__ 
 
 // out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, M = max_s m_s, for one
 // (sequence, query head) row per blockIdx.x and the columns
-// [64 * NJ * blockIdx.y, 64 * NJ * (blockIdx.y + 1)).  The split weights are
-// formed once in LDS; wave w then sums the splits w, w + W, ... (W waves) for
-// every column of the block, lane l owning columns NJ * l .. NJ * l + NJ - 1,
-// so that the loads of different splits are independent and spread over the
-// block; the W wave sums are added in wave order.  TURBO (the whole row in one
-// block) maps the rotated output back with R^T.  A row with no tokens at all
-// writes zeros.
-constexpr int kMergeMaxWaves = 16;
+// [64 * NJ * blockIdx.y, 64 * NJ * (blockIdx.y + 1)).  The splits' (m, l) pairs
+// are read once into LDS and turned into weights there; wave w then sums the
+// splits w, w + W, ... (W waves) for every column of the block, lane l owning
+// columns NJ * l .. NJ * l + NJ - 1, so that the loads of different splits are
+// independent and spread over the block; the W wave sums are added in wave
+// order.  TURBO (the whole row in one block) maps the rotated output back with
+// R^T, every thread taking a slice of the rows of R.  A row with no tokens at
+// all writes zeros.
 constexpr int kMaxSplits = 1024;
 
 template <int NJ>
-__global__ void __launch_bounds__(64 * kMergeMaxWaves) merge_kernel(const float* __restrict__ part, int splits,
-                                                                    int dv, int fmt, const float* __restrict__ rot,
-                                                                    float* __restrict__ out) {
-  constexpr int CW = 64 * NJ;
-  __shared__ float w[kMaxSplits];
-  __shared__ float red[kMergeMaxWaves];
-  __shared__ float sums[kMergeMaxWaves][CW];
+constexpr int merge_max_waves() {
+  return NJ >= 4 ? 4 : 16;
+}
+
+template <int NJ>
+__global__ void __launch_bounds__(64 * merge_max_waves<NJ>()) merge_kernel(const float* __restrict__ part,
+                                                                           int splits, int dv, int fmt,
+                                                                           const float* __restrict__ rot,
+                                                                           float* __restrict__ out) {
+  constexpr int CW = 64 * NJ, MW = merge_max_waves<NJ>();
+  __shared__ float sm_w[kMaxSplits];  // m_s, then the weights
+  __shared__ float sm_l[kMaxSplits];
+  __shared__ float red_m[MW], red_l[MW];
+  __shared__ float sums[MW][CW];
   __shared__ float ov[CW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nthr = blockDim.x, W = nthr >> 6;
@@ -267,42 +274,49 @@ __global__ void __launch_bounds__(64 * kMergeMaxWaves) merge_kernel(const float*
   const size_t stride = (size_t)dv + 2;
   const float* p = part + row * (size_t)splits * stride;
   float M = -INFINITY;
-  for (int s = tid; s < splits; s += nthr) M = fmaxf(M, p[s * stride]);
+  for (int s = tid; s < splits; s += nthr) {
+    const float2 ml = *reinterpret_cast<const float2*>(p + s * stride);
+    sm_w[s] = ml.x;
+    sm_l[s] = ml.y;
+    M = fmaxf(M, ml.x);
+  }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  if (lane == 0) red[wave] = M;
+  if (lane == 0) red_m[wave] = M;
   __syncthreads();
-  M = red[0];
-  for (int i = 1; i < W; ++i) M = fmaxf(M, red[i]);
-  __syncthreads();
+  M = red_m[0];
+  for (int i = 1; i < W; ++i) M = fmaxf(M, red_m[i]);
   float l = 0.f;
-  for (int s = tid; s < splits; s += nthr) {
-    const float ms = p[s * stride];
+  for (int s = tid; s < splits; s += nthr) {  // each thread revisits only its own entries
+    const float ms = sm_w[s];
     const float ws = ms == -INFINITY ? 0.f : exp2f(ms - M);
-    w[s] = ws;
-    l += ws * p[s * stride + 1];
+    sm_w[s] = ws;
+    l += ws * sm_l[s];
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
-  if (lane == 0) red[wave] = l;
+  if (lane == 0) red_l[wave] = l;
   __syncthreads();
-  l = red[0];
-  for (int i = 1; i < W; ++i) l += red[i];
+  l = red_l[0];
+  for (int i = 1; i < W; ++i) l += red_l[i];
   const float inv_l = l > 0.f ? 1.f / l : 0.f;
   const int c0 = CW * blockIdx.y;
   float acc[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) acc[j] = 0.f;
-  const float* pc = p + 2 + c0 + NJ * lane;
-#pragma unroll 4
+  const float* pc = p + 2 + c0 + NJ * lane;  // 8-byte aligned: rows and the header are even
+#pragma unroll(16 / NJ)
   for (int s = wave; s < splits; s += W) {
-    const float ws = w[s];
-    if constexpr (NJ == 2) {
-      const float2 v = *reinterpret_cast<const float2*>(pc + s * stride);
-      acc[0] = fmaf(ws, v.x, acc[0]);
-      acc[1] = fmaf(ws, v.y, acc[1]);
-    } else {
+    const float ws = sm_w[s];
+    if constexpr (NJ == 1) {
       acc[0] = fmaf(ws, pc[s * stride], acc[0]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NJ; j += 2) {
+        const float2 v = *reinterpret_cast<const float2*>(pc + s * stride + j);
+        acc[j] = fmaf(ws, v.x, acc[j]);
+        acc[j + 1] = fmaf(ws, v.y, acc[j + 1]);
+      }
     }
   }
 #pragma unroll
@@ -317,25 +331,42 @@ __global__ void __launch_bounds__(64 * kMergeMaxWaves) merge_kernel(const float*
   }
   if (fmt == KV_FMT_TURBO) {  // CW == dv here
     __syncthreads();
-    for (int c = tid; c < CW; c += nthr) {
+    // P slices of the rows of R: thread (q, c) sums j in [q * CW / P, (q + 1) * CW / P)
+    const int P = nthr >= CW ? min(nthr / CW, MW) : 1;
+    const int span = CW / P;
+    for (int e = tid; e < P * CW; e += nthr) {
+      const int q = e / CW, c = e % CW;
       float a = 0.f;
-      for (int j = 0; j < CW; ++j) a = fmaf(rot[j * CW + c], ov[j], a);
+#pragma unroll 8
+      for (int j = q * span; j < (q + 1) * span; ++j) a = fmaf(rot[j * CW + c], ov[j], a);
+      sums[q][c] = a;
+    }
+    __syncthreads();
+    for (int c = tid; c < CW; c += nthr) {
+      float a = sums[0][c];
+      for (int q = 1; q < P; ++q) a += sums[q][c];
       dst[c] = a;
     }
   }
 }
 
-// Column blocks of 128 (dv a multiple of 128) or 64; TURBO keeps the row in one
-// block.  Waves: about four splits each, at most 16.
+// Column blocks: TURBO and many rows take the whole row per block (up to 8
+// columns per lane); few rows take 64-column blocks so that more workgroups
+// share the loads; otherwise 128 columns.  Waves: about four splits each.
 void launch_merge(const float* part, int rows, int splits, int dv, int fmt, const float* rot, float* out,
                   hipStream_t st) {
-  const int nj = dv % 128 == 0 ? 2 : 1;
-  const int cw = 64 * nj;
-  const int col_blocks = fmt == KV_FMT_TURBO ? 1 : dv / cw;
-  const int waves = std::min(kMergeMaxWaves, std::max(1, (splits + 3) / 4));
+  int nj;
+  if (fmt == KV_FMT_TURBO || rows >= 2048) nj = dv / 64;
+  else if (rows < 256 || dv % 128 != 0) nj = 1;
+  else nj = 2;
+  const int col_blocks = dv / (64 * nj);
   const dim3 grid(rows, col_blocks);
-  if (nj == 2) merge_kernel<2><<<grid, 64 * waves, 0, st>>>(part, splits, dv, fmt, rot, out);
-  else merge_kernel<1><<<grid, 64 * waves, 0, st>>>(part, splits, dv, fmt, rot, out);
+  auto waves = [&](int max_w) { return std::min(max_w, std::max(1, (splits + 3) / 4)); };
+  switch (nj) {
+    case 1: merge_kernel<1><<<grid, 64 * waves(merge_max_waves<1>()), 0, st>>>(part, splits, dv, fmt, rot, out); break;
+    case 2: merge_kernel<2><<<grid, 64 * waves(merge_max_waves<2>()), 0, st>>>(part, splits, dv, fmt, rot, out); break;
+    default: merge_kernel<8><<<grid, 64 * waves(merge_max_waves<8>()), 0, st>>>(part, splits, dv, fmt, rot, out); break;
+  }
 }
 
 template <int FMT, int DK, int DV, int HB>

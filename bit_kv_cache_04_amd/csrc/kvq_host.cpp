@@ -99,8 +99,10 @@ SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int q_dtype, int max_
   const bool latent = latent_fast_path_ok(*L, num_q_heads, q_dtype);
   const int tile = fast ? 128 : 64;
   // the latent kernel keeps one workgroup per compute unit resident and every
-  // split writes Hq x 514 partial floats: a few long splits per sequence
-  const long target = latent ? 512 : 2048;
+  // split writes Hq x 514 partial floats: one round of workgroups, a few long
+  // splits per sequence (4 at batch 64; 8 measured no faster in the kernel and
+  // doubles the partials the merge reads)
+  const long target = latent ? 256 : 2048;
   long units = (long)L->batch * L->num_kv_heads;
   if (!fast && !latent && G > 16) units *= (G + 15) / 16;  // the generic kernel's head blocks
   int splits = requested;

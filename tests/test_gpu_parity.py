@@ -162,6 +162,22 @@ def test_token_by_token_append_equals_bulk(fmt):
     assert_bytes_equal(gpu_buffers(step), gpu_buffers(bulk), fmt)
 
 
+def test_turbo_small_and_bulk_append_kernels_agree():
+    """TurboQuant appends of at most 2048 rows take a latency-oriented kernel, larger
+    ones a persistent one; both must write the same bytes (and the oracle's)."""
+    cfg = SMALL["turbo"].scaled(context=1100)
+    print("[turbo small vs bulk]", flush=True)
+    bulk, K, V = _build(cfg, chunks=1)  # 2 x 2 x 1100 = 4400 rows in one append
+    small = new_cache(cfg)
+    for t0 in range(0, cfg.context, 100):  # 400 rows per append
+        small.append(K[:, :, t0:t0 + 100].contiguous(), V[:, :, t0:t0 + 100].contiguous(), t0)
+    torch.cuda.synchronize()
+    got = gpu_buffers(small)
+    assert_bytes_equal(got, gpu_buffers(bulk), "turbo small vs bulk")
+    want = oracle_encode(cfg, host64(K), host64(V), oracle_constants(cfg))
+    assert_bytes_equal(got, want, "turbo small vs oracle")
+
+
 @pytest.mark.parametrize("fmt", ["fp4", "qjl1", "turbo", "latent"])
 def test_split_count_invariance_and_determinism(fmt):
     cfg = SMALL[fmt]
