@@ -263,7 +263,7 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) decode_latent_kernel(MfmaDecodeArgs a
         s[i] = tok < t_end ? s[i] * a.scale_log2 : -INFINITY;
         tmax = fmaxf(tmax, s[i]);
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      tmax = max_xor32(tmax);
       // the reference max moves only when the tile max passes it by more than 2^8
       const bool bump = tmax > m_run + 8.f;
       const float m_new = bump ? tmax : m_run;

@@ -323,17 +323,27 @@ __device__ __forceinline__ void tile_step(WaveState<KP>& w, uint8_t* st, int lan
   // ---------------- online softmax (this lane: head c, tokens t0 + 16*blk + 4*v + q4)
   float sv[8];
   float tmax = -INFINITY;
+  if (t0 + 32 <= t_end) {  // a whole tile: nothing to mask
 #pragma unroll
-  for (int blk = 0; blk < 2; ++blk)
+    for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int tok = t0 + 16 * blk + 4 * v + q4;
-      const float s = tok < t_end ? sacc[blk][v] * a.scale_log2 : -INFINITY;
-      sv[4 * blk + v] = s;
-      tmax = fmaxf(tmax, s);
-    }
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      for (int v = 0; v < 4; ++v) {
+        sv[4 * blk + v] = sacc[blk][v] * a.scale_log2;
+        tmax = fmaxf(tmax, sv[4 * blk + v]);
+      }
+  } else {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int tok = t0 + 16 * blk + 4 * v + q4;
+        const float s = tok < t_end ? sacc[blk][v] * a.scale_log2 : -INFINITY;
+        sv[4 * blk + v] = s;
+        tmax = fmaxf(tmax, s);
+      }
+  }
+  tmax = max_xor16(tmax);
+  tmax = max_xor32(tmax);
   // The reference max moves only when the tile max exceeds it by more than 2^8
   // (weights up to 256 are exact enough in fp16 and cannot overflow), so the
   // accumulator rescale below is rare.

@@ -185,8 +185,8 @@ __device__ __forceinline__ void tile_step(WaveState<G>& w, uint8_t* st, int lane
     tmax = fmaxf(tmax, s);
   }
   tmax = fmaxf(tmax, row_ror8(tmax));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  tmax = max_xor16(tmax);
+  tmax = max_xor32(tmax);
   const bool bump = tmax > w.m_run + 8.f;
   const float m_new = bump ? tmax : w.m_run;
   const float alpha = bump ? __builtin_amdgcn_exp2f(w.m_run - m_new) : 1.f;

@@ -91,4 +91,18 @@ __device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p, size_t
   return bf16_to_f32(p[i]);
 }
 
+// ---------------------------------------------------------------- cross-row lane exchange
+
+// max of x over lanes l and l ^ 16 (l ^ 32), in registers: v_permlane16_swap
+// (v_permlane32_swap) of x with itself leaves the two lanes' values in the two
+// halves of the result, in either order.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 }  // namespace kvq
