@@ -22,7 +22,7 @@
 // QJL keys: the logit is sqrt(pi/2)/m * n * <S q, sigma> with sigma = +-1 from
 // the sketch bits (page "TurboQuant vs OSCAR vs EpiCache", section
 // "quantization frontiers", stage two).  <S q, sigma> = 2 <S q, b> - sum(S q)
-// for the bits b; each bit enters the product as the fp16 value 2^-14 or 0 and
+// for the bits b; each bit enters the product as the fp16 value 1.0 or 0 and
 // S q as an exact fp16 hi + lo pair, so the sum is exact up to fp32 rounding.
 #include <hip/hip_runtime.h>
 
@@ -72,12 +72,12 @@ __device__ __forceinline__ h8_t dequant8(uint32_t w, h2_t s) {
   return h8_from(fp4x2<0>(w) * s, fp4x2<1>(w) * s, fp4x2<2>(w) * s, fp4x2<3>(w) * s);
 }
 
-// Two sketch bits m and m + 16 of w as the fp16 pair (2^-14 * bit_m, 2^-14 * bit_{m+16}):
-// each bit moved onto bit 10 of its half (the lowest exponent bit).
-template <int M>
-__device__ __forceinline__ h2_t bits2(uint32_t w) {
-  const uint32_t x = w & (0x00010001u << M);
-  return __builtin_bit_cast(h2_t, M <= 10 ? (x << (10 - M)) : (x >> (M - 10)));
+// The 8 bits at positions 0, 4, ..., 28 of m as fp16 1.0 / 0 (element n <- bit
+// 4n): the FP4 converter reads a nibble holding only its low bit as 0.5, scaled
+// by 2.
+__device__ __forceinline__ h8_t bits8(uint32_t m) {
+  return h8_from(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 2.0f, 0), __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 2.0f, 1),
+                 __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 2.0f, 2), __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 2.0f, 3));
 }
 
 // A-operand row c of a 16-token block holds token 4*(c%4) + c/4, so that the
@@ -155,7 +155,7 @@ struct KeysQjl {
   static constexpr int kBytes = 768;  // sketch 512 | norms, one per dword: 128 (+ 128 zeros)
   static constexpr int kDma = 3;      // direct-to-LDS loads issue() makes
   struct Q {
-    // lane (q4, c): head c; MFMA i, k-slot pair p, element e <-> sketch row 32*q4 + 4*i + p + 16*e
+    // lane (q4, c): head c; MFMA i, k-slot j <-> sketch row 32*q4 + 4*j + i
     h8_t hi[4], lo[4];
     float sumq;  // sum of the head's 128 projected-query values
   };
@@ -174,15 +174,13 @@ struct KeysQjl {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const float v = c < G ? qp[4 * i + p + 16 * e] : 0.f;
-          const _Float16 hi = (_Float16)v;
-          q.hi[i][2 * p + e] = hi;
-          q.lo[i][2 * p + e] = (_Float16)(v - (float)hi);
-          s += v;
-        }
+      for (int j = 0; j < 8; ++j) {
+        const float v = c < G ? qp[4 * j + i] : 0.f;
+        const _Float16 hi = (_Float16)v;
+        q.hi[i][j] = hi;
+        q.lo[i][j] = (_Float16)(v - (float)hi);
+        s += v;
+      }
     s += __shfl_xor(s, 16);
     s += __shfl_xor(s, 32);
     q.sumq = s;
@@ -215,22 +213,17 @@ struct KeysQjl {
     for (int blk = 0; blk < 2; ++blk) {
       const uint32_t w = f.w[blk];
       f4_t acc = f4_t{0.f, 0.f, 0.f, 0.f};
-#define KVQ_QJL_STEP(I)                                                                                  \
-  {                                                                                                      \
-    const h8_t A = h8_from(bits2<4 * I + 0>(w), bits2<4 * I + 1>(w), bits2<4 * I + 2>(w), bits2<4 * I + 3>(w)); \
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, q.hi[I], acc, 0, 0, 0);                               \
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, q.lo[I], acc, 0, 0, 0);                               \
-  }
-      KVQ_QJL_STEP(0)
-      KVQ_QJL_STEP(1)
-      KVQ_QJL_STEP(2)
-      KVQ_QJL_STEP(3)
-#undef KVQ_QJL_STEP
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const h8_t A = bits8((w >> i) & 0x11111111u);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, q.hi[i], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, q.lo[i], acc, 0, 0, 0);
+      }
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const float n = f16_to_f32((uint16_t)f.n[4 * blk + v]);
-        // acc = 2^-14 <S q, b>: <S q, sigma> = 2^15 acc - sum(S q)
-        acc[v] = kappa * n * fmaf(32768.f, acc[v], -q.sumq);
+        // acc = <S q, b>: <S q, sigma> = 2 acc - sum(S q)
+        acc[v] = kappa * n * fmaf(2.f, acc[v], -q.sumq);
       }
       sacc[blk] = acc;
     }
