@@ -257,11 +257,19 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) decode_latent_kernel(MfmaDecodeArgs a
       s += s2;
       // -------- 4. online softmax for head 32 wave + col over this lane's 16 tokens
       float tmax = -INFINITY;
+      if (tt + kTile <= t_end) {  // a whole tile: nothing to mask
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int tok = tt + 16 * (i >> 3) + 8 * half + (i & 7);
-        s[i] = tok < t_end ? s[i] * a.scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, s[i]);
+        for (int i = 0; i < 16; ++i) {
+          s[i] = s[i] * a.scale_log2;
+          tmax = fmaxf(tmax, s[i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int tok = tt + 16 * (i >> 3) + 8 * half + (i & 7);
+          s[i] = tok < t_end ? s[i] * a.scale_log2 : -INFINITY;
+          tmax = fmaxf(tmax, s[i]);
+        }
       }
       tmax = max_xor32(tmax);
       // the reference max moves only when the tile max passes it by more than 2^8
