@@ -207,14 +207,74 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
 
 // ---------------------------------------------------------------- query preparation
 
-// Prepared fp32 query: q itself, or [R q, S R q] (TURBO), or S q (QJL1).
+// Nearest E4M3 (OCP FP8, 3 mantissa bits) of y, |y| < 128: the code and its
+// value; magnitudes below the smallest normal, 2^-6, become zero (the caller
+// keeps them in its residual).
+__device__ __forceinline__ uint32_t e4m3_code(float y, float& val) {
+  const uint32_t sgn = __float_as_uint(y) & 0x80000000u;
+  const float ay = fabsf(y);
+  if (!(ay >= 0x1p-6f)) {
+    val = 0.f;
+    return 0u;
+  }
+  uint32_t u = __float_as_uint(ay);
+  u = (u + 0x7FFFFu + ((u >> 20) & 1u)) & ~0xFFFFFu;  // ties to even on 3 mantissa bits
+  val = __uint_as_float(u | sgn);
+  const uint32_t ef = (u >> 23) - 127u + 7u;            // 1 .. 14
+  return (sgn >> 24) | (ef << 3) | ((u >> 20) & 7u);
+}
+
+// TurboQuant query pieces.  The key products take the key bits as FP4 operands
+// (one bit per nibble) against FP8 operands with a power-of-two scale per block
+// of 32 (v_mfma_scale_f32_16x16x128_f8f6f4).  Block j (element e = 8 d + n, the
+// bit 4 n + d of one key word) of
+//   product 0 / 1 (code words 4 m + j, m = 0 / 1): the coefficient of bit d % 2
+//     (a2 for the low bit b0, a1 for the high bit b1) times (R q)[16 (4 m + j) +
+//     2 n + d / 2];
+//   product 2 (sketch dword j): (S R q)[32 j + 4 n + d].
+// Each block is split into 4 FP8 pieces: piece p holds the nearest E4M3 of the
+// residual left by pieces < p, at a scale 2^e that puts the residual's largest
+// magnitude in [64, 128), so the pieces' sum is within 2^-20 of the block's
+// largest value.  Layout per (product, piece): 4 blocks x 32 code bytes, then
+// the 4 blocks' E8M0 scale bytes (e + 127), 144 bytes in all.
+__device__ void prepared_query_pieces(const float* qrot, const float* qsr, float a1, float a2, uint8_t* out) {
+  const int tid = threadIdx.x, e = tid & 31, d = e >> 3, n = e & 7;
+  for (int blk = tid >> 5; blk < 12; blk += 4) {
+    const int prod = blk < 8 ? blk >> 2 : 2, j = blk < 8 ? blk & 3 : blk - 8;
+    float r = blk < 8 ? ((d & 1) ? a1 : a2) * qrot[16 * (4 * prod + j) + 2 * n + (d >> 1)]
+                      : qsr[32 * j + 4 * n + d];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      float M = fabsf(r);
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+      int ex = 0;
+      if (M > 0.f) {
+        int k;
+        frexpf(M, &k);  // M = f 2^k, f in [0.5, 1)
+        ex = k - 7;
+      }
+      float val;
+      const uint32_t code = e4m3_code(ldexpf(r, -ex), val);
+      r -= ldexpf(val, ex);
+      uint8_t* dst = out + (prod * 4 + p) * 144;
+      dst[j * 32 + e] = (uint8_t)code;
+      if (e == 0) dst[128 + j] = (uint8_t)(ex + 127);
+    }
+  }
+}
+
+// Prepared fp32 query: q itself, or [R q, S R q] (TURBO, with its FP8 pieces
+// when `pieces` is given), or S q (QJL1).
 template <typename QT>
 __global__ void __launch_bounds__(128) prep_query_kernel(const QT* __restrict__ q, int qw_in, int qw_out,
                                                          int fmt, const float* __restrict__ rot,
                                                          const float* __restrict__ proj,
-                                                         float* __restrict__ out) {
+                                                         const float* __restrict__ levels,
+                                                         float* __restrict__ out, uint8_t* __restrict__ pieces) {
   __shared__ float qin[640];
   __shared__ float qrot[128];
+  __shared__ float qsr[128];
   const size_t row = blockIdx.x;
   const int tid = threadIdx.x;
   for (int c = tid; c < qw_in; c += 128) qin[c] = load_as_f32(q + row * qw_in, c);
@@ -229,6 +289,12 @@ __global__ void __launch_bounds__(128) prep_query_kernel(const QT* __restrict__ 
     float acc2 = 0.f;
     for (int j = 0; j < 128; ++j) acc2 = fmaf(proj[tid * 128 + j], qrot[j], acc2);
     dst[128 + tid] = acc2;
+    if (pieces) {
+      qsr[tid] = acc2;
+      __syncthreads();
+      prepared_query_pieces(qrot, qsr, levels[2] - levels[0], levels[1] - levels[0],
+                            pieces + row * kTurboPieceBytes);
+    }
   } else if (fmt == KV_FMT_QJL1_FP4V) {
     float acc = 0.f;
     for (int j = 0; j < 128; ++j) acc = fmaf(proj[tid * 128 + j], qin[j], acc);
@@ -413,13 +479,14 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
   const bool mfma = mfma_fast_path_ok(L, num_q_heads, q_dtype);
   // FP4 keys read the caller's bf16 queries as they are; every other format
   // first prepares its fp32 query (projection / rotation)
+  uint8_t* qpieces = turbo_fast_path_ok(L, num_q_heads) ? reinterpret_cast<uint8_t*>(wsb + wsl.qpiece_off) : nullptr;
   if (!(mfma && L.format == KV_FMT_FP4)) {
     if (q_dtype == KV_DT_F32)
       prep_query_kernel<float><<<rows, 128, 0, st>>>(static_cast<const float*>(q), qw_in, qw_out, L.format,
-                                                     c->rot, c->proj, qv);
+                                                     c->rot, c->proj, c->lm_levels, qv, qpieces);
     else
       prep_query_kernel<uint16_t><<<rows, 128, 0, st>>>(static_cast<const uint16_t*>(q), qw_in, qw_out,
-                                                        L.format, c->rot, c->proj, qv);
+                                                        L.format, c->rot, c->proj, c->lm_levels, qv, qpieces);
   }
   if (turbo_fast_path_ok(L, num_q_heads)) {
     TurboDecodeArgs f{};
@@ -431,6 +498,7 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     f.v_norm = static_cast<const uint16_t*>(c->buf[KV_BUF_V_NORM]);
     f.levels = c->lm_levels;
     f.q = qv;
+    f.qpieces = qpieces;
     f.seq_lens = seq_lens;
     f.max_len = max_seq_len;
     f.H = L.num_kv_heads;

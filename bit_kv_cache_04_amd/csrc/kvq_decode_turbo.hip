@@ -40,6 +40,7 @@ typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef int i2_t __attribute__((ext_vector_type(2)));
+typedef int i8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kRsrcFlags = 0x00020000;
@@ -105,10 +106,28 @@ struct Consts {
   float a0, a1, a2;  // level = a0 + a1 b1 + a2 b0
 };
 
+// One bit per nibble of a key word, as the FP4 operand of a scaled product:
+// dword d holds bits d, d + 4, ..., d + 28 (element 8 d + n = bit 4 n + d).
+__device__ __forceinline__ i8_t bit_nibbles(uint32_t w) {
+  const uint32_t m = 0x11111111u;
+  return i8_t{(int)(w & m), (int)((w >> 1) & m), (int)((w >> 2) & m), (int)((w >> 3) & m), 0, 0, 0, 0};
+}
+
+// Key products on v_mfma_scale_f32_16x16x128_f8f6f4: A = key bits (FP4, 0 or
+// 0.5, block scale 2), B = FP8 pieces of the query operand with their block
+// scales.  A lane quarter's 32 elements form one k-block; B lane quarter qb
+// holds k-blocks qb / 2 and 2 + qb / 2 (elements 16 (qb % 2) .. + 15 of each)
+// and the scale of k-block qb.
+__device__ __forceinline__ f4_t key_product(i8_t a, i8_t b, int scale_b, f4_t acc) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 4, 0, 0, 128, 0, scale_b);
+}
+
 template <int G>
 struct WaveState {
-  h8_t blm[8];   // B operand of the 8 code-bit steps: (a1 or a2) * R q, hi or lo
-  h8_t bqs[4];   // B operand of the 4 sketch steps: S R q, hi or lo
+  // B operands of the key products: [product (code words 0..3, 4..7, sketch)]
+  // [piece set]: columns 0..7 carry pieces 2 s, columns 8..15 pieces 2 s + 1
+  i8_t bq[3][2];
+  int bs[3][2];  // their block scales
   float cst;     // a0 * sum(R q) for this lane's head
   float sqs;     // sum(S R q)
   float m_run, l_run, sp;  // running max, sum of p, sum of p * n_v
@@ -129,13 +148,15 @@ __device__ __forceinline__ void tile_step(WaveState<G>& w, uint8_t* st, int lane
   int ko = qk_token(c, 0) * 32, so = qk_token(c, 0) * 16, no = 4 * 8 * q4;
   int vo = (8 * q4 + (c & 7)) * 32 + 8 * (c >> 3);
   asm volatile("" : "+v"(ko), "+v"(so), "+v"(no), "+v"(vo));
-  uint4 kw[2][2], sw[2];
-  // block 1's token is 4 after block 0's: 128 bytes of codes, 64 of sketch
+  // this lane's key words of its A-operand token: code words q4 and 4 + q4,
+  // sketch dword q4 (block 1's token is 4 after block 0's: 128 bytes of codes,
+  // 64 of sketch)
+  uint32_t kw0[2], kw1[2], sw[2];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
-    kw[b][0] = *reinterpret_cast<const uint4*>(st + kSK + ko + 128 * b);
-    kw[b][1] = *reinterpret_cast<const uint4*>(st + kSK + ko + 128 * b + 16);
-    sw[b] = *reinterpret_cast<const uint4*>(st + kSS + so + 64 * b);
+    kw0[b] = *reinterpret_cast<const uint32_t*>(st + kSK + ko + 128 * b + 4 * q4);
+    kw1[b] = *reinterpret_cast<const uint32_t*>(st + kSK + ko + 128 * b + 16 + 4 * q4);
+    sw[b] = *reinterpret_cast<const uint32_t*>(st + kSS + so + 64 * b + 4 * q4);
   }
   // Norms of the 4 tokens this lane scores after the hi + lo combine (below):
   // columns 0..7 take tokens 8 q4 + [0, 4), columns 8..15 tokens 8 q4 + [4, 8).
@@ -154,20 +175,18 @@ __device__ __forceinline__ void tile_step(WaveState<G>& w, uint8_t* st, int lane
   f4_t lm[2], qj[2];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
-    const uint32_t words[8] = {kw[b][0].x, kw[b][0].y, kw[b][0].z, kw[b][0].w,
-                               kw[b][1].x, kw[b][1].y, kw[b][1].z, kw[b][1].w};
+    const i8_t a0 = bit_nibbles(kw0[b]), a1 = bit_nibbles(kw1[b]), as = bit_nibbles(sw[b]);
     lm[b] = f4_t{0.f, 0.f, 0.f, 0.f};
     qj[b] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      lm[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bits8((words[i] >> q4) & 0x11111111u), w.blm[i], lm[b], 0, 0, 0);
-    const uint32_t sks[4] = {sw[b].x, sw[b].y, sw[b].z, sw[b].w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      qj[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bits8((sks[i] >> q4) & 0x11111111u), w.bqs[i], qj[b], 0, 0, 0);
+    for (int ps = 0; ps < 2; ++ps) {
+      lm[b] = key_product(a0, w.bq[0][ps], w.bs[0][ps], lm[b]);
+      lm[b] = key_product(a1, w.bq[1][ps], w.bs[1][ps], lm[b]);
+      qj[b] = key_product(as, w.bq[2][ps], w.bs[2][ps], qj[b]);
+    }
   }
-  // Column c < 8 holds the hi part of head c, column c + 8 its lo part.  Each
-  // lane keeps one block and adds the partner column's part of that block:
+  // Column c < 8 holds pieces 0 and 2 of head c, column c + 8 pieces 1 and 3.
+  // Each lane keeps one block and adds the partner column's part of that block:
   // columns 0..7 finish block 0, columns 8..15 block 1, both for head c % 8.
   const bool upper = c >= 8;
   float sv[4];
@@ -275,28 +294,25 @@ __attribute__((amdgpu_waves_per_eu(KVQ_TURBO_WAVES_PER_EU, KVQ_TURBO_WAVES_PER_E
   }
   WaveState<G> w;
   {
-    // prepared query: [R q (128) | S R q (128)] fp32 per query head
+    // prepared query: [R q (128) | S R q (128)] fp32 per query head, and the FP8
+    // pieces of the key-product operands (layout of prepared_query_pieces)
     const int head = c % 8;
     const bool live = head < G;
-    const bool lo = c >= 8;
-    const float* qp = a.q + ((size_t)b * a.Hq + (size_t)h * G + (live ? head : 0)) * 256;
+    const size_t qrow = (size_t)b * a.Hq + (size_t)h * G + (live ? head : 0);
+    const float* qp = a.q + qrow * 256;
+    const uint8_t* pc = a.qpieces + qrow * kTurboPieceBytes;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float coef = (q4 & 1) ? k.a1 : k.a2;
+    for (int m = 0; m < 3; ++m)
 #pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const float v = live ? coef * qp[16 * i + 2 * n + (q4 >> 1)] : 0.f;
-        const _Float16 hi = (_Float16)v;
-        w.blm[i][n] = lo ? (_Float16)(v - (float)hi) : hi;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const float v = live ? qp[128 + 32 * i + 4 * n + q4] : 0.f;
-        const _Float16 hi = (_Float16)v;
-        w.bqs[i][n] = lo ? (_Float16)(v - (float)hi) : hi;
+      for (int ps = 0; ps < 2; ++ps) {
+        const uint8_t* base = pc + (m * 4 + 2 * ps + (c >> 3)) * 144 + 16 * (q4 & 1);
+        const uint4 lo4 = *reinterpret_cast<const uint4*>(base + 32 * (q4 >> 1));
+        const uint4 hi4 = *reinterpret_cast<const uint4*>(base + 32 * (2 + (q4 >> 1)));
+        const uint8_t* sc = pc + (m * 4 + 2 * ps + (c >> 3)) * 144 + 128;
+        w.bq[m][ps] = live ? i8_t{(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w, (int)hi4.x, (int)hi4.y, (int)hi4.z,
+                                  (int)hi4.w}
+                           : i8_t{0, 0, 0, 0, 0, 0, 0, 0};
+        w.bs[m][ps] = live ? (int)sc[q4] : 127;
       }
     // per-head sums over all 128 entries: this lane's 32 + the other quarters'
     float sr = 0.f, ss = 0.f;

@@ -128,7 +128,8 @@ DecodeWorkspace decode_workspace(const kv_layout* L, int num_q_heads, int splits
   size_t rows = (size_t)L->batch * num_q_heads;
   w.cnt_off = 0;
   w.qprep_off = align((size_t)L->batch * L->num_kv_heads * sizeof(unsigned));
-  w.part_off = w.qprep_off + align(rows * prepared_query_width(L) * sizeof(float));
+  w.qpiece_off = w.qprep_off + align(rows * prepared_query_width(L) * sizeof(float));
+  w.part_off = w.qpiece_off + align(L->format == KV_FMT_TURBO ? rows * (size_t)kTurboPieceBytes : 0);
   w.total = w.part_off + align(rows * (size_t)splits * (value_width(L) + 2) * sizeof(float));
   return w;
 }

@@ -42,8 +42,11 @@ SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int q_dtype, int max_
 // Workspace of a decode call: prepared queries, then per-split partial results
 // (running max, running sum, unnormalised output) — offsets in bytes.
 struct DecodeWorkspace {
-  size_t qprep_off, part_off, cnt_off, total;
+  size_t qprep_off, qpiece_off, part_off, cnt_off, total;
 };
+// Bytes per query row of the TurboQuant query pieces (FP8 operands of the key
+// products): 3 products x 4 pieces x (4 blocks x 32 bytes + 4 scale bytes + 12).
+constexpr int kTurboPieceBytes = 3 * 4 * 144;
 DecodeWorkspace decode_workspace(const kv_layout* L, int num_q_heads, int splits);
 
 // Device launchers (defined in the HIP translation units).  Arguments are
