@@ -224,25 +224,27 @@ __device__ __forceinline__ uint32_t e4m3_code(float y, float& val) {
   return (sgn >> 24) | (ef << 3) | ((u >> 20) & 7u);
 }
 
-// TurboQuant query pieces.  The key products take the key bits as FP4 operands
-// (one bit per nibble) against FP8 operands with a power-of-two scale per block
-// of 32 (v_mfma_scale_f32_16x16x128_f8f6f4).  Block j (element e = 8 d + n, the
-// bit 4 n + d of one key word) of
-//   product 0 / 1 (code words 4 m + j, m = 0 / 1): the coefficient of bit d % 2
-//     (a2 for the low bit b0, a1 for the high bit b1) times (R q)[16 (4 m + j) +
-//     2 n + d / 2];
-//   product 2 (sketch dword j): (S R q)[32 j + 4 n + d].
+// Query pieces of the bit-key products (TurboQuant, QJL).  The key products
+// take the key bits as FP4 operands (one bit per nibble) against FP8 operands
+// with a power-of-two scale per block of 32 (v_mfma_scale_f32_16x16x128_f8f6f4).
+// Block j (element e = 8 d + n, the bit 4 n + d of one key word) of
+//   TURBO product 0 / 1 (code words 4 m + j, m = 0 / 1): the coefficient of
+//     bit d % 2 (a2 for the low bit b0, a1 for the high bit b1) times
+//     (R q)[16 (4 m + j) + 2 n + d / 2];
+//   TURBO product 2, QJL product 0 (sketch dword j): (S R q or S q)[32 j + 4 n + d].
 // Each block is split into 4 FP8 pieces: piece p holds the nearest E4M3 of the
 // residual left by pieces < p, at a scale 2^e that puts the residual's largest
 // magnitude in [64, 128), so the pieces' sum is within 2^-20 of the block's
 // largest value.  Layout per (product, piece): 4 blocks x 32 code bytes, then
-// the 4 blocks' E8M0 scale bytes (e + 127), 144 bytes in all.
-__device__ void prepared_query_pieces(const float* qrot, const float* qsr, float a1, float a2, uint8_t* out) {
+// the 4 blocks' E8M0 scale bytes (e + 127), 144 bytes in all.  128 threads.
+__device__ void prepared_query_pieces(int nprod, const float* qrot, const float* qsk, float a1, float a2,
+                                      uint8_t* out) {
   const int tid = threadIdx.x, e = tid & 31, d = e >> 3, n = e & 7;
-  for (int blk = tid >> 5; blk < 12; blk += 4) {
-    const int prod = blk < 8 ? blk >> 2 : 2, j = blk < 8 ? blk & 3 : blk - 8;
-    float r = blk < 8 ? ((d & 1) ? a1 : a2) * qrot[16 * (4 * prod + j) + 2 * n + (d >> 1)]
-                      : qsr[32 * j + 4 * n + d];
+  for (int blk = tid >> 5; blk < 4 * nprod; blk += 4) {
+    const int prod = blk >> 2, j = blk & 3;
+    const bool code = prod < nprod - 1;
+    float r = code ? ((d & 1) ? a1 : a2) * qrot[16 * (4 * prod + j) + 2 * n + (d >> 1)]
+                   : qsk[32 * j + 4 * n + d];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       float M = fabsf(r);
@@ -255,17 +257,17 @@ __device__ void prepared_query_pieces(const float* qrot, const float* qsr, float
         ex = k - 7;
       }
       float val;
-      const uint32_t code = e4m3_code(ldexpf(r, -ex), val);
+      const uint32_t c8 = e4m3_code(ldexpf(r, -ex), val);
       r -= ldexpf(val, ex);
       uint8_t* dst = out + (prod * 4 + p) * 144;
-      dst[j * 32 + e] = (uint8_t)code;
+      dst[j * 32 + e] = (uint8_t)c8;
       if (e == 0) dst[128 + j] = (uint8_t)(ex + 127);
     }
   }
 }
 
-// Prepared fp32 query: q itself, or [R q, S R q] (TURBO, with its FP8 pieces
-// when `pieces` is given), or S q (QJL1).
+// Prepared fp32 query: q itself, or [R q, S R q] (TURBO), or S q (QJL1); for
+// the last two also the FP8 pieces of the key products when `pieces` is given.
 template <typename QT>
 __global__ void __launch_bounds__(128) prep_query_kernel(const QT* __restrict__ q, int qw_in, int qw_out,
                                                          int fmt, const float* __restrict__ rot,
@@ -292,13 +294,18 @@ __global__ void __launch_bounds__(128) prep_query_kernel(const QT* __restrict__ 
     if (pieces) {
       qsr[tid] = acc2;
       __syncthreads();
-      prepared_query_pieces(qrot, qsr, levels[2] - levels[0], levels[1] - levels[0],
+      prepared_query_pieces(3, qrot, qsr, levels[2] - levels[0], levels[1] - levels[0],
                             pieces + row * kTurboPieceBytes);
     }
   } else if (fmt == KV_FMT_QJL1_FP4V) {
     float acc = 0.f;
     for (int j = 0; j < 128; ++j) acc = fmaf(proj[tid * 128 + j], qin[j], acc);
     dst[tid] = acc;
+    if (pieces) {
+      qsr[tid] = acc;
+      __syncthreads();
+      prepared_query_pieces(1, nullptr, qsr, 0.f, 0.f, pieces + row * kQjlPieceBytes);
+    }
   } else {
     for (int c = tid; c < qw_out; c += 128) dst[c] = qin[c];
   }
@@ -479,7 +486,9 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
   const bool mfma = mfma_fast_path_ok(L, num_q_heads, q_dtype);
   // FP4 keys read the caller's bf16 queries as they are; every other format
   // first prepares its fp32 query (projection / rotation)
-  uint8_t* qpieces = turbo_fast_path_ok(L, num_q_heads) ? reinterpret_cast<uint8_t*>(wsb + wsl.qpiece_off) : nullptr;
+  uint8_t* qpieces = turbo_fast_path_ok(L, num_q_heads) || (mfma && L.format == KV_FMT_QJL1_FP4V)
+                         ? reinterpret_cast<uint8_t*>(wsb + wsl.qpiece_off)
+                         : nullptr;
   if (!(mfma && L.format == KV_FMT_FP4)) {
     if (q_dtype == KV_DT_F32)
       prep_query_kernel<float><<<rows, 128, 0, st>>>(static_cast<const float*>(q), qw_in, qw_out, L.format,
@@ -525,6 +534,7 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     f.v_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_V_CODES]);
     f.v_scale = static_cast<const uint16_t*>(c->buf[KV_BUF_V_SCALE]);
     f.q = L.format == KV_FMT_FP4 ? q : static_cast<const void*>(qv);
+    f.qpieces = qpieces;
     f.seq_lens = seq_lens;
     f.max_len = max_seq_len;
     f.H = L.num_kv_heads;

@@ -35,6 +35,7 @@ namespace kvq {
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef int i8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 namespace {
@@ -72,12 +73,28 @@ __device__ __forceinline__ h8_t dequant8(uint32_t w, h2_t s) {
   return h8_from(fp4x2<0>(w) * s, fp4x2<1>(w) * s, fp4x2<2>(w) * s, fp4x2<3>(w) * s);
 }
 
-// The 8 bits at positions 0, 4, ..., 28 of m as fp16 1.0 / 0 (element n <- bit
-// 4n): the FP4 converter reads a nibble holding only its low bit as 0.5, scaled
-// by 2.
-__device__ __forceinline__ h8_t bits8(uint32_t m) {
-  return h8_from(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 2.0f, 0), __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 2.0f, 1),
-                 __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 2.0f, 2), __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 2.0f, 3));
+// One bit per nibble of a 32-bit key word, as the FP4 operand of a scaled
+// product: dword d holds bits d, d + 4, ..., d + 28 (element 8 d + n = bit 4 n + d).
+__device__ __forceinline__ i8_t bit_nibbles(uint32_t w) {
+  const uint32_t m = 0x11111111u;
+  return i8_t{(int)(w & m), (int)((w >> 1) & m), (int)((w >> 2) & m), (int)((w >> 3) & m), 0, 0, 0, 0};
+}
+
+// v_mfma_scale_f32_16x16x128_f8f6f4: A = key bits (FP4, 0 or 0.5, block scale
+// 2), B = FP8 pieces with their block scales.  A lane quarter's 32 elements
+// form one k-block; B lane quarter qb holds k-blocks qb / 2 and 2 + qb / 2
+// (elements 16 (qb % 2) .. + 15 of each) and the scale of k-block qb.
+__device__ __forceinline__ f4_t key_product(i8_t a, i8_t b, int scale_b, f4_t acc) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 4, 0, 0, 128, 0, scale_b);
+}
+
+// x of lane (l & ~15) | ((l + N) & 15), 0 < N < 16: DPP row_ror:(16 - N) (a
+// rotation right by k hands lane l the value of lane l - k within its row).
+template <int N>
+__device__ __forceinline__ float row_fetch(float x) {
+  static_assert(N > 0 && N < 16, "rotation within a 16-lane row");
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x120 + (16 - N), 0xF, 0xF, false));
 }
 
 // A-operand row c of a 16-token block holds token 4*(c%4) + c/4, so that the
@@ -100,7 +117,8 @@ struct KeysFp4 {
     uint4 kw[2];
     uint32_t s2[2];
   };
-  __device__ static void load_q(Q& q, const MfmaDecodeArgs& a, int b, int h, int G, int q4, int c) {
+  template <int G>
+  __device__ static void load_q(Q& q, const MfmaDecodeArgs& a, int b, int h, int q4, int c) {
     const int head = c < G ? c : 0;
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G + head) * 128 + 32 * q4;
 #pragma unroll
@@ -150,13 +168,21 @@ struct KeysFp4 {
   }
 };
 
-// 1-bit QJL keys: 128 sketch bits (16 B per token) and the fp16 key norm.
+// 1-bit QJL keys: 128 sketch bits (16 B per token) and the fp16 key norm.  The
+// key product runs on the scaled FP4 x FP8 instruction: A = the token's sketch
+// bits (lane quarter q4: sketch dword q4, one bit per nibble), B = FP8 pieces of
+// S q (4 pieces, prepared once per decode).  Column c carries piece c / G of
+// head c % G while pieces fit (16 / G of them per product), so 4 / (16 / G)
+// products (1 for G <= 4) cover the 4 pieces, and rotations within each 16-lane
+// row add a head's pieces onto its column.
 struct KeysQjl {
   static constexpr int kBytes = 768;  // sketch 512 | norms, one per dword: 128 (+ 128 zeros)
   static constexpr int kDma = 3;      // direct-to-LDS loads issue() makes
+  template <int G>
+  static constexpr int kSlots = G >= 16 ? 1 : (G >= 8 ? 2 : 4);  // pieces per product
   struct Q {
-    // lane (q4, c): head c; MFMA i, k-slot j <-> sketch row 32*q4 + 4*j + i
-    h8_t hi[4], lo[4];
+    i8_t bq[4];  // B operands of up to 4 products
+    int bs[4];   // their block scales
     float sumq;  // sum of the head's 128 projected-query values
   };
   struct R {
@@ -167,20 +193,28 @@ struct KeysQjl {
     uint32_t w[2];   // sketch rows 32*q4 .. 32*q4 + 31 of token row_token(c)
     uint32_t n[8];   // fp16 norm bits of tokens 16 blk + 4 v + q4
   };
-  __device__ static void load_q(Q& q, const MfmaDecodeArgs& a, int b, int h, int G, int q4, int c) {
-    const int head = c < G ? c : 0;
-    const float* qp = static_cast<const float*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G + head) * 128 + 32 * q4;
+  template <int G>
+  __device__ static void load_q(Q& q, const MfmaDecodeArgs& a, int b, int h, int q4, int c) {
+    constexpr int NS = kSlots<G>, NP = 4 / NS;
+    const int slot = c / G;
+    const bool live = slot < NS;
+    const size_t qrow = (size_t)b * a.Hq + (size_t)h * G + c % G;
+    const uint8_t* pc = a.qpieces + qrow * kQjlPieceBytes;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int p = i * NS + (live ? slot : 0);
+      const uint8_t* base = pc + p * 144 + 16 * (q4 & 1);
+      const uint4 lo4 = *reinterpret_cast<const uint4*>(base + 32 * (q4 >> 1));
+      const uint4 hi4 = *reinterpret_cast<const uint4*>(base + 32 * (2 + (q4 >> 1)));
+      q.bq[i] = live ? i8_t{(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w, (int)hi4.x, (int)hi4.y, (int)hi4.z,
+                            (int)hi4.w}
+                     : i8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      q.bs[i] = live ? (int)pc[p * 144 + 128 + q4] : 127;
+    }
+    const float* qp = static_cast<const float*>(a.q) + qrow * 128 + 32 * q4;
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float v = c < G ? qp[4 * j + i] : 0.f;
-        const _Float16 hi = (_Float16)v;
-        q.hi[i][j] = hi;
-        q.lo[i][j] = (_Float16)(v - (float)hi);
-        s += v;
-      }
+    for (int x = 0; x < 32; ++x) s += qp[x];
     s += __shfl_xor(s, 16);
     s += __shfl_xor(s, 32);
     q.sumq = s;
@@ -208,22 +242,23 @@ struct KeysQjl {
 #pragma unroll
     for (int j = 0; j < 8; ++j) f.n[j] = *reinterpret_cast<const uint16_t*>(st + no + 16 * j);
   }
+  template <int G>
   __device__ static void logits(const Frag& f, const Q& q, float kappa, f4_t sacc[2]) {
+    constexpr int NS = kSlots<G>, NP = 4 / NS;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      const uint32_t w = f.w[blk];
+      const i8_t A = bit_nibbles(f.w[blk]);
       f4_t acc = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const h8_t A = bits8((w >> i) & 0x11111111u);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, q.hi[i], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, q.lo[i], acc, 0, 0, 0);
-      }
+      for (int i = 0; i < NP; ++i) acc = key_product(A, q.bq[i], q.bs[i], acc);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
+        float x = acc[v];
+        if constexpr (NS >= 2) x += row_fetch<G>(x);      // + column c + G
+        if constexpr (NS >= 4) x += row_fetch<2 * G>(x);  // + columns c + 2G, c + 3G
         const float n = f16_to_f32((uint16_t)f.n[4 * blk + v]);
-        // acc = <S q, b>: <S q, sigma> = 2 acc - sum(S q)
-        acc[v] = kappa * n * fmaf(2.f, acc[v], -q.sumq);
+        // x = <S q, b>: <S q, sigma> = 2 x - sum(S q)
+        acc[v] = kappa * n * fmaf(2.f, x, -q.sumq);
       }
       sacc[blk] = acc;
     }
@@ -232,18 +267,15 @@ struct KeysQjl {
 
 // ---------------------------------------------------------------- the kernel
 
-template <class KP>
-__device__ __forceinline__ void logits_of(const typename KP::Frag& f, const typename KP::Q& q,
-                                          const MfmaDecodeArgs& a, f4_t sacc[2]);
-template <>
-__device__ __forceinline__ void logits_of<KeysFp4>(const KeysFp4::Frag& f, const KeysFp4::Q& q,
-                                                   const MfmaDecodeArgs&, f4_t sacc[2]) {
+template <int G>
+__device__ __forceinline__ void logits_of(const KeysFp4::Frag& f, const KeysFp4::Q& q, const MfmaDecodeArgs&,
+                                          f4_t sacc[2]) {
   KeysFp4::logits(f, q, sacc);
 }
-template <>
-__device__ __forceinline__ void logits_of<KeysQjl>(const KeysQjl::Frag& f, const KeysQjl::Q& q,
-                                                   const MfmaDecodeArgs& a, f4_t sacc[2]) {
-  KeysQjl::logits(f, q, a.kappa, sacc);
+template <int G>
+__device__ __forceinline__ void logits_of(const KeysQjl::Frag& f, const KeysQjl::Q& q, const MfmaDecodeArgs& a,
+                                          f4_t sacc[2]) {
+  KeysQjl::logits<G>(f, q, a.kappa, sacc);
 }
 
 // V region of a stage (after the keys): codes 2048 | scales 512.
@@ -312,7 +344,7 @@ __device__ __forceinline__ void tile_step(WaveState<KP>& w, uint8_t* st, int lan
 
   // ---------------- logits: S^T = K Q^T for the two 16-token blocks
   f4_t sacc[2];
-  logits_of<KP>(kf, w.q, a, sacc);
+  logits_of<G>(kf, w.q, a, sacc);
   // ---------------- online softmax (this lane: head c, tokens t0 + 16*blk + 4*v + q4)
   float sv[8];
   float tmax = -INFINITY;
@@ -444,7 +476,7 @@ __attribute__((amdgpu_waves_per_eu(KVQ_MFMA_WAVES_PER_EU, KVQ_MFMA_WAVES_PER_EU)
   const int t_end = min(L, t_begin + a.per_split);
 
   WaveState<KP> w;
-  KP::load_q(w.q, a, b, h, G, lane >> 4, lane & 15);
+  KP::template load_q<G>(w.q, a, b, h, lane >> 4, lane & 15);
   w.m_run = -INFINITY;
   w.l_run = 0.f;
 #pragma unroll

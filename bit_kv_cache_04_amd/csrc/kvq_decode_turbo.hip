@@ -70,7 +70,7 @@ __device__ __forceinline__ h8_t bits8(uint32_t m) {
 }
 
 // Value of lane (l & ~15) | ((l + 8) & 15): the other half of this lane's
-// 16-lane row (a DPP row rotation by 8).
+// 16-lane row (a DPP row rotation by 8, the same in either direction).
 __device__ __forceinline__ float row_ror8(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
 }

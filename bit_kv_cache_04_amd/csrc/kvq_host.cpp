@@ -129,7 +129,9 @@ DecodeWorkspace decode_workspace(const kv_layout* L, int num_q_heads, int splits
   w.cnt_off = 0;
   w.qprep_off = align((size_t)L->batch * L->num_kv_heads * sizeof(unsigned));
   w.qpiece_off = w.qprep_off + align(rows * prepared_query_width(L) * sizeof(float));
-  w.part_off = w.qpiece_off + align(L->format == KV_FMT_TURBO ? rows * (size_t)kTurboPieceBytes : 0);
+  const size_t piece_bytes = L->format == KV_FMT_TURBO ? kTurboPieceBytes
+                            : L->format == KV_FMT_QJL1_FP4V ? kQjlPieceBytes : 0;
+  w.part_off = w.qpiece_off + align(rows * piece_bytes);
   w.total = w.part_off + align(rows * (size_t)splits * (value_width(L) + 2) * sizeof(float));
   return w;
 }

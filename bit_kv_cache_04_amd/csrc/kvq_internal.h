@@ -44,9 +44,11 @@ SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int q_dtype, int max_
 struct DecodeWorkspace {
   size_t qprep_off, qpiece_off, part_off, cnt_off, total;
 };
-// Bytes per query row of the TurboQuant query pieces (FP8 operands of the key
-// products): 3 products x 4 pieces x (4 blocks x 32 bytes + 4 scale bytes + 12).
-constexpr int kTurboPieceBytes = 3 * 4 * 144;
+// FP8 pieces of the query operand of a bit-key product (TurboQuant, QJL):
+// per product, 4 pieces x (4 blocks x 32 code bytes + 4 scale bytes + 12).
+constexpr int kPieceProductBytes = 4 * 144;
+constexpr int kTurboPieceBytes = 3 * kPieceProductBytes;  // code words 0..3, 4..7, sketch
+constexpr int kQjlPieceBytes = kPieceProductBytes;        // sketch
 DecodeWorkspace decode_workspace(const kv_layout* L, int num_q_heads, int splits);
 
 // Device launchers (defined in the HIP translation units).  Arguments are

@@ -19,6 +19,7 @@ struct MfmaDecodeArgs {
   const uint16_t* v_scale;  // [B][H][cap][8] bf16
   const uint16_t* rope;     // latent: [B][cap][64] bf16 (k_codes [B][cap][256], k_scale [B][cap][32])
   const void* q;            // FP4: bf16 [B][Hq][128]; QJL: fp32 S q [B][Hq][128]
+  const uint8_t* qpieces;   // QJL: [B][Hq][kQjlPieceBytes], FP8 pieces of S q
   const int32_t* seq_lens;
   int max_len, H, cap, Hq;
   float scale_log2;  // softmax scale * log2(e)
