@@ -236,11 +236,12 @@ __device__ __forceinline__ uint32_t e4m3_code(float y, float& val) {
 // residual left by pieces < p, at a scale 2^e that puts the residual's largest
 // magnitude in [64, 128), so the pieces' sum is within 2^-20 of the block's
 // largest value.  Layout per (product, piece): 4 blocks x 32 code bytes, then
-// the 4 blocks' E8M0 scale bytes (e + 127), 144 bytes in all.  128 threads.
+// the 4 blocks' E8M0 scale bytes (e + 127), 144 bytes in all.  32 threads per
+// block, as many blocks at a time as the workgroup has threads for.
 __device__ void prepared_query_pieces(int nprod, const float* qrot, const float* qsk, float a1, float a2,
                                       uint8_t* out) {
   const int tid = threadIdx.x, e = tid & 31, d = e >> 3, n = e & 7;
-  for (int blk = tid >> 5; blk < 4 * nprod; blk += 4) {
+  for (int blk = tid >> 5; blk < 4 * nprod; blk += (int)(blockDim.x >> 5)) {
     const int prod = blk >> 2, j = blk & 3;
     const bool code = prod < nprod - 1;
     float r = code ? ((d & 1) ? a1 : a2) * qrot[16 * (4 * prod + j) + 2 * n + (d >> 1)]
@@ -268,8 +269,10 @@ __device__ void prepared_query_pieces(int nprod, const float* qrot, const float*
 
 // Prepared fp32 query: q itself, or [R q, S R q] (TURBO), or S q (QJL1); for
 // the last two also the FP8 pieces of the key products when `pieces` is given.
+// 128 threads, or 384 for TURBO pieces (all 12 blocks at once); the products
+// take one output per thread of the first 128.
 template <typename QT>
-__global__ void __launch_bounds__(128) prep_query_kernel(const QT* __restrict__ q, int qw_in, int qw_out,
+__global__ void __launch_bounds__(384) prep_query_kernel(const QT* __restrict__ q, int qw_in, int qw_out,
                                                          int fmt, const float* __restrict__ rot,
                                                          const float* __restrict__ proj,
                                                          const float* __restrict__ levels,
@@ -278,36 +281,43 @@ __global__ void __launch_bounds__(128) prep_query_kernel(const QT* __restrict__ 
   __shared__ float qrot[128];
   __shared__ float qsr[128];
   const size_t row = blockIdx.x;
-  const int tid = threadIdx.x;
-  for (int c = tid; c < qw_in; c += 128) qin[c] = load_as_f32(q + row * qw_in, c);
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const bool prod = tid < 128;
+  for (int c = tid; c < qw_in; c += nthr) qin[c] = load_as_f32(q + row * qw_in, c);
   __syncthreads();
   float* dst = out + row * qw_out;
   if (fmt == KV_FMT_TURBO) {
-    float acc = 0.f;
-    for (int j = 0; j < 128; ++j) acc = fmaf(rot[tid * 128 + j], qin[j], acc);
-    qrot[tid] = acc;
-    dst[tid] = acc;
+    if (prod) {
+      float acc = 0.f;
+      for (int j = 0; j < 128; ++j) acc = fmaf(rot[tid * 128 + j], qin[j], acc);
+      qrot[tid] = acc;
+      dst[tid] = acc;
+    }
     __syncthreads();
-    float acc2 = 0.f;
-    for (int j = 0; j < 128; ++j) acc2 = fmaf(proj[tid * 128 + j], qrot[j], acc2);
-    dst[128 + tid] = acc2;
-    if (pieces) {
+    if (prod) {
+      float acc2 = 0.f;
+      for (int j = 0; j < 128; ++j) acc2 = fmaf(proj[tid * 128 + j], qrot[j], acc2);
+      dst[128 + tid] = acc2;
       qsr[tid] = acc2;
+    }
+    if (pieces) {
       __syncthreads();
       prepared_query_pieces(3, qrot, qsr, levels[2] - levels[0], levels[1] - levels[0],
                             pieces + row * kTurboPieceBytes);
     }
   } else if (fmt == KV_FMT_QJL1_FP4V) {
-    float acc = 0.f;
-    for (int j = 0; j < 128; ++j) acc = fmaf(proj[tid * 128 + j], qin[j], acc);
-    dst[tid] = acc;
-    if (pieces) {
+    if (prod) {
+      float acc = 0.f;
+      for (int j = 0; j < 128; ++j) acc = fmaf(proj[tid * 128 + j], qin[j], acc);
+      dst[tid] = acc;
       qsr[tid] = acc;
+    }
+    if (pieces) {
       __syncthreads();
       prepared_query_pieces(1, nullptr, qsr, 0.f, 0.f, pieces + row * kQjlPieceBytes);
     }
   } else {
-    for (int c = tid; c < qw_out; c += 128) dst[c] = qin[c];
+    for (int c = tid; c < qw_out; c += nthr) dst[c] = qin[c];
   }
 }
 
@@ -490,11 +500,12 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
                          ? reinterpret_cast<uint8_t*>(wsb + wsl.qpiece_off)
                          : nullptr;
   if (!(mfma && L.format == KV_FMT_FP4)) {
+    const int prep_threads = qpieces && L.format == KV_FMT_TURBO ? 384 : 128;
     if (q_dtype == KV_DT_F32)
-      prep_query_kernel<float><<<rows, 128, 0, st>>>(static_cast<const float*>(q), qw_in, qw_out, L.format,
+      prep_query_kernel<float><<<rows, prep_threads, 0, st>>>(static_cast<const float*>(q), qw_in, qw_out, L.format,
                                                      c->rot, c->proj, c->lm_levels, qv, qpieces);
     else
-      prep_query_kernel<uint16_t><<<rows, 128, 0, st>>>(static_cast<const uint16_t*>(q), qw_in, qw_out,
+      prep_query_kernel<uint16_t><<<rows, prep_threads, 0, st>>>(static_cast<const uint16_t*>(q), qw_in, qw_out,
                                                         L.format, c->rot, c->proj, c->lm_levels, qv, qpieces);
   }
   if (turbo_fast_path_ok(L, num_q_heads)) {
