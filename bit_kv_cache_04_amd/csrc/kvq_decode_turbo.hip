@@ -10,17 +10,16 @@
 // A symmetric 4-level codebook (levels -l2, -l1, l1, l2 by code 0..3) makes a
 // code's level linear in its two bits b1 (high) and b0 (low):
 //   level = a0 + a1 b1 + a2 b0,  a0 = lv0, a1 = lv2 - lv0, a2 = lv1 - lv0,
-// because the b1 b0 term, lv3 - lv2 - lv1 + lv0, vanishes.  So both products
-// become exact 0/1 bit-plane products on the matrix cores:
+// because the b1 b0 term, lv3 - lv2 - lv1 + lv0, vanishes.  So the key
+// products become exact 0/1 bit-plane products on the matrix cores:
 //   <q, u~>      = a0 sum(q) + <a1 q, b1> + <a2 q, b0>
 //   <qS, sigma>  = 2 <qS, b> - sum(qS)
-//   O            = a0 sum(P') + (a1 P') B1 + (a2 P') B0,   P' = p n_v
-// Bits enter v_mfma_f32_16x16x32_f16 as the fp16 value 1.0 or 0 (the FP4
-// converter turns a nibble holding one set low bit into 0.5, scaled by 2);
-// the fp32 query side is split into fp16 hi + lo parts carried in MFMA columns
-// G..G+7 (G <= 8 query heads share a KV head), so the key products are exact up
-// to fp32 accumulation.  Value codes are transposed to token-major bit planes by
-// ds_read_b64_tr_b4 (a 16 x 16 nibble transpose within each 16-lane group).
+// (key bits as FP4 operands against FP8 pieces of the query side, below).  The
+// value product O = P' V~, P' = p n_v, takes each value code's level itself as
+// an fp16 operand of v_mfma_f32_16x16x32_f16: two byte permutes look a code up
+// in a table of the four levels' low and high bytes.  Value codes are transposed
+// to token-major order by ds_read_b64_tr_b4 (a 16 x 16 nibble transpose within
+// each 16-lane group).
 //
 // Layout per workgroup, as in the FP4 kernel: 4 waves, each streaming its own
 // 32-token tiles through a two-stage LDS ring filled by direct-to-LDS loads,
@@ -57,16 +56,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, size_t 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcFlags);
 }
 
-// 8 bits at positions 0, 4, ..., 28 of m as fp16 1.0 / 0 (element n <- bit 4n)
-__device__ __forceinline__ h8_t bits8(uint32_t m) {
-  h8_t r;
-  const h2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 2.0f, 0);
-  const h2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 2.0f, 1);
-  const h2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 2.0f, 2);
-  const h2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 2.0f, 3);
-  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-  return r;
+// fp16 levels of the 8 two-bit codes at bits [s, s + 2) of the nibbles of w,
+// in the value product's k-slot order: nibbles 0, 2, 4, 6, 1, 3, 5, 7.
+// v_perm_b32 picks byte k of the pair {src0 : src1} (bytes 4..7 from src0):
+// the first permute turns codes c, c' into the selector (c, c + 4, c', c' + 4),
+// the second reads the low and high bytes of levels c and c' from the tables.
+__device__ __forceinline__ h8_t levels8(uint32_t w, int s, uint32_t t_lo, uint32_t t_hi) {
+  const uint32_t e = (w >> s) & 0x03030303u, o = (w >> (s + 4)) & 0x03030303u;
+  const uint32_t e4 = e | 0x04040404u, o4 = o | 0x04040404u;
+  const uint4 d{__builtin_amdgcn_perm(t_hi, t_lo, __builtin_amdgcn_perm(e4, e, 0x05010400u)),
+                __builtin_amdgcn_perm(t_hi, t_lo, __builtin_amdgcn_perm(e4, e, 0x07030602u)),
+                __builtin_amdgcn_perm(t_hi, t_lo, __builtin_amdgcn_perm(o4, o, 0x05010400u)),
+                __builtin_amdgcn_perm(t_hi, t_lo, __builtin_amdgcn_perm(o4, o, 0x07030602u))};
+  return __builtin_bit_cast(h8_t, d);
 }
 
 // Value of lane (l & ~15) | ((l + 8) & 15): the other half of this lane's
@@ -103,7 +105,8 @@ __device__ __forceinline__ void issue_tile(uint8_t* st, int lane, int t0, const 
 }
 
 struct Consts {
-  float a0, a1, a2;  // level = a0 + a1 b1 + a2 b0
+  float a0;            // level of code 0
+  uint32_t t_lo, t_hi;  // low / high bytes of the four levels as fp16, byte c for code c
 };
 
 // One bit per nibble of a key word, as the FP4 operand of a scaled product:
@@ -130,7 +133,7 @@ struct WaveState {
   int bs[3][2];  // their block scales
   float cst;     // a0 * sum(R q) for this lane's head
   float sqs;     // sum(S R q)
-  float m_run, l_run, sp;  // running max, sum of p, sum of p * n_v
+  float m_run, l_run;  // running max, sum of p
   f4_t o[8];
 };
 
@@ -209,35 +212,26 @@ __device__ __forceinline__ void tile_step(WaveState<G>& w, uint8_t* st, int lane
   const bool bump = tmax > w.m_run + 8.f;
   const float m_new = bump ? tmax : w.m_run;
   const float alpha = bump ? __builtin_amdgcn_exp2f(w.m_run - m_new) : 1.f;
-  float psum = 0.f, spsum = 0.f;
-  uint32_t own1[2], own0[2];  // this lane's 4 weights times a1 / a2, as fp16 pairs
+  float psum = 0.f, pv[4];
 #pragma unroll
-  for (int v = 0; v < 4; v += 2) {
-    float pv[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const float p = __builtin_amdgcn_exp2f(sv[v + e] - m_new);
-      pv[e] = p * f16_to_f32((uint16_t)(&nv.x)[v + e]);
-      psum += p;
-      spsum += pv[e];
-    }
-    // round to nearest (a truncating pack would bias every weight low)
-    own1[v / 2] = __builtin_bit_cast(uint32_t, h2_t{(_Float16)(pv[0] * k.a1), (_Float16)(pv[1] * k.a1)});
-    own0[v / 2] = __builtin_bit_cast(uint32_t, h2_t{(_Float16)(pv[0] * k.a2), (_Float16)(pv[1] * k.a2)});
+  for (int v = 0; v < 4; ++v) {
+    const float p = __builtin_amdgcn_exp2f(sv[v] - m_new);
+    pv[v] = p * f16_to_f32((uint16_t)(&nv.x)[v]);
+    psum += p;
   }
+  // this lane's 4 weights P' as fp16 pairs (tokens 0 and 2, 1 and 3 of its 4),
+  // rounded to nearest (a truncating pack would bias every weight low)
+  const uint32_t own02 = __builtin_bit_cast(uint32_t, h2_t{(_Float16)pv[0], (_Float16)pv[2]});
+  const uint32_t own13 = __builtin_bit_cast(uint32_t, h2_t{(_Float16)pv[1], (_Float16)pv[3]});
   w.l_run = w.l_run * alpha + psum;
-  w.sp = w.sp * alpha + spsum;
   w.m_run = m_new;
   // PV A operand of row c (head c for c < 8): tokens 8 q4 + [0, 8) = this lane's
-  // 4 and the partner column's 4 (rows 8..15 are not heads and are discarded)
-  h8_t p1, p0;
+  // 4 and the partner column's 4 in the k-slot order of levels8 (0, 2, 4, 6, 1,
+  // 3, 5, 7); rows 8..15 are not heads and are discarded
+  h8_t pa;
   {
-    const uint32_t o1a = row_ror8(own1[0]), o1b = row_ror8(own1[1]);
-    const uint32_t o0a = row_ror8(own0[0]), o0b = row_ror8(own0[1]);
-    const uint4 w1 = upper ? uint4{o1a, o1b, own1[0], own1[1]} : uint4{own1[0], own1[1], o1a, o1b};
-    const uint4 w0 = upper ? uint4{o0a, o0b, own0[0], own0[1]} : uint4{own0[0], own0[1], o0a, o0b};
-    p1 = __builtin_bit_cast(h8_t, w1);
-    p0 = __builtin_bit_cast(h8_t, w0);
+    const uint32_t oth02 = row_ror8(own02), oth13 = row_ror8(own13);
+    pa = __builtin_bit_cast(h8_t, upper ? uint4{oth02, own02, oth13, own13} : uint4{own02, oth02, own13, oth13});
   }
   if (__ballot(bump && c < G)) {
 #pragma unroll
@@ -247,17 +241,15 @@ __device__ __forceinline__ void tile_step(WaveState<G>& w, uint8_t* st, int lane
       for (int nt = 0; nt < 8; ++nt) w.o[nt][v] *= av;
     }
   }
-  // ---- values: N-tile nt = 2 chunk + parity; column c <-> channel 32 chunk + 2 c + parity
+  // ---- values: N-tile nt = 2 chunk + parity; column c <-> channel 32 chunk + 2 c + parity,
+  // whose code is bits [2 parity, 2 parity + 2) of each nibble (nibble n = token 8 q4 + n)
   const uint32_t vx[4] = {(uint32_t)vx0[0], (uint32_t)vx0[1], (uint32_t)vx1[0], (uint32_t)vx1[1]};
 #pragma unroll
   for (int ch = 0; ch < 4; ++ch) {
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
       const int nt = 2 * ch + par;
-      w.o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p1, bits8((vx[ch] >> (2 * par + 1)) & 0x11111111u), w.o[nt], 0,
-                                                      0, 0);
-      w.o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p0, bits8((vx[ch] >> (2 * par)) & 0x11111111u), w.o[nt], 0, 0,
-                                                      0);
+      w.o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, levels8(vx[ch], 2 * par, k.t_lo, k.t_hi), w.o[nt], 0, 0, 0);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -287,10 +279,15 @@ __attribute__((amdgpu_waves_per_eu(KVQ_TURBO_WAVES_PER_EU, KVQ_TURBO_WAVES_PER_E
 
   Consts k;
   {
-    const float lv0 = a.levels[0], lv1 = a.levels[1], lv2 = a.levels[2];
-    k.a0 = lv0;
-    k.a1 = lv2 - lv0;
-    k.a2 = lv1 - lv0;
+    k.a0 = a.levels[0];
+    k.t_lo = 0;
+    k.t_hi = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t hb = __builtin_bit_cast(uint16_t, (_Float16)a.levels[c]);
+      k.t_lo |= (hb & 0xFFu) << (8 * c);
+      k.t_hi |= (hb >> 8) << (8 * c);
+    }
   }
   WaveState<G> w;
   {
@@ -330,7 +327,6 @@ __attribute__((amdgpu_waves_per_eu(KVQ_TURBO_WAVES_PER_EU, KVQ_TURBO_WAVES_PER_E
   }
   w.m_run = -INFINITY;
   w.l_run = 0.f;
-  w.sp = 0.f;
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) w.o[nt] = f4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -359,27 +355,22 @@ __attribute__((amdgpu_waves_per_eu(KVQ_TURBO_WAVES_PER_EU, KVQ_TURBO_WAVES_PER_E
   const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   const int q4e = lane_e >> 4, ce = lane_e & 15;
   const int tid_e = wave * 64 + lane_e;
-  float l_run = w.l_run, sp = w.sp;
+  float l_run = w.l_run;
   l_run += row_ror8(l_run);  // the two column halves scored disjoint tokens
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  sp += row_ror8(sp);
-  sp += __shfl_xor(sp, 16);
-  sp += __shfl_xor(sp, 32);
   if (q4e == 0) {
     sm_m[wave][ce] = w.m_run;
     sm_l[wave][ce] = l_run;
   }
-  // the a0 sum(P') term of every output channel, for the head of each O row
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int hh = 4 * q4e + v;
-    const float base = k.a0 * __shfl(sp, hh & 15);
     if (hh < G) {
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
         const int ch = 32 * (nt >> 1) + 2 * ce + (nt & 1);
-        sm_o[wave][hh][ch] = w.o[nt][v] + base;
+        sm_o[wave][hh][ch] = w.o[nt][v];
       }
     }
   }
