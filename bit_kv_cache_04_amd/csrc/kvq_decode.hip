@@ -224,21 +224,45 @@ __device__ __forceinline__ uint32_t e4m3_code(float y, float& val) {
   return (sgn >> 24) | (ef << 3) | ((u >> 20) & 7u);
 }
 
+// FP6 E2M3 code of y, |y| < 4.25, rounded to nearest even: steps of 1/8 below 2
+// (subnormals 0 .. 7/8 and [1, 2)), 1/4 in [2, 4), 1/2 from 4.  `val` is the
+// value the code stands for.
+__device__ __forceinline__ uint32_t e2m3_code(float y, float& val) {
+  const uint32_t sgn = __float_as_uint(y) >> 31;
+  const float ay = fabsf(y);
+  const float step = ay < 2.f ? 0.125f : (ay < 4.f ? 0.25f : 0.5f);
+  const float qv = __builtin_rintf(ay / step) * step;  // exact quotient, ties to even
+  val = sgn ? -qv : qv;
+  uint32_t mag;
+  if (qv < 1.f) {
+    mag = (uint32_t)(qv * 8.f);  // exponent field 0
+  } else {
+    const int e = qv < 2.f ? 1 : (qv < 4.f ? 2 : 3);  // exponent field, bias 1
+    mag = ((uint32_t)e << 3) | (uint32_t)((qv / (float)(1 << (e - 1)) - 1.f) * 8.f);
+  }
+  return (sgn << 5) | mag;
+}
+
 // Query pieces of the bit-key products (TurboQuant, QJL).  The key products
-// take the key bits as FP4 operands (one bit per nibble) against FP8 operands
-// with a power-of-two scale per block of 32 (v_mfma_scale_f32_16x16x128_f8f6f4).
-// Block j (element e = 8 d + n, the bit 4 n + d of one key word) of
+// take the key bits as FP4 operands (one bit per nibble) against FP8 (QJL) or
+// FP6 (TurboQuant) operands with a power-of-two scale per block of 32
+// (v_mfma_scale_f32_16x16x128_f8f6f4).  Block j (element e = 8 d + n, the bit
+// 4 n + d of one key word) of
 //   TURBO product 0 / 1 (code words 4 m + j, m = 0 / 1): the coefficient of
 //     bit d % 2 (a2 for the low bit b0, a1 for the high bit b1) times
 //     (R q)[16 (4 m + j) + 2 n + d / 2];
 //   TURBO product 2, QJL product 0 (sketch dword j): (S R q or S q)[32 j + 4 n + d].
-// Each block is split into 4 FP8 pieces: piece p holds the nearest E4M3 of the
+// Each block is split into 4 pieces: piece p holds the nearest code of the
 // residual left by pieces < p, at a scale 2^e that puts the residual's largest
-// magnitude in [64, 128), so the pieces' sum is within 2^-20 of the block's
-// largest value.  Layout per (product, piece): 4 blocks x 32 code bytes, then
-// the 4 blocks' E8M0 scale bytes (e + 127), 144 bytes in all.  32 threads per
-// block, as many blocks at a time as the workgroup has threads for.
-__device__ void prepared_query_pieces(int nprod, const float* qrot, const float* qsk, float a1, float a2,
+// magnitude in [64, 128) for E4M3 (3 mantissa bits to 448: the pieces' sum is
+// within 2^-20 of the block's largest value) or in [2, 4) for E2M3 (3 mantissa
+// bits to 7.5, steps of 1/8 below 2: each piece leaves at most 2^-4 of the
+// residual's largest magnitude, the sum is within 2^-16).  Layout per (product,
+// piece): 4 blocks of 32 bytes (E4M3: byte e = element e; E2M3: 24 bytes, element
+// e at bits [6 e, 6 e + 6)), then the 4 blocks' E8M0 scale bytes (e + 127), 144
+// bytes in all.  32 threads per block, as many blocks at a time as the workgroup
+// has threads for.
+__device__ void prepared_query_pieces(int nprod, const float* qrot, const float* qsk, float a1, float a2, bool fp6,
                                       uint8_t* out) {
   const int tid = threadIdx.x, e = tid & 31, d = e >> 3, n = e & 7;
   for (int blk = tid >> 5; blk < 4 * nprod; blk += (int)(blockDim.x >> 5)) {
@@ -255,13 +279,29 @@ __device__ void prepared_query_pieces(int nprod, const float* qrot, const float*
       if (M > 0.f) {
         int k;
         frexpf(M, &k);  // M = f 2^k, f in [0.5, 1)
-        ex = k - 7;
+        ex = k - (fp6 ? 2 : 7);
+      }
+      if (ex < -127) {  // a residual below the scales' range is left out
+        ex = -127;
+        r = 0.f;
       }
       float val;
-      const uint32_t c8 = e4m3_code(ldexpf(r, -ex), val);
-      r -= ldexpf(val, ex);
       uint8_t* dst = out + (prod * 4 + p) * 144;
-      dst[j * 32 + e] = (uint8_t)c8;
+      if (fp6) {
+        // elements 4 g .. 4 g + 3 fill the 3 bytes from 3 g: gather them in 2 steps
+        int v = (int)(e2m3_code(ldexpf(r, -ex), val) << (6 * (e & 3)));
+        v |= __shfl_xor(v, 1, 32);
+        v |= __shfl_xor(v, 2, 32);
+        if ((e & 3) == 0) {
+          uint8_t* b3 = dst + j * 32 + 3 * (e >> 2);
+          b3[0] = (uint8_t)v;
+          b3[1] = (uint8_t)(v >> 8);
+          b3[2] = (uint8_t)(v >> 16);
+        }
+      } else {
+        dst[j * 32 + e] = (uint8_t)e4m3_code(ldexpf(r, -ex), val);
+      }
+      r -= ldexpf(val, ex);
       if (e == 0) dst[128 + j] = (uint8_t)(ex + 127);
     }
   }
@@ -302,7 +342,7 @@ __global__ void __launch_bounds__(384) prep_query_kernel(const QT* __restrict__ 
     }
     if (pieces) {
       __syncthreads();
-      prepared_query_pieces(3, qrot, qsr, levels[2] - levels[0], levels[1] - levels[0],
+      prepared_query_pieces(3, qrot, qsr, levels[2] - levels[0], levels[1] - levels[0], true,
                             pieces + row * kTurboPieceBytes);
     }
   } else if (fmt == KV_FMT_QJL1_FP4V) {
@@ -314,7 +354,7 @@ __global__ void __launch_bounds__(384) prep_query_kernel(const QT* __restrict__ 
     }
     if (pieces) {
       __syncthreads();
-      prepared_query_pieces(1, nullptr, qsr, 0.f, 0.f, pieces + row * kQjlPieceBytes);
+      prepared_query_pieces(1, nullptr, qsr, 0.f, 0.f, false, pieces + row * kQjlPieceBytes);
     }
   } else {
     for (int c = tid; c < qw_out; c += nthr) dst[c] = qin[c];

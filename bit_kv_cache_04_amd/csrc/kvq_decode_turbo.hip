@@ -14,7 +14,7 @@
 // products become exact 0/1 bit-plane products on the matrix cores:
 //   <q, u~>      = a0 sum(q) + <a1 q, b1> + <a2 q, b0>
 //   <qS, sigma>  = 2 <qS, b> - sum(qS)
-// (key bits as FP4 operands against FP8 pieces of the query side, below).  The
+// (key bits as FP4 operands against FP6 pieces of the query side, below).  The
 // value product O = P' V~, P' = p n_v, takes each value code's level itself as
 // an fp16 operand of v_mfma_f32_16x16x32_f16: two byte permutes look a code up
 // in a table of the four levels' low and high bytes.  Value codes are transposed
@@ -117,18 +117,19 @@ __device__ __forceinline__ i8_t bit_nibbles(uint32_t w) {
 }
 
 // Key products on v_mfma_scale_f32_16x16x128_f8f6f4: A = key bits (FP4, 0 or
-// 0.5, block scale 2), B = FP8 pieces of the query operand with their block
-// scales.  A lane quarter's 32 elements form one k-block; B lane quarter qb
-// holds k-blocks qb / 2 and 2 + qb / 2 (elements 16 (qb % 2) .. + 15 of each)
-// and the scale of k-block qb.
+// 0.5, block scale 2), B = FP6 (E2M3) pieces of the query operand with their
+// block scales.  With these formats lane quarter q of either operand holds
+// k-block q (its 32 elements in order; FP6 packed 6 bits each into 6 dwords)
+// and the scale of k-block q.  FP6 runs at the FP4 rate, faster than FP8.
 __device__ __forceinline__ f4_t key_product(i8_t a, i8_t b, int scale_b, f4_t acc) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 4, 0, 0, 128, 0, scale_b);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 4, 2, 0, 128, 0, scale_b);
 }
 
 template <int G>
 struct WaveState {
-  // B operands of the key products: [product (code words 0..3, 4..7, sketch)]
-  // [piece set]: columns 0..7 carry pieces 2 s, columns 8..15 pieces 2 s + 1
+  // B operands of the key products (6 dwords of FP6 used): [product (code
+  // words 0..3, 4..7, sketch)][piece set]: columns 0..7 carry pieces 2 s,
+  // columns 8..15 pieces 2 s + 1
   i8_t bq[3][2];
   int bs[3][2];  // their block scales
   float cst;     // a0 * sum(R q) for this lane's head
@@ -302,14 +303,12 @@ __attribute__((amdgpu_waves_per_eu(KVQ_TURBO_WAVES_PER_EU, KVQ_TURBO_WAVES_PER_E
     for (int m = 0; m < 3; ++m)
 #pragma unroll
       for (int ps = 0; ps < 2; ++ps) {
-        const uint8_t* base = pc + (m * 4 + 2 * ps + (c >> 3)) * 144 + 16 * (q4 & 1);
-        const uint4 lo4 = *reinterpret_cast<const uint4*>(base + 32 * (q4 >> 1));
-        const uint4 hi4 = *reinterpret_cast<const uint4*>(base + 32 * (2 + (q4 >> 1)));
-        const uint8_t* sc = pc + (m * 4 + 2 * ps + (c >> 3)) * 144 + 128;
-        w.bq[m][ps] = live ? i8_t{(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w, (int)hi4.x, (int)hi4.y, (int)hi4.z,
-                                  (int)hi4.w}
+        const uint8_t* base = pc + (m * 4 + 2 * ps + (c >> 3)) * 144;
+        const uint4 lo4 = *reinterpret_cast<const uint4*>(base + 32 * q4);
+        const uint2 hi2 = *reinterpret_cast<const uint2*>(base + 32 * q4 + 16);
+        w.bq[m][ps] = live ? i8_t{(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w, (int)hi2.x, (int)hi2.y, 0, 0}
                            : i8_t{0, 0, 0, 0, 0, 0, 0, 0};
-        w.bs[m][ps] = live ? (int)sc[q4] : 127;
+        w.bs[m][ps] = live ? (int)base[128 + q4] : 127;
       }
     // per-head sums over all 128 entries: this lane's 32 + the other quarters'
     float sr = 0.f, ss = 0.f;

@@ -44,8 +44,9 @@ SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int q_dtype, int max_
 struct DecodeWorkspace {
   size_t qprep_off, qpiece_off, part_off, cnt_off, total;
 };
-// FP8 pieces of the query operand of a bit-key product (TurboQuant, QJL):
-// per product, 4 pieces x (4 blocks x 32 code bytes + 4 scale bytes + 12).
+// Pieces of the query operand of a bit-key product, FP6 for TurboQuant and FP8
+// for QJL: per product, 4 pieces x (4 blocks x 32 code bytes (FP6: 24 used) +
+// 4 scale bytes + 12 unused).
 constexpr int kPieceProductBytes = 4 * 144;
 constexpr int kTurboPieceBytes = 3 * kPieceProductBytes;  // code words 0..3, 4..7, sketch
 constexpr int kQjlPieceBytes = kPieceProductBytes;        // sketch

@@ -41,7 +41,7 @@ struct TurboDecodeArgs {
   const uint16_t* v_norm;   // [B][H][cap] fp16
   const float* levels;      // 4 codebook levels, ascending, symmetric
   const float* q;           // [B][Hq][256]
-  const uint8_t* qpieces;   // [B][Hq][kTurboPieceBytes]: FP8 pieces of the key-product operands
+  const uint8_t* qpieces;   // [B][Hq][kTurboPieceBytes]: FP6 pieces of the key-product operands
   const int32_t* seq_lens;
   int max_len, H, cap, Hq;
   float scale_log2, kappa;

@@ -273,6 +273,29 @@ def test_growing_logits_rescale(fmt):
     assert err.max() <= RTOL
 
 
+@pytest.mark.parametrize("fmt", ["turbo", "qjl1"])
+def test_wide_range_queries(fmt):
+    """Queries whose channels span 2^-12 .. 2^3 (and some exact zeros): every
+    32-element block of the bit-key products' query operand then needs all its
+    pieces, each at its own power-of-two scale."""
+    cfg = SMALL[fmt]
+    cache, K, V = _build(cfg)
+    consts = oracle_constants(cfg)
+    enc = oracle_encode(cfg, host64(K), host64(V), consts)
+    g = torch.Generator().manual_seed(7)
+    q0 = synth.make_queries(cfg, device="cpu")
+    mult = torch.exp2(torch.empty(q0.shape).uniform_(-12.0, 3.0, generator=g))
+    mult[..., ::11] = 0.0
+    q = (q0.float() * mult).to(q0.dtype).cuda()
+    lens = synth.seq_lens_for(cfg, ragged=True)
+    out = cache.decode(q, torch.from_numpy(lens).cuda(), softmax_scale(cfg)).cpu().numpy()
+    ref = OA.decode_attention(fmt, enc, host64(q), lens, softmax_scale(cfg), cfg.hkv, consts,
+                              latent_dim=cfg.head_dim)
+    err = row_rel_err(out, ref)
+    print(f"  {fmt} wide-range queries: max row rel err {err.max():.3e}", flush=True)
+    assert err.max() <= RTOL
+
+
 @pytest.mark.parametrize("fmt", ["fp4", "qjl1", "turbo", "latent", "kivi2"])
 def test_graph_replay_matches_eager(fmt):
     """Append + decode captured as a HIP graph: every replay, with eager work and
