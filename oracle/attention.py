@@ -1,4 +1,5 @@
-"""Single-query decode attention over a packed cache: the plain definition.
+"""Decode attention over a packed cache: the plain definition (one query token
+per sequence, or several with a causal tail mask).
 
 During decoding every new token attends over the keys and values of all cached
 tokens, and the whole cache is streamed from HBM for each of them (page
@@ -27,6 +28,15 @@ QJL estimate of <q, r> is kappa * ||r|| * <S q, sign(S r)>, unbiased over S
 (page "TurboQuant vs OSCAR vs EpiCache", section "quantization frontiers",
 stage two).  The turbo logit rests on <q, k> = n <R q, u> for orthogonal R
 and u = R k / n = u_tilde + r.
+
+Several query tokens per sequence (decode_attention_multi): a draft model can
+propose several next positions at once for the main model to check in one pass
+(page "How DeepSeek-V4.1-Flash cut KV-cache storage by 4x via CSA2", section
+"numerical precision & hardware efficiency": five draft positions predicted in
+parallel).  Reading: the nq queries are the last nq tokens of the sequence,
+their keys and values already appended, and query j (0-based) sees every token
+up to and including its own position, t < L_b - (nq - 1 - j); nq = 1 is the
+single-query case above.
 
 Logits and dequantised values are computed in token chunks only to bound
 memory; the softmax is taken over the full logit vector.
@@ -141,3 +151,39 @@ def decode_attention(fmt, cache, q, seq_lens, scale, hkv, consts=None, latent_di
         res[(b, hq)] = decode_attention_row_group(fmt, cache, b, h, q[b, hq:hq + 1],
                                                   int(seq_lens[b]), scale, consts, latent_dim)[0]
     return res
+
+
+def decode_attention_multi(fmt, cache, q, seq_lens, scale, hkv, consts=None, latent_dim=512, chunk=CHUNK):
+    """fp64 outputs [B, nq, Hq, dv] for q [B, nq, Hq, dk]: query j of sequence b
+    sees the tokens t < seq_lens[b] - (nq - 1 - j)."""
+    q = np.asarray(q, dtype=np.float64)
+    B, nq, Hq = q.shape[:3]
+    G = Hq // hkv
+    out = None
+    for b in range(B):
+        L = int(seq_lens[b])
+        if L < nq:
+            raise ValueError("every query must see at least its own token")
+        # row (j, g) of the group: query token j, query head h * G + g
+        limit = L - (nq - 1 - np.repeat(np.arange(nq), G))
+        visible = np.arange(L)[None, :] < limit[:, None]
+        for h in range(hkv):
+            qg = q[b, :, h * G:(h + 1) * G].reshape(nq * G, -1)
+            logits = np.concatenate([
+                _key_logits(fmt, cache, b, h, t0, min(L, t0 + chunk), qg, consts, latent_dim)
+                for t0 in range(0, L, chunk)], axis=1) * scale
+            logits = np.where(visible, logits, -np.inf)
+            m = logits.max(axis=1, keepdims=True)
+            p = np.exp(logits - m)
+            p /= p.sum(axis=1, keepdims=True)
+            o = None
+            for t0 in range(0, L, chunk):
+                t1 = min(L, t0 + chunk)
+                part = p[:, t0:t1] @ _values(fmt, cache, b, h, t0, t1, consts, latent_dim)
+                o = part if o is None else o + part
+            if fmt == "turbo":
+                o = o @ np.asarray(consts["rot"], np.float64)
+            if out is None:
+                out = np.zeros((B, nq, Hq, o.shape[1]))
+            out[b, :, h * G:(h + 1) * G] = o.reshape(nq, G, -1)
+    return out
