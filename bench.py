@@ -108,19 +108,21 @@ def measured_traffic(workload):
     return None
 
 
-def roofline(cfg, nbytes, dec_ms):
-    """Roofline of the split-context attention kernel, timed by events around its launch."""
+def roofline(cfg, nbytes, dec_ms, nq=1):
+    """Roofline of the split-context attention kernel, timed by events around its launch.
+    The counter summaries cover the one-query kernels: traffic is None for nq > 1."""
+    traffic = measured_traffic(cfg.name) if nq == 1 else None
     if cfg.fmt == "latent":
         # 128 heads x (576 + 512) x 2 flop per token: a dense contraction on fp16 matrix cores
-        flops = 2.0 * cfg.batch * cfg.context * cfg.hq * (cfg.key_width + cfg.head_dim)
+        flops = 2.0 * nq * cfg.batch * cfg.context * cfg.hq * (cfg.key_width + cfg.head_dim)
         ach = flops / (dec_ms * 1e-3) / 1e12
         return {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4), "traffic": measured_traffic(cfg.name),
+                "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic,
                 "kernel": "split-context attention", "kernel_us": round(dec_ms * 1e3, 2),
                 "hbm_gbs": round(nbytes / (dec_ms * 1e-3) / 1e9, 2)}
     ach = nbytes / (dec_ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(cfg.name),
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": "split-context attention", "kernel_us": round(dec_ms * 1e3, 2)}
 
 
@@ -131,6 +133,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="fp4_b16_t32k")
     ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--queries", type=int, default=1,
+                    help="query tokens per sequence (drafted positions checked in one pass); the step "
+                         "appends that many tokens")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph replay")
     args = ap.parse_args()
@@ -159,7 +164,8 @@ def main():
     # prefill the first T - n tokens (untimed), one sequence and 16K tokens at a
     # time to bound input memory
     # KIVI keys are quantised per whole 32-token group, so its step appends one group
-    n_new = 32 if cfg.fmt == "kivi2" else max(1, cfg.append_new)
+    nq = args.queries
+    n_new = 32 if cfg.fmt == "kivi2" else max(nq, cfg.append_new)
     n_pre = T - n_new
     for b in range(cfg.batch):
         seq = cache.sequence(b)
@@ -177,10 +183,12 @@ def main():
     else:
         k_new, v_new = synth.make_kv(cfg, 0, cfg.batch, T - n_new, T, device=dev)
     q = synth.make_queries(cfg, device=dev)
+    if nq > 1:
+        q = synth.make_queries(cfg.scaled(hq=nq * cfg.hq), device=dev).view(cfg.batch, nq, cfg.hq, -1)
     lens = torch.full((cfg.batch,), T, dtype=torch.int32, device=dev)
     scale = 1.0 / math.sqrt(cfg.key_width)
-    out = torch.empty(cfg.batch, cfg.hq, cfg.head_dim, dtype=torch.float32, device=dev)
-    ws = torch.zeros(cache.workspace_bytes(cfg.hq, T, args.splits, q.dtype), dtype=torch.uint8, device=dev)
+    out = torch.empty(*q.shape[:-1], cfg.head_dim, dtype=torch.float32, device=dev)
+    ws = torch.zeros(cache.workspace_bytes(cfg.hq, T, args.splits, q.dtype, nq), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -261,13 +269,13 @@ def main():
         "config": {"workload": cfg.name, "format": cfg.fmt, "batch": cfg.batch, "q_heads": cfg.hq,
                    "kv_heads": cfg.hkv, "head_dim": cfg.head_dim, "rope_dim": cfg.rope_dim,
                    "context": T, "counted_bytes_per_step": nbytes,
-                   "splits": args.splits or "auto"},
+                   "splits": args.splits or "auto", "queries_per_seq": nq},
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
-        "query_tokens_per_s": round(cfg.batch / (ms_step * 1e-3), 1),
+        "query_tokens_per_s": round(nq * cfg.batch / (ms_step * 1e-3), 1),
         "wall_s": round(wall, 3),
         "timing": "hip-graph replay of the step" if not args.no_graph else "eager launches",
         "ms_per_step_eager": round(ms_eager, 5),
-        "roofline": roofline(cfg, nbytes, dec_ms),
+        "roofline": roofline(cfg, nbytes, dec_ms, nq),
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg)

@@ -114,26 +114,30 @@ class PackedKVCache:
         kvq.kv_quant_append(self.struct, _ptr(k), _ptr(v), _TORCH_DT[k.dtype], start, n,
                             _stream_ptr(self.device))
 
-    def workspace_bytes(self, num_q_heads, max_seq_len, splits=0, q_dtype=torch.bfloat16):
-        opts = KVDecodeOpts(splits, None, None)
+    def workspace_bytes(self, num_q_heads, max_seq_len, splits=0, q_dtype=torch.bfloat16, num_queries=1):
+        opts = KVDecodeOpts(splits, None, None, num_queries)
         return kvq.kv_decode_attention(self.struct, None, _TORCH_DT[q_dtype], num_q_heads, None, max_seq_len,
                                        1.0, None, None, 0, opts)
 
     def decode(self, q, seq_lens, scale, max_seq_len=None, splits=0, out=None, ws=None, events=None):
-        """q: [B, Hq, d(+rope)] fp32/bf16; seq_lens: int32 device [B]. Returns fp32 [B, Hq, d]."""
+        """q: [B, Hq, d(+rope)] fp32/bf16, or [B, nq, Hq, d(+rope)] for nq query tokens per
+        sequence (query j sees the first seq_lens[b] - (nq - 1 - j) tokens); seq_lens: int32
+        device [B]. Returns fp32 [B, Hq, d] (or [B, nq, Hq, d])."""
         q = q.contiguous()
-        Hq = q.shape[1]
+        nq = q.shape[1] if q.dim() == 4 else 1
+        Hq = q.shape[-2]
         max_seq_len = self.T if max_seq_len is None else max_seq_len
-        need = self.workspace_bytes(Hq, max_seq_len, splits, q.dtype)
+        need = self.workspace_bytes(Hq, max_seq_len, splits, q.dtype, nq)
         if ws is None:
             if self._ws is None or self._ws.numel() < need:
                 self._ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
             ws = self._ws
         if out is None:
-            out = torch.empty(self.B, Hq, self.d, dtype=torch.float32, device=self.device)
+            shape = (self.B, nq, Hq, self.d) if q.dim() == 4 else (self.B, Hq, self.d)
+            out = torch.empty(shape, dtype=torch.float32, device=self.device)
         ev = (None, None) if events is None else (ctypes.c_void_p(events[0].cuda_event),
                                                   ctypes.c_void_p(events[1].cuda_event))
-        opts = KVDecodeOpts(splits, ev[0], ev[1])
+        opts = KVDecodeOpts(splits, ev[0], ev[1], nq)
         kvq.kv_decode_attention(self.struct, _ptr(q), _TORCH_DT[q.dtype], Hq, _ptr(seq_lens), max_seq_len,
                                 float(scale), _ptr(out), _ptr(ws), ws.numel(), opts,
                                 _stream_ptr(self.device))

@@ -45,8 +45,11 @@ extern "C" int kv_decode_attention(const kv_cache* c, const void* q, int32_t q_d
   if (!std::isfinite(softmax_scale)) return KV_EINVAL;
   const int req = opts ? opts->num_splits : 0;
   if (req < 0 || req > 1024) return KV_EINVAL;
-  const SplitPlan plan = plan_splits(&L, num_q_heads, q_dtype, max_seq_len, req);
-  const DecodeWorkspace wsl = decode_workspace(&L, num_q_heads, plan.splits);
+  const int nq = opts && opts->num_queries > 0 ? opts->num_queries : 1;
+  if ((opts && opts->num_queries < 0) || nq > max_seq_len) return KV_EINVAL;
+  if (nq > 64) return KV_EUNSUPPORTED;
+  const SplitPlan plan = plan_splits(&L, num_q_heads, nq, q_dtype, max_seq_len, req);
+  const DecodeWorkspace wsl = decode_workspace(&L, nq * num_q_heads, plan.splits);
   if (!ws) {
     if (!ws_bytes) return KV_EINVAL;
     *ws_bytes = wsl.total;
@@ -55,6 +58,6 @@ extern "C" int kv_decode_attention(const kv_cache* c, const void* q, int32_t q_d
   if (!ws_bytes || *ws_bytes < wsl.total) return KV_EWORKSPACE;
   if (!aligned(ws, 256)) return KV_EINVAL;
   if (!q || !seq_lens || !out) return KV_EINVAL;
-  return launch_decode(c, q, q_dtype, num_q_heads, seq_lens, max_seq_len, softmax_scale, out, ws, plan, wsl,
+  return launch_decode(c, q, q_dtype, num_q_heads, nq, seq_lens, max_seq_len, softmax_scale, out, ws, plan, wsl,
                        opts ? opts->ev_begin : nullptr, opts ? opts->ev_end : nullptr, stream);
 }

@@ -35,13 +35,14 @@ struct DecodeArgs {
   const float* levels;
   int H, cap, d, rope_dim;
   // query / output
-  const float* qv;  // prepared queries [B][Hq][QW]
+  const float* qv;  // prepared queries [B][nq][Hq][QW]
   int Hq, G, head_blocks, hb_size;
+  int nq, Gr;       // query tokens per sequence, query heads per KV head (G = nq * Gr)
   const int32_t* seq_lens;
   int max_len;
   float scale_log2;  // softmax scale * log2(e)
   float kappa;       // sqrt(pi/2) / m
-  float* part;       // [B][Hq][splits][DV + 2]: m (log2 units), l, o[DV]
+  float* part;       // [B][nq][Hq][splits][DV + 2]: m (log2 units), l, o[DV]
   int splits, per_split;
 };
 
@@ -117,20 +118,27 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
   const int split = blockIdx.x;
   const int h = blockIdx.y / a.head_blocks, hb = blockIdx.y % a.head_blocks;
   const int b = blockIdx.z;
-  const int hq0 = h * a.G + hb * a.hb_size;
-  const int nh = min(a.hb_size, a.G - hb * a.hb_size);
+  const int vh0 = hb * a.hb_size;  // first row (query j, head g: row j * Gr + g) of this block
+  const int nh = min(a.hb_size, a.G - vh0);
   const size_t bh = (size_t)b * a.H + h;
   const int L = min(min(a.seq_lens[b], a.max_len), a.cap);
   const int t_begin = split * a.per_split;
   const int t_end = min(L, t_begin + a.per_split);
+  // query / output row of block row hh; query j sees the first L - (nq - 1 - j) tokens
+  auto qrow = [&](int hh) {
+    const int vh = vh0 + hh;
+    return ((size_t)b * a.nq + vh / a.Gr) * a.Hq + (size_t)h * a.Gr + vh % a.Gr;
+  };
+  __shared__ int lim[HB];
 
   for (int e = tid; e < HB * DK; e += NT) {
     const int hh = e / DK, c = e % DK;
-    qs[hh][c] = hh < nh ? a.qv[((size_t)b * a.Hq + hq0 + hh) * DK + c] : 0.f;
+    qs[hh][c] = hh < nh ? a.qv[qrow(hh) * DK + c] : 0.f;
   }
   if (tid < HB) {
     ms[tid] = -INFINITY;
     ls[tid] = 0.f;
+    lim[tid] = L - (a.nq - 1 - (vh0 + tid) / a.Gr);
   }
   float o[OPT];
 #pragma unroll
@@ -154,17 +162,18 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
       const int hh = p / TT, t = p % TT;
       float s = 0.f;
       for (int c = 0; c < DK; ++c) s = fmaf(qs[hh][c], ks[t][c], s);
-      ss[hh][t] = (t < nt && hh < nh) ? s * a.scale_log2 : -INFINITY;
+      ss[hh][t] = (t < nt && hh < nh && t0 + t < lim[hh]) ? s * a.scale_log2 : -INFINITY;
     }
     __syncthreads();
     if (tid < nh) {
       float mx = -INFINITY;
       for (int t = 0; t < nt; ++t) mx = fmaxf(mx, ss[tid][t]);
       const float mnew = fmaxf(ms[tid], mx);
-      const float alpha = exp2f(ms[tid] - mnew);
+      const float mref = mnew == -INFINITY ? 0.f : mnew;  // a row that has seen no token yet
+      const float alpha = exp2f(ms[tid] - mref);
       float sum = 0.f;
       for (int t = 0; t < TT; ++t) {
-        const float p = t < nt ? exp2f(ss[tid][t] - mnew) : 0.f;
+        const float p = t < nt ? exp2f(ss[tid][t] - mref) : 0.f;
         ss[tid][t] = p;
         sum += p;
       }
@@ -194,7 +203,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
     if (e < HB * DV) {
       const int hh = e / DV, c = e % DV;
       if (hh < nh) {
-        float* p = a.part + (((size_t)b * a.Hq + hq0 + hh) * a.splits + split) * (DV + 2);
+        float* p = a.part + (qrow(hh) * a.splits + split) * (DV + 2);
         p[2 + c] = o[j];
         if (c == 0) {
           p[0] = ms[hh];
@@ -500,7 +509,7 @@ void launch_split(const DecodeArgs& a, int B, hipStream_t st) {
 
 }  // namespace
 
-int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads, const int32_t* seq_lens,
+int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads, int nq, const int32_t* seq_lens,
                   int max_seq_len, float scale, float* out, void* ws, const SplitPlan& plan,
                   const DecodeWorkspace& wsl, void* ev_begin, void* ev_end, void* stream) {
   const kv_layout& L = c->layout;
@@ -509,9 +518,9 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
   float* qv = reinterpret_cast<float*>(wsb + wsl.qprep_off);
   float* part = reinterpret_cast<float*>(wsb + wsl.part_off);
   const int B = L.batch;
-  const int rows = B * num_q_heads;
+  const int rows = B * nq * num_q_heads;  // (sequence, query token, query head)
   const int qw_in = query_width(&L), qw_out = prepared_query_width(&L);
-  if (latent_fast_path_ok(L, num_q_heads, q_dtype)) {
+  if (latent_fast_path_ok(L, num_q_heads, nq, q_dtype)) {
     MfmaDecodeArgs f{};
     f.k_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_K_CODES]);
     f.k_scale = static_cast<const uint16_t*>(c->buf[KV_BUF_K_SCALE]);
@@ -533,10 +542,10 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     launch_merge(part, rows, plan.splits, L.head_dim, L.format, c->rot, out, st);
     return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
   }
-  const bool mfma = mfma_fast_path_ok(L, num_q_heads, q_dtype);
+  const bool mfma = mfma_fast_path_ok(L, num_q_heads, nq, q_dtype);
   // FP4 keys read the caller's bf16 queries as they are; every other format
   // first prepares its fp32 query (projection / rotation)
-  uint8_t* qpieces = turbo_fast_path_ok(L, num_q_heads) || (mfma && L.format == KV_FMT_QJL1_FP4V)
+  uint8_t* qpieces = turbo_fast_path_ok(L, num_q_heads, nq) || (mfma && L.format == KV_FMT_QJL1_FP4V)
                          ? reinterpret_cast<uint8_t*>(wsb + wsl.qpiece_off)
                          : nullptr;
   if (!(mfma && L.format == KV_FMT_FP4)) {
@@ -548,7 +557,7 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
       prep_query_kernel<uint16_t><<<rows, prep_threads, 0, st>>>(static_cast<const uint16_t*>(q), qw_in, qw_out,
                                                         L.format, c->rot, c->proj, c->lm_levels, qv, qpieces);
   }
-  if (turbo_fast_path_ok(L, num_q_heads)) {
+  if (turbo_fast_path_ok(L, num_q_heads, nq)) {
     TurboDecodeArgs f{};
     f.k_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_K_CODES]);
     f.k_sketch = static_cast<const uint8_t*>(c->buf[KV_BUF_K_SKETCH]);
@@ -596,9 +605,15 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     f.part = part;
     f.splits = plan.splits;
     f.per_split = plan.tokens_per_split;
+    f.nq = nq;
+    f.gr = num_q_heads / L.num_kv_heads;
     if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), st) != hipSuccess) return KV_EDEVICE;
-    int rc = launch_decode_mfma(f, L.format, B, num_q_heads / L.num_kv_heads, st);
-    if (rc != KV_OK) return rc;
+    // one launch per 16 (query, head) pairs of a KV head, each over the whole cache
+    for (f.c0 = 0; f.c0 < nq * f.gr; f.c0 += 16) {
+      f.ncol = std::min(16, nq * f.gr - f.c0);
+      int rc = launch_decode_mfma(f, L.format, B, mfma_columns(f.ncol), st);
+      if (rc != KV_OK) return rc;
+    }
     if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess) return KV_EDEVICE;
     launch_merge(part, rows, plan.splits, L.head_dim, L.format, c->rot, out, st);
     return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
@@ -623,7 +638,9 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
   a.rope_dim = L.rope_dim;
   a.qv = qv;
   a.Hq = num_q_heads;
-  a.G = num_q_heads / L.num_kv_heads;
+  a.nq = nq;
+  a.Gr = num_q_heads / L.num_kv_heads;
+  a.G = nq * a.Gr;  // rows per (sequence, KV head): query j, head g is row j * Gr + g
   a.hb_size = std::min(a.G, 16);
   a.head_blocks = (a.G + a.hb_size - 1) / a.hb_size;
   a.seq_lens = seq_lens;

@@ -119,8 +119,11 @@ struct KeysFp4 {
   };
   template <int G>
   __device__ static void load_q(Q& q, const MfmaDecodeArgs& a, int b, int h, int q4, int c) {
-    const int head = c < G ? c : 0;
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G + head) * 128 + 32 * q4;
+    // column c: pair c0 + c = query token j, head g (columns from ncol on hold none)
+    const bool live = c < a.ncol;
+    const int jq = live ? (a.c0 + c) / a.gr : 0, head = live ? (a.c0 + c) % a.gr : 0;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                         (((size_t)b * a.nq + jq) * a.Hq + (size_t)h * a.gr + head) * 128 + 32 * q4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint4 raw = *reinterpret_cast<const uint4*>(qp + 8 * i);
@@ -128,8 +131,8 @@ struct KeysFp4 {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const h2_t v = bf16x2_to_h2(wd[j]);
-        q.f[i][2 * j] = c < G ? v[0] : (_Float16)0.f;
-        q.f[i][2 * j + 1] = c < G ? v[1] : (_Float16)0.f;
+        q.f[i][2 * j] = live ? v[0] : (_Float16)0.f;
+        q.f[i][2 * j + 1] = live ? v[1] : (_Float16)0.f;
       }
     }
   }
@@ -316,7 +319,8 @@ struct WaveState {
 // when there is none, so that the refill is unconditional and the compiler's
 // wait counts stay exact), then compute.
 template <int G, int NS, class KP>
-__device__ __forceinline__ void tile_step(WaveState<KP>& w, uint8_t* st, int lane, int t0, int t_end, int t_next,
+__device__ __forceinline__ void tile_step(WaveState<KP>& w, uint8_t* st, int lane, int t0, int t_full, int lim,
+                                          int t_next,
                                           const MfmaDecodeArgs& a, const typename KP::R& kr, const VRsrc& vr) {
   const int q4 = lane >> 4, c = lane & 15;
   // This stage's tile has landed once at most the other NS - 1 stages' refills
@@ -348,7 +352,7 @@ __device__ __forceinline__ void tile_step(WaveState<KP>& w, uint8_t* st, int lan
   // ---------------- online softmax (this lane: head c, tokens t0 + 16*blk + 4*v + q4)
   float sv[8];
   float tmax = -INFINITY;
-  if (t0 + 32 <= t_end) {  // a whole tile: nothing to mask
+  if (t0 + 32 <= t_full) {  // a whole tile for every column: nothing to mask
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
@@ -362,7 +366,7 @@ __device__ __forceinline__ void tile_step(WaveState<KP>& w, uint8_t* st, int lan
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int tok = t0 + 16 * blk + 4 * v + q4;
-        const float s = tok < t_end ? sacc[blk][v] * a.scale_log2 : -INFINITY;
+        const float s = tok < lim ? sacc[blk][v] * a.scale_log2 : -INFINITY;
         sv[4 * blk + v] = s;
         tmax = fmaxf(tmax, s);
       }
@@ -375,18 +379,20 @@ __device__ __forceinline__ void tile_step(WaveState<KP>& w, uint8_t* st, int lan
   const bool bump = tmax > w.m_run + 8.f;
   const float m_new = bump ? tmax : w.m_run;
   const float alpha = bump ? __builtin_amdgcn_exp2f(w.m_run - m_new) : 1.f;
+  // a column with several queries can meet a tile before its first visible token
+  const float m_ref = m_new == -INFINITY ? 0.f : m_new;
   h8_t pf;
   float psum = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const float p = __builtin_amdgcn_exp2f(sv[j] - m_new);
+    const float p = __builtin_amdgcn_exp2f(sv[j] - m_ref);
     psum += p;
     pf[j] = (_Float16)p;
   }
   w.l_run = w.l_run * alpha + psum;
   w.m_run = m_new;
   // O rows are heads 4*q4 + v; head hh's alpha lives in lane hh (quarter 0)
-  if (__ballot(bump && c < G)) {
+  if (__ballot(bump && c < a.ncol)) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const float av = __shfl(alpha, (4 * q4 + v) & 15);
@@ -474,6 +480,10 @@ __attribute__((amdgpu_waves_per_eu(KVQ_MFMA_WAVES_PER_EU, KVQ_MFMA_WAVES_PER_EU)
   const int L = min(min(a.seq_lens[b], a.max_len), a.cap);
   const int t_begin = split * a.per_split;
   const int t_end = min(L, t_begin + a.per_split);
+  // this lane's column is query token j = (c0 + lane % 16) / gr, which sees the
+  // first L - (nq - 1 - j) tokens; a tile below t_full is whole for every column
+  const int lim = min(t_end, L - (a.nq - 1 - (a.c0 + (lane & 15)) / a.gr));
+  const int t_full = min(t_end, L - (a.nq - 1 - a.c0 / a.gr));
 
   WaveState<KP> w;
   KP::template load_q<G>(w.q, a, b, h, lane >> 4, lane & 15);
@@ -498,18 +508,18 @@ __attribute__((amdgpu_waves_per_eu(KVQ_MFMA_WAVES_PER_EU, KVQ_MFMA_WAVES_PER_EU)
   if constexpr (NS == 2) {
     for (; t0 < t_end; t0 += 256) {
       // the second tile of a pair may lie past t_end: all its tokens are masked
-      tile_step<G, NS, KP>(w, sa, lane, t0, t_end, tile_or_none(t0 + 256), a, kr, vr);
-      tile_step<G, NS, KP>(w, sb, lane, t0 + 128, t_end, tile_or_none(t0 + 384), a, kr, vr);
+      tile_step<G, NS, KP>(w, sa, lane, t0, t_full, lim, tile_or_none(t0 + 256), a, kr, vr);
+      tile_step<G, NS, KP>(w, sb, lane, t0 + 128, t_full, lim, tile_or_none(t0 + 384), a, kr, vr);
     }
   } else {
     uint8_t* sc = stC + wave * kStage;
     issue_tile<KP>(sc, lane, tile_or_none(t0 + 256), kr, vr);
     while (t0 < t_end) {
-      tile_step<G, NS, KP>(w, sa, lane, t0, t_end, tile_or_none(t0 + 384), a, kr, vr);
+      tile_step<G, NS, KP>(w, sa, lane, t0, t_full, lim, tile_or_none(t0 + 384), a, kr, vr);
       if (t0 + 128 >= t_end) break;
-      tile_step<G, NS, KP>(w, sb, lane, t0 + 128, t_end, tile_or_none(t0 + 512), a, kr, vr);
+      tile_step<G, NS, KP>(w, sb, lane, t0 + 128, t_full, lim, tile_or_none(t0 + 512), a, kr, vr);
       if (t0 + 256 >= t_end) break;
-      tile_step<G, NS, KP>(w, sc, lane, t0 + 256, t_end, tile_or_none(t0 + 640), a, kr, vr);
+      tile_step<G, NS, KP>(w, sc, lane, t0 + 256, t_full, lim, tile_or_none(t0 + 640), a, kr, vr);
       t0 += 384;
     }
   }
@@ -538,7 +548,6 @@ __attribute__((amdgpu_waves_per_eu(KVQ_MFMA_WAVES_PER_EU, KVQ_MFMA_WAVES_PER_EU)
     }
   }
   __syncthreads();
-  const size_t row0 = (size_t)b * a.Hq + (size_t)h * G;  // first query-head row of this group
   for (int e = tid_e; e < G * 128; e += 256) {
     const int hh = e >> 7, ch = e & 127;
     float M = -INFINITY;
@@ -552,7 +561,10 @@ __attribute__((amdgpu_waves_per_eu(KVQ_MFMA_WAVES_PER_EU, KVQ_MFMA_WAVES_PER_EU)
       Ls += f * sm_l[ww][hh];
       O += f * sm_o[ww][hh][ch];
     }
-    float* p = a.part + ((row0 + hh) * a.splits + split) * 130;
+    if (hh >= a.ncol) continue;  // a column with no query
+    const int pc = a.c0 + hh;
+    const size_t row = ((size_t)b * a.nq + pc / a.gr) * a.Hq + (size_t)h * a.gr + pc % a.gr;
+    float* p = a.part + (row * a.splits + split) * 130;
     p[2 + ch] = O;
     if (ch == 0) {
       p[0] = M;

@@ -69,34 +69,42 @@ int prepared_query_width(const kv_layout* L) {
 
 int value_width(const kv_layout* L) { return L->head_dim; }
 
-bool turbo_fast_path_ok(const kv_layout& L, int num_q_heads) {
+bool turbo_fast_path_ok(const kv_layout& L, int num_q_heads, int nq) {
   const int G = num_q_heads / L.num_kv_heads;
-  return L.format == KV_FMT_TURBO && L.head_dim == 128 && L.qjl_m == 128 && L.lm_bits == 2 &&
+  return nq == 1 && L.format == KV_FMT_TURBO && L.head_dim == 128 && L.qjl_m == 128 && L.lm_bits == 2 &&
          (G == 1 || G == 2 || G == 4 || G == 8) && (size_t)L.capacity * 32 < (size_t(1) << 31);
 }
 
-bool latent_fast_path_ok(const kv_layout& L, int num_q_heads, int q_dtype) {
-  return L.format == KV_FMT_LATENT_FP4 && L.head_dim == 512 && L.rope_dim == 64 && q_dtype == KV_DT_BF16 &&
+bool latent_fast_path_ok(const kv_layout& L, int num_q_heads, int nq, int q_dtype) {
+  return nq == 1 && L.format == KV_FMT_LATENT_FP4 && L.head_dim == 512 && L.rope_dim == 64 && q_dtype == KV_DT_BF16 &&
          (num_q_heads == 32 || num_q_heads == 64 || num_q_heads == 128) &&
          (size_t)L.capacity * 256 < (size_t(1) << 31);
 }
 
-bool mfma_fast_path_ok(const kv_layout& L, int num_q_heads, int q_dtype) {
+int mfma_columns(int n) {
+  return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : n <= 8 ? 8 : 16;
+}
+
+bool mfma_fast_path_ok(const kv_layout& L, int num_q_heads, int nq, int q_dtype) {
   const int G = num_q_heads / L.num_kv_heads;
   const bool g_ok = G == 1 || G == 2 || G == 4 || G == 8 || G == 16;
-  if (!g_ok || L.head_dim != 128) return false;
+  if (L.head_dim != 128) return false;
+  // several queries: FP4 keys only, every (query, head) pair a column of its own,
+  // 16 columns per launch
+  if (nq > 1) return L.format == KV_FMT_FP4 && q_dtype == KV_DT_BF16;
+  if (!g_ok) return false;
   if (L.format == KV_FMT_FP4) return q_dtype == KV_DT_BF16;
   if (L.format == KV_FMT_QJL1_FP4V) return L.qjl_m == 128;
   return false;
 }
 
-SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int q_dtype, int max_seq_len, int requested) {
+SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int nq, int q_dtype, int max_seq_len, int requested) {
   // Workgroups cover their split in steps of `tile` tokens; aim for enough
   // workgroups to keep a 256-CU part busy several times over, but no split
   // shorter than a few steps.
   const int G = num_q_heads / L->num_kv_heads;
-  const bool fast = mfma_fast_path_ok(*L, num_q_heads, q_dtype) || turbo_fast_path_ok(*L, num_q_heads);
-  const bool latent = latent_fast_path_ok(*L, num_q_heads, q_dtype);
+  const bool fast = mfma_fast_path_ok(*L, num_q_heads, nq, q_dtype) || turbo_fast_path_ok(*L, num_q_heads, nq);
+  const bool latent = latent_fast_path_ok(*L, num_q_heads, nq, q_dtype);
   const int tile = fast ? 128 : 64;
   // the latent kernel keeps one workgroup per compute unit resident and every
   // split writes Hq x 514 partial floats: one round of workgroups, a few long
@@ -104,7 +112,7 @@ SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int q_dtype, int max_
   // doubles the partials the merge reads)
   const long target = latent ? 256 : 2048;
   long units = (long)L->batch * L->num_kv_heads;
-  if (!fast && !latent && G > 16) units *= (G + 15) / 16;  // the generic kernel's head blocks
+  if (!fast && !latent && nq * G > 16) units *= (nq * G + 15) / 16;  // the generic kernel's head blocks
   int splits = requested;
   if (splits <= 0) {
     long want = (target + units - 1) / units;

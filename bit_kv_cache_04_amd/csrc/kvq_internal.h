@@ -31,13 +31,17 @@ struct SplitPlan {
   int splits;
   int tokens_per_split;
 };
-// The matrix-core decode kernel covers this cache / query combination.
-bool mfma_fast_path_ok(const kv_layout& L, int num_q_heads, int q_dtype);
+// The matrix-core decode kernel covers this cache / query combination (nq query
+// tokens per sequence).
+bool mfma_fast_path_ok(const kv_layout& L, int num_q_heads, int nq, int q_dtype);
 // The TurboQuant matrix-core kernel covers this cache / query combination.
-bool turbo_fast_path_ok(const kv_layout& L, int num_q_heads);
+bool turbo_fast_path_ok(const kv_layout& L, int num_q_heads, int nq);
 // The shared-latent matrix-core kernel covers this cache / query combination.
-bool latent_fast_path_ok(const kv_layout& L, int num_q_heads, int q_dtype);
-SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int q_dtype, int max_seq_len, int requested);
+bool latent_fast_path_ok(const kv_layout& L, int num_q_heads, int nq, int q_dtype);
+// Columns of the matrix-core kernel that takes n (query, head) pairs, n <= 16:
+// n rounded up to 1, 2, 4, 8 or 16.
+int mfma_columns(int n);
+SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int nq, int q_dtype, int max_seq_len, int requested);
 
 // Workspace of a decode call: prepared queries, then per-split partial results
 // (running max, running sum, unnormalised output) — offsets in bytes.
@@ -56,7 +60,7 @@ DecodeWorkspace decode_workspace(const kv_layout* L, int num_q_heads, int splits
 // validated by the caller.
 int launch_append(const kv_cache* c, const void* k, const void* v, int in_dtype, int start,
                   int n_new, void* stream);
-int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads,
+int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads, int nq,
                   const int32_t* seq_lens, int max_seq_len, float scale, float* out, void* ws,
                   const SplitPlan& plan, const DecodeWorkspace& wsl, void* ev_begin, void* ev_end,
                   void* stream);

@@ -24,8 +24,12 @@ struct MfmaDecodeArgs {
   int max_len, H, cap, Hq;
   float scale_log2;  // softmax scale * log2(e)
   float kappa;       // QJL: sqrt(pi/2) / m
-  float* part;       // [B][Hq][splits][130]: running max (log2 units), sum, output
+  float* part;       // [B][nq][Hq][splits][130]: running max (log2 units), sum, output
   int splits, per_split;
+  // nq query tokens per sequence of gr query heads per KV head, numbered
+  // c = j * gr + g (query j, head g; q [B][nq][Hq][.]); one launch takes the
+  // ncol of them from c0 as its columns.  nq = 1 for QJL keys and the latent.
+  int nq, gr, c0, ncol;
 };
 
 int launch_decode_mfma(const MfmaDecodeArgs& a, int format, int B, int G, hipStream_t st);
@@ -52,7 +56,7 @@ struct TurboDecodeArgs {
 int launch_decode_turbo(const TurboDecodeArgs& a, int B, int G, hipStream_t st);
 
 // Shared-latent cache (512 FP4 + 64 bf16 RoPE), bf16 queries, Hq in {32, 64, 128}.
-bool latent_fast_path_ok(const kv_layout& L, int num_q_heads, int q_dtype);
+bool latent_fast_path_ok(const kv_layout& L, int num_q_heads, int nq, int q_dtype);
 int launch_decode_latent(const MfmaDecodeArgs& a, int B, hipStream_t st);
 
 }  // namespace kvq

@@ -43,7 +43,8 @@ class KVCache(ctypes.Structure):
 
 
 class KVDecodeOpts(ctypes.Structure):
-    _fields_ = [("num_splits", ctypes.c_int32), ("ev_begin", ctypes.c_void_p), ("ev_end", ctypes.c_void_p)]
+    _fields_ = [("num_splits", ctypes.c_int32), ("ev_begin", ctypes.c_void_p), ("ev_end", ctypes.c_void_p),
+                ("num_queries", ctypes.c_int32)]
 
 
 _lib = None

@@ -141,11 +141,20 @@ typedef struct kv_cache {
  *   num_splits   context splits per (sequence, KV head); 0 picks one from the
  *                shape; the workspace size depends on it
  *   ev_begin/end optional hipEvent_t recorded on `stream` immediately before
- *                and after the split-context attention kernel (for timing) */
+ *                and after the split-context attention kernel (for timing)
+ *   num_queries  query tokens per sequence, 1..64 (0 means 1): several drafted
+ *                positions checked in one pass (page "How DeepSeek-V4.1-Flash
+ *                cut KV-cache storage by 4x via CSA2", section "numerical
+ *                precision & hardware efficiency": a draft model proposes
+ *                several positions at once).  The queries are the last
+ *                num_queries tokens of each sequence, already appended; query j
+ *                sees the first seq_lens[b] - (num_queries - 1 - j) tokens.
+ *                The workspace size depends on it. */
 typedef struct kv_decode_opts {
   int32_t num_splits;
   void* ev_begin;
   void* ev_end;
+  int32_t num_queries;
 } kv_decode_opts;
 
 /* Bytes of one buffer of a cache with this layout; 0 if the format has no
@@ -177,6 +186,10 @@ int kv_quant_append(const kv_cache* c, const void* k, const void* v, int32_t in_
 /* One query token per sequence attends over the first seq_lens[b] cached
  * tokens of its sequence (no mask; a query head hq reads KV head hq / (Hq/H)):
  *   out[b][hq] = sum_t softmax_t(scale * logit(q[b][hq], t)) * value(t)
+ * (with opts->num_queries = nq > 1: q[b][j][hq] over the first
+ * seq_lens[b] - (nq - 1 - j) tokens into out[b][j][hq]; q and out carry the
+ * extra [nq] dimension after [B], and each seq_lens[b] must be at least nq: a
+ * query that sees no token gets zeros)
  * (page "TurboQuant vs OSCAR vs EpiCache", section on the KV-cache memory
  * bottleneck: each new token reads the whole cache).  Logits per format: the
  * dot product with the dequantised key (KIVI2, FP4; LATENT: latent part plus

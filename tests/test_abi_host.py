@@ -110,9 +110,9 @@ def _append(c, k=FAKE, v=FAKE, dt=kvq.DT_BF16, start=0, n=1):
 
 
 def _decode(c, q=FAKE, qdt=kvq.DT_BF16, hq=4, lens=FAKE, maxlen=64, scale=1.0, out=FAKE, ws=None,
-            wsb=0, splits=0):
+            wsb=0, splits=0, nq=0):
     nb = ctypes.c_size_t(wsb)
-    opts = kvq.KVDecodeOpts(splits, None, None)
+    opts = kvq.KVDecodeOpts(splits, None, None, nq)
     st = kvq.lib().kv_decode_attention(ctypes.byref(c), q, qdt, hq, lens, maxlen, ctypes.c_float(scale), out,
                                        ws, ctypes.byref(nb), ctypes.byref(opts), None)
     return st, nb.value
@@ -156,3 +156,14 @@ def test_decode_validation_and_size_query():
     assert _decode(c, ws=FAKE, wsb=nb, out=None)[0] == EINVAL
     assert _decode(c, ws=FAKE, wsb=nb, lens=None)[0] == EINVAL
     assert _decode(_cache("bf16"))[0] == EUNSUP
+
+
+def test_decode_num_queries_validation_and_size():
+    c = _cache()
+    _, nb1 = _decode(c, ws=None, splits=4)
+    st, nb5 = _decode(c, ws=None, splits=4, nq=5)
+    assert st == OK and nb5 > nb1                                     # five rows of partials per head
+    assert _decode(c, ws=None, splits=4, nq=1)[1] == nb1              # 1 and 0 both mean one query
+    assert _decode(c, nq=-1)[0] == EINVAL
+    assert _decode(c, nq=65, maxlen=64)[0] == EINVAL                  # more queries than tokens
+    assert _decode(_cache(T=128), nq=65, maxlen=128)[0] == EUNSUP     # beyond 64 queries

@@ -273,6 +273,33 @@ def test_growing_logits_rescale(fmt):
     assert err.max() <= RTOL
 
 
+MULTI = [("fp4", 2), ("fp4", 3), ("fp4", 4), ("fp4", 5), ("fp4", 9), ("kivi2", 3), ("turbo", 2), ("qjl1", 5),
+         ("latent", 2)]
+
+
+@pytest.mark.parametrize("fmt,nq", MULTI)
+def test_multi_query_decode_matches_oracle(fmt, nq):
+    """nq query tokens per sequence, query j over the first L - (nq - 1 - j)
+    tokens: FP4 runs on the matrix cores, 16 (query, head) pairs per launch (G = 4:
+    nq = 3 fills 12 of 16 columns, nq = 5 takes 16 + 4, nq = 9 takes 16 + 16 + 4),
+    the other formats on the general kernel.  Ragged lengths, one of them nq."""
+    cfg = SMALL[fmt]
+    print(f"[multi-query] {fmt} nq={nq} {cfg}", flush=True)
+    cache, K, V = _build(cfg)
+    consts = oracle_constants(cfg)
+    enc = oracle_encode(cfg, host64(K), None if fmt == "latent" else host64(V), consts)
+    q = synth.make_queries(cfg.scaled(hq=nq * cfg.hq), device="cuda")
+    q = q.view(cfg.batch, nq, cfg.hq, q.shape[-1])
+    lens = synth.seq_lens_for(cfg, ragged=True)
+    lens[-1] = nq                                       # the first query sees one token
+    out = cache.decode(q, torch.from_numpy(lens).cuda(), softmax_scale(cfg)).cpu().numpy()
+    ref = OA.decode_attention_multi(fmt, enc, host64(q), lens, softmax_scale(cfg), cfg.hkv, consts,
+                                    latent_dim=cfg.head_dim)
+    err = row_rel_err(out.reshape(-1, out.shape[-1]), ref.reshape(-1, ref.shape[-1]))
+    print(f"  max row rel err {err.max():.3e}", flush=True)
+    assert err.max() <= RTOL
+
+
 @pytest.mark.parametrize("fmt", ["turbo", "qjl1"])
 def test_wide_range_queries(fmt):
     """Queries whose channels span 2^-12 .. 2^3 (and some exact zeros): every
