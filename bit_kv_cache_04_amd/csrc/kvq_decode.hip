@@ -608,9 +608,11 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     f.nq = nq;
     f.gr = num_q_heads / L.num_kv_heads;
     if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), st) != hipSuccess) return KV_EDEVICE;
-    // one launch per 16 (query, head) pairs of a KV head, each over the whole cache
-    for (f.c0 = 0; f.c0 < nq * f.gr; f.c0 += 16) {
-      f.ncol = std::min(16, nq * f.gr - f.c0);
+    // one launch per 32 (FP4: two blocks of 16 columns sharing the dequantised
+    // tiles) or 16 (query, head) pairs of a KV head, each over the whole cache
+    const int per_launch = L.format == KV_FMT_FP4 ? 32 : 16;
+    for (f.c0 = 0; f.c0 < nq * f.gr; f.c0 += per_launch) {
+      f.ncol = std::min(per_launch, nq * f.gr - f.c0);
       int rc = launch_decode_mfma(f, L.format, B, mfma_columns(f.ncol), st);
       if (rc != KV_OK) return rc;
     }

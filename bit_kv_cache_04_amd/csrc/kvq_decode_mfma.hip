@@ -26,6 +26,8 @@
 // S q as an exact fp16 hi + lo pair, so the sum is exact up to fp32 rounding.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 #include "kvq_kernels.h"
@@ -118,10 +120,12 @@ struct KeysFp4 {
     uint32_t s2[2];
   };
   template <int G>
-  __device__ static void load_q(Q& q, const MfmaDecodeArgs& a, int b, int h, int q4, int c) {
-    // column c: pair c0 + c = query token j, head g (columns from ncol on hold none)
-    const bool live = c < a.ncol;
-    const int jq = live ? (a.c0 + c) / a.gr : 0, head = live ? (a.c0 + c) % a.gr : 0;
+  __device__ static void load_q(Q& q, const MfmaDecodeArgs& a, int b, int h, int q4, int c, int col0) {
+    // column col0 + c of the launch: pair c0 + col0 + c = query token j, head g
+    // (columns from ncol on hold none)
+    const int pc = a.c0 + col0 + c;
+    const bool live = col0 + c < a.ncol;
+    const int jq = live ? pc / a.gr : 0, head = live ? pc % a.gr : 0;
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
                          (((size_t)b * a.nq + jq) * a.Hq + (size_t)h * a.gr + head) * 128 + 32 * q4;
 #pragma unroll
@@ -156,17 +160,24 @@ struct KeysFp4 {
       f.s2[blk] = *reinterpret_cast<const uint32_t*>(st + kso + 2048 + 256 * blk);
     }
   }
-  // raw logits of the lane's 8 (token, head) pairs: [blk][v] for token 16 blk + 4 v + q4
-  __device__ static void logits(const Frag& f, const Q& q, f4_t sacc[2]) {
+  // raw logits of the lane's 8 (token, column) pairs per column block nb:
+  // [nb][blk][v] for token 16 blk + 4 v + q4; the blocks share the dequantised keys
+  template <int NB>
+  __device__ static void logits(const Frag& f, const Q* q, f4_t (*sacc)[2]) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const h2_t s_lo = splat_bf16(f.s2[blk] & 0xFFFFu), s_hi = splat_bf16(f.s2[blk] >> 16);
-      f4_t acc = f4_t{0.f, 0.f, 0.f, 0.f};
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8(f.kw[blk].x, s_lo), q.f[0], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8(f.kw[blk].y, s_lo), q.f[1], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8(f.kw[blk].z, s_hi), q.f[2], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8(f.kw[blk].w, s_hi), q.f[3], acc, 0, 0, 0);
-      sacc[blk] = acc;
+      const h8_t k0 = dequant8(f.kw[blk].x, s_lo), k1 = dequant8(f.kw[blk].y, s_lo);
+      const h8_t k2 = dequant8(f.kw[blk].z, s_hi), k3 = dequant8(f.kw[blk].w, s_hi);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        f4_t acc = f4_t{0.f, 0.f, 0.f, 0.f};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, q[nb].f[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, q[nb].f[1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k2, q[nb].f[2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k3, q[nb].f[3], acc, 0, 0, 0);
+        sacc[nb][blk] = acc;
+      }
     }
   }
 };
@@ -197,7 +208,7 @@ struct KeysQjl {
     uint32_t n[8];   // fp16 norm bits of tokens 16 blk + 4 v + q4
   };
   template <int G>
-  __device__ static void load_q(Q& q, const MfmaDecodeArgs& a, int b, int h, int q4, int c) {
+  __device__ static void load_q(Q& q, const MfmaDecodeArgs& a, int b, int h, int q4, int c, int) {
     constexpr int NS = kSlots<G>, NP = 4 / NS;
     const int slot = c / G;
     const bool live = slot < NS;
@@ -270,15 +281,16 @@ struct KeysQjl {
 
 // ---------------------------------------------------------------- the kernel
 
-template <int G>
-__device__ __forceinline__ void logits_of(const KeysFp4::Frag& f, const KeysFp4::Q& q, const MfmaDecodeArgs&,
-                                          f4_t sacc[2]) {
-  KeysFp4::logits(f, q, sacc);
+template <int G, int NB>
+__device__ __forceinline__ void logits_of(const KeysFp4::Frag& f, const KeysFp4::Q* q, const MfmaDecodeArgs&,
+                                          f4_t (*sacc)[2]) {
+  KeysFp4::logits<NB>(f, q, sacc);
 }
-template <int G>
-__device__ __forceinline__ void logits_of(const KeysQjl::Frag& f, const KeysQjl::Q& q, const MfmaDecodeArgs& a,
-                                          f4_t sacc[2]) {
-  KeysQjl::logits<G>(f, q, a.kappa, sacc);
+template <int G, int NB>
+__device__ __forceinline__ void logits_of(const KeysQjl::Frag& f, const KeysQjl::Q* q, const MfmaDecodeArgs& a,
+                                          f4_t (*sacc)[2]) {
+  static_assert(NB == 1, "one column block for QJL keys");
+  KeysQjl::logits<G>(f, q[0], a.kappa, sacc[0]);
 }
 
 // V region of a stage (after the keys): codes 2048 | scales 512.
@@ -306,22 +318,29 @@ __device__ __forceinline__ void issue_tile(uint8_t* st, int lane, int t0, const 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(vr.vs, (lds_ptr_t)(st + Stage<KP>::kVs + 256), 4, so + 256, 0, 0, 0);
 }
 
-// Everything one wave carries across tiles.
-template <class KP>
+// Everything one wave carries across tiles, per block of 16 columns.
+template <class KP, int NB>
 struct WaveState {
-  typename KP::Q q;
-  float m_run, l_run;
-  f4_t o[8];
+  typename KP::Q q[NB];
+  float m_run[NB], l_run[NB];
+  f4_t o[NB][8];
+};
+
+// This lane's token limit per column block (its column's query sees the first
+// L - (nq - 1 - j) tokens, capped by the split's end).
+template <int NB>
+struct Limits {
+  int v[NB];
 };
 
 // One tile: read this lane's fragments from the stage, then (once the reads
 // have returned) refill the stage with tile `t_next` (the sentinel `capacity`
 // when there is none, so that the refill is unconditional and the compiler's
 // wait counts stay exact), then compute.
-template <int G, int NS, class KP>
-__device__ __forceinline__ void tile_step(WaveState<KP>& w, uint8_t* st, int lane, int t0, int t_full, int lim,
-                                          int t_next,
-                                          const MfmaDecodeArgs& a, const typename KP::R& kr, const VRsrc& vr) {
+template <int G, int NS, class KP, int NB>
+__device__ __forceinline__ void tile_step(WaveState<KP, NB>& w, uint8_t* st, int lane, int t0, int t_full,
+                                          const Limits<NB>& lim, int t_next, const MfmaDecodeArgs& a,
+                                          const typename KP::R& kr, const VRsrc& vr) {
   const int q4 = lane >> 4, c = lane & 15;
   // This stage's tile has landed once at most the other NS - 1 stages' refills
   // are outstanding.  Waited for explicitly: the compiler's own wait for loads
@@ -347,57 +366,60 @@ __device__ __forceinline__ void tile_step(WaveState<KP>& w, uint8_t* st, int lan
   issue_tile<KP>(st, lane, t_next, kr, vr);
 
   // ---------------- logits: S^T = K Q^T for the two 16-token blocks
-  f4_t sacc[2];
-  logits_of<G>(kf, w.q, a, sacc);
-  // ---------------- online softmax (this lane: head c, tokens t0 + 16*blk + 4*v + q4)
-  float sv[8];
-  float tmax = -INFINITY;
-  if (t0 + 32 <= t_full) {  // a whole tile for every column: nothing to mask
+  f4_t sacc[NB][2];
+  logits_of<G, NB>(kf, w.q, a, sacc);
+  // ---------------- online softmax (this lane: column 16 nb + c, tokens t0 + 16*blk + 4*v + q4)
+  h8_t pf[NB];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+  for (int nb = 0; nb < NB; ++nb) {
+    float sv[8];
+    float tmax = -INFINITY;
+    if (t0 + 32 <= t_full) {  // a whole tile for every column: nothing to mask
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          sv[4 * blk + v] = sacc[nb][blk][v] * a.scale_log2;
+          tmax = fmaxf(tmax, sv[4 * blk + v]);
+        }
+    } else {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int tok = t0 + 16 * blk + 4 * v + q4;
+          const float sx = tok < lim.v[nb] ? sacc[nb][blk][v] * a.scale_log2 : -INFINITY;
+          sv[4 * blk + v] = sx;
+          tmax = fmaxf(tmax, sx);
+        }
+    }
+    tmax = max_xor16(tmax);
+    tmax = max_xor32(tmax);
+    // The reference max moves only when the tile max exceeds it by more than 2^8
+    // (weights up to 256 are exact enough in fp16 and cannot overflow), so the
+    // accumulator rescale below is rare.
+    const bool bump = tmax > w.m_run[nb] + 8.f;
+    const float m_new = bump ? tmax : w.m_run[nb];
+    const float alpha = bump ? __builtin_amdgcn_exp2f(w.m_run[nb] - m_new) : 1.f;
+    // a column with several queries can meet a tile before its first visible token
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p = __builtin_amdgcn_exp2f(sv[j] - m_ref);
+      psum += p;
+      pf[nb][j] = (_Float16)p;
+    }
+    w.l_run[nb] = w.l_run[nb] * alpha + psum;
+    w.m_run[nb] = m_new;
+    // O rows are columns 4*q4 + v; column hh's alpha lives in lane hh (quarter 0)
+    if (__ballot(bump && 16 * nb + c < a.ncol)) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        sv[4 * blk + v] = sacc[blk][v] * a.scale_log2;
-        tmax = fmaxf(tmax, sv[4 * blk + v]);
+        const float av = __shfl(alpha, (4 * q4 + v) & 15);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) w.o[nb][nt][v] *= av;
       }
-  } else {
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int tok = t0 + 16 * blk + 4 * v + q4;
-        const float s = tok < lim ? sacc[blk][v] * a.scale_log2 : -INFINITY;
-        sv[4 * blk + v] = s;
-        tmax = fmaxf(tmax, s);
-      }
-  }
-  tmax = max_xor16(tmax);
-  tmax = max_xor32(tmax);
-  // The reference max moves only when the tile max exceeds it by more than 2^8
-  // (weights up to 256 are exact enough in fp16 and cannot overflow), so the
-  // accumulator rescale below is rare.
-  const bool bump = tmax > w.m_run + 8.f;
-  const float m_new = bump ? tmax : w.m_run;
-  const float alpha = bump ? __builtin_amdgcn_exp2f(w.m_run - m_new) : 1.f;
-  // a column with several queries can meet a tile before its first visible token
-  const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-  h8_t pf;
-  float psum = 0.f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float p = __builtin_amdgcn_exp2f(sv[j] - m_ref);
-    psum += p;
-    pf[j] = (_Float16)p;
-  }
-  w.l_run = w.l_run * alpha + psum;
-  w.m_run = m_new;
-  // O rows are heads 4*q4 + v; head hh's alpha lives in lane hh (quarter 0)
-  if (__ballot(bump && c < a.ncol)) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float av = __shfl(alpha, (4 * q4 + v) & 15);
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) w.o[nt][v] *= av;
     }
   }
   // ---------------- values: lane (q4, c) takes channels 8c..8c+7 of its 8 tokens.
@@ -416,10 +438,12 @@ __device__ __forceinline__ void tile_step(WaveState<KP>& w, uint8_t* st, int lan
   {                                                                                                      \
     const h8_t bx = h8_from(fp4x2<I>(X[0]) * sp[0], fp4x2<I>(X[1]) * sp[1], fp4x2<I>(X[2]) * sp[2],     \
                             fp4x2<I>(X[3]) * sp[3]);                                                     \
-    w.o[2 * I] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, bx, w.o[2 * I], 0, 0, 0);                    \
+    for (int nb = 0; nb < NB; ++nb)                                                                      \
+      w.o[nb][2 * I] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[nb], bx, w.o[nb][2 * I], 0, 0, 0);      \
     const h8_t by = h8_from(fp4x2<I>(Y[0]) * sp[0], fp4x2<I>(Y[1]) * sp[1], fp4x2<I>(Y[2]) * sp[2],     \
                             fp4x2<I>(Y[3]) * sp[3]);                                                     \
-    w.o[2 * I + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, by, w.o[2 * I + 1], 0, 0, 0);            \
+    for (int nb = 0; nb < NB; ++nb)                                                                      \
+      w.o[nb][2 * I + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[nb], by, w.o[nb][2 * I + 1], 0, 0, 0); \
   }
   KVQ_PV_BYTE(0)
   KVQ_PV_BYTE(1)
@@ -452,9 +476,18 @@ struct LdsBytes<0> {
 #define KVQ_MFMA_STAGES 2  // LDS ring depth per wave (tiles in flight + 1)
 #endif
 
-template <int G, class KP>
+// Waves per SIMD the register budget is cut for: 1-bit QJL keys with G <= 4 fit
+// four (128 registers), two column blocks take two.
+template <int G, class KP, int NB>
+constexpr int kWavesPerEu = NB > 1 ? 2 : (std::is_same<KP, KeysQjl>::value && G <= 4 ? 4 : KVQ_MFMA_WAVES_PER_EU);
+
+// NB blocks of G = 16 columns when NB > 1 (FP4 keys): the blocks share every
+// dequantised key and value operand; twice the accumulators cut the waves per SIMD.
+template <int G, class KP, int NB>
 __global__ void __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(KVQ_MFMA_WAVES_PER_EU, KVQ_MFMA_WAVES_PER_EU))) decode_mfma_kernel(MfmaDecodeArgs a) {
+__attribute__((amdgpu_waves_per_eu(kWavesPerEu<G, KP, NB>, kWavesPerEu<G, KP, NB>)))
+decode_mfma_kernel(MfmaDecodeArgs a) {
+  static_assert(NB == 1 || G == 16, "column blocks are 16 wide");
   constexpr int kStage = Stage<KP>::kBytes;
   constexpr int NS = KVQ_MFMA_STAGES;
   static_assert(NS == 2 || NS == 3, "ring depth");
@@ -480,17 +513,23 @@ __attribute__((amdgpu_waves_per_eu(KVQ_MFMA_WAVES_PER_EU, KVQ_MFMA_WAVES_PER_EU)
   const int L = min(min(a.seq_lens[b], a.max_len), a.cap);
   const int t_begin = split * a.per_split;
   const int t_end = min(L, t_begin + a.per_split);
-  // this lane's column is query token j = (c0 + lane % 16) / gr, which sees the
-  // first L - (nq - 1 - j) tokens; a tile below t_full is whole for every column
-  const int lim = min(t_end, L - (a.nq - 1 - (a.c0 + (lane & 15)) / a.gr));
+  // this lane's column 16 nb + lane % 16 is query token j = (c0 + column) / gr,
+  // which sees the first L - (nq - 1 - j) tokens; a tile below t_full is whole
+  // for every column of the launch
+  Limits<NB> lim;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) lim.v[nb] = min(t_end, L - (a.nq - 1 - (a.c0 + 16 * nb + (lane & 15)) / a.gr));
   const int t_full = min(t_end, L - (a.nq - 1 - a.c0 / a.gr));
 
-  WaveState<KP> w;
-  KP::template load_q<G>(w.q, a, b, h, lane >> 4, lane & 15);
-  w.m_run = -INFINITY;
-  w.l_run = 0.f;
+  WaveState<KP, NB> w;
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt) w.o[nt] = f4_t{0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < NB; ++nb) {
+    KP::template load_q<G>(w.q[nb], a, b, h, lane >> 4, lane & 15, 16 * nb);
+    w.m_run[nb] = -INFINITY;
+    w.l_run[nb] = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) w.o[nb][nt] = f4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
   // Buffer resources over this (sequence, KV head)'s rows: 32-bit offsets, and a
   // read past the end of a resource returns zeros instead of faulting.
@@ -508,18 +547,18 @@ __attribute__((amdgpu_waves_per_eu(KVQ_MFMA_WAVES_PER_EU, KVQ_MFMA_WAVES_PER_EU)
   if constexpr (NS == 2) {
     for (; t0 < t_end; t0 += 256) {
       // the second tile of a pair may lie past t_end: all its tokens are masked
-      tile_step<G, NS, KP>(w, sa, lane, t0, t_full, lim, tile_or_none(t0 + 256), a, kr, vr);
-      tile_step<G, NS, KP>(w, sb, lane, t0 + 128, t_full, lim, tile_or_none(t0 + 384), a, kr, vr);
+      tile_step<G, NS, KP, NB>(w, sa, lane, t0, t_full, lim, tile_or_none(t0 + 256), a, kr, vr);
+      tile_step<G, NS, KP, NB>(w, sb, lane, t0 + 128, t_full, lim, tile_or_none(t0 + 384), a, kr, vr);
     }
   } else {
     uint8_t* sc = stC + wave * kStage;
     issue_tile<KP>(sc, lane, tile_or_none(t0 + 256), kr, vr);
     while (t0 < t_end) {
-      tile_step<G, NS, KP>(w, sa, lane, t0, t_full, lim, tile_or_none(t0 + 384), a, kr, vr);
+      tile_step<G, NS, KP, NB>(w, sa, lane, t0, t_full, lim, tile_or_none(t0 + 384), a, kr, vr);
       if (t0 + 128 >= t_end) break;
-      tile_step<G, NS, KP>(w, sb, lane, t0 + 128, t_full, lim, tile_or_none(t0 + 512), a, kr, vr);
+      tile_step<G, NS, KP, NB>(w, sb, lane, t0 + 128, t_full, lim, tile_or_none(t0 + 512), a, kr, vr);
       if (t0 + 256 >= t_end) break;
-      tile_step<G, NS, KP>(w, sc, lane, t0 + 256, t_full, lim, tile_or_none(t0 + 640), a, kr, vr);
+      tile_step<G, NS, KP, NB>(w, sc, lane, t0 + 256, t_full, lim, tile_or_none(t0 + 640), a, kr, vr);
       t0 += 384;
     }
   }
@@ -532,43 +571,47 @@ __attribute__((amdgpu_waves_per_eu(KVQ_MFMA_WAVES_PER_EU, KVQ_MFMA_WAVES_PER_EU)
   const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   const int q4e = lane_e >> 4, ce = lane_e & 15;
   const int tid_e = wave * 64 + lane_e;
-  float l_run = w.l_run;
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  if (q4e == 0) {
-    sm_m[wave][ce] = w.m_run;
-    sm_l[wave][ce] = l_run;
-  }
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int hh = 4 * q4e + v;
-    if (hh < G) {
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) sm_o[wave][hh][8 * ce + nt] = w.o[nt][v];
+  for (int nb = 0; nb < NB; ++nb) {  // one column block at a time through the same LDS
+    if (nb) __syncthreads();          // the previous block's partials are written
+    float l_run = w.l_run[nb];
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    if (q4e == 0) {
+      sm_m[wave][ce] = w.m_run[nb];
+      sm_l[wave][ce] = l_run;
     }
-  }
-  __syncthreads();
-  for (int e = tid_e; e < G * 128; e += 256) {
-    const int hh = e >> 7, ch = e & 127;
-    float M = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sm_m[ww][hh]);
-    float Ls = 0.f, O = 0.f;
+    for (int v = 0; v < 4; ++v) {
+      const int hh = 4 * q4e + v;
+      if (hh < G) {
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
-      const float mw = sm_m[ww][hh];
-      const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
-      Ls += f * sm_l[ww][hh];
-      O += f * sm_o[ww][hh][ch];
+        for (int nt = 0; nt < 8; ++nt) sm_o[wave][hh][8 * ce + nt] = w.o[nb][nt][v];
+      }
     }
-    if (hh >= a.ncol) continue;  // a column with no query
-    const int pc = a.c0 + hh;
-    const size_t row = ((size_t)b * a.nq + pc / a.gr) * a.Hq + (size_t)h * a.gr + pc % a.gr;
-    float* p = a.part + (row * a.splits + split) * 130;
-    p[2 + ch] = O;
-    if (ch == 0) {
-      p[0] = M;
-      p[1] = Ls;
+    __syncthreads();
+    for (int e = tid_e; e < G * 128; e += 256) {
+      const int hh = e >> 7, ch = e & 127;
+      float M = -INFINITY;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sm_m[ww][hh]);
+      float Ls = 0.f, O = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        const float mw = sm_m[ww][hh];
+        const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
+        Ls += f * sm_l[ww][hh];
+        O += f * sm_o[ww][hh][ch];
+      }
+      if (16 * nb + hh >= a.ncol) continue;  // a column with no query
+      const int pc = a.c0 + 16 * nb + hh;
+      const size_t row = ((size_t)b * a.nq + pc / a.gr) * a.Hq + (size_t)h * a.gr + pc % a.gr;
+      float* p = a.part + (row * a.splits + split) * 130;
+      p[2 + ch] = O;
+      if (ch == 0) {
+        p[0] = M;
+        p[1] = Ls;
+      }
     }
   }
 }
@@ -577,11 +620,17 @@ template <class KP>
 int launch_g(const MfmaDecodeArgs& a, int B, int G, hipStream_t st) {
   dim3 grid(a.splits, a.H, B);
   switch (G) {
-    case 1: decode_mfma_kernel<1, KP><<<grid, 256, 0, st>>>(a); break;
-    case 2: decode_mfma_kernel<2, KP><<<grid, 256, 0, st>>>(a); break;
-    case 4: decode_mfma_kernel<4, KP><<<grid, 256, 0, st>>>(a); break;
-    case 8: decode_mfma_kernel<8, KP><<<grid, 256, 0, st>>>(a); break;
-    case 16: decode_mfma_kernel<16, KP><<<grid, 256, 0, st>>>(a); break;
+    case 1: decode_mfma_kernel<1, KP, 1><<<grid, 256, 0, st>>>(a); break;
+    case 2: decode_mfma_kernel<2, KP, 1><<<grid, 256, 0, st>>>(a); break;
+    case 4: decode_mfma_kernel<4, KP, 1><<<grid, 256, 0, st>>>(a); break;
+    case 8: decode_mfma_kernel<8, KP, 1><<<grid, 256, 0, st>>>(a); break;
+    case 16: decode_mfma_kernel<16, KP, 1><<<grid, 256, 0, st>>>(a); break;
+    case 32:
+      if constexpr (std::is_same<KP, KeysFp4>::value) {
+        decode_mfma_kernel<16, KP, 2><<<grid, 256, 0, st>>>(a);
+        break;
+      }
+      return KV_EUNSUPPORTED;
     default: return KV_EUNSUPPORTED;
   }
   return KV_OK;

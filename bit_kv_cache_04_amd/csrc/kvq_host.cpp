@@ -82,7 +82,7 @@ bool latent_fast_path_ok(const kv_layout& L, int num_q_heads, int nq, int q_dtyp
 }
 
 int mfma_columns(int n) {
-  return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : n <= 8 ? 8 : 16;
+  return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : n <= 8 ? 8 : n <= 16 ? 16 : 32;
 }
 
 bool mfma_fast_path_ok(const kv_layout& L, int num_q_heads, int nq, int q_dtype) {

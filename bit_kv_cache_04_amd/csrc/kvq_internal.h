@@ -38,8 +38,8 @@ bool mfma_fast_path_ok(const kv_layout& L, int num_q_heads, int nq, int q_dtype)
 bool turbo_fast_path_ok(const kv_layout& L, int num_q_heads, int nq);
 // The shared-latent matrix-core kernel covers this cache / query combination.
 bool latent_fast_path_ok(const kv_layout& L, int num_q_heads, int nq, int q_dtype);
-// Columns of the matrix-core kernel that takes n (query, head) pairs, n <= 16:
-// n rounded up to 1, 2, 4, 8 or 16.
+// Columns of the matrix-core kernel that takes n (query, head) pairs, n <= 32:
+// n rounded up to 1, 2, 4, 8, 16 or 32 (two blocks of 16, FP4 keys only).
 int mfma_columns(int n);
 SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int nq, int q_dtype, int max_seq_len, int requested);
 
