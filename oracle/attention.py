@@ -38,6 +38,15 @@ their keys and values already appended, and query j (0-based) sees every token
 up to and including its own position, t < L_b - (nq - 1 - j); nq = 1 is the
 single-query case above.
 
+Mixed precision (decode_attention_mixed): the first `sink` tokens of each
+sequence and its last `recent` tokens are kept in BF16 while the rest of the
+history is compressed (page "TurboQuant vs OSCAR vs EpiCache", section
+"quantization frontiers: TurboQuant and OSCAR": sink and recent tokens stay in
+BF16, the history goes to a low-bit code; about 0.24% of a 128K context stays
+BF16).  Reading: token t of a sequence of length L attends through bf16(k_t),
+bf16(v_t) when t < sink or t >= L - recent, and through its packed code
+otherwise; a window token's logit is the plain <q, bf16(k_t)> for every format.
+
 Logits and dequantised values are computed in token chunks only to bound
 memory; the softmax is taken over the full logit vector.
 """
@@ -47,7 +56,7 @@ import math
 import numpy as np
 
 from . import formats as F
-from .numerics import bf16_from_bits, fp16_from_bits
+from .numerics import bf16_from_bits, fp16_from_bits, round_bf16
 
 CHUNK = 65536
 
@@ -186,4 +195,38 @@ def decode_attention_multi(fmt, cache, q, seq_lens, scale, hkv, consts=None, lat
             if out is None:
                 out = np.zeros((B, nq, Hq, o.shape[1]))
             out[b, :, h * G:(h + 1) * G] = o.reshape(nq, G, -1)
+    return out
+
+
+def decode_attention_mixed(fmt, cache, q, seq_lens, scale, hkv, K_in, V_in, sink, recent, consts=None):
+    """fp64 outputs [B, nq, Hq, d] for q [B, nq, Hq, d] over a cache whose tokens
+    t < sink and t >= L - recent are read as bf16 of the inputs K_in, V_in
+    ([B, H, T, d]) and the others through their packed codes; query j sees the
+    first L - (nq - 1 - j) tokens."""
+    if fmt not in ("fp4", "qjl1"):
+        raise ValueError("mixed precision is defined here for caches with FP4 values")
+    q = np.asarray(q, dtype=np.float64)
+    B, nq, Hq = q.shape[:3]
+    G = Hq // hkv
+    out = np.zeros((B, nq, Hq, K_in.shape[-1]))
+    for b in range(B):
+        L = int(seq_lens[b])
+        if L < nq:
+            raise ValueError("every query must see at least its own token")
+        t = np.arange(L)
+        window = (t < sink) | (t >= L - recent)
+        limit = L - (nq - 1 - np.repeat(np.arange(nq), G))
+        visible = t[None, :] < limit[:, None]
+        for h in range(hkv):
+            qg = q[b, :, h * G:(h + 1) * G].reshape(nq * G, -1)
+            kb = round_bf16(np.asarray(K_in[b, h, :L], np.float64))
+            vb = round_bf16(np.asarray(V_in[b, h, :L], np.float64))
+            logits = np.where(window[None, :], qg @ kb.T,
+                              _key_logits(fmt, cache, b, h, 0, L, qg, consts, 0)) * scale
+            logits = np.where(visible, logits, -np.inf)
+            m = logits.max(axis=1, keepdims=True)
+            p = np.exp(logits - m)
+            p /= p.sum(axis=1, keepdims=True)
+            vals = np.where(window[:, None], vb, _values(fmt, cache, b, h, 0, L, consts, 0))
+            out[b, :, h * G:(h + 1) * G] = (p @ vals).reshape(nq, G, -1)
     return out
