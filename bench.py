@@ -29,10 +29,13 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 
 
-def counted_bytes(cfg, lib_layout, kvq):
-    """Packed KV + scales/norms read by one decode step over cfg.context tokens."""
+def counted_bytes(cfg, lib_layout, kvq, sink=0, recent=0):
+    """Packed KV + scales/norms read by one decode step over cfg.context tokens
+    (with bf16 sink / recent windows: those tokens as bf16 K and V instead)."""
     per_tok = kvq.kv_bytes_per_token(lib_layout, 1)
-    return per_tok * cfg.batch * cfg.context
+    window = min(cfg.context, sink + recent)
+    return (per_tok * cfg.batch * (cfg.context - window)
+            + cfg.batch * cfg.hkv * window * cfg.head_dim * 2 * 2)
 
 
 def cpu_baseline(cfg, budget_s=12.0):
@@ -108,10 +111,10 @@ def measured_traffic(workload):
     return None
 
 
-def roofline(cfg, nbytes, dec_ms, nq=1):
+def roofline(cfg, nbytes, dec_ms, nq=1, windowed=False):
     """Roofline of the split-context attention kernel, timed by events around its launch.
     The counter summaries cover the one-query kernels: traffic is None for nq > 1."""
-    traffic = measured_traffic(cfg.name) if nq == 1 else None
+    traffic = measured_traffic(cfg.name) if nq == 1 and not windowed else None
     if cfg.fmt == "latent":
         # 128 heads x (576 + 512) x 2 flop per token: a dense contraction on fp16 matrix cores
         flops = 2.0 * nq * cfg.batch * cfg.context * cfg.hq * (cfg.key_width + cfg.head_dim)
@@ -133,6 +136,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="fp4_b16_t32k")
     ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--sink", type=int, default=0, help="leading tokens kept bf16 (FP4-valued formats)")
+    ap.add_argument("--recent", type=int, default=0, help="trailing tokens kept bf16 (FP4-valued formats)")
     ap.add_argument("--queries", type=int, default=1,
                     help="query tokens per sequence (drafted positions checked in one pass); the step "
                          "appends that many tokens")
@@ -159,7 +164,7 @@ def main():
                                 synth.gaussian_matrix(cfg.seed, cfg.head_dim, cfg.head_dim, stream=1),
                                 synth.gaussian_matrix(cfg.seed, 128, cfg.head_dim, stream=2))
     cache = PackedKVCache(cfg.fmt, cfg.batch, cfg.hkv, cfg.head_dim, cfg.context, cfg.rope_dim, device=dev,
-                          constants=consts)
+                          constants=consts, sink_tokens=args.sink, recent_tokens=args.recent)
     T = cfg.context
     # prefill the first T - n tokens (untimed), one sequence and 16K tokens at a
     # time to bound input memory
@@ -250,7 +255,7 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
         ms_step = s0.elapsed_time(s1) / args.steps
-    nbytes = counted_bytes(cfg, cache.layout, kvq)
+    nbytes = counted_bytes(cfg, cache.layout, kvq, args.sink, args.recent)
     gbs = nbytes / (ms_step * 1e-3) / 1e9
     achieved = nbytes / (dec_ms * 1e-3) / 1e9
     res = {
@@ -269,13 +274,14 @@ def main():
         "config": {"workload": cfg.name, "format": cfg.fmt, "batch": cfg.batch, "q_heads": cfg.hq,
                    "kv_heads": cfg.hkv, "head_dim": cfg.head_dim, "rope_dim": cfg.rope_dim,
                    "context": T, "counted_bytes_per_step": nbytes,
-                   "splits": args.splits or "auto", "queries_per_seq": nq},
+                   "splits": args.splits or "auto", "queries_per_seq": nq,
+                   "bf16_sink_tokens": args.sink, "bf16_recent_tokens": args.recent},
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "query_tokens_per_s": round(nq * cfg.batch / (ms_step * 1e-3), 1),
         "wall_s": round(wall, 3),
         "timing": "hip-graph replay of the step" if not args.no_graph else "eager launches",
         "ms_per_step_eager": round(ms_eager, 5),
-        "roofline": roofline(cfg, nbytes, dec_ms, nq),
+        "roofline": roofline(cfg, nbytes, dec_ms, nq, bool(args.sink or args.recent)),
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg)

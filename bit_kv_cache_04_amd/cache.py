@@ -24,8 +24,18 @@ def _stream_ptr(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def buffer_view_spec(fmt, B, H, T, d, rope=0, m=128):
+def buffer_view_spec(fmt, B, H, T, d, rope=0, m=128, sink=0, recent=0):
     """{name: (torch dtype, shape)} of each buffer's natural element view."""
+    u8, u16, f32 = torch.uint8, torch.uint16, torch.float32
+    win = {}
+    if sink:
+        win.update(sink_k=(u16, (B, H, sink, d)), sink_v=(u16, (B, H, sink, d)))
+    if recent:
+        win.update(recent_k=(u16, (B, H, recent, d)), recent_v=(u16, (B, H, recent, d)))
+    return {**_packed_view_spec(fmt, B, H, T, d, rope, m), **win}
+
+
+def _packed_view_spec(fmt, B, H, T, d, rope, m):
     u8, u16, f32 = torch.uint8, torch.uint16, torch.float32
     if fmt == "kivi2":
         return dict(k_codes=(u8, (B, H, T, d // 4)), k_scale=(f32, (B, H, T // 32, d)),
@@ -59,10 +69,12 @@ def make_constants(fmt, head_dim, rot_gauss=None, proj_gauss=None):
 
 class PackedKVCache:
     def __init__(self, fmt, batch, num_kv_heads, head_dim, capacity, rope_dim=0, device="cuda",
-                 constants=None):
+                 constants=None, sink_tokens=0, recent_tokens=0):
         self.fmt, self.device = fmt, torch.device(device)
         self.B, self.H, self.d, self.T, self.rope = batch, num_kv_heads, head_dim, capacity, rope_dim
-        self.layout = make_layout(fmt, batch, num_kv_heads, head_dim, capacity, rope_dim)
+        self.sink, self.recent = sink_tokens, recent_tokens
+        self.layout = make_layout(fmt, batch, num_kv_heads, head_dim, capacity, rope_dim, sink_tokens,
+                                  recent_tokens)
         self.bufs = {}
         ptrs = []
         for i, name in enumerate(BUFFERS):
@@ -86,7 +98,7 @@ class PackedKVCache:
         sub = PackedKVCache.__new__(PackedKVCache)
         sub.__dict__.update(self.__dict__)
         sub.B = 1
-        sub.layout = make_layout(self.fmt, 1, self.H, self.d, self.T, self.rope)
+        sub.layout = make_layout(self.fmt, 1, self.H, self.d, self.T, self.rope, self.sink, self.recent)
         sub.bufs = {n: t.view(self.B, -1)[b] for n, t in self.bufs.items()}
         ptrs = [sub.bufs[n].data_ptr() if n in sub.bufs else None for n in BUFFERS]
         c = self.struct
@@ -97,7 +109,8 @@ class PackedKVCache:
 
     # ---- views of the packed bytes
     def view(self, name):
-        dt, shape = buffer_view_spec(self.fmt, self.B, self.H, self.T, self.d, self.rope)[name]
+        dt, shape = buffer_view_spec(self.fmt, self.B, self.H, self.T, self.d, self.rope, sink=self.sink,
+                                     recent=self.recent)[name]
         return self.bufs[name].view(dt).view(shape)
 
     def bytes_per_token(self, num_layers=1):

@@ -1,6 +1,7 @@
 // Exported entry points: argument validation on the host, then the launchers.
 // Nothing here touches a GPU before every check has passed, so each error path
 // can be exercised on a machine without one.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -48,8 +49,12 @@ extern "C" int kv_decode_attention(const kv_cache* c, const void* q, int32_t q_d
   const int nq = opts && opts->num_queries > 0 ? opts->num_queries : 1;
   if ((opts && opts->num_queries < 0) || nq > max_seq_len) return KV_EINVAL;
   if (nq > 64) return KV_EUNSUPPORTED;
-  const SplitPlan plan = plan_splits(&L, num_q_heads, nq, q_dtype, max_seq_len, req);
-  const DecodeWorkspace wsl = decode_workspace(&L, nq * num_q_heads, plan.splits);
+  // mixed precision: the splits cover the packed tokens from sink_tokens on, and
+  // the bf16 window adds one split of partial rows
+  const int packed_len = std::max(1, max_seq_len - L.sink_tokens);
+  const SplitPlan plan = plan_splits(&L, num_q_heads, nq, q_dtype, packed_len, req);
+  const int part_splits = plan.splits + window_chunks(L);
+  const DecodeWorkspace wsl = decode_workspace(&L, nq * num_q_heads, part_splits);
   if (!ws) {
     if (!ws_bytes) return KV_EINVAL;
     *ws_bytes = wsl.total;

@@ -7,6 +7,8 @@
 // projection are the only dense contractions here and run on the matrix cores.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include <algorithm>
 
 #include "kvq_device.h"
@@ -932,6 +934,46 @@ __global__ void __launch_bounds__(512) turbo_append_small_kernel(
   }
 }
 
+// bf16 copies of appended tokens [t_a, t_b) (positions; the append covers
+// [start, start + n)) for a mixed-precision cache: token t goes to slot t of the
+// sink, or to slot t mod `slots` of the recent ring when `ring` is set.  Eight
+// channels per thread; fp32 inputs round to nearest even.
+template <typename InT>
+__global__ void __launch_bounds__(256) window_copy_kernel(const InT* __restrict__ k, const InT* __restrict__ v,
+                                                          int d, uint16_t* __restrict__ dk,
+                                                          uint16_t* __restrict__ dv, int slots, int ring,
+                                                          int bh_count, int n, int start, int t_a, int t_b) {
+  const int per_row = d / 8, nt = t_b - t_a;
+  const size_t half = (size_t)bh_count * nt * per_row;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < 2 * half; i += (size_t)gridDim.x * 256) {
+    const bool is_v = i >= half;
+    const size_t j = is_v ? i - half : i;
+    const int c8 = (int)(j % per_row) * 8;
+    const int tt = (int)((j / per_row) % nt);
+    const size_t bh = j / ((size_t)per_row * nt);
+    const int t = t_a + tt;
+    const InT* src = (is_v ? v : k) + (bh * n + (t - start)) * d + c8;
+    uint32_t w[4];
+    if constexpr (std::is_same<InT, uint16_t>::value) {
+      const uint4 r = *reinterpret_cast<const uint4*>(src);
+      w[0] = r.x; w[1] = r.y; w[2] = r.z; w[3] = r.w;
+    } else {
+      const float4 x0 = *reinterpret_cast<const float4*>(src), x1 = *reinterpret_cast<const float4*>(src + 4);
+      const float f[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t lo = __float_as_uint(f[2 * e]), hi = __float_as_uint(f[2 * e + 1]);
+        lo = (lo + 0x7FFFu + ((lo >> 16) & 1u)) >> 16;
+        hi = (hi + 0x7FFFu + ((hi >> 16) & 1u)) >> 16;
+        w[e] = lo | (hi << 16);
+      }
+    }
+    const int slot = ring ? t % slots : t;
+    uint16_t* dst = (is_v ? dv : dk) + (bh * slots + slot) * d + c8;
+    *reinterpret_cast<uint4*>(dst) = uint4{w[0], w[1], w[2], w[3]};
+  }
+}
+
 int blocks_for(size_t threads) { return (int)((threads + 255) / 256); }
 
 // Workgroups of the QJL append: one resident round (each stages S once).
@@ -998,6 +1040,19 @@ int append_typed(const kv_cache* c, const InT* k, const InT* v, int start, int n
     default:
       return KV_EUNSUPPORTED;
   }
+  // mixed precision: bf16 copies of the sink tokens and of the append's last
+  // recent_tokens tokens (older ring slots are overwritten by later appends)
+  auto copies = [&](uint16_t* dk, uint16_t* dv, int slots, int ring, int t_a, int t_b) {
+    if (t_b <= t_a) return;
+    const size_t items = 2 * (size_t)bh * (t_b - t_a) * (d / 8);
+    window_copy_kernel<InT><<<blocks_for(items), 256, 0, st>>>(k, v, d, dk, dv, slots, ring, bh, n, start, t_a, t_b);
+  };
+  if (L.sink_tokens)
+    copies(static_cast<uint16_t*>(c->buf[KV_BUF_SINK_K]), static_cast<uint16_t*>(c->buf[KV_BUF_SINK_V]),
+           L.sink_tokens, 0, start, std::min(start + n, L.sink_tokens));
+  if (L.recent_tokens)
+    copies(static_cast<uint16_t*>(c->buf[KV_BUF_RECENT_K]), static_cast<uint16_t*>(c->buf[KV_BUF_RECENT_V]),
+           L.recent_tokens, 1, std::max(start, start + n - L.recent_tokens), start + n);
   return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
 }
 

@@ -42,8 +42,9 @@ struct DecodeArgs {
   int max_len;
   float scale_log2;  // softmax scale * log2(e)
   float kappa;       // sqrt(pi/2) / m
-  float* part;       // [B][nq][Hq][splits][DV + 2]: m (log2 units), l, o[DV]
+  float* part;       // [B][nq][Hq][part_splits][DV + 2]: m (log2 units), l, o[DV]
   int splits, per_split;
+  int t_lo, recent, part_splits;  // packed tokens [t_lo, L - recent), split s from t_lo + s * per_split
 };
 
 // ---------------------------------------------------------------- per-format element access
@@ -122,8 +123,8 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
   const int nh = min(a.hb_size, a.G - vh0);
   const size_t bh = (size_t)b * a.H + h;
   const int L = min(min(a.seq_lens[b], a.max_len), a.cap);
-  const int t_begin = split * a.per_split;
-  const int t_end = min(L, t_begin + a.per_split);
+  const int t_begin = a.t_lo + split * a.per_split;
+  const int t_end = min(max(a.t_lo, L - a.recent), t_begin + a.per_split);
   // query / output row of block row hh; query j sees the first L - (nq - 1 - j) tokens
   auto qrow = [&](int hh) {
     const int vh = vh0 + hh;
@@ -203,12 +204,142 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
     if (e < HB * DV) {
       const int hh = e / DV, c = e % DV;
       if (hh < nh) {
-        float* p = a.part + (qrow(hh) * a.splits + split) * (DV + 2);
+        float* p = a.part + (qrow(hh) * a.part_splits + split) * (DV + 2);
         p[2 + c] = o[j];
         if (c == 0) {
           p[0] = ms[hh];
           p[1] = ls[hh];
         }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- bf16 windows
+
+// Mixed precision: attention of the (query, head) rows of one (sequence, KV
+// head) over the tokens its cache keeps in bf16, the sink t < S and the recent
+// t >= L - W (the packed kernels cover [S, L - W)).  The logit is <q, bf16 key>.
+// Window positions p enumerate those tokens in order; workgroup (chunk, row
+// block) takes positions [64 chunk, 64 chunk + 64) for 16 rows and writes them
+// as split `split + chunk` of the partial rows, so that the window's short
+// serial chains run side by side.
+constexpr int kWinChunk = 64;
+
+struct WindowArgs {
+  const void* q;  // raw queries [B][nq][Hq][D] (fp32 or bf16)
+  const uint16_t *sink_k, *sink_v, *rec_k, *rec_v;
+  const int32_t* seq_lens;
+  int max_len, cap, H, Hq, gr, nq, S, W;
+  float scale_log2;
+  float* part;
+  int part_splits, split, row_blocks;
+};
+
+template <typename QT, int D>
+__global__ void __launch_bounds__(256) decode_window_kernel(WindowArgs a) {
+  constexpr int NT = 256, HB = 16, TT = 32, OPT = HB * D / NT, C8 = D / 8;
+  __shared__ float qs[HB][D];
+  __shared__ float ks[TT][D + 1];
+  __shared__ float vs[TT][D + 1];
+  __shared__ float ss[HB][TT];
+  __shared__ float ms[HB], ls[HB], al[HB];
+  __shared__ int lim[HB];
+  const int tid = threadIdx.x;
+  const int rb = blockIdx.x % a.row_blocks, chunk = blockIdx.x / a.row_blocks;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int vh0 = rb * HB;
+  const int nh = min(HB, a.nq * a.gr - vh0);
+  const size_t bh = (size_t)b * a.H + h;
+  const int L = min(min(a.seq_lens[b], a.max_len), a.cap);
+  const int ns = min(a.S, L);        // sink tokens [0, ns)
+  const int rs = max(a.S, L - a.W);  // recent tokens [rs, L)
+  const int nw = ns + max(0, L - rs);
+  const int p_begin = chunk * kWinChunk, p_end = min(nw, p_begin + kWinChunk);
+  auto token = [&](int p) { return p < ns ? p : rs + (p - ns); };
+  auto qrow = [&](int hh) {
+    const int vh = vh0 + hh;
+    return ((size_t)b * a.nq + vh / a.gr) * a.Hq + (size_t)h * a.gr + vh % a.gr;
+  };
+  for (int e = tid; e < HB * D; e += NT) {
+    const int hh = e / D, c = e % D;
+    qs[hh][c] = hh < nh ? load_as_f32(static_cast<const QT*>(a.q) + qrow(hh) * D, c) : 0.f;
+  }
+  if (tid < HB) {
+    ms[tid] = -INFINITY;
+    ls[tid] = 0.f;
+    lim[tid] = L - (a.nq - 1 - (vh0 + tid) / a.gr);
+  }
+  float o[OPT];
+#pragma unroll
+  for (int j = 0; j < OPT; ++j) o[j] = 0.f;
+  __syncthreads();
+  for (int p0 = p_begin; p0 < p_end; p0 += TT) {
+    const int nt = min(TT, p_end - p0);
+    // 8 bf16 of one token's K and V per thread and step (16-byte loads)
+    for (int e = tid; e < TT * C8; e += NT) {
+      const int t = e / C8, c8 = (e % C8) * 8;
+      uint4 kr{0u, 0u, 0u, 0u}, vr{0u, 0u, 0u, 0u};
+      if (t < nt) {
+        const int tok = token(p0 + t);
+        const size_t off = tok < a.S ? (bh * a.S + tok) * D + c8 : (bh * a.W + tok % a.W) * D + c8;
+        kr = *reinterpret_cast<const uint4*>((tok < a.S ? a.sink_k : a.rec_k) + off);
+        vr = *reinterpret_cast<const uint4*>((tok < a.S ? a.sink_v : a.rec_v) + off);
+      }
+      const uint32_t kw[4] = {kr.x, kr.y, kr.z, kr.w}, vw[4] = {vr.x, vr.y, vr.z, vr.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ks[t][c8 + 2 * i] = __uint_as_float(kw[i] << 16);
+        ks[t][c8 + 2 * i + 1] = __uint_as_float(kw[i] & 0xFFFF0000u);
+        vs[t][c8 + 2 * i] = __uint_as_float(vw[i] << 16);
+        vs[t][c8 + 2 * i + 1] = __uint_as_float(vw[i] & 0xFFFF0000u);
+      }
+    }
+    __syncthreads();
+    for (int p = tid; p < nh * TT; p += NT) {
+      const int hh = p / TT, t = p % TT;
+      float sx = 0.f;
+      for (int c = 0; c < D; ++c) sx = fmaf(qs[hh][c], ks[t][c], sx);
+      ss[hh][t] = (t < nt && token(p0 + t) < lim[hh]) ? sx * a.scale_log2 : -INFINITY;
+    }
+    __syncthreads();
+    if (tid < nh) {
+      float mx = -INFINITY;
+      for (int t = 0; t < nt; ++t) mx = fmaxf(mx, ss[tid][t]);
+      const float mnew = fmaxf(ms[tid], mx);
+      const float mref = mnew == -INFINITY ? 0.f : mnew;  // a row that has seen no token yet
+      const float alpha = exp2f(ms[tid] - mref);
+      float sum = 0.f;
+      for (int t = 0; t < TT; ++t) {
+        const float pw = t < nt ? exp2f(ss[tid][t] - mref) : 0.f;
+        ss[tid][t] = pw;
+        sum += pw;
+      }
+      ls[tid] = ls[tid] * alpha + sum;
+      ms[tid] = mnew;
+      al[tid] = alpha;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < OPT; ++j) {
+      const int e = tid + j * NT, hh = e / D, c = e % D;
+      if (hh < nh) {
+        float acc = o[j] * al[hh];
+        for (int t = 0; t < nt; ++t) acc = fmaf(ss[hh][t], vs[t][c], acc);
+        o[j] = acc;
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int j = 0; j < OPT; ++j) {
+    const int e = tid + j * NT, hh = e / D, c = e % D;
+    if (hh < nh) {
+      float* p = a.part + (qrow(hh) * a.part_splits + a.split + chunk) * (D + 2);
+      p[2 + c] = o[j];
+      if (c == 0) {
+        p[0] = ms[hh];
+        p[1] = ls[hh];
       }
     }
   }
@@ -507,6 +638,41 @@ void launch_split(const DecodeArgs& a, int B, hipStream_t st) {
   decode_split_kernel<FMT, DK, DV, 32, HB><<<grid, 256, 0, st>>>(a);
 }
 
+// The bf16 window split of a mixed-precision cache (partial split `split`).
+void launch_window(const kv_cache* c, const void* q, int q_dtype, int num_q_heads, int nq, const int32_t* seq_lens,
+                   int max_seq_len, float scale, float* part, int part_splits, int split, hipStream_t st) {
+  const kv_layout& L = c->layout;
+  WindowArgs w{};
+  w.q = q;
+  w.sink_k = static_cast<const uint16_t*>(c->buf[KV_BUF_SINK_K]);
+  w.sink_v = static_cast<const uint16_t*>(c->buf[KV_BUF_SINK_V]);
+  w.rec_k = static_cast<const uint16_t*>(c->buf[KV_BUF_RECENT_K]);
+  w.rec_v = static_cast<const uint16_t*>(c->buf[KV_BUF_RECENT_V]);
+  w.seq_lens = seq_lens;
+  w.max_len = max_seq_len;
+  w.cap = L.capacity;
+  w.H = L.num_kv_heads;
+  w.Hq = num_q_heads;
+  w.gr = num_q_heads / L.num_kv_heads;
+  w.nq = nq;
+  w.S = L.sink_tokens;
+  w.W = L.recent_tokens;
+  w.scale_log2 = scale * kLog2e;
+  w.part = part;
+  w.part_splits = part_splits;
+  w.split = split;
+  w.row_blocks = (nq * w.gr + 15) / 16;
+  const dim3 grid(w.row_blocks * window_chunks(L), L.num_kv_heads, L.batch);
+  const bool f32 = q_dtype == KV_DT_F32;
+  if (L.head_dim == 64) {
+    if (f32) decode_window_kernel<float, 64><<<grid, 256, 0, st>>>(w);
+    else decode_window_kernel<uint16_t, 64><<<grid, 256, 0, st>>>(w);
+  } else {
+    if (f32) decode_window_kernel<float, 128><<<grid, 256, 0, st>>>(w);
+    else decode_window_kernel<uint16_t, 128><<<grid, 256, 0, st>>>(w);
+  }
+}
+
 }  // namespace
 
 int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads, int nq, const int32_t* seq_lens,
@@ -519,6 +685,10 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
   float* part = reinterpret_cast<float*>(wsb + wsl.part_off);
   const int B = L.batch;
   const int rows = B * nq * num_q_heads;  // (sequence, query token, query head)
+  // mixed precision: the packed kernels take [sink, L - recent) and the bf16
+  // window kernel one more split
+  const bool windowed = L.sink_tokens || L.recent_tokens;
+  const int part_splits = plan.splits + window_chunks(L);
   const int qw_in = query_width(&L), qw_out = prepared_query_width(&L);
   if (latent_fast_path_ok(L, num_q_heads, nq, q_dtype)) {
     MfmaDecodeArgs f{};
@@ -539,7 +709,7 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     int rc = launch_decode_latent(f, B, st);
     if (rc != KV_OK) return rc;
     if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess) return KV_EDEVICE;
-    launch_merge(part, rows, plan.splits, L.head_dim, L.format, c->rot, out, st);
+    launch_merge(part, rows, part_splits, L.head_dim, L.format, c->rot, out, st);
     return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
   }
   const bool mfma = mfma_fast_path_ok(L, num_q_heads, nq, q_dtype);
@@ -582,7 +752,7 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     int rc = launch_decode_turbo(f, B, num_q_heads / L.num_kv_heads, st);
     if (rc != KV_OK) return rc;
     if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess) return KV_EDEVICE;
-    launch_merge(part, rows, plan.splits, L.head_dim, L.format, c->rot, out, st);
+    launch_merge(part, rows, part_splits, L.head_dim, L.format, c->rot, out, st);
     return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
   }
   if (mfma) {
@@ -607,6 +777,9 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     f.per_split = plan.tokens_per_split;
     f.nq = nq;
     f.gr = num_q_heads / L.num_kv_heads;
+    f.t_lo = L.sink_tokens;
+    f.recent = L.recent_tokens;
+    f.part_splits = part_splits;
     if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), st) != hipSuccess) return KV_EDEVICE;
     // one launch per 32 (FP4: two blocks of 16 columns sharing the dequantised
     // tiles) or 16 (query, head) pairs of a KV head, each over the whole cache
@@ -616,8 +789,10 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
       int rc = launch_decode_mfma(f, L.format, B, mfma_columns(f.ncol), st);
       if (rc != KV_OK) return rc;
     }
+    if (windowed) launch_window(c, q, q_dtype, num_q_heads, nq, seq_lens, max_seq_len, scale, part, part_splits,
+                                plan.splits, st);
     if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess) return KV_EDEVICE;
-    launch_merge(part, rows, plan.splits, L.head_dim, L.format, c->rot, out, st);
+    launch_merge(part, rows, part_splits, L.head_dim, L.format, c->rot, out, st);
     return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
   }
 
@@ -652,6 +827,9 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
   a.part = part;
   a.splits = plan.splits;
   a.per_split = plan.tokens_per_split;
+  a.t_lo = L.sink_tokens;
+  a.recent = L.recent_tokens;
+  a.part_splits = part_splits;
 
   if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), st) != hipSuccess) return KV_EDEVICE;
   switch (L.format) {
@@ -668,8 +846,10 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     case KV_FMT_LATENT_FP4: launch_split<KV_FMT_LATENT_FP4, 576, 512, 16>(a, B, st); break;
     default: return KV_EUNSUPPORTED;
   }
+  if (windowed) launch_window(c, q, q_dtype, num_q_heads, nq, seq_lens, max_seq_len, scale, part, part_splits,
+                              plan.splits, st);
   if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess) return KV_EDEVICE;
-  launch_merge(part, rows, plan.splits, L.head_dim, L.format, c->rot, out, st);
+  launch_merge(part, rows, part_splits, L.head_dim, L.format, c->rot, out, st);
   return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
 }
 

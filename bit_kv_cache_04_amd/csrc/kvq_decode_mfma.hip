@@ -511,8 +511,8 @@ decode_mfma_kernel(MfmaDecodeArgs a) {
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const size_t bh = (size_t)b * a.H + h;
   const int L = min(min(a.seq_lens[b], a.max_len), a.cap);
-  const int t_begin = split * a.per_split;
-  const int t_end = min(L, t_begin + a.per_split);
+  const int t_begin = a.t_lo + split * a.per_split;
+  const int t_end = min(max(a.t_lo, L - a.recent), t_begin + a.per_split);
   // this lane's column 16 nb + lane % 16 is query token j = (c0 + column) / gr,
   // which sees the first L - (nq - 1 - j) tokens; a tile below t_full is whole
   // for every column of the launch
@@ -606,7 +606,7 @@ decode_mfma_kernel(MfmaDecodeArgs a) {
       if (16 * nb + hh >= a.ncol) continue;  // a column with no query
       const int pc = a.c0 + 16 * nb + hh;
       const size_t row = ((size_t)b * a.nq + pc / a.gr) * a.Hq + (size_t)h * a.gr + pc % a.gr;
-      float* p = a.part + (row * a.splits + split) * 130;
+      float* p = a.part + (row * a.part_splits + split) * 130;
       p[2 + ch] = O;
       if (ch == 0) {
         p[0] = M;

@@ -14,8 +14,12 @@ namespace kvq {
 int check_layout(const kv_layout* L) {
   if (!L) return KV_EINVAL;
   if (L->batch < 1 || L->num_kv_heads < 1 || L->head_dim < 1 || L->capacity < 1 ||
-      L->rope_dim < 0 || L->group < 0 || L->qjl_m < 0 || L->lm_bits < 0)
+      L->rope_dim < 0 || L->group < 0 || L->qjl_m < 0 || L->lm_bits < 0 || L->sink_tokens < 0 ||
+      L->recent_tokens < 0 || L->sink_tokens > L->capacity || L->recent_tokens > L->capacity)
     return KV_EINVAL;
+  // bf16 sink / recent windows: caches whose values are FP4 (outputs in the original basis)
+  if ((L->sink_tokens || L->recent_tokens) && L->format != KV_FMT_FP4 && L->format != KV_FMT_QJL1_FP4V)
+    return KV_EUNSUPPORTED;
   switch (L->format) {
     case KV_FMT_KIVI2:
       if (L->head_dim != 64 && L->head_dim != 128) return KV_EUNSUPPORTED;
@@ -152,6 +156,8 @@ extern "C" size_t kv_buffer_bytes(const kv_layout* L, int32_t which) {
   if (check_layout(L) != KV_OK || which < 0 || which >= KV_BUF_COUNT) return 0;
   const size_t B = L->batch, H = L->num_kv_heads, T = L->capacity, d = L->head_dim;
   const size_t bht = B * H * T;
+  if (which == KV_BUF_SINK_K || which == KV_BUF_SINK_V) return B * H * (size_t)L->sink_tokens * d * 2;
+  if (which == KV_BUF_RECENT_K || which == KV_BUF_RECENT_V) return B * H * (size_t)L->recent_tokens * d * 2;
   switch (L->format) {
     case KV_FMT_KIVI2:
       switch (which) {
@@ -204,7 +210,8 @@ extern "C" size_t kv_bytes_per_token(const kv_layout* L, int32_t num_layers) {
   // token slots (B*capacity for the latent), so divide by that.
   size_t slots = (size_t)L->batch * L->num_kv_heads * L->capacity;
   size_t total = 0;
-  for (int b = 0; b < KV_BUF_COUNT; ++b) total += kv_buffer_bytes(L, b);
+  for (int b = 0; b < KV_BUF_COUNT; ++b)
+    if (b < KV_BUF_SINK_K) total += kv_buffer_bytes(L, b);  // not the per-sequence bf16 windows
   return (size_t)num_layers * L->num_kv_heads * (total / slots);
 }
 

@@ -55,6 +55,9 @@ constexpr int kPieceProductBytes = 4 * 144;
 constexpr int kTurboPieceBytes = 3 * kPieceProductBytes;  // code words 0..3, 4..7, sketch
 constexpr int kQjlPieceBytes = kPieceProductBytes;        // sketch
 DecodeWorkspace decode_workspace(const kv_layout* L, int num_q_heads, int splits);
+// Mixed precision: splits of partial rows the bf16 window takes (one per 64 of
+// its sink_tokens + recent_tokens positions), 0 without a window.
+inline int window_chunks(const kv_layout& L) { return (L.sink_tokens + L.recent_tokens + 63) / 64; }
 
 // Device launchers (defined in the HIP translation units).  Arguments are
 // validated by the caller.

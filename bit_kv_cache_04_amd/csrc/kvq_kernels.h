@@ -30,6 +30,9 @@ struct MfmaDecodeArgs {
   // c = j * gr + g (query j, head g; q [B][nq][Hq][.]); one launch takes the
   // ncol of them from c0 as its columns.  nq = 1 for QJL keys and the latent.
   int nq, gr, c0, ncol;
+  // packed tokens [t_lo, L - recent) of a sequence of length L (split s from
+  // t_lo + s * per_split); partial rows hold part_splits splits
+  int t_lo, recent, part_splits;
 };
 
 int launch_decode_mfma(const MfmaDecodeArgs& a, int format, int B, int G, hipStream_t st);

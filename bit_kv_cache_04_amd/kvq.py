@@ -19,7 +19,7 @@ DT_F32, DT_BF16 = 0, 1
 STATUS = {0: "KV_OK", -1: "KV_EINVAL", -2: "KV_ECAPACITY", -3: "KV_EUNSUPPORTED",
           -4: "KV_EWORKSPACE", -5: "KV_EDEVICE"}
 BUFFERS = ["k_codes", "k_scale", "k_zero", "k_sketch", "k_norm", "k_rnorm",
-           "v_codes", "v_scale", "v_zero", "v_norm", "rope"]
+           "v_codes", "v_scale", "v_zero", "v_norm", "rope", "sink_k", "sink_v", "recent_k", "recent_v"]
 EXPORTED = ["kv_buffer_bytes", "kv_bytes_per_token", "kv_quant_append", "kv_decode_attention",
             "kv_lloyd_max_gaussian", "kv_make_rotation", "kv_make_projection", "kv_status_string"]
 
@@ -33,7 +33,8 @@ class KvError(RuntimeError):
 class KVLayout(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int32), ("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("rope_dim", ctypes.c_int32), ("capacity", ctypes.c_int32),
-                ("group", ctypes.c_int32), ("qjl_m", ctypes.c_int32), ("lm_bits", ctypes.c_int32)]
+                ("group", ctypes.c_int32), ("qjl_m", ctypes.c_int32), ("lm_bits", ctypes.c_int32),
+                ("sink_tokens", ctypes.c_int32), ("recent_tokens", ctypes.c_int32)]
 
 
 class KVCache(ctypes.Structure):
@@ -80,13 +81,14 @@ def lib():
     return _lib
 
 
-def make_layout(fmt, batch, num_kv_heads, head_dim, capacity, rope_dim=0):
-    """A kv_layout with the format's fixed group / sketch / codebook parameters."""
+def make_layout(fmt, batch, num_kv_heads, head_dim, capacity, rope_dim=0, sink=0, recent=0):
+    """A kv_layout with the format's fixed group / sketch / codebook parameters
+    (sink / recent: tokens kept bf16 at the start and end of each sequence)."""
     f = FMT[fmt] if isinstance(fmt, str) else int(fmt)
     group = {1: 32, 2: 16, 4: 16, 5: 16}.get(f, 0)
     qjl_m = 128 if f in (3, 4) else 0
     lm_bits = 2 if f == 3 else 0
-    return KVLayout(f, batch, num_kv_heads, head_dim, rope_dim, capacity, group, qjl_m, lm_bits)
+    return KVLayout(f, batch, num_kv_heads, head_dim, rope_dim, capacity, group, qjl_m, lm_bits, sink, recent)
 
 
 def _check(fn, st):

@@ -85,7 +85,17 @@ enum kv_status {
  * qjl_m 128, lm_bits 2; QJL1_FP4V head_dim 128, qjl_m 128, group 16;
  * LATENT_FP4 num_kv_heads 1, head_dim 512, rope_dim 64, group 16.  Fields a
  * format does not use must be 0, except `group`, which is always the format's
- * quantisation group (0 for TURBO). */
+ * quantisation group (0 for TURBO).
+ *
+ * Mixed precision (FP4 and QJL1_FP4V only, both <= capacity): the first
+ * sink_tokens tokens of every sequence and its last recent_tokens tokens are
+ * also kept in bf16 and decode reads them from there, the rest through the
+ * packed codes (page "TurboQuant vs OSCAR vs EpiCache", section "quantization
+ * frontiers: TurboQuant and OSCAR": sink and recent tokens stay BF16 while the
+ * history is compressed).  A window token's logit is <q, bf16 key>.  The recent
+ * window is a ring of the last recent_tokens tokens appended to a sequence
+ * (slot t mod recent_tokens), so decode must see each sequence at the length
+ * it was appended to.  0 and 0 turn it off. */
 typedef struct kv_layout {
   int32_t format;       /* enum kv_format */
   int32_t batch;        /* sequences B */
@@ -96,6 +106,8 @@ typedef struct kv_layout {
   int32_t group;        /* FP4 scale group (16) or KIVI group (32) */
   int32_t qjl_m;        /* QJL sketch rows (TURBO, QJL1_FP4V) */
   int32_t lm_bits;      /* Lloyd-Max bits (TURBO) */
+  int32_t sink_tokens;   /* leading tokens kept bf16 (mixed precision), else 0 */
+  int32_t recent_tokens; /* trailing tokens kept bf16 (mixed precision), else 0 */
 } kv_layout;
 
 /* Buffers of a cache, by role.  Element types and shapes (Tc = capacity):
@@ -110,11 +122,14 @@ typedef struct kv_layout {
  *   V_SCALE  KIVI2 f32 [B][H][Tc][d/32]; FP4, QJL1 bf16 [B][H][Tc][d/16]
  *   V_ZERO   f32  KIVI2 [B][H][Tc][d/32]
  *   V_NORM   f16  TURBO [B][H][Tc]
- *   ROPE     bf16 LATENT [B][Tc][rope_dim]                                   */
+ *   ROPE     bf16 LATENT [B][Tc][rope_dim]
+ *   SINK_K, SINK_V      bf16 [B][H][sink_tokens][d]    (mixed precision)
+ *   RECENT_K, RECENT_V  bf16 [B][H][recent_tokens][d]  (mixed precision; token
+ *                       t in slot t mod recent_tokens)                         */
 enum kv_buffer {
   KV_BUF_K_CODES = 0, KV_BUF_K_SCALE, KV_BUF_K_ZERO, KV_BUF_K_SKETCH, KV_BUF_K_NORM,
   KV_BUF_K_RNORM, KV_BUF_V_CODES, KV_BUF_V_SCALE, KV_BUF_V_ZERO, KV_BUF_V_NORM,
-  KV_BUF_ROPE, KV_BUF_COUNT
+  KV_BUF_ROPE, KV_BUF_SINK_K, KV_BUF_SINK_V, KV_BUF_RECENT_K, KV_BUF_RECENT_V, KV_BUF_COUNT
 };
 
 /* A cache: its layout, device buffers (NULL where the format has none) and
@@ -166,7 +181,9 @@ size_t kv_buffer_bytes(const kv_layout* L, int32_t which);
  * as 1/32 per token) for all KV heads (page "TurboQuant vs OSCAR vs EpiCache",
  * KV-cache memory bottleneck section: layers x KV heads x head dim x 2 x bytes
  * per element for BF16).  Host only; returns 0 for an invalid layout or
- * num_layers < 1.  BF16 needs only format, num_kv_heads and head_dim. */
+ * num_layers < 1.  BF16 needs only format, num_kv_heads and head_dim.  The
+ * bf16 sink and recent windows of mixed precision are a fixed cost per
+ * sequence, not per token, and are not counted. */
 size_t kv_bytes_per_token(const kv_layout* L, int32_t num_layers);
 
 /* Append n_new tokens at positions [start, start+n_new) of every sequence.
@@ -179,7 +196,9 @@ size_t kv_bytes_per_token(const kv_layout* L, int32_t num_layers);
  * KV_EINVAL otherwise.  start + n_new > capacity: KV_ECAPACITY.  n_new == 0
  * enqueues nothing.  The method's encoding steps are those of the format
  * definitions above (TurboQuant: norm, rotate, divide, Lloyd-Max code,
- * residual, residual norm, sketch of the residual, in that order). */
+ * residual, residual norm, sketch of the residual, in that order).  With mixed
+ * precision every token is still packed; tokens below sink_tokens and the last
+ * recent_tokens of the append are also stored as bf16 (round to nearest even). */
 int kv_quant_append(const kv_cache* c, const void* k, const void* v, int32_t in_dtype,
                     int32_t start, int32_t n_new, void* ws, size_t* ws_bytes, void* stream);
 

@@ -42,9 +42,9 @@ def library_constants(cfg):
     return make_constants(cfg.fmt, cfg.head_dim, g_rot, g_proj)
 
 
-def new_cache(cfg, capacity=None):
+def new_cache(cfg, capacity=None, **kw):
     return PackedKVCache(cfg.fmt, cfg.batch, cfg.hkv, cfg.head_dim, capacity or cfg.context, cfg.rope_dim,
-                         device="cuda", constants=library_constants(cfg))
+                         device="cuda", constants=library_constants(cfg), **kw)
 
 
 def inputs(cfg, device="cuda"):
@@ -82,6 +82,8 @@ def gpu_buffers(cache, t0=0, t1=None):
     t1 = cache.T if t1 is None else t1
     out = {}
     for name in cache.bufs:
+        if name.startswith(("sink_", "recent_")):
+            continue  # bf16 windows: not packed token slots
         v = cache.view(name)
         if cache.fmt == "kivi2" and name in ("k_scale", "k_zero"):
             v = v[:, :, t0 // 32:t1 // 32]

@@ -167,3 +167,31 @@ def test_decode_num_queries_validation_and_size():
     assert _decode(c, nq=-1)[0] == EINVAL
     assert _decode(c, nq=65, maxlen=64)[0] == EINVAL                  # more queries than tokens
     assert _decode(_cache(T=128), nq=65, maxlen=128)[0] == EUNSUP     # beyond 64 queries
+
+
+def test_mixed_precision_layout_validation_and_sizes():
+    lay = kvq.make_layout("fp4", 2, 4, 128, 256, sink=8, recent=32)
+    assert kvq.kv_buffer_bytes(lay, kvq.BUFFERS.index("sink_k")) == 2 * 4 * 8 * 128 * 2
+    assert kvq.kv_buffer_bytes(lay, kvq.BUFFERS.index("recent_v")) == 2 * 4 * 32 * 128 * 2
+    # the windows are a fixed cost per sequence, not counted per token
+    assert kvq.kv_bytes_per_token(lay, 1) == kvq.kv_bytes_per_token(kvq.make_layout("fp4", 2, 4, 128, 256), 1)
+    assert kvq.kv_buffer_bytes(kvq.make_layout("fp4", 2, 4, 128, 256), kvq.BUFFERS.index("sink_k")) == 0
+    # only caches with FP4 values take windows; sizes within the capacity
+    assert kvq.kv_buffer_bytes(kvq.make_layout("turbo", 1, 1, 128, 64, sink=4), 0) == 0
+    assert kvq.kv_buffer_bytes(kvq.make_layout("fp4", 1, 1, 128, 64, recent=65), 0) == 0
+    assert kvq.kv_buffer_bytes(kvq.make_layout("fp4", 1, 1, 128, 64, sink=-1), 0) == 0
+    c = _cache("turbo")
+    c.layout.sink_tokens = 4
+    assert _append(c) == EUNSUP
+    c = _cache()
+    c.layout.recent_tokens = 16
+    assert _append(c) == EINVAL                                        # window buffers missing
+    c = _cache()
+    c.layout.sink_tokens = 4
+    c.layout.recent_tokens = 16
+    c.buf[kvq.BUFFERS.index("sink_k")] = FAKE
+    c.buf[kvq.BUFFERS.index("sink_v")] = FAKE
+    c.buf[kvq.BUFFERS.index("recent_k")] = FAKE
+    c.buf[kvq.BUFFERS.index("recent_v")] = FAKE
+    st, nb_win = _decode(c, ws=None, splits=4)
+    assert st == OK and nb_win > _decode(_cache(), ws=None, splits=4)[1]   # one more split of partials

@@ -300,6 +300,41 @@ def test_multi_query_decode_matches_oracle(fmt, nq):
     assert err.max() <= RTOL
 
 
+WINDOWS = [("fp4", 16, 64, 1), ("fp4", 0, 100, 3), ("fp4", 40, 0, 1), ("fp4", 300, 700, 2), ("qjl1", 16, 64, 1),
+           ("qjl1", 24, 40, 3)]
+
+
+@pytest.mark.parametrize("fmt,sink,recent,nq", WINDOWS)
+def test_mixed_precision_decode_matches_oracle(fmt, sink, recent, nq):
+    """bf16 sink and recent windows over a packed history.  Each sequence is
+    appended to its own (ragged) length, its last tokens one at a time so that
+    the recent ring wraps; one window covers whole sequences."""
+    cfg = SMALL[fmt]
+    print(f"[mixed] {fmt} sink={sink} recent={recent} nq={nq} {cfg}", flush=True)
+    torch.manual_seed(0)
+    consts = oracle_constants(cfg)
+    cache = new_cache(cfg, sink_tokens=sink, recent_tokens=recent)
+    K, V = inputs(cfg)
+    lens = synth.seq_lens_for(cfg, ragged=True)
+    lens[-1] = max(nq, 3)
+    for b in range(cfg.batch):
+        seq, L = cache.sequence(b), int(lens[b])
+        bulk = max(0, L - 5)
+        if bulk:
+            seq.append(K[b:b + 1, :, :bulk].contiguous(), V[b:b + 1, :, :bulk].contiguous(), 0)
+        for t in range(bulk, L):
+            seq.append(K[b:b + 1, :, t:t + 1].contiguous(), V[b:b + 1, :, t:t + 1].contiguous(), t)
+    torch.cuda.synchronize()
+    enc = oracle_encode(cfg, host64(K), host64(V), consts)
+    q = synth.make_queries(cfg.scaled(hq=nq * cfg.hq), device="cuda").view(cfg.batch, nq, cfg.hq, -1)
+    out = cache.decode(q, torch.from_numpy(lens).cuda(), softmax_scale(cfg)).cpu().numpy()
+    ref = OA.decode_attention_mixed(fmt, enc, host64(q), lens, softmax_scale(cfg), cfg.hkv, host64(K), host64(V),
+                                    sink, recent, consts)
+    err = row_rel_err(out.reshape(-1, out.shape[-1]), ref.reshape(-1, ref.shape[-1]))
+    print(f"  max row rel err {err.max():.3e}", flush=True)
+    assert err.max() <= RTOL
+
+
 @pytest.mark.parametrize("fmt", ["turbo", "qjl1"])
 def test_wide_range_queries(fmt):
     """Queries whose channels span 2^-12 .. 2^3 (and some exact zeros): every
