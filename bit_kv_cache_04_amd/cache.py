@@ -118,14 +118,19 @@ class PackedKVCache:
 
     # ---- the two device entry points
     def append(self, k, v, start):
-        """k, v: contiguous [B, H, n, d] (latent: k [B, n, d + rope], v None), fp32 or bf16."""
+        """k, v: contiguous [B, H, n, d] (latent: k [B, n, d + rope], v None), fp32 or bf16;
+        start: one first position for every sequence, or a sequence of B of them."""
         if not k.is_contiguous() or (v is not None and not v.is_contiguous()):
             raise ValueError("append inputs must be contiguous")
         if v is not None and v.dtype != k.dtype:
             raise ValueError("k and v must share a dtype")
         n = k.shape[-2]
-        kvq.kv_quant_append(self.struct, _ptr(k), _ptr(v), _TORCH_DT[k.dtype], start, n,
-                            _stream_ptr(self.device))
+        if isinstance(start, (int, np.integer)):
+            kvq.kv_quant_append(self.struct, _ptr(k), _ptr(v), _TORCH_DT[k.dtype], int(start), n,
+                                _stream_ptr(self.device))
+        else:
+            kvq.kv_quant_append_ragged(self.struct, _ptr(k), _ptr(v), _TORCH_DT[k.dtype], list(start), n,
+                                       _stream_ptr(self.device))
 
     def workspace_bytes(self, num_q_heads, max_seq_len, splits=0, q_dtype=torch.bfloat16, num_queries=1):
         opts = KVDecodeOpts(splits, None, None, num_queries)

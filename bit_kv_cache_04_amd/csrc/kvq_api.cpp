@@ -29,7 +29,30 @@ extern "C" int kv_quant_append(const kv_cache* c, const void* k, const void* v, 
   const bool latent = c->layout.format == KV_FMT_LATENT_FP4;
   if (!k || (!latent && !v) || (latent && v)) return KV_EINVAL;
   if (!aligned(k, 16) || (v && !aligned(v, 16))) return KV_EINVAL;
-  return launch_append(c, k, v, in_dtype, start, n_new, stream);
+  return launch_append(c, k, v, in_dtype, start, nullptr, n_new, stream);
+}
+
+extern "C" int kv_quant_append_ragged(const kv_cache* c, const void* k, const void* v, int32_t in_dtype,
+                                      const int32_t* starts, int32_t n_new, void* ws, size_t* ws_bytes,
+                                      void* stream) {
+  (void)ws;
+  int st = check_cache(c);
+  if (st != KV_OK) return st;
+  if (ws_bytes) *ws_bytes = 0;
+  if (in_dtype != KV_DT_F32 && in_dtype != KV_DT_BF16) return KV_EUNSUPPORTED;
+  if (!starts || n_new < 0) return KV_EINVAL;
+  const kv_layout& L = c->layout;
+  if (L.format == KV_FMT_KIVI2 && n_new % kKiviGroup) return KV_EINVAL;
+  for (int b = 0; b < L.batch; ++b) {
+    if (starts[b] < 0) return KV_EINVAL;
+    if ((int64_t)starts[b] + n_new > L.capacity) return KV_ECAPACITY;
+    if (L.format == KV_FMT_KIVI2 && starts[b] % kKiviGroup) return KV_EINVAL;
+  }
+  if (n_new == 0) return KV_OK;
+  const bool latent = L.format == KV_FMT_LATENT_FP4;
+  if (!k || (!latent && !v) || (latent && v)) return KV_EINVAL;
+  if (!aligned(k, 16) || (v && !aligned(v, 16))) return KV_EINVAL;
+  return launch_append(c, k, v, in_dtype, 0, starts, n_new, stream);
 }
 
 extern "C" int kv_decode_attention(const kv_cache* c, const void* q, int32_t q_dtype, int32_t num_q_heads,

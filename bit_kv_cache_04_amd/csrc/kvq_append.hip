@@ -21,10 +21,24 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
+// First cache positions of an append: one for every sequence, or one per
+// sequence (s[b] for sequence b of the launch, `heads` sequence-head rows each),
+// passed by value so that no device memory holds them.
+constexpr int kMaxRaggedSeqs = 256;
+struct AppendPos {
+  int start;   // every sequence's first position when ragged == 0
+  int ragged;  // 1: sequence b starts at s[b]
+  int heads;   // sequence-head rows per sequence (KV heads; 1 for the latent)
+  int32_t s[kMaxRaggedSeqs];
+};
+__device__ __forceinline__ int start_of(const AppendPos& p, size_t bh) {
+  return p.ragged ? p.s[bh / p.heads] : p.start;
+}
+
 // Token rows of an append are flat indices r in [0, bh_count * n): sequence-head
-// bh = r / n, position start + r % n; the input row r starts at x + r * stride.
-__device__ __forceinline__ size_t dst_row(size_t r, int n, int cap, int start) {
-  return (r / n) * (size_t)cap + start + (r % n);
+// bh = r / n, position start_of(bh) + r % n; the input row r starts at x + r * stride.
+__device__ __forceinline__ size_t dst_row(size_t r, int n, int cap, const AppendPos& pos) {
+  return (r / n) * (size_t)cap + start_of(pos, r / n) + (r % n);
 }
 
 // ---------------------------------------------------------------- FP4
@@ -155,8 +169,8 @@ __device__ __forceinline__ void fp4_store_at(const float (&a)[16], const InT* ta
 template <typename InT>
 __device__ __forceinline__ void fp4_store_group(const float (&a)[16], const InT* tag, size_t r, int g, int d,
                                                 uint8_t* __restrict__ codes, uint16_t* __restrict__ scales, int n,
-                                                int cap, int start) {
-  fp4_store_at(a, tag, dst_row(r, n, cap, start), g, d, codes, scales);
+                                                int cap, AppendPos pos) {
+  fp4_store_at(a, tag, dst_row(r, n, cap, pos), g, d, codes, scales);
 }
 
 // Group gid (= row * (d / 16) + group) of a row-major input with row stride
@@ -164,7 +178,7 @@ __device__ __forceinline__ void fp4_store_group(const float (&a)[16], const InT*
 template <typename InT>
 __device__ __forceinline__ void fp4_group(const InT* __restrict__ x, size_t stride, int d,
                                           uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
-                                          size_t rows, int n, int cap, int start, size_t gid) {
+                                          size_t rows, int n, int cap, AppendPos pos, size_t gid) {
   const int groups = d / 16;
   if (gid >= rows * groups) return;
   const int g = (int)(gid % groups);
@@ -173,7 +187,7 @@ __device__ __forceinline__ void fp4_group(const InT* __restrict__ x, size_t stri
   raw.load(x + r * stride + g * 16);
   float a[16];
   raw.unpack(a);
-  fp4_store_group(a, x, r, g, d, codes, scales, n, cap, start);
+  fp4_store_group(a, x, r, g, d, codes, scales, n, cap, pos);
 }
 
 // K (blockIdx.y = 0) and V (blockIdx.y = 1) of an FP4 cache in one launch.
@@ -181,10 +195,10 @@ template <typename InT>
 __global__ void __launch_bounds__(256) fp4_append_kernel(const InT* __restrict__ k, const InT* __restrict__ v,
                                                          int d, uint8_t* __restrict__ kc, uint16_t* __restrict__ ks,
                                                          uint8_t* __restrict__ vc, uint16_t* __restrict__ vs,
-                                                         size_t rows, int n, int cap, int start) {
+                                                         size_t rows, int n, int cap, AppendPos pos) {
   const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (blockIdx.y == 0) fp4_group(k, d, d, kc, ks, rows, n, cap, start, gid);
-  else fp4_group(v, d, d, vc, vs, rows, n, cap, start, gid);
+  if (blockIdx.y == 0) fp4_group(k, d, d, kc, ks, rows, n, cap, pos, gid);
+  else fp4_group(v, d, d, vc, vs, rows, n, cap, pos, gid);
 }
 
 // Latent: the 512-wide latent as FP4 groups (blockIdx.y = 0) and the RoPE key
@@ -193,16 +207,16 @@ template <typename InT>
 __global__ void __launch_bounds__(256) latent_append_kernel(const InT* __restrict__ x, int d, int rope_dim,
                                                             uint8_t* __restrict__ cc, uint16_t* __restrict__ cs,
                                                             uint16_t* __restrict__ rope, size_t rows, int n,
-                                                            int cap, int start) {
+                                                            int cap, AppendPos pos) {
   const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t stride = (size_t)d + rope_dim;
   if (blockIdx.y == 0) {
-    fp4_group(x, stride, d, cc, cs, rows, n, cap, start, gid);
+    fp4_group(x, stride, d, cc, cs, rows, n, cap, pos, gid);
   } else if (gid < rows * rope_dim) {
     const int c = (int)(gid % rope_dim);
     const size_t r = gid / rope_dim;
     const float val = load_as_f32(x + r * stride + d, c);
-    rope[dst_row(r, n, cap, start) * rope_dim + c] = bf16_from_f64((double)val);
+    rope[dst_row(r, n, cap, pos) * rope_dim + c] = bf16_from_f64((double)val);
   }
 }
 
@@ -234,7 +248,7 @@ template <typename InT>
 __global__ void __launch_bounds__(256) kivi_append_kernel(const InT* __restrict__ k, const InT* __restrict__ v,
                                                           int d, uint8_t* kc, float* ks, float* kz, uint8_t* vc,
                                                           float* vs, float* vz, int bh_count, int n, int cap,
-                                                          int start) {
+                                                          AppendPos pos) {
   __shared__ float xk[32][kKiviMaxD + 1];
   __shared__ float xv[32][kKiviMaxD + 1];
   const int tid = threadIdx.x;
@@ -267,6 +281,7 @@ __global__ void __launch_bounds__(256) kivi_append_kernel(const InT* __restrict_
   }
   __syncthreads();
   const int quads = d / 4;
+  const int start = start_of(pos, bh);
   const size_t slot0 = bh * cap + start + (size_t)g * 32;  // cache row of the group's first token
   if (tid < quads) {
     const int cq = tid;
@@ -545,7 +560,7 @@ qjl_append_kernel(const InT* __restrict__ k, const InT* __restrict__ v,
                                                          const float* __restrict__ proj,
                                                          uint8_t* __restrict__ sketch, uint16_t* __restrict__ knorm,
                                                          uint8_t* __restrict__ vc, uint16_t* __restrict__ vs,
-                                                         size_t rows, int n, int cap, int start) {
+                                                         size_t rows, int n, int cap, AppendPos pos) {
   __shared__ __align__(16) uint16_t S_lds[128 * kSPad];
   __shared__ float srow_norm[128];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -595,7 +610,7 @@ qjl_append_kernel(const InT* __restrict__ k, const InT* __restrict__ v,
         bh += p / (uint32_t)n;
         p %= (uint32_t)n;
       }
-      return bh * (size_t)cap + (size_t)start + p;
+      return bh * (size_t)cap + (size_t)start_of(pos, bh) + p;
     };
     // values first: the 128 groups of rows [base, base + 16), two per lane
     // (group g of the flat row-major input starts at v + 16 g), then the key
@@ -637,7 +652,7 @@ __device__ __forceinline__ void turbo_body(const InT* __restrict__ x, const floa
                                            const float* __restrict__ thresh, uint8_t* __restrict__ codes,
                                            uint8_t* __restrict__ sketch, uint16_t* __restrict__ norm_out,
                                            uint16_t* __restrict__ rnorm_out, size_t rows, int n, int cap,
-                                           int start, uint16_t* R_lds, uint16_t* S_lds,
+                                           AppendPos pos, uint16_t* R_lds, uint16_t* S_lds,
                                            double (*scratch)[16 * 129], uint8_t (*idx_lds)[16 * 128]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   stage_bf16_matrix(rot, R_lds);  // bf16-valued
@@ -703,7 +718,7 @@ __device__ __forceinline__ void turbo_body(const InT* __restrict__ x, const floa
     __builtin_amdgcn_wave_barrier();
     // pack the 2-bit codes: lane < 16 owns token `lane`
     if (lane < 16 && base + lane < rows) {
-      const size_t dr = dst_row(base + lane, n, cap, start);
+      const size_t dr = dst_row(base + lane, n, cap, pos);
       const uint8_t* ip = &idx_lds[wave][lane * 128];
       uint32_t w[8];
 #pragma unroll
@@ -762,7 +777,7 @@ __device__ __forceinline__ void turbo_body(const InT* __restrict__ x, const floa
           uint32_t hi = (uint32_t)(ballots[2 * j + 1][i] >> (16 * q)) & 0xFFFFu;
           w[j] = lo | (hi << 16);
         }
-        const size_t dr = dst_row(base + lane, n, cap, start);
+        const size_t dr = dst_row(base + lane, n, cap, pos);
         *reinterpret_cast<uint4*>(sketch + dr * 16) = make_uint4(w[0], w[1], w[2], w[3]);
         rnorm_out[dr] = f16_from_f64_nonneg(sqrt(g2));
       }
@@ -781,16 +796,16 @@ __global__ void __launch_bounds__(256) turbo_append_kernel(const InT* __restrict
                                                            const float* __restrict__ thresh, uint8_t* kc,
                                                            uint8_t* sketch, uint16_t* knorm, uint16_t* krnorm,
                                                            uint8_t* vc, uint16_t* vnorm, size_t rows, int n,
-                                                           int cap, int start) {
+                                                           int cap, AppendPos pos) {
   __shared__ __align__(16) uint16_t R_lds[128 * kSPad];
   __shared__ __align__(16) uint16_t S_lds[128 * kSPad];
   __shared__ double scratch[4][16 * 129];  // per wave: x tile (as double), then the residual
   __shared__ uint8_t idx_lds[4][16 * 128];
   if (blockIdx.y == 0)
-    turbo_body<InT, true>(k, rot, proj, levels, thresh, kc, sketch, knorm, krnorm, rows, n, cap, start, R_lds,
+    turbo_body<InT, true>(k, rot, proj, levels, thresh, kc, sketch, knorm, krnorm, rows, n, cap, pos, R_lds,
                           S_lds, scratch, idx_lds);
   else
-    turbo_body<InT, false>(v, rot, nullptr, levels, thresh, vc, nullptr, vnorm, nullptr, rows, n, cap, start,
+    turbo_body<InT, false>(v, rot, nullptr, levels, thresh, vc, nullptr, vnorm, nullptr, rows, n, cap, pos,
                            R_lds, S_lds, scratch, idx_lds);
 }
 
@@ -806,7 +821,7 @@ __global__ void __launch_bounds__(512) turbo_append_small_kernel(
     const float* __restrict__ proj, const float* __restrict__ levels, const float* __restrict__ thresh,
     uint8_t* __restrict__ kc, uint8_t* __restrict__ sketch, uint16_t* __restrict__ knorm,
     uint16_t* __restrict__ krnorm, uint8_t* __restrict__ vc, uint16_t* __restrict__ vnorm, size_t rows, int n,
-    int cap, int start) {
+    int cap, AppendPos pos) {
   __shared__ double xs[16 * 129];  // x tile as double
   __shared__ double rs[16 * 129];  // keys: the residual
   __shared__ __align__(16) uint16_t rows_lds[8][2][16 * kSPad];  // per wave: its rows of R, then of S (bf16)
@@ -884,7 +899,7 @@ __global__ void __launch_bounds__(512) turbo_append_small_kernel(
     word |= __shfl_xor(word, 4);
     word |= __shfl_xor(word, 8);
     if (col == 0 && base + tok < rows)
-      *reinterpret_cast<uint32_t*>(codes + dst_row(base + tok, n, cap, start) * 32 + 4 * w) = word;
+      *reinterpret_cast<uint32_t*>(codes + dst_row(base + tok, n, cap, pos) * 32 + 4 * w) = word;
     if (keys) {
       const double lv = id == 0 ? lv0 : id == 1 ? lv1 : id == 2 ? lv2 : lv3;
       const double r = u - lv;
@@ -905,7 +920,7 @@ __global__ void __launch_bounds__(512) turbo_append_small_kernel(
     }
   }
   if (w == 0 && lane < 16 && base + lane < rows)
-    (keys ? knorm : vnorm)[dst_row(base + lane, n, cap, start)] = f16_from_f64_nonneg(nrm);
+    (keys ? knorm : vnorm)[dst_row(base + lane, n, cap, pos)] = f16_from_f64_nonneg(nrm);
   if (!keys) return;
   __syncthreads();
   // S r for sketch rows 16 w .. 16 w + 15
@@ -924,7 +939,7 @@ __global__ void __launch_bounds__(512) turbo_append_small_kernel(
     if ((lane >> 2) == i) my_bits = (uint32_t)(bal >> (16 * (lane & 3))) & 0xFFFFu;
   }
   if (lane < 16 && base + lane < rows) {
-    const size_t dr = dst_row(base + lane, n, cap, start);
+    const size_t dr = dst_row(base + lane, n, cap, pos);
     *reinterpret_cast<uint16_t*>(sketch + dr * 16 + 2 * w) = (uint16_t)my_bits;
     if (w == 0) {
       double g2 = 0.0;
@@ -934,25 +949,30 @@ __global__ void __launch_bounds__(512) turbo_append_small_kernel(
   }
 }
 
-// bf16 copies of appended tokens [t_a, t_b) (positions; the append covers
-// [start, start + n)) for a mixed-precision cache: token t goes to slot t of the
-// sink, or to slot t mod `slots` of the recent ring when `ring` is set.  Eight
-// channels per thread; fp32 inputs round to nearest even.
+// bf16 copies of appended tokens for a mixed-precision cache.  Append token tt
+// (of n) of sequence-head bh lands at position t = start_of(bh) + tt; it goes to
+// slot t of the sink when t < S, and to slot t mod W of the recent ring when it
+// is one of the append's last W tokens.  Virtual index v < Sn = min(n, S) is
+// sink candidate tt = v; v >= Sn is ring token tt = n - Wn + (v - Sn), Wn =
+// min(n, W).  Eight channels per thread; fp32 inputs round to nearest even.
 template <typename InT>
 __global__ void __launch_bounds__(256) window_copy_kernel(const InT* __restrict__ k, const InT* __restrict__ v,
-                                                          int d, uint16_t* __restrict__ dk,
-                                                          uint16_t* __restrict__ dv, int slots, int ring,
-                                                          int bh_count, int n, int start, int t_a, int t_b) {
-  const int per_row = d / 8, nt = t_b - t_a;
-  const size_t half = (size_t)bh_count * nt * per_row;
+                                                          int d, uint16_t* __restrict__ sk, uint16_t* __restrict__ sv,
+                                                          uint16_t* __restrict__ rk, uint16_t* __restrict__ rv,
+                                                          int S, int W, int bh_count, int n, AppendPos pos) {
+  const int per_row = d / 8, Sn = min(n, S), Wn = min(n, W), nv = Sn + Wn;
+  const size_t half = (size_t)bh_count * nv * per_row;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < 2 * half; i += (size_t)gridDim.x * 256) {
     const bool is_v = i >= half;
     const size_t j = is_v ? i - half : i;
     const int c8 = (int)(j % per_row) * 8;
-    const int tt = (int)((j / per_row) % nt);
-    const size_t bh = j / ((size_t)per_row * nt);
-    const int t = t_a + tt;
-    const InT* src = (is_v ? v : k) + (bh * n + (t - start)) * d + c8;
+    const int vi = (int)((j / per_row) % nv);
+    const size_t bh = j / ((size_t)per_row * nv);
+    const bool sink = vi < Sn;
+    const int tt = sink ? vi : n - Wn + (vi - Sn);
+    const int t = start_of(pos, bh) + tt;
+    if (sink && t >= S) continue;  // past the sink
+    const InT* src = (is_v ? v : k) + (bh * n + tt) * d + c8;
     uint32_t w[4];
     if constexpr (std::is_same<InT, uint16_t>::value) {
       const uint4 r = *reinterpret_cast<const uint4*>(src);
@@ -968,8 +988,7 @@ __global__ void __launch_bounds__(256) window_copy_kernel(const InT* __restrict_
         w[e] = lo | (hi << 16);
       }
     }
-    const int slot = ring ? t % slots : t;
-    uint16_t* dst = (is_v ? dv : dk) + (bh * slots + slot) * d + c8;
+    uint16_t* dst = sink ? (is_v ? sv : sk) + (bh * S + t) * d + c8 : (is_v ? rv : rk) + (bh * W + t % W) * d + c8;
     *reinterpret_cast<uint4*>(dst) = uint4{w[0], w[1], w[2], w[3]};
   }
 }
@@ -990,7 +1009,7 @@ int persistent_blocks(size_t rows) {
 }
 
 template <typename InT>
-int append_typed(const kv_cache* c, const InT* k, const InT* v, int start, int n, hipStream_t st) {
+int append_typed(const kv_cache* c, const InT* k, const InT* v, const AppendPos& pos, int n, hipStream_t st) {
   const kv_layout& L = c->layout;
   const int d = L.head_dim, cap = L.capacity;
   const int bh = L.batch * L.num_kv_heads;
@@ -1002,26 +1021,26 @@ int append_typed(const kv_cache* c, const InT* k, const InT* v, int start, int n
   switch (L.format) {
     case KV_FMT_FP4:
       fp4_append_kernel<InT><<<dim3(blocks_for(rows * (d / 16)), 2), 256, 0, st>>>(k, v, d, kc, ks, vc, vs, rows,
-                                                                                  n, cap, start);
+                                                                                  n, cap, pos);
       break;
     case KV_FMT_LATENT_FP4: {
       const size_t work = std::max(rows * (d / 16), rows * (size_t)L.rope_dim);
       latent_append_kernel<InT><<<dim3(blocks_for(work), 2), 256, 0, st>>>(
-          k, d, L.rope_dim, kc, ks, static_cast<uint16_t*>(c->buf[KV_BUF_ROPE]), rows, n, cap, start);
+          k, d, L.rope_dim, kc, ks, static_cast<uint16_t*>(c->buf[KV_BUF_ROPE]), rows, n, cap, pos);
       break;
     }
     case KV_FMT_KIVI2: {
       kivi_append_kernel<InT><<<dim3(bh * (n / 32)), 256, 0, st>>>(
           k, v, d, kc, static_cast<float*>(c->buf[KV_BUF_K_SCALE]), static_cast<float*>(c->buf[KV_BUF_K_ZERO]),
           vc, static_cast<float*>(c->buf[KV_BUF_V_SCALE]), static_cast<float*>(c->buf[KV_BUF_V_ZERO]), bh, n,
-          cap, start);
+          cap, pos);
       break;
     }
     case KV_FMT_QJL1_FP4V: {
       const int blocks = (int)std::min<size_t>((rows + 63) / 64, KVQ_QJL_APPEND_BLOCKS);
       qjl_append_kernel<InT><<<blocks, 256, 0, st>>>(
           k, v, c->proj, static_cast<uint8_t*>(c->buf[KV_BUF_K_SKETCH]), static_cast<uint16_t*>(c->buf[KV_BUF_K_NORM]),
-          vc, vs, rows, n, cap, start);
+          vc, vs, rows, n, cap, pos);
       break;
     }
     case KV_FMT_TURBO:
@@ -1029,42 +1048,63 @@ int append_typed(const kv_cache* c, const InT* k, const InT* v, int start, int n
         turbo_append_small_kernel<InT><<<dim3((unsigned)((rows + 15) / 16), 2), 512, 0, st>>>(
             k, v, c->rot, c->proj, c->lm_levels, c->lm_thresh, kc, static_cast<uint8_t*>(c->buf[KV_BUF_K_SKETCH]),
             static_cast<uint16_t*>(c->buf[KV_BUF_K_NORM]), static_cast<uint16_t*>(c->buf[KV_BUF_K_RNORM]), vc,
-            static_cast<uint16_t*>(c->buf[KV_BUF_V_NORM]), rows, n, cap, start);
+            static_cast<uint16_t*>(c->buf[KV_BUF_V_NORM]), rows, n, cap, pos);
         break;
       }
       turbo_append_kernel<InT><<<dim3(persistent_blocks(rows), 2), 256, 0, st>>>(
           k, v, c->rot, c->proj, c->lm_levels, c->lm_thresh, kc, static_cast<uint8_t*>(c->buf[KV_BUF_K_SKETCH]),
           static_cast<uint16_t*>(c->buf[KV_BUF_K_NORM]), static_cast<uint16_t*>(c->buf[KV_BUF_K_RNORM]), vc,
-          static_cast<uint16_t*>(c->buf[KV_BUF_V_NORM]), rows, n, cap, start);
+          static_cast<uint16_t*>(c->buf[KV_BUF_V_NORM]), rows, n, cap, pos);
       break;
     default:
       return KV_EUNSUPPORTED;
   }
   // mixed precision: bf16 copies of the sink tokens and of the append's last
   // recent_tokens tokens (older ring slots are overwritten by later appends)
-  auto copies = [&](uint16_t* dk, uint16_t* dv, int slots, int ring, int t_a, int t_b) {
-    if (t_b <= t_a) return;
-    const size_t items = 2 * (size_t)bh * (t_b - t_a) * (d / 8);
-    window_copy_kernel<InT><<<blocks_for(items), 256, 0, st>>>(k, v, d, dk, dv, slots, ring, bh, n, start, t_a, t_b);
-  };
-  if (L.sink_tokens)
-    copies(static_cast<uint16_t*>(c->buf[KV_BUF_SINK_K]), static_cast<uint16_t*>(c->buf[KV_BUF_SINK_V]),
-           L.sink_tokens, 0, start, std::min(start + n, L.sink_tokens));
-  if (L.recent_tokens)
-    copies(static_cast<uint16_t*>(c->buf[KV_BUF_RECENT_K]), static_cast<uint16_t*>(c->buf[KV_BUF_RECENT_V]),
-           L.recent_tokens, 1, std::max(start, start + n - L.recent_tokens), start + n);
+  if (L.sink_tokens || L.recent_tokens) {
+    const size_t items = 2 * (size_t)bh * (std::min(n, L.sink_tokens) + std::min(n, L.recent_tokens)) * (d / 8);
+    window_copy_kernel<InT><<<blocks_for(items), 256, 0, st>>>(
+        k, v, d, static_cast<uint16_t*>(c->buf[KV_BUF_SINK_K]), static_cast<uint16_t*>(c->buf[KV_BUF_SINK_V]),
+        static_cast<uint16_t*>(c->buf[KV_BUF_RECENT_K]), static_cast<uint16_t*>(c->buf[KV_BUF_RECENT_V]),
+        L.sink_tokens, L.recent_tokens, bh, n, pos);
+  }
   return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
 }
 
 }  // namespace
 
-int launch_append(const kv_cache* c, const void* k, const void* v, int in_dtype, int start, int n_new,
-                  void* stream) {
+int launch_append(const kv_cache* c, const void* k, const void* v, int in_dtype, int start, const int32_t* starts,
+                  int n_new, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (in_dtype == KV_DT_F32)
-    return append_typed<float>(c, static_cast<const float*>(k), static_cast<const float*>(v), start, n_new, st);
-  return append_typed<uint16_t>(c, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), start,
-                                n_new, st);
+  const kv_layout& L = c->layout;
+  const bool latent = L.format == KV_FMT_LATENT_FP4;
+  const int heads = latent ? 1 : L.num_kv_heads;
+  const size_t in_row = (size_t)L.head_dim + (latent ? L.rope_dim : 0);
+  const size_t in_seq_bytes = (size_t)heads * n_new * in_row * (in_dtype == KV_DT_F32 ? 4 : 2);
+  // per-sequence starts travel by value, kMaxRaggedSeqs sequences per launch;
+  // a launch over sequences [b0, b0 + nb) sees them as a cache of nb sequences
+  const int chunk = starts ? kMaxRaggedSeqs : L.batch;
+  for (int b0 = 0; b0 < L.batch; b0 += chunk) {
+    const int nb = std::min(chunk, L.batch - b0);
+    kv_cache sub = *c;
+    sub.layout.batch = nb;
+    for (int i = 0; i < KV_BUF_COUNT; ++i)
+      if (c->buf[i]) sub.buf[i] = static_cast<char*>(c->buf[i]) + (size_t)b0 * (kv_buffer_bytes(&L, i) / L.batch);
+    AppendPos pos{};
+    pos.start = start;
+    pos.ragged = starts ? 1 : 0;
+    pos.heads = heads;
+    for (int b = 0; starts && b < nb; ++b) pos.s[b] = starts[b0 + b];
+    const char* kb = static_cast<const char*>(k) + (size_t)b0 * in_seq_bytes;
+    const char* vb = v ? static_cast<const char*>(v) + (size_t)b0 * in_seq_bytes : nullptr;
+    const int rc = in_dtype == KV_DT_F32
+                       ? append_typed<float>(&sub, reinterpret_cast<const float*>(kb),
+                                             reinterpret_cast<const float*>(vb), pos, n_new, st)
+                       : append_typed<uint16_t>(&sub, reinterpret_cast<const uint16_t*>(kb),
+                                                reinterpret_cast<const uint16_t*>(vb), pos, n_new, st);
+    if (rc != KV_OK) return rc;
+  }
+  return KV_OK;
 }
 
 }  // namespace kvq

@@ -61,8 +61,10 @@ inline int window_chunks(const kv_layout& L) { return (L.sink_tokens + L.recent_
 
 // Device launchers (defined in the HIP translation units).  Arguments are
 // validated by the caller.
+// Appends at `start` for every sequence, or at starts[b] (host array) when
+// starts is given.
 int launch_append(const kv_cache* c, const void* k, const void* v, int in_dtype, int start,
-                  int n_new, void* stream);
+                  const int32_t* starts, int n_new, void* stream);
 int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads, int nq,
                   const int32_t* seq_lens, int max_seq_len, float scale, float* out, void* ws,
                   const SplitPlan& plan, const DecodeWorkspace& wsl, void* ev_begin, void* ev_end,

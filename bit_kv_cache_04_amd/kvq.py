@@ -20,7 +20,7 @@ STATUS = {0: "KV_OK", -1: "KV_EINVAL", -2: "KV_ECAPACITY", -3: "KV_EUNSUPPORTED"
           -4: "KV_EWORKSPACE", -5: "KV_EDEVICE"}
 BUFFERS = ["k_codes", "k_scale", "k_zero", "k_sketch", "k_norm", "k_rnorm",
            "v_codes", "v_scale", "v_zero", "v_norm", "rope", "sink_k", "sink_v", "recent_k", "recent_v"]
-EXPORTED = ["kv_buffer_bytes", "kv_bytes_per_token", "kv_quant_append", "kv_decode_attention",
+EXPORTED = ["kv_buffer_bytes", "kv_bytes_per_token", "kv_quant_append", "kv_quant_append_ragged", "kv_decode_attention",
             "kv_lloyd_max_gaussian", "kv_make_rotation", "kv_make_projection", "kv_status_string"]
 
 
@@ -66,6 +66,9 @@ def lib():
         L.kv_quant_append.argtypes = [ctypes.POINTER(KVCache), vp, vp, i32, i32, i32, vp,
                                       ctypes.POINTER(sz), vp]
         L.kv_quant_append.restype = ctypes.c_int
+        L.kv_quant_append_ragged.argtypes = [ctypes.POINTER(KVCache), vp, vp, i32, ctypes.POINTER(i32), i32, vp,
+                                             ctypes.POINTER(sz), vp]
+        L.kv_quant_append_ragged.restype = ctypes.c_int
         L.kv_decode_attention.argtypes = [ctypes.POINTER(KVCache), vp, i32, i32, vp, i32, ctypes.c_float,
                                           vp, vp, ctypes.POINTER(sz), ctypes.POINTER(KVDecodeOpts), vp]
         L.kv_decode_attention.restype = ctypes.c_int
@@ -111,6 +114,15 @@ def kv_quant_append(cache: KVCache, k_ptr, v_ptr, in_dtype, start, n_new, stream
     st = lib().kv_quant_append(ctypes.byref(cache), k_ptr, v_ptr, in_dtype, start, n_new, None,
                                ctypes.byref(nbytes), stream)
     _check("kv_quant_append", st)
+
+
+def kv_quant_append_ragged(cache: KVCache, k_ptr, v_ptr, in_dtype, starts, n_new, stream=0):
+    """starts: one first position per sequence (host ints)."""
+    arr = (ctypes.c_int32 * len(starts))(*[int(s) for s in starts])
+    nbytes = ctypes.c_size_t(0)
+    st = lib().kv_quant_append_ragged(ctypes.byref(cache), k_ptr, v_ptr, in_dtype, arr, n_new, None,
+                                      ctypes.byref(nbytes), stream)
+    _check("kv_quant_append_ragged", st)
 
 
 def kv_decode_attention(cache: KVCache, q_ptr, q_dtype, num_q_heads, seq_lens_ptr, max_seq_len, scale,

@@ -202,6 +202,18 @@ size_t kv_bytes_per_token(const kv_layout* L, int32_t num_layers);
 int kv_quant_append(const kv_cache* c, const void* k, const void* v, int32_t in_dtype,
                     int32_t start, int32_t n_new, void* ws, size_t* ws_bytes, void* stream);
 
+/* As kv_quant_append, but sequence b appends its n_new tokens at positions
+ * [starts[b], starts[b] + n_new): sequences at different lengths, as a batch of
+ * token-by-token decodes leaves them.
+ *   starts    host int32 [B], read during the call (the positions travel to the
+ *             kernels by value: nothing is allocated, and a captured graph
+ *             replays the positions it was captured with)
+ * starts NULL or a negative start: KV_EINVAL; starts[b] + n_new > capacity:
+ * KV_ECAPACITY; KIVI2 needs every start and n_new to be multiples of 32
+ * (KV_EINVAL).  Other errors and behaviour as kv_quant_append. */
+int kv_quant_append_ragged(const kv_cache* c, const void* k, const void* v, int32_t in_dtype,
+                           const int32_t* starts, int32_t n_new, void* ws, size_t* ws_bytes, void* stream);
+
 /* One query token per sequence attends over the first seq_lens[b] cached
  * tokens of its sequence (no mask; a query head hq reads KV head hq / (Hq/H)):
  *   out[b][hq] = sum_t softmax_t(scale * logit(q[b][hq], t)) * value(t)

@@ -195,3 +195,22 @@ def test_mixed_precision_layout_validation_and_sizes():
     c.buf[kvq.BUFFERS.index("recent_v")] = FAKE
     st, nb_win = _decode(c, ws=None, splits=4)
     assert st == OK and nb_win > _decode(_cache(), ws=None, splits=4)[1]   # one more split of partials
+
+
+def _append_ragged(c, starts, k=FAKE, v=FAKE, dt=kvq.DT_BF16, n=1):
+    arr = None if starts is None else (ctypes.c_int32 * len(starts))(*starts)
+    nb = ctypes.c_size_t(99)
+    return kvq.lib().kv_quant_append_ragged(ctypes.byref(c), k, v, dt, arr, n, None, ctypes.byref(nb), None)
+
+
+def test_ragged_append_validation():
+    c = _cache(B=2, T=64)
+    assert _append_ragged(c, None) == EINVAL
+    assert _append_ragged(c, [0, -1]) == EINVAL
+    assert _append_ragged(c, [0, 60], n=5) == ECAP
+    assert _append_ragged(c, [0, 59], n=5, k=None) == EINVAL          # checks pass, then the NULL input
+    assert _append_ragged(c, [3, 7], n=0) == OK                        # nothing to do, nothing launched
+    k2 = _cache("kivi2", B=2, d=64, T=64)
+    assert _append_ragged(k2, [0, 16], n=32) == EINVAL                 # a start inside a KIVI key group
+    assert _append_ragged(k2, [0, 32], n=16) == EINVAL                 # a partial group
+    assert _append_ragged(_cache("fp4", d=96), [0, 0]) == EUNSUP

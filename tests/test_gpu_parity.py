@@ -335,6 +335,50 @@ def test_mixed_precision_decode_matches_oracle(fmt, sink, recent, nq):
     assert err.max() <= RTOL
 
 
+RAGGED = [("fp4", {}), ("kivi2", {}), ("turbo", {}), ("qjl1", {}), ("latent", {}),
+          ("fp4", {"sink_tokens": 8, "recent_tokens": 16}), ("qjl1", {"sink_tokens": 40, "recent_tokens": 4})]
+
+
+@pytest.mark.parametrize("fmt,win", RAGGED)
+def test_ragged_append_equals_per_sequence_appends(fmt, win):
+    """One append with a first position per sequence writes exactly the bytes
+    that one append per sequence at that position writes (bf16 windows too)."""
+    cfg = SMALL[fmt].scaled(batch=2)
+    print(f"[ragged append] {fmt} {win} {cfg}", flush=True)
+    K, V = inputs(cfg)
+    n = 32 if fmt == "kivi2" else 20
+    starts = [0, 64] if fmt == "kivi2" else [37, 3]
+    a, b = new_cache(cfg, **win), new_cache(cfg, **win)
+    if fmt == "latent":
+        a.append(K[:, :n].contiguous(), None, starts)
+        for s in range(cfg.batch):
+            b.sequence(s).append(K[s:s + 1, :n].contiguous(), None, starts[s])
+    else:
+        a.append(K[:, :, :n].contiguous(), V[:, :, :n].contiguous(), starts)
+        for s in range(cfg.batch):
+            b.sequence(s).append(K[s:s + 1, :, :n].contiguous(), V[s:s + 1, :, :n].contiguous(), starts[s])
+    torch.cuda.synchronize()
+    for name in a.bufs:
+        assert torch.equal(a.bufs[name], b.bufs[name]), name
+
+
+def test_ragged_append_beyond_one_launch():
+    """300 sequences: the positions go to the kernels by value, 256 sequences per
+    launch; every sequence's bytes match its own append."""
+    cfg = C["fp4_b16_t32k"].scaled(batch=300, hq=1, hkv=1, context=64)
+    print(f"[ragged append 300] {cfg}", flush=True)
+    K, V = synth.make_kv(cfg, 0, 300, 0, 3, device="cuda")
+    rng = np.random.default_rng(3)
+    starts = rng.integers(0, 62, 300).tolist()
+    a, b = new_cache(cfg), new_cache(cfg)
+    a.append(K.contiguous(), V.contiguous(), starts)
+    for s in range(300):
+        b.sequence(s).append(K[s:s + 1].contiguous(), V[s:s + 1].contiguous(), starts[s])
+    torch.cuda.synchronize()
+    for name in a.bufs:
+        assert torch.equal(a.bufs[name], b.bufs[name]), name
+
+
 @pytest.mark.parametrize("fmt", ["turbo", "qjl1"])
 def test_wide_range_queries(fmt):
     """Queries whose channels span 2^-12 .. 2^3 (and some exact zeros): every
