@@ -47,6 +47,13 @@ BF16).  Reading: token t of a sequence of length L attends through bf16(k_t),
 bf16(v_t) when t < sink or t >= L - recent, and through its packed code
 otherwise; a window token's logit is the plain <q, bf16(k_t)> for every format.
 
+KIVI-2 staging (decode_attention_kivi_staged): KIVI quantises keys per channel
+over 32-token groups (page "TurboQuant vs OSCAR vs EpiCache", section
+"quantization frontiers", KIVI paragraph), so the keys of a sequence's last,
+incomplete group have no code yet.  Reading: they are kept as they came in and
+attend exactly; token t of a sequence of length L uses its input key when
+t >= 32 * floor(L / 32), its packed key otherwise, and its packed value always.
+
 Logits and dequantised values are computed in token chunks only to bound
 memory; the softmax is taken over the full logit vector.
 """
@@ -229,4 +236,32 @@ def decode_attention_mixed(fmt, cache, q, seq_lens, scale, hkv, K_in, V_in, sink
             p /= p.sum(axis=1, keepdims=True)
             vals = np.where(window[:, None], vb, _values(fmt, cache, b, h, 0, L, consts, 0))
             out[b, :, h * G:(h + 1) * G] = (p @ vals).reshape(nq, G, -1)
+    return out
+
+
+def decode_attention_kivi_staged(cache, q, seq_lens, scale, hkv, K_in):
+    """fp64 outputs [B, nq, Hq, d] for q [B, nq, Hq, d] over a KIVI-2 cache whose
+    last incomplete key group of each sequence is read from the input keys K_in
+    ([B, H, T, d]); query j sees the first L - (nq - 1 - j) tokens."""
+    q = np.asarray(q, dtype=np.float64)
+    B, nq, Hq = q.shape[:3]
+    G = Hq // hkv
+    out = np.zeros((B, nq, Hq, K_in.shape[-1]))
+    for b in range(B):
+        L = int(seq_lens[b])
+        if L < nq:
+            raise ValueError("every query must see at least its own token")
+        t = np.arange(L)
+        staged = t >= F.KIVI_GROUP * (L // F.KIVI_GROUP)
+        limit = L - (nq - 1 - np.repeat(np.arange(nq), G))
+        visible = t[None, :] < limit[:, None]
+        for h in range(hkv):
+            qg = q[b, :, h * G:(h + 1) * G].reshape(nq * G, -1)
+            exact = qg @ np.asarray(K_in[b, h, :L], np.float64).T
+            logits = np.where(staged[None, :], exact, _key_logits("kivi2", cache, b, h, 0, L, qg, None, 0)) * scale
+            logits = np.where(visible, logits, -np.inf)
+            m = logits.max(axis=1, keepdims=True)
+            p = np.exp(logits - m)
+            p /= p.sum(axis=1, keepdims=True)
+            out[b, :, h * G:(h + 1) * G] = (p @ _values("kivi2", cache, b, h, 0, L, None, 0)).reshape(nq, G, -1)
     return out
