@@ -40,7 +40,8 @@ def _packed_view_spec(fmt, B, H, T, d, rope, m):
     if fmt == "kivi2":
         return dict(k_codes=(u8, (B, H, T, d // 4)), k_scale=(f32, (B, H, T // 32, d)),
                     k_zero=(f32, (B, H, T // 32, d)), v_codes=(u8, (B, H, T, d // 4)),
-                    v_scale=(f32, (B, H, T, d // 32)), v_zero=(f32, (B, H, T, d // 32)))
+                    v_scale=(f32, (B, H, T, d // 32)), v_zero=(f32, (B, H, T, d // 32)),
+                    k_stage=(f32, (B, H, 4 + 32 * d)))
     if fmt == "fp4":
         return dict(k_codes=(u8, (B, H, T, d // 2)), k_scale=(u16, (B, H, T, d // 16)),
                     v_codes=(u8, (B, H, T, d // 2)), v_scale=(u16, (B, H, T, d // 16)))

@@ -24,7 +24,6 @@ extern "C" int kv_quant_append(const kv_cache* c, const void* k, const void* v, 
   if (in_dtype != KV_DT_F32 && in_dtype != KV_DT_BF16) return KV_EUNSUPPORTED;
   if (start < 0 || n_new < 0) return KV_EINVAL;
   if ((int64_t)start + n_new > c->layout.capacity) return KV_ECAPACITY;
-  if (c->layout.format == KV_FMT_KIVI2 && (start % kKiviGroup || n_new % kKiviGroup)) return KV_EINVAL;
   if (n_new == 0) return KV_OK;
   const bool latent = c->layout.format == KV_FMT_LATENT_FP4;
   if (!k || (!latent && !v) || (latent && v)) return KV_EINVAL;
@@ -42,11 +41,9 @@ extern "C" int kv_quant_append_ragged(const kv_cache* c, const void* k, const vo
   if (in_dtype != KV_DT_F32 && in_dtype != KV_DT_BF16) return KV_EUNSUPPORTED;
   if (!starts || n_new < 0) return KV_EINVAL;
   const kv_layout& L = c->layout;
-  if (L.format == KV_FMT_KIVI2 && n_new % kKiviGroup) return KV_EINVAL;
   for (int b = 0; b < L.batch; ++b) {
     if (starts[b] < 0) return KV_EINVAL;
     if ((int64_t)starts[b] + n_new > L.capacity) return KV_ECAPACITY;
-    if (L.format == KV_FMT_KIVI2 && starts[b] % kKiviGroup) return KV_EINVAL;
   }
   if (n_new == 0) return KV_OK;
   const bool latent = L.format == KV_FMT_LATENT_FP4;

@@ -224,6 +224,13 @@ __global__ void __launch_bounds__(256) latent_append_kernel(const InT* __restric
 
 // codes c = clamp(RNE((x - z) / s), 0, 3) in fp32 with s = (max - min) / 3,
 // z = min; c = 0 when s == 0.
+// KIVI key staging per sequence-head: word 0 the tokens appended so far, words
+// 1..3 unused, then the 32 x d keys of the incomplete last group.
+__device__ __forceinline__ float* stage_keys(float* stage, size_t bh, int d) { return stage + bh * (4 + 32 * d) + 4; }
+__device__ __forceinline__ void set_appended(float* stage, size_t bh, int d, int appended) {
+  reinterpret_cast<int*>(stage)[bh * (4 + 32 * d)] = appended;
+}
+
 __device__ __forceinline__ uint32_t kivi_code(float x, float z, float s) {
   if (!(s > 0.f)) return 0;
   float q = rintf(__fdiv_rn(__fsub_rn(x, z), s));
@@ -247,8 +254,8 @@ __device__ __forceinline__ float4 load4_as_f32(const uint16_t* p) {
 template <typename InT>
 __global__ void __launch_bounds__(256) kivi_append_kernel(const InT* __restrict__ k, const InT* __restrict__ v,
                                                           int d, uint8_t* kc, float* ks, float* kz, uint8_t* vc,
-                                                          float* vs, float* vz, int bh_count, int n, int cap,
-                                                          AppendPos pos) {
+                                                          float* vs, float* vz, float* stage, int bh_count, int n,
+                                                          int cap, AppendPos pos) {
   __shared__ float xk[32][kKiviMaxD + 1];
   __shared__ float xv[32][kKiviMaxD + 1];
   const int tid = threadIdx.x;
@@ -283,6 +290,7 @@ __global__ void __launch_bounds__(256) kivi_append_kernel(const InT* __restrict_
   const int quads = d / 4;
   const int start = start_of(pos, bh);
   const size_t slot0 = bh * cap + start + (size_t)g * 32;  // cache row of the group's first token
+  if (tid == 0 && g == ngroups - 1) set_appended(stage, bh, d, start + n);
   if (tid < quads) {
     const int cq = tid;
     float mn[4], mx[4];
@@ -313,6 +321,97 @@ __global__ void __launch_bounds__(256) kivi_append_kernel(const InT* __restrict_
   const int vgroups = d / 32;
   for (int it = tid; it < 32 * vgroups; it += 256) {
     const int t = it / vgroups, vg = it % vgroups;
+    float mn = INFINITY, mx = -INFINITY;
+    for (int i = 0; i < 32; ++i) {
+      mn = fminf(mn, xv[t][32 * vg + i]);
+      mx = fmaxf(mx, xv[t][32 * vg + i]);
+    }
+    const float sc = __fdiv_rn(__fsub_rn(mx, mn), 3.0f);
+    unsigned long long packed = 0;
+    for (int i = 0; i < 32; ++i) packed |= (unsigned long long)kivi_code(xv[t][32 * vg + i], mn, sc) << (2 * i);
+    const size_t dr = slot0 + t;
+    *reinterpret_cast<unsigned long long*>(vc + dr * (d / 4) + vg * 8) = packed;
+    vs[dr * vgroups + vg] = sc;
+    vz[dr * vgroups + vg] = mn;
+  }
+}
+
+// Appends that leave or fill an incomplete key group (any start and length).
+// Workgroup (sequence-head bh, group index gi) takes group G = start / 32 + gi,
+// tokens [32 G, 32 G + 32): its keys before the append come from the staging
+// slots, the new ones from the input.  A group the append completes is coded
+// as in kivi_append_kernel; an incomplete one keeps its new keys in staging
+// (slot t mod 32).  Values are coded per token for the new tokens only.
+template <typename InT>
+__global__ void __launch_bounds__(256) kivi_append_any_kernel(const InT* __restrict__ k, const InT* __restrict__ v,
+                                                              int d, uint8_t* kc, float* ks, float* kz, uint8_t* vc,
+                                                              float* vs, float* vz, float* stage, int n, int cap,
+                                                              AppendPos pos) {
+  __shared__ float xk[32][kKiviMaxD + 1];
+  __shared__ float xv[32][kKiviMaxD + 1];
+  const int tid = threadIdx.x;
+  const int ngmax = n / 32 + 2;  // groups an append of n tokens can touch
+  const int gi = blockIdx.x % ngmax;
+  const size_t bh = blockIdx.x / ngmax;
+  const int s = start_of(pos, bh);
+  const int g0 = 32 * (s / 32 + gi);                 // the group's first token
+  const int a0 = max(g0, s), a1 = min(g0 + 32, s + n);  // its new tokens
+  if (a0 >= a1) return;                              // the whole workgroup: no token of this append
+  const bool complete = s + n >= g0 + 32;
+  for (int e = tid; e < 32 * d; e += 256) {
+    const int t = e / d, c = e % d, tok = g0 + t;
+    float kx = 0.f, vx = 0.f;
+    if (tok < a0) {
+      kx = stage_keys(stage, bh, d)[t * d + c];
+    } else if (tok < a1) {
+      const size_t r = bh * n + (tok - s);
+      kx = load_as_f32(k + r * d, c);
+      vx = load_as_f32(v + r * d, c);
+    }
+    xk[t][c] = kx;
+    xv[t][c] = vx;
+  }
+  __syncthreads();
+  const int quads = d / 4;
+  const size_t slot0 = bh * cap + g0;  // cache row of the group's first token
+  if (complete) {
+    if (tid < quads) {
+      const int cq = tid;
+      float mn[4], mx[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mn[j] = INFINITY, mx[j] = -INFINITY;
+      for (int t = 0; t < 32; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          mn[j] = fminf(mn[j], xk[t][4 * cq + j]);
+          mx[j] = fmaxf(mx[j], xk[t][4 * cq + j]);
+        }
+      float sc[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sc[j] = __fdiv_rn(__fsub_rn(mx[j], mn[j]), 3.0f);
+      for (int t = 0; t < 32; ++t) {
+        uint32_t byte = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) byte |= kivi_code(xk[t][4 * cq + j], mn[j], sc[j]) << (2 * j);
+        kc[(slot0 + t) * quads + cq] = (uint8_t)byte;
+      }
+      const size_t meta = (bh * (cap / 32) + g0 / 32) * (size_t)d + 4 * cq;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ks[meta + j] = sc[j];
+        kz[meta + j] = mn[j];
+      }
+    }
+  } else {
+    for (int e = tid; e < (a1 - a0) * d; e += 256) {
+      const int t = a0 - g0 + e / d, c = e % d;
+      stage_keys(stage, bh, d)[t * d + c] = xk[t][c];
+    }
+  }
+  if (tid == 0 && g0 + 32 >= s + n) set_appended(stage, bh, d, s + n);  // the group of the last token
+  const int vgroups = d / 32;
+  for (int it = tid; it < (a1 - a0) * vgroups; it += 256) {
+    const int t = a0 - g0 + it / vgroups, vg = it % vgroups;
     float mn = INFINITY, mx = -INFINITY;
     for (int i = 0; i < 32; ++i) {
       mn = fminf(mn, xv[t][32 * vg + i]);
@@ -1030,10 +1129,19 @@ int append_typed(const kv_cache* c, const InT* k, const InT* v, const AppendPos&
       break;
     }
     case KV_FMT_KIVI2: {
+      bool aligned = n % 32 == 0 && pos.start % 32 == 0;
+      for (int b = 0; pos.ragged && b < L.batch; ++b) aligned = aligned && pos.s[b] % 32 == 0;
+      if (!aligned) {
+        kivi_append_any_kernel<InT><<<dim3(bh * (n / 32 + 2)), 256, 0, st>>>(
+            k, v, d, kc, static_cast<float*>(c->buf[KV_BUF_K_SCALE]), static_cast<float*>(c->buf[KV_BUF_K_ZERO]),
+            vc, static_cast<float*>(c->buf[KV_BUF_V_SCALE]), static_cast<float*>(c->buf[KV_BUF_V_ZERO]),
+            static_cast<float*>(c->buf[KV_BUF_K_STAGE]), n, cap, pos);
+        break;
+      }
       kivi_append_kernel<InT><<<dim3(bh * (n / 32)), 256, 0, st>>>(
           k, v, d, kc, static_cast<float*>(c->buf[KV_BUF_K_SCALE]), static_cast<float*>(c->buf[KV_BUF_K_ZERO]),
-          vc, static_cast<float*>(c->buf[KV_BUF_V_SCALE]), static_cast<float*>(c->buf[KV_BUF_V_ZERO]), bh, n,
-          cap, pos);
+          vc, static_cast<float*>(c->buf[KV_BUF_V_SCALE]), static_cast<float*>(c->buf[KV_BUF_V_ZERO]),
+          static_cast<float*>(c->buf[KV_BUF_K_STAGE]), bh, n, cap, pos);
       break;
     }
     case KV_FMT_QJL1_FP4V: {

@@ -24,6 +24,7 @@ struct DecodeArgs {
   const uint8_t* k_codes;
   const void* k_scale;
   const float* k_zero;
+  const float* k_stage;  // KIVI2 [B][H][4 + 32 d]: tokens appended (int), then the incomplete group's keys
   const uint8_t* k_sketch;
   const uint16_t* k_norm;
   const uint16_t* k_rnorm;
@@ -51,7 +52,8 @@ struct DecodeArgs {
 
 // Virtual key element c of token (bh, t); the logit is <prepared q, key>.
 template <int FMT>
-__device__ __forceinline__ float key_elem(const DecodeArgs& a, size_t bh, int t, int c) {
+// kstage: the first token whose key is read from staging (KIVI2 only).
+__device__ __forceinline__ float key_elem(const DecodeArgs& a, size_t bh, int t, int c, int kstage) {
   const size_t row = bh * a.cap + t;
   if constexpr (FMT == KV_FMT_FP4 || FMT == KV_FMT_LATENT_FP4) {
     if (FMT == KV_FMT_LATENT_FP4 && c >= a.d) return bf16_to_f32(a.rope[row * a.rope_dim + (c - a.d)]);
@@ -59,6 +61,7 @@ __device__ __forceinline__ float key_elem(const DecodeArgs& a, size_t bh, int t,
     const float s = bf16_to_f32(static_cast<const uint16_t*>(a.k_scale)[row * (a.d / 16) + c / 16]);
     return e2m1_value(nib) * s;
   } else if constexpr (FMT == KV_FMT_KIVI2) {
+    if (t >= kstage) return a.k_stage[bh * (4 + 32 * a.d) + 4 + (t & 31) * a.d + c];  // not yet coded
     const uint32_t code = (a.k_codes[row * (a.d / 4) + c / 4] >> (2 * (c & 3))) & 3u;
     const size_t m = (bh * (a.cap / 32) + t / 32) * a.d + c;
     return fmaf((float)code, static_cast<const float*>(a.k_scale)[m], a.k_zero[m]);
@@ -125,6 +128,8 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
   const int L = min(min(a.seq_lens[b], a.max_len), a.cap);
   const int t_begin = a.t_lo + split * a.per_split;
   const int t_end = min(max(a.t_lo, L - a.recent), t_begin + a.per_split);
+  // KIVI2: keys from the first token of the appended sequence's incomplete group on are staged
+  const int kstage = FMT == KV_FMT_KIVI2 ? reinterpret_cast<const int*>(a.k_stage)[bh * (4 + 32 * a.d)] & ~31 : a.cap;
   // query / output row of block row hh; query j sees the first L - (nq - 1 - j) tokens
   auto qrow = [&](int hh) {
     const int vh = vh0 + hh;
@@ -150,7 +155,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
     const int nt = min(TT, t_end - t0);
     for (int e = tid; e < TT * DK; e += NT) {
       const int t = e / DK, c = e % DK;
-      ks[t][c] = t < nt ? key_elem<FMT>(a, bh, t0 + t, c) : 0.f;
+      ks[t][c] = t < nt ? key_elem<FMT>(a, bh, t0 + t, c, kstage) : 0.f;
     }
     if constexpr (!kAlias) {
       for (int e = tid; e < TT * DV; e += NT) {
@@ -800,6 +805,7 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
   a.k_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_K_CODES]);
   a.k_scale = c->buf[KV_BUF_K_SCALE];
   a.k_zero = static_cast<const float*>(c->buf[KV_BUF_K_ZERO]);
+  a.k_stage = static_cast<const float*>(c->buf[KV_BUF_K_STAGE]);
   a.k_sketch = static_cast<const uint8_t*>(c->buf[KV_BUF_K_SKETCH]);
   a.k_norm = static_cast<const uint16_t*>(c->buf[KV_BUF_K_NORM]);
   a.k_rnorm = static_cast<const uint16_t*>(c->buf[KV_BUF_K_RNORM]);

@@ -158,6 +158,7 @@ extern "C" size_t kv_buffer_bytes(const kv_layout* L, int32_t which) {
   const size_t bht = B * H * T;
   if (which == KV_BUF_SINK_K || which == KV_BUF_SINK_V) return B * H * (size_t)L->sink_tokens * d * 2;
   if (which == KV_BUF_RECENT_K || which == KV_BUF_RECENT_V) return B * H * (size_t)L->recent_tokens * d * 2;
+  if (which == KV_BUF_K_STAGE) return L->format == KV_FMT_KIVI2 ? B * H * (4 + (size_t)kKiviGroup * d) * 4 : 0;
   switch (L->format) {
     case KV_FMT_KIVI2:
       switch (which) {
@@ -211,7 +212,7 @@ extern "C" size_t kv_bytes_per_token(const kv_layout* L, int32_t num_layers) {
   size_t slots = (size_t)L->batch * L->num_kv_heads * L->capacity;
   size_t total = 0;
   for (int b = 0; b < KV_BUF_COUNT; ++b)
-    if (b < KV_BUF_SINK_K) total += kv_buffer_bytes(L, b);  // not the per-sequence bf16 windows
+    if (b < KV_BUF_SINK_K) total += kv_buffer_bytes(L, b);  // not the per-sequence windows and staging
   return (size_t)num_layers * L->num_kv_heads * (total / slots);
 }
 

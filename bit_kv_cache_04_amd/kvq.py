@@ -19,7 +19,8 @@ DT_F32, DT_BF16 = 0, 1
 STATUS = {0: "KV_OK", -1: "KV_EINVAL", -2: "KV_ECAPACITY", -3: "KV_EUNSUPPORTED",
           -4: "KV_EWORKSPACE", -5: "KV_EDEVICE"}
 BUFFERS = ["k_codes", "k_scale", "k_zero", "k_sketch", "k_norm", "k_rnorm",
-           "v_codes", "v_scale", "v_zero", "v_norm", "rope", "sink_k", "sink_v", "recent_k", "recent_v"]
+           "v_codes", "v_scale", "v_zero", "v_norm", "rope", "sink_k", "sink_v", "recent_k", "recent_v",
+           "k_stage"]
 EXPORTED = ["kv_buffer_bytes", "kv_bytes_per_token", "kv_quant_append", "kv_quant_append_ragged", "kv_decode_attention",
             "kv_lloyd_max_gaussian", "kv_make_rotation", "kv_make_projection", "kv_status_string"]
 

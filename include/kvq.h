@@ -125,11 +125,15 @@ typedef struct kv_layout {
  *   ROPE     bf16 LATENT [B][Tc][rope_dim]
  *   SINK_K, SINK_V      bf16 [B][H][sink_tokens][d]    (mixed precision)
  *   RECENT_K, RECENT_V  bf16 [B][H][recent_tokens][d]  (mixed precision; token
- *                       t in slot t mod recent_tokens)                         */
+ *                       t in slot t mod recent_tokens)
+ *   K_STAGE  KIVI2 [B][H][4 + 32 d] 32-bit words: word 0 the number of tokens
+ *                 appended to the sequence (int32), words 1..3 unused, then as
+ *                 f32 [32][d] the keys of its last, incomplete 32-token group
+ *                 (token t in row t mod 32), which have no key code yet        */
 enum kv_buffer {
   KV_BUF_K_CODES = 0, KV_BUF_K_SCALE, KV_BUF_K_ZERO, KV_BUF_K_SKETCH, KV_BUF_K_NORM,
   KV_BUF_K_RNORM, KV_BUF_V_CODES, KV_BUF_V_SCALE, KV_BUF_V_ZERO, KV_BUF_V_NORM,
-  KV_BUF_ROPE, KV_BUF_SINK_K, KV_BUF_SINK_V, KV_BUF_RECENT_K, KV_BUF_RECENT_V, KV_BUF_COUNT
+  KV_BUF_ROPE, KV_BUF_SINK_K, KV_BUF_SINK_V, KV_BUF_RECENT_K, KV_BUF_RECENT_V, KV_BUF_K_STAGE, KV_BUF_COUNT
 };
 
 /* A cache: its layout, device buffers (NULL where the format has none) and
@@ -192,8 +196,16 @@ size_t kv_bytes_per_token(const kv_layout* L, int32_t num_layers);
  *             and v must be NULL
  *   ws        unused by every current format: pass NULL; *ws_bytes (if given)
  *             is set to 0
- * KIVI2 needs start and n_new to be multiples of 32 (whole key groups):
- * KV_EINVAL otherwise.  start + n_new > capacity: KV_ECAPACITY.  n_new == 0
+ * KIVI2 quantises keys per channel over whole 32-token groups: the keys of a
+ * sequence's last incomplete group wait in K_STAGE (as fp32 of the input) and
+ * are coded when a later append completes the group, from the staged keys and
+ * the new ones; values are coded per token at once.  So KIVI2 appends to a
+ * sequence must follow each other (each starting where the previous ended)
+ * whenever a group is left incomplete; decode reads a sequence's staged keys
+ * for its tokens from 32 * floor(A / 32) on, A the tokens appended to it (a
+ * decode over a shorter prefix reads coded groups) (page "TurboQuant vs OSCAR vs
+ * EpiCache", section "quantization frontiers", KIVI paragraph: keys quantised
+ * per channel, values per token).  start + n_new > capacity: KV_ECAPACITY.  n_new == 0
  * enqueues nothing.  The method's encoding steps are those of the format
  * definitions above (TurboQuant: norm, rotate, divide, Lloyd-Max code,
  * residual, residual norm, sketch of the residual, in that order).  With mixed
@@ -209,8 +221,7 @@ int kv_quant_append(const kv_cache* c, const void* k, const void* v, int32_t in_
  *             kernels by value: nothing is allocated, and a captured graph
  *             replays the positions it was captured with)
  * starts NULL or a negative start: KV_EINVAL; starts[b] + n_new > capacity:
- * KV_ECAPACITY; KIVI2 needs every start and n_new to be multiples of 32
- * (KV_EINVAL).  Other errors and behaviour as kv_quant_append. */
+ * KV_ECAPACITY.  Other errors and behaviour as kv_quant_append. */
 int kv_quant_append_ragged(const kv_cache* c, const void* k, const void* v, int32_t in_dtype,
                            const int32_t* starts, int32_t n_new, void* ws, size_t* ws_bytes, void* stream);
 

@@ -51,8 +51,9 @@ KIVI-2 staging (decode_attention_kivi_staged): KIVI quantises keys per channel
 over 32-token groups (page "TurboQuant vs OSCAR vs EpiCache", section
 "quantization frontiers", KIVI paragraph), so the keys of a sequence's last,
 incomplete group have no code yet.  Reading: they are kept as they came in and
-attend exactly; token t of a sequence of length L uses its input key when
-t >= 32 * floor(L / 32), its packed key otherwise, and its packed value always.
+attend exactly; token t of a sequence appended up to A tokens (decoded over its
+first L <= A) uses its input key when t >= 32 * floor(A / 32), its packed key
+otherwise, and its packed value always.
 
 Logits and dequantised values are computed in token chunks only to bound
 memory; the softmax is taken over the full logit vector.
@@ -239,10 +240,12 @@ def decode_attention_mixed(fmt, cache, q, seq_lens, scale, hkv, K_in, V_in, sink
     return out
 
 
-def decode_attention_kivi_staged(cache, q, seq_lens, scale, hkv, K_in):
+def decode_attention_kivi_staged(cache, q, seq_lens, scale, hkv, K_in, appended=None):
     """fp64 outputs [B, nq, Hq, d] for q [B, nq, Hq, d] over a KIVI-2 cache whose
-    last incomplete key group of each sequence is read from the input keys K_in
-    ([B, H, T, d]); query j sees the first L - (nq - 1 - j) tokens."""
+    last incomplete key group of each sequence (appended[b] tokens appended, by
+    default seq_lens[b]) is read from the input keys K_in ([B, H, T, d]); query
+    j sees the first L - (nq - 1 - j) tokens."""
+    appended = seq_lens if appended is None else appended
     q = np.asarray(q, dtype=np.float64)
     B, nq, Hq = q.shape[:3]
     G = Hq // hkv
@@ -252,7 +255,7 @@ def decode_attention_kivi_staged(cache, q, seq_lens, scale, hkv, K_in):
         if L < nq:
             raise ValueError("every query must see at least its own token")
         t = np.arange(L)
-        staged = t >= F.KIVI_GROUP * (L // F.KIVI_GROUP)
+        staged = t >= F.KIVI_GROUP * (int(appended[b]) // F.KIVI_GROUP)
         limit = L - (nq - 1 - np.repeat(np.arange(nq), G))
         visible = t[None, :] < limit[:, None]
         for h in range(hkv):

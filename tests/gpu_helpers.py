@@ -82,7 +82,7 @@ def gpu_buffers(cache, t0=0, t1=None):
     t1 = cache.T if t1 is None else t1
     out = {}
     for name in cache.bufs:
-        if name.startswith(("sink_", "recent_")):
+        if name.startswith(("sink_", "recent_")) or name == "k_stage":
             continue  # bf16 windows: not packed token slots
         v = cache.view(name)
         if cache.fmt == "kivi2" and name in ("k_scale", "k_zero"):

@@ -48,7 +48,8 @@ def test_bytes_per_token_matches_oracle(fmt, H, d, rope):
     lay = kvq.make_layout(fmt, 3, H, d, 96, rope)
     for layers in (1, 40, 80):
         assert kvq.kv_bytes_per_token(lay, layers) == layers * H * per_token_head(fmt, d, rope)
-    total = sum(kvq.kv_buffer_bytes(lay, i) for i in range(len(kvq.BUFFERS)))
+    # the per-token buffers (the bf16 windows and KIVI staging are per sequence)
+    total = sum(kvq.kv_buffer_bytes(lay, i) for i in range(kvq.BUFFERS.index("sink_k")))
     assert total == 3 * H * 96 * per_token_head(fmt, d, rope)
 
 
@@ -126,8 +127,7 @@ def test_append_validation():
     assert _append(_cache(), v=None) == EINVAL
     assert _append(_cache(), k=FAKE + 2) == EINVAL                     # misaligned input
     assert _append(_cache(fill=False)) == EINVAL                      # NULL buffers
-    assert _append(_cache("kivi2", d=64), n=16) == EINVAL             # partial KIVI key group
-    assert _append(_cache("kivi2", d=64), start=16, n=32) == EINVAL
+    assert _append(_cache("kivi2", d=64), start=40, n=25) == ECAP      # partial KIVI groups are fine, capacity is not
     assert _append(_cache("latent", H=1, d=512, rope=64)) == EINVAL   # latent takes no v
     assert _append(_cache("turbo", consts=False)) == EINVAL           # constants missing
     c = _cache("qjl1")
@@ -211,6 +211,9 @@ def test_ragged_append_validation():
     assert _append_ragged(c, [0, 59], n=5, k=None) == EINVAL          # checks pass, then the NULL input
     assert _append_ragged(c, [3, 7], n=0) == OK                        # nothing to do, nothing launched
     k2 = _cache("kivi2", B=2, d=64, T=64)
-    assert _append_ragged(k2, [0, 16], n=32) == EINVAL                 # a start inside a KIVI key group
-    assert _append_ragged(k2, [0, 32], n=16) == EINVAL                 # a partial group
+    assert _append_ragged(k2, [0, 50], n=16) == ECAP                  # a partial KIVI group is fine, capacity is not
+    # the staging buffer of a KIVI cache holds one 32-token key group per sequence-head
+    lay = kvq.make_layout("kivi2", 2, 2, 64, 64)
+    assert kvq.kv_buffer_bytes(lay, kvq.BUFFERS.index("k_stage")) == 2 * 2 * (4 + 32 * 64) * 4
+    assert kvq.kv_buffer_bytes(kvq.make_layout("fp4", 2, 2, 64, 64), kvq.BUFFERS.index("k_stage")) == 0
     assert _append_ragged(_cache("fp4", d=96), [0, 0]) == EUNSUP

@@ -379,6 +379,67 @@ def test_ragged_append_beyond_one_launch():
         assert torch.equal(a.bufs[name], b.bufs[name]), name
 
 
+@pytest.mark.parametrize("nq", [1, 2])
+def test_kivi_unaligned_appends_and_staged_decode(nq):
+    """KIVI-2 appended in uneven chunks down to single tokens: every whole key
+    group and every value is coded exactly as the oracle codes them, and decode
+    reads each sequence's incomplete last group from the staged keys."""
+    cfg = SMALL["kivi2"].scaled(batch=3)
+    print(f"[kivi staging] nq={nq} {cfg}", flush=True)
+    cache = new_cache(cfg)
+    K, V = inputs(cfg)
+    lens = np.array([256, 75, 9], dtype=np.int32)
+    chunks = [5, 27, 40, 1, 1, 3, 31, 64]
+    for b in range(cfg.batch):
+        seq, t = cache.sequence(b), 0
+        for ci in range(100):
+            if t >= lens[b]:
+                break
+            n = min(chunks[ci % len(chunks)], int(lens[b]) - t)
+            seq.append(K[b:b + 1, :, t:t + n].contiguous(), V[b:b + 1, :, t:t + n].contiguous(), t)
+            t += n
+    torch.cuda.synchronize()
+    want = oracle_encode(cfg, host64(K), host64(V), {})
+    got = gpu_buffers(cache)
+    for b in range(cfg.batch):
+        L, Lg = int(lens[b]), int(lens[b]) // 32 * 32
+        np.testing.assert_array_equal(got["k_codes"][b, :, :Lg], want["k_codes"][b, :, :Lg])
+        np.testing.assert_array_equal(got["k_scale"][b, :, :Lg // 32], want["k_scale"][b, :, :Lg // 32])
+        np.testing.assert_array_equal(got["k_zero"][b, :, :Lg // 32], want["k_zero"][b, :, :Lg // 32])
+        for name in ("v_codes", "v_scale", "v_zero"):
+            np.testing.assert_array_equal(got[name][b, :, :L], want[name][b, :, :L])
+    q = synth.make_queries(cfg.scaled(hq=nq * cfg.hq), device="cuda").view(cfg.batch, nq, cfg.hq, -1)
+    out = cache.decode(q, torch.from_numpy(lens).cuda(), softmax_scale(cfg)).cpu().numpy()
+    ref = OA.decode_attention_kivi_staged(want, host64(q), lens, softmax_scale(cfg), cfg.hkv, host64(K))
+    err = row_rel_err(out.reshape(-1, out.shape[-1]), ref.reshape(-1, ref.shape[-1]))
+    print(f"  max row rel err {err.max():.3e}", flush=True)
+    assert err.max() <= RTOL
+    # shorter prefixes of the same sequences: groups the appends completed are read coded
+    short = np.maximum(lens - np.array([100, 20, 6], dtype=np.int32), nq).astype(np.int32)
+    out = cache.decode(q, torch.from_numpy(short).cuda(), softmax_scale(cfg)).cpu().numpy()
+    ref = OA.decode_attention_kivi_staged(want, host64(q), short, softmax_scale(cfg), cfg.hkv, host64(K), lens)
+    err = row_rel_err(out.reshape(-1, out.shape[-1]), ref.reshape(-1, ref.shape[-1]))
+    print(f"  prefixes: max row rel err {err.max():.3e}", flush=True)
+    assert err.max() <= RTOL
+
+
+def test_kivi_ragged_unaligned_append_equals_per_sequence():
+    """A ragged KIVI-2 append with starts inside key groups writes the bytes
+    (codes, staged keys) of one append per sequence."""
+    cfg = SMALL["kivi2"].scaled(batch=2)
+    K, V = inputs(cfg)
+    a, b = new_cache(cfg), new_cache(cfg)
+    for c in (a, b):  # earlier tokens of each sequence: 37 and 70 of them
+        c.sequence(0).append(K[0:1, :, :37].contiguous(), V[0:1, :, :37].contiguous(), 0)
+        c.sequence(1).append(K[1:2, :, :70].contiguous(), V[1:2, :, :70].contiguous(), 0)
+    a.append(K[:, :, 100:120].contiguous(), V[:, :, 100:120].contiguous(), [37, 70])
+    b.sequence(0).append(K[0:1, :, 100:120].contiguous(), V[0:1, :, 100:120].contiguous(), 37)
+    b.sequence(1).append(K[1:2, :, 100:120].contiguous(), V[1:2, :, 100:120].contiguous(), 70)
+    torch.cuda.synchronize()
+    for name in a.bufs:
+        assert torch.equal(a.bufs[name], b.bufs[name]), name
+
+
 @pytest.mark.parametrize("fmt", ["turbo", "qjl1"])
 def test_wide_range_queries(fmt):
     """Queries whose channels span 2^-12 .. 2^3 (and some exact zeros): every

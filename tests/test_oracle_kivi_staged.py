@@ -1,7 +1,8 @@
 """Pins for the oracle's KIVI-2 decode with the last incomplete key group read
 from the input keys.
 
-- Whole groups only (L a multiple of 32): the plain oracle.
+- Whole groups only (L a multiple of 32), or a prefix of a longer append whose
+  groups are all coded: the plain oracle.
 - Everything staged (L < 32): a library attention routine (torch
   scaled_dot_product_attention, fp64) on the input keys and the values the
   oracle's KIVI value decoder gives.
@@ -67,3 +68,15 @@ def test_each_key_comes_from_its_own_representation():
     K4 = K.copy()
     K4[:, :, 63] += 1.0                              # last token of a whole group: read packed
     np.testing.assert_array_equal(A.decode_attention_kivi_staged(cache, q, [L], 0.4, 2, K4), base)
+
+
+def test_prefix_of_a_longer_append_reads_coded_groups():
+    rng = np.random.default_rng(33)
+    K, V, cache = _setup(rng)
+    q = rng.standard_normal((2, 1, 4, 64))
+    lens, appended = np.array([40, 7]), np.array([96, 40])
+    np.testing.assert_allclose(A.decode_attention_kivi_staged(cache, q, lens, 0.2, 2, K, appended),
+                               A.decode_attention_multi("kivi2", cache, q, lens, 0.2, 2), rtol=0, atol=1e-12)
+    # the same prefix of a sequence appended only that far stages its last group
+    assert not np.allclose(A.decode_attention_kivi_staged(cache, q, lens, 0.2, 2, K, lens),
+                           A.decode_attention_multi("kivi2", cache, q, lens, 0.2, 2))
