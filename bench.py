@@ -38,7 +38,7 @@ def counted_bytes(cfg, lib_layout, kvq, sink=0, recent=0):
             + cfg.batch * cfg.hkv * window * cfg.head_dim * 2 * 2)
 
 
-def cpu_baseline(cfg, budget_s=12.0):
+def cpu_baseline(cfg, budget_s=12.0, rotation="haar"):
     """Time the oracle's decode on a bounded sample: one (sequence, KV head) unit at a time."""
     import numpy as np
     from threadpoolctl import threadpool_limits
@@ -48,13 +48,16 @@ def cpu_baseline(cfg, budget_s=12.0):
     from oracle import formats as OF
     from oracle.bytes import per_token_head
     from oracle.lloyd_max import canonical_codebook
-    from oracle.rotation import canonical_projection, canonical_rotation
+    from oracle.rotation import canonical_hadamard_rotation, canonical_projection, canonical_rotation
 
     T = cfg.context
     unit = cfg.scaled(batch=1, hkv=1, hq=cfg.group)
     consts = {}
     if cfg.fmt == "turbo":
-        consts["rot"] = canonical_rotation(synth.gaussian_matrix(cfg.seed, cfg.head_dim, cfg.head_dim, stream=1))
+        if rotation == "haar":
+            consts["rot"] = canonical_rotation(synth.gaussian_matrix(cfg.seed, cfg.head_dim, cfg.head_dim, stream=1))
+        else:
+            consts["rot"] = canonical_hadamard_rotation(cfg.head_dim, rotation == "hadamard")
         consts["levels"], consts["thresholds"] = canonical_codebook(2, cfg.head_dim)
     if cfg.fmt in ("turbo", "qjl1"):
         consts["proj"] = canonical_projection(synth.gaussian_matrix(cfg.seed, 128, cfg.head_dim, stream=2))
@@ -141,6 +144,9 @@ def main():
     ap.add_argument("--queries", type=int, default=1,
                     help="query tokens per sequence (drafted positions checked in one pass); the step "
                          "appends that many tokens")
+    ap.add_argument("--rotation", default="haar", choices=["haar", "hadamard", "hadamard_plain"],
+                    help="TurboQuant rotation: a Haar draw, or the Hadamard transform with (or without) "
+                         "the bit-reversal permutation")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph replay")
     args = ap.parse_args()
@@ -162,7 +168,8 @@ def main():
     if cfg.fmt in ("turbo", "qjl1"):
         consts = make_constants(cfg.fmt, cfg.head_dim,
                                 synth.gaussian_matrix(cfg.seed, cfg.head_dim, cfg.head_dim, stream=1),
-                                synth.gaussian_matrix(cfg.seed, 128, cfg.head_dim, stream=2))
+                                synth.gaussian_matrix(cfg.seed, 128, cfg.head_dim, stream=2),
+                                rotation=args.rotation if cfg.fmt == "turbo" else "haar")
     cache = PackedKVCache(cfg.fmt, cfg.batch, cfg.hkv, cfg.head_dim, cfg.context, cfg.rope_dim, device=dev,
                           constants=consts, sink_tokens=args.sink, recent_tokens=args.recent)
     T = cfg.context
@@ -275,7 +282,8 @@ def main():
                    "kv_heads": cfg.hkv, "head_dim": cfg.head_dim, "rope_dim": cfg.rope_dim,
                    "context": T, "counted_bytes_per_step": nbytes,
                    "splits": args.splits or "auto", "queries_per_seq": nq,
-                   "bf16_sink_tokens": args.sink, "bf16_recent_tokens": args.recent},
+                   "bf16_sink_tokens": args.sink, "bf16_recent_tokens": args.recent,
+                   **({"rotation": args.rotation} if cfg.fmt == "turbo" else {})},
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "query_tokens_per_s": round(nq * cfg.batch / (ms_step * 1e-3), 1),
         "wall_s": round(wall, 3),
@@ -284,7 +292,7 @@ def main():
         "roofline": roofline(cfg, nbytes, dec_ms, nq, bool(args.sink or args.recent)),
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg)
+        res["cpu_baseline"] = cpu_baseline(cfg, rotation=args.rotation if cfg.fmt == "turbo" else "haar")
     print(json.dumps(res), flush=True)
 
 

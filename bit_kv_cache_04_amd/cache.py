@@ -57,11 +57,18 @@ def _packed_view_spec(fmt, B, H, T, d, rope, m):
     raise ValueError(fmt)
 
 
-def make_constants(fmt, head_dim, rot_gauss=None, proj_gauss=None):
-    """The method's constants from caller-drawn Gaussians, made by libkvq's host helpers."""
+def make_constants(fmt, head_dim, rot_gauss=None, proj_gauss=None, rotation="haar"):
+    """The method's constants from caller-drawn Gaussians, made by libkvq's host helpers
+    (rotation: "haar" from rot_gauss, or "hadamard" / "hadamard_plain", the structured
+    rotation with and without the bit-reversal permutation, which needs no draws)."""
     out = {}
     if fmt == "turbo":
-        out["rot"] = kvq.kv_make_rotation(rot_gauss)
+        if rotation == "haar":
+            out["rot"] = kvq.kv_make_rotation(rot_gauss)
+        elif rotation in ("hadamard", "hadamard_plain"):
+            out["rot"] = kvq.kv_make_hadamard_rotation(head_dim, rotation == "hadamard")
+        else:
+            raise ValueError(rotation)
         out["levels"], out["thresholds"] = kvq.kv_lloyd_max_gaussian(2, head_dim)
     if fmt in ("turbo", "qjl1"):
         out["proj"] = kvq.kv_make_projection(proj_gauss)

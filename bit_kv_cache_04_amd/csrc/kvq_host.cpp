@@ -340,6 +340,26 @@ extern "C" int kv_make_rotation(const double* gauss, int32_t d, float* rot) {
   return KV_OK;
 }
 
+extern "C" int kv_make_hadamard_rotation(int32_t d, int32_t bit_reverse, float* rot) {
+  if (!rot || d < 1 || d > 1024 || (d & (d - 1))) return KV_EINVAL;
+  int nbits = 0;
+  while ((1 << nbits) < d) ++nbits;
+  // Entry (i, j) multiplies x[j]; with the permutation first, x[j] meets Walsh
+  // column rev(j), and H[i][k] = (-1)^popcount(i & k).  Every entry is +-1/sqrt(d),
+  // one bf16 value up to sign.
+  const float mag = bf16_round(1.0 / std::sqrt((double)d));
+  for (int j = 0; j < d; ++j) {
+    int col = j;
+    if (bit_reverse) {
+      col = 0;
+      for (int b = 0; b < nbits; ++b) col |= ((j >> b) & 1) << (nbits - 1 - b);
+    }
+    for (int i = 0; i < d; ++i)
+      rot[(size_t)i * d + j] = (__builtin_popcount((unsigned)(i & col)) & 1) ? -mag : mag;
+  }
+  return KV_OK;
+}
+
 extern "C" int kv_make_projection(const double* gauss, int32_t m, int32_t d, float* proj) {
   if (!gauss || !proj || m < 1 || d < 1) return KV_EINVAL;
   for (size_t i = 0; i < (size_t)m * d; ++i) proj[i] = bf16_round(gauss[i]);

@@ -22,7 +22,8 @@ BUFFERS = ["k_codes", "k_scale", "k_zero", "k_sketch", "k_norm", "k_rnorm",
            "v_codes", "v_scale", "v_zero", "v_norm", "rope", "sink_k", "sink_v", "recent_k", "recent_v",
            "k_stage"]
 EXPORTED = ["kv_buffer_bytes", "kv_bytes_per_token", "kv_quant_append", "kv_quant_append_ragged", "kv_decode_attention",
-            "kv_lloyd_max_gaussian", "kv_make_rotation", "kv_make_projection", "kv_status_string"]
+            "kv_lloyd_max_gaussian", "kv_make_rotation", "kv_make_hadamard_rotation",
+            "kv_make_projection", "kv_status_string"]
 
 
 class KvError(RuntimeError):
@@ -77,6 +78,8 @@ def lib():
         L.kv_lloyd_max_gaussian.restype = ctypes.c_int
         L.kv_make_rotation.argtypes = [vp, i32, vp]
         L.kv_make_rotation.restype = ctypes.c_int
+        L.kv_make_hadamard_rotation.argtypes = [i32, i32, vp]
+        L.kv_make_hadamard_rotation.restype = ctypes.c_int
         L.kv_make_projection.argtypes = [vp, i32, i32, vp]
         L.kv_make_projection.restype = ctypes.c_int
         L.kv_status_string.argtypes = [ctypes.c_int]
@@ -149,6 +152,12 @@ def kv_make_rotation(gauss) -> np.ndarray:
     d = g.shape[0]
     out = np.zeros((d, d), np.float32)
     _check("kv_make_rotation", lib().kv_make_rotation(g.ctypes.data, d, out.ctypes.data))
+    return out
+
+
+def kv_make_hadamard_rotation(d: int, bit_reverse: bool = True) -> np.ndarray:
+    out = np.zeros((d, d), np.float32)
+    _check("kv_make_hadamard_rotation", lib().kv_make_hadamard_rotation(d, int(bool(bit_reverse)), out.ctypes.data))
     return out
 
 

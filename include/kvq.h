@@ -271,6 +271,18 @@ int kv_lloyd_max_gaussian(int32_t bits, int32_t dim, float* levels, float* thres
  * d in [1, 1024]; a rank-deficient input gives KV_EINVAL. */
 int kv_make_rotation(const double* gauss, int32_t d, float* rot);
 
+/* Structured rotation in place of the random one: R = H P / sqrt(d), H the
+ * Sylvester Hadamard matrix (H[i][k] = (-1)^popcount(i & k)) and P the
+ * bit-reversal permutation of the d input channels (applied first; identity
+ * when bit_reverse is 0), so that a few loud channels are spread evenly over
+ * every coordinate (page "TurboQuant vs OSCAR vs EpiCache", section
+ * "quantization frontiers", the OSCAR paragraph: a Hadamard transform with a
+ * bit-reversal permutation).  Written as fp32 row-major, y = R x; every entry is
+ * +-bf16(1/sqrt(d)), so R R^T is the identity times a scalar within 2^-8 of 1.
+ * It takes the place of kv_make_rotation's output in kv_cache.rot.  d a power
+ * of two in [1, 1024], else KV_EINVAL. */
+int kv_make_hadamard_rotation(int32_t d, int32_t bit_reverse, float* rot);
+
 /* QJL matrix from m x d iid N(0,1) draws (row-major fp64): each draw rounded
  * to bf16, written as fp32 (same section, stage two). */
 int kv_make_projection(const double* gauss, int32_t m, int32_t d, float* proj);
