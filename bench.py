@@ -114,10 +114,10 @@ def measured_traffic(workload):
     return None
 
 
-def roofline(cfg, nbytes, dec_ms, nq=1, windowed=False):
+def roofline(cfg, nbytes, dec_ms, nq=1, windowed=False, paged=False):
     """Roofline of the split-context attention kernel, timed by events around its launch.
     The counter summaries cover the one-query kernels: traffic is None for nq > 1."""
-    traffic = measured_traffic(cfg.name) if nq == 1 and not windowed else None
+    traffic = measured_traffic(cfg.name) if nq == 1 and not windowed and not paged else None
     if cfg.fmt == "latent":
         # 128 heads x (576 + 512) x 2 flop per token: a dense contraction on fp16 matrix cores
         flops = 2.0 * nq * cfg.batch * cfg.context * cfg.hq * (cfg.key_width + cfg.head_dim)
@@ -147,6 +147,9 @@ def main():
     ap.add_argument("--rotation", default="haar", choices=["haar", "hadamard", "hadamard_plain"],
                     help="TurboQuant rotation: a Haar draw, or the Hadamard transform with (or without) "
                          "the bit-reversal permutation")
+    ap.add_argument("--page-tokens", type=int, default=0,
+                    help="paged storage: tokens per page, the pool's pages assigned to sequences in a seeded "
+                         "shuffled order")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph replay")
     args = ap.parse_args()
@@ -170,8 +173,14 @@ def main():
                                 synth.gaussian_matrix(cfg.seed, cfg.head_dim, cfg.head_dim, stream=1),
                                 synth.gaussian_matrix(cfg.seed, 128, cfg.head_dim, stream=2),
                                 rotation=args.rotation if cfg.fmt == "turbo" else "haar")
+    paging = {}
+    if args.page_tokens:
+        import numpy as np
+        per_seq = cfg.context // args.page_tokens
+        table = np.random.default_rng(cfg.seed).permutation(cfg.batch * per_seq).reshape(cfg.batch, per_seq)
+        paging = dict(page_tokens=args.page_tokens, num_pages=cfg.batch * per_seq, block_table=table)
     cache = PackedKVCache(cfg.fmt, cfg.batch, cfg.hkv, cfg.head_dim, cfg.context, cfg.rope_dim, device=dev,
-                          constants=consts, sink_tokens=args.sink, recent_tokens=args.recent)
+                          constants=consts, sink_tokens=args.sink, recent_tokens=args.recent, **paging)
     T = cfg.context
     # prefill the first T - n tokens (untimed), one sequence and 16K tokens at a
     # time to bound input memory
@@ -283,13 +292,14 @@ def main():
                    "context": T, "counted_bytes_per_step": nbytes,
                    "splits": args.splits or "auto", "queries_per_seq": nq,
                    "bf16_sink_tokens": args.sink, "bf16_recent_tokens": args.recent,
+                   **({"page_tokens": args.page_tokens} if args.page_tokens else {}),
                    **({"rotation": args.rotation} if cfg.fmt == "turbo" else {})},
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "query_tokens_per_s": round(nq * cfg.batch / (ms_step * 1e-3), 1),
         "wall_s": round(wall, 3),
         "timing": "hip-graph replay of the step" if not args.no_graph else "eager launches",
         "ms_per_step_eager": round(ms_eager, 5),
-        "roofline": roofline(cfg, nbytes, dec_ms, nq, bool(args.sink or args.recent)),
+        "roofline": roofline(cfg, nbytes, dec_ms, nq, bool(args.sink or args.recent), bool(args.page_tokens)),
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, rotation=args.rotation if cfg.fmt == "turbo" else "haar")

@@ -24,15 +24,22 @@ def _stream_ptr(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def buffer_view_spec(fmt, B, H, T, d, rope=0, m=128, sink=0, recent=0):
-    """{name: (torch dtype, shape)} of each buffer's natural element view."""
-    u8, u16, f32 = torch.uint8, torch.uint16, torch.float32
+def buffer_view_spec(fmt, B, H, T, d, rope=0, m=128, sink=0, recent=0, page_tokens=0, num_pages=0):
+    """{name: (torch dtype, shape)} of each buffer's natural element view (paged
+    storage: the per-token buffers as [num_pages][H][page_tokens] pools)."""
+    u16 = torch.uint16
     win = {}
+    if page_tokens:
+        spec = _packed_view_spec(fmt, num_pages, H, page_tokens, d, rope, m)
+        if "k_stage" in spec:
+            spec["k_stage"] = (torch.float32, (B, H, 4 + 32 * d))
+    else:
+        spec = _packed_view_spec(fmt, B, H, T, d, rope, m)
     if sink:
         win.update(sink_k=(u16, (B, H, sink, d)), sink_v=(u16, (B, H, sink, d)))
     if recent:
         win.update(recent_k=(u16, (B, H, recent, d)), recent_v=(u16, (B, H, recent, d)))
-    return {**_packed_view_spec(fmt, B, H, T, d, rope, m), **win}
+    return {**spec, **win}
 
 
 def _packed_view_spec(fmt, B, H, T, d, rope, m):
@@ -77,12 +84,22 @@ def make_constants(fmt, head_dim, rot_gauss=None, proj_gauss=None, rotation="haa
 
 class PackedKVCache:
     def __init__(self, fmt, batch, num_kv_heads, head_dim, capacity, rope_dim=0, device="cuda",
-                 constants=None, sink_tokens=0, recent_tokens=0):
+                 constants=None, sink_tokens=0, recent_tokens=0, page_tokens=0, num_pages=0, block_table=None):
+        """Paged storage: page_tokens > 0, a pool of num_pages pages, and block_table
+        int [batch][capacity // page_tokens] naming each sequence's pages (default:
+        sequence b's page j is pool page b * capacity // page_tokens + j)."""
         self.fmt, self.device = fmt, torch.device(device)
         self.B, self.H, self.d, self.T, self.rope = batch, num_kv_heads, head_dim, capacity, rope_dim
         self.sink, self.recent = sink_tokens, recent_tokens
+        self.P, self.num_pages = page_tokens, num_pages
+        self.table = None
+        if page_tokens:
+            per_seq = capacity // page_tokens
+            if block_table is None:
+                block_table = np.arange(batch * per_seq, dtype=np.int32).reshape(batch, per_seq)
+            self.table = torch.as_tensor(np.ascontiguousarray(block_table, dtype=np.int32)).to(self.device)
         self.layout = make_layout(fmt, batch, num_kv_heads, head_dim, capacity, rope_dim, sink_tokens,
-                                  recent_tokens)
+                                  recent_tokens, page_tokens, num_pages)
         self.bufs = {}
         ptrs = []
         for i, name in enumerate(BUFFERS):
@@ -97,7 +114,8 @@ class PackedKVCache:
             self.consts[k] = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(self.device)
         cp = lambda k: self.consts[k].data_ptr() if k in self.consts else None  # noqa: E731
         self.struct = KVCache(self.layout, (ctypes.c_void_p * len(BUFFERS))(*ptrs),
-                              cp("rot"), cp("proj"), cp("levels"), cp("thresholds"))
+                              cp("rot"), cp("proj"), cp("levels"), cp("thresholds"),
+                              self.table.data_ptr() if self.table is not None else None)
         self._ws = None
 
     def sequence(self, b):
@@ -106,19 +124,23 @@ class PackedKVCache:
         sub = PackedKVCache.__new__(PackedKVCache)
         sub.__dict__.update(self.__dict__)
         sub.B = 1
-        sub.layout = make_layout(self.fmt, 1, self.H, self.d, self.T, self.rope, self.sink, self.recent)
-        sub.bufs = {n: t.view(self.B, -1)[b] for n, t in self.bufs.items()}
+        sub.layout = make_layout(self.fmt, 1, self.H, self.d, self.T, self.rope, self.sink, self.recent, self.P,
+                                 self.num_pages)
+        # a paged pool is shared; per-sequence buffers (windows, staging) are sliced
+        pool = lambda n: self.P and BUFFERS.index(n) < BUFFERS.index("sink_k")  # noqa: E731
+        sub.bufs = {n: (t if pool(n) else t.view(self.B, -1)[b]) for n, t in self.bufs.items()}
+        sub.table = self.table[b:b + 1] if self.table is not None else None
         ptrs = [sub.bufs[n].data_ptr() if n in sub.bufs else None for n in BUFFERS]
         c = self.struct
         sub.struct = KVCache(sub.layout, (ctypes.c_void_p * len(BUFFERS))(*ptrs), c.rot, c.proj,
-                             c.lm_levels, c.lm_thresh)
+                             c.lm_levels, c.lm_thresh, sub.table.data_ptr() if sub.table is not None else None)
         sub._ws = None
         return sub
 
     # ---- views of the packed bytes
     def view(self, name):
         dt, shape = buffer_view_spec(self.fmt, self.B, self.H, self.T, self.d, self.rope, sink=self.sink,
-                                     recent=self.recent)[name]
+                                     recent=self.recent, page_tokens=self.P, num_pages=self.num_pages)[name]
         return self.bufs[name].view(dt).view(shape)
 
     def bytes_per_token(self, num_layers=1):

@@ -71,7 +71,7 @@ extern "C" int kv_decode_attention(const kv_cache* c, const void* q, int32_t q_d
   if (nq > 64) return KV_EUNSUPPORTED;
   // mixed precision: the splits cover the packed tokens from sink_tokens on, and
   // the bf16 window adds one split of partial rows
-  const int packed_len = std::max(1, max_seq_len - L.sink_tokens);
+  const int packed_len = std::max(1, max_seq_len - (L.sink_tokens & ~31));  // matrix-core tiles start 32-aligned
   const SplitPlan plan = plan_splits(&L, num_q_heads, nq, q_dtype, packed_len, req);
   const int part_splits = plan.splits + window_chunks(L);
   const DecodeWorkspace wsl = decode_workspace(&L, nq * num_q_heads, part_splits);

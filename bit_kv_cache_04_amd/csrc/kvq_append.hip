@@ -29,16 +29,24 @@ struct AppendPos {
   int start;   // every sequence's first position when ragged == 0
   int ragged;  // 1: sequence b starts at s[b]
   int heads;   // sequence-head rows per sequence (KV heads; 1 for the latent)
+  PageMap pm;  // where the launch's sequences keep their token rows
   int32_t s[kMaxRaggedSeqs];
 };
 __device__ __forceinline__ int start_of(const AppendPos& p, size_t bh) {
   return p.ragged ? p.s[bh / p.heads] : p.start;
 }
 
+// Cache row of sequence-head bh's position t (kNoRow: a page outside the pool,
+// whose stores are dropped).
+__device__ __forceinline__ size_t seq_row(const AppendPos& pos, size_t bh, int t, int cap) {
+  if (!pos.pm.table) return bh * (size_t)cap + t;
+  return token_row(pos.pm, pos.heads, (int)(bh / pos.heads), (int)(bh % pos.heads), t);
+}
+
 // Token rows of an append are flat indices r in [0, bh_count * n): sequence-head
 // bh = r / n, position start_of(bh) + r % n; the input row r starts at x + r * stride.
 __device__ __forceinline__ size_t dst_row(size_t r, int n, int cap, const AppendPos& pos) {
-  return (r / n) * (size_t)cap + start_of(pos, r / n) + (r % n);
+  return seq_row(pos, r / n, start_of(pos, r / n) + (int)(r % n), cap);
 }
 
 // ---------------------------------------------------------------- FP4
@@ -163,6 +171,7 @@ __device__ __forceinline__ void fp4_store_at(const float (&a)[16], const InT* ta
   unsigned long long packed;
   uint16_t sb;
   fp4_encode16(a, packed, sb, tag);
+  if (dr == kNoRow) return;
   *reinterpret_cast<unsigned long long*>(codes + dr * (d / 2) + g * 8) = packed;
   scales[dr * (d / 16) + g] = sb;
 }
@@ -216,7 +225,8 @@ __global__ void __launch_bounds__(256) latent_append_kernel(const InT* __restric
     const int c = (int)(gid % rope_dim);
     const size_t r = gid / rope_dim;
     const float val = load_as_f32(x + r * stride + d, c);
-    rope[dst_row(r, n, cap, pos) * rope_dim + c] = bf16_from_f64((double)val);
+    const size_t dr = dst_row(r, n, cap, pos);
+    if (dr != kNoRow) rope[dr * rope_dim + c] = bf16_from_f64((double)val);
   }
 }
 
@@ -289,8 +299,9 @@ __global__ void __launch_bounds__(256) kivi_append_kernel(const InT* __restrict_
   __syncthreads();
   const int quads = d / 4;
   const int start = start_of(pos, bh);
-  const size_t slot0 = bh * cap + start + (size_t)g * 32;  // cache row of the group's first token
+  const size_t slot0 = seq_row(pos, bh, start + g * 32, cap);  // cache row of the group's first token
   if (tid == 0 && g == ngroups - 1) set_appended(stage, bh, d, start + n);
+  if (slot0 == kNoRow) return;  // a page outside the pool
   if (tid < quads) {
     const int cq = tid;
     float mn[4], mx[4];
@@ -311,7 +322,7 @@ __global__ void __launch_bounds__(256) kivi_append_kernel(const InT* __restrict_
       for (int j = 0; j < 4; ++j) byte |= kivi_code(xk[t][4 * cq + j], mn[j], sc[j]) << (2 * j);
       kc[(slot0 + t) * quads + cq] = (uint8_t)byte;
     }
-    const size_t meta = (bh * (cap / 32) + start / 32 + g) * (size_t)d + 4 * cq;
+    const size_t meta = slot0 / 32 * (size_t)d + 4 * cq;  // pages and the layout hold whole groups
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       ks[meta + j] = sc[j];
@@ -373,9 +384,9 @@ __global__ void __launch_bounds__(256) kivi_append_any_kernel(const InT* __restr
   }
   __syncthreads();
   const int quads = d / 4;
-  const size_t slot0 = bh * cap + g0;  // cache row of the group's first token
+  const size_t slot0 = seq_row(pos, bh, g0, cap);  // cache row of the group's first token
   if (complete) {
-    if (tid < quads) {
+    if (tid < quads && slot0 != kNoRow) {
       const int cq = tid;
       float mn[4], mx[4];
 #pragma unroll
@@ -395,7 +406,7 @@ __global__ void __launch_bounds__(256) kivi_append_any_kernel(const InT* __restr
         for (int j = 0; j < 4; ++j) byte |= kivi_code(xk[t][4 * cq + j], mn[j], sc[j]) << (2 * j);
         kc[(slot0 + t) * quads + cq] = (uint8_t)byte;
       }
-      const size_t meta = (bh * (cap / 32) + g0 / 32) * (size_t)d + 4 * cq;
+      const size_t meta = slot0 / 32 * (size_t)d + 4 * cq;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         ks[meta + j] = sc[j];
@@ -410,7 +421,7 @@ __global__ void __launch_bounds__(256) kivi_append_any_kernel(const InT* __restr
   }
   if (tid == 0 && g0 + 32 >= s + n) set_appended(stage, bh, d, s + n);  // the group of the last token
   const int vgroups = d / 32;
-  for (int it = tid; it < (a1 - a0) * vgroups; it += 256) {
+  for (int it = tid; slot0 != kNoRow && it < (a1 - a0) * vgroups; it += 256) {
     const int t = a0 - g0 + it / vgroups, vg = it % vgroups;
     float mn = INFINITY, mx = -INFINITY;
     for (int i = 0; i < 32; ++i) {
@@ -640,7 +651,7 @@ __device__ __forceinline__ void qjl_key_tile(const KeyFrag<InT>& fr, size_t base
       }
     }
   }
-  if (lane < 16 && base + lane < rows) {
+  if (lane < 16 && base + lane < rows && my_dst != kNoRow) {
     *reinterpret_cast<uint4*>(sketch + my_dst * 16) = make_uint4(words[0], words[1], words[2], words[3]);
     knorm[my_dst] = f16_from_f64_nonneg(nrm);
   }
@@ -709,7 +720,7 @@ qjl_append_kernel(const InT* __restrict__ k, const InT* __restrict__ v,
         bh += p / (uint32_t)n;
         p %= (uint32_t)n;
       }
-      return bh * (size_t)cap + (size_t)start_of(pos, bh) + p;
+      return seq_row(pos, bh, start_of(pos, bh) + (int)p, cap);
     };
     // values first: the 128 groups of rows [base, base + 16), two per lane
     // (group g of the flat row-major input starts at v + 16 g), then the key
@@ -827,10 +838,12 @@ __device__ __forceinline__ void turbo_body(const InT* __restrict__ x, const floa
         for (int b = 0; b < 16; ++b) v |= (uint32_t)ip[j * 16 + b] << (2 * b);
         w[j] = v;
       }
-      uint4* dst = reinterpret_cast<uint4*>(codes + dr * 32);
-      dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-      dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-      norm_out[dr] = f16_from_f64_nonneg(nrm);
+      if (dr != kNoRow) {  // else a page outside the pool
+        uint4* dst = reinterpret_cast<uint4*>(codes + dr * 32);
+        dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        norm_out[dr] = f16_from_f64_nonneg(nrm);
+      }
     }
     if (WITH_SKETCH) {
       // gamma^2 per token: rows are spread over the 16 lanes of each quarter
@@ -877,8 +890,10 @@ __device__ __forceinline__ void turbo_body(const InT* __restrict__ x, const floa
           w[j] = lo | (hi << 16);
         }
         const size_t dr = dst_row(base + lane, n, cap, pos);
-        *reinterpret_cast<uint4*>(sketch + dr * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-        rnorm_out[dr] = f16_from_f64_nonneg(sqrt(g2));
+        if (dr != kNoRow) {
+          *reinterpret_cast<uint4*>(sketch + dr * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+          rnorm_out[dr] = f16_from_f64_nonneg(sqrt(g2));
+        }
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -997,8 +1012,10 @@ __global__ void __launch_bounds__(512) turbo_append_small_kernel(
     word |= __shfl_xor(word, 2);
     word |= __shfl_xor(word, 4);
     word |= __shfl_xor(word, 8);
-    if (col == 0 && base + tok < rows)
-      *reinterpret_cast<uint32_t*>(codes + dst_row(base + tok, n, cap, pos) * 32 + 4 * w) = word;
+    if (col == 0 && base + tok < rows) {
+      const size_t dr = dst_row(base + tok, n, cap, pos);
+      if (dr != kNoRow) *reinterpret_cast<uint32_t*>(codes + dr * 32 + 4 * w) = word;
+    }
     if (keys) {
       const double lv = id == 0 ? lv0 : id == 1 ? lv1 : id == 2 ? lv2 : lv3;
       const double r = u - lv;
@@ -1018,8 +1035,10 @@ __global__ void __launch_bounds__(512) turbo_append_small_kernel(
       if (col == 0) g2part[w][kq + 4 * i] = t;
     }
   }
-  if (w == 0 && lane < 16 && base + lane < rows)
-    (keys ? knorm : vnorm)[dst_row(base + lane, n, cap, pos)] = f16_from_f64_nonneg(nrm);
+  if (w == 0 && lane < 16 && base + lane < rows) {
+    const size_t dr = dst_row(base + lane, n, cap, pos);
+    if (dr != kNoRow) (keys ? knorm : vnorm)[dr] = f16_from_f64_nonneg(nrm);
+  }
   if (!keys) return;
   __syncthreads();
   // S r for sketch rows 16 w .. 16 w + 15
@@ -1039,8 +1058,8 @@ __global__ void __launch_bounds__(512) turbo_append_small_kernel(
   }
   if (lane < 16 && base + lane < rows) {
     const size_t dr = dst_row(base + lane, n, cap, pos);
-    *reinterpret_cast<uint16_t*>(sketch + dr * 16 + 2 * w) = (uint16_t)my_bits;
-    if (w == 0) {
+    if (dr != kNoRow) *reinterpret_cast<uint16_t*>(sketch + dr * 16 + 2 * w) = (uint16_t)my_bits;
+    if (w == 0 && dr != kNoRow) {
       double g2 = 0.0;
       for (int ww = 0; ww < 8; ++ww) g2 += g2part[ww][lane];
       krnorm[dr] = f16_from_f64_nonneg(sqrt(g2));
@@ -1196,12 +1215,18 @@ int launch_append(const kv_cache* c, const void* k, const void* v, int in_dtype,
     const int nb = std::min(chunk, L.batch - b0);
     kv_cache sub = *c;
     sub.layout.batch = nb;
+    // a paged pool is shared by every sequence: only the per-sequence buffers
+    // (windows, staging) and the block table move
+    const bool paged = L.page_tokens > 0;
     for (int i = 0; i < KV_BUF_COUNT; ++i)
-      if (c->buf[i]) sub.buf[i] = static_cast<char*>(c->buf[i]) + (size_t)b0 * (kv_buffer_bytes(&L, i) / L.batch);
+      if (c->buf[i] && !(paged && i < KV_BUF_SINK_K))
+        sub.buf[i] = static_cast<char*>(c->buf[i]) + (size_t)b0 * (kv_buffer_bytes(&L, i) / L.batch);
+    if (paged) sub.block_table = c->block_table + (size_t)b0 * (L.capacity / L.page_tokens);
     AppendPos pos{};
     pos.start = start;
     pos.ragged = starts ? 1 : 0;
     pos.heads = heads;
+    pos.pm = page_map(&sub);
     for (int b = 0; starts && b < nb; ++b) pos.s[b] = starts[b0 + b];
     const char* kb = static_cast<const char*>(k) + (size_t)b0 * in_seq_bytes;
     const char* vb = v ? static_cast<const char*>(v) + (size_t)b0 * in_seq_bytes : nullptr;

@@ -35,6 +35,7 @@ struct DecodeArgs {
   const uint16_t* rope;
   const float* levels;
   int H, cap, d, rope_dim;
+  PageMap pm;  // token rows (paged storage or contiguous)
   // query / output
   const float* qv;  // prepared queries [B][nq][Hq][QW]
   int Hq, G, head_blocks, hb_size;
@@ -50,11 +51,11 @@ struct DecodeArgs {
 
 // ---------------------------------------------------------------- per-format element access
 
-// Virtual key element c of token (bh, t); the logit is <prepared q, key>.
+// Virtual key element c of token t of sequence-head bh, at cache row `row`; the
+// logit is <prepared q, key>.  kstage: the first token whose key is read from
+// staging (KIVI2 only).
 template <int FMT>
-// kstage: the first token whose key is read from staging (KIVI2 only).
-__device__ __forceinline__ float key_elem(const DecodeArgs& a, size_t bh, int t, int c, int kstage) {
-  const size_t row = bh * a.cap + t;
+__device__ __forceinline__ float key_elem(const DecodeArgs& a, size_t bh, size_t row, int t, int c, int kstage) {
   if constexpr (FMT == KV_FMT_FP4 || FMT == KV_FMT_LATENT_FP4) {
     if (FMT == KV_FMT_LATENT_FP4 && c >= a.d) return bf16_to_f32(a.rope[row * a.rope_dim + (c - a.d)]);
     const uint32_t nib = (a.k_codes[row * (a.d / 2) + c / 2] >> (4 * (c & 1))) & 15u;
@@ -63,7 +64,7 @@ __device__ __forceinline__ float key_elem(const DecodeArgs& a, size_t bh, int t,
   } else if constexpr (FMT == KV_FMT_KIVI2) {
     if (t >= kstage) return a.k_stage[bh * (4 + 32 * a.d) + 4 + (t & 31) * a.d + c];  // not yet coded
     const uint32_t code = (a.k_codes[row * (a.d / 4) + c / 4] >> (2 * (c & 3))) & 3u;
-    const size_t m = (bh * (a.cap / 32) + t / 32) * a.d + c;
+    const size_t m = row / 32 * a.d + c;  // pages and the layout hold whole groups
     return fmaf((float)code, static_cast<const float*>(a.k_scale)[m], a.k_zero[m]);
   } else if constexpr (FMT == KV_FMT_TURBO) {
     const float n = f16_to_f32(a.k_norm[row]);
@@ -82,10 +83,10 @@ __device__ __forceinline__ float key_elem(const DecodeArgs& a, size_t bh, int t,
   }
 }
 
-// Value element c of token (bh, t) (TURBO: in the rotated space, times n_v).
+// Value element c of the token at cache row `row` (TURBO: in the rotated space,
+// times n_v).
 template <int FMT>
-__device__ __forceinline__ float value_elem(const DecodeArgs& a, size_t bh, int t, int c) {
-  const size_t row = bh * a.cap + t;
+__device__ __forceinline__ float value_elem(const DecodeArgs& a, size_t row, int c) {
   if constexpr (FMT == KV_FMT_FP4 || FMT == KV_FMT_QJL1_FP4V) {
     const uint32_t nib = (a.v_codes[row * (a.d / 2) + c / 2] >> (4 * (c & 1))) & 15u;
     const float s = bf16_to_f32(static_cast<const uint16_t*>(a.v_scale)[row * (a.d / 16) + c / 16]);
@@ -136,6 +137,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
     return ((size_t)b * a.nq + vh / a.Gr) * a.Hq + (size_t)h * a.Gr + vh % a.Gr;
   };
   __shared__ int lim[HB];
+  __shared__ size_t trow[TT];  // cache rows of the tile's tokens (kNoRow: a page outside the pool)
 
   for (int e = tid; e < HB * DK; e += NT) {
     const int hh = e / DK, c = e % DK;
@@ -153,14 +155,19 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
 
   for (int t0 = t_begin; t0 < t_end; t0 += TT) {
     const int nt = min(TT, t_end - t0);
+    if (tid < TT) trow[tid] = tid < nt ? token_row(a.pm, a.H, b, h, t0 + tid) : kNoRow;
+    __syncthreads();
     for (int e = tid; e < TT * DK; e += NT) {
       const int t = e / DK, c = e % DK;
-      ks[t][c] = t < nt ? key_elem<FMT>(a, bh, t0 + t, c, kstage) : 0.f;
+      const size_t row = trow[t];
+      // a staged KIVI key needs no row
+      const bool live = t < nt && (row != kNoRow || (FMT == KV_FMT_KIVI2 && t0 + t >= kstage));
+      ks[t][c] = live ? key_elem<FMT>(a, bh, row, t0 + t, c, kstage) : 0.f;
     }
     if constexpr (!kAlias) {
       for (int e = tid; e < TT * DV; e += NT) {
         const int t = e / DV, c = e % DV;
-        vs[t][c] = t < nt ? value_elem<FMT>(a, bh, t0 + t, c) : 0.f;
+        vs[t][c] = t < nt && trow[t] != kNoRow ? value_elem<FMT>(a, trow[t], c) : 0.f;
       }
     }
     __syncthreads();
@@ -700,6 +707,7 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     f.k_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_K_CODES]);
     f.k_scale = static_cast<const uint16_t*>(c->buf[KV_BUF_K_SCALE]);
     f.rope = static_cast<const uint16_t*>(c->buf[KV_BUF_ROPE]);
+    f.pm = page_map(c);
     f.q = q;
     f.seq_lens = seq_lens;
     f.max_len = max_seq_len;
@@ -741,6 +749,7 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     f.v_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_V_CODES]);
     f.v_norm = static_cast<const uint16_t*>(c->buf[KV_BUF_V_NORM]);
     f.levels = c->lm_levels;
+    f.pm = page_map(c);
     f.q = qv;
     f.qpieces = qpieces;
     f.seq_lens = seq_lens;
@@ -768,6 +777,7 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     f.k_norm = static_cast<const uint16_t*>(c->buf[KV_BUF_K_NORM]);
     f.v_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_V_CODES]);
     f.v_scale = static_cast<const uint16_t*>(c->buf[KV_BUF_V_SCALE]);
+    f.pm = page_map(c);
     f.q = L.format == KV_FMT_FP4 ? q : static_cast<const void*>(qv);
     f.qpieces = qpieces;
     f.seq_lens = seq_lens;
@@ -819,6 +829,7 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
   a.cap = L.capacity;
   a.d = L.head_dim;
   a.rope_dim = L.rope_dim;
+  a.pm = page_map(c);
   a.qv = qv;
   a.Hq = num_q_heads;
   a.nq = nq;

@@ -95,6 +95,13 @@ struct Res {
   __amdgpu_buffer_rsrc_t codes, scale, rope;
 };
 
+// A tile's loads: resources over its page's token rows (a contiguous cache: the
+// sequence's rows) and its first row in them.
+struct TileSrc {
+  Res r;
+  int t;
+};
+
 // Direct-to-LDS loads of one packed tile, spread evenly over the NW waves
 // (32 / NW loads each).  The token offset rides in the range-checked VGPR
 // offset: a tile at or past the end of the resources reads zeros.
@@ -129,7 +136,8 @@ __device__ __forceinline__ void scale_acc(float& x, float f) {
                : "v"(f));
 }
 
-template <int NW>
+// PAGED: token rows in pool pages named by the block table, resources per tile.
+template <int NW, bool PAGED>
 __global__ void __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(1, 1))) decode_latent_kernel(MfmaDecodeArgs a) {
   constexpr int NT = 64 * NW;
@@ -174,14 +182,31 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) decode_latent_kernel(MfmaDecodeArgs a
   for (int n = 0; n < 16; ++n) o[n] = f16v_t{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  const Res res{rsrc(a.k_codes + (size_t)b * a.cap * 256, (size_t)a.cap * 256),
-                rsrc(a.k_scale + (size_t)b * a.cap * 32, (size_t)a.cap * 64),
-                rsrc(a.rope + (size_t)b * a.cap * 64, (size_t)a.cap * 128)};
-  const int none = a.cap;
-  auto tile_or_none = [&](int t) { return t < t_end ? t : none; };
+  // resources over nrows token rows from row0 (nrows 0: every read is zeros)
+  auto res_at = [&](size_t row0, int nrows) {
+    return Res{rsrc(a.k_codes + row0 * 256, (size_t)nrows * 256), rsrc(a.k_scale + row0 * 32, (size_t)nrows * 64),
+               rsrc(a.rope + row0 * 64, (size_t)nrows * 128)};
+  };
+  const Res res = res_at((size_t)b * a.cap, a.cap);
+  // a missing tile reads past the end of its resources
+  auto tile_or_none = [&](int t) {
+    TileSrc s;
+    if constexpr (!PAGED) {
+      s.r = res;
+      s.t = t < t_end ? t : a.cap;
+    } else {
+      const int pg = t < t_end ? page_of_uniform(a.pm, b, t) : -1;
+      s.r = res_at((size_t)(pg < 0 ? 0 : pg) * a.pm.tokens, pg < 0 ? 0 : a.pm.tokens);
+      s.t = pg < 0 ? 0 : t & (a.pm.tokens - 1);
+    }
+    return s;
+  };
 
-  issue_tile<NW>(stA, wave, lane, tile_or_none(t_begin), res);
-  issue_tile<NW>(stB, wave, lane, tile_or_none(t_begin + kTile), res);
+  {
+    const TileSrc s0 = tile_or_none(t_begin), s1 = tile_or_none(t_begin + kTile);
+    issue_tile<NW>(stA, wave, lane, s0.t, s0.r);
+    issue_tile<NW>(stB, wave, lane, s1.t, s1.r);
+  }
 
   // lane constants of the fragment reads (kept opaque so that the compiler does
   // not hoist one address register per read out of the loop)
@@ -228,7 +253,10 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) decode_latent_kernel(MfmaDecodeArgs a
       }
       __syncthreads();
       // -------- the stage is free: refill it two tiles ahead
-      issue_tile<NW>(st, wave, lane, tile_or_none(tt + 2 * kTile), res);
+      {
+        const TileSrc nx = tile_or_none(tt + 2 * kTile);
+        issue_tile<NW>(st, wave, lane, nx.t, nx.r);
+      }
       // -------- 3. S^T = K Q^T for this wave's 32 heads (two accumulation chains)
       f16v_t s = f16v_t{}, s2 = f16v_t{};
 #pragma unroll
@@ -346,15 +374,22 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) decode_latent_kernel(MfmaDecodeArgs a
 
 }  // namespace
 
-int launch_decode_latent(const MfmaDecodeArgs& a, int B, hipStream_t st) {
+namespace {
+template <bool PAGED>
+int launch_latent(const MfmaDecodeArgs& a, int B, hipStream_t st) {
   dim3 grid(a.splits, B);
   switch (a.Hq) {
-    case 32: decode_latent_kernel<1><<<grid, 64, 0, st>>>(a); break;
-    case 64: decode_latent_kernel<2><<<grid, 128, 0, st>>>(a); break;
-    case 128: decode_latent_kernel<4><<<grid, 256, 0, st>>>(a); break;
+    case 32: decode_latent_kernel<1, PAGED><<<grid, 64, 0, st>>>(a); break;
+    case 64: decode_latent_kernel<2, PAGED><<<grid, 128, 0, st>>>(a); break;
+    case 128: decode_latent_kernel<4, PAGED><<<grid, 256, 0, st>>>(a); break;
     default: return KV_EUNSUPPORTED;
   }
   return KV_OK;
+}
+}  // namespace
+
+int launch_decode_latent(const MfmaDecodeArgs& a, int B, hipStream_t st) {
+  return a.pm.table ? launch_latent<true>(a, B, st) : launch_latent<false>(a, B, st);
 }
 
 }  // namespace kvq

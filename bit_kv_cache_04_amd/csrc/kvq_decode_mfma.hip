@@ -140,9 +140,9 @@ struct KeysFp4 {
       }
     }
   }
-  __device__ static R resources(const MfmaDecodeArgs& a, size_t bh) {
-    return R{rsrc(a.k_codes + bh * a.cap * 64, (size_t)a.cap * 64),
-             rsrc(a.k_scale + bh * a.cap * 8, (size_t)a.cap * 16)};
+  // over nrows token rows from row0
+  __device__ static R resources(const MfmaDecodeArgs& a, size_t row0, int nrows) {
+    return R{rsrc(a.k_codes + row0 * 64, (size_t)nrows * 64), rsrc(a.k_scale + row0 * 8, (size_t)nrows * 16)};
   }
   __device__ static void issue(uint8_t* st, int lane, int t0, const R& r) {
     const int co = t0 * 64 + lane * 16, so = t0 * 16 + lane * 4;
@@ -233,9 +233,8 @@ struct KeysQjl {
     s += __shfl_xor(s, 32);
     q.sumq = s;
   }
-  __device__ static R resources(const MfmaDecodeArgs& a, size_t bh) {
-    return R{rsrc(a.k_sketch + bh * a.cap * 16, (size_t)a.cap * 16),
-             rsrc(a.k_norm + bh * a.cap, (size_t)a.cap * 2), a.cap * 2};
+  __device__ static R resources(const MfmaDecodeArgs& a, size_t row0, int nrows) {
+    return R{rsrc(a.k_sketch + row0 * 16, (size_t)nrows * 16), rsrc(a.k_norm + row0, (size_t)nrows * 2), nrows * 2};
   }
   __device__ static void issue(uint8_t* st, int lane, int t0, const R& r) {
     const int so = t0 * 16 + lane * 4;
@@ -303,6 +302,15 @@ struct VRsrc {
   __amdgpu_buffer_rsrc_t vc, vs;
 };
 
+// Where the next tile's loads go: resources over the token rows of its page (a
+// contiguous cache: the (sequence, KV head)'s rows) and its first row in them.
+template <class KP>
+struct TileSrc {
+  typename KP::R kr;
+  VRsrc vr;
+  int t;
+};
+
 // Direct-to-LDS loads of one tile: lane i moves bytes [size*i, size*i + size) of
 // each chunk.  The token offset travels in the bounds-checked VGPR offset, so a
 // tile past the end of the resource (including the no-tile sentinel, t0 =
@@ -334,13 +342,12 @@ struct Limits {
 };
 
 // One tile: read this lane's fragments from the stage, then (once the reads
-// have returned) refill the stage with tile `t_next` (the sentinel `capacity`
-// when there is none, so that the refill is unconditional and the compiler's
-// wait counts stay exact), then compute.
+// have returned) refill the stage from `nx` (a row past its resources when there
+// is no next tile, so that the refill is unconditional and the compiler's wait
+// counts stay exact), then compute.  Tokens below a.t_lo are masked.
 template <int G, int NS, class KP, int NB>
 __device__ __forceinline__ void tile_step(WaveState<KP, NB>& w, uint8_t* st, int lane, int t0, int t_full,
-                                          const Limits<NB>& lim, int t_next, const MfmaDecodeArgs& a,
-                                          const typename KP::R& kr, const VRsrc& vr) {
+                                          const Limits<NB>& lim, const TileSrc<KP>& nx, const MfmaDecodeArgs& a) {
   const int q4 = lane >> 4, c = lane & 15;
   // This stage's tile has landed once at most the other NS - 1 stages' refills
   // are outstanding.  Waited for explicitly: the compiler's own wait for loads
@@ -363,7 +370,7 @@ __device__ __forceinline__ void tile_step(WaveState<KP, NB>& w, uint8_t* st, int
   }
   // the reads above must have returned before the stage is overwritten
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  issue_tile<KP>(st, lane, t_next, kr, vr);
+  issue_tile<KP>(st, lane, nx.t, nx.kr, nx.vr);
 
   // ---------------- logits: S^T = K Q^T for the two 16-token blocks
   f4_t sacc[NB][2];
@@ -374,7 +381,7 @@ __device__ __forceinline__ void tile_step(WaveState<KP, NB>& w, uint8_t* st, int
   for (int nb = 0; nb < NB; ++nb) {
     float sv[8];
     float tmax = -INFINITY;
-    if (t0 + 32 <= t_full) {  // a whole tile for every column: nothing to mask
+    if (t0 + 32 <= t_full && t0 >= a.t_lo) {  // a whole tile for every column: nothing to mask
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
@@ -388,7 +395,7 @@ __device__ __forceinline__ void tile_step(WaveState<KP, NB>& w, uint8_t* st, int
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int tok = t0 + 16 * blk + 4 * v + q4;
-          const float sx = tok < lim.v[nb] ? sacc[nb][blk][v] * a.scale_log2 : -INFINITY;
+          const float sx = tok < lim.v[nb] && tok >= a.t_lo ? sacc[nb][blk][v] * a.scale_log2 : -INFINITY;
           sv[4 * blk + v] = sx;
           tmax = fmaxf(tmax, sx);
         }
@@ -483,7 +490,10 @@ constexpr int kWavesPerEu = NB > 1 ? 2 : (std::is_same<KP, KeysQjl>::value && G 
 
 // NB blocks of G = 16 columns when NB > 1 (FP4 keys): the blocks share every
 // dequantised key and value operand; twice the accumulators cut the waves per SIMD.
-template <int G, class KP, int NB>
+// PAGED: the token rows live in pool pages named by the block table; each tile's
+// resources cover its page (tiles start on 32-token boundaries and pages, a power
+// of two of at least 32 tokens, hold whole tiles).
+template <int G, class KP, int NB, bool PAGED>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(kWavesPerEu<G, KP, NB>, kWavesPerEu<G, KP, NB>)))
 decode_mfma_kernel(MfmaDecodeArgs a) {
@@ -511,7 +521,8 @@ decode_mfma_kernel(MfmaDecodeArgs a) {
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const size_t bh = (size_t)b * a.H + h;
   const int L = min(min(a.seq_lens[b], a.max_len), a.cap);
-  const int t_begin = a.t_lo + split * a.per_split;
+  // tiles start on 32-token boundaries; tokens [t_lo & ~31, t_lo) are masked
+  const int t_begin = (a.t_lo & ~31) + split * a.per_split;
   const int t_end = min(max(a.t_lo, L - a.recent), t_begin + a.per_split);
   // this lane's column 16 nb + lane % 16 is query token j = (c0 + column) / gr,
   // which sees the first L - (nq - 1 - j) tokens; a tile below t_full is whole
@@ -531,34 +542,60 @@ decode_mfma_kernel(MfmaDecodeArgs a) {
     for (int nt = 0; nt < 8; ++nt) w.o[nb][nt] = f4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Buffer resources over this (sequence, KV head)'s rows: 32-bit offsets, and a
-  // read past the end of a resource returns zeros instead of faulting.
-  const typename KP::R kr = KP::resources(a, bh);
+  // Buffer resources over this (sequence, KV head)'s rows, or over one page's:
+  // 32-bit offsets, and a read past the end of a resource returns zeros instead
+  // of faulting (a missing tile reads past the end; a page outside the pool has
+  // empty resources).
+  const typename KP::R kr = KP::resources(a, bh * a.cap, a.cap);
   const VRsrc vr{rsrc(a.v_codes + bh * a.cap * 64, (size_t)a.cap * 64),
                  rsrc(a.v_scale + bh * a.cap * 8, (size_t)a.cap * 16)};
+  // table entry of tile t (-1: no tile), checked against the pool where it is used
+  auto page_for = [&](int t) { return PAGED && t < t_end ? page_entry_uniform(a.pm, b, t) : -1; };
+  // the loads of tile t, whose table entry the caller looked up
+  auto tile_at = [&](int t, int entry) {
+    TileSrc<KP> s;
+    if constexpr (!PAGED) {
+      s.kr = kr;
+      s.vr = vr;
+      s.t = t < t_end ? t : a.cap;
+    } else {
+      const int pg = page_checked(a.pm, entry);
+      const int nrows = pg < 0 ? 0 : a.pm.tokens;
+      const size_t row0 = ((size_t)(pg < 0 ? 0 : pg) * a.H + h) * a.pm.tokens;
+      s.kr = KP::resources(a, row0, nrows);
+      s.vr = VRsrc{rsrc(a.v_codes + row0 * 64, (size_t)nrows * 64), rsrc(a.v_scale + row0 * 8, (size_t)nrows * 16)};
+      s.t = pg < 0 ? 0 : t & (a.pm.tokens - 1);
+    }
+    return s;
+  };
+  auto tile_or_none = [&](int t) { return tile_at(t, page_for(t)); };
 
   uint8_t* sa = stA[wave];
   uint8_t* sb = stB[wave];
-  const int none = a.cap;  // an offset past every resource: reads zeros, no memory traffic
-  auto tile_or_none = [&](int t) { return t < t_end ? t : none; };
   int t0 = t_begin + wave * 32;
-  issue_tile<KP>(sa, lane, tile_or_none(t0), kr, vr);
-  issue_tile<KP>(sb, lane, tile_or_none(t0 + 128), kr, vr);
+  {
+    const TileSrc<KP> s0 = tile_or_none(t0), s1 = tile_or_none(t0 + 128);
+    issue_tile<KP>(sa, lane, s0.t, s0.kr, s0.vr);
+    issue_tile<KP>(sb, lane, s1.t, s1.kr, s1.vr);
+  }
   if constexpr (NS == 2) {
     for (; t0 < t_end; t0 += 256) {
       // the second tile of a pair may lie past t_end: all its tokens are masked
-      tile_step<G, NS, KP, NB>(w, sa, lane, t0, t_full, lim, tile_or_none(t0 + 256), a, kr, vr);
-      tile_step<G, NS, KP, NB>(w, sb, lane, t0 + 128, t_full, lim, tile_or_none(t0 + 384), a, kr, vr);
+      tile_step<G, NS, KP, NB>(w, sa, lane, t0, t_full, lim, tile_or_none(t0 + 256), a);
+      tile_step<G, NS, KP, NB>(w, sb, lane, t0 + 128, t_full, lim, tile_or_none(t0 + 384), a);
     }
   } else {
     uint8_t* sc = stC + wave * kStage;
-    issue_tile<KP>(sc, lane, tile_or_none(t0 + 256), kr, vr);
+    {
+      const TileSrc<KP> s2 = tile_or_none(t0 + 256);
+      issue_tile<KP>(sc, lane, s2.t, s2.kr, s2.vr);
+    }
     while (t0 < t_end) {
-      tile_step<G, NS, KP, NB>(w, sa, lane, t0, t_full, lim, tile_or_none(t0 + 384), a, kr, vr);
+      tile_step<G, NS, KP, NB>(w, sa, lane, t0, t_full, lim, tile_or_none(t0 + 384), a);
       if (t0 + 128 >= t_end) break;
-      tile_step<G, NS, KP, NB>(w, sb, lane, t0 + 128, t_full, lim, tile_or_none(t0 + 512), a, kr, vr);
+      tile_step<G, NS, KP, NB>(w, sb, lane, t0 + 128, t_full, lim, tile_or_none(t0 + 512), a);
       if (t0 + 256 >= t_end) break;
-      tile_step<G, NS, KP, NB>(w, sc, lane, t0 + 256, t_full, lim, tile_or_none(t0 + 640), a, kr, vr);
+      tile_step<G, NS, KP, NB>(w, sc, lane, t0 + 256, t_full, lim, tile_or_none(t0 + 640), a);
       t0 += 384;
     }
   }
@@ -616,18 +653,18 @@ decode_mfma_kernel(MfmaDecodeArgs a) {
   }
 }
 
-template <class KP>
+template <class KP, bool PAGED>
 int launch_g(const MfmaDecodeArgs& a, int B, int G, hipStream_t st) {
   dim3 grid(a.splits, a.H, B);
   switch (G) {
-    case 1: decode_mfma_kernel<1, KP, 1><<<grid, 256, 0, st>>>(a); break;
-    case 2: decode_mfma_kernel<2, KP, 1><<<grid, 256, 0, st>>>(a); break;
-    case 4: decode_mfma_kernel<4, KP, 1><<<grid, 256, 0, st>>>(a); break;
-    case 8: decode_mfma_kernel<8, KP, 1><<<grid, 256, 0, st>>>(a); break;
-    case 16: decode_mfma_kernel<16, KP, 1><<<grid, 256, 0, st>>>(a); break;
+    case 1: decode_mfma_kernel<1, KP, 1, PAGED><<<grid, 256, 0, st>>>(a); break;
+    case 2: decode_mfma_kernel<2, KP, 1, PAGED><<<grid, 256, 0, st>>>(a); break;
+    case 4: decode_mfma_kernel<4, KP, 1, PAGED><<<grid, 256, 0, st>>>(a); break;
+    case 8: decode_mfma_kernel<8, KP, 1, PAGED><<<grid, 256, 0, st>>>(a); break;
+    case 16: decode_mfma_kernel<16, KP, 1, PAGED><<<grid, 256, 0, st>>>(a); break;
     case 32:
       if constexpr (std::is_same<KP, KeysFp4>::value) {
-        decode_mfma_kernel<16, KP, 2><<<grid, 256, 0, st>>>(a);
+        decode_mfma_kernel<16, KP, 2, PAGED><<<grid, 256, 0, st>>>(a);
         break;
       }
       return KV_EUNSUPPORTED;
@@ -639,8 +676,10 @@ int launch_g(const MfmaDecodeArgs& a, int B, int G, hipStream_t st) {
 }  // namespace
 
 int launch_decode_mfma(const MfmaDecodeArgs& a, int format, int B, int G, hipStream_t st) {
-  if (format == KV_FMT_FP4) return launch_g<KeysFp4>(a, B, G, st);
-  if (format == KV_FMT_QJL1_FP4V) return launch_g<KeysQjl>(a, B, G, st);
+  const bool paged = a.pm.table != nullptr;
+  if (format == KV_FMT_FP4) return paged ? launch_g<KeysFp4, true>(a, B, G, st) : launch_g<KeysFp4, false>(a, B, G, st);
+  if (format == KV_FMT_QJL1_FP4V)
+    return paged ? launch_g<KeysQjl, true>(a, B, G, st) : launch_g<KeysQjl, false>(a, B, G, st);
   return KV_EUNSUPPORTED;
 }
 

@@ -90,6 +90,13 @@ struct Res {
   int n_end;  // a byte offset past every norm resource
 };
 
+// The next tile's loads: resources over its page's token rows (a contiguous
+// cache: the (sequence, KV head)'s rows) and its first row in them.
+struct TileSrc {
+  Res r;
+  int t;
+};
+
 constexpr int kDmaPerTile = 6;  // direct-to-LDS loads issue_tile makes
 
 __device__ __forceinline__ void issue_tile(uint8_t* st, int lane, int t0, const Res& r) {
@@ -140,8 +147,8 @@ struct WaveState {
 
 // One 32-token tile (see tile_step of the FP4 kernel for the ring protocol).
 template <int G>
-__device__ __forceinline__ void tile_step(WaveState<G>& w, uint8_t* st, int lane, int t0, int t_end, int t_next,
-                                          const TurboDecodeArgs& a, const Consts& k, const Res& res) {
+__device__ __forceinline__ void tile_step(WaveState<G>& w, uint8_t* st, int lane, int t0, int t_end,
+                                          const TileSrc& nx, const TurboDecodeArgs& a, const Consts& k) {
   const int q4 = lane >> 4, c = lane & 15;
   // This stage's tile has landed once at most the other stage's refill (the
   // kDmaPerTile loads issued after it) is outstanding.  Waited for explicitly:
@@ -173,7 +180,7 @@ __device__ __forceinline__ void tile_step(WaveState<G>& w, uint8_t* st, int lane
   const i2_t vx1 = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
       (__attribute__((address_space(3))) i2_t*)(st + kSV + vo + 16));
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the stage may be refilled
-  issue_tile(st, lane, t_next, res);
+  issue_tile(st, lane, nx.t, nx.r);
 
   // ---- logits: S^T = K Q^T, code-bit steps then sketch steps, per 16-token block
   f4_t lm[2], qj[2];
@@ -260,7 +267,8 @@ __device__ __forceinline__ void tile_step(WaveState<G>& w, uint8_t* st, int lane
 #define KVQ_TURBO_WAVES_PER_EU 3  // waves per SIMD the register budget is cut for
 #endif
 
-template <int G>
+// PAGED: token rows in pool pages named by the block table, resources per tile.
+template <int G, bool PAGED>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(KVQ_TURBO_WAVES_PER_EU, KVQ_TURBO_WAVES_PER_EU))) decode_turbo_kernel(TurboDecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t stA[4][kStage];
@@ -329,23 +337,38 @@ __attribute__((amdgpu_waves_per_eu(KVQ_TURBO_WAVES_PER_EU, KVQ_TURBO_WAVES_PER_E
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) w.o[nt] = f4_t{0.f, 0.f, 0.f, 0.f};
 
-  const Res res{rsrc(a.k_codes + bh * a.cap * 32, (size_t)a.cap * 32),
-                rsrc(a.k_sketch + bh * a.cap * 16, (size_t)a.cap * 16),
-                rsrc(a.k_norm + bh * a.cap, (size_t)a.cap * 2),
-                rsrc(a.k_rnorm + bh * a.cap, (size_t)a.cap * 2),
-                rsrc(a.v_codes + bh * a.cap * 32, (size_t)a.cap * 32),
-                rsrc(a.v_norm + bh * a.cap, (size_t)a.cap * 2),
-                a.cap * 32};
+  // resources over nrows token rows from row0 (nrows 0: every read is zeros)
+  auto res_at = [&](size_t row0, int nrows) {
+    return Res{rsrc(a.k_codes + row0 * 32, (size_t)nrows * 32), rsrc(a.k_sketch + row0 * 16, (size_t)nrows * 16),
+               rsrc(a.k_norm + row0, (size_t)nrows * 2),        rsrc(a.k_rnorm + row0, (size_t)nrows * 2),
+               rsrc(a.v_codes + row0 * 32, (size_t)nrows * 32), rsrc(a.v_norm + row0, (size_t)nrows * 2),
+               nrows * 32};
+  };
+  const Res res = res_at(bh * a.cap, a.cap);
   uint8_t* sa = stA[wave];
   uint8_t* sb = stB[wave];
-  const int none = a.cap;
-  auto tile_or_none = [&](int t) { return t < t_end ? t : none; };
+  // a missing tile reads past the end of its resources: zeros, no memory traffic
+  auto tile_or_none = [&](int t) {
+    TileSrc s;
+    if constexpr (!PAGED) {
+      s.r = res;
+      s.t = t < t_end ? t : a.cap;
+    } else {
+      const int pg = t < t_end ? page_of_uniform(a.pm, b, t) : -1;
+      s.r = res_at(((size_t)(pg < 0 ? 0 : pg) * a.H + h) * a.pm.tokens, pg < 0 ? 0 : a.pm.tokens);
+      s.t = pg < 0 ? 0 : t & (a.pm.tokens - 1);
+    }
+    return s;
+  };
   int t0 = t_begin + wave * 32;
-  issue_tile(sa, lane, tile_or_none(t0), res);
-  issue_tile(sb, lane, tile_or_none(t0 + 128), res);
+  {
+    const TileSrc s0 = tile_or_none(t0), s1 = tile_or_none(t0 + 128);
+    issue_tile(sa, lane, s0.t, s0.r);
+    issue_tile(sb, lane, s1.t, s1.r);
+  }
   for (; t0 < t_end; t0 += 256) {
-    tile_step<G>(w, sa, lane, t0, t_end, tile_or_none(t0 + 256), a, k, res);
-    tile_step<G>(w, sb, lane, t0 + 128, t_end, tile_or_none(t0 + 384), a, k, res);
+    tile_step<G>(w, sa, lane, t0, t_end, tile_or_none(t0 + 256), a, k);
+    tile_step<G>(w, sb, lane, t0 + 128, t_end, tile_or_none(t0 + 384), a, k);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
@@ -399,16 +422,23 @@ __attribute__((amdgpu_waves_per_eu(KVQ_TURBO_WAVES_PER_EU, KVQ_TURBO_WAVES_PER_E
 
 }  // namespace
 
-int launch_decode_turbo(const TurboDecodeArgs& a, int B, int G, hipStream_t st) {
+namespace {
+template <bool PAGED>
+int launch_turbo(const TurboDecodeArgs& a, int B, int G, hipStream_t st) {
   dim3 grid(a.splits, a.H, B);
   switch (G) {
-    case 1: decode_turbo_kernel<1><<<grid, 256, 0, st>>>(a); break;
-    case 2: decode_turbo_kernel<2><<<grid, 256, 0, st>>>(a); break;
-    case 4: decode_turbo_kernel<4><<<grid, 256, 0, st>>>(a); break;
-    case 8: decode_turbo_kernel<8><<<grid, 256, 0, st>>>(a); break;
+    case 1: decode_turbo_kernel<1, PAGED><<<grid, 256, 0, st>>>(a); break;
+    case 2: decode_turbo_kernel<2, PAGED><<<grid, 256, 0, st>>>(a); break;
+    case 4: decode_turbo_kernel<4, PAGED><<<grid, 256, 0, st>>>(a); break;
+    case 8: decode_turbo_kernel<8, PAGED><<<grid, 256, 0, st>>>(a); break;
     default: return KV_EUNSUPPORTED;
   }
   return KV_OK;
+}
+}  // namespace
+
+int launch_decode_turbo(const TurboDecodeArgs& a, int B, int G, hipStream_t st) {
+  return a.pm.table ? launch_turbo<true>(a, B, G, st) : launch_turbo<false>(a, B, G, st);
 }
 
 }  // namespace kvq

@@ -4,7 +4,49 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kvq_internal.h"
+
 namespace kvq {
+
+// ---------------------------------------------------------------- token rows
+
+constexpr size_t kNoRow = ~size_t(0);
+
+// Pool page of sequence b's position t, or -1 when its table entry names no
+// page of the pool (such a page is never read or written).
+__device__ __forceinline__ int page_of(const PageMap& m, int b, int t) {
+  if (!m.table) return b;
+  const int p = m.table[(size_t)b * m.per_seq + (t >> m.shift)];
+  return (unsigned)p < (unsigned)m.num_pages ? p : -1;
+}
+
+// page_of for a wave-uniform (b, t) of a paged map, read through the scalar
+// cache (the table is read-only in every kernel, so it may be read as constant
+// memory): waiting for it does not wait for the wave's vector loads in flight,
+// which the decode kernels keep across the lookup of their next tile.
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+// The raw entry (not yet checked against the pool, so that the read can stay in
+// flight until the page is used) ...
+__device__ __forceinline__ int page_entry_uniform(const PageMap& m, int b, int t) {
+  const int32_t* p = m.table + (size_t)b * m.per_seq + (t >> m.shift);
+  return *reinterpret_cast<const_i32*>(reinterpret_cast<uintptr_t>(p));
+}
+// ... and the checked page, or -1.
+__device__ __forceinline__ int page_checked(const PageMap& m, int entry) {
+  return (unsigned)entry < (unsigned)m.num_pages ? entry : -1;
+}
+__device__ __forceinline__ int page_of_uniform(const PageMap& m, int b, int t) {
+  return page_checked(m, page_entry_uniform(m, b, t));
+}
+
+// Token row of (sequence b, head h of H, position t) in a per-token buffer, or
+// kNoRow.  KIVI key metadata rows are token row / 32 (pages hold whole groups).
+__device__ __forceinline__ size_t token_row(const PageMap& m, int H, int b, int h, int t) {
+  if (!m.table) return ((size_t)b * H + h) * m.tokens + t;
+  const int p = page_of(m, b, t);
+  if (p < 0) return kNoRow;
+  return ((size_t)p * H + h) * m.tokens + (t & (m.tokens - 1));
+}
 
 // ---------------------------------------------------------------- 16-bit floats
 

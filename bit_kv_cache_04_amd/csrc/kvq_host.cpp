@@ -17,6 +17,12 @@ int check_layout(const kv_layout* L) {
       L->rope_dim < 0 || L->group < 0 || L->qjl_m < 0 || L->lm_bits < 0 || L->sink_tokens < 0 ||
       L->recent_tokens < 0 || L->sink_tokens > L->capacity || L->recent_tokens > L->capacity)
     return KV_EINVAL;
+  // paged storage: whole KIVI groups and decode tiles per page
+  if (L->page_tokens < 0 || L->num_pages < 0) return KV_EINVAL;
+  if (L->page_tokens == 0 && L->num_pages != 0) return KV_EINVAL;
+  if (L->page_tokens > 0 && (L->page_tokens < 32 || (L->page_tokens & (L->page_tokens - 1)) ||
+                             L->capacity % L->page_tokens || L->num_pages < 1))
+    return KV_EINVAL;
   // bf16 sink / recent windows: caches whose values are FP4 (outputs in the original basis)
   if ((L->sink_tokens || L->recent_tokens) && L->format != KV_FMT_FP4 && L->format != KV_FMT_QJL1_FP4V)
     return KV_EUNSUPPORTED;
@@ -58,6 +64,7 @@ int check_cache(const kv_cache* c) {
   int f = c->layout.format;
   if (f == KV_FMT_TURBO && (!c->rot || !c->proj || !c->lm_levels || !c->lm_thresh)) return KV_EINVAL;
   if (f == KV_FMT_QJL1_FP4V && !c->proj) return KV_EINVAL;
+  if (c->layout.page_tokens > 0 && !c->block_table) return KV_EINVAL;
   // the append kernels stage R and S with 16-byte loads
   if ((reinterpret_cast<uintptr_t>(c->rot) | reinterpret_cast<uintptr_t>(c->proj)) & 15) return KV_EINVAL;
   return KV_OK;
@@ -155,7 +162,8 @@ using namespace kvq;
 extern "C" size_t kv_buffer_bytes(const kv_layout* L, int32_t which) {
   if (check_layout(L) != KV_OK || which < 0 || which >= KV_BUF_COUNT) return 0;
   const size_t B = L->batch, H = L->num_kv_heads, T = L->capacity, d = L->head_dim;
-  const size_t bht = B * H * T;
+  // per-token buffers: B x H x capacity rows, or the pool's pages x H x page_tokens
+  const size_t bht = L->page_tokens > 0 ? (size_t)L->num_pages * H * L->page_tokens : B * H * T;
   if (which == KV_BUF_SINK_K || which == KV_BUF_SINK_V) return B * H * (size_t)L->sink_tokens * d * 2;
   if (which == KV_BUF_RECENT_K || which == KV_BUF_RECENT_V) return B * H * (size_t)L->recent_tokens * d * 2;
   if (which == KV_BUF_K_STAGE) return L->format == KV_FMT_KIVI2 ? B * H * (4 + (size_t)kKiviGroup * d) * 4 : 0;
@@ -163,7 +171,7 @@ extern "C" size_t kv_buffer_bytes(const kv_layout* L, int32_t which) {
     case KV_FMT_KIVI2:
       switch (which) {
         case KV_BUF_K_CODES: case KV_BUF_V_CODES: return bht * d / 4;
-        case KV_BUF_K_SCALE: case KV_BUF_K_ZERO: return B * H * (T / kKiviGroup) * d * 4;
+        case KV_BUF_K_SCALE: case KV_BUF_K_ZERO: return bht / kKiviGroup * d * 4;
         case KV_BUF_V_SCALE: case KV_BUF_V_ZERO: return bht * (d / kKiviGroup) * 4;
         default: return 0;
       }
@@ -208,8 +216,10 @@ extern "C" size_t kv_bytes_per_token(const kv_layout* L, int32_t num_layers) {
   }
   if (check_layout(L) != KV_OK) return 0;
   // Sum the per-token share of every buffer: each buffer holds B*H*capacity
-  // token slots (B*capacity for the latent), so divide by that.
-  size_t slots = (size_t)L->batch * L->num_kv_heads * L->capacity;
+  // token slots (B*capacity for the latent; a paged pool num_pages*H*page_tokens),
+  // so divide by that.
+  size_t slots = L->page_tokens > 0 ? (size_t)L->num_pages * L->num_kv_heads * L->page_tokens
+                                    : (size_t)L->batch * L->num_kv_heads * L->capacity;
   size_t total = 0;
   for (int b = 0; b < KV_BUF_COUNT; ++b)
     if (b < KV_BUF_SINK_K) total += kv_buffer_bytes(L, b);  // not the per-sequence windows and staging

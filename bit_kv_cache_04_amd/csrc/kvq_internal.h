@@ -13,6 +13,26 @@ constexpr int kKiviGroup = 32;
 constexpr int kQjlM = 128;
 constexpr int kLmBits = 2;
 
+// Where the token rows of a cache live.  Paged storage: sequence b's position t
+// is slot t % tokens of pool page table[b * per_seq + t / tokens].  A contiguous
+// cache reads as one page of `capacity` tokens per sequence, page b (table NULL).
+struct PageMap {
+  const int32_t* table;  // device [B][per_seq], or nullptr
+  int tokens;            // tokens per page (contiguous: capacity)
+  int per_seq;           // table entries per sequence
+  int num_pages;         // pages in the pool (contiguous: batch)
+  int shift;             // paged: log2(tokens) (pages are a power of two)
+};
+inline PageMap page_map(const kv_cache* c) {
+  const kv_layout& L = c->layout;
+  if (L.page_tokens > 0) {
+    int shift = 0;
+    while ((1 << shift) < L.page_tokens) ++shift;
+    return PageMap{c->block_table, L.page_tokens, L.capacity / L.page_tokens, L.num_pages, shift};
+  }
+  return PageMap{nullptr, L.capacity, 1, L.batch, 0};
+}
+
 // KV_OK if the layout is one this library supports, else the status to return.
 int check_layout(const kv_layout* L);
 // KV_OK if every buffer and constant the format needs is non-NULL.

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "kvq.h"
+#include "kvq_internal.h"
 
 namespace kvq {
 
@@ -18,6 +19,7 @@ struct MfmaDecodeArgs {
   const uint8_t* v_codes;   // [B][H][cap][64]
   const uint16_t* v_scale;  // [B][H][cap][8] bf16
   const uint16_t* rope;     // latent: [B][cap][64] bf16 (k_codes [B][cap][256], k_scale [B][cap][32])
+  PageMap pm;               // token rows: [B][H][cap] above, or a paged pool
   const void* q;            // FP4: bf16 [B][Hq][128]; QJL: fp32 S q [B][Hq][128]
   const uint8_t* qpieces;   // QJL: [B][Hq][kQjlPieceBytes], FP8 pieces of S q
   const int32_t* seq_lens;
@@ -46,6 +48,7 @@ struct TurboDecodeArgs {
   const uint16_t* k_rnorm;  // [B][H][cap] fp16
   const uint8_t* v_codes;   // [B][H][cap][32]
   const uint16_t* v_norm;   // [B][H][cap] fp16
+  PageMap pm;               // token rows: [B][H][cap] above, or a paged pool
   const float* levels;      // 4 codebook levels, ascending, symmetric
   const float* q;           // [B][Hq][256]
   const uint8_t* qpieces;   // [B][Hq][kTurboPieceBytes]: FP6 pieces of the key-product operands

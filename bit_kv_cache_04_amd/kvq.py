@@ -36,13 +36,15 @@ class KVLayout(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int32), ("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("rope_dim", ctypes.c_int32), ("capacity", ctypes.c_int32),
                 ("group", ctypes.c_int32), ("qjl_m", ctypes.c_int32), ("lm_bits", ctypes.c_int32),
-                ("sink_tokens", ctypes.c_int32), ("recent_tokens", ctypes.c_int32)]
+                ("sink_tokens", ctypes.c_int32), ("recent_tokens", ctypes.c_int32),
+                ("page_tokens", ctypes.c_int32), ("num_pages", ctypes.c_int32)]
 
 
 class KVCache(ctypes.Structure):
     _fields_ = [("layout", KVLayout), ("buf", ctypes.c_void_p * len(BUFFERS)),
                 ("rot", ctypes.c_void_p), ("proj", ctypes.c_void_p),
-                ("lm_levels", ctypes.c_void_p), ("lm_thresh", ctypes.c_void_p)]
+                ("lm_levels", ctypes.c_void_p), ("lm_thresh", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p)]
 
 
 class KVDecodeOpts(ctypes.Structure):
@@ -88,14 +90,17 @@ def lib():
     return _lib
 
 
-def make_layout(fmt, batch, num_kv_heads, head_dim, capacity, rope_dim=0, sink=0, recent=0):
+def make_layout(fmt, batch, num_kv_heads, head_dim, capacity, rope_dim=0, sink=0, recent=0, page_tokens=0,
+                num_pages=0):
     """A kv_layout with the format's fixed group / sketch / codebook parameters
-    (sink / recent: tokens kept bf16 at the start and end of each sequence)."""
+    (sink / recent: tokens kept bf16 at the start and end of each sequence;
+    page_tokens / num_pages: paged storage in a pool of pages)."""
     f = FMT[fmt] if isinstance(fmt, str) else int(fmt)
     group = {1: 32, 2: 16, 4: 16, 5: 16}.get(f, 0)
     qjl_m = 128 if f in (3, 4) else 0
     lm_bits = 2 if f == 3 else 0
-    return KVLayout(f, batch, num_kv_heads, head_dim, rope_dim, capacity, group, qjl_m, lm_bits, sink, recent)
+    return KVLayout(f, batch, num_kv_heads, head_dim, rope_dim, capacity, group, qjl_m, lm_bits, sink, recent,
+                    page_tokens, num_pages)
 
 
 def _check(fn, st):

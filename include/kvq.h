@@ -95,7 +95,21 @@ enum kv_status {
  * history is compressed).  A window token's logit is <q, bf16 key>.  The recent
  * window is a ring of the last recent_tokens tokens appended to a sequence
  * (slot t mod recent_tokens), so decode must see each sequence at the length
- * it was appended to.  0 and 0 turn it off. */
+ * it was appended to.  0 and 0 turn it off.
+ *
+ * Paged storage (page_tokens > 0, any format): the per-token buffers hold a
+ * pool of num_pages pages instead of B x capacity slots; page p holds
+ * page_tokens consecutive positions of one sequence for all H heads, token
+ * slot s of head h at row ((p*H + h)*page_tokens + s) (KIVI2 key scale / zero:
+ * row ((p*H + h)*(page_tokens/32) + s/32)).  kv_cache.block_table maps each
+ * sequence's logical page j (positions [j*page_tokens, (j+1)*page_tokens)) to
+ * a pool page, so sequences grow a page at a time and whole pages return to
+ * the pool (page "TurboQuant vs OSCAR vs EpiCache", OSCAR's deployment list:
+ * kernels that work with paged attention; page "How TriAttention cut LLM
+ * memory use 10x", paged memory fragmentation: paged allocators reclaim whole
+ * blocks).  page_tokens is a power of two, at least 32, that divides
+ * capacity; num_pages >= 1.  Windows and K_STAGE stay per sequence.  page_tokens 0 (and num_pages
+ * 0) is the contiguous layout. */
 typedef struct kv_layout {
   int32_t format;       /* enum kv_format */
   int32_t batch;        /* sequences B */
@@ -108,9 +122,14 @@ typedef struct kv_layout {
   int32_t lm_bits;      /* Lloyd-Max bits (TURBO) */
   int32_t sink_tokens;   /* leading tokens kept bf16 (mixed precision), else 0 */
   int32_t recent_tokens; /* trailing tokens kept bf16 (mixed precision), else 0 */
+  int32_t page_tokens;   /* paged storage: tokens per page, else 0 */
+  int32_t num_pages;     /* paged storage: pages in the pool, else 0 */
 } kv_layout;
 
-/* Buffers of a cache, by role.  Element types and shapes (Tc = capacity):
+/* Buffers of a cache, by role.  Element types and shapes (Tc = capacity; with
+ * paged storage every [B][H][Tc] reads [num_pages][H][page_tokens], [B][Tc]
+ * reads [num_pages][page_tokens] and KIVI2's [B][H][Tc/32] reads
+ * [num_pages][H][page_tokens/32]):
  *   K_CODES  u8   KIVI2 [B][H][Tc][d/4]; FP4 [B][H][Tc][d/2]; TURBO [B][H][Tc][d/4];
  *                 LATENT [B][Tc][d/2]
  *   K_SCALE  KIVI2 f32 [B][H][Tc/32][d]; FP4 bf16 [B][H][Tc][d/16]; LATENT bf16 [B][Tc][d/16]
@@ -154,6 +173,14 @@ typedef struct kv_cache {
   const float* proj;
   const float* lm_levels;
   const float* lm_thresh;
+  /* paged storage: device int32 [B][capacity / page_tokens], row-major, the
+   * pool page of each sequence's logical page (caller-owned; read by the
+   * kernels when they run).  Entries a call touches must lie in [0, num_pages)
+   * and no two sequences may append into one page at once.  An entry outside
+   * the pool is never followed: appends to it are dropped and decode reads it
+   * as zero bytes (that sequence's output is then unspecified).  NULL for the
+   * contiguous layout; NULL with page_tokens > 0 is KV_EINVAL. */
+  const int32_t* block_table;
 } kv_cache;
 
 /* Options for kv_decode_attention; pass NULL for defaults.

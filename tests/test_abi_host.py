@@ -231,3 +231,30 @@ def test_ragged_append_validation():
     assert kvq.kv_buffer_bytes(lay, kvq.BUFFERS.index("k_stage")) == 2 * 2 * (4 + 32 * 64) * 4
     assert kvq.kv_buffer_bytes(kvq.make_layout("fp4", 2, 2, 64, 64), kvq.BUFFERS.index("k_stage")) == 0
     assert _append_ragged(_cache("fp4", d=96), [0, 0]) == EUNSUP
+
+
+def test_paged_layout_validation_and_sizes():
+    ok = kvq.make_layout("fp4", 4, 2, 128, 1024, page_tokens=64, num_pages=70)
+    assert kvq.kv_buffer_bytes(ok, 0) == 70 * 2 * 64 * 64          # K_CODES: pages x H x P x d/2
+    assert kvq.kv_buffer_bytes(ok, 1) == 70 * 2 * 64 * 8 * 2       # K_SCALE bf16 per 16 channels
+    contiguous = kvq.make_layout("fp4", 4, 2, 128, 1024)
+    assert kvq.kv_bytes_per_token(ok, 1) == kvq.kv_bytes_per_token(contiguous, 1)
+    kl = kvq.make_layout("kivi2", 2, 2, 64, 256, page_tokens=64, num_pages=9)
+    assert kvq.kv_buffer_bytes(kl, 1) == 9 * 2 * 2 * 64 * 4       # K_SCALE: P/32 rows a page
+    assert kvq.kv_buffer_bytes(kl, 15) == 2 * 2 * (4 + 32 * 64) * 4  # K_STAGE stays per sequence
+    ll = kvq.make_layout("latent", 3, 1, 512, 128, 64, page_tokens=32, num_pages=5)
+    assert kvq.kv_buffer_bytes(ll, 0) == 5 * 32 * 256 and kvq.kv_buffer_bytes(ll, 10) == 5 * 32 * 64 * 2
+    wl = kvq.make_layout("fp4", 4, 2, 128, 1024, sink=40, recent=100, page_tokens=64, num_pages=70)
+    assert kvq.kv_buffer_bytes(wl, 11) == 4 * 2 * 40 * 128 * 2    # SINK_K per sequence
+    for P, n in ((48, 10), (64, 0), (0, 5), (-32, 4), (96, 10), (64, -1), (16, 80), (192, 10)):
+        bad = kvq.make_layout("fp4", 4, 2, 128, 1024, page_tokens=P, num_pages=n)
+        assert kvq.kv_buffer_bytes(bad, 0) == 0, (P, n)
+    # a paged cache needs its block table; calls fail before any launch
+    lay = kvq.make_layout("fp4", 2, 2, 128, 128, page_tokens=64, num_pages=4)
+    bufs = (ctypes.c_void_p * len(kvq.BUFFERS))(
+        *[(FAKE if kvq.kv_buffer_bytes(lay, i) else None) for i in range(len(kvq.BUFFERS))])
+    c = kvq.KVCache(lay, bufs, None, None, None, None, None)
+    assert _append(c) == EINVAL
+    assert _decode(c, hq=4, maxlen=128, ws=FAKE, wsb=1 << 30)[0] == EINVAL
+    c.block_table = FAKE
+    assert _append(c, start=100, n=29) == ECAP                      # capacity stays per sequence
