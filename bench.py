@@ -26,6 +26,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+FP32_VALU_PEAK_TFLOPS = 157.3  # fp32 vector peak (256 CUs, 2.4 GHz)
 HBM_PEAK_GBS = 8000.0
 
 
@@ -150,6 +151,9 @@ def main():
     ap.add_argument("--page-tokens", type=int, default=0,
                     help="paged storage: tokens per page, the pool's pages assigned to sequences in a seeded "
                          "shuffled order")
+    ap.add_argument("--hsi", action="store_true",
+                    help="hierarchical sparse indexing: candidate pool (top 2048 blocks of 8 by synthetic full-mode "
+                         "scores), reindex top 512 (synthetic pool scores), decode over the selected positions")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph replay")
     args = ap.parse_args()
@@ -218,8 +222,33 @@ def main():
         a.record()
         b.record()
 
+    if args.hsi:
+        from bit_kv_cache_04_amd.cache import hsi_candidates, hsi_select
+        if nq != 1 or args.sink or args.recent:
+            raise SystemExit("bench.py: --hsi takes one query per sequence and no bf16 windows")
+        HSI_BLOCK, HSI_TOP_BLOCKS, HSI_TOP_K = 8, 2048, 512
+        pool_cap = HSI_BLOCK * HSI_TOP_BLOCKS
+        full_scores = synth.make_indexer_scores(cfg.seed, cfg.batch, T, device=dev)
+        pool_scores = synth.make_indexer_scores(cfg.seed, cfg.batch, pool_cap, layer=1, device=dev)
+        pool_out = (torch.empty(cfg.batch, pool_cap, dtype=torch.int32, device=dev),
+                    torch.empty(cfg.batch, dtype=torch.int32, device=dev))
+        sel_out = (torch.empty(cfg.batch, HSI_TOP_K, dtype=torch.int32, device=dev),
+                   torch.empty(cfg.batch, dtype=torch.int32, device=dev))
+        hsi_ws = torch.empty(kvq.kv_hsi_candidates(None, cfg.batch, T, None, HSI_BLOCK, HSI_TOP_BLOCKS, None, None,
+                                                   None, 0), dtype=torch.uint8, device=dev)
+        sp_ws = torch.zeros(kvq.kv_decode_attention_sparse(cache.struct, None, kvq.DT_BF16, cfg.hq, None, None,
+                                                           HSI_TOP_K, 1.0, None, None, 0,
+                                                           kvq.KVDecodeOpts(args.splits, None, None, 1)),
+                            dtype=torch.uint8, device=dev)
+
     def step(i=None):
         cache.append(k_new, v_new, T - n_new)
+        if args.hsi:
+            pool, pool_n = hsi_candidates(full_scores, lens, HSI_BLOCK, HSI_TOP_BLOCKS, out=pool_out, ws=hsi_ws)
+            sel, sel_n = hsi_select(pool_scores, pool, pool_n, HSI_TOP_K, out=sel_out)
+            cache.decode_sparse(q, sel, sel_n, scale, splits=args.splits, out=out, ws=sp_ws,
+                                events=None if i is None else ev[i])
+            return
         cache.decode(q, lens, scale, splits=args.splits, out=out, ws=ws,
                      events=None if i is None else ev[i])
 
@@ -272,6 +301,11 @@ def main():
         wall = time.perf_counter() - w0
         ms_step = s0.elapsed_time(s1) / args.steps
     nbytes = counted_bytes(cfg, cache.layout, kvq, args.sink, args.recent)
+    if args.hsi:
+        # the step reads the full-mode scores, the pool's scores and the packed
+        # bytes of the selected positions
+        n_sel = int(sel_out[1].sum())
+        nbytes = 4 * cfg.batch * (T + pool_cap) + kvq.kv_bytes_per_token(cache.layout, 1) * n_sel
     gbs = nbytes / (ms_step * 1e-3) / 1e9
     achieved = nbytes / (dec_ms * 1e-3) / 1e9
     res = {
@@ -301,6 +335,20 @@ def main():
         "ms_per_step_eager": round(ms_eager, 5),
         "roofline": roofline(cfg, nbytes, dec_ms, nq, bool(args.sink or args.recent), bool(args.page_tokens)),
     }
+    if args.hsi:
+        # the dominant kernel is the sparse decode on the general (fp32 vector) kernel:
+        # per selected position and query head, key_width + head_dim multiply-adds
+        # (the latent cache's gather kernel runs them on the fp16 matrix cores)
+        flops = 2.0 * cfg.hq * n_sel * (cfg.key_width + cfg.head_dim)
+        ach = flops / (dec_ms * 1e-3) / 1e12
+        mfma = cfg.fmt == "latent"
+        peak = MFMA_F16_PEAK_TFLOPS if mfma else FP32_VALU_PEAK_TFLOPS
+        res["metric"] = "HSI sparse decode step: bytes read GB/s + query-tokens/s at fixed context"
+        res["config"].update(hsi={"block": HSI_BLOCK, "top_blocks": HSI_TOP_BLOCKS, "top_k": HSI_TOP_K,
+                                  "selected_positions": n_sel})
+        res["roofline"] = {"bound": "mfma" if mfma else "alu", "achieved": round(ach, 2), "peak": peak,
+                           "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+                           "kernel": "sparse split-context attention", "kernel_us": round(dec_ms * 1e3, 2)}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, rotation=args.rotation if cfg.fmt == "turbo" else "haar")
     print(json.dumps(res), flush=True)

@@ -82,6 +82,34 @@ def make_constants(fmt, head_dim, rot_gauss=None, proj_gauss=None, rotation="haa
     return out
 
 
+def hsi_candidates(scores, seq_lens, block=8, top_blocks=2048, out=None, ws=None):
+    """HSI full mode through libkvq: scores fp32 [B, S] and seq_lens int32 [B] on
+    the device; returns (pool int32 [B, top_blocks * block], pool_n int32 [B])."""
+    B, S = scores.shape
+    dev = scores.device
+    need = kvq.kv_hsi_candidates(None, B, S, None, block, top_blocks, None, None, None, 0)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+    pool, pool_n = out if out is not None else (
+        torch.empty(B, top_blocks * block, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev))
+    kvq.kv_hsi_candidates(_ptr(scores), B, S, _ptr(seq_lens), block, top_blocks, _ptr(pool), _ptr(pool_n), _ptr(ws),
+                          ws.numel(), _stream_ptr(dev))
+    return pool, pool_n
+
+
+def hsi_select(pool_scores, pool, pool_n, top_k=512, out=None):
+    """HSI reindex mode through libkvq: pool_scores fp32 [B, pool_cap] (entry i's
+    score), pool / pool_n as hsi_candidates returns them; returns (sel int32
+    [B, top_k] positions ascending, sel_n int32 [B])."""
+    B, cap = pool_scores.shape
+    dev = pool_scores.device
+    sel, sel_n = out if out is not None else (
+        torch.empty(B, top_k, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev))
+    kvq.kv_hsi_select(_ptr(pool_scores), _ptr(pool), _ptr(pool_n), B, cap, top_k, _ptr(sel), _ptr(sel_n),
+                      _stream_ptr(dev))
+    return sel, sel_n
+
+
 class PackedKVCache:
     def __init__(self, fmt, batch, num_kv_heads, head_dim, capacity, rope_dim=0, device="cuda",
                  constants=None, sink_tokens=0, recent_tokens=0, page_tokens=0, num_pages=0, block_table=None):
@@ -166,6 +194,27 @@ class PackedKVCache:
         opts = KVDecodeOpts(splits, None, None, num_queries)
         return kvq.kv_decode_attention(self.struct, None, _TORCH_DT[q_dtype], num_q_heads, None, max_seq_len,
                                        1.0, None, None, 0, opts)
+
+    def decode_sparse(self, q, sel, sel_n, scale, splits=0, out=None, ws=None, events=None):
+        """q: [B, Hq, d(+rope)]; sel int32 [B, K] positions, sel_n int32 [B] (device):
+        query (b, hq) attends over sel[b, :sel_n[b]] only.  Returns fp32 [B, Hq, d]."""
+        q = q.contiguous()
+        Hq, K = q.shape[-2], sel.shape[1]
+        opts = KVDecodeOpts(splits, None, None, 1)
+        need = kvq.kv_decode_attention_sparse(self.struct, None, _TORCH_DT[q.dtype], Hq, None, None, K, 1.0, None,
+                                              None, 0, opts)
+        if ws is None:
+            if self._ws is None or self._ws.numel() < need:
+                self._ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
+            ws = self._ws
+        if out is None:
+            out = torch.empty((self.B, Hq, self.d), dtype=torch.float32, device=self.device)
+        if events is not None:
+            opts = KVDecodeOpts(splits, ctypes.c_void_p(events[0].cuda_event), ctypes.c_void_p(events[1].cuda_event), 1)
+        kvq.kv_decode_attention_sparse(self.struct, _ptr(q), _TORCH_DT[q.dtype], Hq, _ptr(sel), _ptr(sel_n), K,
+                                       float(scale), _ptr(out), _ptr(ws), ws.numel(), opts,
+                                       _stream_ptr(self.device))
+        return out
 
     def decode(self, q, seq_lens, scale, max_seq_len=None, splits=0, out=None, ws=None, events=None):
         """q: [B, Hq, d(+rope)] fp32/bf16, or [B, nq, Hq, d(+rope)] for nq query tokens per

@@ -86,3 +86,64 @@ extern "C" int kv_decode_attention(const kv_cache* c, const void* q, int32_t q_d
   return launch_decode(c, q, q_dtype, num_q_heads, nq, seq_lens, max_seq_len, softmax_scale, out, ws, plan, wsl,
                        opts ? opts->ev_begin : nullptr, opts ? opts->ev_end : nullptr, stream);
 }
+
+extern "C" int kv_hsi_candidates(const float* scores, int32_t batch, int32_t score_stride, const int32_t* seq_lens,
+                                 int32_t block, int32_t top_blocks, int32_t* pool, int32_t* pool_n, void* ws,
+                                 size_t* ws_bytes, void* stream) {
+  if (batch < 1 || batch > 65535 || score_stride < 1 || block < 1 || block > 64 || top_blocks < 1 ||
+      (int64_t)top_blocks * block > INT32_MAX)
+    return KV_EINVAL;
+  const size_t need = hsi_candidates_workspace(batch, score_stride, block);
+  if (!ws) {
+    if (!ws_bytes) return KV_EINVAL;
+    *ws_bytes = need;
+    return KV_OK;
+  }
+  if (!ws_bytes || *ws_bytes < need) return KV_EWORKSPACE;
+  if (!aligned(ws, 4) || !scores || !seq_lens || !pool || !pool_n) return KV_EINVAL;
+  return launch_hsi_candidates(scores, batch, score_stride, seq_lens, block, top_blocks, pool, pool_n, ws, stream);
+}
+
+extern "C" int kv_hsi_select(const float* pool_scores, const int32_t* pool, const int32_t* pool_n, int32_t batch,
+                             int32_t pool_cap, int32_t top_k, int32_t* sel, int32_t* sel_n, void* stream) {
+  if (batch < 1 || batch > 65535 || pool_cap < 1 || top_k < 1) return KV_EINVAL;
+  if (!pool_scores || !pool || !pool_n || !sel || !sel_n) return KV_EINVAL;
+  return launch_hsi_select(pool_scores, pool, pool_n, batch, pool_cap, top_k, sel, sel_n, stream);
+}
+
+extern "C" int kv_decode_attention_sparse(const kv_cache* c, const void* q, int32_t q_dtype, int32_t num_q_heads,
+                                          const int32_t* sel, const int32_t* sel_n, int32_t sel_cap,
+                                          float softmax_scale, float* out, void* ws, size_t* ws_bytes,
+                                          const kv_decode_opts* opts, void* stream) {
+  int st = check_cache(c);
+  if (st != KV_OK) return st;
+  const kv_layout& L = c->layout;
+  if (L.sink_tokens || L.recent_tokens) return KV_EUNSUPPORTED;
+  if (num_q_heads < 1 || num_q_heads % L.num_kv_heads) return KV_EINVAL;
+  if (num_q_heads / L.num_kv_heads > 1024) return KV_EUNSUPPORTED;
+  if (sel_cap < 1) return KV_EINVAL;
+  if (q_dtype != KV_DT_F32 && q_dtype != KV_DT_BF16) return KV_EUNSUPPORTED;
+  if (!std::isfinite(softmax_scale)) return KV_EINVAL;
+  const int req = opts ? opts->num_splits : 0;
+  if (req < 0 || req > 1024) return KV_EINVAL;
+  if (opts && opts->num_queries > 1) return KV_EUNSUPPORTED;
+  if (opts && opts->num_queries < 0) return KV_EINVAL;
+  const bool latent = latent_sparse_ok(L, num_q_heads, q_dtype);
+  SplitPlan plan = plan_splits(&L, num_q_heads, 1, q_dtype, sel_cap, req, !latent);
+  if (latent && plan.tokens_per_split > kLatentSparseSlots) {  // the latent kernel stages a split's positions
+    const int splits = (sel_cap + kLatentSparseSlots - 1) / kLatentSparseSlots;
+    const int per = ((sel_cap + splits - 1) / splits + 63) / 64 * 64;
+    plan = SplitPlan{(sel_cap + per - 1) / per, per};
+  }
+  const DecodeWorkspace wsl = decode_workspace(&L, num_q_heads, plan.splits);
+  if (!ws) {
+    if (!ws_bytes) return KV_EINVAL;
+    *ws_bytes = wsl.total;
+    return KV_OK;
+  }
+  if (!ws_bytes || *ws_bytes < wsl.total) return KV_EWORKSPACE;
+  if (!aligned(ws, 256)) return KV_EINVAL;
+  if (!q || !sel || !sel_n || !out) return KV_EINVAL;
+  return launch_decode(c, q, q_dtype, num_q_heads, 1, sel_n, sel_cap, softmax_scale, out, ws, plan, wsl,
+                       opts ? opts->ev_begin : nullptr, opts ? opts->ev_end : nullptr, stream, sel, sel_cap);
+}

@@ -36,6 +36,10 @@ struct DecodeArgs {
   const float* levels;
   int H, cap, d, rope_dim;
   PageMap pm;  // token rows (paged storage or contiguous)
+  // sparse decode: slot i of sequence b reads position sel[b * sel_stride + i]
+  // (seq_lens then counts slots); nullptr: slot i is position i
+  const int32_t* sel;
+  int sel_stride;
   // query / output
   const float* qv;  // prepared queries [B][nq][Hq][QW]
   int Hq, G, head_blocks, hb_size;
@@ -137,7 +141,8 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
     return ((size_t)b * a.nq + vh / a.Gr) * a.Hq + (size_t)h * a.Gr + vh % a.Gr;
   };
   __shared__ int lim[HB];
-  __shared__ size_t trow[TT];  // cache rows of the tile's tokens (kNoRow: a page outside the pool)
+  __shared__ size_t trow[TT];  // cache rows of the tile's tokens (kNoRow: no row; masked)
+  __shared__ int tpos[TT];     // their positions
 
   for (int e = tid; e < HB * DK; e += NT) {
     const int hh = e / DK, c = e % DK;
@@ -155,14 +160,16 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
 
   for (int t0 = t_begin; t0 < t_end; t0 += TT) {
     const int nt = min(TT, t_end - t0);
-    if (tid < TT) trow[tid] = tid < nt ? token_row(a.pm, a.H, b, h, t0 + tid) : kNoRow;
+    if (tid < TT) {
+      const int pos = tid >= nt ? -1 : a.sel ? a.sel[(size_t)b * a.sel_stride + t0 + tid] : t0 + tid;
+      tpos[tid] = pos;
+      trow[tid] = pos >= 0 && pos < a.cap ? token_row(a.pm, a.H, b, h, pos) : kNoRow;
+    }
     __syncthreads();
     for (int e = tid; e < TT * DK; e += NT) {
       const int t = e / DK, c = e % DK;
       const size_t row = trow[t];
-      // a staged KIVI key needs no row
-      const bool live = t < nt && (row != kNoRow || (FMT == KV_FMT_KIVI2 && t0 + t >= kstage));
-      ks[t][c] = live ? key_elem<FMT>(a, bh, row, t0 + t, c, kstage) : 0.f;
+      ks[t][c] = t < nt && row != kNoRow ? key_elem<FMT>(a, bh, row, tpos[t], c, kstage) : 0.f;
     }
     if constexpr (!kAlias) {
       for (int e = tid; e < TT * DV; e += NT) {
@@ -175,7 +182,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
       const int hh = p / TT, t = p % TT;
       float s = 0.f;
       for (int c = 0; c < DK; ++c) s = fmaf(qs[hh][c], ks[t][c], s);
-      ss[hh][t] = (t < nt && hh < nh && t0 + t < lim[hh]) ? s * a.scale_log2 : -INFINITY;
+      ss[hh][t] = (t < nt && hh < nh && t0 + t < lim[hh] && trow[t] != kNoRow) ? s * a.scale_log2 : -INFINITY;
     }
     __syncthreads();
     if (tid < nh) {
@@ -689,7 +696,8 @@ void launch_window(const kv_cache* c, const void* q, int q_dtype, int num_q_head
 
 int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads, int nq, const int32_t* seq_lens,
                   int max_seq_len, float scale, float* out, void* ws, const SplitPlan& plan,
-                  const DecodeWorkspace& wsl, void* ev_begin, void* ev_end, void* stream) {
+                  const DecodeWorkspace& wsl, void* ev_begin, void* ev_end, void* stream, const int32_t* sel,
+                  int sel_stride) {
   const kv_layout& L = c->layout;
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* wsb = static_cast<char*>(ws);
@@ -702,12 +710,14 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
   const bool windowed = L.sink_tokens || L.recent_tokens;
   const int part_splits = plan.splits + window_chunks(L);
   const int qw_in = query_width(&L), qw_out = prepared_query_width(&L);
-  if (latent_fast_path_ok(L, num_q_heads, nq, q_dtype)) {
+  if (sel ? latent_sparse_ok(L, num_q_heads, q_dtype) : latent_fast_path_ok(L, num_q_heads, nq, q_dtype)) {
     MfmaDecodeArgs f{};
     f.k_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_K_CODES]);
     f.k_scale = static_cast<const uint16_t*>(c->buf[KV_BUF_K_SCALE]);
     f.rope = static_cast<const uint16_t*>(c->buf[KV_BUF_ROPE]);
     f.pm = page_map(c);
+    f.sel = sel;
+    f.sel_stride = sel_stride;
     f.q = q;
     f.seq_lens = seq_lens;
     f.max_len = max_seq_len;
@@ -725,10 +735,11 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     launch_merge(part, rows, part_splits, L.head_dim, L.format, c->rot, out, st);
     return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
   }
-  const bool mfma = mfma_fast_path_ok(L, num_q_heads, nq, q_dtype);
+  const bool mfma = !sel && mfma_fast_path_ok(L, num_q_heads, nq, q_dtype);
+  const bool turbo = !sel && turbo_fast_path_ok(L, num_q_heads, nq);
   // FP4 keys read the caller's bf16 queries as they are; every other format
   // first prepares its fp32 query (projection / rotation)
-  uint8_t* qpieces = turbo_fast_path_ok(L, num_q_heads, nq) || (mfma && L.format == KV_FMT_QJL1_FP4V)
+  uint8_t* qpieces = turbo || (mfma && L.format == KV_FMT_QJL1_FP4V)
                          ? reinterpret_cast<uint8_t*>(wsb + wsl.qpiece_off)
                          : nullptr;
   if (!(mfma && L.format == KV_FMT_FP4)) {
@@ -740,7 +751,7 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
       prep_query_kernel<uint16_t><<<rows, prep_threads, 0, st>>>(static_cast<const uint16_t*>(q), qw_in, qw_out,
                                                         L.format, c->rot, c->proj, c->lm_levels, qv, qpieces);
   }
-  if (turbo_fast_path_ok(L, num_q_heads, nq)) {
+  if (turbo) {
     TurboDecodeArgs f{};
     f.k_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_K_CODES]);
     f.k_sketch = static_cast<const uint8_t*>(c->buf[KV_BUF_K_SKETCH]);
@@ -830,6 +841,8 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
   a.d = L.head_dim;
   a.rope_dim = L.rope_dim;
   a.pm = page_map(c);
+  a.sel = sel;
+  a.sel_stride = sel_stride;
   a.qv = qv;
   a.Hq = num_q_heads;
   a.nq = nq;

@@ -127,6 +127,32 @@ __device__ __forceinline__ void issue_tile(uint8_t* st, int wave, int lane, int 
   }
 }
 
+// Sparse decode: the tile's slots read the staged positions pos[rel .. rel + 32)
+// (-1: none; rel < 0: no tile), each lane its own token row of the chunk it
+// loads (as issue_tile: codes and scales 4 c + lane / 16, RoPE 2 c + lane / 32).
+// A missing position reads past the end of the resources: zeros.
+template <int NW>
+__device__ __forceinline__ void issue_tile_sparse(uint8_t* st, int wave, int lane, int rel, const int* pos,
+                                                  const Res& r) {
+  auto tok = [&](int slot) { return rel < 0 ? -1 : pos[rel + slot]; };
+#pragma unroll
+  for (int k = 0; k < 8 / NW; ++k) {
+    const int c = wave + k * NW;
+    const int p = tok(4 * c + (lane >> 4));
+    const uint32_t oc = p < 0 ? 0xFFFFFFFFu : (uint32_t)p * 256u + (lane & 15) * 16;
+    const uint32_t os = p < 0 ? 0xFFFFFFFFu : (uint32_t)p * 64u + (lane & 15) * 4;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.codes, (lds_ptr_t)(st + kStCodes + c * 1024), 16, oc, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.scale, (lds_ptr_t)(st + kStScale + c * 256), 4, os, 0, 0, 0);
+  }
+#pragma unroll
+  for (int k = 0; k < 16 / NW; ++k) {
+    const int c = wave + k * NW;
+    const int p = tok(2 * c + (lane >> 5));
+    const uint32_t orp = p < 0 ? 0xFFFFFFFFu : (uint32_t)p * 128u + (lane & 31) * 4;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.rope, (lds_ptr_t)(st + kStRope + c * 256), 4, orp, 0, 0, 0);
+  }
+}
+
 // o *= f for one accumulator held in an AGPR, without the compiler staging the
 // whole accumulator array through arch VGPRs.
 __device__ __forceinline__ void scale_acc(float& x, float f) {
@@ -137,7 +163,9 @@ __device__ __forceinline__ void scale_acc(float& x, float f) {
 }
 
 // PAGED: token rows in pool pages named by the block table, resources per tile.
-template <int NW, bool PAGED>
+// SPARSE (contiguous caches): the split's slots read the positions a.sel names,
+// staged in LDS; slots without a valid position are masked.
+template <int NW, bool PAGED, bool SPARSE>
 __global__ void __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(1, 1))) decode_latent_kernel(MfmaDecodeArgs a) {
   constexpr int NT = 64 * NW;
@@ -153,6 +181,24 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) decode_latent_kernel(MfmaDecodeArgs a
   const int t_begin = split * a.per_split;
   const int t_end = min(L, t_begin + a.per_split);
   const int col = lane & 31, half = lane >> 5;
+  static_assert(!(PAGED && SPARSE), "sparse decode reads contiguous caches");
+  __shared__ int spos[SPARSE ? kLatentSparseSlots : 1];
+  __shared__ uint32_t svalid[SPARSE ? kLatentSparseSlots / kTile : 1];  // bit j: slot j of the tile is valid
+  if constexpr (SPARSE) {
+    const int32_t* sb = a.sel + (size_t)b * a.sel_stride;
+    for (int i = tid; i < a.per_split; i += NT) {
+      const int slot = t_begin + i;
+      int p = slot < t_end ? sb[slot] : -1;
+      spos[i] = p >= 0 && p < a.cap ? p : -1;
+    }
+    __syncthreads();
+    for (int ti = tid; ti < a.per_split / kTile; ti += NT) {
+      uint32_t m = 0;
+      for (int j = 0; j < kTile; ++j) m |= (spos[ti * kTile + j] >= 0 ? 1u : 0u) << j;
+      svalid[ti] = m;
+    }
+    __syncthreads();
+  }
 
   // ---------------- the query operand: 32 fp16 latent steps, 4 bf16 RoPE steps
   h8_t ql[32];
@@ -202,11 +248,17 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) decode_latent_kernel(MfmaDecodeArgs a
     return s;
   };
 
-  {
-    const TileSrc s0 = tile_or_none(t_begin), s1 = tile_or_none(t_begin + kTile);
-    issue_tile<NW>(stA, wave, lane, s0.t, s0.r);
-    issue_tile<NW>(stB, wave, lane, s1.t, s1.r);
-  }
+  // the loads of tile t into stage st
+  auto issue_at = [&](uint8_t* st, int t) {
+    if constexpr (SPARSE) {
+      issue_tile_sparse<NW>(st, wave, lane, t < t_end ? t - t_begin : -1, spos, res);
+    } else {
+      const TileSrc s = tile_or_none(t);
+      issue_tile<NW>(st, wave, lane, s.t, s.r);
+    }
+  };
+  issue_at(stA, t_begin);
+  issue_at(stB, t_begin + kTile);
 
   // lane constants of the fragment reads (kept opaque so that the compiler does
   // not hoist one address register per read out of the loop)
@@ -253,10 +305,7 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) decode_latent_kernel(MfmaDecodeArgs a
       }
       __syncthreads();
       // -------- the stage is free: refill it two tiles ahead
-      {
-        const TileSrc nx = tile_or_none(tt + 2 * kTile);
-        issue_tile<NW>(st, wave, lane, nx.t, nx.r);
-      }
+      issue_at(st, tt + 2 * kTile);
       // -------- 3. S^T = K Q^T for this wave's 32 heads (two accumulation chains)
       f16v_t s = f16v_t{}, s2 = f16v_t{};
 #pragma unroll
@@ -285,7 +334,8 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) decode_latent_kernel(MfmaDecodeArgs a
       s += s2;
       // -------- 4. online softmax for head 32 wave + col over this lane's 16 tokens
       float tmax = -INFINITY;
-      if (tt + kTile <= t_end) {  // a whole tile: nothing to mask
+      const uint32_t valid = SPARSE ? svalid[(tt - t_begin) / kTile] : 0xFFFFFFFFu;
+      if (tt + kTile <= t_end && valid == 0xFFFFFFFFu) {  // a whole tile: nothing to mask
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           s[i] = s[i] * a.scale_log2;
@@ -294,8 +344,8 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) decode_latent_kernel(MfmaDecodeArgs a
       } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int tok = tt + 16 * (i >> 3) + 8 * half + (i & 7);
-          s[i] = tok < t_end ? s[i] * a.scale_log2 : -INFINITY;
+          const int j = 16 * (i >> 3) + 8 * half + (i & 7);
+          s[i] = tt + j < t_end && ((valid >> j) & 1u) ? s[i] * a.scale_log2 : -INFINITY;
           tmax = fmaxf(tmax, s[i]);
         }
       }
@@ -375,13 +425,13 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) decode_latent_kernel(MfmaDecodeArgs a
 }  // namespace
 
 namespace {
-template <bool PAGED>
+template <bool PAGED, bool SPARSE>
 int launch_latent(const MfmaDecodeArgs& a, int B, hipStream_t st) {
   dim3 grid(a.splits, B);
   switch (a.Hq) {
-    case 32: decode_latent_kernel<1, PAGED><<<grid, 64, 0, st>>>(a); break;
-    case 64: decode_latent_kernel<2, PAGED><<<grid, 128, 0, st>>>(a); break;
-    case 128: decode_latent_kernel<4, PAGED><<<grid, 256, 0, st>>>(a); break;
+    case 32: decode_latent_kernel<1, PAGED, SPARSE><<<grid, 64, 0, st>>>(a); break;
+    case 64: decode_latent_kernel<2, PAGED, SPARSE><<<grid, 128, 0, st>>>(a); break;
+    case 128: decode_latent_kernel<4, PAGED, SPARSE><<<grid, 256, 0, st>>>(a); break;
     default: return KV_EUNSUPPORTED;
   }
   return KV_OK;
@@ -389,7 +439,8 @@ int launch_latent(const MfmaDecodeArgs& a, int B, hipStream_t st) {
 }  // namespace
 
 int launch_decode_latent(const MfmaDecodeArgs& a, int B, hipStream_t st) {
-  return a.pm.table ? launch_latent<true>(a, B, st) : launch_latent<false>(a, B, st);
+  if (a.sel) return a.pm.table ? KV_EUNSUPPORTED : launch_latent<false, true>(a, B, st);
+  return a.pm.table ? launch_latent<true, false>(a, B, st) : launch_latent<false, false>(a, B, st);
 }
 
 }  // namespace kvq

@@ -109,13 +109,15 @@ bool mfma_fast_path_ok(const kv_layout& L, int num_q_heads, int nq, int q_dtype)
   return false;
 }
 
-SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int nq, int q_dtype, int max_seq_len, int requested) {
+SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int nq, int q_dtype, int max_seq_len, int requested,
+                      bool general) {
   // Workgroups cover their split in steps of `tile` tokens; aim for enough
   // workgroups to keep a 256-CU part busy several times over, but no split
   // shorter than a few steps.
   const int G = num_q_heads / L->num_kv_heads;
-  const bool fast = mfma_fast_path_ok(*L, num_q_heads, nq, q_dtype) || turbo_fast_path_ok(*L, num_q_heads, nq);
-  const bool latent = latent_fast_path_ok(*L, num_q_heads, nq, q_dtype);
+  const bool fast =
+      !general && (mfma_fast_path_ok(*L, num_q_heads, nq, q_dtype) || turbo_fast_path_ok(*L, num_q_heads, nq));
+  const bool latent = !general && latent_fast_path_ok(*L, num_q_heads, nq, q_dtype);
   const int tile = fast ? 128 : 64;
   // the latent kernel keeps one workgroup per compute unit resident and every
   // split writes Hq x 514 partial floats: one round of workgroups, a few long

@@ -61,7 +61,9 @@ bool latent_fast_path_ok(const kv_layout& L, int num_q_heads, int nq, int q_dtyp
 // Columns of the matrix-core kernel that takes n (query, head) pairs, n <= 32:
 // n rounded up to 1, 2, 4, 8, 16 or 32 (two blocks of 16, FP4 keys only).
 int mfma_columns(int n);
-SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int nq, int q_dtype, int max_seq_len, int requested);
+// general: the plan of the general kernel (sparse decode), whatever the layout
+SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int nq, int q_dtype, int max_seq_len, int requested,
+                      bool general = false);
 
 // Workspace of a decode call: prepared queries, then per-split partial results
 // (running max, running sum, unnormalised output) — offsets in bytes.
@@ -85,9 +87,23 @@ inline int window_chunks(const kv_layout& L) { return (L.sink_tokens + L.recent_
 // starts is given.
 int launch_append(const kv_cache* c, const void* k, const void* v, int in_dtype, int start,
                   const int32_t* starts, int n_new, void* stream);
+// sel: sparse decode over the positions sel[b][0 .. seq_lens[b]) (row stride
+// sel_stride) on the general kernel; nullptr for the dense decode.
 int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads, int nq,
                   const int32_t* seq_lens, int max_seq_len, float scale, float* out, void* ws,
                   const SplitPlan& plan, const DecodeWorkspace& wsl, void* ev_begin, void* ev_end,
-                  void* stream);
+                  void* stream, const int32_t* sel = nullptr, int sel_stride = 0);
+// Sparse decode of a contiguous latent cache runs on the latent matrix-core
+// kernel, whose splits stage at most this many selected positions each.
+constexpr int kLatentSparseSlots = 512;
+inline bool latent_sparse_ok(const kv_layout& L, int num_q_heads, int q_dtype) {
+  return latent_fast_path_ok(L, num_q_heads, 1, q_dtype) && L.page_tokens == 0;
+}
+// HSI selection (kvq_hsi.hip).
+size_t hsi_candidates_workspace(int batch, int stride, int blk);
+int launch_hsi_candidates(const float* scores, int batch, int stride, const int32_t* seq_lens, int blk,
+                          int top_blocks, int32_t* pool, int32_t* pool_n, void* ws, void* stream);
+int launch_hsi_select(const float* pool_scores, const int32_t* pool, const int32_t* pool_n, int batch, int pool_cap,
+                      int top_k, int32_t* sel, int32_t* sel_n, void* stream);
 
 }  // namespace kvq

@@ -20,6 +20,10 @@ struct MfmaDecodeArgs {
   const uint16_t* v_scale;  // [B][H][cap][8] bf16
   const uint16_t* rope;     // latent: [B][cap][64] bf16 (k_codes [B][cap][256], k_scale [B][cap][32])
   PageMap pm;               // token rows: [B][H][cap] above, or a paged pool
+  // latent sparse decode: slot i of sequence b reads position sel[b * sel_stride + i]
+  // (seq_lens counts slots, at most kLatentSparseSlots per split); nullptr: dense
+  const int32_t* sel;
+  int sel_stride;
   const void* q;            // FP4: bf16 [B][Hq][128]; QJL: fp32 S q [B][Hq][128]
   const uint8_t* qpieces;   // QJL: [B][Hq][kQjlPieceBytes], FP8 pieces of S q
   const int32_t* seq_lens;

@@ -23,7 +23,8 @@ BUFFERS = ["k_codes", "k_scale", "k_zero", "k_sketch", "k_norm", "k_rnorm",
            "k_stage"]
 EXPORTED = ["kv_buffer_bytes", "kv_bytes_per_token", "kv_quant_append", "kv_quant_append_ragged", "kv_decode_attention",
             "kv_lloyd_max_gaussian", "kv_make_rotation", "kv_make_hadamard_rotation",
-            "kv_make_projection", "kv_status_string"]
+            "kv_make_projection", "kv_status_string", "kv_hsi_candidates", "kv_hsi_select",
+            "kv_decode_attention_sparse"]
 
 
 class KvError(RuntimeError):
@@ -84,6 +85,13 @@ def lib():
         L.kv_make_hadamard_rotation.restype = ctypes.c_int
         L.kv_make_projection.argtypes = [vp, i32, i32, vp]
         L.kv_make_projection.restype = ctypes.c_int
+        L.kv_hsi_candidates.argtypes = [vp, i32, i32, vp, i32, i32, vp, vp, vp, ctypes.POINTER(sz), vp]
+        L.kv_hsi_candidates.restype = ctypes.c_int
+        L.kv_hsi_select.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, vp]
+        L.kv_hsi_select.restype = ctypes.c_int
+        L.kv_decode_attention_sparse.argtypes = [ctypes.POINTER(KVCache), vp, i32, i32, vp, vp, i32, ctypes.c_float,
+                                                 vp, vp, ctypes.POINTER(sz), ctypes.POINTER(KVDecodeOpts), vp]
+        L.kv_decode_attention_sparse.restype = ctypes.c_int
         L.kv_status_string.argtypes = [ctypes.c_int]
         L.kv_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -172,6 +180,32 @@ def kv_make_projection(gauss) -> np.ndarray:
     out = np.zeros((m, d), np.float32)
     _check("kv_make_projection", lib().kv_make_projection(g.ctypes.data, m, d, out.ctypes.data))
     return out
+
+
+def kv_hsi_candidates(scores_ptr, batch, score_stride, seq_lens_ptr, block, top_blocks, pool_ptr, pool_n_ptr,
+                      ws_ptr, ws_bytes, stream=0):
+    """ws_ptr None: returns the workspace size; else runs."""
+    nbytes = ctypes.c_size_t(ws_bytes or 0)
+    _check("kv_hsi_candidates", lib().kv_hsi_candidates(scores_ptr, batch, score_stride, seq_lens_ptr, block,
+                                                        top_blocks, pool_ptr, pool_n_ptr, ws_ptr,
+                                                        ctypes.byref(nbytes), stream))
+    return nbytes.value
+
+
+def kv_hsi_select(pool_scores_ptr, pool_ptr, pool_n_ptr, batch, pool_cap, top_k, sel_ptr, sel_n_ptr, stream=0):
+    _check("kv_hsi_select", lib().kv_hsi_select(pool_scores_ptr, pool_ptr, pool_n_ptr, batch, pool_cap, top_k,
+                                                sel_ptr, sel_n_ptr, stream))
+
+
+def kv_decode_attention_sparse(cache: KVCache, q_ptr, q_dtype, num_q_heads, sel_ptr, sel_n_ptr, sel_cap, scale,
+                               out_ptr, ws_ptr, ws_bytes, opts=None, stream=0):
+    """ws_ptr None: returns the workspace size; else runs and returns ws_bytes."""
+    nbytes = ctypes.c_size_t(ws_bytes or 0)
+    st = lib().kv_decode_attention_sparse(ctypes.byref(cache), q_ptr, q_dtype, num_q_heads, sel_ptr, sel_n_ptr,
+                                          sel_cap, ctypes.c_float(scale), out_ptr, ws_ptr, ctypes.byref(nbytes),
+                                          ctypes.byref(opts) if opts is not None else None, stream)
+    _check("kv_decode_attention_sparse", st)
+    return nbytes.value
 
 
 def kv_status_string(status: int) -> str:

@@ -314,6 +314,52 @@ int kv_make_hadamard_rotation(int32_t d, int32_t bit_reverse, float* rot);
  * to bf16, written as fp32 (same section, stage two). */
 int kv_make_projection(const double* gauss, int32_t m, int32_t d, float* proj);
 
+/* Hierarchical sparse indexing, full mode (page "How DeepSeek-V4.1-Flash cut
+ * KV-cache storage by 4x via CSA2", HSI section: the first layer scores every
+ * position, keeps the blocks of 8 with the largest maximum score, 2048 of them,
+ * as the candidate pool).  Per sequence b with L = min(seq_lens[b],
+ * score_stride): the score of block j is the largest of scores[b][t] over
+ * t in [j*block, min(L, (j+1)*block)); the top_blocks blocks with the largest
+ * scores (all when there are fewer; equal scores: the lower block first) give
+ * pool[b][0 .. pool_n[b]), their positions below L in ascending order.
+ *   scores     device f32 [B][score_stride], finite (-0 equals +0); the
+ *              indexer's scores, an input
+ *   seq_lens   device int32 [B]
+ *   pool       device int32 [B][top_blocks * block] out (entries past pool_n[b]
+ *              are left as they were); pool_n device int32 [B] out
+ *   ws         device workspace, 4-byte aligned; ws NULL: *ws_bytes is set to
+ *              its size (B * ceil(score_stride / block) * 4) and nothing runs
+ * block in [1, 64], top_blocks >= 1, B <= 65535, else KV_EINVAL. */
+int kv_hsi_candidates(const float* scores, int32_t batch, int32_t score_stride, const int32_t* seq_lens,
+                      int32_t block, int32_t top_blocks, int32_t* pool, int32_t* pool_n, void* ws,
+                      size_t* ws_bytes, void* stream);
+
+/* Hierarchical sparse indexing, reindex mode (same section: later layers score
+ * only the pool and keep the final top 512).  Per sequence b: of the entries
+ * pool[b][0 .. min(pool_n[b], pool_cap)), the top_k with the largest
+ * pool_scores[b][i] (all when there are fewer; equal scores: the earlier entry
+ * first) as positions in pool order, sel[b][0 .. sel_n[b]).
+ *   pool_scores  device f32 [B][pool_cap], finite: the layer's score of pool
+ *                entry i (an input)
+ *   pool, pool_n device, as kv_hsi_candidates writes them (pool_cap = its row
+ *                length)
+ *   sel          device int32 [B][top_k] out; sel_n device int32 [B] out */
+int kv_hsi_select(const float* pool_scores, const int32_t* pool, const int32_t* pool_n, int32_t batch,
+                  int32_t pool_cap, int32_t top_k, int32_t* sel, int32_t* sel_n, void* stream);
+
+/* Decode over selected positions (same section: attention reads only the
+ * top-k positions).  As kv_decode_attention with one query per sequence, but
+ * query (b, hq) attends over the positions sel[b][0 .. min(sel_n[b], sel_cap))
+ * only: a softmax over their logits.  Positions outside [0, capacity) (and
+ * rows on pages outside a paged pool) are skipped; a sequence with none left
+ * gets zeros.  KIVI2 keys past a sequence's coded groups come from K_STAGE as
+ * in dense decode.  Caches with bf16 windows and opts->num_queries > 1 are
+ * KV_EUNSUPPORTED.  The workspace size (a call with ws NULL) depends on
+ * sel_cap and opts->num_splits. */
+int kv_decode_attention_sparse(const kv_cache* c, const void* q, int32_t q_dtype, int32_t num_q_heads,
+                               const int32_t* sel, const int32_t* sel_n, int32_t sel_cap, float softmax_scale,
+                               float* out, void* ws, size_t* ws_bytes, const kv_decode_opts* opts, void* stream);
+
 /* Static description of a status code. */
 const char* kv_status_string(int status);
 

@@ -14,6 +14,7 @@ from .configs import CONFIGS, Config, get_config  # noqa: F401
 from .gen import (  # noqa: F401
     gaussian_matrix,
     make_kv,
+    make_indexer_scores,
     make_latent,
     make_queries,
     outlier_channels,

@@ -18,7 +18,7 @@ BLOCK = 4096
 _MASK = (1 << 63) - 1
 
 # stream ids
-_S_K, _S_V, _S_Q, _S_OUT, _S_LAT = 1, 2, 3, 4, 5
+_S_K, _S_V, _S_Q, _S_OUT, _S_LAT, _S_IDX = 1, 2, 3, 4, 5, 6
 
 
 def _mix(*vals: int) -> int:
@@ -117,3 +117,23 @@ def seq_lens_for(cfg, ragged: bool = False, seed: int = 0) -> np.ndarray:
     lens = rng.integers(1, cfg.context + 1, size=cfg.batch).astype(np.int32)
     lens[0] = cfg.context
     return lens
+
+
+def make_indexer_scores(seed: int, batch: int, length: int, layer: int = 0, device="cpu") -> torch.Tensor:
+    """fp32 [batch, length] stand-ins for a sparse indexer's scores: N(0, 1)
+    background with a few raised spans per sequence (the positions a query would
+    look back at), rounded to bf16 values as a low-precision indexer emits them,
+    so that equal scores occur.  `layer` draws an independent set."""
+    out = torch.empty(batch, length, dtype=torch.float32, device=device)
+    for b in range(batch):
+        g = _gen(device, seed, _S_IDX, layer, b)
+        x = torch.randn(length, generator=g, device=device, dtype=torch.float32)
+        nspan = 8
+        starts = torch.randint(0, max(1, length), (nspan,), generator=g, device=device)
+        lens = torch.randint(16, 512, (nspan,), generator=g, device=device)
+        lift = 2.0 + 2.0 * torch.rand(nspan, generator=g, device=device)
+        for i in range(nspan):
+            s0 = int(starts[i])
+            x[s0:s0 + int(lens[i])] += float(lift[i])
+        out[b] = x.to(torch.bfloat16).to(torch.float32)
+    return out

@@ -258,3 +258,40 @@ def test_paged_layout_validation_and_sizes():
     assert _decode(c, hq=4, maxlen=128, ws=FAKE, wsb=1 << 30)[0] == EINVAL
     c.block_table = FAKE
     assert _append(c, start=100, n=29) == ECAP                      # capacity stays per sequence
+
+
+def test_hsi_validation_and_sizes():
+    L = kvq.lib()
+    nb = ctypes.c_size_t(0)
+    assert L.kv_hsi_candidates(None, 3, 1000, None, 8, 2048, None, None, None, ctypes.byref(nb), None) == OK
+    assert nb.value == 3 * 125 * 4
+    assert L.kv_hsi_candidates(None, 1, 1001, None, 8, 16, None, None, None, ctypes.byref(nb), None) == OK
+    assert nb.value == 126 * 4
+    for args in ((0, 100, 8, 4), (2, 0, 8, 4), (2, 100, 0, 4), (2, 100, 65, 4), (2, 100, 8, 0)):
+        B, S, blk, top = args
+        assert L.kv_hsi_candidates(None, B, S, None, blk, top, None, None, None, ctypes.byref(nb), None) == EINVAL
+    small = ctypes.c_size_t(8)
+    assert L.kv_hsi_candidates(FAKE, 3, 1000, FAKE, 8, 16, FAKE, FAKE, FAKE, ctypes.byref(small), None) == EWS
+    assert L.kv_hsi_select(FAKE, FAKE, FAKE, 0, 100, 8, FAKE, FAKE, None) == EINVAL
+    assert L.kv_hsi_select(FAKE, FAKE, FAKE, 2, 100, 0, FAKE, FAKE, None) == EINVAL
+    assert L.kv_hsi_select(None, FAKE, FAKE, 2, 100, 8, FAKE, FAKE, None) == EINVAL
+
+
+def test_sparse_decode_validation_and_size():
+    def sparse(c, sel=FAKE, seln=FAKE, cap=512, ws=None, wsb=0, nq=0):
+        nb = ctypes.c_size_t(wsb)
+        opts = kvq.KVDecodeOpts(0, None, None, nq)
+        st = kvq.lib().kv_decode_attention_sparse(ctypes.byref(c), FAKE, kvq.DT_BF16, 4, sel, seln, cap,
+                                                  ctypes.c_float(1.0), FAKE, ws, ctypes.byref(nb),
+                                                  ctypes.byref(opts), None)
+        return st, nb.value
+    st, need = sparse(_cache(T=1024))
+    assert st == OK and need > 0
+    assert sparse(_cache(T=1024), cap=0)[0] == EINVAL
+    assert sparse(_cache(T=1024), nq=2)[0] == EUNSUP
+    assert sparse(_cache(T=1024), ws=FAKE, wsb=need - 1)[0] == EWS
+    assert sparse(_cache(T=1024), sel=None, ws=FAKE, wsb=need)[0] == EINVAL
+    lay = kvq.make_layout("fp4", 2, 2, 128, 256, sink=16, recent=16)
+    bufs = (ctypes.c_void_p * len(kvq.BUFFERS))(
+        *[(FAKE if kvq.kv_buffer_bytes(lay, i) else None) for i in range(len(kvq.BUFFERS))])
+    assert sparse(kvq.KVCache(lay, bufs, None, None, None, None, None))[0] == EUNSUP
