@@ -49,6 +49,22 @@ __device__ __forceinline__ size_t dst_row(size_t r, int n, int cap, const Append
   return seq_row(pos, r / n, start_of(pos, r / n) + (int)(r % n), cap);
 }
 
+// dst_row with the ragged starts read from an LDS copy (fill_starts): indexing
+// the by-value table itself with a per-row index would copy it to scratch in
+// every thread.
+__device__ __forceinline__ void fill_starts(const AppendPos& pos, int* starts) {
+  if (pos.ragged && threadIdx.x == 0) {
+#pragma unroll
+    for (int j = 0; j < kMaxRaggedSeqs; ++j) starts[j] = pos.s[j];  // constant offsets: kernel-argument reads
+  }
+  __syncthreads();
+}
+__device__ __forceinline__ size_t dst_row_tab(size_t r, int n, int cap, const AppendPos& pos, const int* starts) {
+  const size_t bh = r / n;
+  const int s0 = pos.ragged ? starts[bh / pos.heads] : pos.start;
+  return seq_row(pos, bh, s0 + (int)(r % n), cap);
+}
+
 // ---------------------------------------------------------------- FP4
 
 // 16 consecutive input elements, read with 16-byte loads (input rows and group
@@ -940,6 +956,8 @@ __global__ void __launch_bounds__(512) turbo_append_small_kernel(
   __shared__ double rs[16 * 129];  // keys: the residual
   __shared__ __align__(16) uint16_t rows_lds[8][2][16 * kSPad];  // per wave: its rows of R, then of S (bf16)
   __shared__ double g2part[8][16];  // keys: per-wave partial gamma^2 per token
+  __shared__ int starts[kMaxRaggedSeqs];
+  fill_starts(pos, starts);
   const bool keys = blockIdx.y == 0;
   const InT* x = keys ? k : v;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -1013,7 +1031,7 @@ __global__ void __launch_bounds__(512) turbo_append_small_kernel(
     word |= __shfl_xor(word, 4);
     word |= __shfl_xor(word, 8);
     if (col == 0 && base + tok < rows) {
-      const size_t dr = dst_row(base + tok, n, cap, pos);
+      const size_t dr = dst_row_tab(base + tok, n, cap, pos, starts);
       if (dr != kNoRow) *reinterpret_cast<uint32_t*>(codes + dr * 32 + 4 * w) = word;
     }
     if (keys) {
@@ -1036,7 +1054,7 @@ __global__ void __launch_bounds__(512) turbo_append_small_kernel(
     }
   }
   if (w == 0 && lane < 16 && base + lane < rows) {
-    const size_t dr = dst_row(base + lane, n, cap, pos);
+    const size_t dr = dst_row_tab(base + lane, n, cap, pos, starts);
     if (dr != kNoRow) (keys ? knorm : vnorm)[dr] = f16_from_f64_nonneg(nrm);
   }
   if (!keys) return;
@@ -1057,7 +1075,7 @@ __global__ void __launch_bounds__(512) turbo_append_small_kernel(
     if ((lane >> 2) == i) my_bits = (uint32_t)(bal >> (16 * (lane & 3))) & 0xFFFFu;
   }
   if (lane < 16 && base + lane < rows) {
-    const size_t dr = dst_row(base + lane, n, cap, pos);
+    const size_t dr = dst_row_tab(base + lane, n, cap, pos, starts);
     if (dr != kNoRow) *reinterpret_cast<uint16_t*>(sketch + dr * 16 + 2 * w) = (uint16_t)my_bits;
     if (w == 0 && dr != kNoRow) {
       double g2 = 0.0;
