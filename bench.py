@@ -338,17 +338,26 @@ def main():
     if args.hsi:
         # the dominant kernel is the sparse decode on the general (fp32 vector) kernel:
         # per selected position and query head, key_width + head_dim multiply-adds
-        # (the latent cache's gather kernel runs them on the fp16 matrix cores)
-        flops = 2.0 * cfg.hq * n_sel * (cfg.key_width + cfg.head_dim)
-        ach = flops / (dec_ms * 1e-3) / 1e12
-        mfma = cfg.fmt == "latent"
-        peak = MFMA_F16_PEAK_TFLOPS if mfma else FP32_VALU_PEAK_TFLOPS
+        # (the latent cache's gather kernel runs them on the fp16 matrix cores); the
+        # FP4 / QJL gather kernels are priced by the packed bytes they gather, the
+        # general kernel (other formats) against the fp32 vector peak
         res["metric"] = "HSI sparse decode step: bytes read GB/s + query-tokens/s at fixed context"
         res["config"].update(hsi={"block": HSI_BLOCK, "top_blocks": HSI_TOP_BLOCKS, "top_k": HSI_TOP_K,
                                   "selected_positions": n_sel})
-        res["roofline"] = {"bound": "mfma" if mfma else "alu", "achieved": round(ach, 2), "peak": peak,
-                           "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
-                           "kernel": "sparse split-context attention", "kernel_us": round(dec_ms * 1e3, 2)}
+        if cfg.fmt in ("fp4", "qjl1"):
+            gathered = kvq.kv_bytes_per_token(cache.layout, 1) * n_sel
+            ach = gathered / (dec_ms * 1e-3) / 1e9
+            res["roofline"] = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                               "kernel": "sparse split-context attention", "kernel_us": round(dec_ms * 1e3, 2)}
+        else:
+            flops = 2.0 * cfg.hq * n_sel * (cfg.key_width + cfg.head_dim)
+            ach = flops / (dec_ms * 1e-3) / 1e12
+            mfma = cfg.fmt == "latent"
+            peak = MFMA_F16_PEAK_TFLOPS if mfma else FP32_VALU_PEAK_TFLOPS
+            res["roofline"] = {"bound": "mfma" if mfma else "alu", "achieved": round(ach, 2), "peak": peak,
+                               "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+                               "kernel": "sparse split-context attention", "kernel_us": round(dec_ms * 1e3, 2)}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, rotation=args.rotation if cfg.fmt == "turbo" else "haar")
     print(json.dumps(res), flush=True)

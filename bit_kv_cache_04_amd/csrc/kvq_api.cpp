@@ -128,11 +128,16 @@ extern "C" int kv_decode_attention_sparse(const kv_cache* c, const void* q, int3
   if (req < 0 || req > 1024) return KV_EINVAL;
   if (opts && opts->num_queries > 1) return KV_EUNSUPPORTED;
   if (opts && opts->num_queries < 0) return KV_EINVAL;
+  // the matrix-core kernels stage a split's positions: at most 512 per split, in
+  // whole 128-token steps (FP4 / QJL) or 64-token steps (latent)
   const bool latent = latent_sparse_ok(L, num_q_heads, q_dtype);
-  SplitPlan plan = plan_splits(&L, num_q_heads, 1, q_dtype, sel_cap, req, !latent);
-  if (latent && plan.tokens_per_split > kLatentSparseSlots) {  // the latent kernel stages a split's positions
-    const int splits = (sel_cap + kLatentSparseSlots - 1) / kLatentSparseSlots;
-    const int per = ((sel_cap + splits - 1) / splits + 63) / 64 * 64;
+  const bool mfma = !latent && mfma_sparse_ok(L, num_q_heads, q_dtype);
+  SplitPlan plan = plan_splits(&L, num_q_heads, 1, q_dtype, sel_cap, req, !latent && !mfma);
+  static_assert(kLatentSparseSlots == kMfmaSparseSlots, "one staging bound");
+  if ((latent || mfma) && plan.tokens_per_split > kMfmaSparseSlots) {
+    const int step = latent ? 64 : 128;
+    const int splits = (sel_cap + kMfmaSparseSlots - 1) / kMfmaSparseSlots;
+    const int per = ((sel_cap + splits - 1) / splits + step - 1) / step * step;
     plan = SplitPlan{(sel_cap + per - 1) / per, per};
   }
   const DecodeWorkspace wsl = decode_workspace(&L, num_q_heads, plan.splits);

@@ -735,7 +735,7 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     launch_merge(part, rows, part_splits, L.head_dim, L.format, c->rot, out, st);
     return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
   }
-  const bool mfma = !sel && mfma_fast_path_ok(L, num_q_heads, nq, q_dtype);
+  const bool mfma = sel ? mfma_sparse_ok(L, num_q_heads, q_dtype) : mfma_fast_path_ok(L, num_q_heads, nq, q_dtype);
   const bool turbo = !sel && turbo_fast_path_ok(L, num_q_heads, nq);
   // FP4 keys read the caller's bf16 queries as they are; every other format
   // first prepares its fp32 query (projection / rotation)
@@ -789,6 +789,8 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     f.v_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_V_CODES]);
     f.v_scale = static_cast<const uint16_t*>(c->buf[KV_BUF_V_SCALE]);
     f.pm = page_map(c);
+    f.sel = sel;
+    f.sel_stride = sel_stride;
     f.q = L.format == KV_FMT_FP4 ? q : static_cast<const void*>(qv);
     f.qpieces = qpieces;
     f.seq_lens = seq_lens;

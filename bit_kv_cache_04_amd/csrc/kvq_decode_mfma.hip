@@ -151,6 +151,16 @@ struct KeysFp4 {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r.ks, (lds_ptr_t)(st + 2048), 4, so, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r.ks, (lds_ptr_t)(st + 2304), 4, so + 256, 0, 0, 0);
   }
+  // gather: the lane's rows of the two 16-token halves are pa and pb (-1: none,
+  // reads zeros); the same stage layout as issue()
+  __device__ static void issue_rows(uint8_t* st, int lane, int pa, int pb, int, const R& r) {
+    const uint32_t ca = pa < 0 ? ~0u : (uint32_t)pa * 64u + (lane & 3) * 16, cb = pb < 0 ? ~0u : (uint32_t)pb * 64u + (lane & 3) * 16;
+    const uint32_t sa = pa < 0 ? ~0u : (uint32_t)pa * 16u + (lane & 3) * 4, sb = pb < 0 ? ~0u : (uint32_t)pb * 16u + (lane & 3) * 4;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.kc, (lds_ptr_t)(st), 16, ca, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.kc, (lds_ptr_t)(st + 1024), 16, cb, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.ks, (lds_ptr_t)(st + 2048), 4, sa, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.ks, (lds_ptr_t)(st + 2304), 4, sb, 0, 0, 0);
+  }
   __device__ static void read(Frag& f, const uint8_t* st, int q4, int c) {
     int ko = row_token(c) * 64 + 16 * q4, kso = row_token(c) * 16 + 4 * q4;
     asm volatile("" : "+v"(ko), "+v"(kso));
@@ -247,6 +257,14 @@ struct KeysQjl {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r.nm, (lds_ptr_t)(st + 512), 2, lane < 32 ? t0 * 2 + lane * 2 : r.nm_end,
                                              0, 0, 0);
   }
+  // gather: sketch rows pa, pb of the lane's two halves, norm row pn (lanes < 32)
+  __device__ static void issue_rows(uint8_t* st, int lane, int pa, int pb, int pn, const R& r) {
+    const uint32_t sa = pa < 0 ? ~0u : (uint32_t)pa * 16u + (lane & 3) * 4, sb = pb < 0 ? ~0u : (uint32_t)pb * 16u + (lane & 3) * 4;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.sk, (lds_ptr_t)(st), 4, sa, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.sk, (lds_ptr_t)(st + 256), 4, sb, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.nm, (lds_ptr_t)(st + 512), 2,
+                                             lane < 32 && pn >= 0 ? (uint32_t)pn * 2u : (uint32_t)r.nm_end, 0, 0, 0);
+  }
   __device__ static void read(Frag& f, const uint8_t* st, int q4, int c) {
     int so = row_token(c) * 16 + 4 * q4, no = 512 + 4 * q4;
     asm volatile("" : "+v"(so), "+v"(no));
@@ -326,6 +344,24 @@ __device__ __forceinline__ void issue_tile(uint8_t* st, int lane, int t0, const 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(vr.vs, (lds_ptr_t)(st + Stage<KP>::kVs + 256), 4, so + 256, 0, 0, 0);
 }
 
+// Gather form of issue_tile: slot rel of the staged positions starts the tile
+// (rel < 0: no tile).  Lane rows: slots lane / 4 and 16 + lane / 4 (codes, scales,
+// sketch), slot lane (QJL norms); the number of loads is issue_tile's.
+template <class KP>
+__device__ __forceinline__ void issue_tile_rows(uint8_t* st, int lane, int rel, const int* pos,
+                                                const typename KP::R& kr, const VRsrc& vr) {
+  const int pa = rel < 0 ? -1 : pos[rel + (lane >> 2)];
+  const int pb = rel < 0 ? -1 : pos[rel + 16 + (lane >> 2)];
+  const int pn = rel < 0 ? -1 : pos[rel + (lane & 31)];
+  KP::issue_rows(st, lane, pa, pb, pn, kr);
+  const uint32_t ca = pa < 0 ? ~0u : (uint32_t)pa * 64u + (lane & 3) * 16, cb = pb < 0 ? ~0u : (uint32_t)pb * 64u + (lane & 3) * 16;
+  const uint32_t sa = pa < 0 ? ~0u : (uint32_t)pa * 16u + (lane & 3) * 4, sb = pb < 0 ? ~0u : (uint32_t)pb * 16u + (lane & 3) * 4;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(vr.vc, (lds_ptr_t)(st + Stage<KP>::kVc), 16, ca, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(vr.vc, (lds_ptr_t)(st + Stage<KP>::kVc + 1024), 16, cb, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(vr.vs, (lds_ptr_t)(st + Stage<KP>::kVs), 4, sa, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(vr.vs, (lds_ptr_t)(st + Stage<KP>::kVs + 256), 4, sb, 0, 0, 0);
+}
+
 // Everything one wave carries across tiles, per block of 16 columns.
 template <class KP, int NB>
 struct WaveState {
@@ -345,9 +381,12 @@ struct Limits {
 // have returned) refill the stage from `nx` (a row past its resources when there
 // is no next tile, so that the refill is unconditional and the compiler's wait
 // counts stay exact), then compute.  Tokens below a.t_lo are masked.
-template <int G, int NS, class KP, int NB>
+// SP: gather mode, nx.t the next tile's first staged slot in pos; `valid` bit j:
+// the tile's slot j holds a position.
+template <int G, int NS, class KP, int NB, bool SP = false>
 __device__ __forceinline__ void tile_step(WaveState<KP, NB>& w, uint8_t* st, int lane, int t0, int t_full,
-                                          const Limits<NB>& lim, const TileSrc<KP>& nx, const MfmaDecodeArgs& a) {
+                                          const Limits<NB>& lim, const TileSrc<KP>& nx, const MfmaDecodeArgs& a,
+                                          const int* pos = nullptr, uint32_t valid = ~0u) {
   const int q4 = lane >> 4, c = lane & 15;
   // This stage's tile has landed once at most the other NS - 1 stages' refills
   // are outstanding.  Waited for explicitly: the compiler's own wait for loads
@@ -370,7 +409,8 @@ __device__ __forceinline__ void tile_step(WaveState<KP, NB>& w, uint8_t* st, int
   }
   // the reads above must have returned before the stage is overwritten
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  issue_tile<KP>(st, lane, nx.t, nx.kr, nx.vr);
+  if constexpr (SP) issue_tile_rows<KP>(st, lane, nx.t, pos, nx.kr, nx.vr);
+  else issue_tile<KP>(st, lane, nx.t, nx.kr, nx.vr);
 
   // ---------------- logits: S^T = K Q^T for the two 16-token blocks
   f4_t sacc[NB][2];
@@ -381,7 +421,7 @@ __device__ __forceinline__ void tile_step(WaveState<KP, NB>& w, uint8_t* st, int
   for (int nb = 0; nb < NB; ++nb) {
     float sv[8];
     float tmax = -INFINITY;
-    if (t0 + 32 <= t_full && t0 >= a.t_lo) {  // a whole tile for every column: nothing to mask
+    if (t0 + 32 <= t_full && t0 >= a.t_lo && valid == ~0u) {  // a whole tile for every column: nothing to mask
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
@@ -395,7 +435,8 @@ __device__ __forceinline__ void tile_step(WaveState<KP, NB>& w, uint8_t* st, int
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int tok = t0 + 16 * blk + 4 * v + q4;
-          const float sx = tok < lim.v[nb] && tok >= a.t_lo ? sacc[nb][blk][v] * a.scale_log2 : -INFINITY;
+          const bool in = tok < lim.v[nb] && tok >= a.t_lo && ((valid >> (tok - t0)) & 1u);
+          const float sx = in ? sacc[nb][blk][v] * a.scale_log2 : -INFINITY;
           sv[4 * blk + v] = sx;
           tmax = fmaxf(tmax, sx);
         }
@@ -493,7 +534,9 @@ constexpr int kWavesPerEu = NB > 1 ? 2 : (std::is_same<KP, KeysQjl>::value && G 
 // PAGED: the token rows live in pool pages named by the block table; each tile's
 // resources cover its page (tiles start on 32-token boundaries and pages, a power
 // of two of at least 32 tokens, hold whole tiles).
-template <int G, class KP, int NB, bool PAGED>
+// SPARSE (contiguous caches, one query): split slot i reads position
+// a.sel[b][t_begin + i], staged in LDS; slots without a valid position are masked.
+template <int G, class KP, int NB, bool PAGED, bool SPARSE>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(kWavesPerEu<G, KP, NB>, kWavesPerEu<G, KP, NB>)))
 decode_mfma_kernel(MfmaDecodeArgs a) {
@@ -532,6 +575,31 @@ decode_mfma_kernel(MfmaDecodeArgs a) {
   for (int nb = 0; nb < NB; ++nb) lim.v[nb] = min(t_end, L - (a.nq - 1 - (a.c0 + 16 * nb + (lane & 15)) / a.gr));
   const int t_full = min(t_end, L - (a.nq - 1 - a.c0 / a.gr));
 
+  static_assert(!(PAGED && SPARSE), "gather mode reads contiguous caches");
+  static_assert(!SPARSE || NS == 2, "gather mode runs the two-stage ring");
+  __shared__ int spos[SPARSE ? kMfmaSparseSlots : 1];
+  __shared__ uint32_t svalid[SPARSE ? kMfmaSparseSlots / 32 : 1];  // bit j: slot j of the tile is valid
+  if constexpr (SPARSE) {
+    const int32_t* sb = a.sel + (size_t)b * a.sel_stride;
+    for (int i = threadIdx.x; i < a.per_split; i += 256) {
+      const int slot = t_begin + i;
+      const int p = slot < t_end ? sb[slot] : -1;
+      spos[i] = p >= 0 && p < a.cap ? p : -1;
+    }
+    __syncthreads();
+    for (int ti = threadIdx.x; ti < a.per_split / 32; ti += 256) {
+      uint32_t m = 0;
+      for (int j = 0; j < 32; ++j) m |= (spos[ti * 32 + j] >= 0 ? 1u : 0u) << j;
+      svalid[ti] = m;
+    }
+    __syncthreads();
+  }
+  // the tile's validity mask (gather mode; tiles at or past t_end have none)
+  auto valid_of = [&](int t) -> uint32_t {
+    if constexpr (SPARSE) return t < t_end ? svalid[(t - t_begin) >> 5] : 0u;
+    return ~0u;
+  };
+
   WaveState<KP, NB> w;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -554,7 +622,11 @@ decode_mfma_kernel(MfmaDecodeArgs a) {
   // the loads of tile t, whose table entry the caller looked up
   auto tile_at = [&](int t, int entry) {
     TileSrc<KP> s;
-    if constexpr (!PAGED) {
+    if constexpr (SPARSE) {
+      s.kr = kr;
+      s.vr = vr;
+      s.t = t < t_end ? t - t_begin : -1;  // a staged slot
+    } else if constexpr (!PAGED) {
       s.kr = kr;
       s.vr = vr;
       s.t = t < t_end ? t : a.cap;
@@ -575,14 +647,20 @@ decode_mfma_kernel(MfmaDecodeArgs a) {
   int t0 = t_begin + wave * 32;
   {
     const TileSrc<KP> s0 = tile_or_none(t0), s1 = tile_or_none(t0 + 128);
-    issue_tile<KP>(sa, lane, s0.t, s0.kr, s0.vr);
-    issue_tile<KP>(sb, lane, s1.t, s1.kr, s1.vr);
+    if constexpr (SPARSE) {
+      issue_tile_rows<KP>(sa, lane, s0.t, spos, s0.kr, s0.vr);
+      issue_tile_rows<KP>(sb, lane, s1.t, spos, s1.kr, s1.vr);
+    } else {
+      issue_tile<KP>(sa, lane, s0.t, s0.kr, s0.vr);
+      issue_tile<KP>(sb, lane, s1.t, s1.kr, s1.vr);
+    }
   }
   if constexpr (NS == 2) {
     for (; t0 < t_end; t0 += 256) {
       // the second tile of a pair may lie past t_end: all its tokens are masked
-      tile_step<G, NS, KP, NB>(w, sa, lane, t0, t_full, lim, tile_or_none(t0 + 256), a);
-      tile_step<G, NS, KP, NB>(w, sb, lane, t0 + 128, t_full, lim, tile_or_none(t0 + 384), a);
+      tile_step<G, NS, KP, NB, SPARSE>(w, sa, lane, t0, t_full, lim, tile_or_none(t0 + 256), a, spos, valid_of(t0));
+      tile_step<G, NS, KP, NB, SPARSE>(w, sb, lane, t0 + 128, t_full, lim, tile_or_none(t0 + 384), a, spos,
+                                       valid_of(t0 + 128));
     }
   } else {
     uint8_t* sc = stC + wave * kStage;
@@ -653,18 +731,18 @@ decode_mfma_kernel(MfmaDecodeArgs a) {
   }
 }
 
-template <class KP, bool PAGED>
+template <class KP, bool PAGED, bool SPARSE = false>
 int launch_g(const MfmaDecodeArgs& a, int B, int G, hipStream_t st) {
   dim3 grid(a.splits, a.H, B);
   switch (G) {
-    case 1: decode_mfma_kernel<1, KP, 1, PAGED><<<grid, 256, 0, st>>>(a); break;
-    case 2: decode_mfma_kernel<2, KP, 1, PAGED><<<grid, 256, 0, st>>>(a); break;
-    case 4: decode_mfma_kernel<4, KP, 1, PAGED><<<grid, 256, 0, st>>>(a); break;
-    case 8: decode_mfma_kernel<8, KP, 1, PAGED><<<grid, 256, 0, st>>>(a); break;
-    case 16: decode_mfma_kernel<16, KP, 1, PAGED><<<grid, 256, 0, st>>>(a); break;
+    case 1: decode_mfma_kernel<1, KP, 1, PAGED, SPARSE><<<grid, 256, 0, st>>>(a); break;
+    case 2: decode_mfma_kernel<2, KP, 1, PAGED, SPARSE><<<grid, 256, 0, st>>>(a); break;
+    case 4: decode_mfma_kernel<4, KP, 1, PAGED, SPARSE><<<grid, 256, 0, st>>>(a); break;
+    case 8: decode_mfma_kernel<8, KP, 1, PAGED, SPARSE><<<grid, 256, 0, st>>>(a); break;
+    case 16: decode_mfma_kernel<16, KP, 1, PAGED, SPARSE><<<grid, 256, 0, st>>>(a); break;
     case 32:
-      if constexpr (std::is_same<KP, KeysFp4>::value) {
-        decode_mfma_kernel<16, KP, 2, PAGED><<<grid, 256, 0, st>>>(a);
+      if constexpr (std::is_same<KP, KeysFp4>::value && !SPARSE) {
+        decode_mfma_kernel<16, KP, 2, PAGED, false><<<grid, 256, 0, st>>>(a);
         break;
       }
       return KV_EUNSUPPORTED;
@@ -677,6 +755,12 @@ int launch_g(const MfmaDecodeArgs& a, int B, int G, hipStream_t st) {
 
 int launch_decode_mfma(const MfmaDecodeArgs& a, int format, int B, int G, hipStream_t st) {
   const bool paged = a.pm.table != nullptr;
+  if (a.sel) {  // gather mode: contiguous caches
+    if (paged) return KV_EUNSUPPORTED;
+    if (format == KV_FMT_FP4) return launch_g<KeysFp4, false, true>(a, B, G, st);
+    if (format == KV_FMT_QJL1_FP4V) return launch_g<KeysQjl, false, true>(a, B, G, st);
+    return KV_EUNSUPPORTED;
+  }
   if (format == KV_FMT_FP4) return paged ? launch_g<KeysFp4, true>(a, B, G, st) : launch_g<KeysFp4, false>(a, B, G, st);
   if (format == KV_FMT_QJL1_FP4V)
     return paged ? launch_g<KeysQjl, true>(a, B, G, st) : launch_g<KeysQjl, false>(a, B, G, st);

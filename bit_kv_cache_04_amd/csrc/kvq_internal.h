@@ -99,6 +99,11 @@ constexpr int kLatentSparseSlots = 512;
 inline bool latent_sparse_ok(const kv_layout& L, int num_q_heads, int q_dtype) {
   return latent_fast_path_ok(L, num_q_heads, 1, q_dtype) && L.page_tokens == 0;
 }
+// So does that of a contiguous FP4 or QJL cache on the FP4 / QJL matrix-core kernel.
+constexpr int kMfmaSparseSlots = 512;
+inline bool mfma_sparse_ok(const kv_layout& L, int num_q_heads, int q_dtype) {
+  return mfma_fast_path_ok(L, num_q_heads, 1, q_dtype) && L.page_tokens == 0 && !L.sink_tokens && !L.recent_tokens;
+}
 // HSI selection (kvq_hsi.hip).
 size_t hsi_candidates_workspace(int batch, int stride, int blk);
 int launch_hsi_candidates(const float* scores, int batch, int stride, const int32_t* seq_lens, int blk,

@@ -169,3 +169,32 @@ def test_sparse_latent_kernel_shapes(hq, n, cap):
     err = row_rel_err(out.cpu().numpy(), ref)
     print(f"  max row rel err {err.max():.3e}", flush=True)
     assert err.max() <= RTOL
+
+
+@pytest.mark.parametrize("fmt,G,n", [("fp4", 1, 1500), ("fp4", 16, 700), ("qjl1", 8, 600), ("fp4", 2, 40),
+                                     ("qjl1", 1, 513)])
+def test_sparse_mfma_kernel_shapes(fmt, G, n):
+    """The FP4 / QJL matrix-core kernel's gather mode: query-group sizes, several
+    splits of up to 512 staged positions, ragged tiles and skipped entries."""
+    cfg = SMALL[fmt].scaled(hq=2 * G, hkv=2, context=3000)
+    print(f"[sparse mfma] {fmt} G={G} n={n}", flush=True)
+    cache = new_cache(cfg)
+    K, V = inputs(cfg)
+    cache.append(K, V, 0)
+    rng = np.random.default_rng(G * 1000 + n)
+    cap = n + 8
+    sel = np.full((cfg.batch, cap), -1, np.int32)
+    picks = [np.sort(rng.choice(cfg.context, n, replace=False)).astype(np.int32),
+             np.sort(rng.choice(cfg.context, max(1, n // 5), replace=False)).astype(np.int32)]
+    for b, p in enumerate(picks):
+        sel[b, :p.size] = p
+    sel[1, picks[1].size] = cfg.context + 3  # outside the cache: skipped
+    lens = np.array([n, picks[1].size + 1], np.int32)
+    q = synth.make_queries(cfg, device="cuda")
+    out = cache.decode_sparse(q, torch.from_numpy(sel).cuda(), torch.from_numpy(lens).cuda(), softmax_scale(cfg))
+    consts = oracle_constants(cfg)
+    enc = oracle_encode(cfg, host64(K), host64(V), consts)
+    ref = decode_attention_sparse(fmt, enc, host64(q), picks, softmax_scale(cfg), cfg.hkv, consts)
+    err = row_rel_err(out.cpu().numpy(), ref)
+    print(f"  max row rel err {err.max():.3e}", flush=True)
+    assert err.max() <= RTOL
