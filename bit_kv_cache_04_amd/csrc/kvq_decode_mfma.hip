@@ -220,9 +220,11 @@ struct KeysQjl {
   template <int G>
   __device__ static void load_q(Q& q, const MfmaDecodeArgs& a, int b, int h, int q4, int c, int) {
     constexpr int NS = kSlots<G>, NP = 4 / NS;
-    const int slot = c / G;
-    const bool live = slot < NS;
-    const size_t qrow = (size_t)b * a.Hq + (size_t)h * G + c % G;
+    // column c holds piece slot c / G of pair c0 + c % G = query token j, head g
+    const int slot = c / G, pair = a.c0 + c % G;
+    const bool live = slot < NS && c % G < a.ncol;
+    const size_t qrow =
+        ((size_t)b * a.nq + (live ? pair / a.gr : 0)) * a.Hq + (size_t)h * a.gr + (live ? pair % a.gr : 0);
     const uint8_t* pc = a.qpieces + qrow * kQjlPieceBytes;
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
@@ -570,9 +572,11 @@ decode_mfma_kernel(MfmaDecodeArgs a) {
   // this lane's column 16 nb + lane % 16 is query token j = (c0 + column) / gr,
   // which sees the first L - (nq - 1 - j) tokens; a tile below t_full is whole
   // for every column of the launch
+  // (QJL keys: column c is pair c0 + c % G, its piece slots replicated)
+  const int lane_col = std::is_same<KP, KeysQjl>::value ? (lane & 15) % G : (lane & 15);
   Limits<NB> lim;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) lim.v[nb] = min(t_end, L - (a.nq - 1 - (a.c0 + 16 * nb + (lane & 15)) / a.gr));
+  for (int nb = 0; nb < NB; ++nb) lim.v[nb] = min(t_end, L - (a.nq - 1 - (a.c0 + 16 * nb + lane_col) / a.gr));
   const int t_full = min(t_end, L - (a.nq - 1 - a.c0 / a.gr));
 
   static_assert(!(PAGED && SPARSE), "gather mode reads contiguous caches");

@@ -100,9 +100,10 @@ bool mfma_fast_path_ok(const kv_layout& L, int num_q_heads, int nq, int q_dtype)
   const int G = num_q_heads / L.num_kv_heads;
   const bool g_ok = G == 1 || G == 2 || G == 4 || G == 8 || G == 16;
   if (L.head_dim != 128) return false;
-  // several queries: FP4 keys only, every (query, head) pair a column of its own,
-  // 16 columns per launch
-  if (nq > 1) return L.format == KV_FMT_FP4 && q_dtype == KV_DT_BF16;
+  // several queries: every (query, head) pair a column of its own, 16 columns per
+  // launch (FP4 keys: 32 in two blocks)
+  if (nq > 1)
+    return (L.format == KV_FMT_FP4 && q_dtype == KV_DT_BF16) || (L.format == KV_FMT_QJL1_FP4V && L.qjl_m == 128);
   if (!g_ok) return false;
   if (L.format == KV_FMT_FP4) return q_dtype == KV_DT_BF16;
   if (L.format == KV_FMT_QJL1_FP4V) return L.qjl_m == 128;

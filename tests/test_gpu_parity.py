@@ -274,15 +274,17 @@ def test_growing_logits_rescale(fmt):
 
 
 MULTI = [("fp4", 2), ("fp4", 3), ("fp4", 4), ("fp4", 5), ("fp4", 9), ("kivi2", 3), ("turbo", 2), ("qjl1", 5),
+         ("qjl1", 2), ("qjl1", 3),
          ("latent", 2)]
 
 
 @pytest.mark.parametrize("fmt,nq", MULTI)
 def test_multi_query_decode_matches_oracle(fmt, nq):
     """nq query tokens per sequence, query j over the first L - (nq - 1 - j)
-    tokens: FP4 runs on the matrix cores, 16 (query, head) pairs per launch (G = 4:
-    nq = 3 fills 12 of 16 columns, nq = 5 takes 16 + 4, nq = 9 takes 16 + 16 + 4),
-    the other formats on the general kernel.  Ragged lengths, one of them nq."""
+    tokens: FP4 and QJL keys run on the matrix cores, 16 (query, head) pairs per
+    launch (G = 4: nq = 3 fills 12 of 16 columns, nq = 5 takes 16 + 4, nq = 9 takes
+    16 + 16 + 4; QJL columns repeat a pair per piece slot), the other formats on the
+    general kernel.  Ragged lengths, one of them nq."""
     cfg = SMALL[fmt]
     print(f"[multi-query] {fmt} nq={nq} {cfg}", flush=True)
     cache, K, V = _build(cfg)
