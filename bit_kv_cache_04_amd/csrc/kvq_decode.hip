@@ -728,9 +728,12 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     f.part = part;
     f.splits = plan.splits;
     f.per_split = plan.tokens_per_split;
+    f.nq = nq;
     if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), st) != hipSuccess) return KV_EDEVICE;
-    int rc = launch_decode_latent(f, B, st);
-    if (rc != KV_OK) return rc;
+    for (f.c0 = 0; f.c0 < nq; ++f.c0) {  // one pass over the cache per query token
+      int rc = launch_decode_latent(f, B, st);
+      if (rc != KV_OK) return rc;
+    }
     if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess) return KV_EDEVICE;
     launch_merge(part, rows, part_splits, L.head_dim, L.format, c->rot, out, st);
     return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
@@ -773,9 +776,12 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     f.part = part;
     f.splits = plan.splits;
     f.per_split = plan.tokens_per_split;
+    f.nq = nq;
     if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), st) != hipSuccess) return KV_EDEVICE;
-    int rc = launch_decode_turbo(f, B, num_q_heads / L.num_kv_heads, st);
-    if (rc != KV_OK) return rc;
+    for (f.qj = 0; f.qj < nq; ++f.qj) {  // one pass over the cache per query token
+      int rc = launch_decode_turbo(f, B, num_q_heads / L.num_kv_heads, st);
+      if (rc != KV_OK) return rc;
+    }
     if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess) return KV_EDEVICE;
     launch_merge(part, rows, part_splits, L.head_dim, L.format, c->rot, out, st);
     return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;

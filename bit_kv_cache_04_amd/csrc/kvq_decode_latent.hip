@@ -177,7 +177,10 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) decode_latent_kernel(MfmaDecodeArgs a
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int split = blockIdx.x, b = blockIdx.y;
-  const int L = min(min(a.seq_lens[b], a.max_len), a.cap);
+  // several queries per sequence: this launch takes query j = a.c0 of a.nq,
+  // which sees the first L - (nq - 1 - j) tokens
+  const int L = min(min(a.seq_lens[b], a.max_len), a.cap) - (a.nq - 1 - a.c0);
+  const size_t qrow0 = ((size_t)b * a.nq + a.c0) * a.Hq;  // its first query / output row
   const int t_begin = split * a.per_split;
   const int t_end = min(L, t_begin + a.per_split);
   const int col = lane & 31, half = lane >> 5;
@@ -204,7 +207,7 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) decode_latent_kernel(MfmaDecodeArgs a
   h8_t ql[32];
   b8_t qr[4];
   {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + 32 * wave + col) * (kLat + kRope);
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (qrow0 + 32 * wave + col) * (kLat + kRope);
 #pragma unroll
     for (int s = 0; s < 32; ++s) {
       const uint4 raw = *reinterpret_cast<const uint4*>(qp + 16 * s + 8 * half);
@@ -405,7 +408,7 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) decode_latent_kernel(MfmaDecodeArgs a
 
   // ---------------- partial result of this split
   l_run += __shfl_xor(l_run, 32);
-  const size_t row0 = (size_t)b * a.Hq + 32 * wave;
+  const size_t row0 = qrow0 + 32 * wave;
   const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   const int col_e = lane_e & 31, half_e = lane_e >> 5;
   if (half_e == 0) {

@@ -281,7 +281,10 @@ __attribute__((amdgpu_waves_per_eu(KVQ_TURBO_WAVES_PER_EU, KVQ_TURBO_WAVES_PER_E
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const size_t bh = (size_t)b * a.H + h;
-  const int L = min(min(a.seq_lens[b], a.max_len), a.cap);
+  // several queries per sequence: this launch takes query j = a.qj of a.nq,
+  // which sees the first L - (nq - 1 - j) tokens
+  const int L = min(min(a.seq_lens[b], a.max_len), a.cap) - (a.nq - 1 - a.qj);
+  const size_t qrow0 = ((size_t)b * a.nq + a.qj) * a.Hq;  // its first query / output row
   const int t_begin = split * a.per_split;
   const int t_end = min(L, t_begin + a.per_split);
   const int q4 = lane >> 4, c = lane & 15;
@@ -304,7 +307,7 @@ __attribute__((amdgpu_waves_per_eu(KVQ_TURBO_WAVES_PER_EU, KVQ_TURBO_WAVES_PER_E
     // pieces of the key-product operands (layout of prepared_query_pieces)
     const int head = c % 8;
     const bool live = head < G;
-    const size_t qrow = (size_t)b * a.Hq + (size_t)h * G + (live ? head : 0);
+    const size_t qrow = qrow0 + (size_t)h * G + (live ? head : 0);
     const float* qp = a.q + qrow * 256;
     const uint8_t* pc = a.qpieces + qrow * kTurboPieceBytes;
 #pragma unroll
@@ -397,7 +400,7 @@ __attribute__((amdgpu_waves_per_eu(KVQ_TURBO_WAVES_PER_EU, KVQ_TURBO_WAVES_PER_E
     }
   }
   __syncthreads();
-  const size_t row0 = (size_t)b * a.Hq + (size_t)h * G;
+  const size_t row0 = qrow0 + (size_t)h * G;
   for (int e = tid_e; e < G * 128; e += 256) {
     const int hh = e >> 7, ch = e & 127;
     float M = -INFINITY;

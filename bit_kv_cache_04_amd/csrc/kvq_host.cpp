@@ -82,12 +82,14 @@ int value_width(const kv_layout* L) { return L->head_dim; }
 
 bool turbo_fast_path_ok(const kv_layout& L, int num_q_heads, int nq) {
   const int G = num_q_heads / L.num_kv_heads;
-  return nq == 1 && L.format == KV_FMT_TURBO && L.head_dim == 128 && L.qjl_m == 128 && L.lm_bits == 2 &&
+  (void)nq;  // several queries: one launch per query
+  return L.format == KV_FMT_TURBO && L.head_dim == 128 && L.qjl_m == 128 && L.lm_bits == 2 &&
          (G == 1 || G == 2 || G == 4 || G == 8) && (size_t)L.capacity * 32 < (size_t(1) << 31);
 }
 
 bool latent_fast_path_ok(const kv_layout& L, int num_q_heads, int nq, int q_dtype) {
-  return nq == 1 && L.format == KV_FMT_LATENT_FP4 && L.head_dim == 512 && L.rope_dim == 64 && q_dtype == KV_DT_BF16 &&
+  (void)nq;  // several queries: one launch per query
+  return L.format == KV_FMT_LATENT_FP4 && L.head_dim == 512 && L.rope_dim == 64 && q_dtype == KV_DT_BF16 &&
          (num_q_heads == 32 || num_q_heads == 64 || num_q_heads == 128) &&
          (size_t)L.capacity * 256 < (size_t(1) << 31);
 }

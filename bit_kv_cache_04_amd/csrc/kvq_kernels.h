@@ -34,7 +34,8 @@ struct MfmaDecodeArgs {
   int splits, per_split;
   // nq query tokens per sequence of gr query heads per KV head, numbered
   // c = j * gr + g (query j, head g; q [B][nq][Hq][.]); one launch takes the
-  // ncol of them from c0 as its columns.  nq = 1 for QJL keys and the latent.
+  // ncol of them from c0 as its columns.  The latent kernel takes one query per
+  // launch: query c0 of nq (its heads are the columns).
   int nq, gr, c0, ncol;
   // packed tokens [t_lo, L - recent) of a sequence of length L (split s from
   // t_lo + s * per_split); partial rows hold part_splits splits
@@ -59,8 +60,9 @@ struct TurboDecodeArgs {
   const int32_t* seq_lens;
   int max_len, H, cap, Hq;
   float scale_log2, kappa;
-  float* part;  // [B][Hq][splits][130]
+  float* part;  // [B][nq][Hq][splits][130]
   int splits, per_split;
+  int nq, qj;  // query tokens per sequence; the one this launch takes
 };
 
 int launch_decode_turbo(const TurboDecodeArgs& a, int B, int G, hipStream_t st);

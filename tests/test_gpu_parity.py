@@ -274,7 +274,7 @@ def test_growing_logits_rescale(fmt):
 
 
 MULTI = [("fp4", 2), ("fp4", 3), ("fp4", 4), ("fp4", 5), ("fp4", 9), ("kivi2", 3), ("turbo", 2), ("qjl1", 5),
-         ("qjl1", 2), ("qjl1", 3),
+         ("qjl1", 2), ("qjl1", 3), ("turbo", 5), ("latent", 3),
          ("latent", 2)]
 
 
