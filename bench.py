@@ -339,12 +339,12 @@ def main():
         # the dominant kernel is the sparse decode on the general (fp32 vector) kernel:
         # per selected position and query head, key_width + head_dim multiply-adds
         # (the latent cache's gather kernel runs them on the fp16 matrix cores); the
-        # FP4 / QJL gather kernels are priced by the packed bytes they gather, the
-        # general kernel (other formats) against the fp32 vector peak
+        # FP4 / QJL / TurboQuant gather kernels are priced by the packed bytes they
+        # gather, the general kernel (KIVI-2) against the fp32 vector peak
         res["metric"] = "HSI sparse decode step: bytes read GB/s + query-tokens/s at fixed context"
         res["config"].update(hsi={"block": HSI_BLOCK, "top_blocks": HSI_TOP_BLOCKS, "top_k": HSI_TOP_K,
                                   "selected_positions": n_sel})
-        if cfg.fmt in ("fp4", "qjl1"):
+        if cfg.fmt in ("fp4", "qjl1", "turbo"):
             gathered = kvq.kv_bytes_per_token(cache.layout, 1) * n_sel
             ach = gathered / (dec_ms * 1e-3) / 1e9
             res["roofline"] = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",

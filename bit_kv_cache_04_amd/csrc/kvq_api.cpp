@@ -131,7 +131,7 @@ extern "C" int kv_decode_attention_sparse(const kv_cache* c, const void* q, int3
   // the matrix-core kernels stage a split's positions: at most 512 per split, in
   // whole 128-token steps (FP4 / QJL) or 64-token steps (latent)
   const bool latent = latent_sparse_ok(L, num_q_heads, q_dtype);
-  const bool mfma = !latent && mfma_sparse_ok(L, num_q_heads, q_dtype);
+  const bool mfma = !latent && (mfma_sparse_ok(L, num_q_heads, q_dtype) || turbo_sparse_ok(L, num_q_heads));
   SplitPlan plan = plan_splits(&L, num_q_heads, 1, q_dtype, sel_cap, req, !latent && !mfma);
   static_assert(kLatentSparseSlots == kMfmaSparseSlots, "one staging bound");
   if ((latent || mfma) && plan.tokens_per_split > kMfmaSparseSlots) {

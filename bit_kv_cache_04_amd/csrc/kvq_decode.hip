@@ -739,7 +739,7 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
   }
   const bool mfma = sel ? mfma_sparse_ok(L, num_q_heads, q_dtype) : mfma_fast_path_ok(L, num_q_heads, nq, q_dtype);
-  const bool turbo = !sel && turbo_fast_path_ok(L, num_q_heads, nq);
+  const bool turbo = sel ? turbo_sparse_ok(L, num_q_heads) : turbo_fast_path_ok(L, num_q_heads, nq);
   // FP4 keys read the caller's bf16 queries as they are; every other format
   // first prepares its fp32 query (projection / rotation)
   uint8_t* qpieces = turbo || (mfma && L.format == KV_FMT_QJL1_FP4V)
@@ -764,6 +764,8 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     f.v_norm = static_cast<const uint16_t*>(c->buf[KV_BUF_V_NORM]);
     f.levels = c->lm_levels;
     f.pm = page_map(c);
+    f.sel = sel;
+    f.sel_stride = sel_stride;
     f.q = qv;
     f.qpieces = qpieces;
     f.seq_lens = seq_lens;

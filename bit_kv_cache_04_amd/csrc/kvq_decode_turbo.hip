@@ -111,6 +111,22 @@ __device__ __forceinline__ void issue_tile(uint8_t* st, int lane, int t0, const 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vn, (lds_ptr_t)(st + kSVN), 2, nb, 0, 0, 0);
 }
 
+// Gather form of issue_tile: staged slot rel starts the tile (rel < 0: none);
+// lane rows: slot lane / 2 (codes), slot lane for lanes < 32 (sketch, norms).
+// The number of loads is issue_tile's.
+__device__ __forceinline__ void issue_tile_rows(uint8_t* st, int lane, int rel, const int* pos, const Res& r) {
+  const int pa = rel < 0 ? -1 : pos[rel + (lane >> 1)];
+  const int pn = rel < 0 || lane >= 32 ? -1 : pos[rel + lane];
+  const uint32_t c16 = pa < 0 ? ~0u : (uint32_t)pa * 32u + (lane & 1) * 16;
+  const uint32_t s16 = pn < 0 ? ~0u : (uint32_t)pn * 16u, nb = pn < 0 ? ~0u : (uint32_t)pn * 2u;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.kc, (lds_ptr_t)(st + kSK), 16, c16, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.sk, (lds_ptr_t)(st + kSS), 16, s16, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.kn, (lds_ptr_t)(st + kSN), 2, nb, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.kr, (lds_ptr_t)(st + kSR), 2, nb, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vc, (lds_ptr_t)(st + kSV), 16, c16, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vn, (lds_ptr_t)(st + kSVN), 2, nb, 0, 0, 0);
+}
+
 struct Consts {
   float a0;            // level of code 0
   uint32_t t_lo, t_hi;  // low / high bytes of the four levels as fp16, byte c for code c
@@ -146,9 +162,12 @@ struct WaveState {
 };
 
 // One 32-token tile (see tile_step of the FP4 kernel for the ring protocol).
-template <int G>
+// SP: gather mode (nx.t a staged slot of pos); `valid` bit j: slot j of the tile
+// holds a position.
+template <int G, bool SP = false>
 __device__ __forceinline__ void tile_step(WaveState<G>& w, uint8_t* st, int lane, int t0, int t_end,
-                                          const TileSrc& nx, const TurboDecodeArgs& a, const Consts& k) {
+                                          const TileSrc& nx, const TurboDecodeArgs& a, const Consts& k,
+                                          const int* pos = nullptr, uint32_t valid = ~0u) {
   const int q4 = lane >> 4, c = lane & 15;
   // This stage's tile has landed once at most the other stage's refill (the
   // kDmaPerTile loads issued after it) is outstanding.  Waited for explicitly:
@@ -180,7 +199,8 @@ __device__ __forceinline__ void tile_step(WaveState<G>& w, uint8_t* st, int lane
   const i2_t vx1 = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
       (__attribute__((address_space(3))) i2_t*)(st + kSV + vo + 16));
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the stage may be refilled
-  issue_tile(st, lane, nx.t, nx.r);
+  if constexpr (SP) issue_tile_rows(st, lane, nx.t, pos, nx.r);
+  else issue_tile(st, lane, nx.t, nx.r);
 
   // ---- logits: S^T = K Q^T, code-bit steps then sketch steps, per 16-token block
   f4_t lm[2], qj[2];
@@ -209,7 +229,7 @@ __device__ __forceinline__ void tile_step(WaveState<G>& w, uint8_t* st, int lane
     const float n = f16_to_f32((uint16_t)(&nk.x)[v]), gm = f16_to_f32((uint16_t)(&nr.x)[v]);
     const float logit = n * ((l_ + w.cst) + a.kappa * gm * fmaf(2.f, q_, -w.sqs));
     const int tok = t0 + 8 * q4 + (upper ? 4 : 0) + v;
-    float s = tok < t_end ? logit * a.scale_log2 : -INFINITY;
+    float s = tok < t_end && ((valid >> (tok - t0)) & 1u) ? logit * a.scale_log2 : -INFINITY;
     if ((c & 7) >= G) s = 0.f;  // columns past the group hold no head: keep them finite
     sv[v] = s;
     tmax = fmaxf(tmax, s);
@@ -268,7 +288,9 @@ __device__ __forceinline__ void tile_step(WaveState<G>& w, uint8_t* st, int lane
 #endif
 
 // PAGED: token rows in pool pages named by the block table, resources per tile.
-template <int G, bool PAGED>
+// SPARSE (contiguous caches): split slot i reads position a.sel[b][t_begin + i],
+// staged in LDS; slots without a valid position are masked.
+template <int G, bool PAGED, bool SPARSE>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(KVQ_TURBO_WAVES_PER_EU, KVQ_TURBO_WAVES_PER_EU))) decode_turbo_kernel(TurboDecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t stA[4][kStage];
@@ -348,12 +370,37 @@ __attribute__((amdgpu_waves_per_eu(KVQ_TURBO_WAVES_PER_EU, KVQ_TURBO_WAVES_PER_E
                nrows * 32};
   };
   const Res res = res_at(bh * a.cap, a.cap);
+  static_assert(!(PAGED && SPARSE), "gather mode reads contiguous caches");
+  __shared__ int spos[SPARSE ? kMfmaSparseSlots : 1];
+  __shared__ uint32_t svalid[SPARSE ? kMfmaSparseSlots / 32 : 1];
+  if constexpr (SPARSE) {
+    const int32_t* sbp = a.sel + (size_t)b * a.sel_stride;
+    for (int i = threadIdx.x; i < a.per_split; i += 256) {
+      const int slot = t_begin + i;
+      const int p = slot < t_end ? sbp[slot] : -1;
+      spos[i] = p >= 0 && p < a.cap ? p : -1;
+    }
+    __syncthreads();
+    for (int ti = threadIdx.x; ti < a.per_split / 32; ti += 256) {
+      uint32_t m = 0;
+      for (int j = 0; j < 32; ++j) m |= (spos[ti * 32 + j] >= 0 ? 1u : 0u) << j;
+      svalid[ti] = m;
+    }
+    __syncthreads();
+  }
+  auto valid_of = [&](int t) -> uint32_t {
+    if constexpr (SPARSE) return t < t_end ? svalid[(t - t_begin) >> 5] : 0u;
+    return ~0u;
+  };
   uint8_t* sa = stA[wave];
   uint8_t* sb = stB[wave];
   // a missing tile reads past the end of its resources: zeros, no memory traffic
   auto tile_or_none = [&](int t) {
     TileSrc s;
-    if constexpr (!PAGED) {
+    if constexpr (SPARSE) {
+      s.r = res;
+      s.t = t < t_end ? t - t_begin : -1;  // a staged slot
+    } else if constexpr (!PAGED) {
       s.r = res;
       s.t = t < t_end ? t : a.cap;
     } else {
@@ -366,12 +413,17 @@ __attribute__((amdgpu_waves_per_eu(KVQ_TURBO_WAVES_PER_EU, KVQ_TURBO_WAVES_PER_E
   int t0 = t_begin + wave * 32;
   {
     const TileSrc s0 = tile_or_none(t0), s1 = tile_or_none(t0 + 128);
-    issue_tile(sa, lane, s0.t, s0.r);
-    issue_tile(sb, lane, s1.t, s1.r);
+    if constexpr (SPARSE) {
+      issue_tile_rows(sa, lane, s0.t, spos, s0.r);
+      issue_tile_rows(sb, lane, s1.t, spos, s1.r);
+    } else {
+      issue_tile(sa, lane, s0.t, s0.r);
+      issue_tile(sb, lane, s1.t, s1.r);
+    }
   }
   for (; t0 < t_end; t0 += 256) {
-    tile_step<G>(w, sa, lane, t0, t_end, tile_or_none(t0 + 256), a, k);
-    tile_step<G>(w, sb, lane, t0 + 128, t_end, tile_or_none(t0 + 384), a, k);
+    tile_step<G, SPARSE>(w, sa, lane, t0, t_end, tile_or_none(t0 + 256), a, k, spos, valid_of(t0));
+    tile_step<G, SPARSE>(w, sb, lane, t0 + 128, t_end, tile_or_none(t0 + 384), a, k, spos, valid_of(t0 + 128));
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
@@ -426,14 +478,14 @@ __attribute__((amdgpu_waves_per_eu(KVQ_TURBO_WAVES_PER_EU, KVQ_TURBO_WAVES_PER_E
 }  // namespace
 
 namespace {
-template <bool PAGED>
+template <bool PAGED, bool SPARSE = false>
 int launch_turbo(const TurboDecodeArgs& a, int B, int G, hipStream_t st) {
   dim3 grid(a.splits, a.H, B);
   switch (G) {
-    case 1: decode_turbo_kernel<1, PAGED><<<grid, 256, 0, st>>>(a); break;
-    case 2: decode_turbo_kernel<2, PAGED><<<grid, 256, 0, st>>>(a); break;
-    case 4: decode_turbo_kernel<4, PAGED><<<grid, 256, 0, st>>>(a); break;
-    case 8: decode_turbo_kernel<8, PAGED><<<grid, 256, 0, st>>>(a); break;
+    case 1: decode_turbo_kernel<1, PAGED, SPARSE><<<grid, 256, 0, st>>>(a); break;
+    case 2: decode_turbo_kernel<2, PAGED, SPARSE><<<grid, 256, 0, st>>>(a); break;
+    case 4: decode_turbo_kernel<4, PAGED, SPARSE><<<grid, 256, 0, st>>>(a); break;
+    case 8: decode_turbo_kernel<8, PAGED, SPARSE><<<grid, 256, 0, st>>>(a); break;
     default: return KV_EUNSUPPORTED;
   }
   return KV_OK;
@@ -441,6 +493,7 @@ int launch_turbo(const TurboDecodeArgs& a, int B, int G, hipStream_t st) {
 }  // namespace
 
 int launch_decode_turbo(const TurboDecodeArgs& a, int B, int G, hipStream_t st) {
+  if (a.sel) return a.pm.table ? KV_EUNSUPPORTED : launch_turbo<false, true>(a, B, G, st);
   return a.pm.table ? launch_turbo<true>(a, B, G, st) : launch_turbo<false>(a, B, G, st);
 }
 

@@ -104,6 +104,10 @@ constexpr int kMfmaSparseSlots = 512;
 inline bool mfma_sparse_ok(const kv_layout& L, int num_q_heads, int q_dtype) {
   return mfma_fast_path_ok(L, num_q_heads, 1, q_dtype) && L.page_tokens == 0 && !L.sink_tokens && !L.recent_tokens;
 }
+// ... and that of a contiguous TurboQuant cache on its matrix-core kernel.
+inline bool turbo_sparse_ok(const kv_layout& L, int num_q_heads) {
+  return turbo_fast_path_ok(L, num_q_heads, 1) && L.page_tokens == 0;
+}
 // HSI selection (kvq_hsi.hip).
 size_t hsi_candidates_workspace(int batch, int stride, int blk);
 int launch_hsi_candidates(const float* scores, int batch, int stride, const int32_t* seq_lens, int blk,

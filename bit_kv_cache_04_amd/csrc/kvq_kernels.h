@@ -63,6 +63,10 @@ struct TurboDecodeArgs {
   float* part;  // [B][nq][Hq][splits][130]
   int splits, per_split;
   int nq, qj;  // query tokens per sequence; the one this launch takes
+  // sparse decode: slot i of sequence b reads position sel[b * sel_stride + i]
+  // (seq_lens counts slots, at most kMfmaSparseSlots per split); nullptr: dense
+  const int32_t* sel;
+  int sel_stride;
 };
 
 int launch_decode_turbo(const TurboDecodeArgs& a, int B, int G, hipStream_t st);

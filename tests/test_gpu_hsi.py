@@ -172,9 +172,9 @@ def test_sparse_latent_kernel_shapes(hq, n, cap):
 
 
 @pytest.mark.parametrize("fmt,G,n", [("fp4", 1, 1500), ("fp4", 16, 700), ("qjl1", 8, 600), ("fp4", 2, 40),
-                                     ("qjl1", 1, 513)])
+                                     ("qjl1", 1, 513), ("turbo", 8, 1500), ("turbo", 1, 300), ("turbo", 4, 64)])
 def test_sparse_mfma_kernel_shapes(fmt, G, n):
-    """The FP4 / QJL matrix-core kernel's gather mode: query-group sizes, several
+    """The FP4 / QJL and TurboQuant matrix-core kernels' gather modes: query-group sizes, several
     splits of up to 512 staged positions, ragged tiles and skipped entries."""
     cfg = SMALL[fmt].scaled(hq=2 * G, hkv=2, context=3000)
     print(f"[sparse mfma] {fmt} G={G} n={n}", flush=True)
