@@ -116,8 +116,7 @@ __device__ void radix_threshold(const KeyAt& key_at, int n, int k, uint32_t& thr
 // into it.  Returns the total weight kept.
 template <class KeyAt, class Weight, class Emit>
 __device__ int emit_selected(const KeyAt& key_at, const Weight& weight, const Emit& emit, int n, uint32_t thr,
-                             int take_eq, uint32_t* chunk = nullptr) {
-  int run_eq = 0, run_out = 0;
+                             int take_eq, uint32_t* chunk = nullptr, int run_eq = 0, int run_out = 0) {
   for (int base = 0; base < n; base += kSelThreads * kPer) {
     const int i0 = base + threadIdx.x * kPer;
     if (chunk) {
@@ -250,10 +249,201 @@ __global__ void __launch_bounds__(kSelThreads) hsi_select_kernel(const float* __
   if (threadIdx.x == 0) sel_n[b] = total;
 }
 
+// ---------------------------------------------------------------- many workgroups per sequence
+//
+// For long sequences (more than kSelLdsKeys blocks) the pool is selected by
+// kChunk-key chunks, one workgroup each, in kernels that follow each other on
+// the stream: four histogram passes into a global histogram, each closed by a
+// one-workgroup pick of the bin; then per-chunk counts, a scan over chunks and
+// an ordered emit per chunk.  State per sequence (in the workspace):
+//   st[0] prefix, st[1] keys still to take, st[2] 1 when every block is kept.
+constexpr int kChunk = kSelThreads * kPer;  // keys per workgroup
+
+__device__ __forceinline__ int blocks_of(const int32_t* seq_lens, int b, int stride, int blk) {
+  return (min(max(seq_lens[b], 0), stride) + blk - 1) / blk;
+}
+
+__global__ void __launch_bounds__(256) hsi_multi_init_kernel(const int32_t* __restrict__ seq_lens, int stride,
+                                                             int blk, int top_blocks, int* __restrict__ ghist,
+                                                             int* __restrict__ state) {
+  const int b = blockIdx.x;
+  ghist[(size_t)b * 256 + threadIdx.x] = 0;
+  if (threadIdx.x == 0) {
+    const int nb = blocks_of(seq_lens, b, stride, blk);
+    state[4 * b] = 0;
+    state[4 * b + 1] = min(top_blocks, nb);
+    state[4 * b + 2] = top_blocks >= nb ? 1 : 0;
+  }
+}
+
+// Histogram pass: chunk blockIdx.x of sequence blockIdx.y, keys matching the
+// prefix so far in their top 8 * pass bits.
+__global__ void __launch_bounds__(kSelThreads) hsi_multi_hist_kernel(const uint32_t* __restrict__ keys, int nb_stride,
+                                                                     const int32_t* __restrict__ seq_lens, int stride,
+                                                                     int blk, int pass, int* __restrict__ ghist,
+                                                                     const int* __restrict__ state) {
+  __shared__ int hist[256];
+  const int b = blockIdx.y;
+  if (state[4 * b + 2]) return;  // every block kept
+  const int nb = blocks_of(seq_lens, b, stride, blk);
+  const int base = blockIdx.x * kChunk;
+  if (base >= nb) return;
+  const uint32_t prefix = (uint32_t)state[4 * b];
+  const int shift = 24 - 8 * pass;
+  const uint32_t mask = pass == 0 ? 0u : ~0u << (32 - 8 * pass);
+  if (threadIdx.x < 256) hist[threadIdx.x] = 0;
+  __syncthreads();
+  const uint32_t* kb = keys + (size_t)b * nb_stride;
+  uint32_t u[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = base + j * kSelThreads + threadIdx.x;
+    u[j] = i < nb ? kb[i] : 0u;
+  }
+  int run_bin = -1, run_cnt = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = base + j * kSelThreads + threadIdx.x;
+    const int bin = i < nb && (u[j] & mask) == prefix ? (int)((u[j] >> shift) & 255u) : -1;
+    if (bin != run_bin) {
+      if (run_cnt) atomicAdd(&hist[run_bin], run_cnt);
+      run_bin = bin;
+      run_cnt = 0;
+    }
+    run_cnt += bin >= 0;
+  }
+  if (run_cnt) atomicAdd(&hist[run_bin], run_cnt);
+  __syncthreads();
+  if (threadIdx.x < 256 && hist[threadIdx.x]) atomicAdd(&ghist[(size_t)b * 256 + threadIdx.x], hist[threadIdx.x]);
+}
+
+// Close a pass: the bin holding the k-th largest key extends the prefix; the
+// histogram is cleared for the next pass.
+__global__ void __launch_bounds__(256) hsi_multi_pick_kernel(int pass, int* __restrict__ ghist,
+                                                             int* __restrict__ state) {
+  __shared__ int h[256];
+  const int b = blockIdx.x;
+  if (state[4 * b + 2]) return;
+  const int t = threadIdx.x;
+  h[t] = ghist[(size_t)b * 256 + 255 - t];  // bins from the top
+  ghist[(size_t)b * 256 + 255 - t] = 0;
+  __syncthreads();
+  if (t == 0) {
+    const int krem = state[4 * b + 1];
+    int before = 0, i = 0;
+    for (; i < 255; ++i) {
+      if (before + h[i] >= krem) break;
+      before += h[i];
+    }
+    state[4 * b] = (int)((uint32_t)state[4 * b] | ((uint32_t)(255 - i) << (24 - 8 * pass)));
+    state[4 * b + 1] = krem - before;
+  }
+}
+
+// Per-chunk counts under the final threshold: equal keys, the weight of larger
+// keys, and whether the sequence's last (clipped) block is an equal key here.
+__global__ void __launch_bounds__(kSelThreads) hsi_multi_count_kernel(const uint32_t* __restrict__ keys, int nb_stride,
+                                                                      const int32_t* __restrict__ seq_lens, int stride,
+                                                                      int blk, const int* __restrict__ state,
+                                                                      int* __restrict__ counts, int nchunks) {
+  const int b = blockIdx.y;
+  const int L = min(max(seq_lens[b], 0), stride);
+  const int nb = (L + blk - 1) / blk;
+  const int base = blockIdx.x * kChunk;
+  const bool all = state[4 * b + 2] != 0;
+  const uint32_t thr = all ? 0u : (uint32_t)state[4 * b];
+  const uint32_t* kb = keys + (size_t)b * nb_stride;
+  int c_eq = 0, c_w = 0, last_eq = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = base + j * kSelThreads + threadIdx.x;
+    if (i < nb) {
+      const uint32_t u = kb[i];
+      if (u > thr) c_w += min(blk, L - i * blk);
+      if (u == thr) {
+        ++c_eq;
+        if (i == nb - 1) last_eq = 1;
+      }
+    }
+  }
+  int t_eq, t_w, t_last;
+  wg_exclusive_scan(c_eq, t_eq);
+  wg_exclusive_scan(c_w, t_w);
+  wg_exclusive_scan(last_eq, t_last);
+  if (threadIdx.x == 0) {
+    int* c = counts + ((size_t)b * nchunks + blockIdx.x) * 4;
+    c[0] = t_eq;
+    c[1] = t_w;
+    c[2] = t_last;
+  }
+}
+
+// Running bases of every chunk: equal keys before it, output positions before it.
+__global__ void __launch_bounds__(256) hsi_multi_scan_kernel(const int32_t* __restrict__ seq_lens, int stride,
+                                                             int blk, const int* __restrict__ state,
+                                                             int* __restrict__ counts, int nchunks,
+                                                             int32_t* __restrict__ pool_n) {
+  const int b = blockIdx.x;
+  if (threadIdx.x != 0) return;
+  const int L = min(max(seq_lens[b], 0), stride);
+  const int nb = (L + blk - 1) / blk;
+  const int take = state[4 * b + 2] ? 0 : state[4 * b + 1];
+  const int w_last = nb ? L - (nb - 1) * blk : 0;
+  int eq_base = 0, out_base = 0;
+  for (int c = 0; c < nchunks; ++c) {
+    int* e = counts + ((size_t)b * nchunks + c) * 4;
+    const int n_eq = e[0], w_gt = e[1], last_eq = e[2];
+    const int kept = min(max(take - eq_base, 0), n_eq);
+    const int w_eq = kept * blk - (last_eq && kept == n_eq && kept > 0 ? blk - w_last : 0);
+    e[0] = eq_base;
+    e[1] = out_base;
+    eq_base += n_eq;
+    out_base += w_gt + w_eq;
+  }
+  pool_n[b] = out_base;
+}
+
+// Ordered emit of one chunk from its bases.
+__global__ void __launch_bounds__(kSelThreads) hsi_multi_emit_kernel(const uint32_t* __restrict__ keys, int nb_stride,
+                                                                     const int32_t* __restrict__ seq_lens, int stride,
+                                                                     int blk, const int* __restrict__ state,
+                                                                     const int* __restrict__ counts, int nchunks,
+                                                                     int32_t* __restrict__ pool, int pool_cap) {
+  __shared__ uint32_t lk[kChunk];
+  const int b = blockIdx.y;
+  const int L = min(max(seq_lens[b], 0), stride);
+  const int nb = (L + blk - 1) / blk;
+  const int base = blockIdx.x * kChunk;
+  if (base >= nb) return;
+  const bool all = state[4 * b + 2] != 0;
+  const uint32_t thr = all ? 0u : (uint32_t)state[4 * b];
+  const int take = all ? 0 : state[4 * b + 1];
+  const int* e = counts + ((size_t)b * nchunks + blockIdx.x) * 4;
+  const uint32_t* kb = keys + (size_t)b * nb_stride + base;
+  int32_t* out = pool + (size_t)b * pool_cap;
+  const int n = min(kChunk, nb - base);
+  emit_selected(
+      [&](int i) { return kb[i]; }, [&](int i) { return min(blk, L - (base + i) * blk); },
+      [&](int i, int off) {
+        const int j = base + i, c = min(blk, L - j * blk);
+        for (int r = 0; r < c; ++r) out[off + r] = j * blk + r;
+      },
+      n, thr, take, lk, e[0], e[1]);
+}
+
+}  // namespace
+
+namespace {
+// workspace: keys [B][nbs], then (long sequences) histograms [B][256], state
+// [B][4] and chunk counts [B][nchunks][4], all 32-bit
+int chunks_of(int stride, int blk) { return ((stride + blk - 1) / blk + kChunk - 1) / kChunk; }
+bool multi_of(int stride, int blk) { return (stride + blk - 1) / blk > kSelLdsKeys; }
 }  // namespace
 
 size_t hsi_candidates_workspace(int batch, int stride, int blk) {
-  return (size_t)batch * ((stride + blk - 1) / blk) * sizeof(uint32_t);
+  size_t words = (size_t)batch * ((stride + blk - 1) / blk);
+  if (multi_of(stride, blk)) words += (size_t)batch * (256 + 4 + 4 * (size_t)chunks_of(stride, blk));
+  return words * sizeof(uint32_t);
 }
 
 int launch_hsi_candidates(const float* scores, int batch, int stride, const int32_t* seq_lens, int blk,
@@ -262,8 +452,25 @@ int launch_hsi_candidates(const float* scores, int batch, int stride, const int3
   const int nbs = (stride + blk - 1) / blk;
   uint32_t* keys = static_cast<uint32_t*>(ws);
   hsi_block_max_kernel<<<dim3((nbs + 255) / 256, batch), 256, 0, st>>>(scores, stride, seq_lens, blk, nbs, keys);
-  hsi_pool_kernel<<<batch, kSelThreads, 0, st>>>(keys, nbs, seq_lens, stride, blk, top_blocks, pool,
-                                                 top_blocks * blk, pool_n);
+  if (!multi_of(stride, blk)) {
+    hsi_pool_kernel<<<batch, kSelThreads, 0, st>>>(keys, nbs, seq_lens, stride, blk, top_blocks, pool,
+                                                   top_blocks * blk, pool_n);
+  } else {
+    const int nch = chunks_of(stride, blk);
+    int* ghist = reinterpret_cast<int*>(keys + (size_t)batch * nbs);
+    int* state = ghist + (size_t)batch * 256;
+    int* counts = state + (size_t)batch * 4;
+    const dim3 grid(nch, batch);
+    hsi_multi_init_kernel<<<batch, 256, 0, st>>>(seq_lens, stride, blk, top_blocks, ghist, state);
+    for (int pass = 0; pass < 4; ++pass) {
+      hsi_multi_hist_kernel<<<grid, kSelThreads, 0, st>>>(keys, nbs, seq_lens, stride, blk, pass, ghist, state);
+      hsi_multi_pick_kernel<<<batch, 256, 0, st>>>(pass, ghist, state);
+    }
+    hsi_multi_count_kernel<<<grid, kSelThreads, 0, st>>>(keys, nbs, seq_lens, stride, blk, state, counts, nch);
+    hsi_multi_scan_kernel<<<batch, 256, 0, st>>>(seq_lens, stride, blk, state, counts, nch, pool_n);
+    hsi_multi_emit_kernel<<<grid, kSelThreads, 0, st>>>(keys, nbs, seq_lens, stride, blk, state, counts, nch, pool,
+                                                        top_blocks * blk);
+  }
   return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
 }
 

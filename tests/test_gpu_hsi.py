@@ -26,6 +26,8 @@ def _ties(x, step):
     (70000, [70000, 65536, 123], 8, 2048, 0.125),
     (1 << 20, [1 << 20], 8, 2048, 0.0),
     (1 << 17, [131071], 16, 5000, 0.0),
+    (200000, [200000, 150001, 17, 0], 8, 2048, 0.25),   # > 16,384 blocks: many workgroups per sequence
+    (300000, [299999, 70000], 8, 40000, 0.0),           # every block of the shorter sequence kept
 ])
 def test_candidate_pool_matches_oracle(S, lens, block, top, step):
     B = len(lens)
