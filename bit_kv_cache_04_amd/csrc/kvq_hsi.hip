@@ -321,21 +321,26 @@ __global__ void __launch_bounds__(kSelThreads) hsi_multi_hist_kernel(const uint3
 // histogram is cleared for the next pass.
 __global__ void __launch_bounds__(256) hsi_multi_pick_kernel(int pass, int* __restrict__ ghist,
                                                              int* __restrict__ state) {
-  __shared__ int h[256];
+  __shared__ int wt[4];
   const int b = blockIdx.x;
   if (state[4 * b + 2]) return;
-  const int t = threadIdx.x;
-  h[t] = ghist[(size_t)b * 256 + 255 - t];  // bins from the top
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int krem = state[4 * b + 1];  // read by every thread before the barrier below
+  const uint32_t prefix = (uint32_t)state[4 * b];
+  const int x = ghist[(size_t)b * 256 + 255 - t];  // thread t holds bin 255 - t
   ghist[(size_t)b * 256 + 255 - t] = 0;
+  int v = x;  // inclusive running count from the top bin
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(v, o);
+    if (lane >= o) v += y;
+  }
+  if (lane == 63) wt[wv] = v;
   __syncthreads();
-  if (t == 0) {
-    const int krem = state[4 * b + 1];
-    int before = 0, i = 0;
-    for (; i < 255; ++i) {
-      if (before + h[i] >= krem) break;
-      before += h[i];
-    }
-    state[4 * b] = (int)((uint32_t)state[4 * b] | ((uint32_t)(255 - i) << (24 - 8 * pass)));
+  for (int w = 0; w < wv; ++w) v += wt[w];
+  const int before = v - x;
+  if (before < krem && v >= krem) {  // exactly one bin: it holds the krem-th largest key
+    state[4 * b] = (int)(prefix | ((uint32_t)(255 - t) << (24 - 8 * pass)));
     state[4 * b + 1] = krem - before;
   }
 }
