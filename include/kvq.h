@@ -1,5 +1,5 @@
 /*
- * kvq.h - low-bit KV-cache append and single-query decode attention (C ABI).
+ * kvq.h - low-bit KV-cache append and decode attention (C ABI).
  *
  * The problem, as the pages state it (page "TurboQuant vs OSCAR vs EpiCache:
  * the battle over KV-cache compression", section on the KV-cache memory
@@ -10,9 +10,16 @@
  * This library stores K/V in packed low-bit formats and runs decode attention
  * directly on the packed bytes:
  *
- *   kv_quant_append      write new tokens' K/V into a packed cache (one layer)
- *   kv_decode_attention  one query token per sequence attends over its cache
+ *   kv_quant_append      write new tokens' K/V into a packed cache (one layer);
+ *                        kv_quant_append_ragged: at a position per sequence
+ *   kv_decode_attention  each sequence's query token (or last few tokens)
+ *                        attends over its cache
  *   kv_bytes_per_token   stored bytes per token for a layout and layer count
+ *   kv_hsi_candidates,   hierarchical sparse indexing: a candidate pool of
+ *   kv_hsi_select        positions, then the final selection from it
+ *   kv_decode_attention_sparse  decode over selected positions only
+ * plus host helpers for buffer sizes and the methods' constants.  Caches are
+ * contiguous or paged (a pool of pages and a block table per sequence).
  *
  * Formats (each cited where it is defined):
  *   KV_FMT_KIVI2      2-bit asymmetric; keys per channel over 32-token groups,
