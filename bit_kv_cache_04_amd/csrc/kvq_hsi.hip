@@ -2,10 +2,12 @@
 // storage by 4x via CSA2", HSI section): the candidate pool of the full-mode
 // layer (block maxima over `block` positions, the top blocks) and the top-k of a
 // reindex-mode layer over that pool.  Scores are inputs (the indexer is a model
-// component).  One workgroup selects for one sequence: a radix select finds the
-// k-th largest key in four 8-bit passes, then one pass in index order keeps
-// every larger key and the earliest of the equal ones, so the output comes out
-// in ascending order.
+// component).  A radix select finds the k-th largest key in four 8-bit passes,
+// then one pass in index order keeps every larger key and the earliest of the
+// equal ones, so the output comes out in ascending order.  One workgroup
+// selects for one sequence, or, for pools over sequences longer than
+// kSelLdsKeys blocks, many workgroups do (global histograms, per-chunk counts
+// and bases, ordered emits per chunk).
 #include <hip/hip_runtime.h>
 
 #include "kvq_device.h"
