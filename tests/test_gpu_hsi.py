@@ -200,3 +200,36 @@ def test_sparse_mfma_kernel_shapes(fmt, G, n):
     err = row_rel_err(out.cpu().numpy(), ref)
     print(f"  max row rel err {err.max():.3e}", flush=True)
     assert err.max() <= RTOL
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "latent"])
+def test_sparse_decode_on_paged_cache(fmt):
+    """A paged cache (shuffled 64-token pages) takes sparse decode on the general
+    kernel, which looks each slot's row up through the block table."""
+    cfg = SMALL[fmt].scaled(context=1024)
+    print(f"[sparse paged] {fmt}", flush=True)
+    per_seq = cfg.context // 64
+    table = np.random.default_rng(9).permutation(cfg.batch * per_seq + 3)[:cfg.batch * per_seq]
+    cache = new_cache(cfg, page_tokens=64, num_pages=cfg.batch * per_seq + 3,
+                      block_table=table.reshape(cfg.batch, per_seq))
+    K, V = inputs(cfg)
+    if fmt == "latent":
+        cache.append(K, None, 0)
+    else:
+        cache.append(K, V, 0)
+    rng = np.random.default_rng(4)
+    picks = [np.sort(rng.choice(cfg.context, 300, replace=False)).astype(np.int32),
+             np.sort(rng.choice(cfg.context, 77, replace=False)).astype(np.int32)]
+    sel = np.full((cfg.batch, 300), -1, np.int32)
+    for b, p in enumerate(picks):
+        sel[b, :p.size] = p
+    n = np.array([p.size for p in picks], np.int32)
+    q = synth.make_queries(cfg, device="cuda")
+    out = cache.decode_sparse(q, torch.from_numpy(sel).cuda(), torch.from_numpy(n).cuda(), softmax_scale(cfg))
+    consts = oracle_constants(cfg)
+    enc = oracle_encode(cfg, host64(K), host64(V) if V is not None else None, consts)
+    ref = decode_attention_sparse(fmt, enc, host64(q), picks, softmax_scale(cfg), cfg.hkv, consts,
+                                  latent_dim=cfg.head_dim)
+    err = row_rel_err(out.cpu().numpy(), ref)
+    print(f"  max row rel err {err.max():.3e}", flush=True)
+    assert err.max() <= RTOL
