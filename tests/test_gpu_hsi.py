@@ -233,3 +233,32 @@ def test_sparse_decode_on_paged_cache(fmt):
     err = row_rel_err(out.cpu().numpy(), ref)
     print(f"  max row rel err {err.max():.3e}", flush=True)
     assert err.max() <= RTOL
+
+
+def test_hsi_degenerate_cases():
+    """Block sizes 1 and 64, every score equal (the lowest blocks win), lengths
+    past the score row (clipped) or negative (empty), an empty pool, and a
+    selection asked for more entries than the pool holds."""
+    S, B = 3000, 4
+    lens = [S + 500, -7, 64, 2999]
+    eff = [min(max(x, 0), S) for x in lens]
+    flat = torch.full((B, S), 1.5, dtype=torch.float32, device="cuda")
+    rnd = synth.make_indexer_scores(5, B, S, device="cuda")
+    lt = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    for scores in (flat, rnd):
+        host = scores.cpu().numpy()
+        for block, top in ((1, 700), (64, 5), (64, 1), (8, 1)):
+            print(f"[hsi degenerate] block={block} top={top}", flush=True)
+            pool, pool_n = hsi_candidates(scores, lt, block, top)
+            pool_h, pn = pool.cpu().numpy(), pool_n.cpu().numpy()
+            for b in range(B):
+                want = candidate_pool(host[b], eff[b], block, top)
+                assert pn[b] == want.size
+                np.testing.assert_array_equal(pool_h[b, :want.size], want)
+            ps = torch.full((B, top * block), -2.0, dtype=torch.float32, device="cuda")
+            sel, sel_n = hsi_select(ps, pool, pool_n, 1000)
+            sel_h, sn = sel.cpu().numpy(), sel_n.cpu().numpy()
+            for b in range(B):
+                want = select_top_k(pool_h[b, :pn[b]], ps.cpu().numpy()[b, :pn[b]], 1000)
+                assert sn[b] == want.size
+                np.testing.assert_array_equal(sel_h[b, :want.size], want)
