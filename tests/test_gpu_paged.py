@@ -194,3 +194,25 @@ def test_table_entries_outside_the_pool(fmt):
     full = torch.full((cfg.batch,), cfg.context, dtype=torch.int32, device="cuda")
     paged.decode(q, full, softmax_scale(cfg))
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("page,cap", [(32, 64), (64, 64)])
+def test_paged_ragged_beyond_one_launch(page, cap):
+    """300 sequences (two launches of at most 256, the block table shifted for the
+    second), ragged starts, the smallest page and one page per sequence."""
+    cfg = C["fp4_b16_t32k"].scaled(batch=300, hq=1, hkv=1, context=cap)
+    print(f"[paged 300] page={page} cap={cap}", flush=True)
+    per_seq = cap // page
+    table, num_pages = _table(300, per_seq, 7, seed=page)
+    paged = new_cache(cfg, capacity=cap, page_tokens=page, num_pages=num_pages, block_table=table)
+    flat = new_cache(cfg, capacity=cap)
+    K, V = synth.make_kv(cfg, 0, 300, 0, 3, device="cuda")
+    starts = np.random.default_rng(5).integers(0, cap - 3, 300).tolist()
+    for cache in (paged, flat):
+        cache.append(K.contiguous(), V.contiguous(), starts)
+    torch.cuda.synchronize()
+    _assert_pages_equal(paged, flat, table)
+    q = synth.make_queries(cfg, device="cuda")
+    lens = torch.from_numpy(np.array(starts, np.int32) + 3).cuda()
+    np.testing.assert_array_equal(paged.decode(q, lens, softmax_scale(cfg)).cpu().numpy(),
+                                  flat.decode(q, lens, softmax_scale(cfg)).cpu().numpy())
