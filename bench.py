@@ -39,8 +39,9 @@ def counted_bytes(cfg, lib_layout, kvq, sink=0, recent=0):
             + cfg.batch * cfg.hkv * window * cfg.head_dim * 2 * 2)
 
 
-def cpu_baseline(cfg, budget_s=12.0, rotation="haar"):
-    """Time the oracle's decode on a bounded sample: one (sequence, KV head) unit at a time."""
+def cpu_baseline(cfg, budget_s=12.0, rotation="haar", hsi=False):
+    """Time the oracle's decode on a bounded sample: one (sequence, KV head) unit at a time
+    (hsi: the oracle's candidate pool, reindex top-k and decode over the selection)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -77,14 +78,28 @@ def cpu_baseline(cfg, budget_s=12.0, rotation="haar"):
     q = synth.make_queries(unit, device="cpu").float().numpy().astype(np.float64)
     scale = 1.0 / math.sqrt(cfg.key_width)
     units = 0
+    if hsi:
+        from oracle.hsi import candidate_pool, decode_attention_sparse, select_top_k
+        full = synth.make_indexer_scores(cfg.seed, 1, T).numpy()[0]
+        pool_scores = synth.make_indexer_scores(cfg.seed, 1, 8 * 2048, layer=1).numpy()[0]
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         while True:
-            OA.decode_attention(cfg.fmt, enc, q, [T], scale, 1, consts, latent_dim=cfg.head_dim)
+            if hsi:
+                pool = candidate_pool(full, T, 8, 2048)
+                sel = select_top_k(pool, pool_scores[:pool.size], 512)
+                decode_attention_sparse(cfg.fmt, enc, q, [sel], scale, 1, consts, latent_dim=cfg.head_dim)
+            else:
+                OA.decode_attention(cfg.fmt, enc, q, [T], scale, 1, consts, latent_dim=cfg.head_dim)
             units += 1
             el = time.perf_counter() - t0
             if el >= budget_s:
                 break
+    if hsi:
+        nbytes = units * (4 * (T + 8 * 2048) + 512 * per_token_head(cfg.fmt, cfg.head_dim, cfg.rope_dim))
+        return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"{units} x HSI pool + top-512 + sparse decode of 1 sequence x 1 KV head "
+                          f"({unit.hq} q heads) over {T} tokens, fp64 numpy on 1 thread, {el:.1f} s"}
     nbytes = units * T * per_token_head(cfg.fmt, cfg.head_dim, cfg.rope_dim)
     return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{units} x decode of 1 sequence x 1 KV head ({unit.hq} q heads) over {T} tokens, "
@@ -359,7 +374,8 @@ def main():
                                "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
                                "kernel": "sparse split-context attention", "kernel_us": round(dec_ms * 1e3, 2)}
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, rotation=args.rotation if cfg.fmt == "turbo" else "haar")
+        res["cpu_baseline"] = cpu_baseline(cfg, rotation=args.rotation if cfg.fmt == "turbo" else "haar",
+                                           hsi=args.hsi)
     print(json.dumps(res), flush=True)
 
 
