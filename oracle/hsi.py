@@ -58,9 +58,13 @@ def select_top_k(pool, pool_scores, k=512):
     return pool[chosen]
 
 
-def decode_attention_sparse(fmt, cache, q, selections, scale, hkv, consts=None, latent_dim=512):
+def decode_attention_sparse(fmt, cache, q, selections, scale, hkv, consts=None, latent_dim=512, K_in=None,
+                            appended=None):
     """fp64 outputs [B, Hq, dv]: query (b, hq) attends over the positions
-    selections[b] only (an empty selection gives zeros)."""
+    selections[b] only (an empty selection gives zeros).  KIVI-2 with K_in
+    ([B, H, T, d] input keys) and appended[b] tokens appended: keys of positions
+    from the sequence's incomplete group on (32 * floor(appended[b] / 32)) are
+    read from K_in, as dense decode reads its staged keys."""
     q = np.asarray(q, dtype=np.float64)
     B, Hq = q.shape[:2]
     G = Hq // hkv
@@ -72,8 +76,13 @@ def decode_attention_sparse(fmt, cache, q, selections, scale, hkv, consts=None, 
             continue
         for h in range(hkv):
             qg = q[b, h * G:(h + 1) * G]
-            logits = np.concatenate([A._key_logits(fmt, cache, b, h, t, t + 1, qg, consts, latent_dim)
-                                     for t in sel], axis=1) * scale
+            staged_from = 32 * (int(appended[b]) // 32) if K_in is not None else None
+
+            def logit(t):
+                if staged_from is not None and t >= staged_from:
+                    return qg @ np.asarray(K_in[b, h, t:t + 1], np.float64).T
+                return A._key_logits(fmt, cache, b, h, t, t + 1, qg, consts, latent_dim)
+            logits = np.concatenate([logit(t) for t in sel], axis=1) * scale
             p = np.exp(logits - logits.max(axis=1, keepdims=True))
             p /= p.sum(axis=1, keepdims=True)
             vals = np.concatenate([A._values(fmt, cache, b, h, t, t + 1, consts, latent_dim) for t in sel], 0)

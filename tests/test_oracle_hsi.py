@@ -107,3 +107,31 @@ def test_sparse_decode_reduces_to_dense_and_compact_cache():
     np.testing.assert_allclose(decode_attention_sparse("fp4", enc, q, sel, 0.2, H),
                                A.decode_attention("fp4", compact, q, [5, 5], 0.2, H), rtol=1e-12, atol=1e-12)
     assert not np.any(decode_attention_sparse("fp4", enc, q, [np.array([], int), sel[1]], 0.2, H)[0])
+
+
+def test_sparse_decode_reads_kivi_staged_keys_like_dense():
+    """Over every position, sparse decode with staged KIVI-2 keys is the staged
+    dense decode; a selection of staged positions only uses the input keys."""
+    rng = np.random.default_rng(8)
+    B, H, T, d, G = 2, 2, 96, 64, 2
+    K = rng.standard_normal((B, H, T, d))
+    V = rng.standard_normal((B, H, T, d))
+    enc = F.encode_cache("kivi2", K, V)
+    q = rng.standard_normal((B, H * G, d))
+    appended = np.array([80, 96])
+    lens = appended
+    full = [np.arange(80), np.arange(96)]
+    got = decode_attention_sparse("kivi2", enc, q, full, 0.3, H, K_in=K, appended=appended)
+    want = A.decode_attention_kivi_staged(enc, q[:, None], lens, 0.3, H, K, appended)[:, 0]
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+    # positions 64..79 of sequence 0 are staged: their logits use K, not the codes
+    sel = [np.array([64, 70, 79]), np.array([0, 95])]
+    out = decode_attention_sparse("kivi2", enc, q, sel, 0.3, H, K_in=K, appended=appended)
+    for h in range(H):
+        qg = q[0, h * G:(h + 1) * G]
+        lg = qg @ K[0, h, sel[0]].T * 0.3
+        p = np.exp(lg - lg.max(1, keepdims=True))
+        p /= p.sum(1, keepdims=True)
+        vals = F.kivi2_decode_values(enc["v_codes"][0, h, sel[0]], enc["v_scale"][0, h, sel[0]],
+                                     enc["v_zero"][0, h, sel[0]])
+        np.testing.assert_allclose(out[0, h * G:(h + 1) * G], p @ vals, rtol=1e-12)
