@@ -262,3 +262,32 @@ def test_hsi_degenerate_cases():
                 want = select_top_k(pool_h[b, :pn[b]], ps.cpu().numpy()[b, :pn[b]], 1000)
                 assert sn[b] == want.size
                 np.testing.assert_array_equal(sel_h[b, :want.size], want)
+
+
+def test_sparse_decode_kivi_staged_positions():
+    """KIVI-2 sequences with an incomplete last key group: selected positions in
+    it are read from the staged keys, the others from the codes."""
+    cfg = SMALL["kivi2"].scaled(batch=2, context=512)
+    print("[sparse kivi staged]", flush=True)
+    cache = new_cache(cfg)
+    K, V = inputs(cfg)
+    appended = [500, 451]
+    for b, A_ in enumerate(appended):
+        seq = cache.sequence(b)
+        seq.append(K[b:b + 1, :, :448].contiguous(), V[b:b + 1, :, :448].contiguous(), 0)
+        seq.append(K[b:b + 1, :, 448:A_].contiguous(), V[b:b + 1, :, 448:A_].contiguous(), 448)
+    torch.cuda.synchronize()
+    picks = [np.array([3, 100, 447, 470, 479, 480, 481, 499], np.int32),
+             np.array([0, 447, 448, 449, 450], np.int32)]
+    sel = np.full((cfg.batch, 8), -1, np.int32)
+    for b, p in enumerate(picks):
+        sel[b, :p.size] = p
+    n = np.array([p.size for p in picks], np.int32)
+    q = synth.make_queries(cfg, device="cuda")
+    out = cache.decode_sparse(q, torch.from_numpy(sel).cuda(), torch.from_numpy(n).cuda(), softmax_scale(cfg))
+    enc = oracle_encode(cfg, host64(K), host64(V), {})
+    ref = decode_attention_sparse("kivi2", enc, host64(q), picks, softmax_scale(cfg), cfg.hkv, {},
+                                  K_in=host64(K), appended=appended)
+    err = row_rel_err(out.cpu().numpy(), ref)
+    print(f"  max row rel err {err.max():.3e}", flush=True)
+    assert err.max() <= RTOL
