@@ -216,3 +216,29 @@ def test_paged_ragged_beyond_one_launch(page, cap):
     lens = torch.from_numpy(np.array(starts, np.int32) + 3).cuda()
     np.testing.assert_array_equal(paged.decode(q, lens, softmax_scale(cfg)).cpu().numpy(),
                                   flat.decode(q, lens, softmax_scale(cfg)).cpu().numpy())
+
+
+@pytest.mark.parametrize("fmt,nq", [("turbo", 2), ("latent", 3), ("qjl1", 4)])
+def test_paged_multi_query(fmt, nq):
+    """Several queries per sequence on paged caches: the per-query launches of the
+    TurboQuant and latent kernels, and the QJL columns, read through the table."""
+    cfg = SMALL[fmt]
+    print(f"[paged multi-query] {fmt} nq={nq}", flush=True)
+    paged, flat, table = _pair(cfg, seed=6)
+    K, V = inputs(cfg)
+    for cache in (paged, flat):
+        _append(cache, cfg, K, V, 0, cfg.context)
+    torch.cuda.synchronize()
+    q = synth.make_queries(cfg.scaled(hq=nq * cfg.hq), device="cuda").view(cfg.batch, nq, cfg.hq, -1)
+    lens = np.array([cfg.context, cfg.context // 3], dtype=np.int32)
+    lt = torch.from_numpy(lens).cuda()
+    out_p = paged.decode(q, lt, softmax_scale(cfg)).cpu().numpy()
+    out_f = flat.decode(q, lt, softmax_scale(cfg)).cpu().numpy()
+    np.testing.assert_array_equal(out_p, out_f)
+    consts = oracle_constants(cfg)
+    enc = oracle_encode(cfg, host64(K), host64(V) if V is not None else None, consts)
+    ref = OA.decode_attention_multi(fmt, enc, host64(q), lens, softmax_scale(cfg), cfg.hkv, consts,
+                                    latent_dim=cfg.head_dim)
+    err = row_rel_err(out_p.reshape(-1, out_p.shape[-1]), ref.reshape(-1, ref.shape[-1]))
+    print(f"  max row rel err {err.max():.3e}", flush=True)
+    assert err.max() <= RTOL
