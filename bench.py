@@ -1,25 +1,40 @@
 """Decode-attention bandwidth benchmark for the packed low-bit KV cache.
 
 One step = the whole hot path for one decode token of every sequence: append
-that token's K/V into the packed cache (the format's pack kernel) and run
-single-query attention over the full context (query prep, split-context
-attention, merge), at a fixed context length.
+that token's K/V into the packed cache (the format's pack kernel; the 1M-context
+workload appends 32,768 tokens in bulk) and run attention over the full context
+(query prep, split-context attention, merge), at a fixed context length.
 
-The timed region replays the step as a HIP graph (captured once after the
-warm-up and checked bit for bit against the eager step); the attention kernel's
-own duration, for the roofline, comes from HIP events around its launches in
-an eager pass over the same number of steps.
+With no --config the bench runs all five workloads and prints ONE JSON line:
+the headline fields are those of the largest single-GPU workload,
+latent_b64_t64k (1.88 GB of packed cache read per step), and `workloads` holds
+one record per workload (step time median and min, GB/s, % of HBM peak, query
+tokens/s, the attention kernel's roofline, the CPU oracle baseline).
 
-Prints one JSON line.  `value` is decode KV GB/s: the packed bytes the
-attention reads per step (codes + scales/norms of every cached token) over the
-measured step time.  The default workload is FP4 E2M1 with one bf16 scale per
-16 channels, batch 16, 32 query / 8 KV heads, head dim 128, 32768 tokens.
+Timing, per workload:
+  * inputs are resident in HBM before anything is timed;
+  * before every timed step a streaming read of a separate 1 GiB buffer
+    (outside the event pair) evicts the 256 MB MALL and the L2s, so each step
+    reads its cache from HBM;
+  * the step is captured once as a HIP graph (checked bit for bit against the
+    eager step) and replayed; each replay is bracketed by its own HIP events on
+    the stream it runs on; median and min are reported;
+  * the attention kernel's own duration (for the roofline) comes from HIP
+    events the library records immediately around its launch, in an eager pass
+    over the same number of flushed steps.
+A plain streaming-read kernel (kvq_probe.h) is timed the same way over 1 GiB:
+the bandwidth a kernel that only reads reaches on this part, for context.
+
+`value` is decode KV GB/s: the packed bytes the attention reads per step
+(codes + scales/norms of every cached token) over the median step time.
 """
 
 import argparse
 import json
 import math
 import os
+import platform
+import statistics
 import sys
 import time
 
@@ -27,7 +42,21 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 FP32_VALU_PEAK_TFLOPS = 157.3  # fp32 vector peak (256 CUs, 2.4 GHz)
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16 matrix-core peak
 HBM_PEAK_GBS = 8000.0
+ALL_WORKLOADS = ["kivi2_tiny", "fp4_b16_t32k", "turbo_b8_t128k", "qjl1_b1_t1m", "latent_b64_t64k"]
+HEADLINE = "latent_b64_t64k"  # the largest single-GPU workload by bytes read per step
+FLUSH_BYTES = 1 << 30         # 4x the 256 MB MALL
+CPU_SAMPLE_TOKENS = 131072    # context of the CPU oracle's decode sample (whole context if shorter)
+
+# the arithmetic each workload's attention kernel computes in
+DTYPE = {
+    "kivi2": "fp32 (vector ALU)",
+    "fp4": "fp16 MFMA operands (E2M1 x bf16 scale exact), fp32 accumulate and softmax",
+    "turbo": "fp4 x fp6 and fp16 MFMA operands, fp32 accumulate and softmax",
+    "qjl1": "fp4 x fp8 and fp16 MFMA operands, fp32 accumulate and softmax",
+    "latent": "fp16 / bf16 MFMA operands (E2M1 x bf16 scale exact), fp32 accumulate and softmax",
+}
 
 
 def counted_bytes(cfg, lib_layout, kvq, sink=0, recent=0):
@@ -39,9 +68,26 @@ def counted_bytes(cfg, lib_layout, kvq, sink=0, recent=0):
             + cfg.batch * cfg.hkv * window * cfg.head_dim * 2 * 2)
 
 
-def cpu_baseline(cfg, budget_s=12.0, rotation="haar", hsi=False):
-    """Time the oracle's decode on a bounded sample: one (sequence, KV head) unit at a time
-    (hsi: the oracle's candidate pool, reindex top-k and decode over the selection)."""
+def cpu_info():
+    model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0)), os.cpu_count()
+
+
+def cpu_baseline(cfg, budget_s=2.5, rotation="haar", hsi=False):
+    """The oracle as it stands, on a bounded sample of the workload: one
+    (sequence, KV head) unit (with its query-head group) over the first
+    min(context, CPU_SAMPLE_TOKENS) tokens.  Encode (the oracle's append) of the
+    sample is timed once; decode (or, with hsi, the oracle's candidate pool,
+    reindex top-k and sparse decode) is repeated for about budget_s seconds.
+    BLAS runs on every core this process may use."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -52,7 +98,8 @@ def cpu_baseline(cfg, budget_s=12.0, rotation="haar", hsi=False):
     from oracle.lloyd_max import canonical_codebook
     from oracle.rotation import canonical_hadamard_rotation, canonical_projection, canonical_rotation
 
-    T = cfg.context
+    model, cores, ncpu = cpu_info()
+    T = min(cfg.context, CPU_SAMPLE_TOKENS)
     unit = cfg.scaled(batch=1, hkv=1, hq=cfg.group)
     consts = {}
     if cfg.fmt == "turbo":
@@ -63,26 +110,32 @@ def cpu_baseline(cfg, budget_s=12.0, rotation="haar", hsi=False):
         consts["levels"], consts["thresholds"] = canonical_codebook(2, cfg.head_dim)
     if cfg.fmt in ("turbo", "qjl1"):
         consts["proj"] = canonical_projection(synth.gaussian_matrix(cfg.seed, 128, cfg.head_dim, stream=2))
-    enc_parts = []
-    for t0 in range(0, T, 65536):
-        t1 = min(T, t0 + 65536)
-        if cfg.fmt == "latent":
-            lat = synth.make_latent(unit, 0, 1, t0, t1, device="cpu").float().numpy().astype(np.float64)
-            enc_parts.append(OF.encode_cache("latent", latent=lat, latent_dim=cfg.head_dim))
-        else:
-            K, V = synth.make_kv(unit, 0, 1, t0, t1, device="cpu")
-            enc_parts.append(OF.encode_cache(cfg.fmt, K.float().numpy().astype(np.float64),
-                                             V.float().numpy().astype(np.float64), consts=consts))
-    axis = 1 if cfg.fmt == "latent" else 2
-    enc = {k: np.concatenate([e[k] for e in enc_parts], axis=axis) for k in enc_parts[0]}
-    q = synth.make_queries(unit, device="cpu").float().numpy().astype(np.float64)
-    scale = 1.0 / math.sqrt(cfg.key_width)
-    units = 0
-    if hsi:
-        from oracle.hsi import candidate_pool, decode_attention_sparse, select_top_k
-        full = synth.make_indexer_scores(cfg.seed, 1, T).numpy()[0]
-        pool_scores = synth.make_indexer_scores(cfg.seed, 1, 8 * 2048, layer=1).numpy()[0]
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=cores):
+        inputs = []
+        for t0 in range(0, T, 65536):
+            t1 = min(T, t0 + 65536)
+            if cfg.fmt == "latent":
+                inputs.append(synth.make_latent(unit, 0, 1, t0, t1, device="cpu").float().numpy().astype(np.float64))
+            else:
+                K, V = synth.make_kv(unit, 0, 1, t0, t1, device="cpu")
+                inputs.append((K.float().numpy().astype(np.float64), V.float().numpy().astype(np.float64)))
+        te = time.perf_counter()
+        parts = []
+        for x in inputs:
+            if cfg.fmt == "latent":
+                parts.append(OF.encode_cache("latent", latent=x, latent_dim=cfg.head_dim))
+            else:
+                parts.append(OF.encode_cache(cfg.fmt, x[0], x[1], consts=consts))
+        enc_s = time.perf_counter() - te
+        axis = 1 if cfg.fmt == "latent" else 2
+        enc = {k: np.concatenate([e[k] for e in parts], axis=axis) for k in parts[0]}
+        q = synth.make_queries(unit, device="cpu").float().numpy().astype(np.float64)
+        scale = 1.0 / math.sqrt(cfg.key_width)
+        if hsi:
+            from oracle.hsi import candidate_pool, decode_attention_sparse, select_top_k
+            full = synth.make_indexer_scores(cfg.seed, 1, T).numpy()[0]
+            pool_scores = synth.make_indexer_scores(cfg.seed, 1, 8 * 2048, layer=1).numpy()[0]
+        units = 0
         t0 = time.perf_counter()
         while True:
             if hsi:
@@ -95,97 +148,120 @@ def cpu_baseline(cfg, budget_s=12.0, rotation="haar", hsi=False):
             el = time.perf_counter() - t0
             if el >= budget_s:
                 break
+    pth = per_token_head(cfg.fmt, cfg.head_dim, cfg.rope_dim)
+    base = {"unit": "GB/s", "cores": cores, "kind": "oracle", "cpu_model": model, "cpu_count": ncpu,
+            "encode_value": round(T * pth / enc_s / 1e9, 6), "encode_unit": "GB/s of packed cache written",
+            "encode_tokens_per_s": round(T / enc_s, 1),
+            "encode_sample": f"oracle append of {T} tokens of 1 sequence x 1 KV head, {enc_s:.2f} s"}
+    what = "HSI pool + top-512 + sparse decode" if hsi else "decode"
     if hsi:
-        nbytes = units * (4 * (T + 8 * 2048) + 512 * per_token_head(cfg.fmt, cfg.head_dim, cfg.rope_dim))
-        return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-                "sample": f"{units} x HSI pool + top-512 + sparse decode of 1 sequence x 1 KV head "
-                          f"({unit.hq} q heads) over {T} tokens, fp64 numpy on 1 thread, {el:.1f} s"}
-    nbytes = units * T * per_token_head(cfg.fmt, cfg.head_dim, cfg.rope_dim)
-    return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{units} x decode of 1 sequence x 1 KV head ({unit.hq} q heads) over {T} tokens, "
-                      f"fp64 numpy on 1 thread, {el:.1f} s"}
+        nbytes = units * (4 * (T + 8 * 2048) + 512 * pth)
+    else:
+        nbytes = units * T * pth
+    base.update(value=round(nbytes / el / 1e9, 6),
+                sample=f"{units} x {what} of 1 sequence x 1 KV head ({unit.hq} q heads) over {T} tokens "
+                       f"(workload context {cfg.context}), fp64 numpy, BLAS on {cores} threads, {el:.1f} s")
+    return base
 
 
-MFMA_F16_PEAK_TFLOPS = 2500.0
-
-
-def measured_traffic(workload):
-    """HBM bytes per launch of the attention kernel from the committed counter
-    summary (profiles/*_<workload>_pmc.txt: FETCH_SIZE and WRITE_SIZE scaled by a
-    plain copy of known size), or None when there is none or the kernel's source
+def measured_profile(workload, kind):
+    """Fields of the committed counter summary profiles/*_<workload>_<kind>.txt
+    for the attention kernel, or None when there is none or the kernel's source
     has changed since the counters were taken."""
     import glob
     import hashlib
-    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"*_{workload}_pmc.txt"))):
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"*_{workload}_{kind}.txt"))):
         kv = {}
         for line in open(path):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
         src = os.path.join(ROOT, kv.get("source", ""))
-        if not os.path.isfile(src) or "traffic_bytes_per_launch" not in kv:
+        if not os.path.isfile(src):
             continue
         if hashlib.sha256(open(src, "rb").read()).hexdigest() == kv.get("source_sha256"):
-            return int(kv["traffic_bytes_per_launch"])
+            return kv
     return None
 
 
-def roofline(cfg, nbytes, dec_ms, nq=1, windowed=False, paged=False):
-    """Roofline of the split-context attention kernel, timed by events around its launch.
-    The counter summaries cover the one-query kernels: traffic is None for nq > 1."""
-    traffic = measured_traffic(cfg.name) if nq == 1 and not windowed and not paged else None
+def roofline(cfg, nbytes, kern_us, nq=1, plain=True):
+    """Roofline of the split-context attention kernel from its event-timed duration.
+    The counter summaries cover the one-query, contiguous, window-free kernels."""
+    pmc = measured_profile(cfg.name, "pmc") if plain and nq == 1 else None
+    util = measured_profile(cfg.name, "util") if plain and nq == 1 else None
+    traffic = int(pmc["traffic_bytes_per_launch"]) if pmc and "traffic_bytes_per_launch" in pmc else None
+    sec = kern_us * 1e-6
     if cfg.fmt == "latent":
         # 128 heads x (576 + 512) x 2 flop per token: a dense contraction on fp16 matrix cores
         flops = 2.0 * nq * cfg.batch * cfg.context * cfg.hq * (cfg.key_width + cfg.head_dim)
-        ach = flops / (dec_ms * 1e-3) / 1e12
-        return {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic,
-                "kernel": "split-context attention", "kernel_us": round(dec_ms * 1e3, 2),
-                "hbm_gbs": round(nbytes / (dec_ms * 1e-3) / 1e9, 2)}
-    ach = nbytes / (dec_ms * 1e-3) / 1e9
-    return {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "split-context attention", "kernel_us": round(dec_ms * 1e3, 2)}
+        ach = flops / sec / 1e12
+        r = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic,
+             "hbm_gbs": round(nbytes / sec / 1e9, 2)}
+    else:
+        ach = nbytes / sec / 1e9
+        r = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
+    r.update(kernel="split-context attention", kernel_us=round(kern_us, 2),
+             algorithmic_bytes_per_launch=nbytes)
+    if util:
+        r["utilisation"] = {k: float(util[k]) for k in ("mfma_busy", "valu_busy", "lds_busy") if k in util}
+    return r
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="fp4_b16_t32k")
-    ap.add_argument("--splits", type=int, default=0)
-    ap.add_argument("--sink", type=int, default=0, help="leading tokens kept bf16 (FP4-valued formats)")
-    ap.add_argument("--recent", type=int, default=0, help="trailing tokens kept bf16 (FP4-valued formats)")
-    ap.add_argument("--queries", type=int, default=1,
-                    help="query tokens per sequence (drafted positions checked in one pass); the step "
-                         "appends that many tokens")
-    ap.add_argument("--rotation", default="haar", choices=["haar", "hadamard", "hadamard_plain"],
-                    help="TurboQuant rotation: a Haar draw, or the Hadamard transform with (or without) "
-                         "the bit-reversal permutation")
-    ap.add_argument("--page-tokens", type=int, default=0,
-                    help="paged storage: tokens per page, the pool's pages assigned to sequences in a seeded "
-                         "shuffled order")
-    ap.add_argument("--hsi", action="store_true",
-                    help="hierarchical sparse indexing: candidate pool (top 2048 blocks of 8 by synthetic full-mode "
-                         "scores), reindex top 512 (synthetic pool scores), decode over the selected positions")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph replay")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              f"(the decode shards by sequence and KV head with no exchange; see the design notes)",
-              file=sys.stderr)
-        sys.exit(2)
+class Flusher:
+    """Evicts the MALL and the L2s before a timed launch: a streaming read of a
+    1 GiB buffer (a read, so that the lines it leaves are clean: a copy would
+    leave dirty lines whose write-back then lands inside the timed kernel)."""
 
+    def __init__(self, torch, kvq, dev, nbytes):
+        self.kvq = kvq
+        self.torch = torch
+        self.buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev) if nbytes else None
+        self.sink = torch.zeros(4, dtype=torch.int32, device=dev)
+
+    def __call__(self):
+        if self.buf is not None:
+            self.kvq.kv_stream_read(self.buf.data_ptr(), self.buf.numel() * 4, self.sink.data_ptr(),
+                                    self.torch.cuda.current_stream().cuda_stream)
+
+
+def timed(torch, fn, n, flush):
+    """Run fn n times, each flushed first and bracketed by its own events on the
+    current stream; returns the per-call milliseconds."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        flush()
+        evs[i][0].record()
+        fn(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def stream_read_reference(torch, kvq, dev, flush, steps):
+    buf = torch.full((FLUSH_BYTES // 4,), 7, dtype=torch.int32, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream().cuda_stream
+    for _ in range(3):
+        kvq.kv_stream_read(buf.data_ptr(), buf.numel() * 4, sink.data_ptr(), st)
+    ms = timed(torch, lambda i: kvq.kv_stream_read(buf.data_ptr(), buf.numel() * 4, sink.data_ptr(), st),
+               max(steps, 10), flush)
+    med = statistics.median(ms)
+    gbs = buf.numel() * 4 / (med * 1e-3) / 1e9
+    return {"kernel": "stream_read_kernel (16-byte loads, 8 in flight per thread)", "bytes": buf.numel() * 4,
+            "us_median": round(med * 1e3, 2), "us_min": round(min(ms) * 1e3, 2), "gbs": round(gbs, 1),
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def run_workload(name, args, dev, flush, cpu):
     import torch
 
     import synth
     from bit_kv_cache_04_amd import kvq
     from bit_kv_cache_04_amd.cache import PackedKVCache, make_constants
 
-    cfg = synth.CONFIGS[args.config]
-    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[name]
     consts = None
     if cfg.fmt in ("turbo", "qjl1"):
         consts = make_constants(cfg.fmt, cfg.head_dim,
@@ -231,11 +307,13 @@ def main():
     ws = torch.zeros(cache.workspace_bytes(cfg.hq, T, args.splits, q.dtype, nq), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    for a, b in ev:  # torch creates the HIP event on first record; the library records it afterwards
-        a.record()
-        b.record()
+    steps = args.steps
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    aev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for evs in (kev, aev):
+        for a, b in evs:  # torch creates the HIP event on first record; the library records it afterwards
+            a.record()
+            b.record()
 
     if args.hsi:
         from bit_kv_cache_04_amd.cache import hsi_candidates, hsi_select
@@ -257,34 +335,33 @@ def main():
                             dtype=torch.uint8, device=dev)
 
     def step(i=None):
+        if i is not None:
+            aev[i][0].record()
         cache.append(k_new, v_new, T - n_new)
+        if i is not None:
+            aev[i][1].record()
         if args.hsi:
             pool, pool_n = hsi_candidates(full_scores, lens, HSI_BLOCK, HSI_TOP_BLOCKS, out=pool_out, ws=hsi_ws)
             sel, sel_n = hsi_select(pool_scores, pool, pool_n, HSI_TOP_K, out=sel_out)
             cache.decode_sparse(q, sel, sel_n, scale, splits=args.splits, out=out, ws=sp_ws,
-                                events=None if i is None else ev[i])
+                                events=None if i is None else kev[i])
             return
-        cache.decode(q, lens, scale, splits=args.splits, out=out, ws=ws,
-                     events=None if i is None else ev[i])
+        cache.decode(q, lens, scale, splits=args.splits, out=out, ws=ws, events=None if i is None else kev[i])
 
     for _ in range(args.warmup):
+        flush()
         step()
     torch.cuda.synchronize()
-    # eager timed pass: events around the split-context attention kernel
-    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # eager pass: events around the split-context attention kernel and the append
     w0 = time.perf_counter()
-    s0.record()
-    for i in range(args.steps):
-        step(i)
-    s1.record()
-    torch.cuda.synchronize()
+    eager_ms = timed(torch, step, steps, flush)
     wall = time.perf_counter() - w0
-    ms_eager = s0.elapsed_time(s1) / args.steps
-    dec_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
-    ms_step = ms_eager
+    kern_ms = [a.elapsed_time(b) for a, b in kev]
+    app_ms = [a.elapsed_time(b) for a, b in aev]
+    step_ms = eager_ms
     if not args.no_graph:
         # The same step captured once as a HIP graph and replayed: the launch
-        # overhead of the four kernels leaves the timed region.  Every replay must
+        # overhead of the step's kernels leaves the timed region.  Every replay must
         # reproduce the eager output bit for bit, with eager steps in between.
         ref = out.clone()
         side = torch.cuda.Stream()
@@ -301,81 +378,167 @@ def main():
             graph.replay()
             torch.cuda.synchronize()
             if not torch.equal(out, ref):
-                raise RuntimeError("graph replay differs from the eager step")
+                raise RuntimeError(f"{name}: graph replay differs from the eager step")
             step()
             torch.cuda.synchronize()
         for _ in range(args.warmup):
+            flush()
             graph.replay()
         torch.cuda.synchronize()
         w0 = time.perf_counter()
-        s0.record()
-        for _ in range(args.steps):
-            graph.replay()
-        s1.record()
-        torch.cuda.synchronize()
+        step_ms = timed(torch, lambda i: graph.replay(), steps, flush)
         wall = time.perf_counter() - w0
-        ms_step = s0.elapsed_time(s1) / args.steps
+    ms_med, ms_min = statistics.median(step_ms), min(step_ms)
+    kern_us = statistics.median(kern_ms) * 1e3
     nbytes = counted_bytes(cfg, cache.layout, kvq, args.sink, args.recent)
     if args.hsi:
         # the step reads the full-mode scores, the pool's scores and the packed
         # bytes of the selected positions
         n_sel = int(sel_out[1].sum())
         nbytes = 4 * cfg.batch * (T + pool_cap) + kvq.kv_bytes_per_token(cache.layout, 1) * n_sel
-    gbs = nbytes / (ms_step * 1e-3) / 1e9
-    achieved = nbytes / (dec_ms * 1e-3) / 1e9
-    res = {
-        "metric": "decode-attn KV GB/s read (% of HBM peak) + query-tokens/s at fixed context",
-        "value": round(gbs, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp32",
-        "data": "synthetic",
+    gbs = nbytes / (ms_med * 1e-3) / 1e9
+    plain = not (args.sink or args.recent or args.page_tokens or args.hsi)
+    rec = {
+        "workload": cfg.name,
         "config": {"workload": cfg.name, "format": cfg.fmt, "batch": cfg.batch, "q_heads": cfg.hq,
                    "kv_heads": cfg.hkv, "head_dim": cfg.head_dim, "rope_dim": cfg.rope_dim,
-                   "context": T, "counted_bytes_per_step": nbytes,
+                   "context": T, "appended_per_step": n_new, "counted_bytes_per_step": nbytes,
                    "splits": args.splits or "auto", "queries_per_seq": nq,
                    "bf16_sink_tokens": args.sink, "bf16_recent_tokens": args.recent,
                    **({"page_tokens": args.page_tokens} if args.page_tokens else {}),
                    **({"rotation": args.rotation} if cfg.fmt == "turbo" else {})},
+        "dtype": DTYPE[cfg.fmt],
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "ms_per_step": round(ms_med, 5),
+        "ms_per_step_min": round(ms_min, 5),
+        "ms_per_step_eager": round(statistics.median(eager_ms), 5),
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
-        "query_tokens_per_s": round(nq * cfg.batch / (ms_step * 1e-3), 1),
+        "query_tokens_per_s": round(nq * cfg.batch / (ms_med * 1e-3), 1),
         "wall_s": round(wall, 3),
-        "timing": "hip-graph replay of the step" if not args.no_graph else "eager launches",
-        "ms_per_step_eager": round(ms_eager, 5),
-        "roofline": roofline(cfg, nbytes, dec_ms, nq, bool(args.sink or args.recent), bool(args.page_tokens)),
+        "timing": ("hip-graph replay of the step" if not args.no_graph else "eager launches")
+                  + ", median of per-step HIP events, MALL flushed before each step",
+        "roofline": roofline(cfg, nbytes, kern_us, nq, plain),
+        "attention_kernel_us_min": round(min(kern_ms) * 1e3, 2),
+        "append_us": round(statistics.median(app_ms) * 1e3, 2),
     }
+    if cfg.append_new:
+        # bulk append: bf16 K and V in, packed rows out (QJL keys 18 B + FP4 values 80 B per token-head)
+        rows = cfg.batch * cfg.hkv * n_new
+        io = 2 * rows * cfg.head_dim * 2 + rows * kvq.kv_bytes_per_token(cache.layout, 1) // cfg.hkv
+        a_us = statistics.median(app_ms) * 1e3
+        rec["append_roofline"] = {"bound": "hbm", "achieved": round(io / (a_us * 1e-6) / 1e9, 2),
+                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": round(io / (a_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                  "kernel": "bulk append", "kernel_us": round(a_us, 2),
+                                  "algorithmic_bytes_per_launch": io}
     if args.hsi:
-        # the dominant kernel is the sparse decode on the general (fp32 vector) kernel:
-        # per selected position and query head, key_width + head_dim multiply-adds
-        # (the latent cache's gather kernel runs them on the fp16 matrix cores); the
-        # FP4 / QJL / TurboQuant gather kernels are priced by the packed bytes they
-        # gather, the general kernel (KIVI-2) against the fp32 vector peak
-        res["metric"] = "HSI sparse decode step: bytes read GB/s + query-tokens/s at fixed context"
-        res["config"].update(hsi={"block": HSI_BLOCK, "top_blocks": HSI_TOP_BLOCKS, "top_k": HSI_TOP_K,
+        rec["metric"] = "HSI sparse decode step: bytes read GB/s + query-tokens/s at fixed context"
+        rec["config"].update(hsi={"block": HSI_BLOCK, "top_blocks": HSI_TOP_BLOCKS, "top_k": HSI_TOP_K,
                                   "selected_positions": n_sel})
         if cfg.fmt in ("fp4", "qjl1", "turbo"):
             gathered = kvq.kv_bytes_per_token(cache.layout, 1) * n_sel
-            ach = gathered / (dec_ms * 1e-3) / 1e9
-            res["roofline"] = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            ach = gathered / (kern_us * 1e-6) / 1e9
+            rec["roofline"] = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
-                               "kernel": "sparse split-context attention", "kernel_us": round(dec_ms * 1e3, 2)}
+                               "kernel": "sparse split-context attention", "kernel_us": round(kern_us, 2)}
         else:
+            # per selected position and query head, key_width + head_dim multiply-adds
+            # (the latent cache's gather kernel runs them on the fp16 matrix cores,
+            # KIVI-2 on the general fp32 vector kernel)
             flops = 2.0 * cfg.hq * n_sel * (cfg.key_width + cfg.head_dim)
-            ach = flops / (dec_ms * 1e-3) / 1e12
+            ach = flops / (kern_us * 1e-6) / 1e12
             mfma = cfg.fmt == "latent"
             peak = MFMA_F16_PEAK_TFLOPS if mfma else FP32_VALU_PEAK_TFLOPS
-            res["roofline"] = {"bound": "mfma" if mfma else "alu", "achieved": round(ach, 2), "peak": peak,
+            rec["roofline"] = {"bound": "mfma" if mfma else "alu", "achieved": round(ach, 2), "peak": peak,
                                "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
-                               "kernel": "sparse split-context attention", "kernel_us": round(dec_ms * 1e3, 2)}
+                               "kernel": "sparse split-context attention", "kernel_us": round(kern_us, 2)}
+    if cpu:
+        rec["_cfg"] = cfg
+    if not args.no_graph:
+        del graph
+    del cache, ws, out, k_new, v_new, q
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default=None,
+                    help="one workload; default: all five, with latent_b64_t64k as the headline")
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--sink", type=int, default=0, help="leading tokens kept bf16 (FP4-valued formats)")
+    ap.add_argument("--recent", type=int, default=0, help="trailing tokens kept bf16 (FP4-valued formats)")
+    ap.add_argument("--queries", type=int, default=1,
+                    help="query tokens per sequence (drafted positions checked in one pass); the step "
+                         "appends that many tokens")
+    ap.add_argument("--rotation", default="haar", choices=["haar", "hadamard", "hadamard_plain"],
+                    help="TurboQuant rotation: a Haar draw, or the Hadamard transform with (or without) "
+                         "the bit-reversal permutation")
+    ap.add_argument("--page-tokens", type=int, default=0,
+                    help="paged storage: tokens per page, the pool's pages assigned to sequences in a seeded "
+                         "shuffled order")
+    ap.add_argument("--hsi", action="store_true",
+                    help="hierarchical sparse indexing: candidate pool (top 2048 blocks of 8 by synthetic full-mode "
+                         "scores), reindex top 512 (synthetic pool scores), decode over the selected positions")
+    ap.add_argument("--no-flush", action="store_true", help="do not evict the MALL before each timed step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph replay")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(the decode shards by sequence and KV head with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from bit_kv_cache_04_amd import kvq
+
+    dev = torch.device("cuda:0")
+    flush = Flusher(torch, kvq, dev, 0 if args.no_flush else FLUSH_BYTES)
+    names = [args.config] if args.config else ALL_WORKLOADS
+    headline = args.config or HEADLINE
+    records = {}
+    for name in names:
+        print(f"bench: {name} ...", file=sys.stderr, flush=True)
+        records[name] = run_workload(name, args, dev, flush, not args.no_cpu_baseline)
+    ref = stream_read_reference(torch, kvq, dev, flush, args.steps)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, rotation=args.rotation if cfg.fmt == "turbo" else "haar",
-                                           hsi=args.hsi)
+        for name in names:
+            cfg = records[name].pop("_cfg")
+            print(f"bench: cpu baseline {name} ...", file=sys.stderr, flush=True)
+            records[name]["cpu_baseline"] = cpu_baseline(
+                cfg, rotation=args.rotation if cfg.fmt == "turbo" else "haar", hsi=args.hsi)
+    h = records[headline]
+    res = {
+        "metric": h.get("metric", "decode-attn KV GB/s read (% of HBM peak) + query-tokens/s at fixed context"),
+        "value": h["value"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": h["ms_per_step"],
+        "ms_per_step_min": h["ms_per_step_min"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": h["dtype"],
+        "data": "synthetic (seeded N(0,1) K/V/latent/queries, key outlier channels; no dataset or weights)",
+        "config": h["config"],
+        "pct_hbm_peak": h["pct_hbm_peak"],
+        "query_tokens_per_s": h["query_tokens_per_s"],
+        "timing": h["timing"],
+        "roofline": h["roofline"],
+        "stream_read_reference": ref,
+        "workloads": {n: {k: v for k, v in r.items() if k != "workload"} for n, r in records.items()},
+    }
+    if "cpu_baseline" in h:
+        res["cpu_baseline"] = h["cpu_baseline"]
     print(json.dumps(res), flush=True)
 
 

@@ -11,7 +11,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["kvq_host.cpp", "kvq_api.cpp", "kvq_append.hip", "kvq_decode.hip", "kvq_decode_mfma.hip", "kvq_decode_latent.hip", "kvq_decode_turbo.hip", "kvq_hsi.hip"]
+SOURCES = ["kvq_host.cpp", "kvq_api.cpp", "kvq_append.hip", "kvq_decode.hip", "kvq_decode_mfma.hip", "kvq_decode_latent.hip", "kvq_decode_turbo.hip", "kvq_hsi.hip", "kvq_probe.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -22,20 +22,47 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
-    """Compile every source into libkvq.so next to this file (or `out`); returns its path."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = out + ".tmp"
-    cmd = [HIPCC] + FLAGS + [f"-D{d}" for d in defines] + ["-o", tmp] + srcs + ["-lamdhip64"]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     log = "\n".join(l for l in res.stdout.splitlines() if "packed-fp32-ops" not in l)
-    if res.returncode != 0:
-        sys.stderr.write(log + "\n")
+    return res.returncode, log
+
+
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile every source into libkvq.so next to this file (or `out`); returns its path.
+
+    Each translation unit compiles to its own object (in parallel) under
+    _build/ next to the output, then hipcc links them."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = os.path.join(os.path.dirname(os.path.abspath(out)), "_build")
+    os.makedirs(objdir, exist_ok=True)
+    tag = os.path.basename(out).replace(".so", "")
+    cflags = [f for f in FLAGS if f != "-shared"] + [f"-D{d}" for d in defines]
+    jobs = []
+    for s in SOURCES:
+        obj = os.path.join(objdir, f"{tag}_{s}.o")
+        jobs.append((obj, [HIPCC] + cflags + ["-c", os.path.join(CSRC, s), "-o", obj]))
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        results = list(ex.map(lambda j: _run(j[1], verbose), jobs))
+    failed = False
+    for rc, log in results:
+        if rc != 0:
+            failed = True
+            sys.stderr.write(log + "\n")
+        elif verbose and log.strip():
+            print(log)
+    if failed:
         raise RuntimeError("hipcc failed building libkvq.so")
-    if verbose and log.strip():
-        print(log)
+    tmp = out + ".tmp"
+    rc, log = _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [j[0] for j in jobs]
+                   + ["-lamdhip64"], verbose)
+    if rc != 0:
+        sys.stderr.write(log + "\n")
+        raise RuntimeError("hipcc failed linking libkvq.so")
     os.replace(tmp, out)
     return out
 

@@ -190,17 +190,18 @@ class PackedKVCache:
             kvq.kv_quant_append_ragged(self.struct, _ptr(k), _ptr(v), _TORCH_DT[k.dtype], list(start), n,
                                        _stream_ptr(self.device))
 
-    def workspace_bytes(self, num_q_heads, max_seq_len, splits=0, q_dtype=torch.bfloat16, num_queries=1):
-        opts = KVDecodeOpts(splits, None, None, num_queries)
+    def workspace_bytes(self, num_q_heads, max_seq_len, splits=0, q_dtype=torch.bfloat16, num_queries=1, flags=0):
+        opts = KVDecodeOpts(splits, None, None, num_queries, flags)
         return kvq.kv_decode_attention(self.struct, None, _TORCH_DT[q_dtype], num_q_heads, None, max_seq_len,
                                        1.0, None, None, 0, opts)
 
-    def decode_sparse(self, q, sel, sel_n, scale, splits=0, out=None, ws=None, events=None):
+    def decode_sparse(self, q, sel, sel_n, scale, splits=0, out=None, ws=None, events=None, flags=0):
         """q: [B, Hq, d(+rope)]; sel int32 [B, K] positions, sel_n int32 [B] (device):
-        query (b, hq) attends over sel[b, :sel_n[b]] only.  Returns fp32 [B, Hq, d]."""
+        query (b, hq) attends over sel[b, :sel_n[b]] only.  Returns fp32 [B, Hq, d].
+        flags: kvq.DECODE_FP32 for the fp32 vector kernel."""
         q = q.contiguous()
         Hq, K = q.shape[-2], sel.shape[1]
-        opts = KVDecodeOpts(splits, None, None, 1)
+        opts = KVDecodeOpts(splits, None, None, 1, flags)
         need = kvq.kv_decode_attention_sparse(self.struct, None, _TORCH_DT[q.dtype], Hq, None, None, K, 1.0, None,
                                               None, 0, opts)
         if ws is None:
@@ -210,21 +211,23 @@ class PackedKVCache:
         if out is None:
             out = torch.empty((self.B, Hq, self.d), dtype=torch.float32, device=self.device)
         if events is not None:
-            opts = KVDecodeOpts(splits, ctypes.c_void_p(events[0].cuda_event), ctypes.c_void_p(events[1].cuda_event), 1)
+            opts = KVDecodeOpts(splits, ctypes.c_void_p(events[0].cuda_event), ctypes.c_void_p(events[1].cuda_event), 1,
+                                flags)
         kvq.kv_decode_attention_sparse(self.struct, _ptr(q), _TORCH_DT[q.dtype], Hq, _ptr(sel), _ptr(sel_n), K,
                                        float(scale), _ptr(out), _ptr(ws), ws.numel(), opts,
                                        _stream_ptr(self.device))
         return out
 
-    def decode(self, q, seq_lens, scale, max_seq_len=None, splits=0, out=None, ws=None, events=None):
+    def decode(self, q, seq_lens, scale, max_seq_len=None, splits=0, out=None, ws=None, events=None, flags=0):
         """q: [B, Hq, d(+rope)] fp32/bf16, or [B, nq, Hq, d(+rope)] for nq query tokens per
         sequence (query j sees the first seq_lens[b] - (nq - 1 - j) tokens); seq_lens: int32
-        device [B]. Returns fp32 [B, Hq, d] (or [B, nq, Hq, d])."""
+        device [B]. Returns fp32 [B, Hq, d] (or [B, nq, Hq, d]).  flags: kvq.DECODE_FP32 for
+        the fp32 vector kernel (exact for any magnitude)."""
         q = q.contiguous()
         nq = q.shape[1] if q.dim() == 4 else 1
         Hq = q.shape[-2]
         max_seq_len = self.T if max_seq_len is None else max_seq_len
-        need = self.workspace_bytes(Hq, max_seq_len, splits, q.dtype, nq)
+        need = self.workspace_bytes(Hq, max_seq_len, splits, q.dtype, nq, flags)
         if ws is None:
             if self._ws is None or self._ws.numel() < need:
                 self._ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
@@ -234,7 +237,7 @@ class PackedKVCache:
             out = torch.empty(shape, dtype=torch.float32, device=self.device)
         ev = (None, None) if events is None else (ctypes.c_void_p(events[0].cuda_event),
                                                   ctypes.c_void_p(events[1].cuda_event))
-        opts = KVDecodeOpts(splits, ev[0], ev[1], nq)
+        opts = KVDecodeOpts(splits, ev[0], ev[1], nq, flags)
         kvq.kv_decode_attention(self.struct, _ptr(q), _TORCH_DT[q.dtype], Hq, _ptr(seq_lens), max_seq_len,
                                 float(scale), _ptr(out), _ptr(ws), ws.numel(), opts,
                                 _stream_ptr(self.device))

@@ -69,10 +69,16 @@ extern "C" int kv_decode_attention(const kv_cache* c, const void* q, int32_t q_d
   const int nq = opts && opts->num_queries > 0 ? opts->num_queries : 1;
   if ((opts && opts->num_queries < 0) || nq > max_seq_len) return KV_EINVAL;
   if (nq > 64) return KV_EUNSUPPORTED;
+  const int flags = opts ? opts->flags : 0;
+  if (flags & ~KV_DECODE_FP32) return KV_EINVAL;
+  const bool fp32 = flags & KV_DECODE_FP32;
   // mixed precision: the splits cover the packed tokens from sink_tokens on, and
   // the bf16 window adds one split of partial rows
   const int packed_len = std::max(1, max_seq_len - (L.sink_tokens & ~31));  // matrix-core tiles start 32-aligned
-  const SplitPlan plan = plan_splits(&L, num_q_heads, nq, q_dtype, packed_len, req);
+  // the window's splits and the packed ones share the merge's kMaxPartSplits
+  if (window_chunks(L) >= kMaxPartSplits) return KV_EUNSUPPORTED;
+  const SplitPlan plan = plan_splits(&L, num_q_heads, nq, q_dtype, packed_len, req, fp32,
+                                     kMaxPartSplits - window_chunks(L));
   const int part_splits = plan.splits + window_chunks(L);
   const DecodeWorkspace wsl = decode_workspace(&L, nq * num_q_heads, part_splits);
   if (!ws) {
@@ -84,7 +90,7 @@ extern "C" int kv_decode_attention(const kv_cache* c, const void* q, int32_t q_d
   if (!aligned(ws, 256)) return KV_EINVAL;
   if (!q || !seq_lens || !out) return KV_EINVAL;
   return launch_decode(c, q, q_dtype, num_q_heads, nq, seq_lens, max_seq_len, softmax_scale, out, ws, plan, wsl,
-                       opts ? opts->ev_begin : nullptr, opts ? opts->ev_end : nullptr, stream);
+                       opts ? opts->ev_begin : nullptr, opts ? opts->ev_end : nullptr, stream, nullptr, 0, fp32);
 }
 
 extern "C" int kv_hsi_candidates(const float* scores, int32_t batch, int32_t score_stride, const int32_t* seq_lens,
@@ -128,10 +134,13 @@ extern "C" int kv_decode_attention_sparse(const kv_cache* c, const void* q, int3
   if (req < 0 || req > 1024) return KV_EINVAL;
   if (opts && opts->num_queries > 1) return KV_EUNSUPPORTED;
   if (opts && opts->num_queries < 0) return KV_EINVAL;
+  const int flags = opts ? opts->flags : 0;
+  if (flags & ~KV_DECODE_FP32) return KV_EINVAL;
+  const bool fp32 = flags & KV_DECODE_FP32;
   // the matrix-core kernels stage a split's positions: at most 512 per split, in
   // whole 128-token steps (FP4 / QJL) or 64-token steps (latent)
-  const bool latent = latent_sparse_ok(L, num_q_heads, q_dtype);
-  const bool mfma = !latent && (mfma_sparse_ok(L, num_q_heads, q_dtype) || turbo_sparse_ok(L, num_q_heads));
+  const bool latent = !fp32 && latent_sparse_ok(L, num_q_heads, q_dtype);
+  const bool mfma = !fp32 && !latent && (mfma_sparse_ok(L, num_q_heads, q_dtype) || turbo_sparse_ok(L, num_q_heads));
   SplitPlan plan = plan_splits(&L, num_q_heads, 1, q_dtype, sel_cap, req, !latent && !mfma);
   static_assert(kLatentSparseSlots == kMfmaSparseSlots, "one staging bound");
   if ((latent || mfma) && plan.tokens_per_split > kMfmaSparseSlots) {
@@ -139,6 +148,7 @@ extern "C" int kv_decode_attention_sparse(const kv_cache* c, const void* q, int3
     const int splits = (sel_cap + kMfmaSparseSlots - 1) / kMfmaSparseSlots;
     const int per = ((sel_cap + splits - 1) / splits + step - 1) / step * step;
     plan = SplitPlan{(sel_cap + per - 1) / per, per};
+    if (plan.splits > kMaxPartSplits) return KV_EUNSUPPORTED;  // more than 512 x 1024 selected slots
   }
   const DecodeWorkspace wsl = decode_workspace(&L, num_q_heads, plan.splits);
   if (!ws) {
@@ -150,5 +160,5 @@ extern "C" int kv_decode_attention_sparse(const kv_cache* c, const void* q, int3
   if (!aligned(ws, 256)) return KV_EINVAL;
   if (!q || !sel || !sel_n || !out) return KV_EINVAL;
   return launch_decode(c, q, q_dtype, num_q_heads, 1, sel_n, sel_cap, softmax_scale, out, ws, plan, wsl,
-                       opts ? opts->ev_begin : nullptr, opts ? opts->ev_end : nullptr, stream, sel, sel_cap);
+                       opts ? opts->ev_begin : nullptr, opts ? opts->ev_end : nullptr, stream, sel, sel_cap, fp32);
 }

@@ -369,11 +369,15 @@ __global__ void __launch_bounds__(256) kivi_append_kernel(const InT* __restrict_
 // slots, the new ones from the input.  A group the append completes is coded
 // as in kivi_append_kernel; an incomplete one keeps its new keys in staging
 // (slot t mod 32).  Values are coded per token for the new tokens only.
+// Two launches on one stream: phase 0 codes (reading the old staged keys of the
+// first group), phase 1 then writes the new staged keys of the last, incomplete
+// group.  Both use slots t mod 32, so in one launch a workgroup could overwrite
+// slots another workgroup has still to read.
 template <typename InT>
 __global__ void __launch_bounds__(256) kivi_append_any_kernel(const InT* __restrict__ k, const InT* __restrict__ v,
                                                               int d, uint8_t* kc, float* ks, float* kz, uint8_t* vc,
                                                               float* vs, float* vz, float* stage, int n, int cap,
-                                                              AppendPos pos) {
+                                                              AppendPos pos, int phase) {
   __shared__ float xk[32][kKiviMaxD + 1];
   __shared__ float xv[32][kKiviMaxD + 1];
   const int tid = threadIdx.x;
@@ -385,6 +389,16 @@ __global__ void __launch_bounds__(256) kivi_append_any_kernel(const InT* __restr
   const int a0 = max(g0, s), a1 = min(g0 + 32, s + n);  // its new tokens
   if (a0 >= a1) return;                              // the whole workgroup: no token of this append
   const bool complete = s + n >= g0 + 32;
+  if (phase == 1) {  // the new staged keys of the last, incomplete group, and the appended length
+    if (!complete) {
+      for (int e = tid; e < (a1 - a0) * d; e += 256) {
+        const int t = a0 - g0 + e / d, c = e % d;
+        stage_keys(stage, bh, d)[t * d + c] = load_as_f32(k + (bh * n + (g0 + t - s)) * d, c);
+      }
+    }
+    if (tid == 0 && g0 + 32 >= s + n) set_appended(stage, bh, d, s + n);  // the group of the last token
+    return;
+  }
   for (int e = tid; e < 32 * d; e += 256) {
     const int t = e / d, c = e % d, tok = g0 + t;
     float kx = 0.f, vx = 0.f;
@@ -429,13 +443,7 @@ __global__ void __launch_bounds__(256) kivi_append_any_kernel(const InT* __restr
         kz[meta + j] = mn[j];
       }
     }
-  } else {
-    for (int e = tid; e < (a1 - a0) * d; e += 256) {
-      const int t = a0 - g0 + e / d, c = e % d;
-      stage_keys(stage, bh, d)[t * d + c] = xk[t][c];
-    }
   }
-  if (tid == 0 && g0 + 32 >= s + n) set_appended(stage, bh, d, s + n);  // the group of the last token
   const int vgroups = d / 32;
   for (int it = tid; slot0 != kNoRow && it < (a1 - a0) * vgroups; it += 256) {
     const int t = a0 - g0 + it / vgroups, vg = it % vgroups;
@@ -1169,10 +1177,11 @@ int append_typed(const kv_cache* c, const InT* k, const InT* v, const AppendPos&
       bool aligned = n % 32 == 0 && pos.start % 32 == 0;
       for (int b = 0; pos.ragged && b < L.batch; ++b) aligned = aligned && pos.s[b] % 32 == 0;
       if (!aligned) {
-        kivi_append_any_kernel<InT><<<dim3(bh * (n / 32 + 2)), 256, 0, st>>>(
-            k, v, d, kc, static_cast<float*>(c->buf[KV_BUF_K_SCALE]), static_cast<float*>(c->buf[KV_BUF_K_ZERO]),
-            vc, static_cast<float*>(c->buf[KV_BUF_V_SCALE]), static_cast<float*>(c->buf[KV_BUF_V_ZERO]),
-            static_cast<float*>(c->buf[KV_BUF_K_STAGE]), n, cap, pos);
+        for (int phase = 0; phase < 2; ++phase)  // code from the old staging, then replace it
+          kivi_append_any_kernel<InT><<<dim3(bh * (n / 32 + 2)), 256, 0, st>>>(
+              k, v, d, kc, static_cast<float*>(c->buf[KV_BUF_K_SCALE]), static_cast<float*>(c->buf[KV_BUF_K_ZERO]),
+              vc, static_cast<float*>(c->buf[KV_BUF_V_SCALE]), static_cast<float*>(c->buf[KV_BUF_V_ZERO]),
+              static_cast<float*>(c->buf[KV_BUF_K_STAGE]), n, cap, pos, phase);
         break;
       }
       kivi_append_kernel<InT><<<dim3(bh * (n / 32)), 256, 0, st>>>(

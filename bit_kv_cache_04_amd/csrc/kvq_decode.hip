@@ -532,7 +532,7 @@ __global__ void __launch_bounds__(384) prep_query_kernel(const QT* __restrict__ 
 // order.  TURBO (the whole row in one block) maps the rotated output back with
 // R^T, every thread taking a slice of the rows of R.  A row with no tokens at
 // all writes zeros.
-constexpr int kMaxSplits = 1024;
+constexpr int kMaxSplits = kMaxPartSplits;
 
 template <int NJ>
 constexpr int merge_max_waves() {
@@ -697,7 +697,7 @@ void launch_window(const kv_cache* c, const void* q, int q_dtype, int num_q_head
 int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads, int nq, const int32_t* seq_lens,
                   int max_seq_len, float scale, float* out, void* ws, const SplitPlan& plan,
                   const DecodeWorkspace& wsl, void* ev_begin, void* ev_end, void* stream, const int32_t* sel,
-                  int sel_stride) {
+                  int sel_stride, bool fp32) {
   const kv_layout& L = c->layout;
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* wsb = static_cast<char*>(ws);
@@ -710,7 +710,8 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
   const bool windowed = L.sink_tokens || L.recent_tokens;
   const int part_splits = plan.splits + window_chunks(L);
   const int qw_in = query_width(&L), qw_out = prepared_query_width(&L);
-  if (sel ? latent_sparse_ok(L, num_q_heads, q_dtype) : latent_fast_path_ok(L, num_q_heads, nq, q_dtype)) {
+  // fp32: every format on the general kernel (exact for any magnitude)
+  if (!fp32 && (sel ? latent_sparse_ok(L, num_q_heads, q_dtype) : latent_fast_path_ok(L, num_q_heads, nq, q_dtype))) {
     MfmaDecodeArgs f{};
     f.k_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_K_CODES]);
     f.k_scale = static_cast<const uint16_t*>(c->buf[KV_BUF_K_SCALE]);
@@ -738,8 +739,9 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     launch_merge(part, rows, part_splits, L.head_dim, L.format, c->rot, out, st);
     return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
   }
-  const bool mfma = sel ? mfma_sparse_ok(L, num_q_heads, q_dtype) : mfma_fast_path_ok(L, num_q_heads, nq, q_dtype);
-  const bool turbo = sel ? turbo_sparse_ok(L, num_q_heads) : turbo_fast_path_ok(L, num_q_heads, nq);
+  const bool mfma =
+      !fp32 && (sel ? mfma_sparse_ok(L, num_q_heads, q_dtype) : mfma_fast_path_ok(L, num_q_heads, nq, q_dtype));
+  const bool turbo = !fp32 && (sel ? turbo_sparse_ok(L, num_q_heads) : turbo_fast_path_ok(L, num_q_heads, nq));
   // FP4 keys read the caller's bf16 queries as they are; every other format
   // first prepares its fp32 query (projection / rotation)
   uint8_t* qpieces = turbo || (mfma && L.format == KV_FMT_QJL1_FP4V)

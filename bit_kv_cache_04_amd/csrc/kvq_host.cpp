@@ -113,7 +113,7 @@ bool mfma_fast_path_ok(const kv_layout& L, int num_q_heads, int nq, int q_dtype)
 }
 
 SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int nq, int q_dtype, int max_seq_len, int requested,
-                      bool general) {
+                      bool general, int max_splits) {
   // Workgroups cover their split in steps of `tile` tokens; aim for enough
   // workgroups to keep a 256-CU part busy several times over, but no split
   // shorter than a few steps.
@@ -135,7 +135,7 @@ SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int nq, int q_dtype, 
     long maxs = (max_seq_len + tile - 1) / tile;  // at least one tile per split
     splits = (int)std::max(1L, std::min(want, maxs));
   }
-  if (splits > 1024) splits = 1024;
+  if (splits > max_splits) splits = max_splits;
   if (splits > max_seq_len) splits = max_seq_len;
   if (splits < 1) splits = 1;
   int per = (max_seq_len + splits - 1) / splits;

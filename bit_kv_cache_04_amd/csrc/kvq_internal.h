@@ -61,9 +61,13 @@ bool latent_fast_path_ok(const kv_layout& L, int num_q_heads, int nq, int q_dtyp
 // Columns of the matrix-core kernel that takes n (query, head) pairs, n <= 32:
 // n rounded up to 1, 2, 4, 8, 16 or 32 (two blocks of 16, FP4 keys only).
 int mfma_columns(int n);
-// general: the plan of the general kernel (sparse decode), whatever the layout
+// Partial rows a decode call may write per (sequence, query): the merge keeps
+// each split's (max, sum) in LDS arrays of this length.
+constexpr int kMaxPartSplits = 1024;
+// general: the plan of the general kernel (sparse decode), whatever the layout;
+// max_splits: the most splits the plan may use (at most kMaxPartSplits)
 SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int nq, int q_dtype, int max_seq_len, int requested,
-                      bool general = false);
+                      bool general = false, int max_splits = kMaxPartSplits);
 
 // Workspace of a decode call: prepared queries, then per-split partial results
 // (running max, running sum, unnormalised output) — offsets in bytes.
@@ -92,7 +96,7 @@ int launch_append(const kv_cache* c, const void* k, const void* v, int in_dtype,
 int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads, int nq,
                   const int32_t* seq_lens, int max_seq_len, float scale, float* out, void* ws,
                   const SplitPlan& plan, const DecodeWorkspace& wsl, void* ev_begin, void* ev_end,
-                  void* stream, const int32_t* sel = nullptr, int sel_stride = 0);
+                  void* stream, const int32_t* sel = nullptr, int sel_stride = 0, bool fp32 = false);
 // Sparse decode of a contiguous latent cache runs on the latent matrix-core
 // kernel, whose splits stage at most this many selected positions each.
 constexpr int kLatentSparseSlots = 512;

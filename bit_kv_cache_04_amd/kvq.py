@@ -24,7 +24,7 @@ BUFFERS = ["k_codes", "k_scale", "k_zero", "k_sketch", "k_norm", "k_rnorm",
 EXPORTED = ["kv_buffer_bytes", "kv_bytes_per_token", "kv_quant_append", "kv_quant_append_ragged", "kv_decode_attention",
             "kv_lloyd_max_gaussian", "kv_make_rotation", "kv_make_hadamard_rotation",
             "kv_make_projection", "kv_status_string", "kv_hsi_candidates", "kv_hsi_select",
-            "kv_decode_attention_sparse"]
+            "kv_decode_attention_sparse", "kv_stream_read"]
 
 
 class KvError(RuntimeError):
@@ -48,9 +48,12 @@ class KVCache(ctypes.Structure):
                 ("block_table", ctypes.c_void_p)]
 
 
+DECODE_FP32 = 1  # enum kv_decode_flags
+
+
 class KVDecodeOpts(ctypes.Structure):
     _fields_ = [("num_splits", ctypes.c_int32), ("ev_begin", ctypes.c_void_p), ("ev_end", ctypes.c_void_p),
-                ("num_queries", ctypes.c_int32)]
+                ("num_queries", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 _lib = None
@@ -92,6 +95,8 @@ def lib():
         L.kv_decode_attention_sparse.argtypes = [ctypes.POINTER(KVCache), vp, i32, i32, vp, vp, i32, ctypes.c_float,
                                                  vp, vp, ctypes.POINTER(sz), ctypes.POINTER(KVDecodeOpts), vp]
         L.kv_decode_attention_sparse.restype = ctypes.c_int
+        L.kv_stream_read.argtypes = [vp, sz, vp, vp]
+        L.kv_stream_read.restype = ctypes.c_int
         L.kv_status_string.argtypes = [ctypes.c_int]
         L.kv_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -210,3 +215,8 @@ def kv_decode_attention_sparse(cache: KVCache, q_ptr, q_dtype, num_q_heads, sel_
 
 def kv_status_string(status: int) -> str:
     return lib().kv_status_string(status).decode()
+
+
+def kv_stream_read(src_ptr, nbytes, sink_ptr, stream=0):
+    """The streaming-read reference kernel (kvq_probe.h)."""
+    _check("kv_stream_read", lib().kv_stream_read(src_ptr, nbytes, sink_ptr, stream))

@@ -191,8 +191,12 @@ typedef struct kv_cache {
 } kv_cache;
 
 /* Options for kv_decode_attention; pass NULL for defaults.
- *   num_splits   context splits per (sequence, KV head); 0 picks one from the
- *                shape; the workspace size depends on it
+ *   num_splits   context splits per (sequence, KV head), 0..1024; 0 picks one
+ *                from the shape; the workspace size depends on it.  With bf16
+ *                windows the window takes (sink_tokens + recent_tokens) / 64
+ *                (rounded up) more splits and the packed splits are capped at
+ *                1024 minus those; a window of more than 65,472 tokens is
+ *                KV_EUNSUPPORTED
  *   ev_begin/end optional hipEvent_t recorded on `stream` immediately before
  *                and after the split-context attention kernel (for timing)
  *   num_queries  query tokens per sequence, 1..64 (0 means 1): several drafted
@@ -202,12 +206,24 @@ typedef struct kv_cache {
  *                several positions at once).  The queries are the last
  *                num_queries tokens of each sequence, already appended; query j
  *                sees the first seq_lens[b] - (num_queries - 1 - j) tokens.
- *                The workspace size depends on it. */
+ *                The workspace size depends on it.
+ *   flags        0, or KV_DECODE_FP32: dequantise and compute on the fp32
+ *                vector kernel for every format (slower).
+ * Range of the default path: FP4 keys and values and the LATENT latent feed the
+ * matrix cores as fp16, where E2M1 x bf16 scale is exact when every group scale
+ * s = bf16(absmax / 6) is 0 or lies in [2^-16, 65504 / 6] (absmax from about
+ * 5.5e-4 to 65504), and a bf16 query is exact in fp16 when each |q| is 0 or
+ * lies in [2^-17, 65504].  Outside those ranges values round like fp16 (a
+ * group absmax or query above 65504 becomes infinite); a cache or query that
+ * may leave them is decoded exactly with KV_DECODE_FP32.  fp32 queries always
+ * take the fp32 kernel for FP4 and LATENT caches. */
+enum kv_decode_flags { KV_DECODE_FP32 = 1 };
 typedef struct kv_decode_opts {
   int32_t num_splits;
   void* ev_begin;
   void* ev_end;
   int32_t num_queries;
+  int32_t flags;
 } kv_decode_opts;
 
 /* Bytes of one buffer of a cache with this layout; 0 if the format has no
@@ -361,7 +377,9 @@ int kv_hsi_select(const float* pool_scores, const int32_t* pool, const int32_t* 
  * rows on pages outside a paged pool) are skipped; a sequence with none left
  * gets zeros.  KIVI2 keys past a sequence's coded groups come from K_STAGE as
  * in dense decode.  Caches with bf16 windows and opts->num_queries > 1 are
- * KV_EUNSUPPORTED.  The workspace size (a call with ws NULL) depends on
+ * KV_EUNSUPPORTED, and so is sel_cap > 524,288 on a contiguous FP4, QJL1,
+ * TURBO or LATENT cache (their kernels stage at most 512 positions per split,
+ * 1024 splits).  The workspace size (a call with ws NULL) depends on
  * sel_cap and opts->num_splits. */
 int kv_decode_attention_sparse(const kv_cache* c, const void* q, int32_t q_dtype, int32_t num_q_heads,
                                const int32_t* sel, const int32_t* sel_n, int32_t sel_cap, float softmax_scale,

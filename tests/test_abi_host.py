@@ -16,15 +16,18 @@ from oracle.lloyd_max import canonical_codebook
 from oracle.numerics import round_bf16
 from oracle.rotation import canonical_hadamard_rotation, canonical_rotation
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "kvq.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADERS = sorted(os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h"))
 
 OK, EINVAL, ECAP, EUNSUP, EWS = 0, -1, -2, -3, -4
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(kv_\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(kv_\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
@@ -111,8 +114,8 @@ def test_status_strings():
 FAKE = 0x10000  # never dereferenced: every call below fails validation first
 
 
-def _cache(fmt="fp4", B=2, H=2, d=128, T=64, rope=0, fill=True, consts=True):
-    lay = kvq.make_layout(fmt, B, H, d, T, rope)
+def _cache(fmt="fp4", B=2, H=2, d=128, T=64, rope=0, fill=True, consts=True, recent=0):
+    lay = kvq.make_layout(fmt, B, H, d, T, rope, recent=recent)
     bufs = (ctypes.c_void_p * len(kvq.BUFFERS))(
         *[(FAKE if fill and kvq.kv_buffer_bytes(lay, i) else None) for i in range(len(kvq.BUFFERS))])
     c = FAKE if consts else None
@@ -125,9 +128,9 @@ def _append(c, k=FAKE, v=FAKE, dt=kvq.DT_BF16, start=0, n=1):
 
 
 def _decode(c, q=FAKE, qdt=kvq.DT_BF16, hq=4, lens=FAKE, maxlen=64, scale=1.0, out=FAKE, ws=None,
-            wsb=0, splits=0, nq=0):
+            wsb=0, splits=0, nq=0, flags=0):
     nb = ctypes.c_size_t(wsb)
-    opts = kvq.KVDecodeOpts(splits, None, None, nq)
+    opts = kvq.KVDecodeOpts(splits, None, None, nq, flags)
     st = kvq.lib().kv_decode_attention(ctypes.byref(c), q, qdt, hq, lens, maxlen, ctypes.c_float(scale), out,
                                        ws, ctypes.byref(nb), ctypes.byref(opts), None)
     return st, nb.value
@@ -295,3 +298,31 @@ def test_sparse_decode_validation_and_size():
     bufs = (ctypes.c_void_p * len(kvq.BUFFERS))(
         *[(FAKE if kvq.kv_buffer_bytes(lay, i) else None) for i in range(len(kvq.BUFFERS))])
     assert sparse(kvq.KVCache(lay, bufs, None, None, None, None, None))[0] == EUNSUP
+
+
+def test_stream_read_validation():
+    L = kvq.lib()
+    assert L.kv_stream_read(None, 1024, FAKE, None) == EINVAL
+    assert L.kv_stream_read(FAKE, 1024, None, None) == EINVAL
+    assert L.kv_stream_read(FAKE + 8, 1024, FAKE, None) == EINVAL       # misaligned
+    assert L.kv_stream_read(FAKE, 1000, FAKE, None) == EINVAL           # not whole 16-byte words
+    assert L.kv_stream_read(FAKE, 0, FAKE, None) == EINVAL
+
+
+def test_decode_split_cap_with_windows():
+    # the merge holds at most 1024 partial rows per query: the packed splits
+    # yield to the window's 64-position splits, and a window of 1024 such
+    # splits or more is refused
+    T = 1 << 17
+    _, nb_plain = _decode(_cache("fp4", T=T), ws=None, splits=1024, maxlen=T)
+    st, nb_win = _decode(_cache("fp4", T=T, recent=64 * 8), ws=None, splits=1024, maxlen=T)
+    assert st == OK and nb_win <= nb_plain                            # at most 1016 packed + 8 window splits
+    assert _decode(_cache("fp4", T=T, recent=64 * 1024), ws=None, maxlen=T)[0] == EUNSUP
+    assert _decode(_cache("fp4", T=T, recent=64 * 1023), ws=None, maxlen=T)[0] == OK
+
+
+def test_decode_flags_validation():
+    c = _cache()
+    assert _decode(c, ws=None, flags=kvq.DECODE_FP32)[0] == OK
+    assert _decode(c, flags=2)[0] == EINVAL                            # unknown flag bits
+    assert _decode(c, flags=-1)[0] == EINVAL

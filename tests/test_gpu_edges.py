@@ -1,0 +1,271 @@
+"""GPU parity at the encoders' and the decode kernels' edges.
+
+* The FP4 encoder for bf16 inputs (a reciprocal product, a 16-bit snap and
+  the hardware E2M1 conversion inside [2^-100, 2^100], exact compares outside)
+  over every finite bf16 value in [-A, A] for group maxima A of every bf16
+  mantissa at six exponents on both sides of 2^-100 and 2^100, plus subnormal,
+  smallest-normal and largest-exponent maxima: bytes equal the oracle's.
+* KIVI-2 groups at the edges of the reading (fp32 min / max, s = (max - min) / 3,
+  codes by round-half-even of (x - z) / s): constant groups (s = 0), inputs whose
+  quotient is exactly c + 0.5, signed zeros; aligned and staged appends, fp32 and
+  bf16 inputs; bytes equal the oracle's and decode is within the row bar.
+* The fp16 range of the matrix-core decode (FP4 and the shared latent): data at
+  the edges of the documented exact range pass on the default path; data beyond
+  it (group maxima 1e5 and 1e-6, queries 1e5) pass with KV_DECODE_FP32.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from bit_kv_cache_04_amd import kvq
+from gpu_helpers import (RTOL, assert_bytes_equal, gpu_buffers, host64, new_cache, oracle_constants, oracle_encode,
+                         row_rel_err, softmax_scale)
+from oracle import attention as OA
+from oracle import formats as OF
+
+pytestmark = pytest.mark.gpu
+
+C = synth.CONFIGS
+
+
+# ---------------------------------------------------------------- FP4 exhaustive bf16 sweep
+
+def _positive_bf16():
+    """+0 and every finite positive bf16 value, ascending, as float64."""
+    bits = np.arange(0, 0x7F80, dtype=np.uint32) << 16
+    return bits.view(np.float32).astype(np.float64)
+
+
+def _bf16_of(e_field, m_field):
+    return float(np.array([(e_field << 23) | (m_field << 16)], np.uint32).view(np.float32)[0])
+
+
+def _sweep_groups():
+    """[N, 16] float64 groups: for each maximum A, every finite bf16 in [-A, A]
+    (both zeros included) 15 to a group, each group holding +-A once."""
+    pos = _positive_bf16()
+    maxima = []
+    for e in (-101, -100, -1, 0, 99, 100):
+        maxima += [_bf16_of(e + 127, m) for m in range(128)]
+    maxima += [_bf16_of(0, m) for m in range(8, 128, 8)]      # subnormal maxima
+    maxima += [_bf16_of(1, m) for m in range(0, 128, 8)]      # smallest normal exponent
+    maxima += [_bf16_of(254, m) for m in range(0, 128, 8)]    # largest exponent
+    groups = []
+    for a in maxima:
+        v = pos[pos <= a]
+        vals = np.concatenate([v, -v])                        # -v[0] is -0.0
+        pad = (-len(vals)) % 15
+        vals = np.concatenate([vals, np.zeros(pad)]).reshape(-1, 15)
+        n = vals.shape[0]
+        sign = np.where(np.arange(n) % 2 == 0, 1.0, -1.0)
+        base = np.concatenate([(sign * a)[:, None], vals], axis=1)   # +-A in column 0
+        roll = (np.arange(16)[None, :] - (np.arange(n) % 16)[:, None]) % 16
+        groups.append(base[np.arange(n)[:, None], roll])       # +-A moved to column j % 16
+    return np.concatenate(groups)
+
+
+def test_fp4_encoder_exhaustive_bf16_sweep():
+    groups = _sweep_groups()
+    d = 128
+    T = -(-groups.shape[0] // (d // 16))
+    T = -(-T // 32) * 32
+    x = np.zeros((T * d // 16, 16))
+    x[:groups.shape[0]] = groups
+    K = x.reshape(1, 1, T, d)
+    V = K[:, :, ::-1].copy()                                 # the same groups, in another order
+    print(f"[fp4 sweep] {groups.shape[0]} groups, {T} tokens", flush=True)
+    Kd = torch.from_numpy(K).to(torch.float32).to(torch.bfloat16).cuda()
+    Vd = torch.from_numpy(V).to(torch.float32).to(torch.bfloat16).cuda()
+    assert torch.equal(Kd.double().cpu(), torch.from_numpy(K)), "sweep values are bf16"
+    cfg = C["fp4_b16_t32k"].scaled(batch=1, hq=1, hkv=1, context=T)
+    cache = new_cache(cfg)
+    cache.append(Kd, Vd, 0)
+    torch.cuda.synchronize()
+    got = gpu_buffers(cache)
+    step = 16384
+    for t0 in range(0, T, step):
+        t1 = min(T, t0 + step)
+        for name, src in (("k", K), ("v", V)):
+            codes, scale = OF.fp4_encode(src[:, :, t0:t1])
+            for part, want in (("codes", codes), ("scale", scale)):
+                g = got[f"{name}_{part}"][:, :, t0:t1]
+                bad = np.count_nonzero(g != want.astype(g.dtype))
+                assert bad == 0, f"{name}_{part} tokens [{t0}, {t1}): {bad} differ"
+
+
+# ---------------------------------------------------------------- KIVI-2 edges
+
+def _tie_inputs(dtype, m, M, targets=(0.5, 1.5, 2.5)):
+    """Values x in [m, M] (representable in dtype) whose fp32 quotient
+    fl32(fl32(x - m) / s), s = fl32(fl32(M - m) / 3), is exactly each target."""
+    f = np.float32
+    m, M = f(m), f(M)
+    s = f(f(M - m) / f(3))
+    out = []
+    for t in targets:
+        x0 = f(m + f(t) * s)
+        # look through the neighbours of x0 in the input dtype
+        step = 1 if dtype == torch.float32 else 1 << 16
+        u0 = int(np.array([x0], f).view(np.uint32)[0]) & (~(step - 1) & 0xFFFFFFFF)
+        found = None
+        for k in range(-64, 65):
+            u = (u0 + k * step) & 0xFFFFFFFF
+            x = np.array([u], np.uint32).view(f)[0]
+            if not (m <= x <= M):
+                continue
+            if f(f(x - m) / s) == f(t):
+                found = x
+                break
+        if found is not None:
+            out.append(float(found))
+    return out
+
+
+def _kivi_edge_inputs(dtype, seed):
+    """K, V [1, 2, 256, 64] with planted edge groups over N(0, 1)."""
+    rng = np.random.default_rng(seed)
+    K = rng.standard_normal((1, 2, 256, 64))
+    V = rng.standard_normal((1, 2, 256, 64))
+    # keys: channel c of head h over a 32-token group
+    K[0, 0, 0:32, 0] = 1.25                                   # constant group: s = 0, codes 0, dequant z
+    K[0, 0, 0:32, 1] = -3.0
+    K[0, 0, 0:32, 2] = -0.0                                   # constant negative zero
+    K[0, 1, :, 10] = 7.5                                      # a constant channel over every group
+    grid = -2.0 + 0.5 * np.array([0, 0.5, 1, 1.5, 2, 2.5, 3])  # quotients 0, .5, ..., 3 (power-of-two s)
+    K[0, 0, 32:64, 3] = np.resize(grid, 32)
+    # s = 1.125 / 3 = 0.375 (not a power of two) and quotients exactly 0.5, 1.5, 2.5
+    exact = [0.0, 1.125, 0.1875, 0.5625, 0.9375]
+    K[0, 1, 64:96, 4] = np.resize(np.array(exact), 32)
+    if dtype == torch.float32:
+        # an inexact s (0.9 / 3 in fp32) with inputs whose fp32 quotient is exactly c + 0.5
+        K[0, 1, 96:128, 8] = np.resize(np.array([0.1, 1.0] + _tie_inputs(dtype, 0.1, 1.0)), 32)
+    zz = np.resize(np.array([-2.0, 3.0, -0.0, 0.0, -0.0, 1.0]), 32)  # signed zeros between min and max
+    K[0, 0, 96:128, 5] = zz
+    K[0, 1, 128:160, 6] = np.resize(np.array([-0.0, 0.5, 1.5, 3.0]), 32)    # -0 the only zero, the minimum
+    K[0, 0, 160:192, 7] = np.resize(np.array([-3.0, -1.0, -0.0, -2.5]), 32)  # -0 the maximum
+    # values: 32-channel groups of one token
+    V[0, 0, 3, 0:32] = 2.0
+    V[0, 1, 4, 32:64] = np.resize(grid, 32)
+    V[0, 0, 5, 0:32] = -0.0
+    V[0, 1, 6, 0:32] = np.resize(np.array([-3.0, -1.0, -0.0, -0.75]), 32)
+    V[0, 0, 7, 32:64] = np.resize(np.array(exact), 32)
+    V[0, 1, 8, 0:32] = np.resize(np.array([-2.0, 3.0, -0.0, 0.0, 1.0]), 32)
+    V[0, 0, 9, 0:32] = 0.0
+    return K, V
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("chunks", [[256], [77, 31, 100, 48], [5, 27, 1, 31, 192]])
+def test_kivi_edge_groups_bit_exact(dtype, chunks):
+    cfg = C["kivi2_tiny"]
+    K, V = _kivi_edge_inputs(dtype, 3)
+    Kd = torch.from_numpy(K).to(torch.float32).to(dtype).cuda()
+    Vd = torch.from_numpy(V).to(torch.float32).to(dtype).cuda()
+    # the planted zeros keep their signs through the cast
+    assert np.signbit(host64(Kd)[0, 0, 0:32, 2]).all()
+    print(f"[kivi edges] {dtype} {chunks}", flush=True)
+    cache = new_cache(cfg)
+    t0 = 0
+    for n in chunks:
+        cache.append(Kd[:, :, t0:t0 + n].contiguous(), Vd[:, :, t0:t0 + n].contiguous(), t0)
+        t0 += n
+    torch.cuda.synchronize()
+    enc = oracle_encode(cfg, host64(Kd), host64(Vd), {})
+    assert_bytes_equal(gpu_buffers(cache), enc, f"kivi edges {chunks}")
+    # the planted cases really are what they claim (oracle reading)
+    assert (enc["k_scale"][0, 0, 0, :3] == 0).all()
+    assert np.signbit(enc["k_zero"][0, 0, 0, 2])
+    q = synth.make_queries(cfg, device="cuda")
+    lens = np.array([256], np.int32)
+    out = cache.decode(q, torch.from_numpy(lens).cuda(), softmax_scale(cfg)).cpu().numpy()
+    ref = OA.decode_attention("kivi2", enc, host64(q), lens, softmax_scale(cfg), cfg.hkv)
+    assert row_rel_err(out, ref).max() <= RTOL
+
+
+def test_kivi_tie_construction_is_exact():
+    """The tie inputs used above do give quotients exactly c + 0.5 in fp32."""
+    f = np.float32
+    ties = _tie_inputs(torch.float32, 0.1, 1.0)
+    assert len(ties) >= 1, ties
+    s = f(f(f(1.0) - f(0.1)) / f(3))
+    for x in ties:
+        q = f(f(f(x) - f(0.1)) / s)
+        assert q - np.floor(q) == 0.5
+    s = f(f(f(1.125) - f(0.0)) / f(3))
+    assert s == f(0.375)
+    assert [f(f(x) / s) for x in (0.1875, 0.5625, 0.9375)] == [0.5, 1.5, 2.5]
+
+
+# ---------------------------------------------------------------- fp16 range of the matrix-core decode
+
+def _scaled_groups(x, group, mags, rng):
+    """Scale each `group`-channel group of x so that its absmax is one of mags."""
+    shp = x.shape
+    g = x.reshape(-1, group)
+    amax = np.abs(g).max(-1, keepdims=True)
+    target = rng.choice(np.asarray(mags, np.float64), size=(g.shape[0], 1))
+    return (g / amax * target).reshape(shp)
+
+
+def _bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(torch.float32).to(torch.bfloat16).cuda()
+
+
+# per sequence: (key group maxima, query max, value group maxima); logits stay O(10)
+RANGE_CASES = {
+    # both ends of the documented exact range on the default path: small keys and
+    # values under a large query, large keys and values under a small query
+    "edge_fast": [([6.0e-4, 8.0e-4], 6.0e4, [5.6e-4, 7.0e-4]), ([3.0e4, 6.0e4], 1e-4, [3.0e4, 6.0e4])],
+    # beyond it, with KV_DECODE_FP32 (the fp32 vector kernel)
+    "beyond_fp32": [([1e-6, 3e-7], 1e5, [1e-6, 3e-7]), ([1e5, 2e5], 1e-5, [1e5, 3e5])],
+}
+
+
+@pytest.mark.parametrize("case", list(RANGE_CASES))
+def test_fp4_decode_fp16_range(case):
+    cfg = C["fp4_b16_t32k"].scaled(batch=2, hq=8, hkv=2, context=300)
+    rng = np.random.default_rng(5)
+    K = rng.standard_normal((2, 2, 300, 128))
+    V = rng.standard_normal((2, 2, 300, 128))
+    q = rng.standard_normal((2, 8, 128))
+    for b, (kmag, qmax, vmag) in enumerate(RANGE_CASES[case]):
+        K[b] = _scaled_groups(K[b], 16, kmag, rng)
+        V[b] = _scaled_groups(V[b], 16, vmag, rng)
+        q[b] = q[b] / np.abs(q[b]).max() * qmax
+    flags = kvq.DECODE_FP32 if case == "beyond_fp32" else 0
+    Kd, Vd, qd = _bf16(K), _bf16(V), _bf16(q)
+    cache = new_cache(cfg)
+    cache.append(Kd, Vd, 0)
+    enc = oracle_encode(cfg, host64(Kd), host64(Vd), {})
+    assert_bytes_equal(gpu_buffers(cache), enc, f"fp4 range {case}")
+    lens = np.array([300, 171], np.int32)
+    out = cache.decode(qd, torch.from_numpy(lens).cuda(), softmax_scale(cfg), flags=flags).cpu().numpy()
+    ref = OA.decode_attention("fp4", enc, host64(qd), lens, softmax_scale(cfg), cfg.hkv)
+    err = row_rel_err(out, ref)
+    print(f"[fp4 range {case}] max row rel err {err.max():.3e}", flush=True)
+    assert np.isfinite(out).all() and err.max() <= RTOL
+
+
+@pytest.mark.parametrize("case", list(RANGE_CASES))
+def test_latent_decode_fp16_range(case):
+    cfg = C["latent_b64_t64k"].scaled(batch=2, hq=32, context=200)
+    rng = np.random.default_rng(6)
+    lat = rng.standard_normal((2, 200, 576))
+    q = rng.standard_normal((2, 32, 576))
+    for b, (kmag, qmax, _) in enumerate(RANGE_CASES[case]):
+        lat[b, :, :512] = _scaled_groups(lat[b, :, :512], 16, kmag, rng)
+        q[b, :, :512] = q[b, :, :512] / np.abs(q[b, :, :512]).max() * qmax
+    flags = kvq.DECODE_FP32 if case == "beyond_fp32" else 0
+    latd, qd = _bf16(lat), _bf16(q)
+    cache = new_cache(cfg)
+    cache.append(latd, None, 0)
+    enc = oracle_encode(cfg, host64(latd), None, {})
+    assert_bytes_equal(gpu_buffers(cache), enc, f"latent range {case}")
+    lens = np.array([200, 77], np.int32)
+    out = cache.decode(qd, torch.from_numpy(lens).cuda(), softmax_scale(cfg), flags=flags).cpu().numpy()
+    ref = OA.decode_attention("latent", enc, host64(qd), lens, softmax_scale(cfg), 1, latent_dim=512)
+    err = row_rel_err(out, ref)
+    print(f"[latent range {case}] max row rel err {err.max():.3e}", flush=True)
+    assert np.isfinite(out).all() and err.max() <= RTOL
