@@ -81,6 +81,8 @@ constexpr int kPieceProductBytes = 4 * 144;
 constexpr int kTurboPieceBytes = 3 * kPieceProductBytes;  // code words 0..3, 4..7, sketch
 constexpr int kQjlPieceBytes = kPieceProductBytes;        // sketch
 DecodeWorkspace decode_workspace(const kv_layout* L, int num_q_heads, int splits);
+// Size of the library's own decode workspace (kv_decode_attention_static).
+constexpr size_t kStaticWorkspaceBytes = size_t(128) << 20;
 // Mixed precision: splits of partial rows the bf16 window takes (one per 64 of
 // its sink_tokens + recent_tokens positions), 0 without a window.
 inline int window_chunks(const kv_layout& L) { return (L.sink_tokens + L.recent_tokens + 63) / 64; }

@@ -24,7 +24,7 @@ BUFFERS = ["k_codes", "k_scale", "k_zero", "k_sketch", "k_norm", "k_rnorm",
 EXPORTED = ["kv_buffer_bytes", "kv_bytes_per_token", "kv_quant_append", "kv_quant_append_ragged", "kv_decode_attention",
             "kv_lloyd_max_gaussian", "kv_make_rotation", "kv_make_hadamard_rotation",
             "kv_make_projection", "kv_status_string", "kv_hsi_candidates", "kv_hsi_select",
-            "kv_decode_attention_sparse", "kv_stream_read"]
+            "kv_decode_attention_sparse", "kv_stream_read", "kv_decode_attention_static"]
 
 
 class KvError(RuntimeError):
@@ -95,6 +95,9 @@ def lib():
         L.kv_decode_attention_sparse.argtypes = [ctypes.POINTER(KVCache), vp, i32, i32, vp, vp, i32, ctypes.c_float,
                                                  vp, vp, ctypes.POINTER(sz), ctypes.POINTER(KVDecodeOpts), vp]
         L.kv_decode_attention_sparse.restype = ctypes.c_int
+        L.kv_decode_attention_static.argtypes = [ctypes.POINTER(KVCache), vp, i32, i32, vp, i32, ctypes.c_float, vp,
+                                                 ctypes.POINTER(KVDecodeOpts), vp]
+        L.kv_decode_attention_static.restype = ctypes.c_int
         L.kv_stream_read.argtypes = [vp, sz, vp, vp]
         L.kv_stream_read.restype = ctypes.c_int
         L.kv_status_string.argtypes = [ctypes.c_int]
@@ -220,3 +223,12 @@ def kv_status_string(status: int) -> str:
 def kv_stream_read(src_ptr, nbytes, sink_ptr, stream=0):
     """The streaming-read reference kernel (kvq_probe.h)."""
     _check("kv_stream_read", lib().kv_stream_read(src_ptr, nbytes, sink_ptr, stream))
+
+
+def kv_decode_attention_static(cache: KVCache, q_ptr, q_dtype, num_q_heads, seq_lens_ptr, max_seq_len, scale,
+                               out_ptr, opts=None, stream=0):
+    """kv_decode_attention on the library's own device workspace (allocates nothing)."""
+    st = lib().kv_decode_attention_static(ctypes.byref(cache), q_ptr, q_dtype, num_q_heads, seq_lens_ptr,
+                                          max_seq_len, ctypes.c_float(scale), out_ptr,
+                                          ctypes.byref(opts) if opts is not None else None, stream)
+    _check("kv_decode_attention_static", st)

@@ -304,6 +304,23 @@ int kv_decode_attention(const kv_cache* c, const void* q, int32_t q_dtype, int32
                         float* out, void* ws, size_t* ws_bytes, const kv_decode_opts* opts,
                         void* stream);
 
+/* kv_decode_attention without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The workspace is the library's own
+ * device array of 128 MiB, one per GPU, held until the process ends; it is
+ * looked up (never allocated) on the first call on each device, and this call
+ * allocates and frees nothing.  Every call on a GPU uses that GPU's array, so
+ * calls that overlap on one GPU (on different streams, or from several host
+ * threads) race; calls in stream order do not.  Nothing in it has to start at
+ * zero: each call writes every partial result it reads.
+ * Arguments, behaviour and errors as kv_decode_attention, on the current
+ * device, plus: a call whose workspace (the size kv_decode_attention reports
+ * for it) exceeds 128 MiB is KV_EWORKSPACE, and a failed lookup of the array is
+ * KV_EDEVICE. */
+int kv_decode_attention_static(const kv_cache* c, const void* q, int32_t q_dtype, int32_t num_q_heads,
+                               const int32_t* seq_lens, int32_t max_seq_len, float softmax_scale,
+                               float* out, const kv_decode_opts* opts, void* stream);
+
 /* ---- the method's constants (host memory, host only) ---- */
 
 /* Lloyd-Max quantiser for N(0, 1/dim) with 2^bits levels: the fixed point of

@@ -326,3 +326,18 @@ def test_decode_flags_validation():
     assert _decode(c, ws=None, flags=kvq.DECODE_FP32)[0] == OK
     assert _decode(c, flags=2)[0] == EINVAL                            # unknown flag bits
     assert _decode(c, flags=-1)[0] == EINVAL
+
+
+def test_static_decode_validation_before_any_gpu_call():
+    # the size and argument checks come before the workspace lookup: no GPU needed
+    L = kvq.lib()
+    c = _cache("latent", B=64, H=1, d=512, T=1 << 16, rope=64)
+    opts = kvq.KVDecodeOpts(0, None, None, 4, 0)                     # four queries: 4x the partial rows
+    st = L.kv_decode_attention_static(ctypes.byref(c), FAKE, kvq.DT_BF16, 128, FAKE, 1 << 16, ctypes.c_float(1.0),
+                                      FAKE, ctypes.byref(opts), None)
+    assert st == EWS                                                  # beyond the 128 MiB array
+    c = _cache()
+    assert L.kv_decode_attention_static(ctypes.byref(c), None, kvq.DT_BF16, 4, FAKE, 64, ctypes.c_float(1.0),
+                                        FAKE, None, None) == EINVAL
+    assert L.kv_decode_attention_static(ctypes.byref(c), FAKE, kvq.DT_BF16, 3, FAKE, 64, ctypes.c_float(1.0),
+                                        FAKE, None, None) == EINVAL
