@@ -249,7 +249,7 @@ def stream_read_reference(torch, kvq, dev, flush, steps):
                max(steps, 10), flush)
     med = statistics.median(ms)
     gbs = buf.numel() * 4 / (med * 1e-3) / 1e9
-    return {"kernel": "stream_read_kernel (16-byte loads, 8 in flight per thread)", "bytes": buf.numel() * 4,
+    return {"kernel": "stream_read_kernel (16-byte loads, 8 in flight per thread, a contiguous run per workgroup)", "bytes": buf.numel() * 4,
             "us_median": round(med * 1e3, 2), "us_min": round(min(ms) * 1e3, 2), "gbs": round(gbs, 1),
             "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
