@@ -7,22 +7,25 @@
 //
 // With 128 query heads on one latent the per-token work is a dense contraction
 // (2 x 128 x (576 + 512) flop per 448 packed bytes), far past the HBM ridge, so
-// the whole tile math runs on v_mfma_f32_16x16x32_{f16,bf16}.
+// the whole tile math runs on v_mfma_f32_32x32x16_{f16,bf16}.
 //
-// One workgroup = one (sequence, context split), all Hq = 16 * NW query heads,
-// NW waves: with 128 heads, 8 waves, two per SIMD, so that one wave's
-// dequantisation, softmax and LDS reads overlap the other's matrix products.
-// Wave w owns heads [16 w, 16 w + 16) end to end: its query operand (72
-// registers) and its 16 x 512 fp32 output accumulators (128 registers) stay in
-// registers for the whole split.  Per 32-token tile i, after one workgroup
-// barrier:
-//   1. the loads of tile i + 3 are issued into the stage tile i has freed
-//      (direct-to-LDS, three stages in flight);
-//   2. every thread dequantises its share of tile i + 1 into the other of two
-//      token-major fp16 tiles (RoPE copied as bf16);
-//   3. S^T = K Q^T for the wave's heads: 2 x 18 products on tile i;
-//   4. online softmax per head (each head's 32 logits spread over 4 lanes);
-//   5. O += P V: 32 products, V read transposed from tile i (ds_read_b64_tr_b16).
+// One workgroup = one (sequence, context split), 4 waves, one per SIMD.  Wave w
+// owns heads [32 w, 32 w + 32) (Hq = 32 or 64: the waves past the heads repeat
+// the last head group's work and write nothing): its query operand (144 registers) and its 32 x 512 fp32
+// output accumulators (256 registers) stay in registers for the whole split.
+// Every wave reads the whole dequantised tile from LDS, so the fewer, wider waves
+// keep the LDS instructions per tile (next to the matrix cores, the binding
+// resource) at half those of sixteen-head waves.
+//
+// The packed tiles come into registers by plain buffer loads, one tile ahead
+// (each thread its 1/256 of the tile), and are dequantised from there into one
+// of three token-major fp16 tiles in LDS.  Per 32-token tile i, after one
+// workgroup barrier, each wave:
+//   1. S^T = K Q^T on tile i (36 products);
+//   2. dequantises its share of tile i + 1, then loads its share of tile i + 2;
+//   3. online softmax (each lane pair holds one head; the reference max moves
+//      only when a tile max passes it by 2^8, then the accumulators rescale);
+//   4. O += P V (32 products, V read transposed with ds_read_b64_tr_b16).
 // FP4 element values times their bf16 scale are exact in fp16 (within its range);
 // the bf16 query's latent part is exact in fp16 within the fp16 normal range.
 #include <hip/hip_runtime.h>
@@ -38,28 +41,33 @@ namespace {
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
-typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef float f16v_t __attribute__((ext_vector_type(16)));
 typedef short s4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef int v4i_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s4_t* lds_s4_ptr;
 
+constexpr int kNT = 256;  // threads per workgroup: 4 waves
 constexpr int kTile = 32;
 constexpr int kLat = 512, kRope = 64;
-constexpr int kStages = 3;
-// packed stage: codes 32 x 256 | scales 32 x 64 | RoPE 32 x 128
-constexpr int kStCodes = 0, kStScale = 8192, kStRope = 10240, kStBytes = 14336;
+constexpr int kBufs = 3;  // dequantised tiles in LDS
 // Kt: 32 token rows of 576 halves (fp16 latent, then bf16 RoPE), row stride
-// 73 x 16 bytes.  Token t lives in row kt_phys(t): tokens 8j..8j+7 of each
-// 16-token half on the even (j even) or odd (j odd) rows of that half.  Then the
-// 16 rows a QK operand read touches (tokens 0-15 or 16-31) fall in 16 distinct
-// 16-byte bank groups, and the 8 rows of a transposing PV read's 32 lanes
-// (tokens 8j..8j+7) start on 8 distinct even (or odd) bank groups, their 32-byte
-// spans disjoint.
+// 73 x 16 bytes.  Token t = 16 c + 8 h + 4 h2 + e (e < 4) lives in row
+// kt_phys(t) = 16 c + 8 h2 + 2 e + h, chosen so that both readers see distinct
+// bank groups: the QK operand (lanes of 8 read 8 rows differing in e and h) and
+// the transposing PV reads (4 rows differing in e, 32 bytes each).
 constexpr int kKtStride = kLat + kRope + 8;
 constexpr int kKtHalves = kTile * kKtStride;
 constexpr int kRsrcFlags = 0x00020000;
 
-__host__ __device__ constexpr int kt_phys(int t) { return (t & 16) | ((t & 7) << 1) | ((t >> 3) & 1); }
+__host__ __device__ constexpr int kt_phys(int t) {
+  return (t & 16) | ((t & 4) << 1) | ((t & 3) << 1) | ((t >> 3) & 1);
+}
+
+// Row rho of the QK A operand holds token qk_token(rho) (bits 2 and 3 of rho
+// swapped): then the result rows a lane holds (i % 4 + 8 (i / 4) + 4 (lane / 32),
+// i = 0..15) are the tokens 16 (i / 8) + 8 (lane / 32) + i % 8, exactly the
+// k-slots that lane supplies as the A operand of the two 16-token PV products.
+__host__ __device__ constexpr int qk_token(int rho) { return (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, size_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcFlags);
@@ -86,259 +94,207 @@ __device__ __forceinline__ s4_t read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(p));
 }
 
-// s_waitcnt immediate that waits for vmcnt <= n and nothing else
-constexpr int vmcnt_wait(int n) { return 0x0F70 | (n & 0xF) | ((n >> 4) << 14); }
+// o *= f for one accumulator held in an AGPR, without the compiler staging the
+// whole accumulator array through arch VGPRs.
+__device__ __forceinline__ void scale_acc(float& x, float f) {
+  float t;
+  asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+               : "+a"(x), "=&v"(t)
+               : "v"(f));
+}
 
 struct Res {
   __amdgpu_buffer_rsrc_t codes, scale, rope;
 };
 
-// A tile's loads: resources over its page's token rows (a contiguous cache: the
-// sequence's rows) and its first row in them.
-struct TileSrc {
-  Res r;
-  int t;
+// This thread's share of one packed tile: code chunks of 16 bytes (32 channels
+// of one token: chunk c is token c / 16, channels 32 (c % 16) + [0, 32)), their
+// two bf16 scales (4 bytes), and one 16-byte chunk of the RoPE rows (chunk r is
+// token r / 8, channels 8 (r % 8) + [0, 8)).  Chunks c = tid and tid + 256,
+// RoPE chunk r = tid.
+struct Packed {
+  v4i_t c[2];
+  int s[2];
+  v4i_t r;
 };
 
-// Direct-to-LDS loads of one packed tile, spread evenly over the NW waves
-// (32 / NW loads each).  The token offset rides in the range-checked VGPR
-// offset: a tile at or past the end of the resources reads zeros.
-template <int NW>
-__device__ __forceinline__ void issue_tile(uint8_t* st, int wave, int lane, int t0, const Res& r) {
+// Loads of this thread's share of a tile whose token k (of 32) sits at token
+// offset tok(k) of the resources (tok < 0, or past the end of a resource: zeros).
+template <class TokOf>
+__device__ __forceinline__ void load_tile(Packed& p, int tid, const Res& res, TokOf tok) {
 #pragma unroll
-  for (int k = 0; k < 8 / NW; ++k) {
-    const int c = wave + k * NW;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.codes, (lds_ptr_t)(st + kStCodes + c * 1024), 16,
-                                             t0 * 256 + c * 1024 + lane * 16, 0, 0, 0);
+  for (int j = 0; j < 2; ++j) {
+    const int ch = tid + 256 * j;
+    const int t = tok(ch >> 4);
+    const uint32_t oc = t < 0 ? 0xFFFFFFFFu : (uint32_t)t * 256u + (ch & 15) * 16;
+    const uint32_t os = t < 0 ? 0xFFFFFFFFu : (uint32_t)t * 64u + (ch & 15) * 4;
+    p.c[j] = __builtin_amdgcn_raw_buffer_load_b128(res.codes, oc, 0, 0);
+    p.s[j] = __builtin_amdgcn_raw_buffer_load_b32(res.scale, os, 0, 0);
   }
-#pragma unroll
-  for (int k = 0; k < 8 / NW; ++k) {
-    const int c = wave + k * NW;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.scale, (lds_ptr_t)(st + kStScale + c * 256), 4,
-                                             t0 * 64 + c * 256 + lane * 4, 0, 0, 0);
-  }
-#pragma unroll
-  for (int k = 0; k < 16 / NW; ++k) {
-    const int c = wave + k * NW;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.rope, (lds_ptr_t)(st + kStRope + c * 256), 4,
-                                             t0 * 128 + c * 256 + lane * 4, 0, 0, 0);
-  }
+  const int tr = tok(tid >> 3);
+  const uint32_t orp = tr < 0 ? 0xFFFFFFFFu : (uint32_t)tr * 128u + (tid & 7) * 16;
+  p.r = __builtin_amdgcn_raw_buffer_load_b128(res.rope, orp, 0, 0);
 }
 
-// Sparse decode: the tile's slots read the staged positions pos[rel .. rel + 32)
-// (-1: none; rel < 0: no tile), each lane its own token row of the chunk it
-// loads (as issue_tile: codes and scales 4 c + lane / 16, RoPE 2 c + lane / 32).
-// A missing position reads past the end of the resources: zeros.
-template <int NW>
-__device__ __forceinline__ void issue_tile_sparse(uint8_t* st, int wave, int lane, int rel, const int* pos,
-                                                  const Res& r) {
-  auto tok = [&](int slot) { return rel < 0 ? -1 : pos[rel + slot]; };
+// Dequantise this thread's share of a tile into the token-major fp16 tile kt.
+__device__ __forceinline__ void dequant_tile(const Packed& p, uint16_t* kt, int tid) {
 #pragma unroll
-  for (int k = 0; k < 8 / NW; ++k) {
-    const int c = wave + k * NW;
-    const int p = tok(4 * c + (lane >> 4));
-    const uint32_t oc = p < 0 ? 0xFFFFFFFFu : (uint32_t)p * 256u + (lane & 15) * 16;
-    const uint32_t os = p < 0 ? 0xFFFFFFFFu : (uint32_t)p * 64u + (lane & 15) * 4;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.codes, (lds_ptr_t)(st + kStCodes + c * 1024), 16, oc, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.scale, (lds_ptr_t)(st + kStScale + c * 256), 4, os, 0, 0, 0);
-  }
+  for (int j = 0; j < 2; ++j) {
+    const int ch = tid + 256 * j;
+    const int t = ch >> 4, cc = ch & 15;
+    const uint32_t sw = (uint32_t)p.s[j];
+    const h2_t s0 = splat_bf16(sw & 0xFFFFu), s1 = splat_bf16(sw >> 16);
+    uint16_t* row = kt + kt_phys(t) * kKtStride + 32 * cc;
 #pragma unroll
-  for (int k = 0; k < 16 / NW; ++k) {
-    const int c = wave + k * NW;
-    const int p = tok(2 * c + (lane >> 5));
-    const uint32_t orp = p < 0 ? 0xFFFFFFFFu : (uint32_t)p * 128u + (lane & 31) * 4;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.rope, (lds_ptr_t)(st + kStRope + c * 256), 4, orp, 0, 0, 0);
-  }
-}
-
-// Dequantise one packed stage into a token-major fp16 tile: item (token t,
-// channel octet o) per thread and step, a wave's lanes the 64 octets of one
-// token; RoPE rows copied through (bf16) by the first 256 threads.  The stage is
-// read in one asm block that also waits for the reads (outputs early-clobber, so
-// that no result register doubles as an address still to be read): the compiler would
-// otherwise make every read of a stage wait for all loads into LDS still in
-// flight (it cannot tell the three stages apart), the next tiles' included.
-template <int NW>
-__device__ __forceinline__ void dequant_tile(const uint8_t* st, uint16_t* kt, int tid) {
-  constexpr int NT = 64 * NW;
-  constexpr int NI = 2048 / NT;                   // items per thread: 4, 8 or 16
-  static_assert(NI == 4 || NI == 8 || NI == 16, "items per thread");
-  const int t0 = tid >> 6, o = tid & 63;          // item k: token t0 + (NT / 64) k, octet o
-  // stage byte offsets (LDS addresses) of item 0's code word and scale; item k
-  // adds k * (NT / 64) tokens: 256 and 64 bytes per token
-  const uint32_t ac = (uint32_t)(uintptr_t)(st + kStCodes + t0 * 256 + 4 * o);
-  const uint32_t as = (uint32_t)(uintptr_t)(st + kStScale + t0 * 64 + 2 * (o >> 1));
-  uint32_t cw[NI], sw[NI];
-#pragma unroll
-  for (int k0 = 0; k0 < NI; k0 += 4) {
-    constexpr int dt = NT / 64;
-    asm volatile(
-        "ds_read_b32 %0, %8 offset:%c10\n\t"
-        "ds_read_u16 %4, %9 offset:%c11\n\t"
-        "ds_read_b32 %1, %8 offset:%c12\n\t"
-        "ds_read_u16 %5, %9 offset:%c13\n\t"
-        "ds_read_b32 %2, %8 offset:%c14\n\t"
-        "ds_read_u16 %6, %9 offset:%c15\n\t"
-        "ds_read_b32 %3, %8 offset:%c16\n\t"
-        "ds_read_u16 %7, %9 offset:%c17\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(cw[k0]), "=&v"(cw[k0 + 1]), "=&v"(cw[k0 + 2]), "=&v"(cw[k0 + 3]), "=&v"(sw[k0]),
-          "=&v"(sw[k0 + 1]), "=&v"(sw[k0 + 2]), "=&v"(sw[k0 + 3])
-        : "v"(ac), "v"(as), "i"(256 * dt * k0), "i"(64 * dt * k0), "i"(256 * dt * (k0 + 1)),
-          "i"(64 * dt * (k0 + 1)), "i"(256 * dt * (k0 + 2)), "i"(64 * dt * (k0 + 2)), "i"(256 * dt * (k0 + 3)),
-          "i"(64 * dt * (k0 + 3)));
-  }
-#pragma unroll
-  for (int k = 0; k < NI; ++k) {
-    const int t = t0 + (NT / 64) * k;
-    const h2_t sc = splat_bf16(sw[k]);
-    *reinterpret_cast<uint4*>(kt + kt_phys(t) * kKtStride + 8 * o) =
-        uint4{__builtin_bit_cast(uint32_t, fp4x2<0>(cw[k]) * sc), __builtin_bit_cast(uint32_t, fp4x2<1>(cw[k]) * sc),
-              __builtin_bit_cast(uint32_t, fp4x2<2>(cw[k]) * sc), __builtin_bit_cast(uint32_t, fp4x2<3>(cw[k]) * sc)};
-  }
-  // RoPE: 32 tokens x 8 parts of 16 bytes
-#pragma unroll
-  for (int k = 0; k < (256 + NT - 1) / NT; ++k) {
-    const int it = tid + k * NT;
-    if (it < 256) {
-      const int t = it >> 3, part = it & 7;
-      const uint32_t ar = (uint32_t)(uintptr_t)(st + kStRope + t * 128 + 16 * part);
-      uint4 r;
-      asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r) : "v"(ar));
-      *reinterpret_cast<uint4*>(kt + kt_phys(t) * kKtStride + kLat + 8 * part) = r;
+    for (int q = 0; q < 4; ++q) {  // octet q: channels 32 cc + 8 q + [0, 8), scale group 2 cc + q / 2
+      const uint32_t w = (uint32_t)p.c[j][q];
+      const h2_t sc = q < 2 ? s0 : s1;
+      *reinterpret_cast<uint4*>(row + 8 * q) =
+          uint4{__builtin_bit_cast(uint32_t, fp4x2<0>(w) * sc), __builtin_bit_cast(uint32_t, fp4x2<1>(w) * sc),
+                __builtin_bit_cast(uint32_t, fp4x2<2>(w) * sc), __builtin_bit_cast(uint32_t, fp4x2<3>(w) * sc)};
     }
   }
+  *reinterpret_cast<v4i_t*>(kt + kt_phys(tid >> 3) * kKtStride + kLat + 8 * (tid & 7)) = p.r;
 }
 
 // Per-wave state that lives across tiles.
 struct LatentWave {
-  h8_t ql[16];   // query, latent part (fp16): B operand of 16 k-steps
-  b8_t qr[2];    // query, RoPE part (bf16): 2 k-steps
-  f4_t o[32];    // output accumulators, N block nb = channels 16 nb + [0, 16)
+  h8_t ql[32];   // query, latent part (fp16): B operand of 32 k-steps
+  b8_t qr[4];    // query, RoPE part (bf16): 4 k-steps
+  f16v_t o[16];  // output accumulators, N block n = channels 32 n + [0, 32)
   float m_run;   // running max (log2 units) of this lane's head
-  float l_part;  // this lane's share of the running sum
+  float l_run;   // running sum over this lane's tokens (the lane pair is added at the end)
 };
 
-// QK, softmax and PV of one dequantised tile kt (first token tt, tokens below
-// t_end; SPARSE: slot j valid when bit j of `valid`).  The operand reads run D
-// k-steps (QK) and E products (PV) ahead of the products that use them: as deep
-// as the 256 registers of a wave that shares its SIMD allow without spilling.
-template <bool SPARSE, int D, int E>
-__device__ __forceinline__ void tile_math(LatentWave& w, const uint16_t* kt, int ka, int vb0, int vb1, int grp,
-                                          int tt, int t_end, uint32_t valid, float scale_log2) {
-  constexpr int kHalf = kt_phys(16) * kKtStride;  // token 16 + m: row kt_phys(m) + 16
-  // -------- S^T = K Q^T: tokens col and 16 + col (rows), this wave's heads (columns).
-  h8_t kf[18][2];
-  f4_t s0 = f4_t{}, s1 = f4_t{};
-  auto kread = [&](int k) {
-    kf[k][0] = *reinterpret_cast<const h8_t*>(kt + ka + 32 * k);
-    kf[k][1] = *reinterpret_cast<const h8_t*>(kt + ka + kHalf + 32 * k);
-  };
+// S^T = K Q^T for this wave's 32 heads on tile kt, one accumulation chain; the
+// operand reads run D k-steps ahead of the products.
+template <int D>
+__device__ __forceinline__ f16v_t qk_product(const LatentWave& w, const uint16_t* kt, int ka) {
+  h8_t kf[36];
+  f16v_t s = f16v_t{};
 #pragma unroll
-  for (int k = 0; k < D; ++k) kread(k);
+  for (int k = 0; k < D; ++k) kf[k] = *reinterpret_cast<const h8_t*>(kt + ka + 16 * k);
 #pragma unroll
-  for (int k = 0; k < 18; ++k) {
-    if (k + D < 18) kread(k + D);
-    if (k < 16) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[k][0], w.ql[k], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[k][1], w.ql[k], s1, 0, 0, 0);
-    } else {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8_t, kf[k][0]), w.qr[k - 16], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8_t, kf[k][1]), w.qr[k - 16], s1, 0, 0, 0);
-    }
+  for (int k = 0; k < 36; ++k) {
+    if (k + D < 36) kf[k + D] = *reinterpret_cast<const h8_t*>(kt + ka + 16 * (k + D));
+    if (k < 32) s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[k], w.ql[k], s, 0, 0, 0);
+    else s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(b8_t, kf[k]), w.qr[k - 32], s, 0, 0, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x100, 2 * D, 0);
+  // keep D reads in flight: D reads, then (product, read) pairs, then D products
+  __builtin_amdgcn_sched_group_barrier(0x100, D, 0);
 #pragma unroll
-  for (int k = 0; k < 18 - D; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  for (int k = 0; k < 36 - D; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, 2 * D, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  // -------- online softmax for this lane's head: tokens 4 grp + j (s0) and
-  // 16 + 4 grp + j (s1), j < 4
-  float x[8];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) x[j] = s0[j], x[4 + j] = s1[j];
-  float tmax = -INFINITY;
-  if (tt + kTile <= t_end && valid == 0xFFFFFFFFu) {  // a whole tile: nothing to mask
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      x[j] *= scale_log2;
-      tmax = fmaxf(tmax, x[j]);
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int tok = 16 * (j >> 2) + 4 * grp + (j & 3);
-      x[j] = tt + tok < t_end && ((valid >> tok) & 1u) ? x[j] * scale_log2 : -INFINITY;
-      tmax = fmaxf(tmax, x[j]);
-    }
-  }
-  tmax = max_xor32(max_xor16(tmax));
-  // the reference max moves only when the tile max passes it by more than 2^8
-  const bool bump = tmax > w.m_run + 8.f;
-  const float m_new = bump ? tmax : w.m_run;
-  const float alpha = bump ? __builtin_amdgcn_exp2f(w.m_run - m_new) : 1.f;
-  h8_t pf;
-  float psum = 0.f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float p = __builtin_amdgcn_exp2f(x[j] - m_new);
-    psum += p;
-    pf[j] = (_Float16)p;
-  }
-  w.l_part = w.l_part * alpha + psum;
-  w.m_run = m_new;
-  if (__ballot(bump)) {
-    // output rows are heads 4 grp + r; head h's alpha is in lane h
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float ar = __shfl(alpha, 4 * grp + r);
-#pragma unroll
-      for (int n = 0; n < 32; ++n) w.o[n][r] *= ar;
-    }
-  }
-  // -------- O += P V: A = P (head col, k-slots = tokens 4 grp + [0, 4) and
-  // 16 + 4 grp + [0, 4)), B = V (same k-slots, channel 16 nb + col).
+  __builtin_amdgcn_sched_group_barrier(0x008, D, 0);
+  return s;
+}
+
+// O += P V for tile kt: product (n, c) takes channels 32 n + [0, 32) over tokens
+// 16 c + [0, 16); its B operand is two transposing reads of four tokens each,
+// issued E products ahead.
+template <int E>
+__device__ __forceinline__ void pv_product(LatentWave& w, const h8_t (&pf)[2], const uint16_t* kt, int vb) {
+  constexpr int kH2 = 8 * kKtStride;  // h2 = 1: token + 4 -> row + 8
+  constexpr int kC = 16 * kKtStride;  // c = 1: token + 16 -> row + 16
   s4_t vf[32][2];
-  auto vread = [&](int nb) {
-    vf[nb][0] = read_tr16(kt + vb0 + 16 * nb);
-    vf[nb][1] = read_tr16(kt + vb1 + 16 * nb);
+  auto vread = [&](int j) {
+    const int n = j >> 1, c = j & 1;
+    vf[j][0] = read_tr16(kt + vb + c * kC + 32 * n);
+    vf[j][1] = read_tr16(kt + vb + c * kC + kH2 + 32 * n);
   };
 #pragma unroll
-  for (int nb = 0; nb < E; ++nb) vread(nb);
+  for (int j = 0; j < E; ++j) vread(j);
 #pragma unroll
-  for (int nb = 0; nb < 32; ++nb) {
-    if (nb + E < 32) vread(nb + E);
-    const h8_t v = __builtin_bit_cast(h8_t, __builtin_shufflevector(vf[nb][0], vf[nb][1], 0, 1, 2, 3, 4, 5, 6, 7));
-    w.o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, v, w.o[nb], 0, 0, 0);
+  for (int j = 0; j < 32; ++j) {
+    if (j + E < 32) vread(j + E);
+    const h8_t v = __builtin_bit_cast(h8_t, __builtin_shufflevector(vf[j][0], vf[j][1], 0, 1, 2, 3, 4, 5, 6, 7));
+    w.o[j >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pf[j & 1], v, w.o[j >> 1], 0, 0, 0);
   }
+  // keep 2 E reads in flight: 2 E reads, then (product, 2 reads), then E products
   __builtin_amdgcn_sched_group_barrier(0x100, 2 * E, 1);
 #pragma unroll
-  for (int nb = 0; nb < 32 - E; ++nb) {
+  for (int j = 0; j < 32 - E; ++j) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, E, 1);
-  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Online softmax of one tile's logits s (this lane: head col, tokens
+// 16 (i / 8) + 8 half + i % 8; tile tokens from tt, those below t_end and, when
+// sparse, with their bit set in `valid`): the tile's probabilities as the A
+// operand of the two PV products, the running sum updated, and the factor the
+// accumulators must be scaled by before this tile's products (1 unless the
+// reference max moved).  The reference max moves only when the tile max passes
+// it by more than 2^8.
+__device__ __forceinline__ float softmax_tile(LatentWave& w, f16v_t s, int half, int tt, int t_end, uint32_t valid,
+                                              float scale_log2, h8_t (&pf)[2]) {
+  float tmax = -INFINITY;
+  if (tt + kTile <= t_end && valid == 0xFFFFFFFFu) {  // a whole tile: nothing to mask
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s[i] = s[i] * scale_log2;
+      tmax = fmaxf(tmax, s[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int j = 16 * (i >> 3) + 8 * half + (i & 7);
+      s[i] = tt + j < t_end && ((valid >> j) & 1u) ? s[i] * scale_log2 : -INFINITY;
+      tmax = fmaxf(tmax, s[i]);
+    }
+  }
+  tmax = max_xor32(tmax);
+  const bool bump = tmax > w.m_run + 8.f;
+  const float m_new = bump ? tmax : w.m_run;
+  const float alpha = bump ? __builtin_amdgcn_exp2f(w.m_run - m_new) : 1.f;
+  float psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float p = __builtin_amdgcn_exp2f(s[i] - m_new);
+    psum += p;
+    pf[i >> 3][i & 7] = (_Float16)p;
+  }
+  w.l_run = w.l_run * alpha + psum;
+  w.m_run = m_new;
+  return alpha;
+}
+
+// O *= alpha per head (output rows are heads i % 4 + 8 (i / 4) + 4 half; head
+// r's alpha is in lane r), when any head's reference max moved.
+__device__ __forceinline__ void rescale(LatentWave& w, float alpha, int half) {
+  if (__ballot(alpha != 1.f)) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float ar = __shfl(alpha, (i & 3) + 8 * (i >> 2) + 4 * half);
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {
+        float x = w.o[n][i];
+        scale_acc(x, ar);
+        w.o[n][i] = x;
+      }
+    }
+    asm volatile("s_nop 7");  // VALU writes of the accumulators, then MFMA reads of them
+  }
 }
 
 // PAGED: token rows in pool pages named by the block table, resources per tile.
 // SPARSE (contiguous caches): the split's slots read the positions a.sel names,
 // staged in LDS; slots without a valid position are masked.
-template <int NW, bool PAGED, bool SPARSE>
-__global__ void __launch_bounds__(64 * NW)
-__attribute__((amdgpu_waves_per_eu(NW / 4 > 1 ? NW / 4 : 1, NW / 4 > 1 ? NW / 4 : 1))) decode_latent_kernel(
-    MfmaDecodeArgs a) {
-  constexpr int NT = 64 * NW;
-  constexpr int kLoads = 32 / NW;  // direct-to-LDS loads per wave per tile
-  __shared__ __attribute__((aligned(16))) uint8_t stage[kStages][kStBytes];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][kKtHalves];
+template <bool PAGED, bool SPARSE>
+__global__ void __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+decode_latent_kernel(MfmaDecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[kBufs][kKtHalves];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // waves past the heads (Hq = 32 or 64) compute on the last head group's query
+  // (so that every wave runs the same code) and write nothing
+  const bool heads = 32 * wave < a.Hq;
+  const int hgroup = heads ? wave : a.Hq / 32 - 1;
   const int split = blockIdx.x, b = blockIdx.y;
   // several queries per sequence: this launch takes query j = a.c0 of a.nq,
   // which sees the first L - (nq - 1 - j) tokens
@@ -347,19 +303,19 @@ __attribute__((amdgpu_waves_per_eu(NW / 4 > 1 ? NW / 4 : 1, NW / 4 > 1 ? NW / 4 
   const int t_begin = split * a.per_split;
   const int t_end = min(L, t_begin + a.per_split);
   const int ntiles = t_end > t_begin ? (t_end - t_begin + kTile - 1) / kTile : 0;
-  const int col = lane & 15, grp = lane >> 4;  // head of this lane's column, its lane group
+  const int col = lane & 31, half = lane >> 5;  // head of this lane's column, its lane half
   static_assert(!(PAGED && SPARSE), "sparse decode reads contiguous caches");
   __shared__ int spos[SPARSE ? kLatentSparseSlots : 1];
   __shared__ uint32_t svalid[SPARSE ? kLatentSparseSlots / kTile : 1];  // bit j: slot j of the tile is valid
   if constexpr (SPARSE) {
     const int32_t* sb = a.sel + (size_t)b * a.sel_stride;
-    for (int i = tid; i < a.per_split; i += NT) {
+    for (int i = tid; i < a.per_split; i += kNT) {
       const int slot = t_begin + i;
       int p = slot < t_end ? sb[slot] : -1;
       spos[i] = p >= 0 && p < a.cap ? p : -1;
     }
     __syncthreads();
-    for (int ti = tid; ti < a.per_split / kTile; ti += NT) {
+    for (int ti = tid; ti < a.per_split / kTile; ti += kNT) {
       uint32_t m = 0;
       for (int j = 0; j < kTile; ++j) m |= (spos[ti * kTile + j] >= 0 ? 1u : 0u) << j;
       svalid[ti] = m;
@@ -373,106 +329,108 @@ __attribute__((amdgpu_waves_per_eu(NW / 4 > 1 ? NW / 4 : 1, NW / 4 > 1 ? NW / 4 
                rsrc(a.rope + row0 * 64, (size_t)nrows * 128)};
   };
   const Res res = res_at((size_t)b * a.cap, a.cap);
-  // the loads of tile index ti (token t_begin + 32 ti) into stage st; a missing
-  // tile reads past the end of its resources
-  auto issue_at = [&](uint8_t* st, int ti) {
+  // the loads of tile index ti (tokens t_begin + 32 ti + [0, 32)); a missing
+  // tile or token reads past the end of its resources: zeros
+  auto load_at = [&](Packed& p, int ti) {
     const int t = t_begin + ti * kTile;
     if constexpr (SPARSE) {
-      issue_tile_sparse<NW>(st, wave, lane, t < t_end ? t - t_begin : -1, spos, res);
+      const int rel = t < t_end ? t - t_begin : -1;
+      load_tile(p, tid, res, [&](int k) { return rel < 0 ? -1 : spos[rel + k]; });
     } else if constexpr (!PAGED) {
-      issue_tile<NW>(st, wave, lane, t < t_end ? t : a.cap, res);
+      const int t0 = t < t_end ? t : a.cap;
+      load_tile(p, tid, res, [&](int k) { return t0 + k; });
     } else {
       const int pg = t < t_end ? page_of_uniform(a.pm, b, t) : -1;
-      issue_tile<NW>(st, wave, lane, pg < 0 ? 0 : t & (a.pm.tokens - 1),
-                     res_at((size_t)(pg < 0 ? 0 : pg) * a.pm.tokens, pg < 0 ? 0 : a.pm.tokens));
+      const int t0 = pg < 0 ? 0 : t & (a.pm.tokens - 1);
+      load_tile(p, tid, res_at((size_t)(pg < 0 ? 0 : pg) * a.pm.tokens, pg < 0 ? 0 : a.pm.tokens),
+                [&](int k) { return t0 + k; });
     }
   };
-#pragma unroll
-  for (int s = 0; s < kStages; ++s) issue_at(stage[s], s);
+  Packed pk;  // this thread's share of the next tile to dequantise
+  load_at(pk, 0);
 
   LatentWave w;
-  // ---------------- the query operand: 16 fp16 latent steps, 2 bf16 RoPE steps
-  // (B operand of the 16x16x32 products: head col, channels 32 k + 8 grp + [0, 8))
+  // ---------------- the query operand: 32 fp16 latent steps, 4 bf16 RoPE steps
+  // (B operand of the 32x32x16 products: head col, channels 16 k + 8 half + [0, 8))
   {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (qrow0 + 16 * wave + col) * (kLat + kRope);
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (qrow0 + 32 * hgroup + col) * (kLat + kRope);
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(qp + 32 * s + 8 * grp);
+    for (int s = 0; s < 32; ++s) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(qp + 16 * s + 8 * half);
       w.ql[s] = __builtin_bit_cast(h8_t, uint4{bf16x2_to_h2(raw.x), bf16x2_to_h2(raw.y), bf16x2_to_h2(raw.z),
                                                bf16x2_to_h2(raw.w)});
     }
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
-      w.qr[s] = __builtin_bit_cast(b8_t, *reinterpret_cast<const uint4*>(qp + kLat + 32 * s + 8 * grp));
+    for (int s = 0; s < 4; ++s)
+      w.qr[s] = __builtin_bit_cast(b8_t, *reinterpret_cast<const uint4*>(qp + kLat + 16 * s + 8 * half));
   }
 #pragma unroll
-  for (int n = 0; n < 32; ++n) w.o[n] = f4_t{};
+  for (int n = 0; n < 16; ++n) w.o[n] = f16v_t{};
   w.m_run = -INFINITY;
-  w.l_part = 0.f;
+  w.l_run = 0.f;
 
   // lane constants of the fragment reads (kept opaque so that the compiler does
   // not hoist one address register per read out of the loop)
-  // QK A operand: token col (+16), channels 32 k + 8 grp + [0, 8)
-  int ka = kt_phys(col) * kKtStride + 8 * grp;
-  // transposing PV reads: lane (e = (lane % 16) / 4, q = lane % 4) addresses
-  // channels 16 nb + 4 q + [0, 4) of token 4 grp + e (and 16 + 4 grp + e), so
-  // that it receives channel 16 nb + col of those four tokens: its PV B operand
-  const int e4 = (lane & 15) >> 2, q4 = lane & 3;
-  int vb0 = kt_phys(4 * grp + e4) * kKtStride + 4 * q4;
-  int vb1 = kt_phys(16 + 4 * grp + e4) * kKtStride + 4 * q4;
-  asm volatile("" : "+v"(ka), "+v"(vb0), "+v"(vb1));
+  // this lane's QK A operand: token qk_token(col), channels 16 k + 8 half + [0, 8)
+  int ka = kt_phys(qk_token(col)) * kKtStride + 8 * half;
+  // this lane's transposing PV reads: lane (group G = lane / 16, j = lane % 16)
+  // addresses channels 32 n + 16 (G % 2) + 4 (j % 4) + [0, 4) of token
+  // 16 c + 8 half + 4 h2 + j / 4, so that it receives channel 32 n + col of
+  // tokens 16 c + 8 half + 4 h2 + [0, 4): its PV B operand k-slots
+  const int jj = lane & 15, gg = lane >> 4;
+  int vb = kt_phys(8 * half + (jj >> 2)) * kKtStride + 16 * (gg & 1) + 4 * (jj & 3);
+  asm volatile("" : "+v"(ka), "+v"(vb));
 
-  // prologue: tile 0's loads have landed (tiles 1 and 2 may still be in flight)
+  // prologue: tile 0 into Kt[0], the registers refilled with tile 1
   if (ntiles > 0) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * kLoads));
-    __syncthreads();
-    dequant_tile<NW>(stage[0], Kt[0], tid);
+    dequant_tile(pk, Kt[0], tid);
+    load_at(pk, 1);
   }
-
+  // Tile i: its dequantised copy Kt[i % 3].  After the products of tile i the
+  // wave dequantises tile i + 1 from the registers and refills them with tile
+  // i + 2; three buffers let a wave dequantise tile i + 1 while slower waves
+  // still read tile i.
   for (int i = 0; i < ntiles; ++i) {
-    // this wave's loads of tile i + 1 have landed (tile i + 2's may still be in
-    // flight); the barrier then covers every wave's, the whole of tile i's
-    // dequantised copy, and every wave being done with tile i - 1
-    __builtin_amdgcn_s_waitcnt(vmcnt_wait(kLoads));
+    // every wave's share of tile i is in Kt[i % 3], and every wave is done with
+    // tile i - 2 (whose buffer tile i + 1 takes)
     __syncthreads();
-    issue_at(stage[i % kStages], i + kStages);  // the stage of tile i is free: tile i + 3
-    if (i + 1 < ntiles) dequant_tile<NW>(stage[(i + 1) % kStages], Kt[(i + 1) & 1], tid);
-    tile_math<SPARSE, SPARSE ? 1 : 2, SPARSE ? 2 : 4>(w, Kt[i & 1], ka, vb0, vb1, grp, t_begin + i * kTile, t_end, SPARSE ? svalid[i] : 0xFFFFFFFFu,
-                      a.scale_log2);
+    const uint16_t* kt = Kt[i % kBufs];
+    const f16v_t s = qk_product<4>(w, kt, ka);
+    dequant_tile(pk, Kt[(i + 1) % kBufs], tid);
+    load_at(pk, i + 2);
+    h8_t pf[2];
+    const float alpha = softmax_tile(w, s, half, t_begin + i * kTile, t_end, SPARSE ? svalid[i] : 0xFFFFFFFFu,
+                                     a.scale_log2, pf);
+    rescale(w, alpha, half);
+    pv_product<6>(w, pf, kt, vb);
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load into LDS outlives the workgroup
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the refills past the last tile have returned
 
   // ---------------- partial result of this split
-  float l_run = w.l_part + __shfl_xor(w.l_part, 16);
-  l_run += __shfl_xor(l_run, 32);
-  const size_t row0 = qrow0 + 16 * wave;
-  if (grp == 0) {
+  if (!heads) return;
+  const float l_run = w.l_run + __shfl_xor(w.l_run, 32);
+  const size_t row0 = qrow0 + 32 * wave;
+  if (half == 0) {
     float* p = a.part + ((row0 + col) * a.splits + split) * (kLat + 2);
     p[0] = w.m_run;
     p[1] = l_run;
   }
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float* p = a.part + ((row0 + 4 * grp + r) * a.splits + split) * (kLat + 2) + 2 + col;
+  for (int r = 0; r < 16; ++r) {
+    const int head = (r & 3) + 8 * (r >> 2) + 4 * half;
+    float* p = a.part + ((row0 + head) * a.splits + split) * (kLat + 2) + 2 + col;
 #pragma unroll
-    for (int nb = 0; nb < 32; ++nb) p[16 * nb] = w.o[nb][r];
+    for (int n = 0; n < 16; ++n) p[32 * n] = w.o[n][r];
   }
 }
 
-}  // namespace
-
-namespace {
 template <bool PAGED, bool SPARSE>
 int launch_latent(const MfmaDecodeArgs& a, int B, hipStream_t st) {
-  dim3 grid(a.splits, B);
-  switch (a.Hq) {
-    case 32: decode_latent_kernel<2, PAGED, SPARSE><<<grid, 128, 0, st>>>(a); break;
-    case 64: decode_latent_kernel<4, PAGED, SPARSE><<<grid, 256, 0, st>>>(a); break;
-    case 128: decode_latent_kernel<8, PAGED, SPARSE><<<grid, 512, 0, st>>>(a); break;
-    default: return KV_EUNSUPPORTED;
-  }
+  if (a.Hq != 32 && a.Hq != 64 && a.Hq != 128) return KV_EUNSUPPORTED;
+  decode_latent_kernel<PAGED, SPARSE><<<dim3(a.splits, B), kNT, 0, st>>>(a);
   return KV_OK;
 }
+
 }  // namespace
 
 int launch_decode_latent(const MfmaDecodeArgs& a, int B, hipStream_t st) {
