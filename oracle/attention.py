@@ -206,16 +206,28 @@ def decode_attention_multi(fmt, cache, q, seq_lens, scale, hkv, consts=None, lat
     return out
 
 
-def decode_attention_mixed(fmt, cache, q, seq_lens, scale, hkv, K_in, V_in, sink, recent, consts=None):
+def decode_attention_mixed(fmt, cache, q, seq_lens, scale, hkv, K_in, V_in, sink, recent, consts=None,
+                           appended=None):
     """fp64 outputs [B, nq, Hq, d] for q [B, nq, Hq, d] over a cache whose tokens
     t < sink and t >= L - recent are read as bf16 of the inputs K_in, V_in
     ([B, H, T, d]) and the others through their packed codes; query j sees the
-    first L - (nq - 1 - j) tokens."""
-    if fmt not in ("fp4", "qjl1"):
-        raise ValueError("mixed precision is defined here for caches with FP4 values")
+    first L - (nq - 1 - j) tokens.
+
+    Reading for the 2-bit histories (page "TurboQuant vs OSCAR vs EpiCache",
+    OSCAR deployment list: sink and recent tokens BF16, the history INT2):
+      * TURBO: a packed token's value is n_v R^T u~ (in the original basis, as in
+        decode_attention), a window token's the bf16 input; the logit of a
+        window token is <q, bf16 k> with the caller's query;
+      * KIVI2: keys of a sequence's last incomplete group (from
+        32 * floor(appended[b] / 32) on, appended defaulting to the length) have
+        no code yet and are read from the inputs unrounded, unless the token is
+        in a window (bf16 there too)."""
+    if fmt not in ("fp4", "qjl1", "kivi2", "turbo"):
+        raise ValueError("mixed precision is defined here for the fp4, qjl1, kivi2 and turbo caches")
     q = np.asarray(q, dtype=np.float64)
     B, nq, Hq = q.shape[:3]
     G = Hq // hkv
+    appended = seq_lens if appended is None else appended
     out = np.zeros((B, nq, Hq, K_in.shape[-1]))
     for b in range(B):
         L = int(seq_lens[b])
@@ -223,19 +235,26 @@ def decode_attention_mixed(fmt, cache, q, seq_lens, scale, hkv, K_in, V_in, sink
             raise ValueError("every query must see at least its own token")
         t = np.arange(L)
         window = (t < sink) | (t >= L - recent)
+        staged = (t >= F.KIVI_GROUP * (int(appended[b]) // F.KIVI_GROUP)) if fmt == "kivi2" else np.zeros(L, bool)
         limit = L - (nq - 1 - np.repeat(np.arange(nq), G))
         visible = t[None, :] < limit[:, None]
         for h in range(hkv):
             qg = q[b, :, h * G:(h + 1) * G].reshape(nq * G, -1)
-            kb = round_bf16(np.asarray(K_in[b, h, :L], np.float64))
+            kin = np.asarray(K_in[b, h, :L], np.float64)
+            kb = round_bf16(kin)
             vb = round_bf16(np.asarray(V_in[b, h, :L], np.float64))
-            logits = np.where(window[None, :], qg @ kb.T,
-                              _key_logits(fmt, cache, b, h, 0, L, qg, consts, 0)) * scale
+            packed = _key_logits(fmt, cache, b, h, 0, L, qg, consts, 0)
+            if fmt == "kivi2":
+                packed = np.where(staged[None, :], qg @ kin.T, packed)
+            logits = np.where(window[None, :], qg @ kb.T, packed) * scale
             logits = np.where(visible, logits, -np.inf)
             m = logits.max(axis=1, keepdims=True)
             p = np.exp(logits - m)
             p /= p.sum(axis=1, keepdims=True)
-            vals = np.where(window[:, None], vb, _values(fmt, cache, b, h, 0, L, consts, 0))
+            hist = _values(fmt, cache, b, h, 0, L, consts, 0)
+            if fmt == "turbo":
+                hist = hist @ np.asarray(consts["rot"], np.float64)   # R^T applied to each value
+            vals = np.where(window[:, None], vb, hist)
             out[b, :, h * G:(h + 1) * G] = (p @ vals).reshape(nq, G, -1)
     return out
 
