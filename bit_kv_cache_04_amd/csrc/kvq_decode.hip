@@ -530,8 +530,9 @@ __global__ void __launch_bounds__(384) prep_query_kernel(const QT* __restrict__ 
 // columns NJ * l .. NJ * l + NJ - 1, so that the loads of different splits are
 // independent and spread over the block; the W wave sums are added in wave
 // order.  TURBO (the whole row in one block) maps the rotated output back with
-// R^T, every thread taking a slice of the rows of R.  A row with no tokens at
-// all writes zeros.
+// R^T, every thread taking a slice of the rows of R; its splits from rot_splits
+// on (the bf16 window's) are already in the original basis and are added after
+// that product.  A row with no tokens at all writes zeros.
 constexpr int kMaxSplits = kMaxPartSplits;
 
 template <int NJ>
@@ -541,15 +542,17 @@ constexpr int merge_max_waves() {
 
 template <int NJ>
 __global__ void __launch_bounds__(64 * merge_max_waves<NJ>()) merge_kernel(const float* __restrict__ part,
-                                                                           int splits, int dv, int fmt,
-                                                                           const float* __restrict__ rot,
+                                                                           int splits, int rot_splits, int dv,
+                                                                           int fmt, const float* __restrict__ rot,
                                                                            float* __restrict__ out) {
   constexpr int CW = 64 * NJ, MW = merge_max_waves<NJ>();
+  constexpr bool kTurboCols = NJ == 2;  // TURBO rows (dv = 128) take this column blocking
   __shared__ float sm_w[kMaxSplits];  // m_s, then the weights
   __shared__ float sm_l[kMaxSplits];
   __shared__ float red_m[MW], red_l[MW];
   __shared__ float sums[MW][CW];
-  __shared__ float ov[CW];
+  __shared__ float sums_o[kTurboCols ? MW : 1][kTurboCols ? CW : 1];  // TURBO: splits past rot_splits
+  __shared__ float ov[CW], ovo[kTurboCols ? CW : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nthr = blockDim.x, W = nthr >> 6;
   const size_t row = blockIdx.x;
@@ -583,35 +586,58 @@ __global__ void __launch_bounds__(64 * merge_max_waves<NJ>()) merge_kernel(const
   for (int i = 1; i < W; ++i) l += red_l[i];
   const float inv_l = l > 0.f ? 1.f / l : 0.f;
   const int c0 = CW * blockIdx.y;
-  float acc[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) acc[j] = 0.f;
   const float* pc = p + 2 + c0 + NJ * lane;  // 8-byte aligned: rows and the header are even
-#pragma unroll(16 / NJ)
-  for (int s = wave; s < splits; s += W) {
-    const float ws = sm_w[s];
-    if constexpr (NJ == 1) {
-      acc[0] = fmaf(ws, pc[s * stride], acc[0]);
-    } else {
+  constexpr int kMergeUnroll = 16 / NJ;
+  // weighted sum of the splits s0, s0 + W, ... below s1 for this lane's columns
+  auto weighted = [&](int s0, int s1, float (&acc)[NJ]) {
 #pragma unroll
-      for (int j = 0; j < NJ; j += 2) {
-        const float2 v = *reinterpret_cast<const float2*>(pc + s * stride + j);
-        acc[j] = fmaf(ws, v.x, acc[j]);
-        acc[j + 1] = fmaf(ws, v.y, acc[j + 1]);
+    for (int j = 0; j < NJ; ++j) acc[j] = 0.f;
+#pragma unroll kMergeUnroll
+    for (int s = s0; s < s1; s += W) {
+      const float ws = sm_w[s];
+      if constexpr (NJ == 1) {
+        acc[0] = fmaf(ws, pc[s * stride], acc[0]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < NJ; j += 2) {
+          const float2 v = *reinterpret_cast<const float2*>(pc + s * stride + j);
+          acc[j] = fmaf(ws, v.x, acc[j]);
+          acc[j + 1] = fmaf(ws, v.y, acc[j + 1]);
+        }
+      }
+    }
+  };
+  const bool turbo = fmt == KV_FMT_TURBO;
+  const int s_rot = turbo ? rot_splits : splits;
+  {
+    float acc[NJ];
+    weighted(wave, s_rot, acc);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) sums[wave][NJ * lane + j] = acc[j];
+    if constexpr (kTurboCols) {
+      if (turbo) {
+        weighted(s_rot + wave, splits, acc);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) sums_o[wave][NJ * lane + j] = acc[j];
       }
     }
   }
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) sums[wave][NJ * lane + j] = acc[j];
   __syncthreads();
   float* dst = out + row * dv;
   for (int c = tid; c < CW; c += nthr) {
     float t = sums[0][c];
     for (int i = 1; i < W; ++i) t += sums[i][c];
-    if (fmt == KV_FMT_TURBO) ov[c] = t * inv_l;
-    else dst[c0 + c] = t * inv_l;
+    if (!turbo) {
+      dst[c0 + c] = t * inv_l;
+    } else if constexpr (kTurboCols) {
+      ov[c] = t * inv_l;
+      float t2 = sums_o[0][c];
+      for (int i = 1; i < W; ++i) t2 += sums_o[i][c];
+      ovo[c] = t2 * inv_l;
+    }
   }
-  if (fmt == KV_FMT_TURBO) {  // CW == dv here
+  if constexpr (kTurboCols) {
+    if (!turbo) return;  // CW == dv below
     __syncthreads();
     // P slices of the rows of R: thread (q, c) sums j in [q * CW / P, (q + 1) * CW / P)
     const int P = nthr >= CW ? min(nthr / CW, MW) : 1;
@@ -627,7 +653,7 @@ __global__ void __launch_bounds__(64 * merge_max_waves<NJ>()) merge_kernel(const
     for (int c = tid; c < CW; c += nthr) {
       float a = sums[0][c];
       for (int q = 1; q < P; ++q) a += sums[q][c];
-      dst[c] = a;
+      dst[c] = a + ovo[c];
     }
   }
 }
@@ -635,8 +661,8 @@ __global__ void __launch_bounds__(64 * merge_max_waves<NJ>()) merge_kernel(const
 // Column blocks: TURBO and many rows take the whole row per block (up to 8
 // columns per lane); few rows take 64-column blocks so that more workgroups
 // share the loads; otherwise 128 columns.  Waves: about four splits each.
-void launch_merge(const float* part, int rows, int splits, int dv, int fmt, const float* rot, float* out,
-                  hipStream_t st) {
+void launch_merge(const float* part, int rows, int splits, int rot_splits, int dv, int fmt, const float* rot,
+                  float* out, hipStream_t st) {
   int nj;
   if (fmt == KV_FMT_TURBO || rows >= 2048) nj = dv / 64;
   else if (rows < 256 || dv % 128 != 0) nj = 1;
@@ -645,9 +671,9 @@ void launch_merge(const float* part, int rows, int splits, int dv, int fmt, cons
   const dim3 grid(rows, col_blocks);
   auto waves = [&](int max_w) { return std::min(max_w, std::max(1, (splits + 3) / 4)); };
   switch (nj) {
-    case 1: merge_kernel<1><<<grid, 64 * waves(merge_max_waves<1>()), 0, st>>>(part, splits, dv, fmt, rot, out); break;
-    case 2: merge_kernel<2><<<grid, 64 * waves(merge_max_waves<2>()), 0, st>>>(part, splits, dv, fmt, rot, out); break;
-    default: merge_kernel<8><<<grid, 64 * waves(merge_max_waves<8>()), 0, st>>>(part, splits, dv, fmt, rot, out); break;
+    case 1: merge_kernel<1><<<grid, 64 * waves(merge_max_waves<1>()), 0, st>>>(part, splits, rot_splits, dv, fmt, rot, out); break;
+    case 2: merge_kernel<2><<<grid, 64 * waves(merge_max_waves<2>()), 0, st>>>(part, splits, rot_splits, dv, fmt, rot, out); break;
+    default: merge_kernel<8><<<grid, 64 * waves(merge_max_waves<8>()), 0, st>>>(part, splits, rot_splits, dv, fmt, rot, out); break;
   }
 }
 
@@ -736,7 +762,7 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
       if (rc != KV_OK) return rc;
     }
     if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess) return KV_EDEVICE;
-    launch_merge(part, rows, part_splits, L.head_dim, L.format, c->rot, out, st);
+    launch_merge(part, rows, part_splits, plan.splits, L.head_dim, L.format, c->rot, out, st);
     return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
   }
   const bool mfma =
@@ -781,13 +807,18 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     f.splits = plan.splits;
     f.per_split = plan.tokens_per_split;
     f.nq = nq;
+    f.t_lo = L.sink_tokens;
+    f.recent = L.recent_tokens;
+    f.part_splits = part_splits;
     if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), st) != hipSuccess) return KV_EDEVICE;
     for (f.qj = 0; f.qj < nq; ++f.qj) {  // one pass over the cache per query token
       int rc = launch_decode_turbo(f, B, num_q_heads / L.num_kv_heads, st);
       if (rc != KV_OK) return rc;
     }
+    if (windowed) launch_window(c, q, q_dtype, num_q_heads, nq, seq_lens, max_seq_len, scale, part, part_splits,
+                                plan.splits, st);
     if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess) return KV_EDEVICE;
-    launch_merge(part, rows, part_splits, L.head_dim, L.format, c->rot, out, st);
+    launch_merge(part, rows, part_splits, plan.splits, L.head_dim, L.format, c->rot, out, st);
     return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
   }
   if (mfma) {
@@ -830,7 +861,7 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     if (windowed) launch_window(c, q, q_dtype, num_q_heads, nq, seq_lens, max_seq_len, scale, part, part_splits,
                                 plan.splits, st);
     if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess) return KV_EDEVICE;
-    launch_merge(part, rows, part_splits, L.head_dim, L.format, c->rot, out, st);
+    launch_merge(part, rows, part_splits, plan.splits, L.head_dim, L.format, c->rot, out, st);
     return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
   }
 
@@ -891,7 +922,7 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
   if (windowed) launch_window(c, q, q_dtype, num_q_heads, nq, seq_lens, max_seq_len, scale, part, part_splits,
                               plan.splits, st);
   if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess) return KV_EDEVICE;
-  launch_merge(part, rows, part_splits, L.head_dim, L.format, c->rot, out, st);
+  launch_merge(part, rows, part_splits, plan.splits, L.head_dim, L.format, c->rot, out, st);
   return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
 }
 

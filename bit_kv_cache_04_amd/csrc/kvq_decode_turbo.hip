@@ -305,10 +305,13 @@ __attribute__((amdgpu_waves_per_eu(KVQ_TURBO_WAVES_PER_EU, KVQ_TURBO_WAVES_PER_E
   const size_t bh = (size_t)b * a.H + h;
   // several queries per sequence: this launch takes query j = a.qj of a.nq,
   // which sees the first L - (nq - 1 - j) tokens
-  const int L = min(min(a.seq_lens[b], a.max_len), a.cap) - (a.nq - 1 - a.qj);
+  const int L = min(min(a.seq_lens[b], a.max_len), a.cap);
   const size_t qrow0 = ((size_t)b * a.nq + a.qj) * a.Hq;  // its first query / output row
-  const int t_begin = split * a.per_split;
-  const int t_end = min(L, t_begin + a.per_split);
+  // packed tokens [t_lo, L - recent) this query sees; a split none of whose
+  // tokens reach t_lo has no work (its tiles would be masked whole)
+  const int t_begin = (a.t_lo & ~31) + split * a.per_split;
+  const int t_stop = min(L - (a.nq - 1 - a.qj), max(a.t_lo, L - a.recent));
+  const int t_end = t_stop <= a.t_lo ? t_begin : min(t_stop, t_begin + a.per_split);
   const int q4 = lane >> 4, c = lane & 15;
 
   Consts k;
@@ -390,7 +393,7 @@ __attribute__((amdgpu_waves_per_eu(KVQ_TURBO_WAVES_PER_EU, KVQ_TURBO_WAVES_PER_E
   }
   auto valid_of = [&](int t) -> uint32_t {
     if constexpr (SPARSE) return t < t_end ? svalid[(t - t_begin) >> 5] : 0u;
-    return ~0u;
+    return t >= a.t_lo ? ~0u : a.t_lo - t >= 32 ? 0u : ~0u << (a.t_lo - t);  // below t_lo: the bf16 sink's
   };
   uint8_t* sa = stA[wave];
   uint8_t* sb = stB[wave];
@@ -466,7 +469,7 @@ __attribute__((amdgpu_waves_per_eu(KVQ_TURBO_WAVES_PER_EU, KVQ_TURBO_WAVES_PER_E
       Ls += f * sm_l[ww][hh];
       O += f * sm_o[ww][hh][ch];
     }
-    float* p = a.part + ((row0 + hh) * a.splits + split) * 130;
+    float* p = a.part + ((row0 + hh) * a.part_splits + split) * 130;
     p[2 + ch] = O;
     if (ch == 0) {
       p[0] = M;

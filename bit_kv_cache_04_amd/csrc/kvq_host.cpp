@@ -23,8 +23,8 @@ int check_layout(const kv_layout* L) {
   if (L->page_tokens > 0 && (L->page_tokens < 32 || (L->page_tokens & (L->page_tokens - 1)) ||
                              L->capacity % L->page_tokens || L->num_pages < 1))
     return KV_EINVAL;
-  // bf16 sink / recent windows: caches whose values are FP4 (outputs in the original basis)
-  if ((L->sink_tokens || L->recent_tokens) && L->format != KV_FMT_FP4 && L->format != KV_FMT_QJL1_FP4V)
+  // bf16 sink / recent windows: every per-head format (the latent cache has none)
+  if ((L->sink_tokens || L->recent_tokens) && (L->format == KV_FMT_LATENT_FP4 || L->format == KV_FMT_BF16))
     return KV_EUNSUPPORTED;
   switch (L->format) {
     case KV_FMT_KIVI2:

@@ -60,9 +60,12 @@ struct TurboDecodeArgs {
   const int32_t* seq_lens;
   int max_len, H, cap, Hq;
   float scale_log2, kappa;
-  float* part;  // [B][nq][Hq][splits][130]
+  float* part;  // [B][nq][Hq][part_splits][130]
   int splits, per_split;
   int nq, qj;  // query tokens per sequence; the one this launch takes
+  // mixed precision: packed tokens [t_lo, L - recent); split s from
+  // (t_lo & ~31) + s * per_split (tiles start 32-aligned, tokens below t_lo masked)
+  int t_lo, recent, part_splits;
   // sparse decode: slot i of sequence b reads position sel[b * sel_stride + i]
   // (seq_lens counts slots, at most kMfmaSparseSlots per split); nullptr: dense
   const int32_t* sel;

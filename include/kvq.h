@@ -94,15 +94,18 @@ enum kv_status {
  * format does not use must be 0, except `group`, which is always the format's
  * quantisation group (0 for TURBO).
  *
- * Mixed precision (FP4 and QJL1_FP4V only, both <= capacity): the first
+ * Mixed precision (every format but LATENT_FP4, both <= capacity): the first
  * sink_tokens tokens of every sequence and its last recent_tokens tokens are
  * also kept in bf16 and decode reads them from there, the rest through the
  * packed codes (page "TurboQuant vs OSCAR vs EpiCache", section "quantization
  * frontiers: TurboQuant and OSCAR": sink and recent tokens stay BF16 while the
- * history is compressed).  A window token's logit is <q, bf16 key>.  The recent
- * window is a ring of the last recent_tokens tokens appended to a sequence
- * (slot t mod recent_tokens), so decode must see each sequence at the length
- * it was appended to.  0 and 0 turn it off.
+ * history is compressed).  A window token's logit is <q, bf16 key> and its
+ * value the bf16 value, in the original basis (TURBO: the history's output is
+ * mapped back through R^T, the window's is not).  KIVI2 keys of a sequence's
+ * incomplete group that fall outside the window keep their exact staged fp32
+ * values.  The recent window is a ring of the last recent_tokens tokens
+ * appended to a sequence (slot t mod recent_tokens), so decode must see each
+ * sequence at the length it was appended to.  0 and 0 turn it off.
  *
  * Paged storage (page_tokens > 0, any format): the per-token buffers hold a
  * pool of num_pages pages instead of B x capacity slots; page p holds

@@ -193,13 +193,21 @@ def test_mixed_precision_layout_validation_and_sizes():
     # the windows are a fixed cost per sequence, not counted per token
     assert kvq.kv_bytes_per_token(lay, 1) == kvq.kv_bytes_per_token(kvq.make_layout("fp4", 2, 4, 128, 256), 1)
     assert kvq.kv_buffer_bytes(kvq.make_layout("fp4", 2, 4, 128, 256), kvq.BUFFERS.index("sink_k")) == 0
-    # only caches with FP4 values take windows; sizes within the capacity
-    assert kvq.kv_buffer_bytes(kvq.make_layout("turbo", 1, 1, 128, 64, sink=4), 0) == 0
+    # every per-head format takes windows, the shared latent cache none; sizes within the capacity
+    for fmt in ("kivi2", "turbo", "qjl1"):
+        lay = kvq.make_layout(fmt, 1, 1, 128, 64, sink=4, recent=8)
+        assert kvq.kv_buffer_bytes(lay, kvq.BUFFERS.index("recent_k")) == 8 * 128 * 2
+    assert kvq.kv_buffer_bytes(kvq.make_layout("latent", 1, 1, 512, 64, rope_dim=64, sink=4), 0) == 0
     assert kvq.kv_buffer_bytes(kvq.make_layout("fp4", 1, 1, 128, 64, recent=65), 0) == 0
     assert kvq.kv_buffer_bytes(kvq.make_layout("fp4", 1, 1, 128, 64, sink=-1), 0) == 0
-    c = _cache("turbo")
+    c = _cache("latent", d=512, rope=64)
     c.layout.sink_tokens = 4
     assert _append(c) == EUNSUP
+    for fmt in ("kivi2", "turbo"):
+        c = _cache(fmt, recent=16)
+        c.layout.sink_tokens = 0
+        st, nb_win = _decode(c, ws=None, splits=4)
+        assert st == OK and nb_win > _decode(_cache(fmt), ws=None, splits=4)[1]
     c = _cache()
     c.layout.recent_tokens = 16
     assert _append(c) == EINVAL                                        # window buffers missing

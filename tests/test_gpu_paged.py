@@ -106,7 +106,7 @@ def test_paged_cache_matches_contiguous_and_oracle(fmt):
     assert err.max() <= RTOL
 
 
-@pytest.mark.parametrize("fmt,nq", [("fp4", 3), ("qjl1", 1)])
+@pytest.mark.parametrize("fmt,nq", [("fp4", 3), ("qjl1", 1), ("kivi2", 2), ("turbo", 1), ("turbo", 2)])
 def test_paged_windows_and_queries(fmt, nq):
     """bf16 sink (40 tokens: matrix-core tiles start at 32 and mask 32..39) and
     recent windows over a paged history, sequences appended to ragged lengths

@@ -14,6 +14,7 @@ import torch
 import synth
 from gpu_helpers import (RTOL, assert_bytes_equal, gpu_buffers, host64, inputs, new_cache, oracle_constants,
                          oracle_encode, row_rel_err, softmax_scale)
+from bit_kv_cache_04_amd import kvq
 from oracle import attention as OA
 
 pytestmark = pytest.mark.gpu
@@ -302,23 +303,32 @@ def test_multi_query_decode_matches_oracle(fmt, nq):
     assert err.max() <= RTOL
 
 
-WINDOWS = [("fp4", 16, 64, 1), ("fp4", 0, 100, 3), ("fp4", 40, 0, 1), ("fp4", 300, 700, 2), ("qjl1", 16, 64, 1),
-           ("qjl1", 24, 40, 3)]
+WINDOWS = [("fp4", 16, 64, 1, 0), ("fp4", 0, 100, 3, 0), ("fp4", 40, 0, 1, 0), ("fp4", 300, 700, 2, 0),
+           ("qjl1", 16, 64, 1, 0), ("qjl1", 24, 40, 3, 0),
+           ("kivi2", 16, 64, 1, 0), ("kivi2", 8, 20, 2, 0), ("kivi2", 0, 5, 1, 0),
+           ("turbo", 16, 64, 1, 0), ("turbo", 40, 100, 2, 0), ("turbo", 5, 0, 1, 0), ("turbo", 300, 700, 1, 0),
+           ("turbo", 16, 64, 1, kvq.DECODE_FP32)]
 
 
-@pytest.mark.parametrize("fmt,sink,recent,nq", WINDOWS)
-def test_mixed_precision_decode_matches_oracle(fmt, sink, recent, nq):
+@pytest.mark.parametrize("fmt,sink,recent,nq,flags", WINDOWS)
+def test_mixed_precision_decode_matches_oracle(fmt, sink, recent, nq, flags):
     """bf16 sink and recent windows over a packed history.  Each sequence is
     appended to its own (ragged) length, its last tokens one at a time so that
-    the recent ring wraps; one window covers whole sequences."""
-    cfg = SMALL[fmt]
-    print(f"[mixed] {fmt} sink={sink} recent={recent} nq={nq} {cfg}", flush=True)
+    the recent ring wraps; one window covers whole sequences.  KIVI-2: the
+    sequences end inside a key group, so staged keys outside a short recent
+    window attend exact.  TurboQuant: the history's output goes back through
+    R^T and the window's does not (matrix-core kernel, and the general one
+    under DECODE_FP32)."""
+    cfg = SMALL[fmt] if fmt != "kivi2" else SMALL[fmt].scaled(batch=3)
+    print(f"[mixed] {fmt} sink={sink} recent={recent} nq={nq} flags={flags} {cfg}", flush=True)
     torch.manual_seed(0)
     consts = oracle_constants(cfg)
     cache = new_cache(cfg, sink_tokens=sink, recent_tokens=recent)
     K, V = inputs(cfg)
     lens = synth.seq_lens_for(cfg, ragged=True)
     lens[-1] = max(nq, 3)
+    if fmt == "kivi2":
+        lens[0] -= 7                                    # 25 keys of the last group staged
     for b in range(cfg.batch):
         seq, L = cache.sequence(b), int(lens[b])
         bulk = max(0, L - 5)
@@ -329,7 +339,7 @@ def test_mixed_precision_decode_matches_oracle(fmt, sink, recent, nq):
     torch.cuda.synchronize()
     enc = oracle_encode(cfg, host64(K), host64(V), consts)
     q = synth.make_queries(cfg.scaled(hq=nq * cfg.hq), device="cuda").view(cfg.batch, nq, cfg.hq, -1)
-    out = cache.decode(q, torch.from_numpy(lens).cuda(), softmax_scale(cfg)).cpu().numpy()
+    out = cache.decode(q, torch.from_numpy(lens).cuda(), softmax_scale(cfg), flags=flags).cpu().numpy()
     ref = OA.decode_attention_mixed(fmt, enc, host64(q), lens, softmax_scale(cfg), cfg.hkv, host64(K), host64(V),
                                     sink, recent, consts)
     err = row_rel_err(out.reshape(-1, out.shape[-1]), ref.reshape(-1, ref.shape[-1]))
