@@ -471,8 +471,8 @@ def main():
     ap.add_argument("--config", default=None,
                     help="one workload; default: all five, with latent_b64_t64k as the headline")
     ap.add_argument("--splits", type=int, default=0)
-    ap.add_argument("--sink", type=int, default=0, help="leading tokens kept bf16 (FP4-valued formats)")
-    ap.add_argument("--recent", type=int, default=0, help="trailing tokens kept bf16 (FP4-valued formats)")
+    ap.add_argument("--sink", type=int, default=0, help="leading tokens kept bf16 (per-head formats)")
+    ap.add_argument("--recent", type=int, default=0, help="trailing tokens kept bf16 (per-head formats)")
     ap.add_argument("--queries", type=int, default=1,
                     help="query tokens per sequence (drafted positions checked in one pass); the step "
                          "appends that many tokens")

@@ -410,7 +410,7 @@ __device__ __forceinline__ uint32_t e2m3_code(float y, float& val) {
 //   TURBO product 0 / 1 (code words 4 m + j, m = 0 / 1): the coefficient of
 //     bit d % 2 (a2 for the low bit b0, a1 for the high bit b1) times
 //     (R q)[16 (4 m + j) + 2 n + d / 2];
-//   TURBO product 2, QJL product 0 (sketch dword j): (S R q or S q)[32 j + 4 n + d].
+//   TURBO product 2, QJL product 0 (sketch dword j): ask (S R q or S q)[32 j + 4 n + d].
 // Each block is split into 4 pieces: piece p holds the nearest code of the
 // residual left by pieces < p, at a scale 2^e that puts the residual's largest
 // magnitude in [64, 128) for E4M3 (3 mantissa bits to 448: the pieces' sum is
@@ -421,14 +421,17 @@ __device__ __forceinline__ uint32_t e2m3_code(float y, float& val) {
 // e at bits [6 e, 6 e + 6)), then the 4 blocks' E8M0 scale bytes (e + 127), 144
 // bytes in all.  32 threads per block, as many blocks at a time as the workgroup
 // has threads for.
-__device__ void prepared_query_pieces(int nprod, const float* qrot, const float* qsk, float a1, float a2, bool fp6,
-                                      uint8_t* out) {
+__device__ void prepared_query_pieces(int nprod, const float* qrot, const float* qsk, float a1, float a2, float ask,
+                                      bool fp6, uint8_t* out) {
   const int tid = threadIdx.x, e = tid & 31, d = e >> 3, n = e & 7;
+  // TURBO (FP6): the key operand's element 8 d + n is its bit times 1, 2, 4, 4
+  // for d = 0, 1, 2, 3, so this side carries 1, 1/2, 1/4, 1/4
+  const float dfac = fp6 ? (d == 0 ? 1.f : d == 1 ? 0.5f : 0.25f) : 1.f;
   for (int blk = tid >> 5; blk < 4 * nprod; blk += (int)(blockDim.x >> 5)) {
     const int prod = blk >> 2, j = blk & 3;
     const bool code = prod < nprod - 1;
-    float r = code ? ((d & 1) ? a1 : a2) * qrot[16 * (4 * prod + j) + 2 * n + (d >> 1)]
-                   : qsk[32 * j + 4 * n + d];
+    float r = dfac * (code ? ((d & 1) ? a1 : a2) * qrot[16 * (4 * prod + j) + 2 * n + (d >> 1)]
+                           : ask * qsk[32 * j + 4 * n + d]);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       float M = fabsf(r);
@@ -467,18 +470,23 @@ __device__ void prepared_query_pieces(int nprod, const float* qrot, const float*
 }
 
 // Prepared fp32 query: q itself, or [R q, S R q] (TURBO), or S q (QJL1); for
-// the last two also the FP8 pieces of the key products when `pieces` is given.
-// 128 threads, or 384 for TURBO pieces (all 12 blocks at once); the products
-// take one output per thread of the first 128.
+// the last two also the pieces of the key products when `pieces` is given
+// (QJL: of S q; TURBO: of the products scaled by scale_log2, the softmax scale
+// in log2 units, the sketch's also by 2 kappa, with the constant terms
+// lv0 scale_log2 sum(R q) and -kappa scale_log2 sum(S R q) after the first
+// record's scale bytes).  128 threads, or 384 for TURBO pieces (all 12 blocks
+// at once); the products take one output per thread of the first 128.
 template <typename QT>
 __global__ void __launch_bounds__(384) prep_query_kernel(const QT* __restrict__ q, int qw_in, int qw_out,
                                                          int fmt, const float* __restrict__ rot,
                                                          const float* __restrict__ proj,
-                                                         const float* __restrict__ levels,
-                                                         float* __restrict__ out, uint8_t* __restrict__ pieces) {
+                                                         const float* __restrict__ levels, float scale_log2,
+                                                         float kappa, float* __restrict__ out,
+                                                         uint8_t* __restrict__ pieces) {
   __shared__ float qin[640];
   __shared__ float qrot[128];
   __shared__ float qsr[128];
+  __shared__ float red[2][2];
   const size_t row = blockIdx.x;
   const int tid = threadIdx.x, nthr = blockDim.x;
   const bool prod = tid < 128;
@@ -501,8 +509,27 @@ __global__ void __launch_bounds__(384) prep_query_kernel(const QT* __restrict__ 
     }
     if (pieces) {
       __syncthreads();
-      prepared_query_pieces(3, qrot, qsr, levels[2] - levels[0], levels[1] - levels[0], true,
-                            pieces + row * kTurboPieceBytes);
+      uint8_t* pr = pieces + row * kTurboPieceBytes;
+      prepared_query_pieces(3, qrot, qsr, (levels[2] - levels[0]) * scale_log2, (levels[1] - levels[0]) * scale_log2,
+                            2.f * kappa * scale_log2, true, pr);
+      if (tid < 128) {  // the sums of R q and S R q: two waves of 64
+        float sr = qrot[tid], ss = qsr[tid];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+          sr += __shfl_xor(sr, off);
+          ss += __shfl_xor(ss, off);
+        }
+        if ((tid & 63) == 0) {
+          red[tid >> 6][0] = sr;
+          red[tid >> 6][1] = ss;
+        }
+      }
+      __syncthreads();
+      if (tid == 0) {
+        float* cst = reinterpret_cast<float*>(pr + kTurboPieceConstOff);
+        cst[0] = levels[0] * scale_log2 * (red[0][0] + red[1][0]);
+        cst[1] = -kappa * scale_log2 * (red[0][1] + red[1][1]);
+      }
     }
   } else if (fmt == KV_FMT_QJL1_FP4V) {
     if (prod) {
@@ -513,7 +540,7 @@ __global__ void __launch_bounds__(384) prep_query_kernel(const QT* __restrict__ 
     }
     if (pieces) {
       __syncthreads();
-      prepared_query_pieces(1, nullptr, qsr, 0.f, 0.f, false, pieces + row * kQjlPieceBytes);
+      prepared_query_pieces(1, nullptr, qsr, 0.f, 0.f, 1.f, false, pieces + row * kQjlPieceBytes);
     }
   } else {
     for (int c = tid; c < qw_out; c += nthr) dst[c] = qin[c];
@@ -773,14 +800,17 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
   uint8_t* qpieces = turbo || (mfma && L.format == KV_FMT_QJL1_FP4V)
                          ? reinterpret_cast<uint8_t*>(wsb + wsl.qpiece_off)
                          : nullptr;
+  const float kappa = (float)(1.2533141373155002512 / (double)(L.qjl_m > 0 ? L.qjl_m : 1));
   if (!(mfma && L.format == KV_FMT_FP4)) {
     const int prep_threads = qpieces && L.format == KV_FMT_TURBO ? 384 : 128;
     if (q_dtype == KV_DT_F32)
       prep_query_kernel<float><<<rows, prep_threads, 0, st>>>(static_cast<const float*>(q), qw_in, qw_out, L.format,
-                                                     c->rot, c->proj, c->lm_levels, qv, qpieces);
+                                                     c->rot, c->proj, c->lm_levels, scale * kLog2e, kappa, qv,
+                                                     qpieces);
     else
       prep_query_kernel<uint16_t><<<rows, prep_threads, 0, st>>>(static_cast<const uint16_t*>(q), qw_in, qw_out,
-                                                        L.format, c->rot, c->proj, c->lm_levels, qv, qpieces);
+                                                        L.format, c->rot, c->proj, c->lm_levels, scale * kLog2e,
+                                                        kappa, qv, qpieces);
   }
   if (turbo) {
     TurboDecodeArgs f{};
@@ -794,25 +824,26 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     f.pm = page_map(c);
     f.sel = sel;
     f.sel_stride = sel_stride;
-    f.q = qv;
     f.qpieces = qpieces;
     f.seq_lens = seq_lens;
     f.max_len = max_seq_len;
     f.H = L.num_kv_heads;
     f.cap = L.capacity;
     f.Hq = num_q_heads;
-    f.scale_log2 = scale * kLog2e;
-    f.kappa = (float)(1.2533141373155002512 / (double)L.qjl_m);
     f.part = part;
     f.splits = plan.splits;
     f.per_split = plan.tokens_per_split;
     f.nq = nq;
+    f.gr = num_q_heads / L.num_kv_heads;
     f.t_lo = L.sink_tokens;
     f.recent = L.recent_tokens;
     f.part_splits = part_splits;
     if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), st) != hipSuccess) return KV_EDEVICE;
-    for (f.qj = 0; f.qj < nq; ++f.qj) {  // one pass over the cache per query token
-      int rc = launch_decode_turbo(f, B, num_q_heads / L.num_kv_heads, st);
+    // one launch per 16 (query, head) pairs of a KV head, each over the whole
+    // cache: a sequence's queries share the tiles
+    for (f.c0 = 0; f.c0 < nq * f.gr; f.c0 += 16) {
+      f.ncol = std::min(16, nq * f.gr - f.c0);
+      int rc = launch_decode_turbo(f, B, st);
       if (rc != KV_OK) return rc;
     }
     if (windowed) launch_window(c, q, q_dtype, num_q_heads, nq, seq_lens, max_seq_len, scale, part, part_splits,

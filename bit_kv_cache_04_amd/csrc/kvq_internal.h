@@ -79,6 +79,9 @@ struct DecodeWorkspace {
 // 4 scale bytes + 12 unused).
 constexpr int kPieceProductBytes = 4 * 144;
 constexpr int kTurboPieceBytes = 3 * kPieceProductBytes;  // code words 0..3, 4..7, sketch
+// TURBO: the two constant terms (fp32) in the unused bytes of the first
+// (product, piece) record: lv0 * scale * sum(R q), -kappa * scale * sum(S R q)
+constexpr int kTurboPieceConstOff = 132;
 constexpr int kQjlPieceBytes = kPieceProductBytes;        // sketch
 DecodeWorkspace decode_workspace(const kv_layout* L, int num_q_heads, int splits);
 // Size of the library's own decode workspace (kv_decode_attention_static).

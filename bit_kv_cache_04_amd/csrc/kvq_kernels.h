@@ -44,8 +44,9 @@ struct MfmaDecodeArgs {
 
 int launch_decode_mfma(const MfmaDecodeArgs& a, int format, int B, int G, hipStream_t st);
 
-// TurboQuant cache (d = 128, m = 128, 2-bit symmetric codebook), G = Hq / H in
-// {1, 2, 4, 8}; queries prepared as [R q | S R q] fp32.
+// TurboQuant cache (d = 128, m = 128, 2-bit symmetric codebook): per query
+// row the FP6 pieces of the scaled key-product operands and the two constant
+// terms (kTurboPieceBytes, written by the query preparation).
 struct TurboDecodeArgs {
   const uint8_t* k_codes;   // [B][H][cap][32]
   const uint8_t* k_sketch;  // [B][H][cap][16]
@@ -55,14 +56,15 @@ struct TurboDecodeArgs {
   const uint16_t* v_norm;   // [B][H][cap] fp16
   PageMap pm;               // token rows: [B][H][cap] above, or a paged pool
   const float* levels;      // 4 codebook levels, ascending, symmetric
-  const float* q;           // [B][Hq][256]
-  const uint8_t* qpieces;   // [B][Hq][kTurboPieceBytes]: FP6 pieces of the key-product operands
+  const uint8_t* qpieces;   // [B][nq][Hq][kTurboPieceBytes]
   const int32_t* seq_lens;
   int max_len, H, cap, Hq;
-  float scale_log2, kappa;
   float* part;  // [B][nq][Hq][part_splits][130]
   int splits, per_split;
-  int nq, qj;  // query tokens per sequence; the one this launch takes
+  // nq query tokens per sequence of gr query heads per KV head, numbered
+  // c = j * gr + g (query j, head g); one launch takes the ncol <= 16 of them
+  // from c0 as its columns
+  int nq, gr, c0, ncol;
   // mixed precision: packed tokens [t_lo, L - recent); split s from
   // (t_lo & ~31) + s * per_split (tiles start 32-aligned, tokens below t_lo masked)
   int t_lo, recent, part_splits;
@@ -72,7 +74,7 @@ struct TurboDecodeArgs {
   int sel_stride;
 };
 
-int launch_decode_turbo(const TurboDecodeArgs& a, int B, int G, hipStream_t st);
+int launch_decode_turbo(const TurboDecodeArgs& a, int B, hipStream_t st);
 
 // Shared-latent cache (512 FP4 + 64 bf16 RoPE), bf16 queries, Hq in {32, 64, 128}.
 bool latent_fast_path_ok(const kv_layout& L, int num_q_heads, int nq, int q_dtype);

@@ -12,6 +12,10 @@
 * The fp16 range of the matrix-core decode (FP4 and the shared latent): data at
   the edges of the documented exact range pass on the default path; data beyond
   it (group maxima 1e5 and 1e-6, queries 1e5) pass with KV_DECODE_FP32.
+* TurboQuant decode at even and odd capacities: the matrix-core kernel loads
+  the fp16 norms as token pairs when every row range has even length and one
+  token at a time otherwise; the last token of a full-capacity sequence must
+  count in both (no outlier channels, so logits near 0 make a lost token show).
 """
 
 import numpy as np
@@ -269,3 +273,26 @@ def test_latent_decode_fp16_range(case):
     err = row_rel_err(out, ref)
     print(f"[latent range {case}] max row rel err {err.max():.3e}", flush=True)
     assert np.isfinite(out).all() and err.max() <= RTOL
+
+
+# ---------------------------------------------------------------- TurboQuant norms at the end of a row range
+
+@pytest.mark.parametrize("cap", [776, 777])
+@pytest.mark.parametrize("nq", [1, 2])
+def test_turbo_last_token_at_even_and_odd_capacity(cap, nq):
+    cfg = C["turbo_b8_t128k"].scaled(batch=2, hq=16, hkv=2, context=cap, n_outlier=0)
+    print(f"[turbo capacity] cap={cap} nq={nq}", flush=True)
+    torch.manual_seed(0)
+    consts = oracle_constants(cfg)
+    cache = new_cache(cfg)
+    K, V = synth.make_kv(cfg, device="cuda")
+    cache.append(K.contiguous(), V.contiguous(), 0)
+    torch.cuda.synchronize()
+    enc = oracle_encode(cfg, host64(K), host64(V), consts)
+    q = synth.make_queries(cfg.scaled(hq=nq * cfg.hq), device="cuda").view(cfg.batch, nq, cfg.hq, -1)
+    lens = np.array([cap, cap - 1], dtype=np.int32)
+    out = cache.decode(q, torch.from_numpy(lens).cuda(), softmax_scale(cfg)).cpu().numpy()
+    ref = OA.decode_attention_multi("turbo", enc, host64(q), lens, softmax_scale(cfg), cfg.hkv, consts)
+    err = row_rel_err(out.reshape(-1, out.shape[-1]), ref.reshape(-1, ref.shape[-1]))
+    print(f"  max row rel err {err.max():.3e}", flush=True)
+    assert err.max() <= RTOL
