@@ -421,13 +421,15 @@ __device__ __forceinline__ uint32_t e2m3_code(float y, float& val) {
 // e at bits [6 e, 6 e + 6)), then the 4 blocks' E8M0 scale bytes (e + 127), 144
 // bytes in all.  32 threads per block, as many blocks at a time as the workgroup
 // has threads for.
+// Threads [0, nthr) of the caller's group (tid = index in the group, both
+// multiples of 32 apart from tid's low bits) do the work.
 __device__ void prepared_query_pieces(int nprod, const float* qrot, const float* qsk, float a1, float a2, float ask,
-                                      bool fp6, uint8_t* out) {
-  const int tid = threadIdx.x, e = tid & 31, d = e >> 3, n = e & 7;
+                                      bool fp6, uint8_t* out, int tid, int nthr) {
+  const int e = tid & 31, d = e >> 3, n = e & 7;
   // TURBO (FP6): the key operand's element 8 d + n is its bit times 1, 2, 4, 4
   // for d = 0, 1, 2, 3, so this side carries 1, 1/2, 1/4, 1/4
   const float dfac = fp6 ? (d == 0 ? 1.f : d == 1 ? 0.5f : 0.25f) : 1.f;
-  for (int blk = tid >> 5; blk < 4 * nprod; blk += (int)(blockDim.x >> 5)) {
+  for (int blk = tid >> 5; blk < 4 * nprod; blk += nthr >> 5) {
     const int prod = blk >> 2, j = blk & 3;
     const bool code = prod < nprod - 1;
     float r = dfac * (code ? ((d & 1) ? a1 : a2) * qrot[16 * (4 * prod + j) + 2 * n + (d >> 1)]
@@ -469,81 +471,111 @@ __device__ void prepared_query_pieces(int nprod, const float* qrot, const float*
   }
 }
 
-// Prepared fp32 query: q itself, or [R q, S R q] (TURBO), or S q (QJL1); for
-// the last two also the pieces of the key products when `pieces` is given
-// (QJL: of S q; TURBO: of the products scaled by scale_log2, the softmax scale
-// in log2 units, the sketch's also by 2 kappa, with the constant terms
-// lv0 scale_log2 sum(R q) and -kappa scale_log2 sum(S R q) after the first
-// record's scale bytes).  128 threads, or 384 for TURBO pieces (all 12 blocks
-// at once); the products take one output per thread of the first 128.
+// Prepared fp32 query of the formats other than TURBO (prep_turbo_kernel):
+// S q (QJL1), with the FP8 pieces of its key product when `pieces` is given,
+// or q itself.  128 threads; the product takes one output per thread.
 template <typename QT>
-__global__ void __launch_bounds__(384) prep_query_kernel(const QT* __restrict__ q, int qw_in, int qw_out,
-                                                         int fmt, const float* __restrict__ rot,
-                                                         const float* __restrict__ proj,
-                                                         const float* __restrict__ levels, float scale_log2,
-                                                         float kappa, float* __restrict__ out,
+__global__ void __launch_bounds__(128) prep_query_kernel(const QT* __restrict__ q, int qw_in, int qw_out, int fmt,
+                                                         const float* __restrict__ proj, float* __restrict__ out,
                                                          uint8_t* __restrict__ pieces) {
   __shared__ float qin[640];
-  __shared__ float qrot[128];
   __shared__ float qsr[128];
-  __shared__ float red[2][2];
   const size_t row = blockIdx.x;
   const int tid = threadIdx.x, nthr = blockDim.x;
-  const bool prod = tid < 128;
   for (int c = tid; c < qw_in; c += nthr) qin[c] = load_as_f32(q + row * qw_in, c);
   __syncthreads();
   float* dst = out + row * qw_out;
-  if (fmt == KV_FMT_TURBO) {
-    if (prod) {
-      float acc = 0.f;
-      for (int j = 0; j < 128; ++j) acc = fmaf(rot[tid * 128 + j], qin[j], acc);
-      qrot[tid] = acc;
-      dst[tid] = acc;
-    }
-    __syncthreads();
-    if (prod) {
-      float acc2 = 0.f;
-      for (int j = 0; j < 128; ++j) acc2 = fmaf(proj[tid * 128 + j], qrot[j], acc2);
-      dst[128 + tid] = acc2;
-      qsr[tid] = acc2;
-    }
+  if (fmt == KV_FMT_QJL1_FP4V) {
+    float acc = 0.f;
+    for (int j = 0; j < 128; ++j) acc = fmaf(proj[tid * 128 + j], qin[j], acc);
+    dst[tid] = acc;
+    qsr[tid] = acc;
     if (pieces) {
       __syncthreads();
-      uint8_t* pr = pieces + row * kTurboPieceBytes;
-      prepared_query_pieces(3, qrot, qsr, (levels[2] - levels[0]) * scale_log2, (levels[1] - levels[0]) * scale_log2,
-                            2.f * kappa * scale_log2, true, pr);
-      if (tid < 128) {  // the sums of R q and S R q: two waves of 64
-        float sr = qrot[tid], ss = qsr[tid];
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-          sr += __shfl_xor(sr, off);
-          ss += __shfl_xor(ss, off);
-        }
-        if ((tid & 63) == 0) {
-          red[tid >> 6][0] = sr;
-          red[tid >> 6][1] = ss;
-        }
-      }
-      __syncthreads();
-      if (tid == 0) {
-        float* cst = reinterpret_cast<float*>(pr + kTurboPieceConstOff);
-        cst[0] = levels[0] * scale_log2 * (red[0][0] + red[1][0]);
-        cst[1] = -kappa * scale_log2 * (red[0][1] + red[1][1]);
-      }
-    }
-  } else if (fmt == KV_FMT_QJL1_FP4V) {
-    if (prod) {
-      float acc = 0.f;
-      for (int j = 0; j < 128; ++j) acc = fmaf(proj[tid * 128 + j], qin[j], acc);
-      dst[tid] = acc;
-      qsr[tid] = acc;
-    }
-    if (pieces) {
-      __syncthreads();
-      prepared_query_pieces(1, nullptr, qsr, 0.f, 0.f, 1.f, false, pieces + row * kQjlPieceBytes);
+      prepared_query_pieces(1, nullptr, qsr, 0.f, 0.f, 1.f, false, pieces + row * kQjlPieceBytes, tid, nthr);
     }
   } else {
     for (int c = tid; c < qw_out; c += nthr) dst[c] = qin[c];
+  }
+}
+
+// TurboQuant query preparation, one query row per workgroup of 384 threads:
+// threads i < 128 form (R q)[i] and then (S R q)[i] from row i of R and S
+// (float4 loads), [R q | S R q] is written (fp32, for the general kernel), and
+// when `pieces` is given all 12 blocks of FP6 pieces (prepared_query_pieces)
+// are made at once, with the constant terms.  An asymmetric codebook (lv0 +
+// lv3 != lv1 + lv2), which the bit-plane key products cannot represent, makes
+// the constant terms NaN: every output of the matrix-core kernel is then NaN
+// rather than silently wrong.
+constexpr int kTurboPrepThreads = 384;
+
+template <typename QT>
+__global__ void __launch_bounds__(kTurboPrepThreads) prep_turbo_kernel(
+    const QT* __restrict__ q, const float* __restrict__ rot, const float* __restrict__ proj,
+    const float* __restrict__ levels, float scale_log2, float kappa, float* __restrict__ out,
+    uint8_t* __restrict__ pieces) {
+  __shared__ float qin[128];
+  __shared__ float qrot[128];
+  __shared__ float qsr[128];
+  __shared__ float red[2][2];
+  const int tid = threadIdx.x;
+  const size_t row = blockIdx.x;
+  const bool prod = tid < 128;
+  if (prod) qin[tid] = load_as_f32(q + row * 128, tid);
+  __syncthreads();
+  auto matvec = [&](const float* __restrict__ m, const float* x) {
+    const float4* mr = reinterpret_cast<const float4*>(m + (size_t)tid * 128);
+    float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll 8
+    for (int j4 = 0; j4 < 32; j4 += 2) {
+      const float4 v = mr[j4], u = mr[j4 + 1];
+      acc0 = fmaf(v.x, x[4 * j4], acc0);
+      acc0 = fmaf(v.y, x[4 * j4 + 1], acc0);
+      acc0 = fmaf(v.z, x[4 * j4 + 2], acc0);
+      acc0 = fmaf(v.w, x[4 * j4 + 3], acc0);
+      acc1 = fmaf(u.x, x[4 * j4 + 4], acc1);
+      acc1 = fmaf(u.y, x[4 * j4 + 5], acc1);
+      acc1 = fmaf(u.z, x[4 * j4 + 6], acc1);
+      acc1 = fmaf(u.w, x[4 * j4 + 7], acc1);
+    }
+    return acc0 + acc1;
+  };
+  float rq = 0.f, srq = 0.f;
+  if (prod) {
+    rq = matvec(rot, qin);
+    qrot[tid] = rq;
+  }
+  __syncthreads();
+  if (prod) {
+    srq = matvec(proj, qrot);
+    qsr[tid] = srq;
+    out[row * 256 + tid] = rq;
+    out[row * 256 + 128 + tid] = srq;
+  }
+  if (!pieces) return;  // uniform across the workgroup
+  __syncthreads();
+  const float lv0 = levels[0], lv1 = levels[1], lv2 = levels[2], lv3 = levels[3];
+  uint8_t* pr = pieces + row * kTurboPieceBytes;
+  prepared_query_pieces(3, qrot, qsr, (lv2 - lv0) * scale_log2, (lv1 - lv0) * scale_log2, 2.f * kappa * scale_log2,
+                        true, pr, tid, kTurboPrepThreads);
+  if (prod) {  // the sums of R q and S R q: two waves
+    float sr = rq, ss = srq;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      sr += __shfl_xor(sr, off);
+      ss += __shfl_xor(ss, off);
+    }
+    if ((tid & 63) == 0) {
+      red[tid >> 6][0] = sr;
+      red[tid >> 6][1] = ss;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const bool symmetric = lv0 + lv3 == lv1 + lv2;
+    float* cst = reinterpret_cast<float*>(pr + kTurboPieceConstOff);
+    cst[0] = symmetric ? lv0 * scale_log2 * (red[0][0] + red[1][0]) : __builtin_nanf("");
+    cst[1] = -kappa * scale_log2 * (red[0][1] + red[1][1]);
   }
 }
 
@@ -801,16 +833,20 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
                          ? reinterpret_cast<uint8_t*>(wsb + wsl.qpiece_off)
                          : nullptr;
   const float kappa = (float)(1.2533141373155002512 / (double)(L.qjl_m > 0 ? L.qjl_m : 1));
-  if (!(mfma && L.format == KV_FMT_FP4)) {
-    const int prep_threads = qpieces && L.format == KV_FMT_TURBO ? 384 : 128;
+  if (L.format == KV_FMT_TURBO) {
     if (q_dtype == KV_DT_F32)
-      prep_query_kernel<float><<<rows, prep_threads, 0, st>>>(static_cast<const float*>(q), qw_in, qw_out, L.format,
-                                                     c->rot, c->proj, c->lm_levels, scale * kLog2e, kappa, qv,
-                                                     qpieces);
+      prep_turbo_kernel<float><<<rows, kTurboPrepThreads, 0, st>>>(static_cast<const float*>(q), c->rot, c->proj,
+                                                                   c->lm_levels, scale * kLog2e, kappa, qv, qpieces);
     else
-      prep_query_kernel<uint16_t><<<rows, prep_threads, 0, st>>>(static_cast<const uint16_t*>(q), qw_in, qw_out,
-                                                        L.format, c->rot, c->proj, c->lm_levels, scale * kLog2e,
-                                                        kappa, qv, qpieces);
+      prep_turbo_kernel<uint16_t><<<rows, kTurboPrepThreads, 0, st>>>(
+          static_cast<const uint16_t*>(q), c->rot, c->proj, c->lm_levels, scale * kLog2e, kappa, qv, qpieces);
+  } else if (!(mfma && L.format == KV_FMT_FP4)) {
+    if (q_dtype == KV_DT_F32)
+      prep_query_kernel<float><<<rows, 128, 0, st>>>(static_cast<const float*>(q), qw_in, qw_out, L.format, c->proj,
+                                                     qv, qpieces);
+    else
+      prep_query_kernel<uint16_t><<<rows, 128, 0, st>>>(static_cast<const uint16_t*>(q), qw_in, qw_out, L.format,
+                                                        c->proj, qv, qpieces);
   }
   if (turbo) {
     TurboDecodeArgs f{};

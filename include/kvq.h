@@ -173,7 +173,9 @@ enum kv_buffer {
  *              16-byte aligned
  *   lm_levels  TURBO: 2^lm_bits Lloyd-Max levels, ascending and symmetric
  *              (levels[i] = -levels[last - i], as kv_lloyd_max_gaussian makes
- *              them: the decode kernel relies on it)
+ *              them: the matrix-core decode relies on it and, given levels
+ *              with lv0 + lv3 != lv1 + lv2, returns NaN outputs; the general
+ *              kernel, opts->flags KV_DECODE_FP32, reads any levels)
  *   lm_thresh  TURBO: 2^lm_bits - 1 thresholds, ascending
  * A missing or misaligned constant is KV_EINVAL.                           */
 typedef struct kv_cache {

@@ -12,6 +12,9 @@
 * The fp16 range of the matrix-core decode (FP4 and the shared latent): data at
   the edges of the documented exact range pass on the default path; data beyond
   it (group maxima 1e5 and 1e-6, queries 1e5) pass with KV_DECODE_FP32.
+* TurboQuant with an asymmetric codebook, which the matrix-core kernel's
+  bit-plane key products cannot represent: its outputs are NaN, and the
+  general kernel (KV_DECODE_FP32) still matches the oracle.
 * TurboQuant decode at even and odd capacities: the matrix-core kernel loads
   the fp16 norms as token pairs when every row range has even length and one
   token at a time otherwise; the last token of a full-capacity sequence must
@@ -295,4 +298,31 @@ def test_turbo_last_token_at_even_and_odd_capacity(cap, nq):
     ref = OA.decode_attention_multi("turbo", enc, host64(q), lens, softmax_scale(cfg), cfg.hkv, consts)
     err = row_rel_err(out.reshape(-1, out.shape[-1]), ref.reshape(-1, ref.shape[-1]))
     print(f"  max row rel err {err.max():.3e}", flush=True)
+    assert err.max() <= RTOL
+
+
+# ---------------------------------------------------------------- TurboQuant codebook precondition
+
+def test_turbo_asymmetric_codebook_is_loud_on_the_matrix_cores():
+    cfg = C["turbo_b8_t128k"].scaled(batch=2, hq=16, hkv=2, context=300)
+    print("[turbo asymmetric codebook]", flush=True)
+    consts = oracle_constants(cfg)
+    f32 = lambda x: np.asarray(x, np.float32).astype(np.float64)  # noqa: E731  (both sides read the same values)
+    lv = f32(np.array([-1.4, -0.5, 0.4, 1.6]) / np.sqrt(cfg.head_dim))  # lv0 + lv3 != lv1 + lv2
+    consts["levels"], consts["thresholds"] = lv, f32((lv[1:] + lv[:-1]) / 2)
+    lib = {k: np.asarray(v, np.float32) for k, v in consts.items()}
+    from bit_kv_cache_04_amd.cache import PackedKVCache
+    cache = PackedKVCache("turbo", cfg.batch, cfg.hkv, cfg.head_dim, cfg.context, device="cuda", constants=lib)
+    K, V = synth.make_kv(cfg, device="cuda")
+    cache.append(K.contiguous(), V.contiguous(), 0)
+    torch.cuda.synchronize()
+    q = synth.make_queries(cfg, device="cuda")
+    lens = torch.tensor([cfg.context, 123], dtype=torch.int32, device="cuda")
+    out = cache.decode(q, lens, softmax_scale(cfg)).cpu().numpy()
+    assert np.isnan(out).all()
+    enc = oracle_encode(cfg, host64(K), host64(V), consts)
+    got = cache.decode(q, lens, softmax_scale(cfg), flags=kvq.DECODE_FP32).cpu().numpy()
+    ref = OA.decode_attention("turbo", enc, host64(q), lens.cpu().numpy(), softmax_scale(cfg), cfg.hkv, consts)
+    err = row_rel_err(got, ref)
+    print(f"  general kernel max row rel err {err.max():.3e}", flush=True)
     assert err.max() <= RTOL
