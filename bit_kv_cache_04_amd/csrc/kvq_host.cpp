@@ -81,10 +81,10 @@ int prepared_query_width(const kv_layout* L) {
 int value_width(const kv_layout* L) { return L->head_dim; }
 
 bool turbo_fast_path_ok(const kv_layout& L, int num_q_heads, int nq) {
-  const int G = num_q_heads / L.num_kv_heads;
-  (void)nq;  // several queries: one launch per query
+  (void)num_q_heads;  // any group: (query, head) pairs, 16 per launch
+  (void)nq;
   return L.format == KV_FMT_TURBO && L.head_dim == 128 && L.qjl_m == 128 && L.lm_bits == 2 &&
-         (G == 1 || G == 2 || G == 4 || G == 8) && (size_t)L.capacity * 32 < (size_t(1) << 31);
+         (size_t)L.capacity * 32 < (size_t(1) << 31);
 }
 
 bool latent_fast_path_ok(const kv_layout& L, int num_q_heads, int nq, int q_dtype) {

@@ -15,6 +15,9 @@
 * TurboQuant with an asymmetric codebook, which the matrix-core kernel's
   bit-plane key products cannot represent: its outputs are NaN, and the
   general kernel (KV_DECODE_FP32) still matches the oracle.
+* TurboQuant head groups beyond 1, 2, 4, 8 on the matrix-core kernel (its
+  columns are (query, head) pairs, 16 per launch): G = 16, and G = 3 with 3
+  queries (9 pairs, then 16 + 2 with 6 queries).
 * TurboQuant decode at even and odd capacities: the matrix-core kernel loads
   the fp16 norms as token pairs when every row range has even length and one
   token at a time otherwise; the last token of a full-capacity sequence must
@@ -325,4 +328,26 @@ def test_turbo_asymmetric_codebook_is_loud_on_the_matrix_cores():
     ref = OA.decode_attention("turbo", enc, host64(q), lens.cpu().numpy(), softmax_scale(cfg), cfg.hkv, consts)
     err = row_rel_err(got, ref)
     print(f"  general kernel max row rel err {err.max():.3e}", flush=True)
+    assert err.max() <= RTOL
+
+
+# ---------------------------------------------------------------- TurboQuant head groups
+
+@pytest.mark.parametrize("hq,hkv,nq", [(16, 1, 1), (32, 2, 1), (6, 2, 3), (6, 2, 6)])
+def test_turbo_any_head_group_on_the_matrix_cores(hq, hkv, nq):
+    cfg = C["turbo_b8_t128k"].scaled(batch=2, hq=hq, hkv=hkv, context=500)
+    print(f"[turbo group] hq={hq} hkv={hkv} nq={nq}", flush=True)
+    torch.manual_seed(0)
+    consts = oracle_constants(cfg)
+    cache = new_cache(cfg)
+    K, V = synth.make_kv(cfg, device="cuda")
+    cache.append(K.contiguous(), V.contiguous(), 0)
+    torch.cuda.synchronize()
+    enc = oracle_encode(cfg, host64(K), host64(V), consts)
+    q = synth.make_queries(cfg.scaled(hq=nq * cfg.hq), device="cuda").view(cfg.batch, nq, cfg.hq, -1)
+    lens = np.array([cfg.context, 211], dtype=np.int32)
+    out = cache.decode(q, torch.from_numpy(lens).cuda(), softmax_scale(cfg)).cpu().numpy()
+    ref = OA.decode_attention_multi("turbo", enc, host64(q), lens, softmax_scale(cfg), cfg.hkv, consts)
+    err = row_rel_err(out.reshape(-1, out.shape[-1]), ref.reshape(-1, ref.shape[-1]))
+    print(f"  max row rel err {err.max():.3e}", flush=True)
     assert err.max() <= RTOL
