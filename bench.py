@@ -177,7 +177,7 @@ def measured_profile(workload, kind):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
         src = os.path.join(ROOT, kv.get("source", ""))
-        if not os.path.isfile(src):
+        if kv.get("role", "attention") != "attention" or not os.path.isfile(src):
             continue
         if hashlib.sha256(open(src, "rb").read()).hexdigest() == kv.get("source_sha256"):
             return kv
@@ -205,7 +205,8 @@ def roofline(cfg, nbytes, kern_us, nq=1, plain=True):
     r.update(kernel="split-context attention", kernel_us=round(kern_us, 2),
              algorithmic_bytes_per_launch=nbytes)
     if util:
-        r["utilisation"] = {k: float(util[k]) for k in ("mfma_busy", "valu_busy", "lds_busy") if k in util}
+        r["utilisation"] = {k: float(util[k]) for k in ("mfma_busy", "valu_active", "lds_active", "wait_inst_share")
+                            if k in util}
     return r
 
 
