@@ -17,15 +17,20 @@
 // keep the LDS instructions per tile (next to the matrix cores, the binding
 // resource) at half those of sixteen-head waves.
 //
-// The packed tiles come into registers by plain buffer loads, one tile ahead
+// The packed tiles come into registers by plain buffer loads, two tiles ahead
 // (each thread its 1/256 of the tile), and are dequantised from there into one
-// of three token-major fp16 tiles in LDS.  Per 32-token tile i, after one
-// workgroup barrier, each wave:
-//   1. S^T = K Q^T on tile i (36 products);
-//   2. dequantises its share of tile i + 1, then loads its share of tile i + 2;
-//   3. online softmax (each lane pair holds one head; the reference max moves
-//      only when a tile max passes it by 2^8, then the accumulators rescale);
-//   4. O += P V (32 products, V read transposed with ds_read_b64_tr_b16).
+// of three token-major fp16 tiles in LDS.  A wave issues in order, and its
+// vector and LDS work runs beside a matrix product only when issued after it,
+// so each tile's work is split in two phases of fenced groups, each group one
+// product followed by the vector work that hides behind it:
+//   1. S^T = K Q^T on tile i (36 products), with the dequantisation of tile
+//      i + 1 and then the loads of tile i + 2;
+//   2. O += P V for tile i - 1 (32 products, V read transposed with
+//      ds_read_b64_tr_b16), with the online softmax of tile i (each lane pair
+//      holds one head; the reference max moves only when a tile max passes it
+//      by 2^8, and the accumulators are rescaled before the products of the
+//      next tile).
+// One workgroup barrier per tile.
 // FP4 element values times their bf16 scale are exact in fp16 (within its range);
 // the bf16 query's latent part is exact in fp16 within the fp16 normal range.
 #include <hip/hip_runtime.h>
@@ -108,9 +113,11 @@ struct Res {
 };
 
 // This thread's share of one packed tile: code chunks of 16 bytes (32 channels
-// of one token: chunk c is token c / 16, channels 32 (c % 16) + [0, 32)), their
-// two bf16 scales (4 bytes), and one 16-byte chunk of the RoPE rows (chunk r is
-// token r / 8, channels 8 (r % 8) + [0, 8)).  Chunks c = tid and tid + 256,
+// of one token), their two bf16 scales (4 bytes), and one 16-byte chunk of the
+// RoPE rows (chunk r is token r / 8, channels 8 (r % 8) + [0, 8)).  Code chunk
+// j of thread tid is token chunk_token(tid, j), channels 32 (tid / 16) + [0, 32):
+// sixteen consecutive lanes take sixteen tokens, whose fp16 rows start in
+// distinct LDS banks, so that their dequantised writes do not conflict.
 // RoPE chunk r = tid.
 struct Packed {
   v4i_t c[2];
@@ -118,43 +125,64 @@ struct Packed {
   v4i_t r;
 };
 
-// Loads of this thread's share of a tile whose token k (of 32) sits at token
-// offset tok(k) of the resources (tok < 0, or past the end of a resource: zeros).
-template <class TokOf>
-__device__ __forceinline__ void load_tile(Packed& p, int tid, const Res& res, TokOf tok) {
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int ch = tid + 256 * j;
-    const int t = tok(ch >> 4);
-    const uint32_t oc = t < 0 ? 0xFFFFFFFFu : (uint32_t)t * 256u + (ch & 15) * 16;
-    const uint32_t os = t < 0 ? 0xFFFFFFFFu : (uint32_t)t * 64u + (ch & 15) * 4;
-    p.c[j] = __builtin_amdgcn_raw_buffer_load_b128(res.codes, oc, 0, 0);
-    p.s[j] = __builtin_amdgcn_raw_buffer_load_b32(res.scale, os, 0, 0);
-  }
-  const int tr = tok(tid >> 3);
-  const uint32_t orp = tr < 0 ? 0xFFFFFFFFu : (uint32_t)tr * 128u + (tid & 7) * 16;
-  p.r = __builtin_amdgcn_raw_buffer_load_b128(res.rope, orp, 0, 0);
-}
+__device__ __forceinline__ int chunk_token(int tid, int j) { return 16 * j + (tid & 15); }
 
-// Dequantise this thread's share of a tile into the token-major fp16 tile kt.
-__device__ __forceinline__ void dequant_tile(const Packed& p, uint16_t* kt, int tid) {
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int ch = tid + 256 * j;
-    const int t = ch >> 4, cc = ch & 15;
-    const uint32_t sw = (uint32_t)p.s[j];
-    const h2_t s0 = splat_bf16(sw & 0xFFFFu), s1 = splat_bf16(sw >> 16);
-    uint16_t* row = kt + kt_phys(t) * kKtStride + 32 * cc;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {  // octet q: channels 32 cc + 8 q + [0, 8), scale group 2 cc + q / 2
-      const uint32_t w = (uint32_t)p.c[j][q];
-      const h2_t sc = q < 2 ? s0 : s1;
-      *reinterpret_cast<uint4*>(row + 8 * q) =
-          uint4{__builtin_bit_cast(uint32_t, fp4x2<0>(w) * sc), __builtin_bit_cast(uint32_t, fp4x2<1>(w) * sc),
-                __builtin_bit_cast(uint32_t, fp4x2<2>(w) * sc), __builtin_bit_cast(uint32_t, fp4x2<3>(w) * sc)};
+// Load P of this thread's share of a tile whose token k (of 32) sits at token
+// offset tok(k) of the resources (tok < 0, or past the end of a resource:
+// zeros): P = 2 j is code chunk j, P = 2 j + 1 its scales, P = 4 the RoPE chunk.
+template <int P, class TokOf>
+__device__ __forceinline__ void load_part(Packed& p, int tid, const Res& res, TokOf tok) {
+  if constexpr (P == 4) {
+    const int tr = tok(tid >> 3);
+    const uint32_t orp = tr < 0 ? 0xFFFFFFFFu : (uint32_t)tr * 128u + (tid & 7) * 16;
+    p.r = __builtin_amdgcn_raw_buffer_load_b128(res.rope, orp, 0, 0);
+  } else {
+    constexpr int j = P / 2;
+    const int t = tok(chunk_token(tid, j)), cc = tid >> 4;
+    if constexpr (P % 2 == 0) {
+      const uint32_t oc = t < 0 ? 0xFFFFFFFFu : (uint32_t)t * 256u + cc * 16;
+      p.c[j] = __builtin_amdgcn_raw_buffer_load_b128(res.codes, oc, 0, 0);
+    } else {
+      const uint32_t os = t < 0 ? 0xFFFFFFFFu : (uint32_t)t * 64u + cc * 4;
+      p.s[j] = __builtin_amdgcn_raw_buffer_load_b32(res.scale, os, 0, 0);
     }
   }
-  *reinterpret_cast<v4i_t*>(kt + kt_phys(tid >> 3) * kKtStride + kLat + 8 * (tid & 7)) = p.r;
+}
+
+// Dequantisation of this thread's share of a tile into the token-major fp16
+// tile kt, in nine units: unit u < 8 is octet u % 4 (8 channels) of code chunk
+// u / 4, unit 8 the RoPE chunk.  sc holds the chunks' two scales as fp16 pairs,
+// set by each chunk's first unit.
+template <int U>
+__device__ __forceinline__ void dequant_unit(const Packed& p, uint16_t* kt, int tid, h2_t (&sc)[2][2]) {
+  if constexpr (U == 8) {
+    *reinterpret_cast<v4i_t*>(kt + kt_phys(tid >> 3) * kKtStride + kLat + 8 * (tid & 7)) = p.r;
+  } else {
+    constexpr int j = U / 4, q = U % 4;  // octet q: channels 32 cc + 8 q + [0, 8), scale group 2 cc + q / 2
+    const int t = chunk_token(tid, j), cc = tid >> 4;
+    if constexpr (q == 0) {
+      const uint32_t sw = (uint32_t)p.s[j];
+      sc[j][0] = splat_bf16(sw & 0xFFFFu);
+      sc[j][1] = splat_bf16(sw >> 16);
+    }
+    const uint32_t w = (uint32_t)p.c[j][q];
+    const h2_t s = sc[j][q >> 1];
+    *reinterpret_cast<uint4*>(kt + kt_phys(t) * kKtStride + 32 * cc + 8 * q) =
+        uint4{__builtin_bit_cast(uint32_t, fp4x2<0>(w) * s), __builtin_bit_cast(uint32_t, fp4x2<1>(w) * s),
+              __builtin_bit_cast(uint32_t, fp4x2<2>(w) * s), __builtin_bit_cast(uint32_t, fp4x2<3>(w) * s)};
+  }
+}
+
+// f(integral_constant<int, K>) for K in the sequence, in order.
+template <typename F, int... K>
+__device__ __forceinline__ void for_each_index(std::integer_sequence<int, K...>, F&& f) {
+  (f(std::integral_constant<int, K>{}), ...);
+}
+
+// The whole dequantisation of this thread's share, unscheduled (first tile).
+__device__ __forceinline__ void dequant_tile(const Packed& p, uint16_t* kt, int tid) {
+  h2_t sc[2][2];
+  for_each_index(std::make_integer_sequence<int, 9>{}, [&](auto U) { dequant_unit<decltype(U)::value>(p, kt, tid, sc); });
 }
 
 // Per-wave state that lives across tiles.
@@ -162,110 +190,147 @@ struct LatentWave {
   h8_t ql[32];   // query, latent part (fp16): B operand of 32 k-steps
   b8_t qr[4];    // query, RoPE part (bf16): 4 k-steps
   f16v_t o[16];  // output accumulators, N block n = channels 32 n + [0, 32)
-  float m_run;   // running max (log2 units) of this lane's head
+  float m_run;   // running reference max (log2 units) of this lane's head
   float l_run;   // running sum over this lane's tokens (the lane pair is added at the end)
 };
 
-// S^T = K Q^T for this wave's 32 heads on tile kt, one accumulation chain; the
-// operand reads run D k-steps ahead of the products.
-template <int D>
-__device__ __forceinline__ f16v_t qk_product(const LatentWave& w, const uint16_t* kt, int ka) {
+// Phase 1 of a tile: S^T = K Q^T for this wave's 32 heads on tile kt (one
+// accumulation chain in VGPRs, so that the output accumulators keep every
+// AGPR; operand reads D products ahead), with this thread's
+// dequantisation of the next tile into kt_next (unit u behind product 3 u + 1)
+// and, each once its registers are free, the five loads of the tile after it
+// (refill(pk, P) issues load P).
+template <int D, class Refill>
+__device__ __forceinline__ f16v_t qk_phase(const LatentWave& w, const uint16_t* kt, int ka, Packed& pk,
+                                           uint16_t* kt_next, int tid, Refill refill) {
   h8_t kf[36];
+  h2_t sc[2][2];
   f16v_t s = f16v_t{};
+  auto read = [&](int k) { kf[k] = *reinterpret_cast<const h8_t*>(kt + ka + 16 * k); };
 #pragma unroll
-  for (int k = 0; k < D; ++k) kf[k] = *reinterpret_cast<const h8_t*>(kt + ka + 16 * k);
-#pragma unroll
-  for (int k = 0; k < 36; ++k) {
-    if (k + D < 36) kf[k + D] = *reinterpret_cast<const h8_t*>(kt + ka + 16 * (k + D));
-    if (k < 32) s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[k], w.ql[k], s, 0, 0, 0);
-    else s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(b8_t, kf[k]), w.qr[k - 32], s, 0, 0, 0);
-  }
-  // keep D reads in flight: D reads, then (product, read) pairs, then D products
-  __builtin_amdgcn_sched_group_barrier(0x100, D, 0);
-#pragma unroll
-  for (int k = 0; k < 36 - D; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, D, 0);
+  for (int k = 0; k < D; ++k) read(k);
+  __builtin_amdgcn_sched_barrier(0);
+  for_each_index(std::make_integer_sequence<int, 36>{}, [&](auto K) {
+    constexpr int k = decltype(K)::value;
+    if constexpr (k + D < 36) read(k + D);
+    if constexpr (k == 0)
+      asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(s) : "v"(kf[0]), "v"(w.ql[0]));
+    else if constexpr (k < 32)
+      asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(s) : "v"(kf[k]), "v"(w.ql[k]));
+    else
+      asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(kf[k]), "v"(w.qr[k - 32]));
+    if constexpr (k % 3 == 1 && k / 3 < 9) dequant_unit<k / 3>(pk, kt_next, tid, sc);
+    // each load once the units before it have consumed its registers
+    if constexpr (k == 12) refill(pk, std::integral_constant<int, 0>{});
+    if constexpr (k == 14) refill(pk, std::integral_constant<int, 1>{});
+    if constexpr (k == 24) refill(pk, std::integral_constant<int, 2>{});
+    if constexpr (k == 27) refill(pk, std::integral_constant<int, 3>{});
+    if constexpr (k == 29) refill(pk, std::integral_constant<int, 4>{});
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  // the logits are read by vector instructions next: the last product's result
+  // needs its wait states (the assembler statements are opaque to the compiler)
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+  __builtin_amdgcn_sched_barrier(0);
   return s;
 }
 
-// O += P V for tile kt: product (n, c) takes channels 32 n + [0, 32) over tokens
-// 16 c + [0, 16); its B operand is two transposing reads of four tokens each,
-// issued E products ahead.
-template <int E>
-__device__ __forceinline__ void pv_product(LatentWave& w, const h8_t (&pf)[2], const uint16_t* kt, int vb) {
+// Softmax of one tile's logits s (this lane: head col, tokens 16 (i / 8) +
+// 8 half + i % 8; masked tokens hold -inf), spread over the 32 groups of a
+// product phase: group g runs softmax_part<g>.  Makes the tile's probabilities
+// (fp16, the A operand of the two PV products of the tile), adds their sum to
+// l_run and leaves in alpha the factor the accumulators must be scaled by
+// before the tile's products (1 unless the reference max moved).
+struct SoftmaxState {
+  float mx;      // running max of the raw logits, then the tile max (log2 units)
+  float m_use;   // the reference max the exponents subtract
+  float psum;
+  float alpha;
+};
+
+template <int G>
+__device__ __forceinline__ void softmax_part(LatentWave& w, SoftmaxState& st, const f16v_t& s, float c,
+                                             h8_t (&pn)[2]) {
+  // groups 2..5: the max of the 16 raw logits (c > 0 keeps the order)
+  if constexpr (G == 2) st.mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  if constexpr (G >= 3 && G <= 5) {
+    constexpr int i = 4 * (G - 2);
+    st.mx = fmaxf(fmaxf(st.mx, s[i]), fmaxf(s[i + 1], fmaxf(s[i + 2], s[i + 3])));
+  }
+  if constexpr (G == 6) {
+    const float tmax = max_xor32(st.mx) * c;
+    const bool bump = tmax > w.m_run + 8.f;
+    const float m_new = bump ? tmax : w.m_run;
+    st.alpha = bump ? __builtin_amdgcn_exp2f(w.m_run - m_new) : 1.f;
+    w.m_run = m_new;
+    st.m_use = m_new == -INFINITY ? 0.f : m_new;  // a head with no token yet: every p is 0
+    st.psum = 0.f;
+  }
+  if constexpr (G >= 7 && G < 15) {  // two logits per group
+    constexpr int i = 2 * (G - 7);
+    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -st.m_use));
+    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i + 1], c, -st.m_use));
+    st.psum += p0 + p1;
+    const h2_t pp = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(p0, p1));
+    pn[i >> 3][i & 7] = pp[0];
+    pn[i >> 3][(i & 7) + 1] = pp[1];
+  }
+  if constexpr (G == 15) w.l_run = w.l_run * st.alpha + st.psum;
+}
+
+// Phase 2 of a tile: O += P V for the previous tile (if PV; its probabilities
+// pf, its fp16 copy kt): product (n, c) takes channels 32 n + [0, 32) over
+// tokens 16 c + [0, 16), its B operand two transposing reads of four tokens
+// each, issued E products ahead; with the softmax of this tile's logits s (if
+// SM).  Returns the factor the accumulators must be scaled by before this
+// tile's products.
+template <bool PV, bool SM, int E>
+__device__ __forceinline__ float pv_phase(LatentWave& w, const h8_t (&pf)[2], const uint16_t* kt, int vb,
+                                          const f16v_t& s, float c, h8_t (&pn)[2]) {
   constexpr int kH2 = 8 * kKtStride;  // h2 = 1: token + 4 -> row + 8
   constexpr int kC = 16 * kKtStride;  // c = 1: token + 16 -> row + 16
   s4_t vf[32][2];
+  SoftmaxState st;
   auto vread = [&](int j) {
-    const int n = j >> 1, c = j & 1;
-    vf[j][0] = read_tr16(kt + vb + c * kC + 32 * n);
-    vf[j][1] = read_tr16(kt + vb + c * kC + kH2 + 32 * n);
+    const int n = j >> 1, cc = j & 1;
+    vf[j][0] = read_tr16(kt + vb + cc * kC + 32 * n);
+    vf[j][1] = read_tr16(kt + vb + cc * kC + kH2 + 32 * n);
   };
+  if constexpr (PV) {
 #pragma unroll
-  for (int j = 0; j < E; ++j) vread(j);
-#pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    if (j + E < 32) vread(j + E);
-    const h8_t v = __builtin_bit_cast(h8_t, __builtin_shufflevector(vf[j][0], vf[j][1], 0, 1, 2, 3, 4, 5, 6, 7));
-    w.o[j >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pf[j & 1], v, w.o[j >> 1], 0, 0, 0);
+    for (int j = 0; j < E; ++j) vread(j);
   }
-  // keep 2 E reads in flight: 2 E reads, then (product, 2 reads), then E products
-  __builtin_amdgcn_sched_group_barrier(0x100, 2 * E, 1);
-#pragma unroll
-  for (int j = 0; j < 32 - E; ++j) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, E, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  for_each_index(std::make_integer_sequence<int, 32>{}, [&](auto J) {
+    constexpr int j = decltype(J)::value;
+    if constexpr (PV) {
+      if constexpr (j + E < 32) vread(j + E);
+      const h8_t v = __builtin_bit_cast(h8_t, __builtin_shufflevector(vf[j][0], vf[j][1], 0, 1, 2, 3, 4, 5, 6, 7));
+      w.o[j >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pf[j & 1], v, w.o[j >> 1], 0, 0, 0);
+    }
+    if constexpr (SM) softmax_part<j>(w, st, s, c, pn);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  return SM ? st.alpha : 1.f;
 }
 
-// Online softmax of one tile's logits s (this lane: head col, tokens
-// 16 (i / 8) + 8 half + i % 8; tile tokens from tt, those below t_end and, when
-// sparse, with their bit set in `valid`): the tile's probabilities as the A
-// operand of the two PV products, the running sum updated, and the factor the
-// accumulators must be scaled by before this tile's products (1 unless the
-// reference max moved).  The reference max moves only when the tile max passes
-// it by more than 2^8.
-__device__ __forceinline__ float softmax_tile(LatentWave& w, f16v_t s, int half, int tt, int t_end, uint32_t valid,
-                                              float scale_log2, h8_t (&pf)[2]) {
-  float tmax = -INFINITY;
-  if (tt + kTile <= t_end && valid == 0xFFFFFFFFu) {  // a whole tile: nothing to mask
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s[i] = s[i] * scale_log2;
-      tmax = fmaxf(tmax, s[i]);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int j = 16 * (i >> 3) + 8 * half + (i & 7);
-      s[i] = tt + j < t_end && ((valid >> j) & 1u) ? s[i] * scale_log2 : -INFINITY;
-      tmax = fmaxf(tmax, s[i]);
-    }
-  }
-  tmax = max_xor32(tmax);
-  const bool bump = tmax > w.m_run + 8.f;
-  const float m_new = bump ? tmax : w.m_run;
-  const float alpha = bump ? __builtin_amdgcn_exp2f(w.m_run - m_new) : 1.f;
-  float psum = 0.f;
+// The logits of tile tokens not below t_end or (sparse) without their bit in
+// `valid` become -inf (this lane: tokens 16 (i / 8) + 8 half + i % 8).
+__device__ __forceinline__ void mask_tile(f16v_t& s, int half, int tt, int t_end, uint32_t valid) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const float p = __builtin_amdgcn_exp2f(s[i] - m_new);
-    psum += p;
-    pf[i >> 3][i & 7] = (_Float16)p;
+    const int j = 16 * (i >> 3) + 8 * half + (i & 7);
+    if (!(tt + j < t_end && ((valid >> j) & 1u))) s[i] = -INFINITY;
   }
-  w.l_run = w.l_run * alpha + psum;
-  w.m_run = m_new;
-  return alpha;
 }
 
 // O *= alpha per head (output rows are heads i % 4 + 8 (i / 4) + 4 half; head
-// r's alpha is in lane r), when any head's reference max moved.
+// r's alpha is in lane r), when any head's reference max moved.  The reads
+// start at least 48 wait states after the last product that wrote them (more
+// than a 32x32x16 product's latency).
 __device__ __forceinline__ void rescale(LatentWave& w, float alpha, int half) {
   if (__ballot(alpha != 1.f)) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float ar = __shfl(alpha, (i & 3) + 8 * (i >> 2) + 4 * half);
@@ -329,23 +394,38 @@ decode_latent_kernel(MfmaDecodeArgs a) {
                rsrc(a.rope + row0 * 64, (size_t)nrows * 128)};
   };
   const Res res = res_at((size_t)b * a.cap, a.cap);
-  // the loads of tile index ti (tokens t_begin + 32 ti + [0, 32)); a missing
-  // tile or token reads past the end of its resources: zeros
-  auto load_at = [&](Packed& p, int ti) {
+  // where tile index ti (tokens t_begin + 32 ti + [0, 32)) is read from: its
+  // resources and first token offset (sparse: its first slot); a missing tile
+  // or token reads past the end of its resources: zeros
+  struct TileSrc {
+    Res res;
+    int t0;
+  };
+  auto tile_src = [&](int ti) -> TileSrc {
     const int t = t_begin + ti * kTile;
     if constexpr (SPARSE) {
-      const int rel = t < t_end ? t - t_begin : -1;
-      load_tile(p, tid, res, [&](int k) { return rel < 0 ? -1 : spos[rel + k]; });
+      return TileSrc{res, t < t_end ? t - t_begin : -1};
     } else if constexpr (!PAGED) {
-      const int t0 = t < t_end ? t : a.cap;
-      load_tile(p, tid, res, [&](int k) { return t0 + k; });
+      return TileSrc{res, t < t_end ? t : a.cap};
     } else {
       const int pg = t < t_end ? page_of_uniform(a.pm, b, t) : -1;
-      const int t0 = pg < 0 ? 0 : t & (a.pm.tokens - 1);
-      load_tile(p, tid, res_at((size_t)(pg < 0 ? 0 : pg) * a.pm.tokens, pg < 0 ? 0 : a.pm.tokens),
-                [&](int k) { return t0 + k; });
+      return TileSrc{res_at((size_t)(pg < 0 ? 0 : pg) * a.pm.tokens, pg < 0 ? 0 : a.pm.tokens),
+                     pg < 0 ? 0 : t & (a.pm.tokens - 1)};
     }
   };
+  // load P of the tile src names
+  auto load_from = [&](Packed& p, const TileSrc& src, auto P) {
+    constexpr int part = decltype(P)::value;
+    if constexpr (SPARSE)
+      load_part<part>(p, tid, src.res, [&](int k) { return src.t0 < 0 ? -1 : spos[src.t0 + k]; });
+    else
+      load_part<part>(p, tid, src.res, [&](int k) { return src.t0 + k; });
+  };
+  auto load_at = [&](Packed& p, int ti) {
+    const TileSrc src = tile_src(ti);
+    for_each_index(std::make_integer_sequence<int, 5>{}, [&](auto P) { load_from(p, src, P); });
+  };
+  auto refill_from = [&](const TileSrc& src) { return [&, src](Packed& p, auto P) { load_from(p, src, P); }; };
   Packed pk;  // this thread's share of the next tile to dequantise
   load_at(pk, 0);
 
@@ -381,28 +461,42 @@ decode_latent_kernel(MfmaDecodeArgs a) {
   int vb = kt_phys(8 * half + (jj >> 2)) * kKtStride + 16 * (gg & 1) + 4 * (jj & 3);
   asm volatile("" : "+v"(ka), "+v"(vb));
 
-  // prologue: tile 0 into Kt[0], the registers refilled with tile 1
+  // Tile i: its dequantised copy Kt[i % 3], written during tile i - 1.  Before
+  // the products of tile i every wave has finished tile i - 1, whose phase 2
+  // read Kt[(i - 2) % 3], the buffer tile i + 1 takes.
+  const float c = a.scale_log2;
+  h8_t pf[2];           // probabilities of the previous tile
+  float alpha = 1.f;    // the accumulators' pending factor
   if (ntiles > 0) {
     dequant_tile(pk, Kt[0], tid);
     load_at(pk, 1);
-  }
-  // Tile i: its dequantised copy Kt[i % 3].  After the products of tile i the
-  // wave dequantises tile i + 1 from the registers and refills them with tile
-  // i + 2; three buffers let a wave dequantise tile i + 1 while slower waves
-  // still read tile i.
-  for (int i = 0; i < ntiles; ++i) {
-    // every wave's share of tile i is in Kt[i % 3], and every wave is done with
-    // tile i - 2 (whose buffer tile i + 1 takes)
     __syncthreads();
-    const uint16_t* kt = Kt[i % kBufs];
-    const f16v_t s = qk_product<4>(w, kt, ka);
-    dequant_tile(pk, Kt[(i + 1) % kBufs], tid);
-    load_at(pk, i + 2);
-    h8_t pf[2];
-    const float alpha = softmax_tile(w, s, half, t_begin + i * kTile, t_end, SPARSE ? svalid[i] : 0xFFFFFFFFu,
-                                     a.scale_log2, pf);
+    f16v_t s = qk_phase<3>(w, Kt[0], ka, pk, Kt[1], tid, refill_from(tile_src(2)));
+    if (kTile > t_end - t_begin || (SPARSE && svalid[0] != 0xFFFFFFFFu))
+      mask_tile(s, half, t_begin, t_end, SPARSE ? svalid[0] : 0xFFFFFFFFu);
+    alpha = pv_phase<false, true, 3>(w, pf, Kt[0], vb, s, c, pf);
+  }
+  int cur = 1;  // buffer of tile i
+  for (int i = 1; i < ntiles; ++i) {
+    __syncthreads();
+    const int prv = cur == 0 ? kBufs - 1 : cur - 1, nxt = cur == kBufs - 1 ? 0 : cur + 1;
+    const int tt = t_begin + i * kTile;
+    const TileSrc src = tile_src(i + 2);
+    f16v_t s = qk_phase<3>(w, Kt[cur], ka, pk, Kt[nxt], tid, refill_from(src));
     rescale(w, alpha, half);
-    pv_product<6>(w, pf, kt, vb);
+    if (tt + kTile > t_end || (SPARSE && svalid[i] != 0xFFFFFFFFu))
+      mask_tile(s, half, tt, t_end, SPARSE ? svalid[i] : 0xFFFFFFFFu);
+    h8_t pn[2];
+    alpha = pv_phase<true, true, 3>(w, pf, Kt[prv], vb, s, c, pn);
+    pf[0] = pn[0];
+    pf[1] = pn[1];
+    cur = nxt;
+  }
+  if (ntiles > 0) {  // the last tile's products
+    rescale(w, alpha, half);
+    const int prv = cur == 0 ? kBufs - 1 : cur - 1;
+    h8_t unused[2];
+    pv_phase<true, false, 3>(w, pf, Kt[prv], vb, f16v_t{}, c, unused);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the refills past the last tile have returned
 
