@@ -151,25 +151,42 @@ __device__ __forceinline__ void load_part(Packed& p, int tid, const Res& res, To
 
 // Dequantisation of this thread's share of a tile into the token-major fp16
 // tile kt, in nine units: unit u < 8 is octet u % 4 (8 channels) of code chunk
-// u / 4, unit 8 the RoPE chunk.  sc holds the chunks' two scales as fp16 pairs,
-// set by each chunk's first unit.
-template <int U>
-__device__ __forceinline__ void dequant_unit(const Packed& p, uint16_t* kt, int tid, h2_t (&sc)[2][2]) {
+// u / 4, unit 8 the RoPE chunk.  A unit runs in three stages (convert, scale,
+// store), each in a later group than the one before it, so that no stage waits
+// on a result of its own group; stage 0 of a chunk's first unit also makes the
+// chunk's two scales into fp16 pairs.
+struct DequantState {
+  h2_t sc[2][2];   // the chunks' scales as fp16 pairs
+  h2_t v[9][4];    // unit values: converted, then scaled
+};
+
+template <int U, int STAGE>
+__device__ __forceinline__ void dequant_stage(const Packed& p, uint16_t* kt, int tid, DequantState& d) {
   if constexpr (U == 8) {
-    *reinterpret_cast<v4i_t*>(kt + kt_phys(tid >> 3) * kKtStride + kLat + 8 * (tid & 7)) = p.r;
+    if constexpr (STAGE == 2)
+      *reinterpret_cast<v4i_t*>(kt + kt_phys(tid >> 3) * kKtStride + kLat + 8 * (tid & 7)) = p.r;
   } else {
     constexpr int j = U / 4, q = U % 4;  // octet q: channels 32 cc + 8 q + [0, 8), scale group 2 cc + q / 2
-    const int t = chunk_token(tid, j), cc = tid >> 4;
-    if constexpr (q == 0) {
-      const uint32_t sw = (uint32_t)p.s[j];
-      sc[j][0] = splat_bf16(sw & 0xFFFFu);
-      sc[j][1] = splat_bf16(sw >> 16);
+    if constexpr (STAGE == 0) {
+      if constexpr (q == 0) {
+        const uint32_t sw = (uint32_t)p.s[j];
+        d.sc[j][0] = splat_bf16(sw & 0xFFFFu);
+        d.sc[j][1] = splat_bf16(sw >> 16);
+      }
+      const uint32_t w = (uint32_t)p.c[j][q];
+      d.v[U][0] = fp4x2<0>(w);
+      d.v[U][1] = fp4x2<1>(w);
+      d.v[U][2] = fp4x2<2>(w);
+      d.v[U][3] = fp4x2<3>(w);
+    } else if constexpr (STAGE == 1) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d.v[U][e] = d.v[U][e] * d.sc[j][q >> 1];
+    } else {
+      const int t = chunk_token(tid, j), cc = tid >> 4;
+      *reinterpret_cast<uint4*>(kt + kt_phys(t) * kKtStride + 32 * cc + 8 * q) =
+          uint4{__builtin_bit_cast(uint32_t, d.v[U][0]), __builtin_bit_cast(uint32_t, d.v[U][1]),
+                __builtin_bit_cast(uint32_t, d.v[U][2]), __builtin_bit_cast(uint32_t, d.v[U][3])};
     }
-    const uint32_t w = (uint32_t)p.c[j][q];
-    const h2_t s = sc[j][q >> 1];
-    *reinterpret_cast<uint4*>(kt + kt_phys(t) * kKtStride + 32 * cc + 8 * q) =
-        uint4{__builtin_bit_cast(uint32_t, fp4x2<0>(w) * s), __builtin_bit_cast(uint32_t, fp4x2<1>(w) * s),
-              __builtin_bit_cast(uint32_t, fp4x2<2>(w) * s), __builtin_bit_cast(uint32_t, fp4x2<3>(w) * s)};
   }
 }
 
@@ -181,8 +198,13 @@ __device__ __forceinline__ void for_each_index(std::integer_sequence<int, K...>,
 
 // The whole dequantisation of this thread's share, unscheduled (first tile).
 __device__ __forceinline__ void dequant_tile(const Packed& p, uint16_t* kt, int tid) {
-  h2_t sc[2][2];
-  for_each_index(std::make_integer_sequence<int, 9>{}, [&](auto U) { dequant_unit<decltype(U)::value>(p, kt, tid, sc); });
+  DequantState d;
+  for_each_index(std::make_integer_sequence<int, 9>{}, [&](auto U) {
+    constexpr int u = decltype(U)::value;
+    dequant_stage<u, 0>(p, kt, tid, d);
+    dequant_stage<u, 1>(p, kt, tid, d);
+    dequant_stage<u, 2>(p, kt, tid, d);
+  });
 }
 
 // Per-wave state that lives across tiles.
@@ -197,14 +219,15 @@ struct LatentWave {
 // Phase 1 of a tile: S^T = K Q^T for this wave's 32 heads on tile kt (one
 // accumulation chain in VGPRs, so that the output accumulators keep every
 // AGPR; operand reads D products ahead), with this thread's
-// dequantisation of the next tile into kt_next (unit u behind product 3 u + 1)
+// dequantisation of the next tile into kt_next (unit u behind products 3 u + 1
+// to 3 u + 3)
 // and, each once its registers are free, the five loads of the tile after it
 // (refill(pk, P) issues load P).
 template <int D, class Refill>
 __device__ __forceinline__ f16v_t qk_phase(const LatentWave& w, const uint16_t* kt, int ka, Packed& pk,
                                            uint16_t* kt_next, int tid, Refill refill) {
   h8_t kf[36];
-  h2_t sc[2][2];
+  DequantState dq;
   f16v_t s = f16v_t{};
   auto read = [&](int k) { kf[k] = *reinterpret_cast<const h8_t*>(kt + ka + 16 * k); };
 #pragma unroll
@@ -219,7 +242,8 @@ __device__ __forceinline__ f16v_t qk_phase(const LatentWave& w, const uint16_t* 
       asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(s) : "v"(kf[k]), "v"(w.ql[k]));
     else
       asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(kf[k]), "v"(w.qr[k - 32]));
-    if constexpr (k % 3 == 1 && k / 3 < 9) dequant_unit<k / 3>(pk, kt_next, tid, sc);
+    // unit u: convert behind product 3 u + 1, scale behind 3 u + 2, store behind 3 u + 3
+    if constexpr (k >= 1 && (k - 1) / 3 < 9) dequant_stage<(k - 1) / 3, (k - 1) % 3>(pk, kt_next, tid, dq);
     // each load once the units before it have consumed its registers
     if constexpr (k == 12) refill(pk, std::integral_constant<int, 0>{});
     if constexpr (k == 14) refill(pk, std::integral_constant<int, 1>{});
@@ -235,47 +259,78 @@ __device__ __forceinline__ f16v_t qk_phase(const LatentWave& w, const uint16_t* 
   return s;
 }
 
+// max of three floats (the logits come from matrix products written in
+// assembler statements, so the compiler cannot prove them canonical and would
+// add a canonicalising max per operand to fmaxf)
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // Softmax of one tile's logits s (this lane: head col, tokens 16 (i / 8) +
 // 8 half + i % 8; masked tokens hold -inf), spread over the 32 groups of a
 // product phase: group g runs softmax_part<g>.  Makes the tile's probabilities
 // (fp16, the A operand of the two PV products of the tile), adds their sum to
 // l_run and leaves in alpha the factor the accumulators must be scaled by
-// before the tile's products (1 unless the reference max moved).
+// before the tile's products (1 unless the reference max moved).  A wave
+// issues in order, so each group's vector work depends only on results of
+// earlier groups: the max is a tree over groups 2..8, and logit pair m is
+// scaled in group 12 + m, exponentiated in 13 + m and packed and summed in
+// 14 + m.
 struct SoftmaxState {
-  float mx;      // running max of the raw logits, then the tile max (log2 units)
-  float m_use;   // the reference max the exponents subtract
-  float psum;
-  float alpha;
+  float mx[7];      // partial maxima of the raw logits
+  float sw[2];      // the two halves' maxima after the lane-pair swap
+  float tmax, m_new, arg, m_use, alpha, psum;
+  bool bump;
+  float x[8][2], p[8][2];
 };
 
 template <int G>
 __device__ __forceinline__ void softmax_part(LatentWave& w, SoftmaxState& st, const f16v_t& s, float c,
                                              h8_t (&pn)[2]) {
-  // groups 2..5: the max of the 16 raw logits (c > 0 keeps the order)
-  if constexpr (G == 2) st.mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-  if constexpr (G >= 3 && G <= 5) {
-    constexpr int i = 4 * (G - 2);
-    st.mx = fmaxf(fmaxf(st.mx, s[i]), fmaxf(s[i + 1], fmaxf(s[i + 2], s[i + 3])));
+  // the max of the 16 raw logits (c > 0 keeps the order), then of the lane pair
+  if constexpr (G == 2) { st.mx[0] = max3(s[0], s[1], s[2]); st.mx[1] = max3(s[3], s[4], s[5]); }
+  if constexpr (G == 3) { st.mx[2] = max3(s[6], s[7], s[8]); st.mx[3] = max3(s[9], s[10], s[11]); }
+  if constexpr (G == 4) { st.mx[4] = max3(s[12], s[13], s[14]); st.mx[5] = max3(st.mx[0], st.mx[1], s[15]); }
+  if constexpr (G == 5) st.mx[6] = max3(st.mx[2], st.mx[3], st.mx[4]);
+  if constexpr (G == 6) st.mx[0] = fmaxf(st.mx[5], st.mx[6]);
+  if constexpr (G == 7) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.mx[0]), __float_as_uint(st.mx[0]), false, false);
+    st.sw[0] = __uint_as_float(r[0]);
+    st.sw[1] = __uint_as_float(r[1]);
   }
-  if constexpr (G == 6) {
-    const float tmax = max_xor32(st.mx) * c;
-    const bool bump = tmax > w.m_run + 8.f;
-    const float m_new = bump ? tmax : w.m_run;
-    st.alpha = bump ? __builtin_amdgcn_exp2f(w.m_run - m_new) : 1.f;
-    w.m_run = m_new;
-    st.m_use = m_new == -INFINITY ? 0.f : m_new;  // a head with no token yet: every p is 0
-    st.psum = 0.f;
+  if constexpr (G == 8) st.tmax = fmaxf(st.sw[0], st.sw[1]) * c;
+  if constexpr (G == 9) {
+    st.bump = st.tmax > w.m_run + 8.f;
+    st.m_new = st.bump ? st.tmax : w.m_run;
   }
-  if constexpr (G >= 7 && G < 15) {  // two logits per group
-    constexpr int i = 2 * (G - 7);
-    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -st.m_use));
-    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i + 1], c, -st.m_use));
-    st.psum += p0 + p1;
-    const h2_t pp = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(p0, p1));
+  if constexpr (G == 10) {
+    st.arg = w.m_run - st.m_new;
+    st.m_use = st.m_new == -INFINITY ? 0.f : st.m_new;  // a head with no token yet: every p is 0
+    w.m_run = st.m_new;
+  }
+  if constexpr (G == 11) st.alpha = __builtin_amdgcn_exp2f(st.arg);
+  if constexpr (G >= 12 && G < 20) {
+    constexpr int m = G - 12;
+    st.x[m][0] = __builtin_fmaf(s[2 * m], c, -st.m_use);
+    st.x[m][1] = __builtin_fmaf(s[2 * m + 1], c, -st.m_use);
+  }
+  if constexpr (G >= 13 && G < 21) {
+    constexpr int m = G - 13;
+    st.p[m][0] = __builtin_amdgcn_exp2f(st.x[m][0]);
+    st.p[m][1] = __builtin_amdgcn_exp2f(st.x[m][1]);
+  }
+  if constexpr (G == 13) st.alpha = st.bump ? st.alpha : 1.f;
+  if constexpr (G >= 14 && G < 22) {
+    constexpr int m = G - 14, i = 2 * m;
+    const float ps = st.p[m][0] + st.p[m][1];
+    st.psum = m == 0 ? ps : st.psum + ps;
+    const h2_t pp = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(st.p[m][0], st.p[m][1]));
     pn[i >> 3][i & 7] = pp[0];
     pn[i >> 3][(i & 7) + 1] = pp[1];
   }
-  if constexpr (G == 15) w.l_run = w.l_run * st.alpha + st.psum;
+  if constexpr (G == 22) w.l_run = w.l_run * st.alpha + st.psum;
 }
 
 // Phase 2 of a tile: O += P V for the previous tile (if PV; its probabilities
