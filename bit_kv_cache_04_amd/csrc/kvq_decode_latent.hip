@@ -56,17 +56,29 @@ constexpr int kTile = 32;
 constexpr int kLat = 512, kRope = 64;
 constexpr int kBufs = 3;  // dequantised tiles in LDS
 // Kt: 32 token rows of 576 halves (fp16 latent, then bf16 RoPE), row stride
-// 73 x 16 bytes.  Token t = 16 c + 8 h + 4 h2 + e (e < 4) lives in row
-// kt_phys(t) = 16 c + 8 h2 + 2 e + h, chosen so that both readers see distinct
-// bank groups: the QK operand (lanes of 8 read 8 rows differing in e and h) and
-// the transposing PV reads (4 rows differing in e, 32 bytes each).
+// 73 x 16 bytes, so that row r starts at bank word 36 r mod 64 (distinct
+// 16-byte bank groups for the 16 rows of a half).  Token t = 16 c + 8 h +
+// 4 h2 + e (e < 4) lives in row kt_phys(t) = 16 c + 4 e + 2 h + h2: the four
+// tokens e = 0..3 that a transposing PV read takes sit in rows whose starts
+// are 16 bank words apart, so the read's 32-byte pieces fill all 64 banks;
+// the key reads and the dequantised writes touch sixteen rows of one half at
+// a time, which any arrangement of the half keeps apart.
 constexpr int kKtStride = kLat + kRope + 8;
 constexpr int kKtHalves = kTile * kKtStride;
 constexpr int kRsrcFlags = 0x00020000;
 
-__host__ __device__ constexpr int kt_phys(int t) {
-  return (t & 16) | ((t & 4) << 1) | ((t & 3) << 1) | ((t >> 3) & 1);
+__host__ __device__ constexpr int kt_phys(int t) { return (t & 16) | ((t & 3) << 2) | ((t >> 2) & 3); }
+
+// rows between tokens t and t + 4 (h2), t and t + 16 (c)
+constexpr int kRowH2 = 1, kRowC = 16;
+__host__ __device__ constexpr bool kt_phys_steps_hold() {
+  for (int t = 0; t < 32; ++t) {
+    if (!(t & 4) && kt_phys(t + 4) != kt_phys(t) + kRowH2) return false;
+    if (t < 16 && kt_phys(t + 16) != kt_phys(t) + kRowC) return false;
+  }
+  return true;
 }
+static_assert(kt_phys_steps_hold(), "token row steps");
 
 // Row rho of the QK A operand holds token qk_token(rho) (bits 2 and 3 of rho
 // swapped): then the result rows a lane holds (i % 4 + 8 (i / 4) + 4 (lane / 32),
@@ -114,7 +126,7 @@ struct Res {
 
 // This thread's share of one packed tile: code chunks of 16 bytes (32 channels
 // of one token), their two bf16 scales (4 bytes), and one 16-byte chunk of the
-// RoPE rows (chunk r is token r / 8, channels 8 (r % 8) + [0, 8)).  Code chunk
+// RoPE rows (chunk r is token r % 32, channels 8 (r / 32) + [0, 8)).  Code chunk
 // j of thread tid is token chunk_token(tid, j), channels 32 (tid / 16) + [0, 32):
 // sixteen consecutive lanes take sixteen tokens, whose fp16 rows start in
 // distinct LDS banks, so that their dequantised writes do not conflict.
@@ -133,8 +145,8 @@ __device__ __forceinline__ int chunk_token(int tid, int j) { return 16 * j + (ti
 template <int P, class TokOf>
 __device__ __forceinline__ void load_part(Packed& p, int tid, const Res& res, TokOf tok) {
   if constexpr (P == 4) {
-    const int tr = tok(tid >> 3);
-    const uint32_t orp = tr < 0 ? 0xFFFFFFFFu : (uint32_t)tr * 128u + (tid & 7) * 16;
+    const int tr = tok(tid & 31);
+    const uint32_t orp = tr < 0 ? 0xFFFFFFFFu : (uint32_t)tr * 128u + (tid >> 5) * 16;
     p.r = __builtin_amdgcn_raw_buffer_load_b128(res.rope, orp, 0, 0);
   } else {
     constexpr int j = P / 2;
@@ -164,7 +176,7 @@ template <int U, int STAGE>
 __device__ __forceinline__ void dequant_stage(const Packed& p, uint16_t* kt, int tid, DequantState& d) {
   if constexpr (U == 8) {
     if constexpr (STAGE == 2)
-      *reinterpret_cast<v4i_t*>(kt + kt_phys(tid >> 3) * kKtStride + kLat + 8 * (tid & 7)) = p.r;
+      *reinterpret_cast<v4i_t*>(kt + kt_phys(tid & 31) * kKtStride + kLat + 8 * (tid >> 5)) = p.r;
   } else {
     constexpr int j = U / 4, q = U % 4;  // octet q: channels 32 cc + 8 q + [0, 8), scale group 2 cc + q / 2
     if constexpr (STAGE == 0) {
@@ -342,8 +354,8 @@ __device__ __forceinline__ void softmax_part(LatentWave& w, SoftmaxState& st, co
 template <bool PV, bool SM, int E>
 __device__ __forceinline__ float pv_phase(LatentWave& w, const h8_t (&pf)[2], const uint16_t* kt, int vb,
                                           const f16v_t& s, float c, h8_t (&pn)[2]) {
-  constexpr int kH2 = 8 * kKtStride;  // h2 = 1: token + 4 -> row + 8
-  constexpr int kC = 16 * kKtStride;  // c = 1: token + 16 -> row + 16
+  constexpr int kH2 = kRowH2 * kKtStride;  // h2 = 1: token + 4
+  constexpr int kC = kRowC * kKtStride;    // c = 1: token + 16
   s4_t vf[32][2];
   SoftmaxState st;
   auto vread = [&](int j) {
