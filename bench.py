@@ -263,6 +263,10 @@ def run_workload(name, args, dev, flush, cpu):
     from bit_kv_cache_04_amd.cache import PackedKVCache, make_constants
 
     cfg = synth.CONFIGS[name]
+    ov = {k: v for k, v in (("batch", args.batch), ("context", args.context), ("hq", args.q_heads),
+                            ("hkv", args.kv_heads), ("head_dim", args.head_dim)) if v}
+    if ov:  # a resized copy of the workload: its own name, so no committed counter summary applies
+        cfg = cfg.scaled(name=name + "@" + ",".join(f"{k}={v}" for k, v in ov.items()), **ov)
     consts = None
     if cfg.fmt in ("turbo", "qjl1"):
         consts = make_constants(cfg.fmt, cfg.head_dim,
@@ -472,6 +476,11 @@ def main():
     ap.add_argument("--config", default=None,
                     help="one workload; default: all five, with latent_b64_t64k as the headline")
     ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--batch", type=int, default=0, help="resize the workload: sequences")
+    ap.add_argument("--context", type=int, default=0, help="resize the workload: cached tokens per sequence")
+    ap.add_argument("--q-heads", type=int, default=0, help="resize the workload: query heads")
+    ap.add_argument("--kv-heads", type=int, default=0, help="resize the workload: KV heads")
+    ap.add_argument("--head-dim", type=int, default=0, help="resize the workload: head dimension")
     ap.add_argument("--sink", type=int, default=0, help="leading tokens kept bf16 (per-head formats)")
     ap.add_argument("--recent", type=int, default=0, help="trailing tokens kept bf16 (per-head formats)")
     ap.add_argument("--queries", type=int, default=1,

@@ -11,7 +11,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["kvq_host.cpp", "kvq_api.cpp", "kvq_append.hip", "kvq_decode.hip", "kvq_decode_mfma.hip", "kvq_decode_latent.hip", "kvq_decode_turbo.hip", "kvq_hsi.hip", "kvq_probe.hip", "kvq_static.hip"]
+SOURCES = ["kvq_host.cpp", "kvq_api.cpp", "kvq_append.hip", "kvq_decode.hip", "kvq_decode_mfma.hip", "kvq_decode_latent.hip", "kvq_decode_turbo.hip", "kvq_decode_kivi.hip", "kvq_hsi.hip", "kvq_probe.hip", "kvq_static.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -75,11 +75,12 @@ extern "C" int kv_decode_attention(const kv_cache* c, const void* q, int32_t q_d
   // mixed precision: the splits cover the packed tokens from sink_tokens on, and
   // the bf16 window adds one split of partial rows
   const int packed_len = std::max(1, max_seq_len - (L.sink_tokens & ~31));  // matrix-core tiles start 32-aligned
-  // the window's splits and the packed ones share the merge's kMaxPartSplits
-  if (window_chunks(L) >= kMaxPartSplits) return KV_EUNSUPPORTED;
-  const SplitPlan plan = plan_splits(&L, num_q_heads, nq, q_dtype, packed_len, req, fp32,
-                                     kMaxPartSplits - window_chunks(L));
-  const int part_splits = plan.splits + window_chunks(L);
+  // the window's and the KIVI-2 staging tail's splits and the packed ones share
+  // the merge's kMaxPartSplits
+  const int extra = window_chunks(L) + tail_chunks(L);
+  if (extra >= kMaxPartSplits) return KV_EUNSUPPORTED;
+  const SplitPlan plan = plan_splits(&L, num_q_heads, nq, q_dtype, packed_len, req, fp32, kMaxPartSplits - extra);
+  const int part_splits = plan.splits + extra;
   const DecodeWorkspace wsl = decode_workspace(&L, nq * num_q_heads, part_splits);
   if (!ws) {
     if (!ws_bytes) return KV_EINVAL;

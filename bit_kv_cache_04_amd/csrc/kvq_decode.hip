@@ -51,6 +51,10 @@ struct DecodeArgs {
   float* part;       // [B][nq][Hq][part_splits][DV + 2]: m (log2 units), l, o[DV]
   int splits, per_split;
   int t_lo, recent, part_splits;  // packed tokens [t_lo, L - recent), split s from t_lo + s * per_split
+  // KIVI2 dense decode: the splits stop at the first staged token; tail_split
+  // >= 0 runs one workgroup per (KV head, head block, sequence) over the staged
+  // tokens instead, writing partial split tail_split
+  int tail_split;
 };
 
 // ---------------------------------------------------------------- per-format element access
@@ -131,10 +135,13 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
   const int nh = min(a.hb_size, a.G - vh0);
   const size_t bh = (size_t)b * a.H + h;
   const int L = min(min(a.seq_lens[b], a.max_len), a.cap);
-  const int t_begin = a.t_lo + split * a.per_split;
-  const int t_end = min(max(a.t_lo, L - a.recent), t_begin + a.per_split);
   // KIVI2: keys from the first token of the appended sequence's incomplete group on are staged
   const int kstage = FMT == KV_FMT_KIVI2 ? reinterpret_cast<const int*>(a.k_stage)[bh * (4 + 32 * a.d)] & ~31 : a.cap;
+  const bool tail = FMT == KV_FMT_KIVI2 && a.tail_split >= 0;
+  const int t_begin = tail ? max(a.t_lo, kstage) : a.t_lo + split * a.per_split;
+  int t_end = tail ? max(a.t_lo, L - a.recent) : min(max(a.t_lo, L - a.recent), t_begin + a.per_split);
+  if (FMT == KV_FMT_KIVI2 && !a.sel && !tail) t_end = min(t_end, kstage);  // the staged tokens: the tail split
+  const int out_split = tail ? a.tail_split : split;
   // query / output row of block row hh; query j sees the first L - (nq - 1 - j) tokens
   auto qrow = [&](int hh) {
     const int vh = vh0 + hh;
@@ -223,7 +230,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
     if (e < HB * DV) {
       const int hh = e / DV, c = e % DV;
       if (hh < nh) {
-        float* p = a.part + (qrow(hh) * a.part_splits + split) * (DV + 2);
+        float* p = a.part + (qrow(hh) * a.part_splits + out_split) * (DV + 2);
         p[2 + c] = o[j];
         if (c == 0) {
           p[0] = ms[hh];
@@ -779,6 +786,62 @@ void launch_window(const kv_cache* c, const void* q, int q_dtype, int num_q_head
 
 }  // namespace
 
+// Arguments of the general kernel (and of the KIVI2 staging tail).
+static DecodeArgs general_args(const kv_cache* c, int num_q_heads, int nq, const int32_t* seq_lens, int max_seq_len,
+                               float scale, const float* qv, float* part, const SplitPlan& plan, int part_splits,
+                               const int32_t* sel, int sel_stride) {
+  const kv_layout& L = c->layout;
+  DecodeArgs a{};
+  a.k_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_K_CODES]);
+  a.k_scale = c->buf[KV_BUF_K_SCALE];
+  a.k_zero = static_cast<const float*>(c->buf[KV_BUF_K_ZERO]);
+  a.k_stage = static_cast<const float*>(c->buf[KV_BUF_K_STAGE]);
+  a.k_sketch = static_cast<const uint8_t*>(c->buf[KV_BUF_K_SKETCH]);
+  a.k_norm = static_cast<const uint16_t*>(c->buf[KV_BUF_K_NORM]);
+  a.k_rnorm = static_cast<const uint16_t*>(c->buf[KV_BUF_K_RNORM]);
+  a.v_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_V_CODES]);
+  a.v_scale = c->buf[KV_BUF_V_SCALE];
+  a.v_zero = static_cast<const float*>(c->buf[KV_BUF_V_ZERO]);
+  a.v_norm = static_cast<const uint16_t*>(c->buf[KV_BUF_V_NORM]);
+  a.rope = static_cast<const uint16_t*>(c->buf[KV_BUF_ROPE]);
+  a.levels = c->lm_levels;
+  a.H = L.num_kv_heads;
+  a.cap = L.capacity;
+  a.d = L.head_dim;
+  a.rope_dim = L.rope_dim;
+  a.pm = page_map(c);
+  a.sel = sel;
+  a.sel_stride = sel_stride;
+  a.qv = qv;
+  a.Hq = num_q_heads;
+  a.nq = nq;
+  a.Gr = num_q_heads / L.num_kv_heads;
+  a.G = nq * a.Gr;  // rows per (sequence, KV head): query j, head g is row j * Gr + g
+  a.hb_size = std::min(a.G, 16);
+  a.head_blocks = (a.G + a.hb_size - 1) / a.hb_size;
+  a.seq_lens = seq_lens;
+  a.max_len = max_seq_len;
+  a.scale_log2 = scale * kLog2e;
+  a.kappa = (float)(1.2533141373155002512 / (double)(L.qjl_m > 0 ? L.qjl_m : 1));
+  a.part = part;
+  a.splits = plan.splits;
+  a.per_split = plan.tokens_per_split;
+  a.t_lo = L.sink_tokens;
+  a.recent = L.recent_tokens;
+  a.part_splits = part_splits;
+  a.tail_split = -1;
+  return a;
+}
+
+// KIVI2 dense decode: the staged tokens of every (sequence, KV head) as partial
+// split `split` (one workgroup per (KV head, head block, sequence)).
+static void launch_kivi_tail(DecodeArgs a, int split, int B, hipStream_t st) {
+  a.tail_split = split;
+  const dim3 grid(1, a.H * a.head_blocks, B);
+  if (a.d == 64) decode_split_kernel<KV_FMT_KIVI2, 64, 64, 32, 16><<<grid, 256, 0, st>>>(a);
+  else decode_split_kernel<KV_FMT_KIVI2, 128, 128, 32, 16><<<grid, 256, 0, st>>>(a);
+}
+
 int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads, int nq, const int32_t* seq_lens,
                   int max_seq_len, float scale, float* out, void* ws, const SplitPlan& plan,
                   const DecodeWorkspace& wsl, void* ev_begin, void* ev_end, void* stream, const int32_t* sel,
@@ -793,7 +856,9 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
   // mixed precision: the packed kernels take [sink, L - recent) and the bf16
   // window kernel one more split
   const bool windowed = L.sink_tokens || L.recent_tokens;
-  const int part_splits = plan.splits + window_chunks(L);
+  // KIVI2 dense decode: the staged tokens take the split after the window's
+  const int tail_split = sel || !tail_chunks(L) ? -1 : plan.splits + window_chunks(L);
+  const int part_splits = plan.splits + window_chunks(L) + (tail_split >= 0 ? 1 : 0);
   const int qw_in = query_width(&L), qw_out = prepared_query_width(&L);
   // fp32: every format on the general kernel (exact for any magnitude)
   if (!fp32 && (sel ? latent_sparse_ok(L, num_q_heads, q_dtype) : latent_fast_path_ok(L, num_q_heads, nq, q_dtype))) {
@@ -932,44 +997,43 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
   }
 
-  DecodeArgs a{};
-  a.k_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_K_CODES]);
-  a.k_scale = c->buf[KV_BUF_K_SCALE];
-  a.k_zero = static_cast<const float*>(c->buf[KV_BUF_K_ZERO]);
-  a.k_stage = static_cast<const float*>(c->buf[KV_BUF_K_STAGE]);
-  a.k_sketch = static_cast<const uint8_t*>(c->buf[KV_BUF_K_SKETCH]);
-  a.k_norm = static_cast<const uint16_t*>(c->buf[KV_BUF_K_NORM]);
-  a.k_rnorm = static_cast<const uint16_t*>(c->buf[KV_BUF_K_RNORM]);
-  a.v_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_V_CODES]);
-  a.v_scale = c->buf[KV_BUF_V_SCALE];
-  a.v_zero = static_cast<const float*>(c->buf[KV_BUF_V_ZERO]);
-  a.v_norm = static_cast<const uint16_t*>(c->buf[KV_BUF_V_NORM]);
-  a.rope = static_cast<const uint16_t*>(c->buf[KV_BUF_ROPE]);
-  a.levels = c->lm_levels;
-  a.H = L.num_kv_heads;
-  a.cap = L.capacity;
-  a.d = L.head_dim;
-  a.rope_dim = L.rope_dim;
-  a.pm = page_map(c);
-  a.sel = sel;
-  a.sel_stride = sel_stride;
-  a.qv = qv;
-  a.Hq = num_q_heads;
-  a.nq = nq;
-  a.Gr = num_q_heads / L.num_kv_heads;
-  a.G = nq * a.Gr;  // rows per (sequence, KV head): query j, head g is row j * Gr + g
-  a.hb_size = std::min(a.G, 16);
-  a.head_blocks = (a.G + a.hb_size - 1) / a.hb_size;
-  a.seq_lens = seq_lens;
-  a.max_len = max_seq_len;
-  a.scale_log2 = scale * kLog2e;
-  a.kappa = (float)(1.2533141373155002512 / (double)(L.qjl_m > 0 ? L.qjl_m : 1));
-  a.part = part;
-  a.splits = plan.splits;
-  a.per_split = plan.tokens_per_split;
-  a.t_lo = L.sink_tokens;
-  a.recent = L.recent_tokens;
-  a.part_splits = part_splits;
+  DecodeArgs a = general_args(c, num_q_heads, nq, seq_lens, max_seq_len, scale, qv, part, plan, part_splits,
+                               sel, sel_stride);
+  if (!fp32 && !sel && kivi_fast_path_ok(L)) {
+    MfmaDecodeArgs f{};
+    f.k_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_K_CODES]);
+    f.v_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_V_CODES]);
+    f.k_scale_f = static_cast<const float*>(c->buf[KV_BUF_K_SCALE]);
+    f.k_zero_f = static_cast<const float*>(c->buf[KV_BUF_K_ZERO]);
+    f.v_scale_f = static_cast<const float*>(c->buf[KV_BUF_V_SCALE]);
+    f.v_zero_f = static_cast<const float*>(c->buf[KV_BUF_V_ZERO]);
+    f.k_stage = static_cast<const float*>(c->buf[KV_BUF_K_STAGE]);
+    f.pm = page_map(c);
+    f.q = qv;
+    f.seq_lens = seq_lens;
+    f.max_len = max_seq_len;
+    f.H = L.num_kv_heads;
+    f.cap = L.capacity;
+    f.Hq = num_q_heads;
+    f.scale_log2 = scale * kLog2e;
+    f.part = part;
+    f.splits = plan.splits;
+    f.per_split = plan.tokens_per_split;
+    f.nq = nq;
+    f.gr = num_q_heads / L.num_kv_heads;
+    f.part_splits = part_splits;
+    if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), st) != hipSuccess) return KV_EDEVICE;
+    // one launch per 16 (query, head) pairs of a KV head, each over the whole cache
+    for (f.c0 = 0; f.c0 < nq * f.gr; f.c0 += 16) {
+      f.ncol = std::min(16, nq * f.gr - f.c0);
+      int rc = launch_decode_kivi(f, B, st);
+      if (rc != KV_OK) return rc;
+    }
+    launch_kivi_tail(a, tail_split, B, st);
+    if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess) return KV_EDEVICE;
+    launch_merge(part, rows, part_splits, plan.splits, L.head_dim, L.format, c->rot, out, st);
+    return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
+  }
 
   if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), st) != hipSuccess) return KV_EDEVICE;
   switch (L.format) {
@@ -988,6 +1052,7 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
   }
   if (windowed) launch_window(c, q, q_dtype, num_q_heads, nq, seq_lens, max_seq_len, scale, part, part_splits,
                               plan.splits, st);
+  if (tail_split >= 0) launch_kivi_tail(a, tail_split, B, st);
   if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess) return KV_EDEVICE;
   launch_merge(part, rows, part_splits, plan.splits, L.head_dim, L.format, c->rot, out, st);
   return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;

@@ -1,0 +1,404 @@
+// Decode attention on the matrix cores (gfx950) for KIVI-2 caches with 128
+// channels: keys quantised per channel over groups of 32 tokens, values per
+// token over groups of 32 channels, 2-bit codes with fp32 scale and zero (page
+// "TurboQuant vs OSCAR vs EpiCache", section "quantization frontiers", KIVI
+// paragraph).
+//
+// One workgroup = 4 waves over one (sequence, KV head, context split); each
+// wave streams its own 32-token tiles (one key group each) from HBM into a
+// private two-stage LDS ring with direct-to-LDS loads and keeps the online
+// softmax of 16 (query, head) columns.  Per tile and wave:
+//   keys    S_t = sum_c (q_c s_c) code_tc + sum_c q_c z_c for the group's scale
+//           s and zero z.  The codes (0..3) are exact fp16 operands, q_c s_c an
+//           exact fp16 hi + lo pair: 16 v_mfma_f32_16x16x32_f16 (rows = tokens,
+//           columns = heads); the zero term is an fp32 sum per column.
+//   softmax per column = per lane column, the reference max moving only when
+//           a tile max passes it by 2^8.
+//   values  v_tc = code_tc s_t + z_t for the token's 32-channel group, made in
+//           fp16 (one rounding) as the B operand of 8 PV products.
+// Tokens of a sequence's incomplete last group are not coded yet (their keys
+// wait in staging); the general kernel takes them as one more split.
+#include <hip/hip_runtime.h>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+#include "kvq_kernels.h"
+
+namespace kvq {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+namespace {
+
+constexpr int kRsrcFlags = 0x00020000;
+constexpr int kD = 128;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcFlags);
+}
+
+// Stage of one 32-token tile (bytes): key codes (32 B per token row), the
+// group's 128 key scales and zeros, value codes, and the tokens' value scales
+// and zeros (4 per token).
+constexpr int kKc = 0, kKs = 1024, kKz = 1536, kVc = 2048, kVs = 3072, kVz = 3584, kStage = 4096;
+constexpr int kDma = 10;  // direct-to-LDS loads per tile
+
+struct Res {
+  __amdgpu_buffer_rsrc_t kc, ks, kz, vc, vs, vz;
+};
+
+// The tile from token t0 (a multiple of 32; t0 = capacity: no tile, every load
+// reads past its resource and writes zeros): lane l moves bytes [s l, s l + s)
+// of each chunk.
+__device__ __forceinline__ void issue_tile(uint8_t* st, int lane, int t0, const Res& r) {
+  const int co = t0 * 32 + lane * 16, go = (t0 >> 5) * 512 + lane * 4, vo = t0 * 16 + lane * 4;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.kc, (lds_ptr_t)(st + kKc), 16, co, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.ks, (lds_ptr_t)(st + kKs), 4, go, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.ks, (lds_ptr_t)(st + kKs + 256), 4, go + 256, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.kz, (lds_ptr_t)(st + kKz), 4, go, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.kz, (lds_ptr_t)(st + kKz + 256), 4, go + 256, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vc, (lds_ptr_t)(st + kVc), 16, co, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vs, (lds_ptr_t)(st + kVs), 4, vo, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vs, (lds_ptr_t)(st + kVs + 256), 4, vo + 256, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vz, (lds_ptr_t)(st + kVz), 4, vo, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vz, (lds_ptr_t)(st + kVz + 256), 4, vo + 256, 0, 0, 0);
+}
+
+// Codes 0..3 in nibbles as the exact fp16 values: an E2M1 nibble 0..3 is
+// 0, 0.5, 1, 1.5, and the conversion's power-of-two scale 2 restores the code.
+template <int SEL>
+__device__ __forceinline__ h2_t code_pair(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 2.0f, SEL);
+}
+
+// 8 two-bit codes (bits 2 i, 2 i + 1 of x) into the low bits of 8 nibbles (nibble i).
+__device__ __forceinline__ uint32_t spread_codes(uint32_t x) {
+  uint32_t t = (x | (x << 8)) & 0x00FF00FFu;
+  t = (t | (t << 4)) & 0x0F0F0F0Fu;
+  return (t | (t << 2)) & 0x33333333u;
+}
+
+__device__ __forceinline__ h8_t h8_from(h2_t a, h2_t b, h2_t c, h2_t d) {
+  h8_t r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+// 8 codes (16 bits) as the fp16 A operand of a key product, in k-slot order.
+__device__ __forceinline__ h8_t codes8(uint32_t x16) {
+  const uint32_t n = spread_codes(x16);
+  return h8_from(code_pair<0>(n), code_pair<1>(n), code_pair<2>(n), code_pair<3>(n));
+}
+
+// A-operand row c of a 16-token block holds token 4*(c%4) + c/4, so that the
+// C rows 4*q4 + v of a lane quarter are the tokens 4*v + q4.
+__device__ __forceinline__ int row_token(int c) { return 4 * (c & 3) + (c >> 2); }
+
+// Everything one wave carries across tiles.
+struct WaveState {
+  float q[4][8];  // prepared query of the lane's column, channels 32 kk + 8 q4 + i
+  float m_run, l_run;
+  f4_t o[8];      // O rows = columns 4 q4 + v; N-tile nt = channels 8 c + nt
+};
+
+// One tile: read this lane's fragments from the stage, refill the stage from
+// tile `next` once the reads have returned, then compute.  lim: the lane
+// column's token limit; t_full: a tile below it is whole for every column.
+__device__ __forceinline__ void tile_step(WaveState& w, uint8_t* st, int lane, int t0, int t_full, int lim, int next,
+                                          const Res& r, const MfmaDecodeArgs& a) {
+  const int q4 = lane >> 4, c = lane & 15;
+  // This stage's tile has landed once at most the other stage's refill is
+  // outstanding (explicit: the compiler's own wait for loads into LDS is not
+  // placed reliably across the loop back-edge).
+  static_assert(kDma < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | kDma);
+  // key codes: row c of block blk, channels 32 kk + 8 q4 + [0, 8) (bytes 8 kk + 2 q4, +1)
+  uint32_t kx[2][4];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    int ko = (16 * blk + row_token(c)) * 32 + 2 * q4;
+    asm volatile("" : "+v"(ko));
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) kx[blk][kk] = *reinterpret_cast<const uint16_t*>(st + kKc + ko + 8 * kk);
+  }
+  // the group's key scales and zeros of the lane's 32 channels
+  float ks[4][8], kz[4][8];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const float4* ps = reinterpret_cast<const float4*>(st + kKs + 4 * (32 * kk + 8 * q4));
+    const float4* pz = reinterpret_cast<const float4*>(st + kKz + 4 * (32 * kk + 8 * q4));
+    const float4 s0 = ps[0], s1 = ps[1], z0 = pz[0], z1 = pz[1];
+    ks[kk][0] = s0.x; ks[kk][1] = s0.y; ks[kk][2] = s0.z; ks[kk][3] = s0.w;
+    ks[kk][4] = s1.x; ks[kk][5] = s1.y; ks[kk][6] = s1.z; ks[kk][7] = s1.w;
+    kz[kk][0] = z0.x; kz[kk][1] = z0.y; kz[kk][2] = z0.z; kz[kk][3] = z0.w;
+    kz[kk][4] = z1.x; kz[kk][5] = z1.y; kz[kk][6] = z1.z; kz[kk][7] = z1.w;
+  }
+  // the lane's 8 tokens j (tile row 16 (j / 4) + 4 (j % 4) + q4): value codes of
+  // channels 8 c .. 8 c + 7 (bytes 2 c, 2 c + 1) and the scale and zero of their group c / 4
+  uint32_t vx[8];
+  float vs[8], vz[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int tok = 16 * (j >> 2) + 4 * (j & 3) + q4;
+    vx[j] = *reinterpret_cast<const uint16_t*>(st + kVc + tok * 32 + 2 * c);
+    vs[j] = *reinterpret_cast<const float*>(st + kVs + tok * 16 + 4 * (c >> 2));
+    vz[j] = *reinterpret_cast<const float*>(st + kVz + tok * 16 + 4 * (c >> 2));
+  }
+  // the reads above must have returned before the stage is overwritten
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  issue_tile(st, lane, next, r);
+
+  // ---------------- keys: B = q s as an fp16 hi + lo pair, A = the codes
+  h8_t bh[4], bl[4];
+  float zs = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const float x0 = w.q[kk][i] * ks[kk][i], x1 = w.q[kk][i + 1] * ks[kk][i + 1];
+      const h2_t hi = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(x0, x1));
+      const h2_t lo = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(x0 - (float)hi[0], x1 - (float)hi[1]));
+      bh[kk][i] = hi[0];
+      bh[kk][i + 1] = hi[1];
+      bl[kk][i] = lo[0];
+      bl[kk][i + 1] = lo[1];
+      zs = __builtin_fmaf(w.q[kk][i], kz[kk][i], zs);
+      zs = __builtin_fmaf(w.q[kk][i + 1], kz[kk][i + 1], zs);
+    }
+  }
+  zs += __shfl_xor(zs, 16);
+  zs += __shfl_xor(zs, 32);  // the column's zero term, in every lane of the column
+  f4_t sacc[2];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    f4_t acc = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const h8_t A = codes8(kx[blk][kk]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bh[kk], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bl[kk], acc, 0, 0, 0);
+    }
+    sacc[blk] = acc;
+  }
+
+  // ---------------- online softmax (this lane: column c, tokens t0 + 16 blk + 4 v + q4)
+  float sv[8];
+  float tmax = -INFINITY;
+  if (t0 + 32 <= t_full) {  // a whole tile for every column: nothing to mask
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        sv[4 * blk + v] = (sacc[blk][v] + zs) * a.scale_log2;
+        tmax = fmaxf(tmax, sv[4 * blk + v]);
+      }
+  } else {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int tok = t0 + 16 * blk + 4 * v + q4;
+        const float sx = tok < lim ? (sacc[blk][v] + zs) * a.scale_log2 : -INFINITY;
+        sv[4 * blk + v] = sx;
+        tmax = fmaxf(tmax, sx);
+      }
+  }
+  tmax = max_xor16(tmax);
+  tmax = max_xor32(tmax);
+  const bool bump = tmax > w.m_run + 8.f;
+  const float m_new = bump ? tmax : w.m_run;
+  const float alpha = bump ? __builtin_amdgcn_exp2f(w.m_run - m_new) : 1.f;
+  const float m_ref = m_new == -INFINITY ? 0.f : m_new;  // a column with no visible token yet
+  float psum = 0.f;
+  h8_t pf;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float p = __builtin_amdgcn_exp2f(sv[j] - m_ref);
+    psum += p;
+    pf[j] = (_Float16)p;
+  }
+  w.l_run = w.l_run * alpha + psum;
+  w.m_run = m_new;
+  // O rows are columns 4 q4 + v; column hh's alpha lives in lane hh (quarter 0)
+  if (__ballot(bump && c < a.ncol)) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float av = __shfl(alpha, (4 * q4 + v) & 15);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) w.o[nt][v] *= av;
+    }
+  }
+
+  // ---------------- values: B of N-tile nt = channel 8 c + nt over the lane's 8 tokens.
+  // e_j byte k = nibble k of token j's 16 bits (channels 8c + 2k, 8c + 2k + 1);
+  // X[p] byte k pairs channel 8c + 2k of tokens 2p and 2p + 1, Y[p] channel 8c + 2k + 1.
+  uint32_t X[4], Y[4];
+  h2_t s2[4], z2[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    uint32_t e0 = (vx[2 * p] | (vx[2 * p] << 8)) & 0x00FF00FFu;
+    e0 = (e0 | (e0 << 4)) & 0x0F0F0F0Fu;
+    uint32_t e1 = (vx[2 * p + 1] | (vx[2 * p + 1] << 8)) & 0x00FF00FFu;
+    e1 = (e1 | (e1 << 4)) & 0x0F0F0F0Fu;
+    X[p] = (e0 & 0x03030303u) | ((e1 & 0x03030303u) << 4);
+    Y[p] = ((e0 >> 2) & 0x03030303u) | ((e1 << 2) & 0x30303030u);
+    s2[p] = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(vs[2 * p], vs[2 * p + 1]));
+    z2[p] = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(vz[2 * p], vz[2 * p + 1]));
+  }
+#define KVQ_KIVI_PV(K)                                                                                          \
+  {                                                                                                             \
+    const h8_t bx = h8_from(__builtin_elementwise_fma(code_pair<K>(X[0]), s2[0], z2[0]),                        \
+                            __builtin_elementwise_fma(code_pair<K>(X[1]), s2[1], z2[1]),                        \
+                            __builtin_elementwise_fma(code_pair<K>(X[2]), s2[2], z2[2]),                        \
+                            __builtin_elementwise_fma(code_pair<K>(X[3]), s2[3], z2[3]));                       \
+    w.o[2 * K] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, bx, w.o[2 * K], 0, 0, 0);                           \
+    const h8_t by = h8_from(__builtin_elementwise_fma(code_pair<K>(Y[0]), s2[0], z2[0]),                        \
+                            __builtin_elementwise_fma(code_pair<K>(Y[1]), s2[1], z2[1]),                        \
+                            __builtin_elementwise_fma(code_pair<K>(Y[2]), s2[2], z2[2]),                        \
+                            __builtin_elementwise_fma(code_pair<K>(Y[3]), s2[3], z2[3]));                       \
+    w.o[2 * K + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, by, w.o[2 * K + 1], 0, 0, 0);                   \
+  }
+  KVQ_KIVI_PV(0)
+  KVQ_KIVI_PV(1)
+  KVQ_KIVI_PV(2)
+  KVQ_KIVI_PV(3)
+#undef KVQ_KIVI_PV
+  // keep the scheduler from interleaving two tiles (register pressure)
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+decode_kivi_kernel(MfmaDecodeArgs a) {
+  // LDS stages per wave, as separate arrays so that the compiler can tell which
+  // stage a direct-to-LDS load writes
+  __shared__ __attribute__((aligned(16))) uint8_t stA[4][kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t stB[4][kStage];
+  // the waves' running max / sum are combined through stage-B memory, their
+  // outputs through stage-A memory, 8 columns x 128 floats per wave at a time
+  float (*sm_o)[8][128] = reinterpret_cast<float (*)[8][128]>(&stA[0][0]);
+  float (*sm_m)[16] = reinterpret_cast<float (*)[16]>(&stB[0][0]);
+  float (*sm_l)[16] = reinterpret_cast<float (*)[16]>(&stB[0][0] + 4 * 16 * sizeof(float));
+  static_assert(sizeof(float) * 4 * 8 * 128 <= sizeof(stA), "stage A too small");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const size_t bh = (size_t)b * a.H + h;
+  const int L = min(min(a.seq_lens[b], a.max_len), a.cap);
+  // the coded tokens end at the first token of the incomplete group
+  const int kstage = reinterpret_cast<const int*>(a.k_stage)[bh * (4 + 32 * kD)] & ~31;
+  const int t_begin = split * a.per_split;
+  const int t_end = min(min(L, kstage), t_begin + a.per_split);
+  // column c is (query j, head g) pair c0 + c; query j sees the first L - (nq - 1 - j) tokens
+  const int c = lane & 15, q4 = lane >> 4;
+  const int lim = min(t_end, L - (a.nq - 1 - (a.c0 + c) / a.gr));
+  const int t_full = min(t_end, L - (a.nq - 1 - a.c0 / a.gr));
+
+  WaveState w;
+  {
+    const int pair = a.c0 + c;
+    const bool live = c < a.ncol;
+    const size_t qrow = ((size_t)b * a.nq + (live ? pair / a.gr : 0)) * a.Hq + (size_t)h * a.gr + (live ? pair % a.gr : 0);
+    const float* qp = static_cast<const float*>(a.q) + qrow * kD + 8 * q4;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const float4 x0 = *reinterpret_cast<const float4*>(qp + 32 * kk);
+      const float4 x1 = *reinterpret_cast<const float4*>(qp + 32 * kk + 4);
+      w.q[kk][0] = live ? x0.x : 0.f; w.q[kk][1] = live ? x0.y : 0.f;
+      w.q[kk][2] = live ? x0.z : 0.f; w.q[kk][3] = live ? x0.w : 0.f;
+      w.q[kk][4] = live ? x1.x : 0.f; w.q[kk][5] = live ? x1.y : 0.f;
+      w.q[kk][6] = live ? x1.z : 0.f; w.q[kk][7] = live ? x1.w : 0.f;
+    }
+  }
+  w.m_run = -INFINITY;
+  w.l_run = 0.f;
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) w.o[nt] = f4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Buffer resources over this (sequence, KV head)'s rows: a read past the end
+  // of a resource returns zeros instead of faulting (a missing tile reads past
+  // the end).
+  const size_t row0 = bh * a.cap;
+  const Res r{rsrc(a.k_codes + row0 * 32, (size_t)a.cap * 32),
+              rsrc(reinterpret_cast<const uint8_t*>(a.k_scale_f) + row0 / 32 * 512, (size_t)a.cap / 32 * 512),
+              rsrc(reinterpret_cast<const uint8_t*>(a.k_zero_f) + row0 / 32 * 512, (size_t)a.cap / 32 * 512),
+              rsrc(a.v_codes + row0 * 32, (size_t)a.cap * 32),
+              rsrc(reinterpret_cast<const uint8_t*>(a.v_scale_f) + row0 * 16, (size_t)a.cap * 16),
+              rsrc(reinterpret_cast<const uint8_t*>(a.v_zero_f) + row0 * 16, (size_t)a.cap * 16)};
+  auto tile_or_none = [&](int t) { return t < t_end ? t : a.cap; };
+
+  uint8_t* sa = stA[wave];
+  uint8_t* sb = stB[wave];
+  int t0 = t_begin + wave * 32;
+  issue_tile(sa, lane, tile_or_none(t0), r);
+  issue_tile(sb, lane, tile_or_none(t0 + 128), r);
+  for (; t0 < t_end; t0 += 256) {
+    // the second tile of a pair may lie past t_end: all its tokens are masked
+    tile_step(w, sa, lane, t0, t_full, lim, tile_or_none(t0 + 256), r, a);
+    tile_step(w, sb, lane, t0 + 128, t_full, lim, tile_or_none(t0 + 384), r, a);
+  }
+  // drain the refills still in flight before the waves' LDS is reused or the wave exits
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+
+  // ---------------- combine the four waves, write this split's partial result
+  __syncthreads();  // every wave is done with its stages before they hold outputs
+  const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int q4e = lane_e >> 4, ce = lane_e & 15;
+  const int tid_e = wave * 64 + lane_e;
+  float l_run = w.l_run;
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (q4e == 0) {
+    sm_m[wave][ce] = w.m_run;
+    sm_l[wave][ce] = l_run;
+  }
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {  // columns 8 r .. 8 r + 7 (rows 4 q4 + v of lane quarters 2 r, 2 r + 1)
+    if (r) __syncthreads();       // the previous round's outputs are read
+    if ((q4e >> 1) == r) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) sm_o[wave][4 * (q4e & 1) + v][8 * ce + nt] = w.o[nt][v];
+      }
+    }
+    __syncthreads();
+    for (int e = tid_e; e < 8 * kD; e += 256) {
+      const int hh = 8 * r + (e >> 7), ch = e & 127;
+      if (hh >= a.ncol) continue;  // a column with no query
+      float M = -INFINITY;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sm_m[ww][hh]);
+      float Ls = 0.f, O = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        const float mw = sm_m[ww][hh];
+        const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
+        Ls += f * sm_l[ww][hh];
+        O += f * sm_o[ww][hh - 8 * r][ch];
+      }
+      const int pc = a.c0 + hh;
+      const size_t row = ((size_t)b * a.nq + pc / a.gr) * a.Hq + (size_t)h * a.gr + pc % a.gr;
+      float* p = a.part + (row * a.part_splits + split) * (kD + 2);
+      p[2 + ch] = O;
+      if (ch == 0) {
+        p[0] = M;
+        p[1] = Ls;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+int launch_decode_kivi(const MfmaDecodeArgs& a, int B, hipStream_t st) {
+  if (a.pm.table || a.sel || a.ncol < 1 || a.ncol > 16) return KV_EUNSUPPORTED;
+  decode_kivi_kernel<<<dim3(a.splits, a.H, B), 256, 0, st>>>(a);
+  return KV_OK;
+}
+
+}  // namespace kvq

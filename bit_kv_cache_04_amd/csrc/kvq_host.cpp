@@ -94,6 +94,11 @@ bool latent_fast_path_ok(const kv_layout& L, int num_q_heads, int nq, int q_dtyp
          (size_t)L.capacity * 256 < (size_t(1) << 31);
 }
 
+bool kivi_fast_path_ok(const kv_layout& L) {
+  return L.format == KV_FMT_KIVI2 && L.head_dim == 128 && L.page_tokens == 0 && L.sink_tokens == 0 &&
+         L.recent_tokens == 0 && (size_t)L.capacity * 32 < (size_t(1) << 31);
+}
+
 int mfma_columns(int n) {
   return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : n <= 8 ? 8 : n <= 16 ? 16 : 32;
 }
@@ -118,8 +123,8 @@ SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int nq, int q_dtype, 
   // workgroups to keep a 256-CU part busy several times over, but no split
   // shorter than a few steps.
   const int G = num_q_heads / L->num_kv_heads;
-  const bool fast =
-      !general && (mfma_fast_path_ok(*L, num_q_heads, nq, q_dtype) || turbo_fast_path_ok(*L, num_q_heads, nq));
+  const bool fast = !general && (mfma_fast_path_ok(*L, num_q_heads, nq, q_dtype) ||
+                                 turbo_fast_path_ok(*L, num_q_heads, nq) || kivi_fast_path_ok(*L));
   const bool latent = !general && latent_fast_path_ok(*L, num_q_heads, nq, q_dtype);
   const int tile = fast ? 128 : 64;
   // the latent kernel keeps one workgroup per compute unit resident and every

@@ -58,6 +58,8 @@ bool mfma_fast_path_ok(const kv_layout& L, int num_q_heads, int nq, int q_dtype)
 bool turbo_fast_path_ok(const kv_layout& L, int num_q_heads, int nq);
 // The shared-latent matrix-core kernel covers this cache / query combination.
 bool latent_fast_path_ok(const kv_layout& L, int num_q_heads, int nq, int q_dtype);
+// The KIVI-2 matrix-core kernel covers this cache.
+bool kivi_fast_path_ok(const kv_layout& L);
 // Columns of the matrix-core kernel that takes n (query, head) pairs, n <= 32:
 // n rounded up to 1, 2, 4, 8, 16 or 32 (two blocks of 16, FP4 keys only).
 int mfma_columns(int n);
@@ -89,6 +91,9 @@ constexpr size_t kStaticWorkspaceBytes = size_t(128) << 20;
 // Mixed precision: splits of partial rows the bf16 window takes (one per 64 of
 // its sink_tokens + recent_tokens positions), 0 without a window.
 inline int window_chunks(const kv_layout& L) { return (L.sink_tokens + L.recent_tokens + 63) / 64; }
+// KIVI-2: the keys of a sequence's incomplete last group wait uncoded in
+// staging; a dense decode reads those tokens in one more split of partial rows.
+inline int tail_chunks(const kv_layout& L) { return L.format == KV_FMT_KIVI2 ? 1 : 0; }
 
 // Device launchers (defined in the HIP translation units).  Arguments are
 // validated by the caller.
