@@ -16,6 +16,10 @@
 //           a tile max passes it by 2^8.
 //   values  v_tc = code_tc s_t + z_t for the token's 32-channel group, made in
 //           fp16 (one rounding) as the B operand of 8 PV products.
+// With fewer than 16 (query, head) pairs per launch the 16 columns carry each
+// pair S = 16 / P times (P pair slots), column c taking pair c % P over the
+// channel part c / P only, and rotations within each 16-lane row add the
+// parts: each lane scales 128 / S query channels per tile instead of 128.
 // Tokens of a sequence's incomplete last group are not coded yet (their keys
 // wait in staging); the general kernel takes them as one more split.
 #include <hip/hip_runtime.h>
@@ -98,9 +102,18 @@ __device__ __forceinline__ h8_t codes8(uint32_t x16) {
 // C rows 4*q4 + v of a lane quarter are the tokens 4*v + q4.
 __device__ __forceinline__ int row_token(int c) { return 4 * (c & 3) + (c >> 2); }
 
+// x of lane (l & ~15) | ((l + N) & 15), 0 < N < 16: DPP row_ror:(16 - N) (a
+// rotation right by k hands lane l the value of lane l - k within its row).
+template <int N>
+__device__ __forceinline__ float row_fetch(float x) {
+  static_assert(N > 0 && N < 16, "rotation within a 16-lane row");
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x120 + (16 - N), 0xF, 0xF, false));
+}
+
 // Everything one wave carries across tiles.
 struct WaveState {
-  float q[4][8];  // prepared query of the lane's column, channels 32 kk + 8 q4 + i
+  float q[4][8];  // prepared query of the lane's column: its part's k-steps kp, channels 32 kk + 8 q4 + i
   float m_run, l_run;
   f4_t o[8];      // O rows = columns 4 q4 + v; N-tile nt = channels 8 c + nt
 };
@@ -108,9 +121,14 @@ struct WaveState {
 // One tile: read this lane's fragments from the stage, refill the stage from
 // tile `next` once the reads have returned, then compute.  lim: the lane
 // column's token limit; t_full: a tile below it is whole for every column.
+// S: channel parts per pair (column c: pair c % (16 / S), k-steps of part c / (16 / S)).
+template <int S>
 __device__ __forceinline__ void tile_step(WaveState& w, uint8_t* st, int lane, int t0, int t_full, int lim, int next,
                                           const Res& r, const MfmaDecodeArgs& a) {
+  constexpr int P = 16 / S, KP = 4 / S;  // pair slots, k-steps per part
   const int q4 = lane >> 4, c = lane & 15;
+  const int part = c / P;
+  const int pc = c % P;
   // This stage's tile has landed once at most the other stage's refill is
   // outstanding (explicit: the compiler's own wait for loads into LDS is not
   // placed reliably across the loop back-edge).
@@ -125,12 +143,13 @@ __device__ __forceinline__ void tile_step(WaveState& w, uint8_t* st, int lane, i
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) kx[blk][kk] = *reinterpret_cast<const uint16_t*>(st + kKc + ko + 8 * kk);
   }
-  // the group's key scales and zeros of the lane's 32 channels
-  float ks[4][8], kz[4][8];
+  // the group's key scales and zeros of the lane's channels: 8 per k-step of its part
+  float ks[KP][8], kz[KP][8];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const float4* ps = reinterpret_cast<const float4*>(st + kKs + 4 * (32 * kk + 8 * q4));
-    const float4* pz = reinterpret_cast<const float4*>(st + kKz + 4 * (32 * kk + 8 * q4));
+  for (int kk = 0; kk < KP; ++kk) {
+    const int ch = 32 * (KP * part + kk) + 8 * q4;
+    const float4* ps = reinterpret_cast<const float4*>(st + kKs + 4 * ch);
+    const float4* pz = reinterpret_cast<const float4*>(st + kKz + 4 * ch);
     const float4 s0 = ps[0], s1 = ps[1], z0 = pz[0], z1 = pz[1];
     ks[kk][0] = s0.x; ks[kk][1] = s0.y; ks[kk][2] = s0.z; ks[kk][3] = s0.w;
     ks[kk][4] = s1.x; ks[kk][5] = s1.y; ks[kk][6] = s1.z; ks[kk][7] = s1.w;
@@ -152,26 +171,41 @@ __device__ __forceinline__ void tile_step(WaveState& w, uint8_t* st, int lane, i
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   issue_tile(st, lane, next, r);
 
-  // ---------------- keys: B = q s as an fp16 hi + lo pair, A = the codes
+  // ---------------- keys: B = q s as an fp16 hi + lo pair, A = the codes.  The
+  // lane scales its part's k-steps only (the others hold zeros): k-step kk of
+  // part u is kk = KP u + kp.
   h8_t bh[4], bl[4];
-  float zs = 0.f;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
+    bh[kk] = h8_t{};
+    bl[kk] = h8_t{};
+  }
+  float zs = 0.f;
+  h8_t ph[KP], pl[KP];
+#pragma unroll
+  for (int kp = 0; kp < KP; ++kp) {
 #pragma unroll
     for (int i = 0; i < 8; i += 2) {
-      const float x0 = w.q[kk][i] * ks[kk][i], x1 = w.q[kk][i + 1] * ks[kk][i + 1];
+      const float x0 = w.q[kp][i] * ks[kp][i], x1 = w.q[kp][i + 1] * ks[kp][i + 1];
       const h2_t hi = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(x0, x1));
       const h2_t lo = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(x0 - (float)hi[0], x1 - (float)hi[1]));
-      bh[kk][i] = hi[0];
-      bh[kk][i + 1] = hi[1];
-      bl[kk][i] = lo[0];
-      bl[kk][i + 1] = lo[1];
-      zs = __builtin_fmaf(w.q[kk][i], kz[kk][i], zs);
-      zs = __builtin_fmaf(w.q[kk][i + 1], kz[kk][i + 1], zs);
+      ph[kp][i] = hi[0];
+      ph[kp][i + 1] = hi[1];
+      pl[kp][i] = lo[0];
+      pl[kp][i + 1] = lo[1];
+      zs = __builtin_fmaf(w.q[kp][i], kz[kp][i], zs);
+      zs = __builtin_fmaf(w.q[kp][i + 1], kz[kp][i + 1], zs);
+    }
+  }
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    if (kk / KP == part) {  // place the part's operands at their k-steps
+      bh[kk] = ph[kk % KP];
+      bl[kk] = pl[kk % KP];
     }
   }
   zs += __shfl_xor(zs, 16);
-  zs += __shfl_xor(zs, 32);  // the column's zero term, in every lane of the column
+  zs += __shfl_xor(zs, 32);  // the column part's zero term, in every lane of the column
   f4_t sacc[2];
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
@@ -181,6 +215,13 @@ __device__ __forceinline__ void tile_step(WaveState& w, uint8_t* st, int lane, i
       const h8_t A = codes8(kx[blk][kk]);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bh[kk], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bl[kk], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {  // the pair's logit: its parts summed along the row
+      float x = acc[v] + zs;
+      if constexpr (S >= 2) x += row_fetch<P>(x);
+      if constexpr (S >= 4) x += row_fetch<2 * P>(x);
+      acc[v] = x;
     }
     sacc[blk] = acc;
   }
@@ -193,7 +234,7 @@ __device__ __forceinline__ void tile_step(WaveState& w, uint8_t* st, int lane, i
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        sv[4 * blk + v] = (sacc[blk][v] + zs) * a.scale_log2;
+        sv[4 * blk + v] = sacc[blk][v] * a.scale_log2;
         tmax = fmaxf(tmax, sv[4 * blk + v]);
       }
   } else {
@@ -202,7 +243,7 @@ __device__ __forceinline__ void tile_step(WaveState& w, uint8_t* st, int lane, i
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int tok = t0 + 16 * blk + 4 * v + q4;
-        const float sx = tok < lim ? (sacc[blk][v] + zs) * a.scale_log2 : -INFINITY;
+        const float sx = tok < lim ? sacc[blk][v] * a.scale_log2 : -INFINITY;
         sv[4 * blk + v] = sx;
         tmax = fmaxf(tmax, sx);
       }
@@ -224,7 +265,7 @@ __device__ __forceinline__ void tile_step(WaveState& w, uint8_t* st, int lane, i
   w.l_run = w.l_run * alpha + psum;
   w.m_run = m_new;
   // O rows are columns 4 q4 + v; column hh's alpha lives in lane hh (quarter 0)
-  if (__ballot(bump && c < a.ncol)) {
+  if (__ballot(bump && pc < a.ncol)) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const float av = __shfl(alpha, (4 * q4 + v) & 15);
@@ -271,8 +312,10 @@ __device__ __forceinline__ void tile_step(WaveState& w, uint8_t* st, int lane, i
   __builtin_amdgcn_sched_barrier(0);
 }
 
+template <int S>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_kivi_kernel(MfmaDecodeArgs a) {
+  constexpr int P = 16 / S, KP = 4 / S;  // pair slots, k-steps per channel part
   // LDS stages per wave, as separate arrays so that the compiler can tell which
   // stage a direct-to-LDS load writes
   __shared__ __attribute__((aligned(16))) uint8_t stA[4][kStage];
@@ -293,21 +336,28 @@ decode_kivi_kernel(MfmaDecodeArgs a) {
   const int kstage = reinterpret_cast<const int*>(a.k_stage)[bh * (4 + 32 * kD)] & ~31;
   const int t_begin = split * a.per_split;
   const int t_end = min(min(L, kstage), t_begin + a.per_split);
-  // column c is (query j, head g) pair c0 + c; query j sees the first L - (nq - 1 - j) tokens
+  // column c is (query j, head g) pair c0 + c % P; query j sees the first L - (nq - 1 - j) tokens
   const int c = lane & 15, q4 = lane >> 4;
-  const int lim = min(t_end, L - (a.nq - 1 - (a.c0 + c) / a.gr));
+  const int pc = c % P, part = c / P;
+  const int lim = min(t_end, L - (a.nq - 1 - (a.c0 + pc) / a.gr));
   const int t_full = min(t_end, L - (a.nq - 1 - a.c0 / a.gr));
 
   WaveState w;
   {
-    const int pair = a.c0 + c;
-    const bool live = c < a.ncol;
+    const int pair = a.c0 + pc;
+    const bool live = pc < a.ncol;
     const size_t qrow = ((size_t)b * a.nq + (live ? pair / a.gr : 0)) * a.Hq + (size_t)h * a.gr + (live ? pair % a.gr : 0);
     const float* qp = static_cast<const float*>(a.q) + qrow * kD + 8 * q4;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const float4 x0 = *reinterpret_cast<const float4*>(qp + 32 * kk);
-      const float4 x1 = *reinterpret_cast<const float4*>(qp + 32 * kk + 4);
+      if (kk >= KP) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w.q[kk][i] = 0.f;
+        continue;
+      }
+      const int k = KP * part + kk;
+      const float4 x0 = *reinterpret_cast<const float4*>(qp + 32 * k);
+      const float4 x1 = *reinterpret_cast<const float4*>(qp + 32 * k + 4);
       w.q[kk][0] = live ? x0.x : 0.f; w.q[kk][1] = live ? x0.y : 0.f;
       w.q[kk][2] = live ? x0.z : 0.f; w.q[kk][3] = live ? x0.w : 0.f;
       w.q[kk][4] = live ? x1.x : 0.f; w.q[kk][5] = live ? x1.y : 0.f;
@@ -338,8 +388,8 @@ decode_kivi_kernel(MfmaDecodeArgs a) {
   issue_tile(sb, lane, tile_or_none(t0 + 128), r);
   for (; t0 < t_end; t0 += 256) {
     // the second tile of a pair may lie past t_end: all its tokens are masked
-    tile_step(w, sa, lane, t0, t_full, lim, tile_or_none(t0 + 256), r, a);
-    tile_step(w, sb, lane, t0 + 128, t_full, lim, tile_or_none(t0 + 384), r, a);
+    tile_step<S>(w, sa, lane, t0, t_full, lim, tile_or_none(t0 + 256), r, a);
+    tile_step<S>(w, sb, lane, t0 + 128, t_full, lim, tile_or_none(t0 + 384), r, a);
   }
   // drain the refills still in flight before the waves' LDS is reused or the wave exits
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -369,7 +419,7 @@ decode_kivi_kernel(MfmaDecodeArgs a) {
     __syncthreads();
     for (int e = tid_e; e < 8 * kD; e += 256) {
       const int hh = 8 * r + (e >> 7), ch = e & 127;
-      if (hh >= a.ncol) continue;  // a column with no query
+      if (hh >= P || hh >= a.ncol) continue;  // a column with no query, or a pair's copy
       float M = -INFINITY;
 #pragma unroll
       for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sm_m[ww][hh]);
@@ -397,7 +447,10 @@ decode_kivi_kernel(MfmaDecodeArgs a) {
 
 int launch_decode_kivi(const MfmaDecodeArgs& a, int B, hipStream_t st) {
   if (a.pm.table || a.sel || a.ncol < 1 || a.ncol > 16) return KV_EUNSUPPORTED;
-  decode_kivi_kernel<<<dim3(a.splits, a.H, B), 256, 0, st>>>(a);
+  const dim3 grid(a.splits, a.H, B);
+  if (a.ncol <= 4) decode_kivi_kernel<4><<<grid, 256, 0, st>>>(a);
+  else if (a.ncol <= 8) decode_kivi_kernel<2><<<grid, 256, 0, st>>>(a);
+  else decode_kivi_kernel<1><<<grid, 256, 0, st>>>(a);
   return KV_OK;
 }
 
