@@ -265,9 +265,12 @@ __device__ __forceinline__ uint32_t kivi_code(float x, float z, float s) {
 }
 
 // One workgroup per (sequence x KV head, 32-token group): the group's keys and
-// values are staged in LDS with coalesced loads, then
-//   keys:   one thread per channel quad, min / max over the 32 tokens;
-//   values: one thread per (token, 32-channel group).
+// values are staged in LDS with coalesced loads, then all 256 threads code:
+//   keys:   per channel, min / max over the 32 tokens, the tokens split over
+//           256 / d threads;
+//   values: per (token, 32-channel group), min / max over the group, its
+//           channels split over 256 / (d / 32 x 32) threads (16 channels each
+//           at d = 128, 8 at d = 64).
 constexpr int kKiviMaxD = 128;
 
 __device__ __forceinline__ float4 load4_as_f32(const float* p) { return *reinterpret_cast<const float4*>(p); }
@@ -318,48 +321,51 @@ __global__ void __launch_bounds__(256) kivi_append_kernel(const InT* __restrict_
   const size_t slot0 = seq_row(pos, bh, start + g * 32, cap);  // cache row of the group's first token
   if (tid == 0 && g == ngroups - 1) set_appended(stage, bh, d, start + n);
   if (slot0 == kNoRow) return;  // a page outside the pool
-  if (tid < quads) {
-    const int cq = tid;
-    float mn[4], mx[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) mn[j] = INFINITY, mx[j] = -INFINITY;
-    for (int t = 0; t < 32; ++t)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        mn[j] = fminf(mn[j], xk[t][4 * cq + j]);
-        mx[j] = fmaxf(mx[j], xk[t][4 * cq + j]);
-      }
-    float sc[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sc[j] = __fdiv_rn(__fsub_rn(mx[j], mn[j]), 3.0f);
+  // keys: thread (token part kp, channel c), d * kparts = 256; every thread
+  // takes its channel's min / max over the 32 tokens, then codes its part's
+  // 32 / kparts tokens (lanes c .. c + 3 of a wave pack one byte per token)
+  {
+    const int kparts = 256 / d, c = tid % d, kp = tid / d, tpp = 32 / kparts;
+    float mn = INFINITY, mx = -INFINITY;
     for (int t = 0; t < 32; ++t) {
-      uint32_t byte = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) byte |= kivi_code(xk[t][4 * cq + j], mn[j], sc[j]) << (2 * j);
-      kc[(slot0 + t) * quads + cq] = (uint8_t)byte;
+      mn = fminf(mn, xk[t][c]);
+      mx = fmaxf(mx, xk[t][c]);
     }
-    const size_t meta = slot0 / 32 * (size_t)d + 4 * cq;  // pages and the layout hold whole groups
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ks[meta + j] = sc[j];
-      kz[meta + j] = mn[j];
+    const float sc = __fdiv_rn(__fsub_rn(mx, mn), 3.0f);
+    for (int t = kp * tpp; t < (kp + 1) * tpp; ++t) {
+      uint32_t code = kivi_code(xk[t][c], mn, sc) << (2 * (c & 3));
+      code |= __shfl_xor(code, 1);
+      code |= __shfl_xor(code, 2);
+      if ((c & 3) == 0) kc[(slot0 + t) * quads + c / 4] = (uint8_t)code;
+    }
+    if (kp == 0) {
+      const size_t meta = slot0 / 32 * (size_t)d + c;  // pages and the layout hold whole groups
+      ks[meta] = sc;
+      kz[meta] = mn;
     }
   }
-  const int vgroups = d / 32;
-  for (int it = tid; it < 32 * vgroups; it += 256) {
-    const int t = it / vgroups, vg = it % vgroups;
+  // values: thread (token t, channel group vg, channel part vp), 32 * vgroups *
+  // vparts = 256; every thread takes the group's min / max over its 32 channels
+  // and codes its part's 32 / vparts of them
+  {
+    const int vgroups = d / 32, vparts = 256 / (32 * vgroups), cpp = 32 / vparts;
+    const int vp = tid % vparts, vg = (tid / vparts) % vgroups, t = tid / (vparts * vgroups);
     float mn = INFINITY, mx = -INFINITY;
     for (int i = 0; i < 32; ++i) {
       mn = fminf(mn, xv[t][32 * vg + i]);
       mx = fmaxf(mx, xv[t][32 * vg + i]);
     }
     const float sc = __fdiv_rn(__fsub_rn(mx, mn), 3.0f);
-    unsigned long long packed = 0;
-    for (int i = 0; i < 32; ++i) packed |= (unsigned long long)kivi_code(xv[t][32 * vg + i], mn, sc) << (2 * i);
+    uint32_t packed = 0;
+    for (int i = 0; i < cpp; ++i) packed |= kivi_code(xv[t][32 * vg + vp * cpp + i], mn, sc) << (2 * i);
     const size_t dr = slot0 + t;
-    *reinterpret_cast<unsigned long long*>(vc + dr * (d / 4) + vg * 8) = packed;
-    vs[dr * vgroups + vg] = sc;
-    vz[dr * vgroups + vg] = mn;
+    uint8_t* dst = vc + dr * (d / 4) + vg * 8 + vp * (cpp / 4);
+    if (cpp == 16) *reinterpret_cast<uint32_t*>(dst) = packed;
+    else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)packed;
+    if (vp == 0) {
+      vs[dr * vgroups + vg] = sc;
+      vz[dr * vgroups + vg] = mn;
+    }
   }
 }
 
