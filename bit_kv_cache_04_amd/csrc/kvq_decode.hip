@@ -51,9 +51,10 @@ struct DecodeArgs {
   float* part;       // [B][nq][Hq][part_splits][DV + 2]: m (log2 units), l, o[DV]
   int splits, per_split;
   int t_lo, recent, part_splits;  // packed tokens [t_lo, L - recent), split s from t_lo + s * per_split
-  // KIVI2 dense decode: the splits stop at the first staged token; tail_split
-  // >= 0 runs one workgroup per (KV head, head block, sequence) over the staged
-  // tokens instead, writing partial split tail_split
+  // KIVI2 dense decode: the splits stop at the first staged token; with
+  // tail_split >= 0 the workgroups of grid column `splits` (one per KV head,
+  // head block and sequence) take the staged tokens and write partial split
+  // tail_split
   int tail_split;
 };
 
@@ -137,7 +138,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
   const int L = min(min(a.seq_lens[b], a.max_len), a.cap);
   // KIVI2: keys from the first token of the appended sequence's incomplete group on are staged
   const int kstage = FMT == KV_FMT_KIVI2 ? reinterpret_cast<const int*>(a.k_stage)[bh * (4 + 32 * a.d)] & ~31 : a.cap;
-  const bool tail = FMT == KV_FMT_KIVI2 && a.tail_split >= 0;
+  const bool tail = FMT == KV_FMT_KIVI2 && a.tail_split >= 0 && split == a.splits;
   const int t_begin = tail ? max(a.t_lo, kstage) : a.t_lo + split * a.per_split;
   int t_end = tail ? max(a.t_lo, L - a.recent) : min(max(a.t_lo, L - a.recent), t_begin + a.per_split);
   if (FMT == KV_FMT_KIVI2 && !a.sel && !tail) t_end = min(t_end, kstage);  // the staged tokens: the tail split
@@ -745,7 +746,7 @@ void launch_merge(const float* part, int rows, int splits, int rot_splits, int d
 
 template <int FMT, int DK, int DV, int HB>
 void launch_split(const DecodeArgs& a, int B, hipStream_t st) {
-  dim3 grid(a.splits, a.H * a.head_blocks, B);
+  dim3 grid(a.splits + (a.tail_split >= 0 ? 1 : 0), a.H * a.head_blocks, B);
   decode_split_kernel<FMT, DK, DV, 32, HB><<<grid, 256, 0, st>>>(a);
 }
 
@@ -837,6 +838,7 @@ static DecodeArgs general_args(const kv_cache* c, int num_q_heads, int nq, const
 // split `split` (one workgroup per (KV head, head block, sequence)).
 static void launch_kivi_tail(DecodeArgs a, int split, int B, hipStream_t st) {
   a.tail_split = split;
+  a.splits = 0;  // the launch's workgroups are all tail workgroups
   const dim3 grid(1, a.H * a.head_blocks, B);
   if (a.d == 64) decode_split_kernel<KV_FMT_KIVI2, 64, 64, 32, 16><<<grid, 256, 0, st>>>(a);
   else decode_split_kernel<KV_FMT_KIVI2, 128, 128, 32, 16><<<grid, 256, 0, st>>>(a);
@@ -1035,6 +1037,8 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
   }
 
+  // KIVI2: the staged tokens' workgroups follow the splits' in the same launch
+  a.tail_split = tail_split;
   if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), st) != hipSuccess) return KV_EDEVICE;
   switch (L.format) {
     case KV_FMT_KIVI2:
@@ -1052,7 +1056,6 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
   }
   if (windowed) launch_window(c, q, q_dtype, num_q_heads, nq, seq_lens, max_seq_len, scale, part, part_splits,
                               plan.splits, st);
-  if (tail_split >= 0) launch_kivi_tail(a, tail_split, B, st);
   if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess) return KV_EDEVICE;
   launch_merge(part, rows, part_splits, plan.splits, L.head_dim, L.format, c->rot, out, st);
   return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;

@@ -26,10 +26,22 @@ def _fields(path):
     return kv
 
 
+# bench flags that resize a workload, and the field each sets
+RESIZE = {"--batch": "batch", "--context": "context", "--q-heads": "hq", "--kv-heads": "hkv", "--head-dim": "head_dim"}
+
+
 def _workload(path):
+    """The workload a summary covers: the one its file name holds, resized by
+    the flags of its quoted bench command (all its commands agree)."""
     names = [w for w in CONFIGS if f"_{w}_" in os.path.basename(path)]
     assert len(names) == 1, path
-    return CONFIGS[names[0]]
+    sizes = set()
+    for line in open(path):
+        if line.startswith("# command") and "bench.py" in line:
+            args = line.split("bench.py", 1)[1].split()
+            sizes.add(tuple(sorted((RESIZE[a], int(args[i + 1])) for i, a in enumerate(args) if a in RESIZE)))
+    assert len(sizes) <= 1, path
+    return CONFIGS[names[0]].scaled(**dict(sizes.pop())) if sizes else CONFIGS[names[0]]
 
 
 PMC = sorted(glob.glob(os.path.join(PROFILES, "*_pmc.txt")))
@@ -41,6 +53,15 @@ def test_every_workload_has_traffic_and_utilisation_summaries():
     for w in CONFIGS:
         assert any(f"_{w}_pmc" in p for p in PMC), w
         assert any(p.endswith(f"_{w}_util.txt") for p in UTIL), w
+
+
+def test_resized_summaries_are_not_read_as_the_workload_itself():
+    """The bench reads profiles/*_<workload>_<kind>.txt for a workload's own
+    sizes: a summary of a resized copy must carry more in its name."""
+    for path in PMC + UTIL:
+        base = os.path.basename(path)
+        if _workload(path) not in CONFIGS.values():
+            assert not any(base.endswith(f"_{w}_pmc.txt") or base.endswith(f"_{w}_util.txt") for w in CONFIGS), base
 
 
 @pytest.mark.parametrize("path", PMC, ids=os.path.basename)
