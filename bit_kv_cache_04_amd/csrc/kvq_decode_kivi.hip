@@ -342,6 +342,27 @@ decode_kivi_kernel(MfmaDecodeArgs a) {
   const int lim = min(t_end, L - (a.nq - 1 - (a.c0 + pc) / a.gr));
   const int t_full = min(t_end, L - (a.nq - 1 - a.c0 / a.gr));
 
+
+  // Buffer resources over this (sequence, KV head)'s rows: a read past the end
+  // of a resource returns zeros instead of faulting (a missing tile reads past
+  // the end).
+  const size_t row0 = bh * a.cap;
+  const Res r{rsrc(a.k_codes + row0 * 32, (size_t)a.cap * 32),
+              rsrc(reinterpret_cast<const uint8_t*>(a.k_scale_f) + row0 / 32 * 512, (size_t)a.cap / 32 * 512),
+              rsrc(reinterpret_cast<const uint8_t*>(a.k_zero_f) + row0 / 32 * 512, (size_t)a.cap / 32 * 512),
+              rsrc(a.v_codes + row0 * 32, (size_t)a.cap * 32),
+              rsrc(reinterpret_cast<const uint8_t*>(a.v_scale_f) + row0 * 16, (size_t)a.cap * 16),
+              rsrc(reinterpret_cast<const uint8_t*>(a.v_zero_f) + row0 * 16, (size_t)a.cap * 16)};
+  auto tile_or_none = [&](int t) { return t < t_end ? t : a.cap; };
+
+  uint8_t* sa = stA[wave];
+  uint8_t* sb = stB[wave];
+  int t0 = t_begin + wave * 32;
+  // The first two tiles are issued before the sequence length, the staging
+  // marker and the query have arrived: a tile past the end is read from the
+  // cache's own rows and never used, or has all its tokens masked.
+  issue_tile(sa, lane, t0 < a.cap ? t0 : a.cap, r);
+  issue_tile(sb, lane, t0 + 128 < a.cap ? t0 + 128 : a.cap, r);
   WaveState w;
   {
     const int pair = a.c0 + pc;
@@ -368,24 +389,6 @@ decode_kivi_kernel(MfmaDecodeArgs a) {
   w.l_run = 0.f;
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) w.o[nt] = f4_t{0.f, 0.f, 0.f, 0.f};
-
-  // Buffer resources over this (sequence, KV head)'s rows: a read past the end
-  // of a resource returns zeros instead of faulting (a missing tile reads past
-  // the end).
-  const size_t row0 = bh * a.cap;
-  const Res r{rsrc(a.k_codes + row0 * 32, (size_t)a.cap * 32),
-              rsrc(reinterpret_cast<const uint8_t*>(a.k_scale_f) + row0 / 32 * 512, (size_t)a.cap / 32 * 512),
-              rsrc(reinterpret_cast<const uint8_t*>(a.k_zero_f) + row0 / 32 * 512, (size_t)a.cap / 32 * 512),
-              rsrc(a.v_codes + row0 * 32, (size_t)a.cap * 32),
-              rsrc(reinterpret_cast<const uint8_t*>(a.v_scale_f) + row0 * 16, (size_t)a.cap * 16),
-              rsrc(reinterpret_cast<const uint8_t*>(a.v_zero_f) + row0 * 16, (size_t)a.cap * 16)};
-  auto tile_or_none = [&](int t) { return t < t_end ? t : a.cap; };
-
-  uint8_t* sa = stA[wave];
-  uint8_t* sb = stB[wave];
-  int t0 = t_begin + wave * 32;
-  issue_tile(sa, lane, tile_or_none(t0), r);
-  issue_tile(sb, lane, tile_or_none(t0 + 128), r);
   for (; t0 < t_end; t0 += 256) {
     // the second tile of a pair may lie past t_end: all its tokens are masked
     tile_step<S>(w, sa, lane, t0, t_full, lim, tile_or_none(t0 + 256), r, a);

@@ -604,16 +604,6 @@ decode_mfma_kernel(MfmaDecodeArgs a) {
     return ~0u;
   };
 
-  WaveState<KP, NB> w;
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    KP::template load_q<G>(w.q[nb], a, b, h, lane >> 4, lane & 15, 16 * nb);
-    w.m_run[nb] = -INFINITY;
-    w.l_run[nb] = 0.f;
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) w.o[nb][nt] = f4_t{0.f, 0.f, 0.f, 0.f};
-  }
-
   // Buffer resources over this (sequence, KV head)'s rows, or over one page's:
   // 32-bit offsets, and a read past the end of a resource returns zeros instead
   // of faulting (a missing tile reads past the end; a page outside the pool has
@@ -650,7 +640,14 @@ decode_mfma_kernel(MfmaDecodeArgs a) {
   uint8_t* sb = stB[wave];
   int t0 = t_begin + wave * 32;
   {
-    const TileSrc<KP> s0 = tile_or_none(t0), s1 = tile_or_none(t0 + 128);
+    // A contiguous cache's first two tiles are issued before the sequence
+    // length has arrived (and before the query): tiles past the end are read
+    // from the cache's own rows and weighted by zero, or never used.
+    auto first = [&](int t) {
+      if constexpr (PAGED || SPARSE) return tile_or_none(t);
+      return TileSrc<KP>{kr, vr, t < a.cap ? t : a.cap};
+    };
+    const TileSrc<KP> s0 = first(t0), s1 = first(t0 + 128);
     if constexpr (SPARSE) {
       issue_tile_rows<KP>(sa, lane, s0.t, spos, s0.kr, s0.vr);
       issue_tile_rows<KP>(sb, lane, s1.t, spos, s1.kr, s1.vr);
@@ -658,6 +655,15 @@ decode_mfma_kernel(MfmaDecodeArgs a) {
       issue_tile<KP>(sa, lane, s0.t, s0.kr, s0.vr);
       issue_tile<KP>(sb, lane, s1.t, s1.kr, s1.vr);
     }
+  }
+  WaveState<KP, NB> w;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    KP::template load_q<G>(w.q[nb], a, b, h, lane >> 4, lane & 15, 16 * nb);
+    w.m_run[nb] = -INFINITY;
+    w.l_run[nb] = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) w.o[nb][nt] = f4_t{0.f, 0.f, 0.f, 0.f};
   }
   if constexpr (NS == 2) {
     for (; t0 < t_end; t0 += 256) {

@@ -457,49 +457,6 @@ decode_turbo_kernel(TurboDecodeArgs a) {
   // tiles below t_full hold no position any live pair must skip
   const int t_full = min(t_end, L - (a.nq - 1 - j_first));
 
-  WaveState<STEPS> w;
-  TileMask mk;
-  constexpr int kCols = STEPS == 2 ? 8 : 16;  // distinct pairs per launch
-  {
-    const int col = c % kCols;
-    const int pair = a.c0 + col;
-    mk.live = col < a.ncol;
-    const int jq = (mk.live ? pair : a.c0) / G, g = (mk.live ? pair : a.c0) % G;
-    mk.t_lo = a.t_lo;
-    mk.lim = min(t_end, L - (a.nq - 1 - jq));
-    const size_t qrow = ((size_t)b * a.nq + jq) * a.Hq + (size_t)h * G + g;
-    const uint8_t* pc = a.qpieces + qrow * kTurboPieceBytes;
-    const int p0 = STEPS == 2 && c >= 8 ? 2 : 0;  // this column's first piece
-#pragma unroll
-    for (int m = 0; m < 3; ++m) {
-      int sc = 0;
-#pragma unroll
-      for (int p = 0; p < STEPS; ++p) {
-        const uint8_t* base = pc + (m * 4 + p0 + p) * 144;
-        const uint4 lo4 = *reinterpret_cast<const uint4*>(base + 32 * q4);
-        const uint2 hi2 = *reinterpret_cast<const uint2*>(base + 32 * q4 + 16);
-        w.bq[m][p] = mk.live ? i8_t{(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w, (int)hi2.x, (int)hi2.y, 0, 0}
-                             : i8_t{0, 0, 0, 0, 0, 0, 0, 0};
-        sc |= (mk.live ? (int)base[128 + q4] : 127) << (8 * p);
-      }
-      w.bs[m] = sc;
-    }
-    const float2 cst = *reinterpret_cast<const float2*>(pc + kTurboPieceConstOff);
-    w.lc = mk.live && p0 == 0 ? cst.x : 0.f;  // the constant terms once per pair
-    w.qc = mk.live && p0 == 0 ? cst.y : 0.f;
-    w.t_lo = 0;
-    w.t_hi = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t hb = __builtin_bit_cast(uint16_t, (_Float16)a.levels[k]);
-      w.t_lo |= (hb & 0xFFu) << (8 * k);
-      w.t_hi |= (hb >> 8) << (8 * k);
-    }
-  }
-  w.m_run = mk.live ? -INFINITY : 0.f;  // a column past the launch's pairs never moves
-  w.l_run = 0.f;
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt) w.o[nt] = f4_t{0.f, 0.f, 0.f, 0.f};
 
   // resources over nrows token rows from row0 (nrows 0: every read is zeros)
   auto res_at = [&](size_t row0, int nrows) {
@@ -566,8 +523,62 @@ decode_turbo_kernel(TurboDecodeArgs a) {
   // value product of tile i (matrix-core and vector work of one wave overlap),
   // then tile i + 1's softmax.
   const int t_first = t_begin + wave * 32;
+  if constexpr (PAGED || SPARSE) {
 #pragma unroll
-  for (int i = 0; i < kStages - 1; ++i) issue(i, t_first + 128 * i);
+    for (int i = 0; i < kStages - 1; ++i) issue(i, t_first + 128 * i);
+  } else {
+    // A contiguous cache's first tiles are issued before the sequence length
+    // and the query have arrived: a tile past the end is read from the cache's
+    // own rows and never used, and a partial tile's extra tokens are masked.
+#pragma unroll
+    for (int i = 0; i < kStages - 1; ++i) {
+      const int t = t_first + 128 * i;
+      issue_tile<PAIRS>(my_ring + i * kStage, lane, t < a.cap ? t : a.cap, res);
+    }
+  }
+  WaveState<STEPS> w;
+  TileMask mk;
+  constexpr int kCols = STEPS == 2 ? 8 : 16;  // distinct pairs per launch
+  {
+    const int col = c % kCols;
+    const int pair = a.c0 + col;
+    mk.live = col < a.ncol;
+    const int jq = (mk.live ? pair : a.c0) / G, g = (mk.live ? pair : a.c0) % G;
+    mk.t_lo = a.t_lo;
+    mk.lim = min(t_end, L - (a.nq - 1 - jq));
+    const size_t qrow = ((size_t)b * a.nq + jq) * a.Hq + (size_t)h * G + g;
+    const uint8_t* pc = a.qpieces + qrow * kTurboPieceBytes;
+    const int p0 = STEPS == 2 && c >= 8 ? 2 : 0;  // this column's first piece
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+      int sc = 0;
+#pragma unroll
+      for (int p = 0; p < STEPS; ++p) {
+        const uint8_t* base = pc + (m * 4 + p0 + p) * 144;
+        const uint4 lo4 = *reinterpret_cast<const uint4*>(base + 32 * q4);
+        const uint2 hi2 = *reinterpret_cast<const uint2*>(base + 32 * q4 + 16);
+        w.bq[m][p] = mk.live ? i8_t{(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w, (int)hi2.x, (int)hi2.y, 0, 0}
+                             : i8_t{0, 0, 0, 0, 0, 0, 0, 0};
+        sc |= (mk.live ? (int)base[128 + q4] : 127) << (8 * p);
+      }
+      w.bs[m] = sc;
+    }
+    const float2 cst = *reinterpret_cast<const float2*>(pc + kTurboPieceConstOff);
+    w.lc = mk.live && p0 == 0 ? cst.x : 0.f;  // the constant terms once per pair
+    w.qc = mk.live && p0 == 0 ? cst.y : 0.f;
+    w.t_lo = 0;
+    w.t_hi = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t hb = __builtin_bit_cast(uint16_t, (_Float16)a.levels[k]);
+      w.t_lo |= (hb & 0xFFu) << (8 * k);
+      w.t_hi |= (hb >> 8) << (8 * k);
+    }
+  }
+  w.m_run = mk.live ? -INFINITY : 0.f;  // a column past the launch's pairs never moves
+  w.l_run = 0.f;
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) w.o[nt] = f4_t{0.f, 0.f, 0.f, 0.f};
   h8_t pa;        // weights of the tile whose value product is pending
   i2_t vx0, vx1;  // its value codes
   // tile t0 in stage st: refill the stage read last (its reads have completed)

@@ -130,8 +130,11 @@ SplitPlan plan_splits(const kv_layout* L, int num_q_heads, int nq, int q_dtype, 
   // the latent kernel keeps one workgroup per compute unit resident and every
   // split writes Hq x 514 partial floats: one round of workgroups, a few long
   // splits per sequence (4 at batch 64; 8 measured no faster in the kernel and
-  // doubles the partials the merge reads)
-  const long target = latent ? 256 : 2048;
+  // doubles the partials the merge reads).  The streaming matrix-core kernels
+  // keep three workgroups per compute unit resident; FP4 and TurboQuant
+  // measured fastest at about 1,024 workgroups (each one's start and finish
+  // leave its compute unit's share of the stream idle), QJL keys at 2,048.
+  const long target = latent ? 256 : fast && L->format != KV_FMT_QJL1_FP4V ? 1024 : 2048;
   long units = (long)L->batch * L->num_kv_heads;
   if (!fast && !latent && nq * G > 16) units *= (nq * G + 15) / 16;  // the generic kernel's head blocks
   int splits = requested;

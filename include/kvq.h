@@ -158,7 +158,11 @@ typedef struct kv_layout {
  *   K_STAGE  KIVI2 [B][H][4 + 32 d] 32-bit words: word 0 the number of tokens
  *                 appended to the sequence (int32), words 1..3 unused, then as
  *                 f32 [32][d] the keys of its last, incomplete 32-token group
- *                 (token t in row t mod 32), which have no key code yet        */
+ *                 (token t in row t mod 32), which have no key code yet
+ * Decode reads whole 32-token tiles and may read a few tiles past a
+ * sequence's end, giving those slots zero weight: every slot within capacity
+ * (every page of a pool) must hold finite data, as zeroed buffers and appends
+ * of finite inputs do.                                                         */
 enum kv_buffer {
   KV_BUF_K_CODES = 0, KV_BUF_K_SCALE, KV_BUF_K_ZERO, KV_BUF_K_SKETCH, KV_BUF_K_NORM,
   KV_BUF_K_RNORM, KV_BUF_V_CODES, KV_BUF_V_SCALE, KV_BUF_V_ZERO, KV_BUF_V_NORM,
