@@ -398,14 +398,16 @@ __device__ __forceinline__ uint32_t e2m3_code(float y, float& val) {
   const uint32_t sgn = __float_as_uint(y) >> 31;
   const float ay = fabsf(y);
   const float step = ay < 2.f ? 0.125f : (ay < 4.f ? 0.25f : 0.5f);
-  const float qv = __builtin_rintf(ay / step) * step;  // exact quotient, ties to even
+  const float inv = ay < 2.f ? 8.f : (ay < 4.f ? 4.f : 2.f);  // 1 / step, a power of two
+  const float qv = __builtin_rintf(ay * inv) * step;           // exact quotient, ties to even
   val = sgn ? -qv : qv;
   uint32_t mag;
   if (qv < 1.f) {
     mag = (uint32_t)(qv * 8.f);  // exponent field 0
   } else {
     const int e = qv < 2.f ? 1 : (qv < 4.f ? 2 : 3);  // exponent field, bias 1
-    mag = ((uint32_t)e << 3) | (uint32_t)((qv / (float)(1 << (e - 1)) - 1.f) * 8.f);
+    const float unit = e == 1 ? 1.f : (e == 2 ? 0.5f : 0.25f);  // 2^-(e - 1)
+    mag = ((uint32_t)e << 3) | (uint32_t)((qv * unit - 1.f) * 8.f);
   }
   return (sgn << 5) | mag;
 }
@@ -431,6 +433,21 @@ __device__ __forceinline__ uint32_t e2m3_code(float y, float& val) {
 // has threads for.
 // Threads [0, nthr) of the caller's group (tid = index in the group, both
 // multiples of 32 apart from tid's low bits) do the work.
+// Lane exchanges within a 16-lane row by DPP (quad permutations, row rotations).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, false);
+}
+// max of x over the 32 lanes of its half-wave: quad exchanges, two row
+// rotations, then the row pair
+__device__ __forceinline__ float max_half_wave(float x) {
+  x = fmaxf(x, __uint_as_float(dpp_u<0xB1>(__float_as_uint(x))));   // lane ^ 1
+  x = fmaxf(x, __uint_as_float(dpp_u<0x4E>(__float_as_uint(x))));   // lane ^ 2
+  x = fmaxf(x, __uint_as_float(dpp_u<0x124>(__float_as_uint(x))));  // row_ror:4
+  x = fmaxf(x, __uint_as_float(dpp_u<0x128>(__float_as_uint(x))));  // row_ror:8
+  return max_xor16(x);
+}
+
 __device__ void prepared_query_pieces(int nprod, const float* qrot, const float* qsk, float a1, float a2, float ask,
                                       bool fp6, uint8_t* out, int tid, int nthr) {
   const int e = tid & 31, d = e >> 3, n = e & 7;
@@ -444,9 +461,7 @@ __device__ void prepared_query_pieces(int nprod, const float* qrot, const float*
                            : ask * qsk[32 * j + 4 * n + d]);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      float M = fabsf(r);
-#pragma unroll
-      for (int off = 1; off < 32; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+      const float M = max_half_wave(fabsf(r));
       int ex = 0;
       if (M > 0.f) {
         int k;
@@ -461,9 +476,9 @@ __device__ void prepared_query_pieces(int nprod, const float* qrot, const float*
       uint8_t* dst = out + (prod * 4 + p) * 144;
       if (fp6) {
         // elements 4 g .. 4 g + 3 fill the 3 bytes from 3 g: gather them in 2 steps
-        int v = (int)(e2m3_code(ldexpf(r, -ex), val) << (6 * (e & 3)));
-        v |= __shfl_xor(v, 1, 32);
-        v |= __shfl_xor(v, 2, 32);
+        uint32_t v = e2m3_code(ldexpf(r, -ex), val) << (6 * (e & 3));
+        v |= dpp_u<0xB1>(v);  // lane ^ 1
+        v |= dpp_u<0x4E>(v);  // lane ^ 2
         if ((e & 3) == 0) {
           uint8_t* b3 = dst + j * 32 + 3 * (e >> 2);
           b3[0] = (uint8_t)v;
@@ -481,7 +496,8 @@ __device__ void prepared_query_pieces(int nprod, const float* qrot, const float*
 
 // Prepared fp32 query of the formats other than TURBO (prep_turbo_kernel):
 // S q (QJL1), with the FP8 pieces of its key product when `pieces` is given,
-// or q itself.  128 threads; the product takes one output per thread.
+// or q itself.  128 threads; the product takes one output per thread, whose
+// row of S is loaded into registers beside the query.
 template <typename QT>
 __global__ void __launch_bounds__(128) prep_query_kernel(const QT* __restrict__ q, int qw_in, int qw_out, int fmt,
                                                          const float* __restrict__ proj, float* __restrict__ out,
@@ -490,12 +506,31 @@ __global__ void __launch_bounds__(128) prep_query_kernel(const QT* __restrict__ 
   __shared__ float qsr[128];
   const size_t row = blockIdx.x;
   const int tid = threadIdx.x, nthr = blockDim.x;
+  const bool qjl = fmt == KV_FMT_QJL1_FP4V;
+  float4 m[32];
+  if (qjl) {
+    const float4* src = reinterpret_cast<const float4*>(proj + (size_t)tid * 128);
+#pragma unroll
+    for (int j4 = 0; j4 < 32; ++j4) m[j4] = src[j4];
+  }
   for (int c = tid; c < qw_in; c += nthr) qin[c] = load_as_f32(q + row * qw_in, c);
   __syncthreads();
   float* dst = out + row * qw_out;
-  if (fmt == KV_FMT_QJL1_FP4V) {
-    float acc = 0.f;
-    for (int j = 0; j < 128; ++j) acc = fmaf(proj[tid * 128 + j], qin[j], acc);
+  if (qjl) {
+    float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+    for (int j4 = 0; j4 < 32; j4 += 2) {
+      const float4 v = m[j4], u = m[j4 + 1];
+      acc0 = fmaf(v.x, qin[4 * j4], acc0);
+      acc0 = fmaf(v.y, qin[4 * j4 + 1], acc0);
+      acc0 = fmaf(v.z, qin[4 * j4 + 2], acc0);
+      acc0 = fmaf(v.w, qin[4 * j4 + 3], acc0);
+      acc1 = fmaf(u.x, qin[4 * j4 + 4], acc1);
+      acc1 = fmaf(u.y, qin[4 * j4 + 5], acc1);
+      acc1 = fmaf(u.z, qin[4 * j4 + 6], acc1);
+      acc1 = fmaf(u.w, qin[4 * j4 + 7], acc1);
+    }
+    const float acc = acc0 + acc1;
     dst[tid] = acc;
     qsr[tid] = acc;
     if (pieces) {
@@ -530,6 +565,7 @@ __global__ void __launch_bounds__(kTurboPrepThreads) prep_turbo_kernel(
   const size_t row = blockIdx.x;
   const bool prod = tid < 128;
   if (prod) qin[tid] = load_as_f32(q + row * 128, tid);
+  const float lv0 = levels[0], lv1 = levels[1], lv2 = levels[2], lv3 = levels[3];
   __syncthreads();
   auto matvec = [&](const float* __restrict__ m, const float* x) {
     const float4* mr = reinterpret_cast<const float4*>(m + (size_t)tid * 128);
@@ -562,7 +598,6 @@ __global__ void __launch_bounds__(kTurboPrepThreads) prep_turbo_kernel(
   }
   if (!pieces) return;  // uniform across the workgroup
   __syncthreads();
-  const float lv0 = levels[0], lv1 = levels[1], lv2 = levels[2], lv3 = levels[3];
   uint8_t* pr = pieces + row * kTurboPieceBytes;
   prepared_query_pieces(3, qrot, qsr, (lv2 - lv0) * scale_log2, (lv1 - lv0) * scale_log2, 2.f * kappa * scale_log2,
                         true, pr, tid, kTurboPrepThreads);
