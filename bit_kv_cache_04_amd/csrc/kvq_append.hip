@@ -619,6 +619,14 @@ __device__ __forceinline__ void qjl_key_tile(const KeyFrag<InT>& fr, size_t base
   // the C tiles, lanes 16 (t >> 2) .. 16 (t >> 2) + 15 of each ballot.
   uint32_t words[4] = {0u, 0u, 0u, 0u};
   const int my_q = (lane >> 2) & 3, my_i = lane & 3;
+  // the norms and validity of the tokens 4 kq + i whose C rows this lane holds
+  float tn[4];
+  bool tvalid[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    tn[i] = (float)__shfl(nrm, kq * 4 + i);
+    tvalid[i] = base + kq * 4 + i < rows;
+  }
   // S rows in two halves of 64 (n-tiles 4 hf .. 4 hf + 3), sketch words 2 hf, 2 hf + 1
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
@@ -639,38 +647,50 @@ __device__ __forceinline__ void qjl_key_tile(const KeyFrag<InT>& fr, size_t base
           acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[p], b, acc[nt], 0, 0, 0);
       }
     }
+    // bit 4 i + nt of sgn: the sign bit of element (token 4 kq + i, S row
+    // (4 hf + nt) 16 + col); of close: the element lies within the accumulation
+    // error bound of zero, and its sign is then recomputed in fp64 (the whole
+    // wave takes part, one element at a time)
+    uint32_t close = 0u, sgn = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        close |= (fabsf(acc[nt][i]) <= sbound[4 * hf + nt] * tn[i] && tvalid[i] ? 1u : 0u) << (4 * i + nt);
+        sgn |= (acc[nt][i] >= 0.f ? 1u : 0u) << (4 * i + nt);
+      }
+    if (__ballot(close != 0u)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          unsigned long long todo = __ballot((close >> (4 * i + nt)) & 1u);
+          while (todo) {
+            const int src = __builtin_ctzll(todo);
+            todo &= todo - 1;
+            const int ct = (src >> 4) * 4 + i;               // token of that element
+            const int sr = (4 * hf + nt) * 16 + (src & 15);  // its row of S
+            double e = 0.0;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+              const uint4 sw = *reinterpret_cast<const uint4*>(&S_lds[sr * kSPad + ks * 32 + kq * 8]);
+              const uint32_t w[4] = {sw.x, sw.y, sw.z, sw.w};
+#pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                const float sv = __uint_as_float((j & 1) ? (w[j >> 1] & 0xFFFF0000u) : (w[j >> 1] << 16));
+                e = fma((double)sv, (double)fr.value(ks, j), e);
+              }
+            }
+            const double tot = (__shfl(e, ct) + __shfl(e, ct + 16)) + (__shfl(e, ct + 32) + __shfl(e, ct + 48));
+            if (lane == src) sgn = (sgn & ~(1u << (4 * i + nt))) | ((tot >= 0.0 ? 1u : 0u) << (4 * i + nt));
+          }
+        }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       unsigned long long bal[4];
-      const int tok = kq * 4 + i;  // C-operand rows held by this lane
-      const float tn = (float)__shfl(nrm, tok);
-      const bool tvalid = base + tok < rows;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const float y = acc[nt][i];
-        bool bit = y >= 0.f;
-        unsigned long long close = __ballot(fabsf(y) <= sbound[4 * hf + nt] * tn && tvalid);
-        while (close) {
-          const int src = __builtin_ctzll(close);
-          close &= close - 1;
-          const int ct = (src >> 4) * 4 + i;  // token of that element
-          const int sr = (4 * hf + nt) * 16 + (src & 15);  // its row of S
-          double e = 0.0;
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const uint4 sw = *reinterpret_cast<const uint4*>(&S_lds[sr * kSPad + ks * 32 + kq * 8]);
-            const uint32_t w[4] = {sw.x, sw.y, sw.z, sw.w};
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const float sv = __uint_as_float((j & 1) ? (w[j >> 1] & 0xFFFF0000u) : (w[j >> 1] << 16));
-              e = fma((double)sv, (double)fr.value(ks, j), e);
-            }
-          }
-          const double tot = (__shfl(e, ct) + __shfl(e, ct + 16)) + (__shfl(e, ct + 32) + __shfl(e, ct + 48));
-          if (lane == src) bit = tot >= 0.0;
-        }
-        bal[nt] = __ballot(bit);
-      }
+      for (int nt = 0; nt < 4; ++nt) bal[nt] = __ballot((sgn >> (4 * i + nt)) & 1u);
       if (my_i == i) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
