@@ -591,11 +591,13 @@ __device__ __forceinline__ void stage_bf16_matrix(const float* __restrict__ m, u
 
 // Keys of one wave's 16 tokens [base, base + 16): sketch bit i = [(S k)_i >= 0]
 // and the token's fp16 norm.  C = K_tile S^T on v_mfma_f32_16x16x32_bf16 (S^T
-// read from LDS, fp32 accumulation of exact products).  Where |y| is within a
-// conservative bound of the fp32 accumulation error (2^-14 ||S_i|| ||k||; 2^-12
-// for three slices), about one element in 2^11, the sign is recomputed in fp64
-// from the registers: each of the token's four lanes sums its 32 products and
-// the four partial sums are added.
+// read from LDS, fp32 accumulation of exact products).  Summing n exact
+// products in fp32, in any order and grouping, errs by at most (n - 1) 2^-24
+// sum_j |s_j k_j| <= (n - 1) 2^-24 ||S_i|| ||k|| (twice that if every addition
+// truncated): 2^-17 ||S_i|| ||k|| for n = 128.  Where |y| is within 2^-15
+// ||S_i|| ||k|| of zero (2^-12 for three slices, n = 384), about one element
+// in 2^12, the sign is recomputed in fp64 from the registers: each of the
+// token's four lanes sums its 32 products and the four partial sums are added.
 template <typename InT>
 __device__ __forceinline__ void qjl_key_tile(const KeyFrag<InT>& fr, size_t base, size_t rows,
                                              const uint16_t* S_lds, const float (&sbound)[8], size_t my_dst,
@@ -749,7 +751,7 @@ qjl_append_kernel(const InT* __restrict__ k, const InT* __restrict__ v,
   float sbound[8];
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt)
-    sbound[nt] = (KeyFrag<InT>::NP == 1 ? 0x1p-14f : 0x1p-12f) * srow_norm[nt * 16 + (lane & 15)];
+    sbound[nt] = (KeyFrag<InT>::NP == 1 ? 0x1p-15f : 0x1p-12f) * srow_norm[nt * 16 + (lane & 15)];
   const size_t tiles = (rows + 63) / 64;
   const size_t vgroups = rows * 8;
   for (size_t t = blockIdx.x; t < tiles; t += gridDim.x) {
