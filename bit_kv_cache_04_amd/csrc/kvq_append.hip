@@ -589,6 +589,27 @@ __device__ __forceinline__ void stage_bf16_matrix(const float* __restrict__ m, u
   }
 }
 
+// x of lane l plus x of lane l ^ 16 (ROW = 16) or l ^ 32 (ROW = 32), in
+// registers (v_permlane16_swap / v_permlane32_swap of each half with itself
+// leaves the two lanes' halves in the two results, in either order).
+template <int ROW>
+__device__ __forceinline__ double add_swapped(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+  uint32_t a0, a1, b0, b1;
+  if constexpr (ROW == 16) {
+    const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    a0 = l[0]; a1 = l[1]; b0 = h[0]; b1 = h[1];
+  } else {
+    const auto l = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto h = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    a0 = l[0]; a1 = l[1]; b0 = h[0]; b1 = h[1];
+  }
+  return __builtin_bit_cast(double, (uint64_t)a0 | ((uint64_t)b0 << 32)) +
+         __builtin_bit_cast(double, (uint64_t)a1 | ((uint64_t)b1 << 32));
+}
+
 // Keys of one wave's 16 tokens [base, base + 16): sketch bit i = [(S k)_i >= 0]
 // and the token's fp16 norm.  C = K_tile S^T on v_mfma_f32_16x16x32_bf16 (S^T
 // read from LDS, fp32 accumulation of exact products).  Summing n exact
@@ -683,8 +704,13 @@ __device__ __forceinline__ void qjl_key_tile(const KeyFrag<InT>& fr, size_t base
                 e = fma((double)sv, (double)fr.value(ks, j), e);
               }
             }
-            const double tot = (__shfl(e, ct) + __shfl(e, ct + 16)) + (__shfl(e, ct + 32) + __shfl(e, ct + 48));
-            if (lane == src) sgn = (sgn & ~(1u << (4 * i + nt))) | ((tot >= 0.0 ? 1u : 0u) << (4 * i + nt));
+            // each lane: its token's four partial sums, (q0 + q1) + (q2 + q3);
+            // token ct's is read from lane ct
+            const double tot = add_swapped<32>(add_swapped<16>(e));
+            const uint32_t tlo = __builtin_amdgcn_readlane((uint32_t)__builtin_bit_cast(uint64_t, tot), ct);
+            const uint32_t thi = __builtin_amdgcn_readlane((uint32_t)(__builtin_bit_cast(uint64_t, tot) >> 32), ct);
+            const double tct = __builtin_bit_cast(double, (uint64_t)tlo | ((uint64_t)thi << 32));
+            if (lane == src) sgn = (sgn & ~(1u << (4 * i + nt))) | ((tct >= 0.0 ? 1u : 0u) << (4 * i + nt));
           }
         }
     }
