@@ -660,6 +660,28 @@ __global__ void __launch_bounds__(64 * merge_max_waves<NJ>()) merge_kernel(const
   const size_t row = blockIdx.x;
   const size_t stride = (size_t)dv + 2;
   const float* p = part + row * (size_t)splits * stride;
+  const bool turbo = fmt == KV_FMT_TURBO;
+  const int s_rot = turbo ? rot_splits : splits;
+  const int c0 = CW * blockIdx.y;
+  const float* pc = p + 2 + c0 + NJ * lane;  // 8-byte aligned: rows and the header are even
+  // this wave's first PF splits' outputs (s = wave + W k below s_rot), loaded
+  // beside the (m, l) pairs instead of after the weights
+  constexpr int PF = 32 / NJ;
+  float pre[PF][NJ];
+#pragma unroll
+  for (int k = 0; k < PF; ++k) {
+    const int s = wave + k * W;
+#pragma unroll
+    for (int j = 0; j < NJ; j += (NJ == 1 ? 1 : 2)) {
+      if constexpr (NJ == 1) {
+        pre[k][0] = s < s_rot ? pc[s * stride] : 0.f;
+      } else {
+        const float2 v = s < s_rot ? *reinterpret_cast<const float2*>(pc + s * stride + j) : float2{0.f, 0.f};
+        pre[k][j] = v.x;
+        pre[k][j + 1] = v.y;
+      }
+    }
+  }
   float M = -INFINITY;
   for (int s = tid; s < splits; s += nthr) {
     const float2 ml = *reinterpret_cast<const float2*>(p + s * stride);
@@ -687,15 +709,25 @@ __global__ void __launch_bounds__(64 * merge_max_waves<NJ>()) merge_kernel(const
   l = red_l[0];
   for (int i = 1; i < W; ++i) l += red_l[i];
   const float inv_l = l > 0.f ? 1.f / l : 0.f;
-  const int c0 = CW * blockIdx.y;
-  const float* pc = p + 2 + c0 + NJ * lane;  // 8-byte aligned: rows and the header are even
   constexpr int kMergeUnroll = 16 / NJ;
-  // weighted sum of the splits s0, s0 + W, ... below s1 for this lane's columns
-  auto weighted = [&](int s0, int s1, float (&acc)[NJ]) {
+  // weighted sum of the splits s0, s0 + W, ... below s1 for this lane's
+  // columns, in that order (the first PF from the prefetched values if pre)
+  auto weighted = [&](int s0, int s1, float (&acc)[NJ], bool use_pre) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[j] = 0.f;
+    int s = s0;
+    if (use_pre) {
+#pragma unroll
+      for (int k = 0; k < PF; ++k, s += W) {
+        if (s < s1) {
+          const float ws = sm_w[s];
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) acc[j] = fmaf(ws, pre[k][j], acc[j]);
+        }
+      }
+    }
 #pragma unroll kMergeUnroll
-    for (int s = s0; s < s1; s += W) {
+    for (; s < s1; s += W) {
       const float ws = sm_w[s];
       if constexpr (NJ == 1) {
         acc[0] = fmaf(ws, pc[s * stride], acc[0]);
@@ -709,16 +741,14 @@ __global__ void __launch_bounds__(64 * merge_max_waves<NJ>()) merge_kernel(const
       }
     }
   };
-  const bool turbo = fmt == KV_FMT_TURBO;
-  const int s_rot = turbo ? rot_splits : splits;
   {
     float acc[NJ];
-    weighted(wave, s_rot, acc);
+    weighted(wave, s_rot, acc, true);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) sums[wave][NJ * lane + j] = acc[j];
     if constexpr (kTurboCols) {
       if (turbo) {
-        weighted(s_rot + wave, splits, acc);
+        weighted(s_rot + wave, splits, acc, false);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) sums_o[wave][NJ * lane + j] = acc[j];
       }
