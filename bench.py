@@ -51,7 +51,7 @@ CPU_SAMPLE_TOKENS = 131072    # context of the CPU oracle's decode sample (whole
 
 # the arithmetic each workload's attention kernel computes in
 DTYPE = {
-    "kivi2": "fp32 (vector ALU)",
+    "kivi2": "fp16 MFMA operands (codes exact, query x scale as an fp16 pair, values rounded once), fp32 accumulate and softmax",
     "fp4": "fp16 MFMA operands (E2M1 x bf16 scale exact), fp32 accumulate and softmax",
     "turbo": "fp4 x fp6 and fp16 MFMA operands, fp32 accumulate and softmax",
     "qjl1": "fp4 x fp8 and fp16 MFMA operands, fp32 accumulate and softmax",

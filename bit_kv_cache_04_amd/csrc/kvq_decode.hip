@@ -1093,7 +1093,7 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     // one launch per 16 (query, head) pairs of a KV head, each over the whole cache
     for (f.c0 = 0; f.c0 < nq * f.gr; f.c0 += 16) {
       f.ncol = std::min(16, nq * f.gr - f.c0);
-      int rc = launch_decode_kivi(f, B, st);
+      int rc = launch_decode_kivi(f, L.head_dim, B, st);
       if (rc != KV_OK) return rc;
     }
     launch_kivi_tail(a, tail_split, B, st);

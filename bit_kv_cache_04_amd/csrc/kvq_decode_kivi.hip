@@ -1,8 +1,8 @@
-// Decode attention on the matrix cores (gfx950) for KIVI-2 caches with 128
-// channels: keys quantised per channel over groups of 32 tokens, values per
-// token over groups of 32 channels, 2-bit codes with fp32 scale and zero (page
-// "TurboQuant vs OSCAR vs EpiCache", section "quantization frontiers", KIVI
-// paragraph).
+// Decode attention on the matrix cores (gfx950) for KIVI-2 caches with D = 64
+// or 128 channels: keys quantised per channel over groups of 32 tokens, values
+// per token over groups of 32 channels, 2-bit codes with fp32 scale and zero
+// (page "TurboQuant vs OSCAR vs EpiCache", section "quantization frontiers",
+// KIVI paragraph).
 //
 // One workgroup = 4 waves over one (sequence, KV head, context split); each
 // wave streams its own 32-token tiles (one key group each) from HBM into a
@@ -10,16 +10,17 @@
 // softmax of 16 (query, head) columns.  Per tile and wave:
 //   keys    S_t = sum_c (q_c s_c) code_tc + sum_c q_c z_c for the group's scale
 //           s and zero z.  The codes (0..3) are exact fp16 operands, q_c s_c an
-//           exact fp16 hi + lo pair: 16 v_mfma_f32_16x16x32_f16 (rows = tokens,
-//           columns = heads); the zero term is an fp32 sum per column.
+//           exact fp16 hi + lo pair: D / 8 v_mfma_f32_16x16x32_f16 (rows =
+//           tokens, columns = heads); the zero term is an fp32 sum per column.
 //   softmax per column = per lane column, the reference max moving only when
 //           a tile max passes it by 2^8.
 //   values  v_tc = code_tc s_t + z_t for the token's 32-channel group, made in
-//           fp16 (one rounding) as the B operand of 8 PV products.
+//           fp32 and rounded once to fp16 (nearest) as the B operand of D / 16
+//           PV products.
 // With fewer than 16 (query, head) pairs per launch the 16 columns carry each
-// pair S = 16 / P times (P pair slots), column c taking pair c % P over the
-// channel part c / P only, and rotations within each 16-lane row add the
-// parts: each lane scales 128 / S query channels per tile instead of 128.
+// pair S = 16 / P times (P pair slots, S at most D / 32), column c taking pair
+// c % P over the channel part c / P only, and rotations within each 16-lane row
+// add the parts: each lane scales D / S query channels per tile instead of D.
 // Tokens of a sequence's incomplete last group are not coded yet (their keys
 // wait in staging); the general kernel takes them as one more split.
 #include <hip/hip_runtime.h>
@@ -38,17 +39,19 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 namespace {
 
 constexpr int kRsrcFlags = 0x00020000;
-constexpr int kD = 128;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, size_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcFlags);
 }
 
-// Stage of one 32-token tile (bytes): key codes (32 B per token row), the
-// group's 128 key scales and zeros, value codes, and the tokens' value scales
-// and zeros (4 per token).
-constexpr int kKc = 0, kKs = 1024, kKz = 1536, kVc = 2048, kVs = 3072, kVz = 3584, kStage = 4096;
-constexpr int kDma = 10;  // direct-to-LDS loads per tile
+// Stage of one 32-token tile of a D-channel cache (bytes): key codes (D / 4 per
+// token row), the group's D key scales and zeros, value codes, and the tokens'
+// value scales and zeros (D / 32 per token).
+template <int D>
+struct Stage {
+  static constexpr int kKc = 0, kKs = 8 * D, kKz = 12 * D, kVc = 16 * D, kVs = 24 * D, kVz = 28 * D, kBytes = 32 * D;
+  static constexpr int kDma = D == 128 ? 10 : 8;  // direct-to-LDS loads per tile
+};
 
 struct Res {
   __amdgpu_buffer_rsrc_t kc, ks, kz, vc, vs, vz;
@@ -56,19 +59,29 @@ struct Res {
 
 // The tile from token t0 (a multiple of 32; t0 = capacity: no tile, every load
 // reads past its resource and writes zeros): lane l moves bytes [s l, s l + s)
-// of each chunk.
+// of each chunk (D = 128: 16-byte code chunks; D = 64: 4-byte pieces throughout).
+template <int D>
 __device__ __forceinline__ void issue_tile(uint8_t* st, int lane, int t0, const Res& r) {
-  const int co = t0 * 32 + lane * 16, go = (t0 >> 5) * 512 + lane * 4, vo = t0 * 16 + lane * 4;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.kc, (lds_ptr_t)(st + kKc), 16, co, 0, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.ks, (lds_ptr_t)(st + kKs), 4, go, 0, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.ks, (lds_ptr_t)(st + kKs + 256), 4, go + 256, 0, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.kz, (lds_ptr_t)(st + kKz), 4, go, 0, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.kz, (lds_ptr_t)(st + kKz + 256), 4, go + 256, 0, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vc, (lds_ptr_t)(st + kVc), 16, co, 0, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vs, (lds_ptr_t)(st + kVs), 4, vo, 0, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vs, (lds_ptr_t)(st + kVs + 256), 4, vo + 256, 0, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vz, (lds_ptr_t)(st + kVz), 4, vo, 0, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vz, (lds_ptr_t)(st + kVz + 256), 4, vo + 256, 0, 0, 0);
+  using G = Stage<D>;
+  const int go = (t0 >> 5) * (4 * D) + lane * 4, vo = t0 * (D / 8) + lane * 4;
+  if constexpr (D == 128) {
+    const int co = t0 * 32 + lane * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.kc, (lds_ptr_t)(st + G::kKc), 16, co, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vc, (lds_ptr_t)(st + G::kVc), 16, co, 0, 0, 0);
+  } else {
+    const int co = t0 * 16 + lane * 4;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.kc, (lds_ptr_t)(st + G::kKc), 4, co, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.kc, (lds_ptr_t)(st + G::kKc + 256), 4, co + 256, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vc, (lds_ptr_t)(st + G::kVc), 4, co, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vc, (lds_ptr_t)(st + G::kVc + 256), 4, co + 256, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) {  // 4 D bytes each: 256 per load
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.ks, (lds_ptr_t)(st + G::kKs + 256 * i), 4, go + 256 * i, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.kz, (lds_ptr_t)(st + G::kKz + 256 * i), 4, go + 256 * i, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vs, (lds_ptr_t)(st + G::kVs + 256 * i), 4, vo + 256 * i, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.vz, (lds_ptr_t)(st + G::kVz + 256 * i), 4, vo + 256 * i, 0, 0, 0);
+  }
 }
 
 // Codes 0..3 in nibbles as the exact fp16 values: an E2M1 nibble 0..3 is
@@ -112,44 +125,48 @@ __device__ __forceinline__ float row_fetch(float x) {
 }
 
 // Everything one wave carries across tiles.
+template <int D>
 struct WaveState {
-  float q[4][8];  // prepared query of the lane's column: its part's k-steps kp, channels 32 kk + 8 q4 + i
+  float q[D / 32][8];  // prepared query of the lane's column: its part's k-steps kp, channels 32 kk + 8 q4 + i
   float m_run, l_run;
-  f4_t o[8];      // O rows = columns 4 q4 + v; N-tile nt = channels 8 c + nt
+  f4_t o[D / 16];      // O rows = columns 4 q4 + v; N-tile nt = channels (D / 16) c + nt
 };
 
 // One tile: read this lane's fragments from the stage, refill the stage from
 // tile `next` once the reads have returned, then compute.  lim: the lane
 // column's token limit; t_full: a tile below it is whole for every column.
 // S: channel parts per pair (column c: pair c % (16 / S), k-steps of part c / (16 / S)).
-template <int S>
-__device__ __forceinline__ void tile_step(WaveState& w, uint8_t* st, int lane, int t0, int t_full, int lim, int next,
-                                          const Res& r, const MfmaDecodeArgs& a) {
-  constexpr int P = 16 / S, KP = 4 / S;  // pair slots, k-steps per part
+template <int D, int S>
+__device__ __forceinline__ void tile_step(WaveState<D>& w, uint8_t* st, int lane, int t0, int t_full, int lim,
+                                          int next, const Res& r, const MfmaDecodeArgs& a) {
+  using G = Stage<D>;
+  constexpr int NK = D / 32, NT = D / 16, CL = D / 16;  // k-steps, value N-tiles, value channels per lane
+  constexpr int P = 16 / S, KP = NK / S;                  // pair slots, k-steps per part
+  static_assert(KP >= 1, "a part holds at least one k-step");
   const int q4 = lane >> 4, c = lane & 15;
   const int part = c / P;
   const int pc = c % P;
   // This stage's tile has landed once at most the other stage's refill is
   // outstanding (explicit: the compiler's own wait for loads into LDS is not
   // placed reliably across the loop back-edge).
-  static_assert(kDma < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | kDma);
+  static_assert(G::kDma < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | G::kDma);
   // key codes: row c of block blk, channels 32 kk + 8 q4 + [0, 8) (bytes 8 kk + 2 q4, +1)
-  uint32_t kx[2][4];
+  uint32_t kx[2][NK];
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
-    int ko = (16 * blk + row_token(c)) * 32 + 2 * q4;
+    int ko = (16 * blk + row_token(c)) * (D / 4) + 2 * q4;
     asm volatile("" : "+v"(ko));
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) kx[blk][kk] = *reinterpret_cast<const uint16_t*>(st + kKc + ko + 8 * kk);
+    for (int kk = 0; kk < NK; ++kk) kx[blk][kk] = *reinterpret_cast<const uint16_t*>(st + G::kKc + ko + 8 * kk);
   }
   // the group's key scales and zeros of the lane's channels: 8 per k-step of its part
   float ks[KP][8], kz[KP][8];
 #pragma unroll
   for (int kk = 0; kk < KP; ++kk) {
     const int ch = 32 * (KP * part + kk) + 8 * q4;
-    const float4* ps = reinterpret_cast<const float4*>(st + kKs + 4 * ch);
-    const float4* pz = reinterpret_cast<const float4*>(st + kKz + 4 * ch);
+    const float4* ps = reinterpret_cast<const float4*>(st + G::kKs + 4 * ch);
+    const float4* pz = reinterpret_cast<const float4*>(st + G::kKz + 4 * ch);
     const float4 s0 = ps[0], s1 = ps[1], z0 = pz[0], z1 = pz[1];
     ks[kk][0] = s0.x; ks[kk][1] = s0.y; ks[kk][2] = s0.z; ks[kk][3] = s0.w;
     ks[kk][4] = s1.x; ks[kk][5] = s1.y; ks[kk][6] = s1.z; ks[kk][7] = s1.w;
@@ -157,26 +174,29 @@ __device__ __forceinline__ void tile_step(WaveState& w, uint8_t* st, int lane, i
     kz[kk][4] = z1.x; kz[kk][5] = z1.y; kz[kk][6] = z1.z; kz[kk][7] = z1.w;
   }
   // the lane's 8 tokens j (tile row 16 (j / 4) + 4 (j % 4) + q4): value codes of
-  // channels 8 c .. 8 c + 7 (bytes 2 c, 2 c + 1) and the scale and zero of their group c / 4
+  // channels CL c .. CL c + CL - 1 (CL / 4 bytes from CL c / 4) and the scale and
+  // zero of their group CL c / 32
   uint32_t vx[8];
   float vs[8], vz[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int tok = 16 * (j >> 2) + 4 * (j & 3) + q4;
-    vx[j] = *reinterpret_cast<const uint16_t*>(st + kVc + tok * 32 + 2 * c);
-    vs[j] = *reinterpret_cast<const float*>(st + kVs + tok * 16 + 4 * (c >> 2));
-    vz[j] = *reinterpret_cast<const float*>(st + kVz + tok * 16 + 4 * (c >> 2));
+    if constexpr (CL == 8) vx[j] = *reinterpret_cast<const uint16_t*>(st + G::kVc + tok * (D / 4) + 2 * c);
+    else vx[j] = st[G::kVc + tok * (D / 4) + c];
+    const int vg = tok * (D / 8) + 4 * ((CL * c) >> 5);
+    vs[j] = *reinterpret_cast<const float*>(st + G::kVs + vg);
+    vz[j] = *reinterpret_cast<const float*>(st + G::kVz + vg);
   }
   // the reads above must have returned before the stage is overwritten
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  issue_tile(st, lane, next, r);
+  issue_tile<D>(st, lane, next, r);
 
   // ---------------- keys: B = q s as an fp16 hi + lo pair, A = the codes.  The
   // lane scales its part's k-steps only (the others hold zeros): k-step kk of
   // part u is kk = KP u + kp.
-  h8_t bh[4], bl[4];
+  h8_t bh[NK], bl[NK];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
+  for (int kk = 0; kk < NK; ++kk) {
     bh[kk] = h8_t{};
     bl[kk] = h8_t{};
   }
@@ -198,7 +218,7 @@ __device__ __forceinline__ void tile_step(WaveState& w, uint8_t* st, int lane, i
     }
   }
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
+  for (int kk = 0; kk < NK; ++kk) {
     if (kk / KP == part) {  // place the part's operands at their k-steps
       bh[kk] = ph[kk % KP];
       bl[kk] = pl[kk % KP];
@@ -211,7 +231,7 @@ __device__ __forceinline__ void tile_step(WaveState& w, uint8_t* st, int lane, i
   for (int blk = 0; blk < 2; ++blk) {
     f4_t acc = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < NK; ++kk) {
       const h8_t A = codes8(kx[blk][kk]);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bh[kk], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bl[kk], acc, 0, 0, 0);
@@ -270,62 +290,71 @@ __device__ __forceinline__ void tile_step(WaveState& w, uint8_t* st, int lane, i
     for (int v = 0; v < 4; ++v) {
       const float av = __shfl(alpha, (4 * q4 + v) & 15);
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) w.o[nt][v] *= av;
+      for (int nt = 0; nt < NT; ++nt) w.o[nt][v] *= av;
     }
   }
 
-  // ---------------- values: B of N-tile nt = channel 8 c + nt over the lane's 8 tokens.
-  // e_j byte k = nibble k of token j's 16 bits (channels 8c + 2k, 8c + 2k + 1);
-  // X[p] byte k pairs channel 8c + 2k of tokens 2p and 2p + 1, Y[p] channel 8c + 2k + 1.
+  // ---------------- values: B of N-tile nt = channel CL c + nt over the lane's 8 tokens.
+  // e_j byte k = nibble k of token j's codes (channels CL c + 2k, CL c + 2k + 1);
+  // X[p] byte k pairs channel CL c + 2k of tokens 2p and 2p + 1, Y[p] channel CL c + 2k + 1.
   uint32_t X[4], Y[4];
-  h2_t s2[4], z2[4];
+  auto nibble_bytes = [](uint32_t x) {
+    if constexpr (CL == 8) {
+      const uint32_t t = (x | (x << 8)) & 0x00FF00FFu;
+      return (t | (t << 4)) & 0x0F0F0F0Fu;
+    } else {
+      return (x | (x << 4)) & 0x0F0Fu;
+    }
+  };
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    uint32_t e0 = (vx[2 * p] | (vx[2 * p] << 8)) & 0x00FF00FFu;
-    e0 = (e0 | (e0 << 4)) & 0x0F0F0F0Fu;
-    uint32_t e1 = (vx[2 * p + 1] | (vx[2 * p + 1] << 8)) & 0x00FF00FFu;
-    e1 = (e1 | (e1 << 4)) & 0x0F0F0F0Fu;
+    const uint32_t e0 = nibble_bytes(vx[2 * p]), e1 = nibble_bytes(vx[2 * p + 1]);
     X[p] = (e0 & 0x03030303u) | ((e1 & 0x03030303u) << 4);
     Y[p] = ((e0 >> 2) & 0x03030303u) | ((e1 << 2) & 0x30303030u);
-    s2[p] = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(vs[2 * p], vs[2 * p + 1]));
-    z2[p] = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(vz[2 * p], vz[2 * p + 1]));
   }
+  // tokens 2 p, 2 p + 1 of byte K of x: code s + z in fp32, rounded once to fp16
+  auto vpair = [&](uint32_t x, int p, auto K) {
+    const auto c2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 2.0f, decltype(K)::value);
+    h2_t r;
+    r[0] = (_Float16)__builtin_fmaf(c2[0], vs[2 * p], vz[2 * p]);
+    r[1] = (_Float16)__builtin_fmaf(c2[1], vs[2 * p + 1], vz[2 * p + 1]);
+    return r;
+  };
 #define KVQ_KIVI_PV(K)                                                                                          \
   {                                                                                                             \
-    const h8_t bx = h8_from(__builtin_elementwise_fma(code_pair<K>(X[0]), s2[0], z2[0]),                        \
-                            __builtin_elementwise_fma(code_pair<K>(X[1]), s2[1], z2[1]),                        \
-                            __builtin_elementwise_fma(code_pair<K>(X[2]), s2[2], z2[2]),                        \
-                            __builtin_elementwise_fma(code_pair<K>(X[3]), s2[3], z2[3]));                       \
+    constexpr std::integral_constant<int, K> k{};                                                               \
+    const h8_t bx = h8_from(vpair(X[0], 0, k), vpair(X[1], 1, k), vpair(X[2], 2, k), vpair(X[3], 3, k));        \
     w.o[2 * K] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, bx, w.o[2 * K], 0, 0, 0);                           \
-    const h8_t by = h8_from(__builtin_elementwise_fma(code_pair<K>(Y[0]), s2[0], z2[0]),                        \
-                            __builtin_elementwise_fma(code_pair<K>(Y[1]), s2[1], z2[1]),                        \
-                            __builtin_elementwise_fma(code_pair<K>(Y[2]), s2[2], z2[2]),                        \
-                            __builtin_elementwise_fma(code_pair<K>(Y[3]), s2[3], z2[3]));                       \
+    const h8_t by = h8_from(vpair(Y[0], 0, k), vpair(Y[1], 1, k), vpair(Y[2], 2, k), vpair(Y[3], 3, k));        \
     w.o[2 * K + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, by, w.o[2 * K + 1], 0, 0, 0);                   \
   }
   KVQ_KIVI_PV(0)
   KVQ_KIVI_PV(1)
-  KVQ_KIVI_PV(2)
-  KVQ_KIVI_PV(3)
+  if constexpr (CL == 8) {
+    KVQ_KIVI_PV(2)
+    KVQ_KIVI_PV(3)
+  }
 #undef KVQ_KIVI_PV
   // keep the scheduler from interleaving two tiles (register pressure)
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int S>
+template <int D, int S>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_kivi_kernel(MfmaDecodeArgs a) {
-  constexpr int P = 16 / S, KP = 4 / S;  // pair slots, k-steps per channel part
+  constexpr int NK = D / 32, NT = D / 16, CL = D / 16;  // k-steps, value N-tiles, value channels per lane
+  constexpr int P = 16 / S, KP = NK / S;                  // pair slots, k-steps per channel part
   // LDS stages per wave, as separate arrays so that the compiler can tell which
   // stage a direct-to-LDS load writes
-  __shared__ __attribute__((aligned(16))) uint8_t stA[4][kStage];
-  __shared__ __attribute__((aligned(16))) uint8_t stB[4][kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t stA[4][Stage<D>::kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t stB[4][Stage<D>::kBytes];
   // the waves' running max / sum are combined through stage-B memory, their
-  // outputs through stage-A memory, 8 columns x 128 floats per wave at a time
-  float (*sm_o)[8][128] = reinterpret_cast<float (*)[8][128]>(&stA[0][0]);
+  // outputs through stage-A memory, 8 columns x D floats per wave at a time
+  float (*sm_o)[8][D] = reinterpret_cast<float (*)[8][D]>(&stA[0][0]);
   float (*sm_m)[16] = reinterpret_cast<float (*)[16]>(&stB[0][0]);
   float (*sm_l)[16] = reinterpret_cast<float (*)[16]>(&stB[0][0] + 4 * 16 * sizeof(float));
-  static_assert(sizeof(float) * 4 * 8 * 128 <= sizeof(stA), "stage A too small");
+  static_assert(sizeof(float) * 4 * 8 * D <= sizeof(stA), "stage A too small");
+  static_assert(2 * 4 * 16 * sizeof(float) <= sizeof(stB), "stage B too small");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -333,7 +362,7 @@ decode_kivi_kernel(MfmaDecodeArgs a) {
   const size_t bh = (size_t)b * a.H + h;
   const int L = min(min(a.seq_lens[b], a.max_len), a.cap);
   // the coded tokens end at the first token of the incomplete group
-  const int kstage = reinterpret_cast<const int*>(a.k_stage)[bh * (4 + 32 * kD)] & ~31;
+  const int kstage = reinterpret_cast<const int*>(a.k_stage)[bh * (4 + 32 * D)] & ~31;
   const int t_begin = split * a.per_split;
   const int t_end = min(min(L, kstage), t_begin + a.per_split);
   // column c is (query j, head g) pair c0 + c % P; query j sees the first L - (nq - 1 - j) tokens
@@ -347,12 +376,12 @@ decode_kivi_kernel(MfmaDecodeArgs a) {
   // of a resource returns zeros instead of faulting (a missing tile reads past
   // the end).
   const size_t row0 = bh * a.cap;
-  const Res r{rsrc(a.k_codes + row0 * 32, (size_t)a.cap * 32),
-              rsrc(reinterpret_cast<const uint8_t*>(a.k_scale_f) + row0 / 32 * 512, (size_t)a.cap / 32 * 512),
-              rsrc(reinterpret_cast<const uint8_t*>(a.k_zero_f) + row0 / 32 * 512, (size_t)a.cap / 32 * 512),
-              rsrc(a.v_codes + row0 * 32, (size_t)a.cap * 32),
-              rsrc(reinterpret_cast<const uint8_t*>(a.v_scale_f) + row0 * 16, (size_t)a.cap * 16),
-              rsrc(reinterpret_cast<const uint8_t*>(a.v_zero_f) + row0 * 16, (size_t)a.cap * 16)};
+  const Res r{rsrc(a.k_codes + row0 * (D / 4), (size_t)a.cap * (D / 4)),
+              rsrc(reinterpret_cast<const uint8_t*>(a.k_scale_f) + row0 / 32 * (4 * D), (size_t)a.cap / 32 * (4 * D)),
+              rsrc(reinterpret_cast<const uint8_t*>(a.k_zero_f) + row0 / 32 * (4 * D), (size_t)a.cap / 32 * (4 * D)),
+              rsrc(a.v_codes + row0 * (D / 4), (size_t)a.cap * (D / 4)),
+              rsrc(reinterpret_cast<const uint8_t*>(a.v_scale_f) + row0 * (D / 8), (size_t)a.cap * (D / 8)),
+              rsrc(reinterpret_cast<const uint8_t*>(a.v_zero_f) + row0 * (D / 8), (size_t)a.cap * (D / 8))};
   auto tile_or_none = [&](int t) { return t < t_end ? t : a.cap; };
 
   uint8_t* sa = stA[wave];
@@ -361,16 +390,16 @@ decode_kivi_kernel(MfmaDecodeArgs a) {
   // The first two tiles are issued before the sequence length, the staging
   // marker and the query have arrived: a tile past the end is read from the
   // cache's own rows and never used, or has all its tokens masked.
-  issue_tile(sa, lane, t0 < a.cap ? t0 : a.cap, r);
-  issue_tile(sb, lane, t0 + 128 < a.cap ? t0 + 128 : a.cap, r);
-  WaveState w;
+  issue_tile<D>(sa, lane, t0 < a.cap ? t0 : a.cap, r);
+  issue_tile<D>(sb, lane, t0 + 128 < a.cap ? t0 + 128 : a.cap, r);
+  WaveState<D> w;
   {
     const int pair = a.c0 + pc;
     const bool live = pc < a.ncol;
     const size_t qrow = ((size_t)b * a.nq + (live ? pair / a.gr : 0)) * a.Hq + (size_t)h * a.gr + (live ? pair % a.gr : 0);
-    const float* qp = static_cast<const float*>(a.q) + qrow * kD + 8 * q4;
+    const float* qp = static_cast<const float*>(a.q) + qrow * D + 8 * q4;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < NK; ++kk) {
       if (kk >= KP) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) w.q[kk][i] = 0.f;
@@ -388,11 +417,11 @@ decode_kivi_kernel(MfmaDecodeArgs a) {
   w.m_run = -INFINITY;
   w.l_run = 0.f;
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt) w.o[nt] = f4_t{0.f, 0.f, 0.f, 0.f};
+  for (int nt = 0; nt < NT; ++nt) w.o[nt] = f4_t{0.f, 0.f, 0.f, 0.f};
   for (; t0 < t_end; t0 += 256) {
     // the second tile of a pair may lie past t_end: all its tokens are masked
-    tile_step<S>(w, sa, lane, t0, t_full, lim, tile_or_none(t0 + 256), r, a);
-    tile_step<S>(w, sb, lane, t0 + 128, t_full, lim, tile_or_none(t0 + 384), r, a);
+    tile_step<D, S>(w, sa, lane, t0, t_full, lim, tile_or_none(t0 + 256), r, a);
+    tile_step<D, S>(w, sb, lane, t0 + 128, t_full, lim, tile_or_none(t0 + 384), r, a);
   }
   // drain the refills still in flight before the waves' LDS is reused or the wave exits
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -416,12 +445,12 @@ decode_kivi_kernel(MfmaDecodeArgs a) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) sm_o[wave][4 * (q4e & 1) + v][8 * ce + nt] = w.o[nt][v];
+        for (int nt = 0; nt < NT; ++nt) sm_o[wave][4 * (q4e & 1) + v][CL * ce + nt] = w.o[nt][v];
       }
     }
     __syncthreads();
-    for (int e = tid_e; e < 8 * kD; e += 256) {
-      const int hh = 8 * r + (e >> 7), ch = e & 127;
+    for (int e = tid_e; e < 8 * D; e += 256) {
+      const int hh = 8 * r + e / D, ch = e % D;
       if (hh >= P || hh >= a.ncol) continue;  // a column with no query, or a pair's copy
       float M = -INFINITY;
 #pragma unroll
@@ -436,7 +465,7 @@ decode_kivi_kernel(MfmaDecodeArgs a) {
       }
       const int pc = a.c0 + hh;
       const size_t row = ((size_t)b * a.nq + pc / a.gr) * a.Hq + (size_t)h * a.gr + pc % a.gr;
-      float* p = a.part + (row * a.part_splits + split) * (kD + 2);
+      float* p = a.part + (row * a.part_splits + split) * (D + 2);
       p[2 + ch] = O;
       if (ch == 0) {
         p[0] = M;
@@ -448,12 +477,17 @@ decode_kivi_kernel(MfmaDecodeArgs a) {
 
 }  // namespace
 
-int launch_decode_kivi(const MfmaDecodeArgs& a, int B, hipStream_t st) {
-  if (a.pm.table || a.sel || a.ncol < 1 || a.ncol > 16) return KV_EUNSUPPORTED;
+int launch_decode_kivi(const MfmaDecodeArgs& a, int d, int B, hipStream_t st) {
+  if (a.pm.table || a.sel || a.ncol < 1 || a.ncol > 16 || (d != 64 && d != 128)) return KV_EUNSUPPORTED;
   const dim3 grid(a.splits, a.H, B);
-  if (a.ncol <= 4) decode_kivi_kernel<4><<<grid, 256, 0, st>>>(a);
-  else if (a.ncol <= 8) decode_kivi_kernel<2><<<grid, 256, 0, st>>>(a);
-  else decode_kivi_kernel<1><<<grid, 256, 0, st>>>(a);
+  if (d == 128) {
+    if (a.ncol <= 4) decode_kivi_kernel<128, 4><<<grid, 256, 0, st>>>(a);
+    else if (a.ncol <= 8) decode_kivi_kernel<128, 2><<<grid, 256, 0, st>>>(a);
+    else decode_kivi_kernel<128, 1><<<grid, 256, 0, st>>>(a);
+  } else {
+    if (a.ncol <= 8) decode_kivi_kernel<64, 2><<<grid, 256, 0, st>>>(a);
+    else decode_kivi_kernel<64, 1><<<grid, 256, 0, st>>>(a);
+  }
   return KV_OK;
 }
 

@@ -95,7 +95,7 @@ bool latent_fast_path_ok(const kv_layout& L, int num_q_heads, int nq, int q_dtyp
 }
 
 bool kivi_fast_path_ok(const kv_layout& L) {
-  return L.format == KV_FMT_KIVI2 && L.head_dim == 128 && L.page_tokens == 0 && L.sink_tokens == 0 &&
+  return L.format == KV_FMT_KIVI2 && (L.head_dim == 64 || L.head_dim == 128) && L.page_tokens == 0 && L.sink_tokens == 0 &&
          L.recent_tokens == 0 && (size_t)L.capacity * 32 < (size_t(1) << 31);
 }
 

@@ -19,8 +19,8 @@ struct MfmaDecodeArgs {
   const uint8_t* v_codes;   // [B][H][cap][64]
   const uint16_t* v_scale;  // [B][H][cap][8] bf16
   const uint16_t* rope;     // latent: [B][cap][64] bf16 (k_codes [B][cap][256], k_scale [B][cap][32])
-  // KIVI-2 (k_codes, v_codes [B][H][cap][32]): key scale / zero f32 [B][H][cap / 32][128],
-  // value scale / zero f32 [B][H][cap][4], key staging [B][H][4 + 32 * 128] (count, then keys)
+  // KIVI-2 (k_codes, v_codes [B][H][cap][d / 4]): key scale / zero f32 [B][H][cap / 32][d],
+  // value scale / zero f32 [B][H][cap][d / 32], key staging [B][H][4 + 32 d] (count, then keys)
   const float *k_scale_f, *k_zero_f, *v_scale_f, *v_zero_f, *k_stage;
   PageMap pm;               // token rows: [B][H][cap] above, or a paged pool
   // latent sparse decode: slot i of sequence b reads position sel[b * sel_stride + i]
@@ -47,10 +47,10 @@ struct MfmaDecodeArgs {
 
 int launch_decode_mfma(const MfmaDecodeArgs& a, int format, int B, int G, hipStream_t st);
 
-// KIVI-2 on the matrix cores (d = 128, contiguous, dense; columns c0 .. c0 + ncol
-// of the (query, head) pairs, ncol <= 16, q the prepared fp32 queries): the
-// coded tokens of each split, up to the sequence's incomplete group.
-int launch_decode_kivi(const MfmaDecodeArgs& a, int B, hipStream_t st);
+// KIVI-2 on the matrix cores (d = 64 or 128, contiguous, dense; columns c0 ..
+// c0 + ncol of the (query, head) pairs, ncol <= 16, q the prepared fp32
+// queries): the coded tokens of each split, up to the sequence's incomplete group.
+int launch_decode_kivi(const MfmaDecodeArgs& a, int d, int B, hipStream_t st);
 
 // TurboQuant cache (d = 128, m = 128, 2-bit symmetric codebook): per query
 // row the FP6 pieces of the scaled key-product operands and the two constant

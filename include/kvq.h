@@ -225,11 +225,11 @@ typedef struct kv_cache {
  * lies in [2^-17, 65504].  Outside those ranges values round like fp16 (a
  * group absmax or query above 65504 becomes infinite); a cache or query that
  * may leave them is decoded exactly with KV_DECODE_FP32.  fp32 queries always
- * take the fp32 kernel for FP4 and LATENT caches.  KIVI-2 caches with 128
- * channels (contiguous, no windows) read their coded key groups on the matrix
- * cores: a key term q_c * s_c enters as an fp16 pair hi + lo (error below
- * 2^-20 relative or 2^-24 absolute), the zero term sum_c q_c z_c in fp32, and
- * a value as fp16(code * fp16(s) + fp16(z)); |q_c * s_c|, |s|, |z| and every
+ * take the fp32 kernel for FP4 and LATENT caches.  KIVI-2 caches with 64 or
+ * 128 channels (contiguous, no windows) read their coded key groups on the
+ * matrix cores: a key term q_c * s_c enters as an fp16 pair hi + lo (error
+ * below 2^-20 relative or 2^-24 absolute), the zero term sum_c q_c z_c in fp32,
+ * and a value as code * s + z rounded once to fp16; |q_c * s_c| and every
  * dequantised value must stay below 65504 there.  The keys of a sequence's
  * incomplete last group (still in staging) are read by the fp32 kernel. */
 enum kv_decode_flags { KV_DECODE_FP32 = 1 };

@@ -1,4 +1,4 @@
-"""KIVI-2 decode at 128 channels on the matrix cores against the oracle.
+"""KIVI-2 decode at 64 and 128 channels on the matrix cores against the oracle.
 
 The matrix-core kernel reads the coded key groups of each sequence; the
 tokens of its incomplete last group (keys still in staging) go through the
@@ -57,43 +57,47 @@ def _check(cfg, lens, nq=1, splits=0, flags=0, ramp=None, decode_lens=None, what
     return out
 
 
-@pytest.mark.parametrize("G,nq", [(1, 1), (4, 1), (8, 2), (16, 1), (32, 1), (4, 5)])
-def test_kivi_matrix_cores_match_oracle(G, nq):
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("G,nq", [(1, 1), (2, 1), (4, 1), (8, 2), (16, 1), (32, 1), (4, 5)])
+def test_kivi_matrix_cores_match_oracle(G, nq, d):
     """Head groups of 1 to 32 and several queries per sequence (more than 16
     (query, head) pairs take several launches), ragged lengths ending inside a
-    key group, with outlier key channels."""
-    cfg = BASE.scaled(hq=G * BASE.hkv)
+    key group, with outlier key channels, at 64 and 128 channels."""
+    cfg = BASE.scaled(hq=G * BASE.hkv, head_dim=d)
     lens = np.array([1024, 517, 33], dtype=np.int32)
-    print(f"[kivi mfma] G={G} nq={nq} lens={lens.tolist()}", flush=True)
-    _check(cfg, lens, nq=nq, what=f"G={G} nq={nq}")
+    print(f"[kivi mfma] d={d} G={G} nq={nq} lens={lens.tolist()}", flush=True)
+    _check(cfg, lens, nq=nq, what=f"d={d} G={G} nq={nq}")
 
 
-def test_kivi_short_sequences_and_split_counts():
+@pytest.mark.parametrize("d", [64, 128])
+def test_kivi_short_sequences_and_split_counts(d):
     """Sequences shorter than one key group (staged tokens only), exactly one
     group, and one token; the result does not depend on the split count."""
-    cfg = BASE.scaled(hq=4 * BASE.hkv, batch=4)
+    cfg = BASE.scaled(hq=4 * BASE.hkv, batch=4, head_dim=d)
     lens = np.array([1, 31, 32, 800], dtype=np.int32)
-    print(f"[kivi short] lens={lens.tolist()}", flush=True)
+    print(f"[kivi short] d={d} lens={lens.tolist()}", flush=True)
     outs = [_check(cfg, lens, splits=s, what=f"splits={s}") for s in (0, 1, 5)]
     for o in outs[1:]:
         np.testing.assert_allclose(o, outs[0], rtol=0, atol=1e-3 * np.abs(outs[0]).max())
 
 
-def test_kivi_matrix_cores_agree_with_the_fp32_kernel():
+@pytest.mark.parametrize("d", [64, 128])
+def test_kivi_matrix_cores_agree_with_the_fp32_kernel(d):
     """The same cache on the fp32 general kernel (every split reads through it)."""
-    cfg = BASE.scaled(hq=4 * BASE.hkv)
+    cfg = BASE.scaled(hq=4 * BASE.hkv, head_dim=d)
     lens = np.array([1000, 259, 70], dtype=np.int32)
-    print(f"[kivi fp32] lens={lens.tolist()}", flush=True)
+    print(f"[kivi fp32] d={d} lens={lens.tolist()}", flush=True)
     a = _check(cfg, lens, what="matrix cores")
     b = _check(cfg, lens, flags=kvq.DECODE_FP32, what="fp32 kernel")
     np.testing.assert_allclose(a, b, rtol=0, atol=2e-3 * np.abs(b).max())
 
 
-def test_kivi_growing_logits_rescale():
+@pytest.mark.parametrize("d", [64, 128])
+def test_kivi_growing_logits_rescale(d):
     """Keys growing along the sequence move the running max often."""
-    cfg = BASE.scaled(hq=4 * BASE.hkv, batch=2)
+    cfg = BASE.scaled(hq=4 * BASE.hkv, batch=2, head_dim=d)
     lens = np.array([1024, 700], dtype=np.int32)
-    print("[kivi ramp]", flush=True)
+    print(f"[kivi ramp] d={d}", flush=True)
     _check(cfg, lens, ramp=12.0, what="ramped keys")
 
 
