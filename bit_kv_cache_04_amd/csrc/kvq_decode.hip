@@ -1090,13 +1090,17 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     f.gr = num_q_heads / L.num_kv_heads;
     f.part_splits = part_splits;
     if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), st) != hipSuccess) return KV_EDEVICE;
+    // The staged tokens take a last grid column of each launch when the grid
+    // is small (its launch latency then dominates; at scale that column's code
+    // measured slower for the main workgroups), else the general kernel.
+    const bool fold = (long)plan.splits * L.num_kv_heads * B < 256;
     // one launch per 16 (query, head) pairs of a KV head, each over the whole cache
     for (f.c0 = 0; f.c0 < nq * f.gr; f.c0 += 16) {
       f.ncol = std::min(16, nq * f.gr - f.c0);
-      int rc = launch_decode_kivi(f, L.head_dim, B, st);
+      int rc = launch_decode_kivi(f, L.head_dim, fold, B, st);
       if (rc != KV_OK) return rc;
     }
-    launch_kivi_tail(a, tail_split, B, st);
+    if (!fold) launch_kivi_tail(a, tail_split, B, st);
     if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess) return KV_EDEVICE;
     launch_merge(part, rows, part_splits, plan.splits, L.head_dim, L.format, c->rot, out, st);
     return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;

@@ -22,7 +22,8 @@
 // c % P over the channel part c / P only, and rotations within each 16-lane row
 // add the parts: each lane scales D / S query channels per tile instead of D.
 // Tokens of a sequence's incomplete last group are not coded yet (their keys
-// wait in staging); the general kernel takes them as one more split.
+// wait in staging); they take one more split in fp32: on small grids a last
+// column of workgroups of the same launch, else the general kernel.
 #include <hip/hip_runtime.h>
 
 #include "kvq_device.h"
@@ -339,7 +340,76 @@ __device__ __forceinline__ void tile_step(WaveState<D>& w, uint8_t* st, int lane
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int D, int S>
+// The staged tokens [kstage, L) of a sequence's incomplete key group (keys still
+// fp32 in staging, token t in row t mod 32; values coded) for the launch's
+// pairs, written as partial split a.splits: fp32 logits, softmax and value sums.
+// kbuf: 32 x D floats of LDS, sbuf: 16 x 32 + 32 floats.
+template <int D>
+__device__ void staged_tail(const MfmaDecodeArgs& a, int b, int h, float* kbuf, float* sbuf) {
+  const int tid = threadIdx.x;
+  const size_t bh = (size_t)b * a.H + h;
+  const int L = min(min(a.seq_lens[b], a.max_len), a.cap);
+  const float* stg = a.k_stage + bh * (4 + 32 * D);
+  const int t0 = reinterpret_cast<const int*>(stg)[0] & ~31;
+  const int n = max(0, L - t0);  // below 32: the coded groups end at t0
+  float* sm = sbuf;              // [16][32] logits, then weights
+  float* mm = sbuf + 16 * 32;    // [16] max, [16] sum
+  for (int e = tid; e < n * D; e += 256) kbuf[e] = stg[4 + ((t0 + e / D) & 31) * D + e % D];
+  __syncthreads();
+  for (int e = tid; e < a.ncol * 32; e += 256) {
+    const int pc = e >> 5, i = e & 31, pair = a.c0 + pc, j = pair / a.gr;
+    float x = -INFINITY;
+    if (i < n && t0 + i < L - (a.nq - 1 - j)) {  // query j sees the first L - (nq - 1 - j) tokens
+      const size_t qrow = ((size_t)b * a.nq + j) * a.Hq + (size_t)h * a.gr + pair % a.gr;
+      const float* q = static_cast<const float*>(a.q) + qrow * D;
+      float acc = 0.f;
+#pragma unroll 4
+      for (int ch = 0; ch < D; ++ch) acc = fmaf(q[ch], kbuf[i * D + ch], acc);
+      x = acc * a.scale_log2;
+    }
+    sm[e] = x;
+  }
+  __syncthreads();
+  if (tid < a.ncol) {
+    float M = -INFINITY, l = 0.f;
+#pragma unroll 4
+    for (int i = 0; i < 32; ++i) M = fmaxf(M, sm[tid * 32 + i]);
+#pragma unroll 4
+    for (int i = 0; i < 32; ++i) {
+      const float p = M == -INFINITY ? 0.f : exp2f(sm[tid * 32 + i] - M);
+      sm[tid * 32 + i] = p;
+      l += p;
+    }
+    mm[tid] = M;
+    mm[16 + tid] = l;
+  }
+  // the staged tokens' values, dequantised in place of the keys
+  for (int e = tid; e < n * D; e += 256) {
+    const size_t row = bh * a.cap + t0 + e / D;
+    const int ch = e % D;
+    const uint32_t code = (a.v_codes[row * (D / 4) + ch / 4] >> (2 * (ch & 3))) & 3u;
+    const size_t g = row * (D / 32) + ch / 32;
+    kbuf[e] = fmaf((float)code, a.v_scale_f[g], a.v_zero_f[g]);
+  }
+  __syncthreads();
+  for (int e = tid; e < a.ncol * D; e += 256) {
+    const int pc = e / D, ch = e % D, pair = a.c0 + pc;
+    float O = 0.f;
+#pragma unroll 4
+    for (int i = 0; i < n; ++i) O = fmaf(sm[pc * 32 + i], kbuf[i * D + ch], O);
+    const size_t row = ((size_t)b * a.nq + pair / a.gr) * a.Hq + (size_t)h * a.gr + pair % a.gr;
+    float* p = a.part + (row * a.part_splits + a.splits) * (D + 2);
+    p[2 + ch] = O;
+    if (ch == 0) {
+      p[0] = mm[pc];
+      p[1] = mm[16 + pc];
+    }
+  }
+}
+
+// TAIL: the grid has one more column of workgroups, which take the staged
+// tokens (staged_tail); else the caller runs them separately.
+template <int D, int S, bool TAIL>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_kivi_kernel(MfmaDecodeArgs a) {
   constexpr int NK = D / 32, NT = D / 16, CL = D / 16;  // k-steps, value N-tiles, value channels per lane
@@ -359,6 +429,14 @@ decode_kivi_kernel(MfmaDecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  static_assert(sizeof(float) * 32 * D <= sizeof(stA) && sizeof(float) * (16 * 32 + 32) <= sizeof(stB),
+                "the staged tail fits the stages");
+  if constexpr (TAIL) {
+    if (split == a.splits) {  // the grid's last column: the staged tokens
+      staged_tail<D>(a, b, h, reinterpret_cast<float*>(&stA[0][0]), reinterpret_cast<float*>(&stB[0][0]));
+      return;
+    }
+  }
   const size_t bh = (size_t)b * a.H + h;
   const int L = min(min(a.seq_lens[b], a.max_len), a.cap);
   // the coded tokens end at the first token of the incomplete group
@@ -477,17 +555,23 @@ decode_kivi_kernel(MfmaDecodeArgs a) {
 
 }  // namespace
 
-int launch_decode_kivi(const MfmaDecodeArgs& a, int d, int B, hipStream_t st) {
-  if (a.pm.table || a.sel || a.ncol < 1 || a.ncol > 16 || (d != 64 && d != 128)) return KV_EUNSUPPORTED;
-  const dim3 grid(a.splits, a.H, B);
+template <bool TAIL>
+static void launch_kivi(const MfmaDecodeArgs& a, int d, int B, hipStream_t st) {
+  const dim3 grid(a.splits + (TAIL ? 1 : 0), a.H, B);
   if (d == 128) {
-    if (a.ncol <= 4) decode_kivi_kernel<128, 4><<<grid, 256, 0, st>>>(a);
-    else if (a.ncol <= 8) decode_kivi_kernel<128, 2><<<grid, 256, 0, st>>>(a);
-    else decode_kivi_kernel<128, 1><<<grid, 256, 0, st>>>(a);
+    if (a.ncol <= 4) decode_kivi_kernel<128, 4, TAIL><<<grid, 256, 0, st>>>(a);
+    else if (a.ncol <= 8) decode_kivi_kernel<128, 2, TAIL><<<grid, 256, 0, st>>>(a);
+    else decode_kivi_kernel<128, 1, TAIL><<<grid, 256, 0, st>>>(a);
   } else {
-    if (a.ncol <= 8) decode_kivi_kernel<64, 2><<<grid, 256, 0, st>>>(a);
-    else decode_kivi_kernel<64, 1><<<grid, 256, 0, st>>>(a);
+    if (a.ncol <= 8) decode_kivi_kernel<64, 2, TAIL><<<grid, 256, 0, st>>>(a);
+    else decode_kivi_kernel<64, 1, TAIL><<<grid, 256, 0, st>>>(a);
   }
+}
+
+int launch_decode_kivi(const MfmaDecodeArgs& a, int d, bool tail, int B, hipStream_t st) {
+  if (a.pm.table || a.sel || a.ncol < 1 || a.ncol > 16 || (d != 64 && d != 128)) return KV_EUNSUPPORTED;
+  if (tail) launch_kivi<true>(a, d, B, st);
+  else launch_kivi<false>(a, d, B, st);
   return KV_OK;
 }
 

@@ -49,8 +49,10 @@ int launch_decode_mfma(const MfmaDecodeArgs& a, int format, int B, int G, hipStr
 
 // KIVI-2 on the matrix cores (d = 64 or 128, contiguous, dense; columns c0 ..
 // c0 + ncol of the (query, head) pairs, ncol <= 16, q the prepared fp32
-// queries): the coded tokens of each split, up to the sequence's incomplete group.
-int launch_decode_kivi(const MfmaDecodeArgs& a, int d, int B, hipStream_t st);
+// queries): the coded tokens of each split, up to the sequence's incomplete
+// group, and with `tail` (a last grid column) that group's staged tokens as
+// partial split `splits`.
+int launch_decode_kivi(const MfmaDecodeArgs& a, int d, bool tail, int B, hipStream_t st);
 
 // TurboQuant cache (d = 128, m = 128, 2-bit symmetric codebook): per query
 // row the FP6 pieces of the scaled key-product operands and the two constant

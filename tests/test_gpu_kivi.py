@@ -1,8 +1,9 @@
 """KIVI-2 decode at 64 and 128 channels on the matrix cores against the oracle.
 
 The matrix-core kernel reads the coded key groups of each sequence; the
-tokens of its incomplete last group (keys still in staging) go through the
-general kernel as one more split.  Every case appends in uneven chunks, so the
+tokens of its incomplete last group (keys still in staging) take one more
+split in fp32 (a last grid column of the same launch on small grids, the
+general kernel on large ones).  Every case appends in uneven chunks, so the
 sequences end inside a key group, and compares with the oracle's staged
 reference (page "TurboQuant vs OSCAR vs EpiCache", section "quantization
 frontiers", KIVI paragraph: keys per channel, values per token, 2 bits).
@@ -125,3 +126,13 @@ def test_kivi_bytes_still_match_after_decode():
         np.testing.assert_array_equal(got["k_codes"][b, :, :Lg], want["k_codes"][b, :, :Lg])
         np.testing.assert_array_equal(got["k_scale"][b, :, :Lg // 32], want["k_scale"][b, :, :Lg // 32])
         np.testing.assert_array_equal(got["v_codes"][b, :, :L], want["v_codes"][b, :, :L])
+
+
+def test_kivi_large_grid_staged_tail_on_the_general_kernel():
+    """A grid of at least 256 workgroups leaves the staged tokens to the general
+    kernel (small grids take them in a last column of the same launch): 16
+    sequences x 8 KV heads, lengths ending inside a key group."""
+    cfg = BASE.scaled(batch=16, hkv=8, hq=32, context=4096)
+    lens = np.array([4096 - 5 * b - (b % 3) * 11 for b in range(16)], dtype=np.int32)
+    print(f"[kivi large grid] lens={lens.tolist()}", flush=True)
+    _check(cfg, lens, what="large grid")
