@@ -179,7 +179,7 @@ def test_turbo_small_and_bulk_append_kernels_agree():
     assert_bytes_equal(got, want, "turbo small vs oracle")
 
 
-@pytest.mark.parametrize("fmt", ["fp4", "qjl1", "turbo", "latent"])
+@pytest.mark.parametrize("fmt", ["kivi2", "fp4", "qjl1", "turbo", "latent"])
 def test_split_count_invariance_and_determinism(fmt):
     cfg = SMALL[fmt]
     cache, _, _ = _build(cfg)
@@ -187,15 +187,15 @@ def test_split_count_invariance_and_determinism(fmt):
     lens = torch.from_numpy(synth.seq_lens_for(cfg)).cuda()
     outs = [cache.decode(q, lens, softmax_scale(cfg), splits=s).cpu().numpy() for s in (1, 0, 5, 0)]
     np.testing.assert_array_equal(outs[1], outs[3])
-    # The matrix-core kernels feed softmax weights to the PV product in fp16, so
-    # each split configuration moves an output channel by up to 2^-11 of the
-    # largest value it averages; two configurations differ by up to twice that,
-    # and TurboQuant's R^T mixes the rotated channels' rounding into every output.
-    # A split-boundary bug (a token lost or counted twice) shows as ~1e-1.  The
-    # fp32 general kernel agrees with itself to fp32 rounding.
-    tol = 1.5e-3 if fmt in ("fp4", "qjl1", "latent", "turbo") else 1e-5
-    for o in outs[:3]:
-        assert row_rel_err(o, outs[0]).max() < tol
+    # The matrix-core kernels (every format here) feed softmax weights to the PV
+    # product in fp16, so each split configuration moves an output channel by up
+    # to 2^-11 of the largest value it averages; two configurations differ by up
+    # to twice that, 9.8e-4 (measured: 2.9e-4 to 5.6e-4).  A split-boundary bug
+    # (a token lost or counted twice) shows as ~1e-1.
+    tol = 1e-3
+    errs = [float(row_rel_err(o, outs[0]).max()) for o in outs[:3]]
+    print(f"  {fmt}: split configurations differ by {max(errs):.2e}", flush=True)
+    assert max(errs) < tol
 
 
 @pytest.mark.parametrize("fmt", ["fp4", "qjl1", "turbo"])
