@@ -59,10 +59,12 @@ __device__ __forceinline__ void fill_starts(const AppendPos& pos, int* starts) {
   }
   __syncthreads();
 }
+__device__ __forceinline__ int start_tab(const AppendPos& pos, const int* starts, size_t bh) {
+  return pos.ragged ? starts[bh / pos.heads] : pos.start;
+}
 __device__ __forceinline__ size_t dst_row_tab(size_t r, int n, int cap, const AppendPos& pos, const int* starts) {
   const size_t bh = r / n;
-  const int s0 = pos.ragged ? starts[bh / pos.heads] : pos.start;
-  return seq_row(pos, bh, s0 + (int)(r % n), cap);
+  return seq_row(pos, bh, start_tab(pos, starts, bh) + (int)(r % n), cap);
 }
 
 // ---------------------------------------------------------------- FP4
@@ -194,8 +196,8 @@ __device__ __forceinline__ void fp4_store_at(const float (&a)[16], const InT* ta
 template <typename InT>
 __device__ __forceinline__ void fp4_store_group(const float (&a)[16], const InT* tag, size_t r, int g, int d,
                                                 uint8_t* __restrict__ codes, uint16_t* __restrict__ scales, int n,
-                                                int cap, AppendPos pos) {
-  fp4_store_at(a, tag, dst_row(r, n, cap, pos), g, d, codes, scales);
+                                                int cap, const AppendPos& pos, const int* starts) {
+  fp4_store_at(a, tag, dst_row_tab(r, n, cap, pos, starts), g, d, codes, scales);
 }
 
 // Group gid (= row * (d / 16) + group) of a row-major input with row stride
@@ -203,7 +205,8 @@ __device__ __forceinline__ void fp4_store_group(const float (&a)[16], const InT*
 template <typename InT>
 __device__ __forceinline__ void fp4_group(const InT* __restrict__ x, size_t stride, int d,
                                           uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
-                                          size_t rows, int n, int cap, AppendPos pos, size_t gid) {
+                                          size_t rows, int n, int cap, const AppendPos& pos, const int* starts,
+                                          size_t gid) {
   const int groups = d / 16;
   if (gid >= rows * groups) return;
   const int g = (int)(gid % groups);
@@ -212,7 +215,7 @@ __device__ __forceinline__ void fp4_group(const InT* __restrict__ x, size_t stri
   raw.load(x + r * stride + g * 16);
   float a[16];
   raw.unpack(a);
-  fp4_store_group(a, x, r, g, d, codes, scales, n, cap, pos);
+  fp4_store_group(a, x, r, g, d, codes, scales, n, cap, pos, starts);
 }
 
 // K (blockIdx.y = 0) and V (blockIdx.y = 1) of an FP4 cache in one launch.
@@ -221,9 +224,11 @@ __global__ void __launch_bounds__(256) fp4_append_kernel(const InT* __restrict__
                                                          int d, uint8_t* __restrict__ kc, uint16_t* __restrict__ ks,
                                                          uint8_t* __restrict__ vc, uint16_t* __restrict__ vs,
                                                          size_t rows, int n, int cap, AppendPos pos) {
+  __shared__ int starts[kMaxRaggedSeqs];
+  fill_starts(pos, starts);
   const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (blockIdx.y == 0) fp4_group(k, d, d, kc, ks, rows, n, cap, pos, gid);
-  else fp4_group(v, d, d, vc, vs, rows, n, cap, pos, gid);
+  if (blockIdx.y == 0) fp4_group(k, d, d, kc, ks, rows, n, cap, pos, starts, gid);
+  else fp4_group(v, d, d, vc, vs, rows, n, cap, pos, starts, gid);
 }
 
 // Latent: the 512-wide latent as FP4 groups (blockIdx.y = 0) and the RoPE key
@@ -233,15 +238,17 @@ __global__ void __launch_bounds__(256) latent_append_kernel(const InT* __restric
                                                             uint8_t* __restrict__ cc, uint16_t* __restrict__ cs,
                                                             uint16_t* __restrict__ rope, size_t rows, int n,
                                                             int cap, AppendPos pos) {
+  __shared__ int starts[kMaxRaggedSeqs];
+  fill_starts(pos, starts);
   const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t stride = (size_t)d + rope_dim;
   if (blockIdx.y == 0) {
-    fp4_group(x, stride, d, cc, cs, rows, n, cap, pos, gid);
+    fp4_group(x, stride, d, cc, cs, rows, n, cap, pos, starts, gid);
   } else if (gid < rows * rope_dim) {
     const int c = (int)(gid % rope_dim);
     const size_t r = gid / rope_dim;
     const float val = load_as_f32(x + r * stride + d, c);
-    const size_t dr = dst_row(r, n, cap, pos);
+    const size_t dr = dst_row_tab(r, n, cap, pos, starts);
     if (dr != kNoRow) rope[dr * rope_dim + c] = bf16_from_f64((double)val);
   }
 }
@@ -287,6 +294,8 @@ __global__ void __launch_bounds__(256) kivi_append_kernel(const InT* __restrict_
                                                           int cap, AppendPos pos) {
   __shared__ float xk[32][kKiviMaxD + 1];
   __shared__ float xv[32][kKiviMaxD + 1];
+  __shared__ int starts[kMaxRaggedSeqs];
+  fill_starts(pos, starts);
   const int tid = threadIdx.x;
   const int ngroups = n / 32;
   const int g = blockIdx.x % ngroups;
@@ -317,7 +326,7 @@ __global__ void __launch_bounds__(256) kivi_append_kernel(const InT* __restrict_
   }
   __syncthreads();
   const int quads = d / 4;
-  const int start = start_of(pos, bh);
+  const int start = start_tab(pos, starts, bh);
   const size_t slot0 = seq_row(pos, bh, start + g * 32, cap);  // cache row of the group's first token
   if (tid == 0 && g == ngroups - 1) set_appended(stage, bh, d, start + n);
   if (slot0 == kNoRow) return;  // a page outside the pool
@@ -386,11 +395,13 @@ __global__ void __launch_bounds__(256) kivi_append_any_kernel(const InT* __restr
                                                               AppendPos pos, int phase) {
   __shared__ float xk[32][kKiviMaxD + 1];
   __shared__ float xv[32][kKiviMaxD + 1];
+  __shared__ int starts[kMaxRaggedSeqs];
+  fill_starts(pos, starts);
   const int tid = threadIdx.x;
   const int ngmax = n / 32 + 2;  // groups an append of n tokens can touch
   const int gi = blockIdx.x % ngmax;
   const size_t bh = blockIdx.x / ngmax;
-  const int s = start_of(pos, bh);
+  const int s = start_tab(pos, starts, bh);
   const int g0 = 32 * (s / 32 + gi);                 // the group's first token
   const int a0 = max(g0, s), a1 = min(g0 + 32, s + n);  // its new tokens
   if (a0 >= a1) return;                              // the whole workgroup: no token of this append
@@ -1158,6 +1169,8 @@ __global__ void __launch_bounds__(256) window_copy_kernel(const InT* __restrict_
                                                           int d, uint16_t* __restrict__ sk, uint16_t* __restrict__ sv,
                                                           uint16_t* __restrict__ rk, uint16_t* __restrict__ rv,
                                                           int S, int W, int bh_count, int n, AppendPos pos) {
+  __shared__ int starts[kMaxRaggedSeqs];
+  fill_starts(pos, starts);
   const int per_row = d / 8, Sn = min(n, S), Wn = min(n, W), nv = Sn + Wn;
   const size_t half = (size_t)bh_count * nv * per_row;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < 2 * half; i += (size_t)gridDim.x * 256) {
@@ -1168,7 +1181,7 @@ __global__ void __launch_bounds__(256) window_copy_kernel(const InT* __restrict_
     const size_t bh = j / ((size_t)per_row * nv);
     const bool sink = vi < Sn;
     const int tt = sink ? vi : n - Wn + (vi - Sn);
-    const int t = start_of(pos, bh) + tt;
+    const int t = start_tab(pos, starts, bh) + tt;
     if (sink && t >= S) continue;  // past the sink
     const InT* src = (is_v ? v : k) + (bh * n + tt) * d + c8;
     uint32_t w[4];
