@@ -965,6 +965,14 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
                          ? reinterpret_cast<uint8_t*>(wsb + wsl.qpiece_off)
                          : nullptr;
   const float kappa = (float)(1.2533141373155002512 / (double)(L.qjl_m > 0 ? L.qjl_m : 1));
+  // KIVI-2 on the matrix cores: on grids under 256 workgroups the staged tokens
+  // take a last column of the same launch (their launch latency then
+  // dominates; at scale that column's code measured slower for the main
+  // workgroups), else the general kernel; there fp32 queries are read as they
+  // are (every other path reads the prepared copy).
+  const bool kivi = !fp32 && !sel && kivi_fast_path_ok(L);
+  const bool kivi_fold = kivi && (long)plan.splits * L.num_kv_heads * B < 256;
+  const bool q_direct = kivi_fold && q_dtype == KV_DT_F32;
   if (L.format == KV_FMT_TURBO) {
     if (q_dtype == KV_DT_F32)
       prep_turbo_kernel<float><<<rows, kTurboPrepThreads, 0, st>>>(static_cast<const float*>(q), c->rot, c->proj,
@@ -972,7 +980,7 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     else
       prep_turbo_kernel<uint16_t><<<rows, kTurboPrepThreads, 0, st>>>(
           static_cast<const uint16_t*>(q), c->rot, c->proj, c->lm_levels, scale * kLog2e, kappa, qv, qpieces);
-  } else if (!(mfma && L.format == KV_FMT_FP4)) {
+  } else if (!(mfma && L.format == KV_FMT_FP4) && !q_direct) {
     if (q_dtype == KV_DT_F32)
       prep_query_kernel<float><<<rows, 128, 0, st>>>(static_cast<const float*>(q), qw_in, qw_out, L.format, c->proj,
                                                      qv, qpieces);
@@ -1066,7 +1074,7 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
 
   DecodeArgs a = general_args(c, num_q_heads, nq, seq_lens, max_seq_len, scale, qv, part, plan, part_splits,
                                sel, sel_stride);
-  if (!fp32 && !sel && kivi_fast_path_ok(L)) {
+  if (kivi) {
     MfmaDecodeArgs f{};
     f.k_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_K_CODES]);
     f.v_codes = static_cast<const uint8_t*>(c->buf[KV_BUF_V_CODES]);
@@ -1076,7 +1084,7 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     f.v_zero_f = static_cast<const float*>(c->buf[KV_BUF_V_ZERO]);
     f.k_stage = static_cast<const float*>(c->buf[KV_BUF_K_STAGE]);
     f.pm = page_map(c);
-    f.q = qv;
+    f.q = q_direct ? q : qv;
     f.seq_lens = seq_lens;
     f.max_len = max_seq_len;
     f.H = L.num_kv_heads;
@@ -1090,17 +1098,13 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     f.gr = num_q_heads / L.num_kv_heads;
     f.part_splits = part_splits;
     if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), st) != hipSuccess) return KV_EDEVICE;
-    // The staged tokens take a last grid column of each launch when the grid
-    // is small (its launch latency then dominates; at scale that column's code
-    // measured slower for the main workgroups), else the general kernel.
-    const bool fold = (long)plan.splits * L.num_kv_heads * B < 256;
     // one launch per 16 (query, head) pairs of a KV head, each over the whole cache
     for (f.c0 = 0; f.c0 < nq * f.gr; f.c0 += 16) {
       f.ncol = std::min(16, nq * f.gr - f.c0);
-      int rc = launch_decode_kivi(f, L.head_dim, fold, B, st);
+      int rc = launch_decode_kivi(f, L.head_dim, kivi_fold, B, st);
       if (rc != KV_OK) return rc;
     }
-    if (!fold) launch_kivi_tail(a, tail_split, B, st);
+    if (!kivi_fold) launch_kivi_tail(a, tail_split, B, st);
     if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess) return KV_EDEVICE;
     launch_merge(part, rows, part_splits, plan.splits, L.head_dim, L.format, c->rot, out, st);
     return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
