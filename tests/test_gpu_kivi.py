@@ -128,11 +128,23 @@ def test_kivi_bytes_still_match_after_decode():
         np.testing.assert_array_equal(got["v_codes"][b, :, :L], want["v_codes"][b, :, :L])
 
 
-def test_kivi_large_grid_staged_tail_on_the_general_kernel():
+@pytest.mark.parametrize("d", [64, 128])
+def test_kivi_large_grid_staged_tail_on_the_general_kernel(d):
     """A grid of at least 256 workgroups leaves the staged tokens to the general
-    kernel (small grids take them in a last column of the same launch): 16
-    sequences x 8 KV heads, lengths ending inside a key group."""
-    cfg = BASE.scaled(batch=16, hkv=8, hq=32, context=4096)
+    kernel (small grids take them in a last column of the same launch) and reads
+    the prepared query copy: 16 sequences x 8 KV heads, lengths ending inside a
+    key group."""
+    cfg = BASE.scaled(batch=16, hkv=8, hq=32, context=4096, head_dim=d)
     lens = np.array([4096 - 5 * b - (b % 3) * 11 for b in range(16)], dtype=np.int32)
-    print(f"[kivi large grid] lens={lens.tolist()}", flush=True)
+    print(f"[kivi large grid] d={d} lens={lens.tolist()}", flush=True)
     _check(cfg, lens, what="large grid")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_kivi_bf16_queries(d):
+    """bf16 queries on a small grid (the prepared fp32 copy, not the caller's
+    queries, feeds the kernel), with several queries per sequence."""
+    cfg = BASE.scaled(hq=4 * BASE.hkv, head_dim=d, q_dtype="bf16")
+    lens = np.array([1000, 300, 45], dtype=np.int32)
+    print(f"[kivi bf16 q] d={d} lens={lens.tolist()}", flush=True)
+    _check(cfg, lens, nq=2, what="bf16 queries")
