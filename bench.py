@@ -23,7 +23,12 @@ Timing, per workload:
     events the library records immediately around its launch, in an eager pass
     over the same number of flushed steps.
 A plain streaming-read kernel (kvq_probe.h) is timed the same way over 1 GiB:
-the bandwidth a kernel that only reads reaches on this part, for context.
+the bandwidth a kernel that only reads reaches on this part, for context.  Two
+more reference kernels (kvq_probe.h), a loop of 32x32x16 fp16 matrix products
+and a loop of LDS reads, one workgroup of 4 waves per compute unit, give the
+compute and LDS rates the part delivers as clocked under such load; the latent
+record carries its kernel's fraction of the first and the time its LDS reads
+alone would take at the second (`measured_ceilings`).
 
 `value` is decode KV GB/s: the packed bytes the attention reads per step
 (codes + scales/norms of every cached token) over the median step time.
@@ -255,6 +260,36 @@ def stream_read_reference(torch, kvq, dev, flush, steps):
             "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def compute_references(torch, kvq, dev, steps):
+    """Median rates of the matrix-core and LDS reference kernels (kvq_probe.h),
+    256 workgroups of 4 waves (one wave per SIMD, as in the latent decode)."""
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream().cuda_stream
+    blocks, it_mfma, it_lds = 256, 2048, 2048
+    flop = blocks * 4 * it_mfma * 8 * 32768.0
+    lds_bytes = blocks * 4 * it_lds * 8 * 1024.0
+    for _ in range(3):
+        kvq.kv_mfma_probe(blocks, it_mfma, sink.data_ptr(), st)
+        kvq.kv_lds_probe(blocks, it_lds, sink.data_ptr(), st)
+    n = max(steps, 10)
+    ms_m = timed(torch, lambda i: kvq.kv_mfma_probe(blocks, it_mfma, sink.data_ptr(), st), n, lambda: None)
+    ms_l = timed(torch, lambda i: kvq.kv_lds_probe(blocks, it_lds, sink.data_ptr(), st), n, lambda: None)
+    tflops = flop / (statistics.median(ms_m) * 1e-3) / 1e12
+    lds_tbs = lds_bytes / (statistics.median(ms_l) * 1e-3) / 1e12
+    return {"mfma_kernel": "mfma_probe_kernel (v_mfma_f32_32x32x16_f16, 2 chains, operands in registers)",
+            "mfma_tflops": round(tflops, 1), "mfma_frac_of_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+            "lds_kernel": "lds_probe_kernel (ds_read_b128, 1 KiB per wave and read, conflict-free)",
+            "lds_tbs": round(lds_tbs, 2)}
+
+
+def latent_lds_bytes(cfg, nq=1):
+    """LDS bytes the latent decode reads per launch: each of a workgroup's 4
+    waves reads the whole dequantised 32-token tile, its keys (576 fp16/bf16
+    channels) for S = K Q^T and its values (512 channels, transposed) for P V."""
+    tiles = nq * cfg.batch * cfg.context / 32
+    return tiles * 4 * 32 * (cfg.key_width + cfg.head_dim) * 2
+
+
 def run_workload(name, args, dev, flush, cpu):
     import torch
 
@@ -458,8 +493,7 @@ def run_workload(name, args, dev, flush, cpu):
             rec["roofline"] = {"bound": "mfma" if mfma else "alu", "achieved": round(ach, 2), "peak": peak,
                                "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
                                "kernel": "sparse split-context attention", "kernel_us": round(kern_us, 2)}
-    if cpu:
-        rec["_cfg"] = cfg
+    rec["_cfg"] = cfg
     if not args.no_graph:
         del graph
     del cache, ws, out, k_new, v_new, q
@@ -518,6 +552,19 @@ def main():
         print(f"bench: {name} ...", file=sys.stderr, flush=True)
         records[name] = run_workload(name, args, dev, flush, not args.no_cpu_baseline)
     ref = stream_read_reference(torch, kvq, dev, flush, args.steps)
+    cref = compute_references(torch, kvq, dev, args.steps)
+    for name, rec in records.items():
+        cfg = rec.get("_cfg")
+        if cfg is not None and cfg.fmt == "latent" and rec["roofline"].get("bound") == "mfma":
+            r = rec["roofline"]
+            lds = latent_lds_bytes(cfg, rec["config"].get("queries_per_seq", 1))
+            r["measured_ceilings"] = {
+                "mfma_tflops": cref["mfma_tflops"],
+                "frac_of_measured_mfma": round(r["achieved"] / cref["mfma_tflops"], 4),
+                "mfma_floor_us": round(r["achieved"] * r["kernel_us"] / cref["mfma_tflops"], 1),
+                "lds_bytes_per_launch": int(lds),
+                "lds_tbs": cref["lds_tbs"],
+                "lds_floor_us": round(lds / (cref["lds_tbs"] * 1e12) * 1e6, 1)}
     if not args.no_cpu_baseline:
         for name in names:
             cfg = records[name].pop("_cfg")
@@ -545,7 +592,8 @@ def main():
         "timing": h["timing"],
         "roofline": h["roofline"],
         "stream_read_reference": ref,
-        "workloads": {n: {k: v for k, v in r.items() if k != "workload"} for n, r in records.items()},
+        "compute_reference": cref,
+        "workloads": {n: {k: v for k, v in r.items() if k not in ("workload", "_cfg")} for n, r in records.items()},
     }
     if "cpu_baseline" in h:
         res["cpu_baseline"] = h["cpu_baseline"]

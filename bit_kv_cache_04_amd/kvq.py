@@ -24,7 +24,8 @@ BUFFERS = ["k_codes", "k_scale", "k_zero", "k_sketch", "k_norm", "k_rnorm",
 EXPORTED = ["kv_buffer_bytes", "kv_bytes_per_token", "kv_quant_append", "kv_quant_append_ragged", "kv_decode_attention",
             "kv_lloyd_max_gaussian", "kv_make_rotation", "kv_make_hadamard_rotation",
             "kv_make_projection", "kv_status_string", "kv_hsi_candidates", "kv_hsi_select",
-            "kv_decode_attention_sparse", "kv_stream_read", "kv_decode_attention_static"]
+            "kv_decode_attention_sparse", "kv_stream_read", "kv_decode_attention_static", "kv_mfma_probe",
+            "kv_lds_probe"]
 
 
 class KvError(RuntimeError):
@@ -100,6 +101,10 @@ def lib():
         L.kv_decode_attention_static.restype = ctypes.c_int
         L.kv_stream_read.argtypes = [vp, sz, vp, vp]
         L.kv_stream_read.restype = ctypes.c_int
+        L.kv_mfma_probe.argtypes = [i32, i32, vp, vp]
+        L.kv_mfma_probe.restype = ctypes.c_int
+        L.kv_lds_probe.argtypes = [i32, i32, vp, vp]
+        L.kv_lds_probe.restype = ctypes.c_int
         L.kv_status_string.argtypes = [ctypes.c_int]
         L.kv_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -223,6 +228,16 @@ def kv_status_string(status: int) -> str:
 def kv_stream_read(src_ptr, nbytes, sink_ptr, stream=0):
     """The streaming-read reference kernel (kvq_probe.h)."""
     _check("kv_stream_read", lib().kv_stream_read(src_ptr, nbytes, sink_ptr, stream))
+
+
+def kv_mfma_probe(blocks, iters, sink_ptr, stream=0):
+    """The matrix-core reference kernel (kvq_probe.h): blocks * 4 * iters * 8 products of 32 x 32 x 16."""
+    _check("kv_mfma_probe", lib().kv_mfma_probe(blocks, iters, sink_ptr, stream))
+
+
+def kv_lds_probe(blocks, iters, sink_ptr, stream=0):
+    """The LDS read reference kernel (kvq_probe.h): blocks * 4 * iters * 8 KiB read from LDS."""
+    _check("kv_lds_probe", lib().kv_lds_probe(blocks, iters, sink_ptr, stream))
 
 
 def kv_decode_attention_static(cache: KVCache, q_ptr, q_dtype, num_q_heads, seq_lens_ptr, max_seq_len, scale,

@@ -317,6 +317,16 @@ def test_stream_read_validation():
     assert L.kv_stream_read(FAKE, 0, FAKE, None) == EINVAL
 
 
+def test_compute_probe_validation():
+    L = kvq.lib()
+    for fn in (L.kv_mfma_probe, L.kv_lds_probe):
+        assert fn(0, 16, FAKE, None) == EINVAL          # no workgroups
+        assert fn(65536, 16, FAKE, None) == EINVAL      # past the grid limit
+        assert fn(4, 0, FAKE, None) == EINVAL           # no iterations
+        assert fn(4, (1 << 20) + 1, FAKE, None) == EINVAL
+        assert fn(4, 16, None, None) == EINVAL          # no sink
+
+
 def test_decode_split_cap_with_windows():
     # the merge holds at most 1024 partial rows per query: the packed splits
     # yield to the window's 64-position splits, and a window of 1024 such
