@@ -314,8 +314,13 @@ def run_workload(name, args, dev, flush, cpu):
         per_seq = cfg.context // args.page_tokens
         table = np.random.default_rng(cfg.seed).permutation(cfg.batch * per_seq).reshape(cfg.batch, per_seq)
         paging = dict(page_tokens=args.page_tokens, num_pages=cfg.batch * per_seq, block_table=table)
+    rot_kind = {}
+    if cfg.fmt == "turbo" and args.butterfly:
+        # the structured rotation applied as a butterfly: no dense matrix at all
+        rot_kind = dict(rotation=kvq.ROT_HADAMARD_BITREV if args.rotation == "hadamard" else kvq.ROT_HADAMARD)
+        consts.pop("rot")
     cache = PackedKVCache(cfg.fmt, cfg.batch, cfg.hkv, cfg.head_dim, cfg.context, cfg.rope_dim, device=dev,
-                          constants=consts, sink_tokens=args.sink, recent_tokens=args.recent, **paging)
+                          constants=consts, sink_tokens=args.sink, recent_tokens=args.recent, **paging, **rot_kind)
     T = cfg.context
     # prefill the first T - n tokens (untimed), one sequence and 16K tokens at a
     # time to bound input memory
@@ -520,6 +525,9 @@ def main():
     ap.add_argument("--queries", type=int, default=1,
                     help="query tokens per sequence (drafted positions checked in one pass); the step "
                          "appends that many tokens")
+    ap.add_argument("--butterfly", action="store_true",
+                    help="with --rotation hadamard / hadamard_plain: apply R as a Hadamard butterfly "
+                         "(layout.rotation) instead of a dense matrix")
     ap.add_argument("--rotation", default="haar", choices=["haar", "hadamard", "hadamard_plain"],
                     help="TurboQuant rotation: a Haar draw, or the Hadamard transform with (or without) "
                          "the bit-reversal permutation")
@@ -533,6 +541,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph replay")
     args = ap.parse_args()
+    if args.butterfly and args.rotation == "haar":
+        ap.error("--butterfly needs --rotation hadamard or hadamard_plain (a Haar rotation has no butterfly)")
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               f"(the decode shards by sequence and KV head with no exchange; see the design notes)",

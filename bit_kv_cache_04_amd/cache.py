@@ -112,14 +112,17 @@ def hsi_select(pool_scores, pool, pool_n, top_k=512, out=None):
 
 class PackedKVCache:
     def __init__(self, fmt, batch, num_kv_heads, head_dim, capacity, rope_dim=0, device="cuda",
-                 constants=None, sink_tokens=0, recent_tokens=0, page_tokens=0, num_pages=0, block_table=None):
+                 constants=None, sink_tokens=0, recent_tokens=0, page_tokens=0, num_pages=0, block_table=None,
+                 rotation=0):
         """Paged storage: page_tokens > 0, a pool of num_pages pages, and block_table
         int [batch][capacity // page_tokens] naming each sequence's pages (default:
-        sequence b's page j is pool page b * capacity // page_tokens + j)."""
+        sequence b's page j is pool page b * capacity // page_tokens + j).  rotation:
+        TURBO's kind of R (kvq.ROT_*); with a Hadamard kind the constants need no "rot"."""
         self.fmt, self.device = fmt, torch.device(device)
         self.B, self.H, self.d, self.T, self.rope = batch, num_kv_heads, head_dim, capacity, rope_dim
         self.sink, self.recent = sink_tokens, recent_tokens
         self.P, self.num_pages = page_tokens, num_pages
+        self.rotation = rotation
         self.table = None
         if page_tokens:
             per_seq = capacity // page_tokens
@@ -127,7 +130,7 @@ class PackedKVCache:
                 block_table = np.arange(batch * per_seq, dtype=np.int32).reshape(batch, per_seq)
             self.table = torch.as_tensor(np.ascontiguousarray(block_table, dtype=np.int32)).to(self.device)
         self.layout = make_layout(fmt, batch, num_kv_heads, head_dim, capacity, rope_dim, sink_tokens,
-                                  recent_tokens, page_tokens, num_pages)
+                                  recent_tokens, page_tokens, num_pages, rotation)
         self.bufs = {}
         ptrs = []
         for i, name in enumerate(BUFFERS):
@@ -153,7 +156,7 @@ class PackedKVCache:
         sub.__dict__.update(self.__dict__)
         sub.B = 1
         sub.layout = make_layout(self.fmt, 1, self.H, self.d, self.T, self.rope, self.sink, self.recent, self.P,
-                                 self.num_pages)
+                                 self.num_pages, self.rotation)
         # a paged pool is shared; per-sequence buffers (windows, staging) are sliced
         pool = lambda n: self.P and BUFFERS.index(n) < BUFFERS.index("sink_k")  # noqa: E731
         sub.bufs = {n: (t if pool(n) else t.view(self.B, -1)[b]) for n, t in self.bufs.items()}

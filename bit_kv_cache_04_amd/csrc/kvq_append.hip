@@ -846,7 +846,7 @@ qjl_append_kernel(const InT* __restrict__ k, const InT* __restrict__ v,
 // bf16/fp32, so each product term is exact and the fp64 sums match the
 // exact-arithmetic decisions except at exact ties.
 template <typename InT, bool WITH_SKETCH>
-__device__ __forceinline__ void turbo_body(const InT* __restrict__ x, const float* __restrict__ rot,
+__device__ __forceinline__ void turbo_body(const InT* __restrict__ x, RotArg ra,
                                            const float* __restrict__ proj, const float* __restrict__ levels,
                                            const float* __restrict__ thresh, uint8_t* __restrict__ codes,
                                            uint8_t* __restrict__ sketch, uint16_t* __restrict__ norm_out,
@@ -854,7 +854,8 @@ __device__ __forceinline__ void turbo_body(const InT* __restrict__ x, const floa
                                            AppendPos pos, uint16_t* R_lds, uint16_t* S_lds,
                                            double (*scratch)[16 * 129], uint8_t (*idx_lds)[16 * 128]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  stage_bf16_matrix(rot, R_lds);  // bf16-valued
+  const bool dense = ra.kind == KV_ROT_DENSE;
+  if (dense) stage_bf16_matrix(ra.rot, R_lds);  // bf16-valued
   if (WITH_SKETCH) stage_bf16_matrix(proj, S_lds);
   __syncthreads();
   const double t0 = thresh[0], t1 = thresh[1], t2 = thresh[2];
@@ -864,13 +865,14 @@ __device__ __forceinline__ void turbo_body(const InT* __restrict__ x, const floa
   for (size_t base = ((size_t)blockIdx.x * 4 + wave) * 16; base < rows; base += (size_t)gridDim.x * 64) {
     // stage 16 tokens x 128 as double, zero past the last row: lane takes token
     // lane / 4, channels 32 (lane % 4) + [0, 32), all loads in flight at once
+    // (a structured rotation: channel c at position rot_perm(c), its own inverse)
     {
       const int tk = lane >> 2, c0 = 32 * (lane & 3);
       const bool ok = base + tk < rows;
       float xv[32];
       load32_as_f32(x + (base + (ok ? tk : 0)) * 128 + c0, xv);
 #pragma unroll
-      for (int j = 0; j < 32; ++j) xs[tk * 129 + c0 + j] = ok ? (double)xv[j] : 0.0;
+      for (int j = 0; j < 32; ++j) xs[tk * 129 + (dense ? c0 + j : rot_perm(c0 + j, ra.kind))] = ok ? (double)xv[j] : 0.0;
     }
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
@@ -884,14 +886,32 @@ __device__ __forceinline__ void turbo_body(const InT* __restrict__ x, const floa
     f64x4 acc[8];
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) acc[nt] = f64x4{0.0, 0.0, 0.0, 0.0};
-    for (int ks = 0; ks < 32; ++ks) {
-      const double a = xs[col * 129 + ks * 4 + kq];
+    if (dense) {
+      for (int ks = 0; ks < 32; ++ks) {
+        const double a = xs[col * 129 + ks * 4 + kq];
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const double b = (double)bf16_to_f32(R_lds[(nt * 16 + col) * kSPad + ks * 4 + kq]);
-        acc[nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[nt], 0, 0, 0);
+        for (int nt = 0; nt < 8; ++nt) {
+          const double b = (double)bf16_to_f32(R_lds[(nt * 16 + col) * kSPad + ks * 4 + kq]);
+          acc[nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[nt], 0, 0, 0);
+        }
       }
+    } else {
+      // the butterfly over this wave's 16 tokens in place (the norms above have
+      // read them), then y = mag (H x') in the product's element order
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_wave_barrier();
+      for (int h = 1; h < 128; h <<= 1) {
+        hadamard_stage(xs, 16, 129, h, lane, 64);
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_wave_barrier();
+      }
+      const double mag = (double)ra.mag;
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[nt][i] = mag * xs[(kq + 4 * i) * 129 + nt * 16 + col];
     }
+    __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
     // quantise: the fp64 16x16x4 product leaves y[token kq + 4i][row nt*16 + col]
     // in element i of this lane's accumulators
@@ -993,7 +1013,7 @@ __device__ __forceinline__ void turbo_body(const InT* __restrict__ x, const floa
 // (blockIdx.y = 1) in one launch; each wave takes 16-token tiles.
 template <typename InT>
 __global__ void __launch_bounds__(256) turbo_append_kernel(const InT* __restrict__ k, const InT* __restrict__ v,
-                                                           const float* __restrict__ rot,
+                                                           RotArg rot,
                                                            const float* __restrict__ proj,
                                                            const float* __restrict__ levels,
                                                            const float* __restrict__ thresh, uint8_t* kc,
@@ -1020,7 +1040,7 @@ __global__ void __launch_bounds__(256) turbo_append_kernel(const InT* __restrict
 // the same order as in turbo_body, so the codes and signs are the same.
 template <typename InT>
 __global__ void __launch_bounds__(512) turbo_append_small_kernel(
-    const InT* __restrict__ k, const InT* __restrict__ v, const float* __restrict__ rot,
+    const InT* __restrict__ k, const InT* __restrict__ v, RotArg ra,
     const float* __restrict__ proj, const float* __restrict__ levels, const float* __restrict__ thresh,
     uint8_t* __restrict__ kc, uint8_t* __restrict__ sketch, uint16_t* __restrict__ knorm,
     uint16_t* __restrict__ krnorm, uint8_t* __restrict__ vc, uint16_t* __restrict__ vnorm, size_t rows, int n,
@@ -1039,11 +1059,12 @@ __global__ void __launch_bounds__(512) turbo_append_small_kernel(
   // this wave's 16 rows of R (and S, keys only): 8 KB contiguous each, read
   // with full-line loads (lane l, load j: float4 64 j + l of the rows) and kept
   // in LDS as bf16 (both matrices are bf16-valued)
+  const bool dense = ra.kind == KV_ROT_DENSE;
   float4 mr[2][8];
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
-    const float4* src = reinterpret_cast<const float4*>((m == 0 ? rot : proj) + 16 * w * 128);
-    if (m == 0 || keys) {
+    const float4* src = reinterpret_cast<const float4*>((m == 0 ? ra.rot : proj) + 16 * w * 128);
+    if (m == 0 ? dense : keys) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) mr[m][j] = src[64 * j + lane];
     }
@@ -1053,14 +1074,17 @@ __global__ void __launch_bounds__(512) turbo_append_small_kernel(
     const int tk = tid >> 5, c0 = 4 * (tid & 31);
     const bool ok = base + tk < rows;
     const float4 xv = load4_as_f32(x + (base + (ok ? tk : 0)) * 128 + c0);
-    xs[tk * 129 + c0] = ok ? (double)xv.x : 0.0;
-    xs[tk * 129 + c0 + 1] = ok ? (double)xv.y : 0.0;
-    xs[tk * 129 + c0 + 2] = ok ? (double)xv.z : 0.0;
-    xs[tk * 129 + c0 + 3] = ok ? (double)xv.w : 0.0;
+    // a structured rotation: channel c at position rot_perm(c)
+    const int p0 = dense ? c0 : rot_perm(c0, ra.kind), p1 = dense ? c0 + 1 : rot_perm(c0 + 1, ra.kind);
+    const int p2 = dense ? c0 + 2 : rot_perm(c0 + 2, ra.kind), p3 = dense ? c0 + 3 : rot_perm(c0 + 3, ra.kind);
+    xs[tk * 129 + p0] = ok ? (double)xv.x : 0.0;
+    xs[tk * 129 + p1] = ok ? (double)xv.y : 0.0;
+    xs[tk * 129 + p2] = ok ? (double)xv.z : 0.0;
+    xs[tk * 129 + p3] = ok ? (double)xv.w : 0.0;
   }
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
-    if (m == 0 || keys) {
+    if (m == 0 ? dense : keys) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int f = 64 * j + lane, r = f >> 5, c4 = 4 * (f & 31);
@@ -1080,11 +1104,23 @@ __global__ void __launch_bounds__(512) turbo_append_small_kernel(
   ss += __shfl_xor(ss, 32);
   const double nrm = sqrt(ss);
   f64x4 acc = f64x4{0.0, 0.0, 0.0, 0.0};
-  const uint16_t* Rw = &rows_lds[w][0][col * kSPad + kq];
+  if (dense) {
+    const uint16_t* Rw = &rows_lds[w][0][col * kSPad + kq];
 #pragma unroll
-  for (int ks = 0; ks < 32; ++ks)
-    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xs[col * 129 + ks * 4 + kq], (double)bf16_to_f32(Rw[4 * ks]), acc,
-                                               0, 0, 0);
+    for (int ks = 0; ks < 32; ++ks)
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xs[col * 129 + ks * 4 + kq], (double)bf16_to_f32(Rw[4 * ks]),
+                                                 acc, 0, 0, 0);
+  } else {
+    // the butterfly over all 16 tokens in place once every wave has read its
+    // norms, then y = mag (H x') for this wave's rows in the product's order
+    __syncthreads();
+    for (int h = 1; h < 128; h <<= 1) {
+      hadamard_stage(xs, 16, 129, h, tid, 512);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = (double)ra.mag * xs[(kq + 4 * i) * 129 + 16 * w + col];
+  }
   const double t0 = thresh[0], t1 = thresh[1], t2 = thresh[2];
   const double lv0 = levels[0], lv1 = levels[1], lv2 = levels[2], lv3 = levels[3];
   // element i of acc is y[token kq + 4 i][row 16 w + col]; the 2-bit codes of
@@ -1267,13 +1303,13 @@ int append_typed(const kv_cache* c, const InT* k, const InT* v, const AppendPos&
     case KV_FMT_TURBO:
       if (rows <= kTurboSmallRows) {
         turbo_append_small_kernel<InT><<<dim3((unsigned)((rows + 15) / 16), 2), 512, 0, st>>>(
-            k, v, c->rot, c->proj, c->lm_levels, c->lm_thresh, kc, static_cast<uint8_t*>(c->buf[KV_BUF_K_SKETCH]),
+            k, v, rot_arg(c), c->proj, c->lm_levels, c->lm_thresh, kc, static_cast<uint8_t*>(c->buf[KV_BUF_K_SKETCH]),
             static_cast<uint16_t*>(c->buf[KV_BUF_K_NORM]), static_cast<uint16_t*>(c->buf[KV_BUF_K_RNORM]), vc,
             static_cast<uint16_t*>(c->buf[KV_BUF_V_NORM]), rows, n, cap, pos);
         break;
       }
       turbo_append_kernel<InT><<<dim3(persistent_blocks(rows), 2), 256, 0, st>>>(
-          k, v, c->rot, c->proj, c->lm_levels, c->lm_thresh, kc, static_cast<uint8_t*>(c->buf[KV_BUF_K_SKETCH]),
+          k, v, rot_arg(c), c->proj, c->lm_levels, c->lm_thresh, kc, static_cast<uint8_t*>(c->buf[KV_BUF_K_SKETCH]),
           static_cast<uint16_t*>(c->buf[KV_BUF_K_NORM]), static_cast<uint16_t*>(c->buf[KV_BUF_K_RNORM]), vc,
           static_cast<uint16_t*>(c->buf[KV_BUF_V_NORM]), rows, n, cap, pos);
       break;

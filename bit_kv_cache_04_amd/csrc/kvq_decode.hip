@@ -554,7 +554,7 @@ constexpr int kTurboPrepThreads = 384;
 
 template <typename QT>
 __global__ void __launch_bounds__(kTurboPrepThreads) prep_turbo_kernel(
-    const QT* __restrict__ q, const float* __restrict__ rot, const float* __restrict__ proj,
+    const QT* __restrict__ q, RotArg ra, const float* __restrict__ proj,
     const float* __restrict__ levels, float scale_log2, float kappa, float* __restrict__ out,
     uint8_t* __restrict__ pieces) {
   __shared__ float qin[128];
@@ -564,7 +564,9 @@ __global__ void __launch_bounds__(kTurboPrepThreads) prep_turbo_kernel(
   const int tid = threadIdx.x;
   const size_t row = blockIdx.x;
   const bool prod = tid < 128;
-  if (prod) qin[tid] = load_as_f32(q + row * 128, tid);
+  const bool dense = ra.kind == KV_ROT_DENSE;
+  // a structured rotation: channel rot_perm(k) at position k, then the butterfly
+  if (prod) (dense ? qin : qrot)[tid] = load_as_f32(q + row * 128, dense ? tid : rot_perm(tid, ra.kind));
   const float lv0 = levels[0], lv1 = levels[1], lv2 = levels[2], lv3 = levels[3];
   __syncthreads();
   auto matvec = [&](const float* __restrict__ m, const float* x) {
@@ -585,9 +587,20 @@ __global__ void __launch_bounds__(kTurboPrepThreads) prep_turbo_kernel(
     return acc0 + acc1;
   };
   float rq = 0.f, srq = 0.f;
-  if (prod) {
-    rq = matvec(rot, qin);
-    qrot[tid] = rq;
+  if (dense) {
+    if (prod) {
+      rq = matvec(ra.rot, qin);
+      qrot[tid] = rq;
+    }
+  } else {
+    for (int h = 1; h < 128; h <<= 1) {
+      hadamard_stage(qrot, 1, 128, h, tid, kTurboPrepThreads);
+      __syncthreads();
+    }
+    if (prod) {
+      rq = ra.mag * qrot[tid];
+      qrot[tid] = rq;
+    }
   }
   __syncthreads();
   if (prod) {
@@ -645,7 +658,7 @@ constexpr int merge_max_waves() {
 template <int NJ>
 __global__ void __launch_bounds__(64 * merge_max_waves<NJ>()) merge_kernel(const float* __restrict__ part,
                                                                            int splits, int rot_splits, int dv,
-                                                                           int fmt, const float* __restrict__ rot,
+                                                                           int fmt, RotArg ra,
                                                                            float* __restrict__ out) {
   constexpr int CW = 64 * NJ, MW = merge_max_waves<NJ>();
   constexpr bool kTurboCols = NJ == 2;  // TURBO rows (dv = 128) take this column blocking
@@ -771,6 +784,16 @@ __global__ void __launch_bounds__(64 * merge_max_waves<NJ>()) merge_kernel(const
   if constexpr (kTurboCols) {
     if (!turbo) return;  // CW == dv below
     __syncthreads();
+    if (ra.kind != KV_ROT_DENSE) {
+      // R^T o = mag (H o) read at the reversed positions
+      for (int h = 1; h < CW; h <<= 1) {
+        hadamard_stage(ov, 1, CW, h, tid, nthr);
+        __syncthreads();
+      }
+      for (int c = tid; c < CW; c += nthr) dst[c] = ra.mag * ov[rot_perm(c, ra.kind)] + ovo[c];
+      return;
+    }
+    const float* __restrict__ rot = ra.rot;
     // P slices of the rows of R: thread (q, c) sums j in [q * CW / P, (q + 1) * CW / P)
     const int P = nthr >= CW ? min(nthr / CW, MW) : 1;
     const int span = CW / P;
@@ -793,7 +816,7 @@ __global__ void __launch_bounds__(64 * merge_max_waves<NJ>()) merge_kernel(const
 // Column blocks: TURBO and many rows take the whole row per block (up to 8
 // columns per lane); few rows take 64-column blocks so that more workgroups
 // share the loads; otherwise 128 columns.  Waves: about four splits each.
-void launch_merge(const float* part, int rows, int splits, int rot_splits, int dv, int fmt, const float* rot,
+void launch_merge(const float* part, int rows, int splits, int rot_splits, int dv, int fmt, RotArg rot,
                   float* out, hipStream_t st) {
   int nj;
   if (fmt == KV_FMT_TURBO || rows >= 2048) nj = dv / 64;
@@ -953,7 +976,7 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
       if (rc != KV_OK) return rc;
     }
     if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess) return KV_EDEVICE;
-    launch_merge(part, rows, part_splits, plan.splits, L.head_dim, L.format, c->rot, out, st);
+    launch_merge(part, rows, part_splits, plan.splits, L.head_dim, L.format, rot_arg(c), out, st);
     return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
   }
   const bool mfma =
@@ -975,11 +998,11 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
   const bool q_direct = kivi_fold && q_dtype == KV_DT_F32;
   if (L.format == KV_FMT_TURBO) {
     if (q_dtype == KV_DT_F32)
-      prep_turbo_kernel<float><<<rows, kTurboPrepThreads, 0, st>>>(static_cast<const float*>(q), c->rot, c->proj,
+      prep_turbo_kernel<float><<<rows, kTurboPrepThreads, 0, st>>>(static_cast<const float*>(q), rot_arg(c), c->proj,
                                                                    c->lm_levels, scale * kLog2e, kappa, qv, qpieces);
     else
       prep_turbo_kernel<uint16_t><<<rows, kTurboPrepThreads, 0, st>>>(
-          static_cast<const uint16_t*>(q), c->rot, c->proj, c->lm_levels, scale * kLog2e, kappa, qv, qpieces);
+          static_cast<const uint16_t*>(q), rot_arg(c), c->proj, c->lm_levels, scale * kLog2e, kappa, qv, qpieces);
   } else if (!(mfma && L.format == KV_FMT_FP4) && !q_direct) {
     if (q_dtype == KV_DT_F32)
       prep_query_kernel<float><<<rows, 128, 0, st>>>(static_cast<const float*>(q), qw_in, qw_out, L.format, c->proj,
@@ -1025,7 +1048,7 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     if (windowed) launch_window(c, q, q_dtype, num_q_heads, nq, seq_lens, max_seq_len, scale, part, part_splits,
                                 plan.splits, st);
     if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess) return KV_EDEVICE;
-    launch_merge(part, rows, part_splits, plan.splits, L.head_dim, L.format, c->rot, out, st);
+    launch_merge(part, rows, part_splits, plan.splits, L.head_dim, L.format, rot_arg(c), out, st);
     return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
   }
   if (mfma) {
@@ -1068,7 +1091,7 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     if (windowed) launch_window(c, q, q_dtype, num_q_heads, nq, seq_lens, max_seq_len, scale, part, part_splits,
                                 plan.splits, st);
     if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess) return KV_EDEVICE;
-    launch_merge(part, rows, part_splits, plan.splits, L.head_dim, L.format, c->rot, out, st);
+    launch_merge(part, rows, part_splits, plan.splits, L.head_dim, L.format, rot_arg(c), out, st);
     return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
   }
 
@@ -1106,7 +1129,7 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
     }
     if (!kivi_fold) launch_kivi_tail(a, tail_split, B, st);
     if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess) return KV_EDEVICE;
-    launch_merge(part, rows, part_splits, plan.splits, L.head_dim, L.format, c->rot, out, st);
+    launch_merge(part, rows, part_splits, plan.splits, L.head_dim, L.format, rot_arg(c), out, st);
     return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
   }
 
@@ -1130,7 +1153,7 @@ int launch_decode(const kv_cache* c, const void* q, int q_dtype, int num_q_heads
   if (windowed) launch_window(c, q, q_dtype, num_q_heads, nq, seq_lens, max_seq_len, scale, part, part_splits,
                               plan.splits, st);
   if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), st) != hipSuccess) return KV_EDEVICE;
-  launch_merge(part, rows, part_splits, plan.splits, L.head_dim, L.format, c->rot, out, st);
+  launch_merge(part, rows, part_splits, plan.splits, L.head_dim, L.format, rot_arg(c), out, st);
   return hipGetLastError() == hipSuccess ? KV_OK : KV_EDEVICE;
 }
 

@@ -147,4 +147,33 @@ __device__ __forceinline__ float max_xor32(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// ---------------------------------------------------------------- structured rotation
+
+// The structured rotation R = mag H P (page "TurboQuant vs OSCAR vs EpiCache",
+// section "quantization frontiers", the OSCAR paragraph: a Hadamard transform
+// behind a bit-reversal permutation): (R x)[i] = mag sum_k (-1)^popcount(i & k)
+// x[rev(k)], and (R^T y)[j] = mag (H y)[rev(j)], rev the reversal of the seven
+// index bits of a 128-channel row (the identity for KV_ROT_HADAMARD).
+__device__ __forceinline__ int rot_perm(int k, int kind) {
+  return kind == KV_ROT_HADAMARD_BITREV ? (int)(__builtin_bitreverse32((uint32_t)k) >> 25) : k;
+}
+
+// Stage h (1, 2, 4, ..., 64) of the in-place Walsh-Hadamard butterfly over
+// `rows` rows of 128 values at x + r * pitch: butterfly p (of rows * 64) pairs
+// positions i and i + h, i the p % 64-th index whose bit h is clear, taken by
+// the calling thread for p = first, first + step, ...  After the seven stages
+// row r holds H times what it held (Sylvester order, unnormalised).  The caller
+// orders the stages (a barrier between them).
+template <typename T>
+__device__ __forceinline__ void hadamard_stage(T* x, int rows, int pitch, int h, int first, int step) {
+  for (int p = first; p < rows * 64; p += step) {
+    const int b = p & 63;
+    const int i = ((b & ~(h - 1)) << 1) | (b & (h - 1));
+    T* v = x + (size_t)(p >> 6) * pitch;
+    const T a = v[i], c = v[i + h];
+    v[i] = a + c;
+    v[i + h] = a - c;
+  }
+}
+
 }  // namespace kvq

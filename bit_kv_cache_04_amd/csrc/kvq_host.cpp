@@ -23,6 +23,9 @@ int check_layout(const kv_layout* L) {
   if (L->page_tokens > 0 && (L->page_tokens < 32 || (L->page_tokens & (L->page_tokens - 1)) ||
                              L->capacity % L->page_tokens || L->num_pages < 1))
     return KV_EINVAL;
+  // structured rotations: TurboQuant only
+  if (L->rotation < KV_ROT_DENSE || L->rotation > KV_ROT_HADAMARD) return KV_EINVAL;
+  if (L->rotation != KV_ROT_DENSE && L->format != KV_FMT_TURBO) return KV_EINVAL;
   // bf16 sink / recent windows: every per-head format (the latent cache has none)
   if ((L->sink_tokens || L->recent_tokens) && (L->format == KV_FMT_LATENT_FP4 || L->format == KV_FMT_BF16))
     return KV_EUNSUPPORTED;
@@ -62,7 +65,9 @@ int check_cache(const kv_cache* c) {
   for (int b = 0; b < KV_BUF_COUNT; ++b)
     if (kv_buffer_bytes(&c->layout, b) && !c->buf[b]) return KV_EINVAL;
   int f = c->layout.format;
-  if (f == KV_FMT_TURBO && (!c->rot || !c->proj || !c->lm_levels || !c->lm_thresh)) return KV_EINVAL;
+  if (f == KV_FMT_TURBO && ((!c->rot && c->layout.rotation == KV_ROT_DENSE) || !c->proj || !c->lm_levels ||
+                            !c->lm_thresh))
+    return KV_EINVAL;
   if (f == KV_FMT_QJL1_FP4V && !c->proj) return KV_EINVAL;
   if (c->layout.page_tokens > 0 && !c->block_table) return KV_EINVAL;
   // the append kernels stage R and S with 16-byte loads
@@ -279,6 +284,10 @@ double std_normal_pdf(double z) { return std::exp(-0.5 * z * z) / std::sqrt(2.0 
 double std_normal_cdf(double z) { return 0.5 * std::erfc(-z / std::sqrt(2.0)); }
 
 }  // namespace
+
+namespace kvq {
+float hadamard_magnitude(int d) { return bf16_round(1.0 / std::sqrt((double)d)); }
+}  // namespace kvq
 
 extern "C" int kv_lloyd_max_gaussian(int32_t bits, int32_t dim, float* levels, float* thresholds) {
   if (bits < 1 || bits > 4 || dim < 1 || !levels || !thresholds) return KV_EINVAL;

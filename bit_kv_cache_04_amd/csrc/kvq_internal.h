@@ -23,6 +23,22 @@ struct PageMap {
   int num_pages;         // pages in the pool (contiguous: batch)
   int shift;             // paged: log2(tokens) (pages are a power of two)
 };
+// bf16(1/sqrt(d)): the magnitude of every entry of the structured rotation
+float hadamard_magnitude(int d);
+
+// TurboQuant's rotation as the kernels take it: the dense matrix (kind
+// KV_ROT_DENSE) or a Hadamard transform, behind a bit-reversal of the channels
+// for KV_ROT_HADAMARD_BITREV, scaled by mag.
+struct RotArg {
+  const float* rot;
+  int kind;
+  float mag;
+};
+inline RotArg rot_arg(const kv_cache* c) {
+  const int kind = c->layout.rotation;
+  return RotArg{c->rot, kind, kind == KV_ROT_DENSE ? 0.f : hadamard_magnitude(c->layout.head_dim)};
+}
+
 inline PageMap page_map(const kv_cache* c) {
   const kv_layout& L = c->layout;
   if (L.page_tokens > 0) {

@@ -39,7 +39,12 @@ class KVLayout(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("rope_dim", ctypes.c_int32), ("capacity", ctypes.c_int32),
                 ("group", ctypes.c_int32), ("qjl_m", ctypes.c_int32), ("lm_bits", ctypes.c_int32),
                 ("sink_tokens", ctypes.c_int32), ("recent_tokens", ctypes.c_int32),
-                ("page_tokens", ctypes.c_int32), ("num_pages", ctypes.c_int32)]
+                ("page_tokens", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("rotation", ctypes.c_int32)]
+
+
+# enum kv_rotation: how TURBO applies R (a dense matrix, or the Hadamard butterfly
+# with or without the bit-reversal of the channels)
+ROT_DENSE, ROT_HADAMARD_BITREV, ROT_HADAMARD = 0, 1, 2
 
 
 class KVCache(ctypes.Structure):
@@ -112,16 +117,17 @@ def lib():
 
 
 def make_layout(fmt, batch, num_kv_heads, head_dim, capacity, rope_dim=0, sink=0, recent=0, page_tokens=0,
-                num_pages=0):
+                num_pages=0, rotation=ROT_DENSE):
     """A kv_layout with the format's fixed group / sketch / codebook parameters
     (sink / recent: tokens kept bf16 at the start and end of each sequence;
-    page_tokens / num_pages: paged storage in a pool of pages)."""
+    page_tokens / num_pages: paged storage in a pool of pages; rotation: the
+    TURBO rotation's kind, enum kv_rotation)."""
     f = FMT[fmt] if isinstance(fmt, str) else int(fmt)
     group = {1: 32, 2: 16, 4: 16, 5: 16}.get(f, 0)
     qjl_m = 128 if f in (3, 4) else 0
     lm_bits = 2 if f == 3 else 0
     return KVLayout(f, batch, num_kv_heads, head_dim, rope_dim, capacity, group, qjl_m, lm_bits, sink, recent,
-                    page_tokens, num_pages)
+                    page_tokens, num_pages, rotation)
 
 
 def _check(fn, st):

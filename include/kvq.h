@@ -134,7 +134,22 @@ typedef struct kv_layout {
   int32_t recent_tokens; /* trailing tokens kept bf16 (mixed precision), else 0 */
   int32_t page_tokens;   /* paged storage: tokens per page, else 0 */
   int32_t num_pages;     /* paged storage: pages in the pool, else 0 */
+  int32_t rotation;      /* TURBO: enum kv_rotation; every other format 0 */
 } kv_layout;
+
+/* How TURBO applies its rotation R (layout.rotation).  KV_ROT_DENSE reads R from
+ * kv_cache.rot as a d x d matrix.  The two structured kinds are the rotation
+ * kv_make_hadamard_rotation writes (bit_reverse 1 or 0): R = H P / sqrt(d), a
+ * Hadamard transform behind a bit-reversal permutation of the channels (page
+ * "TurboQuant vs OSCAR vs EpiCache", section "quantization frontiers", the
+ * OSCAR paragraph).  With them the append, the query preparation and the merge
+ * apply R (and R^T) as a butterfly in O(d log d) instead of a d x d product,
+ * every entry being +-bf16(1/sqrt(d)); the results are those of the dense
+ * product with that matrix (bit for bit in the append wherever its fp64 sums
+ * are exact, as they are for bf16 inputs), and kv_cache.rot is not read (it may
+ * be NULL).  Any other value, or a nonzero one for another format, is
+ * KV_EINVAL. */
+enum kv_rotation { KV_ROT_DENSE = 0, KV_ROT_HADAMARD_BITREV = 1, KV_ROT_HADAMARD = 2 };
 
 /* Buffers of a cache, by role.  Element types and shapes (Tc = capacity; with
  * paged storage every [B][H][Tc] reads [num_pages][H][page_tokens], [B][Tc]
@@ -171,8 +186,9 @@ enum kv_buffer {
 
 /* A cache: its layout, device buffers (NULL where the format has none) and
  * the method's constants, as device arrays of fp32 (made by the helpers below):
- *   rot        TURBO: d x d rotation R, row-major, y = R x, bf16-valued,
- *              16-byte aligned
+ *   rot        TURBO with layout.rotation KV_ROT_DENSE: d x d rotation R,
+ *              row-major, y = R x, bf16-valued, 16-byte aligned (not read,
+ *              and may be NULL, with a structured rotation)
  *   proj       TURBO, QJL1: m x d QJL matrix S, row-major, bf16-valued,
  *              16-byte aligned
  *   lm_levels  TURBO: 2^lm_bits Lloyd-Max levels, ascending and symmetric

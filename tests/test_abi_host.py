@@ -317,6 +317,24 @@ def test_stream_read_validation():
     assert L.kv_stream_read(FAKE, 0, FAKE, None) == EINVAL
 
 
+def test_rotation_kind_validation():
+    # a structured rotation is TURBO's alone, and lets the cache go without a matrix
+    assert kvq.kv_bytes_per_token(kvq.make_layout("turbo", 1, 8, 128, 64, rotation=kvq.ROT_HADAMARD_BITREV), 1) > 0
+    assert kvq.kv_bytes_per_token(kvq.make_layout("turbo", 1, 8, 128, 64, rotation=3), 1) == 0
+    assert kvq.kv_bytes_per_token(kvq.make_layout("turbo", 1, 8, 128, 64, rotation=-1), 1) == 0
+    assert kvq.kv_bytes_per_token(kvq.make_layout("fp4", 1, 8, 128, 64, rotation=kvq.ROT_HADAMARD), 1) == 0
+    L = kvq.lib()
+    for kind, ok in ((kvq.ROT_DENSE, False), (kvq.ROT_HADAMARD_BITREV, True), (kvq.ROT_HADAMARD, True)):
+        lay = kvq.make_layout("turbo", 1, 1, 128, 64, rotation=kind)
+        bufs = (ctypes.c_void_p * len(kvq.BUFFERS))(
+            *[(FAKE if kvq.kv_buffer_bytes(lay, i) else None) for i in range(len(kvq.BUFFERS))])
+        cache = kvq.KVCache(lay, bufs, None, FAKE, FAKE, FAKE, None)   # no rotation matrix
+        need = ctypes.c_size_t(0)
+        st = L.kv_decode_attention(ctypes.byref(cache), FAKE, 0, 8, FAKE, 64, ctypes.c_float(0.1), FAKE, None,
+                                   ctypes.byref(need), None, None)
+        assert (st == 0) == ok, (kind, st)
+
+
 def test_compute_probe_validation():
     L = kvq.lib()
     for fn in (L.kv_mfma_probe, L.kv_lds_probe):
