@@ -1063,8 +1063,8 @@ __global__ void __launch_bounds__(512) turbo_append_small_kernel(
   float4 mr[2][8];
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
-    const float4* src = reinterpret_cast<const float4*>((m == 0 ? ra.rot : proj) + 16 * w * 128);
-    if (m == 0 ? dense : keys) {
+    if (m == 0 ? dense : keys) {  // (a structured rotation has no matrix: ra.rot may be NULL)
+      const float4* src = reinterpret_cast<const float4*>((m == 0 ? ra.rot : proj) + 16 * w * 128);
 #pragma unroll
       for (int j = 0; j < 8; ++j) mr[m][j] = src[64 * j + lane];
     }
